@@ -1,0 +1,126 @@
+"""ORACLE — test infrastructure only.
+
+Plain CPU reference implementations of the Gated DeltaNet forward pass:
+
+* ``forward`` / ``decode_step``: fp64 token-by-token recurrence (C, OpenMP),
+  oracle/gdn_recurrence.c.  This is the definition the GPU path is judged against.
+* ``chunk_form.chunk_forward``: an independent fp64 chunk-wise implementation
+  (numpy, general dense inverse) exposing the per-chunk intermediates
+  (cumulative gate, A, W, U, chunk-start state, U - W S).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP library
+and never imports it.
+
+Pins (tests/test_oracle.py, run without a GPU): the recurrence and the chunk
+form agree for C in {1, 2, 3, 16, 64, >= L} including ragged tails; beta = 0
+reduces to pure decay (closed form); alpha = beta = 1 with unit keys makes
+k_t S_t = v_t exactly and q_t = k_t reads back v_t; orthonormal keys with
+alpha = beta = 1 give S = sum_t k_t^T v_t; the delta write equals one gradient
+step on 1/2 ||k S - v||^2 (checked with torch autograd); the two algebraic
+forms of the update agree; alpha = 1 reduces to DeltaNet; outputs are affine
+in the initial state and linear in V when S0 = 0; GVA equals explicit head
+repetition; splitting a sequence and passing the state equals running it whole;
+a hand-derived d = 2 worked example (tests/golden/).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import chunk_form  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgdn_oracle.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+
+        _b.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.gdn_oracle_forward.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_double, P, P, P, P, I64,
+                                       P, ctypes.c_int]
+    lib.gdn_oracle_forward.restype = ctypes.c_int
+    lib.gdn_oracle_decode_step.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_double, P, P, P, I64,
+                                           ctypes.c_int]
+    lib.gdn_oracle_decode_step.restype = ctypes.c_int
+    lib.gdn_oracle_max_threads.argtypes = []
+    lib.gdn_oracle_max_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def max_threads() -> int:
+    return int(_load().gdn_oracle_max_threads())
+
+
+def forward(q, k, v, g, beta, cu_seqlens, H_q, H_v, scale, initial_state=None, heads=None,
+            want_out=True, want_delta=False, num_threads=0):
+    """fp64 recurrence over a packed batch.
+
+    q, k: [T, H_q, d_k]; v: [T, H_v, d_v]; g, beta: [T, H_v] — any float arrays,
+    converted to float32 (pass exact float32 / bf16-upcast values).
+    initial_state: [N, H_v, d_k, d_v] (float64 after conversion) or None.
+    heads: optional list of value heads to compute (others left zero).
+    Returns (out [T, H_v, d_v] float64 or None, final [N, H_v, d_k, d_v] float64[, delta]).
+    """
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    beta = np.ascontiguousarray(beta, dtype=np.float32)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    T, _, d_k = k.shape
+    d_v = v.shape[2]
+    N = len(cu) - 1
+    s0 = None if initial_state is None else np.ascontiguousarray(initial_state, dtype=np.float64)
+    out = np.zeros((T, H_v, d_v)) if want_out else None
+    fin = np.zeros((N, H_v, d_k, d_v))
+    hs = None if heads is None else np.ascontiguousarray(heads, dtype=np.int32)
+    delta = np.zeros((T, H_v, d_v)) if want_delta else None
+    rc = lib.gdn_oracle_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu), N, H_q, H_v, d_k, d_v,
+                                float(scale), _ptr(s0), _ptr(out), _ptr(fin), _ptr(hs),
+                                0 if hs is None else len(hs), _ptr(delta), int(num_threads))
+    if rc != 0:
+        raise ValueError("gdn_oracle_forward: bad arguments")
+    if want_delta:
+        return out, fin, delta
+    return out, fin
+
+
+def decode_step(q, k, v, g, beta, state, H_q, H_v, scale, heads=None, num_threads=0):
+    """One recurrent step for N sequences; ``state`` (float64 [N, H_v, d_k, d_v],
+    C-contiguous) is updated in place.  Returns out [N, H_v, d_v] float64."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    beta = np.ascontiguousarray(beta, dtype=np.float32)
+    if state.dtype != np.float64 or not state.flags["C_CONTIGUOUS"]:
+        raise ValueError("state must be C-contiguous float64")
+    N, _, d_k = k.shape
+    d_v = v.shape[2]
+    out = np.zeros((N, H_v, d_v))
+    hs = None if heads is None else np.ascontiguousarray(heads, dtype=np.int32)
+    rc = lib.gdn_oracle_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), N, H_q, H_v, d_k, d_v,
+                                    float(scale), _ptr(state), _ptr(out), _ptr(hs), 0 if hs is None else len(hs),
+                                    int(num_threads))
+    if rc != 0:
+        raise ValueError("gdn_oracle_decode_step: bad arguments")
+    return out
