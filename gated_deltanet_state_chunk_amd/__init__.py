@@ -1,0 +1,240 @@
+"""Gated DeltaNet forward pass on MI355X (gfx950): Python binding of libgdn.so.
+
+Argument marshalling only — every step of the computation runs in the HIP
+kernels of libgdn.so (see include/gdn.h for the C ABI, layouts and errors).
+PyTorch supplies device memory and the current stream.  There is no fallback:
+if libgdn.so is missing, importing the library functions raises.
+
+    import gated_deltanet_state_chunk_amd as gdn
+    out, final_state = gdn.chunk_fwd(q, k, v, g, beta, cu_seqlens, initial_state)
+    o = gdn.recurrent_step(q1, k1, v1, g1, beta1, state)   # state updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+__all__ = ["chunk_fwd", "recurrent_step", "workspace_layout", "workspace_size", "lib_path", "load_library",
+           "GdnError", "CHUNK"]
+
+CHUNK = 64
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgdn.so")
+_lib = None
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+_STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace", -4: "hip"}
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        lib = load_library()
+        msg = lib.gdn_status_string(status).decode()
+        hip = lib.gdn_last_hip_error().decode() if status == -4 else ""
+        super().__init__(f"{what}: {msg} ({status}){' — ' + hip if hip else ''}")
+        self.status = status
+
+
+class WorkspaceLayout(ctypes.Structure):
+    _fields_ = [("n_chunks", ctypes.c_int64), ("off_gc", ctypes.c_size_t), ("off_A", ctypes.c_size_t),
+                ("off_W", ctypes.c_size_t), ("off_Ut", ctypes.c_size_t), ("off_Kt", ctypes.c_size_t),
+                ("off_Ht", ctypes.c_size_t), ("off_Xt", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t)]
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libgdn.so (built in-tree by gated_deltanet_state_chunk_amd.build); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -m gated_deltanet_state_chunk_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    lib.gdn_version.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_last_hip_error.restype = ctypes.c_char_p
+    lib.gdn_chunk_fwd_workspace_layout.argtypes = [I32, I32, P, I32, I32, I32, I32, ctypes.c_int,
+                                                   ctypes.POINTER(WorkspaceLayout)]
+    lib.gdn_chunk_fwd_workspace_layout.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_workspace_size.argtypes = [I32, I32, P, I32, I32, I32, I32, ctypes.c_int]
+    lib.gdn_chunk_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.gdn_chunk_fwd.argtypes = [P, P, P, P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P,
+                                  ctypes.c_size_t, P]
+    lib.gdn_chunk_fwd.restype = ctypes.c_int
+    lib.gdn_recurrent_step.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P]
+    lib.gdn_recurrent_step.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_dev(name, t, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _host_cu(cu_seqlens) -> "ctypes.Array":
+    torch = _torch()
+    if isinstance(cu_seqlens, torch.Tensor):
+        if cu_seqlens.is_cuda:
+            raise TypeError("cu_seqlens must be a host array (list, numpy or CPU tensor)")
+        vals = [int(x) for x in cu_seqlens.tolist()]
+    else:
+        vals = [int(x) for x in cu_seqlens]
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def _stream_ptr(stream) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def workspace_layout(T: int, cu_seqlens, H_q: int, H_v: int, d_k: int, d_v: int, dtype) -> dict:
+    """Byte offsets of the workspace regions (see gdn_workspace_layout in include/gdn.h)."""
+    lib = load_library()
+    cu = _host_cu(cu_seqlens)
+    code = dtype if isinstance(dtype, int) else _dtype_code_from(dtype)
+    lay = WorkspaceLayout()
+    rc = lib.gdn_chunk_fwd_workspace_layout(T, len(cu) - 1, cu, H_q, H_v, d_k, d_v, code, ctypes.byref(lay))
+    if rc != 0:
+        raise GdnError(rc, "gdn_chunk_fwd_workspace_layout")
+    return {f: getattr(lay, f) for f, _ in WorkspaceLayout._fields_}
+
+
+def _dtype_code_from(dtype) -> int:
+    torch = _torch()
+    if dtype in (torch.bfloat16, "bf16"):
+        return DTYPE_BF16
+    if dtype in (torch.float32, "f32"):
+        return DTYPE_F32
+    raise TypeError(f"unsupported dtype {dtype}")
+
+
+def workspace_size(T: int, cu_seqlens, H_q: int, H_v: int, d_k: int, d_v: int, dtype) -> int:
+    return workspace_layout(T, cu_seqlens, H_q, H_v, d_k, d_v, dtype)["total_bytes"]
+
+
+# ---------------------------------------------------------------------------
+# operations
+# ---------------------------------------------------------------------------
+
+def chunk_fwd(q, k, v, g, beta, cu_seqlens: Sequence[int], initial_state=None, scale: Optional[float] = None,
+              out=None, final_state=None, output_final_state: bool = True, workspace=None, stream=None):
+    """Chunk-wise GDN prefill over a packed batch (gdn_chunk_fwd).
+
+    q, k: [T, H_q, d_k]; v: [T, H_v, d_v] (bf16 or fp32, same dtype); g, beta:
+    [T, H_v] fp32 (g = ln alpha per token); cu_seqlens: host int sequence [N+1];
+    initial_state: fp32 [N, H_v, d_k, d_v] or None.  Returns (out, final_state)
+    with final_state None when output_final_state is False.  ``workspace`` may
+    be a preallocated uint8 device tensor of at least workspace_size() bytes.
+    """
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("g", g, torch.float32)
+    _check_dev("beta", beta, torch.float32)
+    T, H_q, d_k = q.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    if k.shape != q.shape or v.shape[0] != T or g.shape != (T, H_v) or beta.shape != (T, H_v):
+        raise ValueError("inconsistent q/k/v/g/beta shapes")
+    cu = _host_cu(cu_seqlens)
+    N = len(cu) - 1
+    if initial_state is not None:
+        _check_dev("initial_state", initial_state, torch.float32)
+        if tuple(initial_state.shape) != (N, H_v, d_k, d_v):
+            raise ValueError("initial_state must be [N, H_v, d_k, d_v]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    if out is None:
+        out = torch.empty((T, H_v, d_v), dtype=q.dtype, device=q.device)
+    else:
+        _check_dev("out", out, q.dtype)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H_v, d_k, d_v), dtype=torch.float32, device=q.device)
+    elif final_state is not None:
+        _check_dev("final_state", final_state, torch.float32)
+    ws_bytes = lib.gdn_chunk_fwd_workspace_size(T, N, cu, H_q, H_v, d_k, d_v, dt)
+    if ws_bytes == 0 and N > 0 and T > 0:
+        lay = WorkspaceLayout()
+        rc = lib.gdn_chunk_fwd_workspace_layout(T, N, cu, H_q, H_v, d_k, d_v, dt, ctypes.byref(lay))
+        raise GdnError(rc, "gdn_chunk_fwd_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _check_dev("workspace", workspace)
+    rc = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), cu, N, _ptr(initial_state), _ptr(out),
+                           _ptr(final_state), T, H_q, H_v, d_k, d_v, float(scale), dt, _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_chunk_fwd")
+    return out, final_state
+
+
+def recurrent_step(q, k, v, g, beta, state, scale: Optional[float] = None, out=None, stream=None):
+    """One recurrent decode step (gdn_recurrent_step); ``state`` is updated in place.
+
+    q, k: [N, H_q, d_k]; v: [N, H_v, d_v] (bf16 or fp32); g, beta: [N, H_v] fp32;
+    state: fp32 [N, H_v, d_k, d_v].  Returns out [N, H_v, d_v] in q's dtype.
+    """
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("g", g, torch.float32)
+    _check_dev("beta", beta, torch.float32)
+    _check_dev("state", state, torch.float32)
+    N, H_q, d_k = q.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    if k.shape != q.shape or v.shape[0] != N or g.shape != (N, H_v) or beta.shape != (N, H_v) or \
+            tuple(state.shape) != (N, H_v, d_k, d_v):
+        raise ValueError("inconsistent decode shapes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    if out is None:
+        out = torch.empty((N, H_v, d_v), dtype=q.dtype, device=q.device)
+    else:
+        _check_dev("out", out, q.dtype)
+    rc = lib.gdn_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out), N, H_q, H_v,
+                                d_k, d_v, float(scale), dt, _stream_ptr(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_recurrent_step")
+    return out

@@ -1,0 +1,195 @@
+// Host side of libgdn.so: argument validation, workspace layout, launch
+// grouping.  Every check runs before any HIP call, so a rejected call writes
+// nothing and never touches the device (all-or-nothing entry points).
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "../../include/gdn.h"
+#include "gdn_params.h"
+
+namespace {
+
+thread_local std::string g_last_hip_error;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline size_t elem_size(gdn_dtype dt) { return dt == GDN_DTYPE_BF16 ? 2 : 4; }
+
+int check_shapes(int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype) {
+    if (H_q <= 0 || H_v <= 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_INVALID;
+    if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
+    if (d_k != d_v || (d_k != 64 && d_k != 128)) return GDN_ERR_UNSUPPORTED;
+    if (H_v % H_q != 0) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+// Validates cu_seqlens and counts chunks (each sequence chunked from its own start).
+int check_seqlens(int32_t T, int32_t num_seqs, const int32_t* cu, int64_t* n_chunks) {
+    if (T < 0 || num_seqs < 0) return GDN_ERR_INVALID;
+    if (num_seqs == 0) {
+        if (T != 0) return GDN_ERR_INVALID;
+        *n_chunks = 0;
+        return GDN_OK;
+    }
+    if (!cu) return GDN_ERR_INVALID;
+    if (cu[0] != 0 || cu[num_seqs] != T) return GDN_ERR_INVALID;
+    int64_t nc = 0;
+    for (int32_t i = 0; i < num_seqs; ++i) {
+        const int64_t len = (int64_t)cu[i + 1] - cu[i];
+        if (len < 0) return GDN_ERR_INVALID;
+        nc += (len + GDN_CHUNK - 1) / GDN_CHUNK;
+    }
+    if (nc > (int64_t)INT32_MAX / 1024) return GDN_ERR_UNSUPPORTED;
+    *n_chunks = nc;
+    return GDN_OK;
+}
+
+template <typename T, int D>
+hipError_t dispatch_chunk(const gdn::ChunkParams& p, hipStream_t s) {
+    return gdn::launch_chunk_pipeline<T, D>(p, s);
+}
+
+hipError_t run_chunk(const gdn::ChunkParams& p, gdn_dtype dt, int d, hipStream_t s) {
+    if (dt == GDN_DTYPE_BF16) return d == 128 ? dispatch_chunk<gdn::bf16, 128>(p, s) : dispatch_chunk<gdn::bf16, 64>(p, s);
+    return d == 128 ? dispatch_chunk<float, 128>(p, s) : dispatch_chunk<float, 64>(p, s);
+}
+
+hipError_t run_decode(const gdn::DecodeParams& p, gdn_dtype dt, int d, hipStream_t s) {
+    if (dt == GDN_DTYPE_BF16)
+        return d == 128 ? gdn::launch_recurrent_step<gdn::bf16, 128>(p, s) : gdn::launch_recurrent_step<gdn::bf16, 64>(p, s);
+    return d == 128 ? gdn::launch_recurrent_step<float, 128>(p, s) : gdn::launch_recurrent_step<float, 64>(p, s);
+}
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = hipGetErrorString(e);
+    return GDN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_version(void) { return "0.1.0"; }
+
+const char* gdn_status_string(int status) {
+    switch (status) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_INVALID: return "invalid argument";
+        case GDN_ERR_UNSUPPORTED: return "unsupported shape, dtype or alignment";
+        case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+        case GDN_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+const char* gdn_last_hip_error(void) { return g_last_hip_error.c_str(); }
+
+int gdn_chunk_fwd_workspace_layout(int32_t T, int32_t num_seqs, const int32_t* cu_seqlens_host, int32_t H_q,
+                                   int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype,
+                                   gdn_workspace_layout* layout) {
+    if (!layout) return GDN_ERR_INVALID;
+    int rc = check_shapes(H_q, H_v, d_k, d_v, dtype);
+    if (rc != GDN_OK) return rc;
+    int64_t nc = 0;
+    rc = check_seqlens(T, num_seqs, cu_seqlens_host, &nc);
+    if (rc != GDN_OK) return rc;
+    const size_t es = elem_size(dtype);
+    const size_t C = GDN_CHUNK;
+    const size_t chv = (size_t)nc * (size_t)H_v;
+    size_t off = 0;
+    gdn_workspace_layout L;
+    L.n_chunks = nc;
+    L.off_gc = off; off = align_up(off + chv * C * sizeof(float));
+    L.off_A = off;  off = align_up(off + chv * C * C * es);
+    L.off_W = off;  off = align_up(off + chv * C * (size_t)d_k * es);
+    L.off_Ut = off; off = align_up(off + chv * (size_t)d_v * C * es);
+    L.off_Kt = off; off = align_up(off + (size_t)nc * H_q * (size_t)d_k * C * es);
+    L.off_Ht = off; off = align_up(off + chv * (size_t)d_v * (size_t)d_k * es);
+    L.off_Xt = off; off = align_up(off + chv * (size_t)d_v * C * es);
+    L.total_bytes = off;
+    *layout = L;
+    return GDN_OK;
+}
+
+size_t gdn_chunk_fwd_workspace_size(int32_t T, int32_t num_seqs, const int32_t* cu_seqlens_host, int32_t H_q,
+                                    int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype) {
+    gdn_workspace_layout L;
+    if (gdn_chunk_fwd_workspace_layout(T, num_seqs, cu_seqlens_host, H_q, H_v, d_k, d_v, dtype, &L) != GDN_OK)
+        return 0;
+    return L.total_bytes;
+}
+
+int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                  const int32_t* cu_seqlens_host, int32_t num_seqs, const float* initial_state, void* out,
+                  float* final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
+                  gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    gdn_workspace_layout L;
+    int rc = gdn_chunk_fwd_workspace_layout(T, num_seqs, cu_seqlens_host, H_q, H_v, d_k, d_v, dtype, &L);
+    if (rc != GDN_OK) return rc;
+    if (num_seqs == 0) return GDN_OK;
+    // Pointers: tensors with T > 0 rows must be present; all must be 16-byte aligned.
+    if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_INVALID;
+    const void* ptrs[] = {q, k, v, g, beta, out, initial_state, final_state, workspace};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return GDN_ERR_INVALID;  // NaN
+    if (L.n_chunks > 0 && (!workspace || workspace_bytes < L.total_bytes)) return GDN_ERR_WORKSPACE;
+
+    char* ws = static_cast<char*>(workspace);
+    gdn::ChunkParams p;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.s0 = initial_state; p.out = out; p.sfinal = final_state;
+    p.gc = reinterpret_cast<float*>(ws + L.off_gc);
+    p.A = ws + L.off_A; p.W = ws + L.off_W; p.Ut = ws + L.off_Ut; p.Kt = ws + L.off_Kt;
+    p.Ht = ws + L.off_Ht; p.Xt = ws + L.off_Xt;
+    p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // Launch groups of up to MAX_SEQS_PER_LAUNCH sequences, each with its table in the kernel arguments.
+    int32_t chunk_base = 0;
+    for (int32_t s0 = 0; s0 < num_seqs; s0 += gdn::MAX_SEQS_PER_LAUNCH) {
+        const int32_t ns = std::min<int32_t>(gdn::MAX_SEQS_PER_LAUNCH, num_seqs - s0);
+        gdn::SeqTable& tab = p.tab;
+        tab.num_seqs = ns;
+        tab.seq_base = s0;
+        tab.chunk_begin = chunk_base;
+        int32_t c = chunk_base;
+        for (int32_t i = 0; i <= ns; ++i) {
+            tab.cu[i] = cu_seqlens_host[s0 + i];
+            tab.choff[i] = c;
+            if (i < ns) c += (cu_seqlens_host[s0 + i + 1] - cu_seqlens_host[s0 + i] + GDN_CHUNK - 1) / GDN_CHUNK;
+        }
+        tab.n_chunks = c - chunk_base;
+        chunk_base = c;
+        const hipError_t e = run_chunk(p, dtype, d_k, s);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return GDN_OK;
+}
+
+int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g, const float* beta, float* state,
+                       void* out, int32_t N, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
+                       gdn_dtype dtype, void* stream) {
+    int rc = check_shapes(H_q, H_v, d_k, d_v, dtype);
+    if (rc != GDN_OK) return rc;
+    if (N < 0) return GDN_ERR_INVALID;
+    if (N == 0) return GDN_OK;
+    if ((int64_t)N * H_v > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !g || !beta || !state || !out) return GDN_ERR_INVALID;
+    const void* ptrs[] = {q, k, v, g, beta, state, out};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return GDN_ERR_INVALID;
+    gdn::DecodeParams p;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.state = state; p.out = out;
+    p.N = N; p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
+    const hipError_t e = run_decode(p, dtype, d_k, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+    return GDN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Recurrent Gated DeltaNet decode step for gfx950.
+//
+// The update of one (sequence, value head) state S (d_k x d_v, fp32) for one
+// token ("实验三：GDN Prefill 前向优化", section "GLA, DeltaNet 与 Gated DeltaNet";
+// "Qwen3.5-397B-A17B" trace page, Decode-GDN node 7, its decay / delta / read
+// steps):
+//     Sbar = alpha S,  delta = beta (v - k Sbar),  S' = Sbar + k^T delta,  o = scale q S'.
+// It is computed in ONE pass over S: k Sbar = alpha (k S) and
+// q S' = alpha (q S) + (q . k) delta, so both column reductions k S and q S are
+// taken from the values read once, and S' is written once.  The pass is bound
+// by HBM bandwidth (64 KiB read + 64 KiB written per head at d = 128).
+//
+// One 256-thread workgroup per (sequence, value head).  Thread t owns a 16-byte
+// column group cg = t % (d/4) of rows rg + RG*m (RG = 1024/d row groups), so
+// each wave reads whole contiguous rows with 128-bit loads.  Column sums are
+// reduced across row groups with lane shuffles inside a wave and through LDS
+// across the four waves.
+#include "gdn_device.h"
+#include "gdn_params.h"
+
+namespace gdn {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void recurrent_step_kernel(const DecodeParams p) {
+    constexpr int CPR = D / 4;      // float4 column groups per row
+    constexpr int RG = 256 / CPR;   // row groups
+    constexpr int RPT = D / RG;     // rows per thread
+    constexpr int RGW = 64 / CPR;   // row groups per wave
+    constexpr int NV = 9;           // reduced values: k S (4), q S (4), q . k
+    const int nh = blockIdx.x;
+    const int n = nh / p.H_v, h = nh % p.H_v;
+    const int hq = h / p.G;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int cg = tid % CPR, rg = tid / CPR;
+
+    __shared__ float s_red[4][CPR][NV];
+
+    const size_t sidx = (size_t)nh * D * D;
+    float4* Sp = reinterpret_cast<float4*>(p.state + sidx);
+    const T* qp = reinterpret_cast<const T*>(p.q) + ((size_t)n * p.H_q + hq) * D;
+    const T* kp = reinterpret_cast<const T*>(p.k) + ((size_t)n * p.H_q + hq) * D;
+    const T* vp = reinterpret_cast<const T*>(p.v) + (size_t)nh * D;
+    const float alpha = __expf(p.g[nh]);
+    const float beta = p.beta[nh];
+
+    float4 s[RPT];
+    float kr[RPT], qr[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int row = rg + RG * m;
+        s[m] = Sp[row * CPR + cg];
+        kr[m] = to_f32<T>(kp[row]);
+        qr[m] = to_f32<T>(qp[row]);
+    }
+    float red[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) red[e] = 0.f;
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        red[0] += kr[m] * s[m].x;
+        red[1] += kr[m] * s[m].y;
+        red[2] += kr[m] * s[m].z;
+        red[3] += kr[m] * s[m].w;
+        red[4] += qr[m] * s[m].x;
+        red[5] += qr[m] * s[m].y;
+        red[6] += qr[m] * s[m].z;
+        red[7] += qr[m] * s[m].w;
+        red[8] += qr[m] * kr[m];
+    }
+    // Row groups inside a wave differ in the lane bits above log2(CPR).
+#pragma unroll
+    for (int msk = CPR; msk < 64; msk <<= 1)
+#pragma unroll
+        for (int e = 0; e < NV; ++e) red[e] += wave_shfl_xor(red[e], msk);
+    if (lane < CPR) {
+#pragma unroll
+        for (int e = 0; e < NV; ++e) s_red[w][lane][e] = red[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < NV; ++e) red[e] = s_red[0][cg][e] + s_red[1][cg][e] + s_red[2][cg][e] + s_red[3][cg][e];
+    (void)RGW;
+
+    float vv[4];
+    load4(vp + 4 * cg, vv[0], vv[1], vv[2], vv[3]);
+    float dl[4], o[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        dl[c] = beta * (vv[c] - alpha * red[c]);
+        o[c] = p.scale * (alpha * red[4 + c] + red[8] * dl[c]);
+    }
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int row = rg + RG * m;
+        float4 t = s[m];
+        t.x = alpha * t.x + kr[m] * dl[0];
+        t.y = alpha * t.y + kr[m] * dl[1];
+        t.z = alpha * t.z + kr[m] * dl[2];
+        t.w = alpha * t.w + kr[m] * dl[3];
+        Sp[row * CPR + cg] = t;
+    }
+    if (rg == 0) store4(reinterpret_cast<T*>(p.out) + (size_t)nh * D + 4 * cg, o[0], o[1], o[2], o[3]);
+}
+
+template <typename T, int D>
+hipError_t launch_recurrent_step(const DecodeParams& p, hipStream_t stream) {
+    const int nwg = p.N * p.H_v;
+    if (nwg > 0) hipLaunchKernelGGL((recurrent_step_kernel<T, D>), dim3(nwg), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+template hipError_t launch_recurrent_step<bf16, 128>(const DecodeParams&, hipStream_t);
+template hipError_t launch_recurrent_step<bf16, 64>(const DecodeParams&, hipStream_t);
+template hipError_t launch_recurrent_step<float, 128>(const DecodeParams&, hipStream_t);
+template hipError_t launch_recurrent_step<float, 64>(const DecodeParams&, hipStream_t);
+
+}  // namespace gdn

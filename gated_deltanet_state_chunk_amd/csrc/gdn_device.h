@@ -1,0 +1,151 @@
+// Device helpers shared by the gfx950 kernels: MFMA fragments, element
+// conversion, layout permutation and XCD-aware work mapping.
+//
+// MFMA conventions (gfx950, wave64).  A 16x16 output tile D = A B + C is held
+// as f32x4 per lane: lane l holds column (l & 15), rows 4*(l >> 4) + {0..3}.
+// An operand fragment covers 16 rows (A) or 16 columns (B) by 32 contraction
+// indices and holds 8 values per lane: lane l serves row/column (l & 15) and
+// slots j = 0..7 of lane group a = (l >> 4).  Which contraction index a slot
+// stands for is a free choice as long as A and B agree; two conventions are
+// used:
+//   * "contiguous": slot j of group a is index 8a + j (both operands loaded
+//     from memory with 16-byte loads);
+//   * "perm32": slot j = 4h + b of group a is index 16h + 4a + b, so that two
+//     vertically stacked D tiles (rows 0..15 and 16..31) ARE a B fragment
+//     without any data movement.  Operands stored in memory with the perm32
+//     layout (index 16h + 4a + b at offset 8a + 4h + b) load with one 16-byte
+//     access per fragment.
+// For bf16 one fragment feeds one v_mfma_f32_16x16x32_bf16; for fp32 it feeds
+// eight v_mfma_f32_16x16x4_f32, instruction j consuming slot j of every lane
+// (group a supplies contraction row a), which is the same pairing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int CHUNK = 64;
+
+// 8-value operand fragment of element type T.
+template <typename T>
+struct Frag;
+template <>
+struct Frag<bf16> {
+    bf16x8 v;
+};
+template <>
+struct Frag<float> {
+    float v[8];
+};
+
+__device__ __forceinline__ f32x4 mma(const Frag<bf16>& a, const Frag<bf16>& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const Frag<float>& a, const Frag<float>& b, f32x4 c) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
+    return c;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---- element conversion --------------------------------------------------
+template <typename T>
+__device__ __forceinline__ float to_f32(T x);
+template <>
+__device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ float to_f32<bf16>(bf16 x) { return (float)x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // round to nearest even
+
+// ---- fragment loads ------------------------------------------------------
+// 8 consecutive elements at p (16-byte aligned for bf16, 32-byte for fp32).
+__device__ __forceinline__ void load8(Frag<bf16>& f, const bf16* p) { f.v = *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ void load8(Frag<float>& f, const float* p) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+// Same, but the 8 values are zero when `valid` is false (no memory access).
+template <typename T>
+__device__ __forceinline__ void load8_masked(Frag<T>& f, const T* p, bool valid) {
+    if (valid) {
+        load8(f, p);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f.v[j] = from_f32<T>(0.f);
+    }
+}
+
+// Set slot j of a fragment from an fp32 value.
+template <typename T>
+__device__ __forceinline__ void frag_set(Frag<T>& f, int j, float x) {
+    f.v[j] = from_f32<T>(x);
+}
+template <typename T>
+__device__ __forceinline__ float frag_get(const Frag<T>& f, int j) {
+    return to_f32<T>(f.v[j]);
+}
+
+// Two stacked D tiles (rows 0..15 -> lo, rows 16..31 -> hi) as a perm32 B fragment,
+// each value multiplied by s.
+template <typename T>
+__device__ __forceinline__ Frag<T> pack_perm32(const f32x4& lo, const f32x4& hi, float s) {
+    Frag<T> f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        f.v[b] = from_f32<T>(lo[b] * s);
+        f.v[4 + b] = from_f32<T>(hi[b] * s);
+    }
+    return f;
+}
+
+// ---- stores of 4 consecutive values --------------------------------------
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+    bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+    *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void load4(const bf16* p, float& a, float& b, float& c, float& d) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+    a = (float)v[0]; b = (float)v[1]; c = (float)v[2]; d = (float)v[3];
+}
+__device__ __forceinline__ void load4(const float* p, float& a, float& b, float& c, float& d) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    a = v.x; b = v.y; c = v.z; d = v.w;
+}
+
+// perm32 storage offset of logical index i.
+__host__ __device__ __forceinline__ int perm32(int i) {
+    const int blk = i & ~31, r = i & 31;
+    const int h = r >> 4, a = (r >> 2) & 3, b = r & 3;
+    return blk + 8 * a + 4 * h + b;
+}
+
+// ---- XCD-aware work mapping ----------------------------------------------
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
+// XCD i % 8).  Mapping workgroup i to work item (i % 8) * per + i / 8 hands
+// each XCD one contiguous run of work items, so neighbouring items (the value
+// heads sharing a key head, consecutive chunks of a sequence) share that XCD's
+// L2.  `padded` is the grid size, a multiple of 8.
+__device__ __forceinline__ int xcd_remap(int i, int padded) { return (i & 7) * (padded >> 3) + (i >> 3); }
+
+// ---- wave helpers --------------------------------------------------------
+__device__ __forceinline__ float wave_shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
+
+}  // namespace gdn

@@ -1,0 +1,69 @@
+// Launch parameters shared by the host library and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+
+// Sequences handled by one launch of the chunk pipeline.  A packed batch with
+// more sequences is processed in several launches over disjoint sequence
+// ranges (sequences are independent, so this is exact).
+constexpr int MAX_SEQS_PER_LAUNCH = 64;
+
+// Per-launch sequence table, passed by value in the kernel arguments so that
+// no host->device copy (and no host synchronisation) is needed per call.
+struct SeqTable {
+    int32_t num_seqs;     // sequences in this launch
+    int32_t seq_base;     // global index of the first one (indexes the state arrays)
+    int32_t chunk_begin;  // global index of its first chunk
+    int32_t n_chunks;     // chunks in this launch
+    int32_t cu[MAX_SEQS_PER_LAUNCH + 1];     // global token offsets
+    int32_t choff[MAX_SEQS_PER_LAUNCH + 1];  // global chunk offsets, choff[num_seqs] = chunk_begin + n_chunks
+};
+
+struct ChunkParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const float* s0;  // may be null
+    void* out;
+    float* sfinal;  // may be null
+    // workspace regions
+    float* gc;
+    void* A;
+    void* W;
+    void* Ut;
+    void* Kt;
+    void* Ht;
+    void* Xt;
+    int32_t H_q, H_v, G;
+    float scale;
+    SeqTable tab;
+};
+
+struct DecodeParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    float* state;
+    void* out;
+    int32_t N, H_q, H_v, G;
+    float scale;
+};
+
+// Kernel launchers (defined in the .hip translation units).  T is float or
+// __bf16, D is d_k = d_v.
+template <typename T, int D>
+hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream);
+
+template <typename T, int D>
+hipError_t launch_recurrent_step(const DecodeParams& p, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,166 @@
+/*
+ * gdn.h — Gated DeltaNet forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libgdn.so.  Two operations:
+ *
+ *   gdn_chunk_fwd       chunk-wise parallel prefill over packed variable-length
+ *                       sequences (chunk size C = 64), with optional initial
+ *                       states and returned final states;
+ *   gdn_recurrent_step  one recurrent decode step for a batch of fp32 states,
+ *                       updated in place.
+ *
+ * Notation (row vectors): q_t, k_t in R^{1 x d_k}, v_t in R^{1 x d_v},
+ * S in R^{d_k x d_v}.  The recurrence both calls compute is the Gated DeltaNet
+ * rule of "实验三：GDN Prefill 前向优化" (section "GLA, DeltaNet 与 Gated
+ * DeltaNet"):
+ *
+ *     Sbar_t = alpha_t S_{t-1},   S_t = Sbar_t + beta_t k_t^T (v_t - k_t Sbar_t),
+ *     o_t    = scale * q_t S_t        (the read sees the updated state)
+ *
+ * with alpha_t = exp(g_t); g is the per-token log decay (raw_g on that page,
+ * section "输入输出定义"), never a cumulative sum.  `scale` is the 1/sqrt(d_k)
+ * factor of the chunk output formula (section "计算过程描述"); callers pass it
+ * explicitly so prefill and decode agree.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless the name ends in _host.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call is
+ *     asynchronous on that stream; the library never synchronises and never
+ *     allocates or frees memory: all buffers are owned by the caller.
+ *   - Layouts are row-major with the last dimension contiguous:
+ *       q, k   [T, H_q, d_k]          v, out [T, H_v, d_v]
+ *       g, beta [T, H_v]  (always fp32)
+ *       states  [N, H_v, d_k, d_v]  (always fp32, d_v contiguous)
+ *     Value head h reads query/key head floor(h / (H_v / H_q)) (GVA grouping,
+ *     section "输入输出定义" of the same page).
+ *   - q, k, v and out share one element type, `dtype`.
+ *   - Every device pointer must be 16-byte aligned.
+ *   - Arguments are validated before any work is queued; on any error nothing
+ *     is written and a negative status is returned.  There is no fallback path.
+ *   - Supported shapes: d_k == d_v in {64, 128}; H_v a multiple of H_q.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_dtype {
+    GDN_DTYPE_F32 = 0,  /* IEEE binary32 */
+    GDN_DTYPE_BF16 = 1, /* bfloat16, round-to-nearest-even on output */
+} gdn_dtype;
+
+enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID = -1,     /* NULL / inconsistent arguments, bad cu_seqlens */
+    GDN_ERR_UNSUPPORTED = -2, /* d_k != d_v, d not in {64,128}, H_v % H_q != 0, misaligned pointer */
+    GDN_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than gdn_chunk_fwd_workspace_size() */
+    GDN_ERR_HIP = -4,         /* a HIP launch failed; gdn_last_hip_error() names it */
+};
+
+/* Chunk length of the prefill (fixed; section "Chunk-wise Parallel"). */
+#define GDN_CHUNK 64
+
+/*
+ * Workspace of gdn_chunk_fwd.  One region per intermediate of the chunk form
+ * (section "计算过程描述": g^cumsum, A, W, U, the chunk-start states, U - W S),
+ * each starting on a 256-byte boundary.  The intermediates stay in the
+ * workspace after the call and may be read back for inspection; chunks are
+ * numbered in sequence order, each sequence's chunks starting at its own first
+ * token, so chunk c of sequence n has global index chunk_offset(n) + c where
+ * chunk_offset(n) = sum_{m<n} ceil(L_m / 64).  Positions beyond a tail chunk's
+ * valid length hold zeros.  "perm32" below means: within every block of 32
+ * consecutive indices, index 16*h + 4*a + b (h in {0,1}, a, b in 0..3) is
+ * stored at offset 8*a + 4*h + b.
+ *
+ *   gc  fp32  [n_chunks][H_v][64]            inclusive in-chunk cumsum of g
+ *   A   dtype [n_chunks][H_v][64][64]        (I + StrictLower(B Gamma K K^T Gamma^-1))^-1
+ *   W   dtype [n_chunks][H_v][64][d_k]       A B Gamma K, last index perm32
+ *   Ut  dtype [n_chunks][H_v][d_v][64]       (A B V)^T
+ *   Kt  dtype [n_chunks][H_q][d_k][64]       K^T of the chunk, last index perm32
+ *   Ht  dtype [n_chunks][H_v][d_v][d_k]      (state at chunk start)^T
+ *   Xt  dtype [n_chunks][H_v][d_v][64]       (U - W S)^T, last index perm32
+ */
+typedef struct gdn_workspace_layout {
+    int64_t n_chunks;
+    size_t off_gc, off_A, off_W, off_Ut, off_Kt, off_Ht, off_Xt; /* byte offsets */
+    size_t total_bytes;
+} gdn_workspace_layout;
+
+/*
+ * Host-only.  Validates the batch description and fills `layout`.
+ * cu_seqlens_host: HOST int32 [num_seqs + 1], 0 = c[0] <= c[1] <= ... <= c[num_seqs] = T.
+ * Returns GDN_OK or GDN_ERR_INVALID / GDN_ERR_UNSUPPORTED.
+ */
+int gdn_chunk_fwd_workspace_layout(int32_t T, int32_t num_seqs, const int32_t *cu_seqlens_host, int32_t H_q,
+                                   int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype,
+                                   gdn_workspace_layout *layout);
+
+/* Host-only.  Bytes of workspace gdn_chunk_fwd needs, or 0 if the arguments are invalid. */
+size_t gdn_chunk_fwd_workspace_size(int32_t T, int32_t num_seqs, const int32_t *cu_seqlens_host, int32_t H_q,
+                                    int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype);
+
+/*
+ * Chunk-wise prefill ("实验三：GDN Prefill 前向优化", sections "计算过程描述" and
+ * "输入输出定义").  For every sequence n (tokens c[n] .. c[n+1]-1) and value
+ * head h, starting from initial_state[n, h] (zeros if initial_state == NULL),
+ * computes per chunk of <= 64 tokens
+ *     A = (I + StrictLower(B Gamma K K^T Gamma^-1))^-1,  U = A B V,  W = A B Gamma K,
+ *     S_next = gamma_l S + gamma_l K^T Gamma^-1 (U - W S),
+ *     O      = scale [Gamma Q S + Gamma Lower(Q K^T) Gamma^-1 (U - W S)],
+ * Gamma = Diag(exp(in-chunk inclusive cumsum of g)), B = Diag(beta), gamma_l the
+ * last valid token's entry; this equals the token recurrence above.
+ *
+ *   q, k      dtype [T, H_q, d_k]      v dtype [T, H_v, d_v]
+ *   g, beta   fp32  [T, H_v]           g = ln(alpha) per token
+ *   cu_seqlens_host  HOST int32 [num_seqs + 1] (see above); sequences may be empty
+ *   initial_state  fp32 [num_seqs, H_v, d_k, d_v] or NULL
+ *   out       dtype [T, H_v, d_v]      (written for every token)
+ *   final_state fp32 [num_seqs, H_v, d_k, d_v] or NULL; may equal initial_state
+ *             (read fully before written).  Other overlaps are undefined.
+ *   workspace  device buffer of >= gdn_chunk_fwd_workspace_size() bytes; its
+ *             contents on return are documented in gdn_workspace_layout.
+ * num_seqs == 0 or T == 0 is a no-op returning GDN_OK.
+ */
+int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                  const int32_t *cu_seqlens_host, int32_t num_seqs, const float *initial_state, void *out,
+                  float *final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
+                  gdn_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One recurrent decode step ("Qwen3.5-397B-A17B" trace page, Decode-GDN node 7,
+ * gdn_packed_recurrent_qk_norm_gating_state_update — its decay, delta update and
+ * read; the Q/K normalisation and gate transform of that node are not part of
+ * this call: q, k arrive normalised and g, beta arrive final).  For every
+ * sequence n and value head h, with alpha = exp(g[n,h]):
+ *     S = alpha S;  delta = beta (v - k S);  S = S + k^T delta;  o = scale * q S
+ * computed in fp32 in one pass over S (read once, written once).
+ *
+ *   q, k   dtype [N, H_q, d_k]    v dtype [N, H_v, d_v]
+ *   g, beta fp32 [N, H_v]
+ *   state  fp32 [N, H_v, d_k, d_v], updated IN PLACE
+ *   out    dtype [N, H_v, d_v]
+ * N == 0 is a no-op returning GDN_OK.
+ */
+int gdn_recurrent_step(const void *q, const void *k, const void *v, const float *g, const float *beta, float *state,
+                       void *out, int32_t N, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
+                       gdn_dtype dtype, void *stream);
+
+/* Static string naming a status code. */
+const char *gdn_status_string(int status);
+
+/* Text of the last HIP error seen by this thread inside the library ("" if none). */
+const char *gdn_last_hip_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char *gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

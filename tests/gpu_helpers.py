@@ -1,0 +1,69 @@
+"""Helpers for the GPU parity tests: host->device transfer of seeded inputs,
+the error metric, and un-permuting the documented workspace layout."""
+import numpy as np
+
+
+def rel_err(x, ref) -> float:
+    """max|x - ref| / max|ref| over the whole tensor (the metric the tolerances use)."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    num = float(np.max(np.abs(x - ref))) if ref.size else 0.0
+    return num / den if den > 0 else num
+
+
+def to_dev(arr, dtype: str, device="cuda"):
+    import torch
+
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def f32_dev(arr, device="cuda"):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def to_host(t) -> np.ndarray:
+    import torch
+
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def perm32_index(n: int) -> np.ndarray:
+    """perm32 storage offset of each logical index 0..n-1 (n a multiple of 32)."""
+    i = np.arange(n)
+    blk, r = i & ~31, i & 31
+    h, a, b = r >> 4, (r >> 2) & 3, r & 3
+    return blk + 8 * a + 4 * h + b
+
+
+def unperm32(stored: np.ndarray) -> np.ndarray:
+    """Logical array from a perm32-stored one (permutation along the last axis)."""
+    return stored[..., perm32_index(stored.shape[-1])]
+
+
+def chunk_fwd_device(inp, device="cuda", initial_state="from_inputs", return_ws=False):
+    """Run gdn_chunk_fwd on seeded inputs; returns (out, final, workspace-or-None) as host arrays / tensor."""
+    import torch
+
+    import gated_deltanet_state_chunk_amd as gdn
+
+    q = to_dev(inp.q, inp.dtype, device)
+    k = to_dev(inp.k, inp.dtype, device)
+    v = to_dev(inp.v, inp.dtype, device)
+    g = f32_dev(inp.g, device)
+    beta = f32_dev(inp.beta, device)
+    s0 = None
+    if initial_state == "from_inputs" and inp.initial_state is not None:
+        s0 = f32_dev(inp.initial_state, device)
+    ws = torch.empty(max(gdn.workspace_size(inp.T, inp.cu_seqlens, inp.H_q, inp.H_v, inp.d_k, inp.d_v,
+                                            inp.dtype), 1), dtype=torch.uint8, device=device)
+    out, fin = gdn.chunk_fwd(q, k, v, g, beta, inp.cu_seqlens, initial_state=s0, scale=inp.scale, workspace=ws)
+    torch.cuda.synchronize()
+    res = (to_host(out), to_host(fin))
+    if return_ws:
+        return res + (ws,)
+    return res

@@ -1,0 +1,161 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function
+include/gdn.h declares, computes workspace layouts on the host, and rejects bad
+arguments before touching the device (no compute call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import gated_deltanet_state_chunk_amd as gdn
+
+    if not os.path.exists(gdn.lib_path()):
+        from gated_deltanet_state_chunk_amd import build
+
+        build.build()
+    gdn.load_library()
+    return gdn
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(gdn):
+    names = _declared()
+    assert {"gdn_chunk_fwd", "gdn_recurrent_step", "gdn_chunk_fwd_workspace_size"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.lib_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (gdn_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    lib = ctypes.CDLL(gdn.lib_path())
+    for n in names:
+        getattr(lib, n)
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "gdn.h"\nint main(void){ return GDN_OK; }\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(tmp_path / "t")], check=True)
+
+
+def test_status_strings(gdn):
+    lib = gdn.load_library()
+    assert lib.gdn_status_string(0) == b"ok"
+    assert lib.gdn_status_string(-3).startswith(b"workspace")
+    assert lib.gdn_version().startswith(b"0.")
+    assert lib.gdn_last_hip_error() == b""
+
+
+def _cu(vals):
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def test_workspace_layout(gdn):
+    lay = gdn.workspace_layout(4096, [0, 4096], 16, 32, 128, 128, "bf16")
+    assert lay["n_chunks"] == 64
+    offs = [lay[k] for k in ("off_gc", "off_A", "off_W", "off_Ut", "off_Kt", "off_Ht", "off_Xt", "total_bytes")]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    chv = 64 * 32
+    assert lay["off_A"] - lay["off_gc"] == chv * 64 * 4
+    assert lay["off_Ht"] - lay["off_Kt"] == 64 * 16 * 128 * 64 * 2
+    assert lay["off_Xt"] - lay["off_Ht"] == chv * 128 * 128 * 2
+    # chunks are counted per sequence: ceil(100/64) + 0 + ceil(1/64) + ceil(128/64)
+    lay2 = gdn.workspace_layout(229, [0, 100, 100, 101, 229], 2, 4, 64, 64, "f32")
+    assert lay2["n_chunks"] == 2 + 0 + 1 + 2
+    assert gdn.workspace_size(0, [0], 2, 4, 64, 64, "f32") >= 0
+
+
+@pytest.mark.parametrize("args,status", [
+    # (T, cu, H_q, H_v, d_k, d_v, dtype) -> status
+    ((10, [0, 5, 10], 2, 4, 128, 128, 1), 0),
+    ((10, [0, 5, 9], 2, 4, 128, 128, 1), -1),   # cu[N] != T
+    ((10, [1, 5, 10], 2, 4, 128, 128, 1), -1),  # cu[0] != 0
+    ((10, [0, 6, 5, 10], 2, 4, 128, 128, 1), -1),  # decreasing
+    ((10, [0, 10], 3, 4, 128, 128, 1), -2),     # H_v % H_q
+    ((10, [0, 10], 2, 4, 128, 64, 1), -2),      # d_k != d_v
+    ((10, [0, 10], 2, 4, 96, 96, 1), -2),       # unsupported d
+    ((10, [0, 10], 2, 4, 128, 128, 7), -2),     # dtype
+    ((10, [0, 10], 0, 4, 128, 128, 1), -1),     # H_q = 0
+])
+def test_layout_validation(gdn, args, status):
+    lib = gdn.load_library()
+    T, cu, H_q, H_v, dk, dv, dt = args
+    lay = gdn.WorkspaceLayout()
+    rc = lib.gdn_chunk_fwd_workspace_layout(T, len(cu) - 1, _cu(cu), H_q, H_v, dk, dv, dt, ctypes.byref(lay))
+    assert rc == status
+    size = lib.gdn_chunk_fwd_workspace_size(T, len(cu) - 1, _cu(cu), H_q, H_v, dk, dv, dt)
+    assert (size > 0) == (status == 0)
+
+
+def _fake(n=1):
+    # 256-byte aligned host addresses that are never dereferenced: every call
+    # below fails validation before the library touches memory or the device.
+    buf = np.zeros(64 * n + 64, dtype=np.uint8)
+    base = (buf.ctypes.data + 255) // 256 * 256
+    return buf, base
+
+
+def test_chunk_fwd_rejects_before_any_device_work(gdn):
+    lib = gdn.load_library()
+    keep, p = _fake()
+    cu = _cu([0, 10])
+    good = dict(q=p, k=p, v=p, g=p, beta=p, cu=cu, N=1, s0=None, out=p, fin=p, T=10, H_q=2, H_v=4, dk=128, dv=128,
+                scale=0.1, dt=1, ws=p, wsb=1 << 40, stream=None)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return lib.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"], a["s0"], a["out"],
+                                 a["fin"], a["T"], a["H_q"], a["H_v"], a["dk"], a["dv"], a["scale"], a["dt"],
+                                 a["ws"], a["wsb"], a["stream"])
+
+    assert call(q=None) == -1
+    assert call(out=None) == -1
+    assert call(q=p + 8) == -2                 # misaligned
+    assert call(H_q=3) == -2
+    assert call(dk=64) == -2
+    assert call(scale=float("nan")) == -1
+    assert call(ws=None) == -3
+    assert call(wsb=16) == -3
+    assert call(cu=_cu([0, 11])) == -1
+    # empty batch is a no-op that succeeds without launching anything
+    assert call(N=0, T=0, cu=_cu([0])) == 0
+
+
+def test_recurrent_step_rejects_before_any_device_work(gdn):
+    lib = gdn.load_library()
+    keep, p = _fake()
+
+    def call(**kw):
+        a = dict(q=p, k=p, v=p, g=p, beta=p, st=p, out=p, N=4, H_q=2, H_v=4, dk=128, dv=128, scale=0.1, dt=1)
+        a.update(kw)
+        return lib.gdn_recurrent_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["st"], a["out"], a["N"],
+                                      a["H_q"], a["H_v"], a["dk"], a["dv"], a["scale"], a["dt"], None)
+
+    assert call(st=None) == -1
+    assert call(N=-1) == -1
+    assert call(H_q=3) == -2
+    assert call(dk=32, dv=32) == -2
+    assert call(out=p + 4) == -2
+    assert call(N=0) == 0
+
+
+def test_binding_refuses_host_tensors(gdn):
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(4, 2, 64)
+    with pytest.raises(ValueError):
+        gdn.chunk_fwd(q, q, torch.zeros(4, 4, 64), torch.zeros(4, 4), torch.zeros(4, 4), [0, 4])
+    with pytest.raises(TypeError):
+        gdn.chunk_fwd(q.to(torch.float16), q, q, q, q, [0, 4])

@@ -1,0 +1,221 @@
+"""GPU parity: libgdn.so (through its C ABI) against the fp64 oracle.
+
+Tolerances (max|err| / max|ref| per tensor): fp32 inputs 1e-4; bf16 q/k/v with
+fp32 accumulation 1e-2 on the output and the final state.  Sizes span several
+chunks and ragged tails; the full workloads are covered in
+test_gpu_workloads.py.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import gdn_inputs
+from tests.gpu_helpers import chunk_fwd_device, f32_dev, rel_err, to_dev, to_host, unperm32
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 1e-2}
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_deltanet_state_chunk_amd as gdn
+
+    gdn.load_library()
+    return torch
+
+
+def _oracle_prefill(oracle_mod, inp, heads=None):
+    s0 = None if inp.initial_state is None else inp.initial_state.astype(np.float64)
+    return oracle_mod.forward(inp.q32(), inp.k32(), inp.v32(), inp.g, inp.beta, inp.cu_seqlens, inp.H_q, inp.H_v,
+                              inp.scale, initial_state=s0, heads=heads)
+
+
+# ---------------------------------------------------------------------------
+# Decode step
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
+def test_recurrent_step_matches_oracle(torch_cuda, oracle_mod, dtype, d):
+    import gated_deltanet_state_chunk_amd as gdn
+
+    N, H_q, H_v = 5, 2, 4
+    scale = 1 / math.sqrt(d)
+    s0 = gdn_inputs.make_decode_state(77, N, H_v, d, d, std=0.1)
+    st = f32_dev(s0)
+    ref_state = s0.astype(np.float64)
+    for step in range(3):
+        tok = gdn_inputs.make_decode_token(900 + step, N, H_q, H_v, d, d, dtype=dtype)
+        o = gdn.recurrent_step(to_dev(tok.q, dtype), to_dev(tok.k, dtype), to_dev(tok.v, dtype), f32_dev(tok.g),
+                               f32_dev(tok.beta), st, scale=scale)
+        ref_o = oracle_mod.decode_step(tok.q32(), tok.k32(), tok.v32(), tok.g, tok.beta, ref_state, H_q, H_v, scale)
+        torch_cuda.cuda.synchronize()
+        tol = TOL[dtype]
+        assert rel_err(to_host(o), ref_o) < tol, f"step {step} out"
+        assert rel_err(to_host(st), ref_state) < tol, f"step {step} state"
+
+
+# ---------------------------------------------------------------------------
+# Chunk prefill, small cases
+# ---------------------------------------------------------------------------
+def test_chunk_tiny_f32_workload(torch_cuda, oracle_mod):
+    """The small fp32 workload: T=100 (64-chunk + 36-token tail), H=2, d=64, zero S0."""
+    inp = gdn_inputs.make_workload("tiny_f32_T100")
+    out, fin = chunk_fwd_device(inp)
+    ref_o, ref_s = _oracle_prefill(oracle_mod, inp)
+    assert rel_err(out, ref_o) < 1e-4
+    assert rel_err(fin, ref_s) < 1e-4
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("lens", [[1], [63], [64], [65], [200], [130, 0, 5, 64, 71]])
+def test_chunk_matches_oracle(torch_cuda, oracle_mod, dtype, d, lens):
+    inp = gdn_inputs.make_prefill(seed=31 + len(lens) + sum(lens), seqlens=lens, H_q=2, H_v=4, d_k=d, d_v=d,
+                                  dtype=dtype, state_std=0.05)
+    out, fin = chunk_fwd_device(inp)
+    ref_o, ref_s = _oracle_prefill(oracle_mod, inp)
+    assert rel_err(out, ref_o) < TOL[dtype]
+    assert rel_err(fin, ref_s) < TOL[dtype]
+
+
+def test_chunk_zero_initial_state_and_no_final(torch_cuda, oracle_mod):
+    import gated_deltanet_state_chunk_amd as gdn
+
+    inp = gdn_inputs.make_prefill(seed=5, seqlens=[100], H_q=1, H_v=2, d_k=128, d_v=128, dtype="bf16",
+                                  state_std=None)
+    out, fin = chunk_fwd_device(inp)
+    ref_o, ref_s = _oracle_prefill(oracle_mod, inp)
+    assert rel_err(out, ref_o) < 1e-2 and rel_err(fin, ref_s) < 1e-2
+    o2, f2 = gdn.chunk_fwd(to_dev(inp.q, "bf16"), to_dev(inp.k, "bf16"), to_dev(inp.v, "bf16"), f32_dev(inp.g),
+                           f32_dev(inp.beta), inp.cu_seqlens, output_final_state=False)
+    assert f2 is None
+    assert np.array_equal(to_host(o2), out)
+
+
+def test_chunk_in_place_state_and_determinism(torch_cuda, oracle_mod):
+    """final_state may alias initial_state; two runs are bitwise identical."""
+    import gated_deltanet_state_chunk_amd as gdn
+
+    inp = gdn_inputs.make_prefill(seed=6, seqlens=[150, 70], H_q=2, H_v=4, d_k=128, d_v=128, dtype="bf16")
+    out1, fin1 = chunk_fwd_device(inp)
+    out2, fin2 = chunk_fwd_device(inp)
+    assert np.array_equal(out1, out2) and np.array_equal(fin1, fin2)
+    st = f32_dev(inp.initial_state)
+    o3, f3 = gdn.chunk_fwd(to_dev(inp.q, "bf16"), to_dev(inp.k, "bf16"), to_dev(inp.v, "bf16"), f32_dev(inp.g),
+                           f32_dev(inp.beta), inp.cu_seqlens, initial_state=st, final_state=st)
+    torch_cuda.cuda.synchronize()
+    assert f3.data_ptr() == st.data_ptr()
+    assert np.array_equal(to_host(st), fin1) and np.array_equal(to_host(o3), out1)
+
+
+def test_chunk_many_sequences_multiple_launch_groups(torch_cuda, oracle_mod):
+    """More sequences than one launch's table holds (the host splits the batch)."""
+    rng = np.random.default_rng(40)
+    lens = [int(x) for x in rng.integers(0, 90, size=150)]
+    inp = gdn_inputs.make_prefill(seed=41, seqlens=lens, H_q=1, H_v=2, d_k=64, d_v=64, dtype="bf16")
+    out, fin = chunk_fwd_device(inp)
+    ref_o, ref_s = _oracle_prefill(oracle_mod, inp)
+    assert rel_err(out, ref_o) < 1e-2 and rel_err(fin, ref_s) < 1e-2
+
+
+def test_prefill_then_decode_continues(torch_cuda, oracle_mod):
+    """prefill(T) + decode(token T+1) == prefill(T+1) on the last output and the state."""
+    import gated_deltanet_state_chunk_amd as gdn
+
+    inp = gdn_inputs.make_prefill(seed=8, seqlens=[97], H_q=2, H_v=4, d_k=128, d_v=128, dtype="f32")
+    T = inp.T
+    q, k, v = to_dev(inp.q, "f32"), to_dev(inp.k, "f32"), to_dev(inp.v, "f32")
+    g, beta = f32_dev(inp.g), f32_dev(inp.beta)
+    s0 = f32_dev(inp.initial_state)
+    out_all, fin_all = gdn.chunk_fwd(q, k, v, g, beta, [0, T], initial_state=s0)
+    _, fin_pre = gdn.chunk_fwd(q[:T - 1].contiguous(), k[:T - 1].contiguous(), v[:T - 1].contiguous(),
+                               g[:T - 1].contiguous(), beta[:T - 1].contiguous(), [0, T - 1], initial_state=s0)
+    o_dec = gdn.recurrent_step(q[T - 1:], k[T - 1:], v[T - 1:], g[T - 1:], beta[T - 1:], fin_pre)
+    torch_cuda.cuda.synchronize()
+    assert rel_err(to_host(o_dec), to_host(out_all[T - 1:])) < 1e-5
+    assert rel_err(to_host(fin_pre), to_host(fin_all)) < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# Per-stage intermediates against the chunk-form oracle
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,d,tol", [("f32", 64, 1e-4), ("bf16", 128, 1e-2)])
+def test_chunk_intermediates_match_chunk_form(torch_cuda, dtype, d, tol):
+    import gated_deltanet_state_chunk_amd as gdn
+    from oracle import chunk_form
+
+    lens = [100, 64, 30]
+    H_q, H_v = 1, 2
+    inp = gdn_inputs.make_prefill(seed=9, seqlens=lens, H_q=H_q, H_v=H_v, d_k=d, d_v=d, dtype=dtype)
+    _, _, ws = chunk_fwd_device(inp, return_ws=True)
+    lay = gdn.workspace_layout(inp.T, inp.cu_seqlens, H_q, H_v, d, d, dtype)
+    nc = lay["n_chunks"]
+    assert nc == 2 + 1 + 1
+    wsb = ws.cpu().numpy()
+
+    def region(off, shape, is_f32=False):
+        import torch
+
+        nbytes = int(np.prod(shape)) * (4 if (is_f32 or dtype == "f32") else 2)
+        raw = ws[off:off + nbytes]
+        t = raw.view(torch.float32) if (is_f32 or dtype == "f32") else raw.view(torch.bfloat16)
+        return t.float().cpu().numpy().astype(np.float64).reshape(shape)
+
+    del wsb
+    gc = region(lay["off_gc"], (nc, H_v, 64), is_f32=True)
+    A = region(lay["off_A"], (nc, H_v, 64, 64))
+    W = unperm32(region(lay["off_W"], (nc, H_v, 64, d)))
+    U = np.swapaxes(region(lay["off_Ut"], (nc, H_v, d, 64)), -1, -2)
+    Kt = unperm32(region(lay["off_Kt"], (nc, H_q, d, 64)))
+    Hs = np.swapaxes(region(lay["off_Ht"], (nc, H_v, d, d)), -1, -2)
+    X = np.swapaxes(unperm32(region(lay["off_Xt"], (nc, H_v, d, 64))), -1, -2)
+
+    ref = chunk_form.chunk_forward(inp.q32(), inp.k32(), inp.v32(), inp.g, inp.beta, inp.cu_seqlens, H_q, H_v,
+                                   inp.scale, initial_state=inp.initial_state, keep_intermediates=True)
+    ci = 0
+    k32 = inp.k32()
+    for n, L in enumerate(lens):
+        for c in range((L + 63) // 64):
+            ell = min(64, L - 64 * c)
+            t0 = int(inp.cu_seqlens[n]) + 64 * c
+            for h in range(H_v):
+                r = ref["chunks"][(n, h)][c]
+                assert rel_err(gc[ci, h, :ell], r["gc"]) < 1e-5
+                assert np.all(gc[ci, h, ell:] == 0)
+                assert rel_err(A[ci, h, :ell, :ell], r["A"]) < tol
+                assert np.all(A[ci, h, ell:, :] == 0) and np.all(A[ci, h, :, ell:] == 0)
+                assert rel_err(W[ci, h, :ell], r["W"]) < tol
+                assert rel_err(U[ci, h, :ell], r["U"]) < tol
+                assert rel_err(Hs[ci, h], r["h"]) < tol
+                assert rel_err(X[ci, h, :ell], r["X"]) < 3 * tol
+                assert np.all(W[ci, h, ell:] == 0) and np.all(X[ci, h, ell:] == 0)
+            for hq in range(H_q):
+                assert np.array_equal(Kt[ci, hq, :, :ell], k32[t0:t0 + ell, hq, :].T)
+            ci += 1
+
+
+# ---------------------------------------------------------------------------
+# Pages' invariants on the device path
+# ---------------------------------------------------------------------------
+def test_beta_zero_pure_decay_on_gpu(torch_cuda):
+    inp = gdn_inputs.make_prefill(seed=11, seqlens=[150], H_q=2, H_v=2, d_k=64, d_v=64, dtype="f32",
+                                  beta_override=0.0, state_std=0.5)
+    out, fin = chunk_fwd_device(inp)
+    gam = np.exp(np.cumsum(inp.g.astype(np.float64), axis=0))
+    for h in range(2):
+        assert rel_err(fin[0, h], gam[-1, h] * inp.initial_state[0, h]) < 1e-5
+        exp_o = inp.scale * gam[:, h, None] * (inp.q32()[:, h, :].astype(np.float64) @ inp.initial_state[0, h])
+        assert rel_err(out[:, h, :], exp_o) < 1e-5
+
+
+def test_strong_decay_stays_finite(torch_cuda, oracle_mod):
+    """g down to -10 per token: Gamma^-1 alone would overflow fp32 within a chunk."""
+    inp = gdn_inputs.make_prefill(seed=12, seqlens=[130], H_q=1, H_v=2, d_k=64, d_v=64, dtype="f32")
+    inp.g[:] = np.float32(-10.0) * np.random.default_rng(3).uniform(0, 1, inp.g.shape).astype(np.float32)
+    out, fin = chunk_fwd_device(inp)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(fin))
+    ref_o, ref_s = _oracle_prefill(oracle_mod, inp)
+    assert rel_err(out, ref_o) < 1e-4 and rel_err(fin, ref_s) < 1e-4
