@@ -1,0 +1,379 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet forward hot path on one MI355X.
+
+One step = one gdn_chunk_fwd over the headline prefill workload (one sequence
+of T = 4096 tokens, H_q = 16 query/key heads, H_v = 32 value heads,
+d_k = d_v = 128, bf16 q/k/v, fp32 gates and states, nonzero initial state),
+all four kernels, inputs resident in HBM.  The batched decode step (256
+sequences x 1 token, 537 MB of fp32 state updated in place, fresh seeded tokens
+each step) is measured in the same run and reported under "decode".
+
+Prints ONE JSON line.  Timing: W untimed warm-up steps, then K timed steps
+between two device synchronisations, with HIP events recorded by the library
+on the launch stream before/after each kernel (per-kernel durations) and around
+the whole step.  "roofline" reports the slowest kernel of the step against the
+HBM roofline on its algorithmic bytes; "cpu_baseline" times the fp64 oracle on
+the host cores over a bounded prefix of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN prefill tokens/s (Hv=32,d=128,T=4096) + MFMA util; decode state GB/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+FP32_MFMA_PEAK_TFLOPS = 157.3
+STAGES = ["kkt_solve", "recompute_w_u", "chunk_state_h", "chunk_output_o"]
+KERNEL_SYMBOL = {"kkt_solve": "kkt_solve_kernel", "recompute_w_u": "recompute_w_u_kernel",
+                 "chunk_state_h": "chunk_state_h_kernel", "chunk_output_o": "chunk_output_o_kernel",
+                 "recurrent_step": "recurrent_step_kernel"}
+CHUNK = 64
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work of each kernel (bytes: every distinct input read once, every
+# output written once; flops: 2 x multiply-adds of the chunk form, triangles
+# exploited)
+# ---------------------------------------------------------------------------
+
+def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True):
+    C = CHUNK
+    chv, chq = n_chunks * H_v, n_chunks * H_q
+    q_b = k_b = T * H_q * d * es
+    v_b = o_b = T * H_v * d * es
+    gate_b = T * H_v * 4  # g or beta
+    gc_b = chv * C * 4
+    A_b = chv * C * C * es
+    W_b = U_b = X_b = chv * C * d * es
+    Kt_b = chq * d * C * es
+    H_b = chv * d * d * es
+    S_b = N * H_v * d * d * 4
+    tri = C * (C - 1) // 2   # strictly lower entries
+    tri1 = C * (C + 1) // 2  # lower incl. diagonal
+    per = {  # multiply-adds per (chunk, value head) at full chunks
+        "kkt_solve": tri * d + C ** 3 // 6,
+        "recompute_w_u": 2 * tri1 * d,
+        "chunk_state_h": 2 * C * d * d,
+        "chunk_output_o": C * d * d + 2 * tri1 * d,
+    }
+    bytes_ = {
+        "kkt_solve": k_b + 2 * gate_b + gc_b + A_b,
+        "recompute_w_u": A_b + k_b + v_b + gate_b + gc_b + W_b + U_b + Kt_b,
+        "chunk_state_h": W_b + U_b + Kt_b + gc_b + (S_b if has_s0 else 0) + H_b + X_b + S_b,
+        "chunk_output_o": q_b + k_b + gc_b + H_b + X_b + o_b,
+    }
+    flops = {k: 2 * v * chv for k, v in per.items()}
+    return bytes_, flops
+
+
+def decode_work(N, H_q, H_v, d, es):
+    state = N * H_v * d * d * 4
+    io = 2 * N * H_q * d * es + 2 * N * H_v * d * es + 2 * N * H_v * 4
+    return 2 * state + io, N * H_v * d * d * 8
+
+
+# ---------------------------------------------------------------------------
+# HIP events through the runtime torch loaded (same soname as libgdn's dependency)
+# ---------------------------------------------------------------------------
+
+class Hip:
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        P = ctypes.c_void_p
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(P)]
+        self.lib.hipEventRecord.argtypes = [P, P]
+        self.lib.hipEventSynchronize.argtypes = [P]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+        self.lib.hipEventDestroy.argtypes = [P]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e
+
+    def record(self, e, stream_ptr):
+        rc = self.lib.hipEventRecord(e, ctypes.c_void_p(stream_ptr))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, a, b):
+        self.lib.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+
+def _dev(arr, dtype, torch, device):
+    import numpy as np
+
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def _source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("gdn_chunk.hip", "gdn_decode.hip", "gdn_device.h", "gdn_params.h"):
+        with open(os.path.join(ROOT, "gated_deltanet_state_chunk_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on
+    the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("#") or "=" not in line:
+            continue
+        k, v = line.split("=", 1)
+        vals[k.strip()] = v.strip()
+    if vals.get("source_sha") != _source_sha():
+        return None
+    key = f"{kernel}.hbm_bytes_per_launch"
+    return float(vals[key]) if key in vals else None
+
+
+# ---------------------------------------------------------------------------
+# measurements
+# ---------------------------------------------------------------------------
+
+def bench_prefill(args, torch, gdn, hip, device):
+    import gdn_inputs
+
+    inp = gdn_inputs.make_workload(args.workload)
+    dt = inp.dtype
+    q, k, v = (_dev(x, dt, torch, device) for x in (inp.q, inp.k, inp.v))
+    g, beta = _dev(inp.g, "f32", torch, device), _dev(inp.beta, "f32", torch, device)
+    s0 = _dev(inp.initial_state, "f32", torch, device) if inp.initial_state is not None else None
+    lay = gdn.workspace_layout(inp.T, inp.cu_seqlens, inp.H_q, inp.H_v, inp.d_k, inp.d_v, dt)
+    ws = torch.empty(lay["total_bytes"], dtype=torch.uint8, device=device)
+    out = torch.empty((inp.T, inp.H_v, inp.d_v), dtype=q.dtype, device=device)
+    fin = torch.empty((inp.N, inp.H_v, inp.d_k, inp.d_v), dtype=torch.float32, device=device)
+    lib = gdn.load_library()
+    cu = (ctypes.c_int32 * (inp.N + 1))(*[int(x) for x in inp.cu_seqlens])
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    code = gdn.DTYPE_BF16 if dt == "bf16" else gdn.DTYPE_F32
+    K = args.steps
+    ev = [[hip.event() for _ in range(5)] for _ in range(max(K, 1))]
+
+    def step(events=None):
+        arr = None
+        if events is not None:
+            arr = (ctypes.c_void_p * 5)(*[e.value for e in events])
+        rc = lib.gdn_chunk_fwd_timed(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), cu,
+                                     inp.N, None if s0 is None else s0.data_ptr(), out.data_ptr(), fin.data_ptr(),
+                                     inp.T, inp.H_q, inp.H_v, inp.d_k, inp.d_v, inp.scale, code, ws.data_ptr(),
+                                     lay["total_bytes"], ctypes.c_void_p(sptr), arr)
+        if rc != 0:
+            raise gdn.GdnError(rc, "gdn_chunk_fwd_timed")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(K):
+        step(ev[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    stage_ms = {s: sum(hip.elapsed_ms(ev[i][j], ev[i][j + 1]) for i in range(K)) / K for j, s in enumerate(STAGES)}
+    ms_step = total_ms / K
+    es = 2 if dt == "bf16" else 4
+    bytes_, flops = prefill_work(inp.T, inp.N, lay["n_chunks"], inp.H_q, inp.H_v, inp.d_k, es,
+                                 has_s0=s0 is not None)
+    return dict(inp=inp, lay=lay, ms_step=ms_step, wall_s=wall, stage_ms=stage_ms, bytes=bytes_, flops=flops)
+
+
+def bench_decode(args, torch, gdn, hip, device):
+    import gdn_inputs
+
+    cfg = gdn_inputs.DECODE_WORKLOAD
+    N, H_q, H_v, d, dt = cfg["N"], cfg["H_q"], cfg["H_v"], cfg["d_k"], cfg["dtype"]
+    state = _dev(gdn_inputs.make_decode_state(cfg["seed"], N, H_v, d, d, cfg["state_std"]), "f32", torch, device)
+    toks = []
+    for s in range(cfg["steps"]):
+        t = gdn_inputs.make_decode_token(gdn_inputs.decode_step_seed(s), N, H_q, H_v, d, d, dt)
+        toks.append(tuple(_dev(x, dt, torch, device) for x in (t.q, t.k, t.v)) +
+                    (_dev(t.g, "f32", torch, device), _dev(t.beta, "f32", torch, device)))
+    out = torch.empty((N, H_v, d), dtype=toks[0][0].dtype, device=device)
+    scale = 1.0 / math.sqrt(d)
+    K = max(args.steps, cfg["steps"])
+    for i in range(args.warmup):
+        gdn.recurrent_step(*toks[i % len(toks)], state, scale=scale, out=out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(hip.event(), hip.event()) for _ in range(K)]
+    for i in range(K):
+        hip.record(evs[i][0], stream.cuda_stream)
+        gdn.recurrent_step(*toks[i % len(toks)], state, scale=scale, out=out)
+        hip.record(evs[i][1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = sum(hip.elapsed_ms(a, b) for a, b in evs) / K
+    nbytes, nflops = decode_work(N, H_q, H_v, d, 2 if dt == "bf16" else 4)
+    return dict(N=N, ms_step=ms, bytes=nbytes, flops=nflops, steps=K)
+
+
+def cpu_baseline(inp, target_s=12.0):
+    """fp64 oracle on the host cores over a prefix of the prefill workload (all heads)."""
+    import oracle
+
+    threads = oracle.max_threads()
+
+    def run(Tp):
+        t = time.perf_counter()
+        oracle.forward(inp.q32()[:Tp], inp.k32()[:Tp], inp.v32()[:Tp], inp.g[:Tp], inp.beta[:Tp], [0, Tp],
+                       inp.H_q, inp.H_v, inp.scale,
+                       initial_state=None if inp.initial_state is None else inp.initial_state[:1].astype("float64"))
+        return time.perf_counter() - t
+
+    probe_T = min(256, inp.T)
+    tp = run(probe_T)
+    Ts = int(min(inp.T, max(probe_T, probe_T * target_s / max(tp, 1e-6))))
+    Ts = max(CHUNK, Ts // CHUNK * CHUNK) if inp.T >= CHUNK else inp.T
+    ts = run(Ts)
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return dict(value=Ts / ts, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"fp64 token recurrence (oracle/gdn_recurrence.c, OpenMP over value heads) on the first "
+                       f"{Ts} of {inp.T} tokens, all {inp.H_v} value heads, {ts:.2f} s wall; "
+                       f"{avail} host cores visible")
+
+
+def copy_calibration(torch, device, gib=1.0):
+    """A plain device copy of known size, run under rocprofv3 --pmc to calibrate HBM byte counters."""
+    n = int(gib * (1 << 30))
+    src = torch.empty(n, dtype=torch.uint8, device=device).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_T4096",
+                    choices=["prefill_T4096", "varlen_8seq", "long_T65536", "tiny_f32_T100"])
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
+                    help="restrict the run (used for counter collection)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported (the GDN core shards over "
+              f"sequences and value heads with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_deltanet_state_chunk_amd as gdn
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    device = torch.device("cuda:0")
+    gdn.load_library()
+    hip = Hip()
+    if args.only == "copy":
+        copy_calibration(torch, device)
+        return
+
+    res = {}
+    pre = dec = None
+    if args.only in ("all", "prefill"):
+        pre = bench_prefill(args, torch, gdn, hip, device)
+        print(f"[bench] prefill {args.workload}: {pre['ms_step']:.4f} ms/step, stages "
+              + ", ".join(f"{s} {pre['stage_ms'][s] * 1e3:.1f} us" for s in STAGES), file=sys.stderr, flush=True)
+    if args.only in ("all", "decode"):
+        dec = bench_decode(args, torch, gdn, hip, device)
+        print(f"[bench] decode: {dec['ms_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    if pre is not None:
+        inp = pre["inp"]
+        ms = pre["ms_step"]
+        tokens = inp.T
+        dom = max(STAGES, key=lambda s: pre["stage_ms"][s])
+        dom_s = pre["stage_ms"][dom] * 1e-3
+        achieved = pre["bytes"][dom] / dom_s / 1e9
+        traffic = _traffic_from_profiles(dom, args.workload)
+        total_flops = sum(pre["flops"].values())
+        mfma_peak = BF16_MFMA_PEAK_TFLOPS if inp.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+        res.update({
+            "metric": METRIC,
+            "value": tokens / (ms * 1e-3),
+            "unit": "tokens/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": ms,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": inp.dtype,
+            "data": "synthetic",
+            "config": {"workload": args.workload, "seqlens": [int(x) for x in
+                                                             (inp.cu_seqlens[1:] - inp.cu_seqlens[:-1])],
+                       "T": inp.T, "H_q": inp.H_q, "H_v": inp.H_v, "d_k": inp.d_k, "d_v": inp.d_v,
+                       "chunk": CHUNK, "initial_state": inp.initial_state is not None},
+            "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": traffic},
+            "stages_us": {s: pre["stage_ms"][s] * 1e3 for s in STAGES},
+            "stage_hbm_frac": {s: pre["bytes"][s] / (pre["stage_ms"][s] * 1e-3) / 1e9 / HBM_PEAK_GBS
+                               for s in STAGES},
+            "mfma_util": {"whole_step": total_flops / (ms * 1e-3) / 1e12 / mfma_peak,
+                          **{s: pre["flops"][s] / (pre["stage_ms"][s] * 1e-3) / 1e12 / mfma_peak for s in STAGES}},
+            "algorithmic": {"gflop": total_flops / 1e9, "mbytes": {s: pre["bytes"][s] / 1e6 for s in STAGES}},
+        })
+    if dec is not None:
+        gbs = dec["bytes"] / (dec["ms_step"] * 1e-3) / 1e9
+        decode = {"workload": "decode_256x1", "us_per_step": dec["ms_step"] * 1e3, "state_gb_per_s": gbs,
+                  "tokens_per_s": dec["N"] / (dec["ms_step"] * 1e-3), "steps": dec["steps"],
+                  "roofline": {"bound": "hbm", "kernel": "recurrent_step", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                               "traffic": _traffic_from_profiles("recurrent_step", "decode_256x1")}}
+        if pre is None:
+            res.update({"metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": dec["steps"],
+                        "warmup": args.warmup, "ms_per_step": dec["ms_step"], "higher_is_better": True,
+                        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                        "config": {"workload": "decode_256x1"}, "roofline": decode["roofline"]})
+        res["decode"] = decode
+    if pre is not None and args.only == "all" and not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(pre["inp"])
+    res["source_sha"] = _source_sha()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

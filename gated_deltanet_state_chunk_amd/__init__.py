@@ -17,7 +17,7 @@ import os
 from typing import Optional, Sequence
 
 __all__ = ["chunk_fwd", "recurrent_step", "workspace_layout", "workspace_size", "lib_path", "load_library",
-           "GdnError", "CHUNK"]
+           "GdnError", "CHUNK", "DTYPE_F32", "DTYPE_BF16"]
 
 CHUNK = 64
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -56,6 +56,9 @@ def load_library():
         return _lib
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is not built; run `python -m gated_deltanet_state_chunk_amd.build`")
+    # torch first: its HIP runtime (soname libamdhip64.so.7) then satisfies
+    # libgdn.so's dependency, so streams and memory come from one runtime.
+    _torch()
     lib = ctypes.CDLL(_LIB_PATH)
     P, I32, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
     lib.gdn_version.restype = ctypes.c_char_p
@@ -70,6 +73,8 @@ def load_library():
     lib.gdn_chunk_fwd.argtypes = [P, P, P, P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P,
                                   ctypes.c_size_t, P]
     lib.gdn_chunk_fwd.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_timed.argtypes = lib.gdn_chunk_fwd.argtypes + [P]
+    lib.gdn_chunk_fwd_timed.restype = ctypes.c_int
     lib.gdn_recurrent_step.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P]
     lib.gdn_recurrent_step.restype = ctypes.c_int
     _lib = lib

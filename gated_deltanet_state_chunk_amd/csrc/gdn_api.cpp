@@ -48,14 +48,11 @@ int check_seqlens(int32_t T, int32_t num_seqs, const int32_t* cu, int64_t* n_chu
     return GDN_OK;
 }
 
-template <typename T, int D>
-hipError_t dispatch_chunk(const gdn::ChunkParams& p, hipStream_t s) {
-    return gdn::launch_chunk_pipeline<T, D>(p, s);
-}
-
-hipError_t run_chunk(const gdn::ChunkParams& p, gdn_dtype dt, int d, hipStream_t s) {
-    if (dt == GDN_DTYPE_BF16) return d == 128 ? dispatch_chunk<gdn::bf16, 128>(p, s) : dispatch_chunk<gdn::bf16, 64>(p, s);
-    return d == 128 ? dispatch_chunk<float, 128>(p, s) : dispatch_chunk<float, 64>(p, s);
+hipError_t run_chunk(const gdn::ChunkParams& p, gdn_dtype dt, int d, hipStream_t s, hipEvent_t const* ev) {
+    if (dt == GDN_DTYPE_BF16)
+        return d == 128 ? gdn::launch_chunk_pipeline<gdn::bf16, 128>(p, s, ev)
+                        : gdn::launch_chunk_pipeline<gdn::bf16, 64>(p, s, ev);
+    return d == 128 ? gdn::launch_chunk_pipeline<float, 128>(p, s, ev) : gdn::launch_chunk_pipeline<float, 64>(p, s, ev);
 }
 
 hipError_t run_decode(const gdn::DecodeParams& p, gdn_dtype dt, int d, hipStream_t s) {
@@ -127,6 +124,15 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                   const int32_t* cu_seqlens_host, int32_t num_seqs, const float* initial_state, void* out,
                   float* final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
                   gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    return gdn_chunk_fwd_timed(q, k, v, g, beta, cu_seqlens_host, num_seqs, initial_state, out, final_state, T, H_q,
+                               H_v, d_k, d_v, scale, dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+int gdn_chunk_fwd_timed(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                        const int32_t* cu_seqlens_host, int32_t num_seqs, const float* initial_state, void* out,
+                        float* final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v,
+                        float scale, gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream,
+                        void* const* stage_events) {
     gdn_workspace_layout L;
     int rc = gdn_chunk_fwd_workspace_layout(T, num_seqs, cu_seqlens_host, H_q, H_v, d_k, d_v, dtype, &L);
     if (rc != GDN_OK) return rc;
@@ -165,7 +171,8 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
         }
         tab.n_chunks = c - chunk_base;
         chunk_base = c;
-        const hipError_t e = run_chunk(p, dtype, d_k, s);
+        hipEvent_t const* ev = (s0 == 0 && stage_events) ? reinterpret_cast<hipEvent_t const*>(stage_events) : nullptr;
+        const hipError_t e = run_chunk(p, dtype, d_k, s, ev);
         if (e != hipSuccess) return hip_fail(e);
     }
     return GDN_OK;

@@ -549,25 +549,32 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
 static inline int pad8(int x) { return (x + 7) & ~7; }
 
 template <typename T, int D>
-hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream) {
+hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEvent_t const* events) {
     const int work_ch = p.tab.n_chunks * p.H_v;
     const int grid_ch = pad8(work_ch);
-    if (work_ch > 0) {
-        hipLaunchKernelGGL((kkt_solve_kernel<T, D>), dim3(grid_ch), dim3(256), 0, stream, p, grid_ch);
-        hipLaunchKernelGGL((recompute_w_u_kernel<T, D>), dim3(grid_ch), dim3(256), 0, stream, p, grid_ch);
-    }
     const int work_st = p.tab.num_seqs * p.H_v * (D / 16);
     const int grid_st = pad8(work_st);
+    auto mark = [&](int i) {
+        if (events) (void)hipEventRecord(events[i], stream);
+    };
+    mark(0);
+    if (work_ch > 0) hipLaunchKernelGGL((kkt_solve_kernel<T, D>), dim3(grid_ch), dim3(256), 0, stream, p, grid_ch);
+    mark(1);
+    if (work_ch > 0)
+        hipLaunchKernelGGL((recompute_w_u_kernel<T, D>), dim3(grid_ch), dim3(256), 0, stream, p, grid_ch);
+    mark(2);
     if (work_st > 0)
         hipLaunchKernelGGL((chunk_state_h_kernel<T, D>), dim3(grid_st), dim3(64), 0, stream, p, grid_st);
+    mark(3);
     if (work_ch > 0)
         hipLaunchKernelGGL((chunk_output_o_kernel<T, D>), dim3(grid_ch), dim3(256), 0, stream, p, grid_ch);
+    mark(4);
     return hipGetLastError();
 }
 
-template hipError_t launch_chunk_pipeline<bf16, 128>(const ChunkParams&, hipStream_t);
-template hipError_t launch_chunk_pipeline<bf16, 64>(const ChunkParams&, hipStream_t);
-template hipError_t launch_chunk_pipeline<float, 128>(const ChunkParams&, hipStream_t);
-template hipError_t launch_chunk_pipeline<float, 64>(const ChunkParams&, hipStream_t);
+template hipError_t launch_chunk_pipeline<bf16, 128>(const ChunkParams&, hipStream_t, hipEvent_t const*);
+template hipError_t launch_chunk_pipeline<bf16, 64>(const ChunkParams&, hipStream_t, hipEvent_t const*);
+template hipError_t launch_chunk_pipeline<float, 128>(const ChunkParams&, hipStream_t, hipEvent_t const*);
+template hipError_t launch_chunk_pipeline<float, 64>(const ChunkParams&, hipStream_t, hipEvent_t const*);
 
 }  // namespace gdn

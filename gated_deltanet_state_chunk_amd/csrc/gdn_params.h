@@ -59,9 +59,10 @@ struct DecodeParams {
 };
 
 // Kernel launchers (defined in the .hip translation units).  T is float or
-// __bf16, D is d_k = d_v.
+// __bf16, D is d_k = d_v.  `events` is null or five events recorded before the
+// first and after each of the four chunk kernels.
 template <typename T, int D>
-hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream);
+hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEvent_t const* events);
 
 template <typename T, int D>
 hipError_t launch_recurrent_step(const DecodeParams& p, hipStream_t stream);

@@ -132,6 +132,21 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
                   gdn_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gdn_chunk_fwd with stage timing, for profiling and benchmarks.  Same
+ * arguments, same results.  `stage_events` is NULL or an array of five
+ * hipEvent_t created by the caller; they are recorded on `stream` before the
+ * first kernel and after each of the four kernels (kkt_solve, recompute_w_u,
+ * chunk_state_h, chunk_output_o) of the first launch (a launch covers up to 64
+ * sequences; larger batches take several).  Event k+1 minus event k is then the
+ * device time of kernel k.
+ */
+int gdn_chunk_fwd_timed(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                        const int32_t *cu_seqlens_host, int32_t num_seqs, const float *initial_state, void *out,
+                        float *final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v,
+                        float scale, gdn_dtype dtype, void *workspace, size_t workspace_bytes, void *stream,
+                        void *const *stage_events);
+
+/*
  * One recurrent decode step ("Qwen3.5-397B-A17B" trace page, Decode-GDN node 7,
  * gdn_packed_recurrent_qk_norm_gating_state_update — its decay, delta update and
  * read; the Q/K normalisation and gate transform of that node are not part of
