@@ -41,7 +41,7 @@ class GdnError(RuntimeError):
 
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [("n_chunks", ctypes.c_int64), ("off_gc", ctypes.c_size_t), ("off_A", ctypes.c_size_t),
-                ("off_W", ctypes.c_size_t), ("off_Ut", ctypes.c_size_t), ("off_Kt", ctypes.c_size_t),
+                ("off_W", ctypes.c_size_t), ("off_U", ctypes.c_size_t), ("off_Kd", ctypes.c_size_t),
                 ("off_Ht", ctypes.c_size_t), ("off_Xt", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t)]
 
 

@@ -5,7 +5,7 @@
 
 #include <string>
 
-#include "../../include/gdn.h"
+#include "gdn.h"
 #include "gdn_params.h"
 
 namespace {
@@ -103,8 +103,8 @@ int gdn_chunk_fwd_workspace_layout(int32_t T, int32_t num_seqs, const int32_t* c
     L.off_gc = off; off = align_up(off + chv * C * sizeof(float));
     L.off_A = off;  off = align_up(off + chv * C * C * es);
     L.off_W = off;  off = align_up(off + chv * C * (size_t)d_k * es);
-    L.off_Ut = off; off = align_up(off + chv * (size_t)d_v * C * es);
-    L.off_Kt = off; off = align_up(off + (size_t)nc * H_q * (size_t)d_k * C * es);
+    L.off_U = off; off = align_up(off + chv * (size_t)d_v * C * es);
+    L.off_Kd = off; off = align_up(off + chv * (size_t)d_k * C * es);
     L.off_Ht = off; off = align_up(off + chv * (size_t)d_v * (size_t)d_k * es);
     L.off_Xt = off; off = align_up(off + chv * (size_t)d_v * C * es);
     L.total_bytes = off;
@@ -150,7 +150,7 @@ int gdn_chunk_fwd_timed(const void* q, const void* k, const void* v, const float
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
     p.s0 = initial_state; p.out = out; p.sfinal = final_state;
     p.gc = reinterpret_cast<float*>(ws + L.off_gc);
-    p.A = ws + L.off_A; p.W = ws + L.off_W; p.Ut = ws + L.off_Ut; p.Kt = ws + L.off_Kt;
+    p.A = ws + L.off_A; p.W = ws + L.off_W; p.Ut = ws + L.off_U; p.Kt = ws + L.off_Kd;
     p.Ht = ws + L.off_Ht; p.Xt = ws + L.off_Xt;
     p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
 

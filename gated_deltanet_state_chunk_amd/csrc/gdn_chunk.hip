@@ -72,6 +72,25 @@ __device__ __forceinline__ void tile_to_lds(float (*M)[LPAD], int r0, int c0, co
 
 }  // namespace
 
+// Fragment-order offsets (in elements) of the per-(chunk, value head) blocks
+// written by recompute_w_u and read by chunk_state_h.  A fragment holds 8
+// values per lane; lane = 16 a + r with r the row (A operand) and a the lane
+// group; "perm32" slot 4 h + b stands for contraction index 16 h + 4 a + b.
+//   W  (rows pos, contraction d_k): fragment (pos / 16, K-step), lane, slot
+template <int D>
+__host__ __device__ __forceinline__ int frag_w_offset(int pos_tile, int ks, int lane) {
+    return ((pos_tile * (D / 32) + ks) * 64 + lane) * 8;
+}
+//   Kd^T (rows d_k, contraction pos): element (dk, pos) with pos a multiple of 4
+__host__ __device__ __forceinline__ int frag_k_offset(int dk, int pos4) {
+    const int m = dk >> 4, r = dk & 15, ks = pos4 >> 5, h = (pos4 >> 4) & 1, a = (pos4 >> 2) & 3;
+    return ((m * 2 + ks) * 64 + 16 * a + r) * 8 + 4 * h;
+}
+//   U (accumulator order): column tile of d_v, row tile of pos, lane -> 4 rows
+__host__ __device__ __forceinline__ int frag_u_offset(int col_tile, int pos_tile, int lane) {
+    return ((col_tile * 4 + pos_tile) * 64 + lane) * 4;
+}
+
 // ---------------------------------------------------------------------------
 // 1. kkt_solve: one workgroup (4 waves) per (chunk, value head).
 // ---------------------------------------------------------------------------
@@ -204,9 +223,11 @@ __global__ __launch_bounds__(256) void kkt_solve_kernel(const ChunkParams p, int
 
 // ---------------------------------------------------------------------------
 // 2. recompute_w_u: one workgroup per (chunk, value head).
-//    W^T = (B Gamma K)^T A^T  -> W stored [pos][perm32(d_k)]
-//    U   = A (B V)            -> Ut stored [d_v][pos]
-//    Kt  = K^T                -> [d_k][perm32(pos)], written once per key head
+//    W^T = (B Gamma K)^T A^T,  U = A (B V),  Kd^T = (diag(gamma_l / gamma_r) K)^T
+//    (the keys of the state update, already carrying the decay to the end of
+//    the chunk).  All three are written in the MFMA fragment order in which
+//    chunk_state_h consumes them (frag_w / frag_k / frag_u below), so that
+//    stage can copy each chunk's block into LDS with contiguous 1 KiB loads.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void recompute_w_u_kernel(const ChunkParams p, int padded) {
@@ -222,14 +243,16 @@ __global__ __launch_bounds__(256) void recompute_w_u_kernel(const ChunkParams p,
 
     __shared__ T s_K[CHUNK][SP];
     __shared__ T s_V[CHUNK][SP];
-    __shared__ float s_sk[CHUNK], s_sv[CHUNK];
+    __shared__ float s_sk[CHUNK], s_sv[CHUNK], s_kd[CHUNK];
 
     if (tid < CHUNK) {
         const size_t gi = (size_t)(cp.t0 + tid) * p.H_v + h;
+        const float* gcb = p.gc + ((size_t)cp.ci * p.H_v + h) * CHUNK;
         const float b = tid < ell ? p.beta[gi] : 0.f;
-        const float gcv = p.gc[((size_t)cp.ci * p.H_v + h) * CHUNK + tid];
+        const float gcv = gcb[tid];
         s_sk[tid] = b * __expf(gcv);
         s_sv[tid] = b;
+        s_kd[tid] = tid < ell ? __expf(gcb[ell - 1] - gcv) : 0.f;  // gamma_l / gamma_r
     }
     // Stage the chunk's K and V rows (zeros past the valid length).
     {
@@ -266,6 +289,7 @@ __global__ __launch_bounds__(256) void recompute_w_u_kernel(const ChunkParams p,
         for (int ks = 0; ks < 2; ++ks) load8(Af[mt][ks], Ab + (size_t)(16 * mt + r16) * CHUNK + 32 * ks + 8 * grp);
 
     constexpr int TPW = D / 64;  // 16-wide tiles of d_k (or d_v) per wave
+    constexpr int KS = D / 32;
     // W^T tiles: rows d_k (this wave's tiles), columns pos.  A is lower triangular,
     // so column tile nt only needs contraction steps ks with 32 ks <= 16 nt + 15.
     T* Wb = reinterpret_cast<T*>(p.W) + ((size_t)cp.ci * p.H_v + h) * CHUNK * D;
@@ -286,13 +310,14 @@ __global__ __launch_bounds__(256) void recompute_w_u_kernel(const ChunkParams p,
             f32x4 c = zero4();
             c = mma(kf[0], Af[nt][0], c);
             if (nt >= 2) c = mma(kf[1], Af[nt][1], c);
-            // lane: column pos = 16 nt + r16, rows d_k = 16 mt + 4 grp + i
-            const int pos = 16 * nt + r16;
-            store4(Wb + (size_t)pos * D + perm32(16 * mt + 4 * grp), c[0], c[1], c[2], c[3]);
+            // lane: column pos = 16 nt + r16, rows d_k = 16 mt + 4 grp + i: in fragment
+            // order this is fragment (pos tile nt, K-step mt / 2), same lane, slots 4 (mt % 2) + i
+            store4(Wb + frag_w_offset<D>(nt, mt >> 1, lane) + 4 * (mt & 1), c[0], c[1], c[2], c[3]);
         }
     }
     // U tiles: rows pos, columns d_v (this wave's tiles).
     T* Ub = reinterpret_cast<T*>(p.Ut) + ((size_t)cp.ci * p.H_v + h) * D * CHUNK;
+    (void)KS;
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
         const int nt = w * TPW + tt;
@@ -310,128 +335,215 @@ __global__ __launch_bounds__(256) void recompute_w_u_kernel(const ChunkParams p,
             f32x4 c = zero4();
             c = mma(Af[mt][0], vf[0], c);
             if (mt >= 2) c = mma(Af[mt][1], vf[1], c);
-            // lane: column d_v, rows pos = 16 mt + 4 grp + i
-            store4(Ub + (size_t)dv * CHUNK + 16 * mt + 4 * grp, c[0], c[1], c[2], c[3]);
+            // lane: column d_v = 16 nt + r16, rows pos = 16 mt + 4 grp + i (accumulator order)
+            store4(Ub + frag_u_offset(nt, mt, lane), c[0], c[1], c[2], c[3]);
         }
     }
-    // K^T of the chunk, once per key head.
-    if (h % p.G == 0) {
-        T* Kb = reinterpret_cast<T*>(p.Kt) + ((size_t)cp.ci * p.H_q + hq) * D * CHUNK;
+    // Decayed keys of the state update, transposed.
+    {
+        T* Kb = reinterpret_cast<T*>(p.Kt) + ((size_t)cp.ci * p.H_v + h) * D * CHUNK;
         for (int e = tid; e < D * (CHUNK / 4); e += 256) {
             const int dk = e / (CHUNK / 4), r4 = (e % (CHUNK / 4)) * 4;
-            store4(Kb + (size_t)dk * CHUNK + perm32(r4), to_f32<T>(s_K[r4][dk]), to_f32<T>(s_K[r4 + 1][dk]),
-                   to_f32<T>(s_K[r4 + 2][dk]), to_f32<T>(s_K[r4 + 3][dk]));
+            store4(Kb + frag_k_offset(dk, r4), s_kd[r4] * to_f32<T>(s_K[r4][dk]),
+                   s_kd[r4 + 1] * to_f32<T>(s_K[r4 + 1][dk]), s_kd[r4 + 2] * to_f32<T>(s_K[r4 + 2][dk]),
+                   s_kd[r4 + 3] * to_f32<T>(s_K[r4 + 3][dk]));
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// 3. chunk_state_h: one wave per (sequence, value head, 16-column tile of d_v),
-//    serial over the sequence's chunks.  The fp32 state slice S[:, tile] lives
-//    in MFMA accumulators for the whole sequence; its bf16/fp32 copy feeds the
-//    next product directly through the perm32 fragment convention, so the
-//    serial chain has no LDS traffic and no barrier.
+// 3. chunk_state_h: one workgroup per (sequence, value head, 16-column tile of
+//    d_v), serial over the sequence's chunks; four compute waves (one per SIMD)
+//    and one producer wave.
+//
+//    Compute waves.  The fp32 state slice S[:, tile] (d_k x 16) stays in MFMA
+//    accumulators, split by rows over the waves.  Per chunk:
+//      X = U - W S          wave w: positions 16w..16w+15, contraction over d_k
+//      S = gamma_l S + Kd^T X   wave w: its rows of S, contraction over positions
+//    The two products exchange bf16 copies of -S and X through LDS in MFMA
+//    operand order (one 16-byte access per lane and fragment), two barriers a
+//    chunk, and read their operands from the LDS stage of that chunk.
+//
+//    Producer wave.  Streams each chunk's W, Kd, U and gate blocks (stored by
+//    recompute_w_u in exactly the LDS stage order) into a ring of stages with
+//    direct global->LDS loads, NST - 1 chunks ahead, so the compute waves never
+//    issue a global load: the per-chunk operands (about 34 KiB) would otherwise
+//    stall their instruction stream on the CU's vector-memory path.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(64) void chunk_state_h_kernel(const ChunkParams p, int padded) {
-    constexpr int NT = D / 16;  // d_k row tiles of S (= d_v column tiles per head)
-    constexpr int KS = D / 32;  // contraction steps over d_k
+struct StateStage {
+    static constexpr int W_BYTES = CHUNK * D * (int)sizeof(T);
+    static constexpr int K_BYTES = D * CHUNK * (int)sizeof(T);
+    static constexpr int U_BYTES = 4 * 64 * 4 * (int)sizeof(T);  // one 16-column tile
+    static constexpr int G_BYTES = CHUNK * 4;
+    static constexpr int BYTES = W_BYTES + K_BYTES + U_BYTES + G_BYTES;
+    static constexpr int NDMA = (W_BYTES + K_BYTES + U_BYTES) / 1024 + 1;  // loads per chunk
+    static constexpr int EXCH = (D / 32 + 2) * 64 * 8 * (int)sizeof(T);    // -S and X exchange
+    static constexpr int NST = (3 * BYTES + EXCH <= 150 * 1024 && NDMA <= 63) ? 3 : 2;
+};
+
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// Wave-wide copy of 1 KiB (64 lanes x 16 B) from global `src` to LDS `dst`.
+__device__ __forceinline__ void dma_1k(const char* src, char* dst, int lane) {
+    __builtin_amdgcn_global_load_lds((gptr_t)(src + 16 * lane), (lptr_t)dst, 16, 0, 0);
+}
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void state_issue(char* stage, const ChunkParams& p, size_t ch, int tile, int lane) {
+    using SS = StateStage<T, D>;
+    constexpr int NT = D / 16;
+    const char* wg = reinterpret_cast<const char*>(p.W) + ch * SS::W_BYTES;
+    const char* kg = reinterpret_cast<const char*>(p.Kt) + ch * SS::K_BYTES;
+    const char* ug = reinterpret_cast<const char*>(p.Ut) + (ch * NT + tile) * SS::U_BYTES;
+#pragma unroll
+    for (int j = 0; j < SS::W_BYTES / 1024; ++j) dma_1k(wg + 1024 * j, stage + 1024 * j, lane);
+#pragma unroll
+    for (int j = 0; j < SS::K_BYTES / 1024; ++j) dma_1k(kg + 1024 * j, stage + SS::W_BYTES + 1024 * j, lane);
+#pragma unroll
+    for (int j = 0; j < SS::U_BYTES / 1024; ++j)
+        dma_1k(ug + 1024 * j, stage + SS::W_BYTES + SS::K_BYTES + 1024 * j, lane);
+    __builtin_amdgcn_global_load_lds((gptr_t)(p.gc + ch * CHUNK + lane),
+                                     (lptr_t)(stage + SS::W_BYTES + SS::K_BYTES + SS::U_BYTES), 4, 0, 0);
+}
+
+// Write a D tile's four values (rows 4 grp + i of one 16-row tile) into the
+// perm32 fragment they belong to: even tile -> slots 0..3, odd -> slots 4..7.
+template <typename T>
+__device__ __forceinline__ void lds_put4(Frag<T>& f, int half, const f32x4& v, float s) {
+    if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(&f) + 4 * half) = cvt4_bf16(v, s);
+    } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(&f) + 4 * half) =
+            make_float4(s * v[0], s * v[1], s * v[2], s * v[3]);
+    }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(320) void chunk_state_h_kernel(const ChunkParams p, int padded) {
+    using SS = StateStage<T, D>;
+    constexpr int NT = D / 16;   // column tiles of d_v per head
+    constexpr int KS = D / 32;   // contraction steps over d_k
+    constexpr int TPW = D / 64;  // S row tiles per compute wave
+    constexpr int NST = SS::NST;
     const int wid = xcd_remap(blockIdx.x, padded);
     if (wid >= p.tab.num_seqs * p.H_v * NT) return;
     const int tile = wid % NT;
     const int u = wid / NT;
     const int h = u % p.H_v, n = u / p.H_v;
-    const int hq = h / p.G;
-    const int lane = threadIdx.x, r16 = lane & 15, grp = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r16 = lane & 15, grp = lane >> 4;
     const int col = 16 * tile + r16;
     const size_t state_off = ((size_t)(p.tab.seq_base + n) * p.H_v + h) * D * D;
+    const int L_n = p.tab.cu[n + 1] - p.tab.cu[n];
+    const int nch = p.tab.choff[n + 1] - p.tab.choff[n];
+    const int c0 = p.tab.choff[n];
 
-    f32x4 S[NT];
+    __shared__ __attribute__((aligned(16))) char smem[NST * SS::BYTES + SS::EXCH];
+    Frag<T>(*LS)[64] = reinterpret_cast<Frag<T>(*)[64]>(smem + NST * SS::BYTES);           // [KS][64]: -S
+    Frag<T>(*LX)[64] = reinterpret_cast<Frag<T>(*)[64]>(smem + NST * SS::BYTES + KS * 64 * sizeof(Frag<T>));  // [2][64]: X
+
+    if (w == 4) {
+        // ---------------- producer ----------------
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[mt][i] = p.s0 ? p.s0[state_off + (size_t)(16 * mt + 4 * grp + i) * D + col] : 0.f;
+        for (int b = 0; b < NST - 1; ++b)
+            if (b < nch) state_issue<T, D>(smem + b * SS::BYTES, p, (size_t)(c0 + b) * p.H_v + h, tile, lane);
+        wait_vmcnt<0>();
+        // The producer's barriers are plain s_barrier: a workgroup release fence
+        // would wait for the direct-to-LDS loads just issued, and the whole point
+        // is that they stay in flight.  Visibility is ensured explicitly: chunk c
+        // is complete (vmcnt) before this wave arrives at B1(c).  The asm's memory
+        // clobber keeps the compiler from moving loads across the barrier.
+        for (int c = 0; c < nch; ++c) {
+            asm volatile("s_barrier" ::: "memory");  // B1(c): stage c % NST is complete and visible
+            const int cn = c + NST - 1;
+            if (cn < nch) state_issue<T, D>(smem + (cn % NST) * SS::BYTES, p, (size_t)(c0 + cn) * p.H_v + h, tile, lane);
+            asm volatile("s_barrier" ::: "memory");  // B2(c)
+            // chunk c + 1 must be in LDS before B1(c + 1); the chunk issued above may stay in flight
+            if (NST == 3 && cn < nch)
+                wait_vmcnt<(NST == 3 ? SS::NDMA : 0)>();
+            else
+                wait_vmcnt<0>();
+        }
+        return;
     }
 
-    const int L = p.tab.cu[n + 1] - p.tab.cu[n];
-    const int nch = p.tab.choff[n + 1] - p.tab.choff[n];
+    // ---------------- compute waves ----------------
+    f32x4 S[TPW];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+        const int m = w * TPW + tt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            S[tt][i] = p.s0 ? p.s0[state_off + (size_t)(16 * m + 4 * grp + i) * D + col] : 0.f;
+        lds_put4(LS[m >> 1][lane], m & 1, S[tt], -1.f);
+    }
     for (int c = 0; c < nch; ++c) {
-        const int ci = p.tab.choff[n] + c;
-        const int ell = min(CHUNK, L - c * CHUNK);
+        const int ci = c0 + c;
+        const int ell = min(CHUNK, L_n - c * CHUNK);
         const size_t ch = (size_t)ci * p.H_v + h;
+        const char* st = smem + (c % NST) * SS::BYTES;
+        const Frag<T>* Wst = reinterpret_cast<const Frag<T>*>(st);
+        const Frag<T>* Kst = reinterpret_cast<const Frag<T>*>(st + SS::W_BYTES);
+        const Raw4<T>* Ust = reinterpret_cast<const Raw4<T>*>(st + SS::W_BYTES + SS::K_BYTES);
+        const float* Gst = reinterpret_cast<const float*>(st + SS::W_BYTES + SS::K_BYTES + SS::U_BYTES);
+        __syncthreads();  // B1(c): -S in LS, stage c ready
+        Frag<T> wf[KS], sb[KS], kf[TPW][2];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            wf[ks] = Wst[(w * KS + ks) * 64 + lane];
+            sb[ks] = LS[ks][lane];
+        }
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) kf[tt][ks] = Kst[((w * TPW + tt) * 2 + ks) * 64 + lane];
+        const Raw4<T> uf = Ust[w * 64 + lane];
+        const float eg = __expf(Gst[ell - 1]);
 
-        // Chunk-start state h_c, stored transposed [d_v][d_k].
+        // h_c = S (this wave's rows), stored transposed [d_v][d_k]
         T* Hb = reinterpret_cast<T*>(p.Ht) + (ch * D + col) * D;
 #pragma unroll
-        for (int mt = 0; mt < NT; ++mt) store4(Hb + 16 * mt + 4 * grp, S[mt][0], S[mt][1], S[mt][2], S[mt][3]);
-
-        // Operands of this chunk.
-        const T* Wb = reinterpret_cast<const T*>(p.W) + ch * CHUNK * D;
-        const T* Kb = reinterpret_cast<const T*>(p.Kt) + ((size_t)ci * p.H_q + hq) * D * CHUNK;
-        const T* Ub = reinterpret_cast<const T*>(p.Ut) + (ch * D + col) * CHUNK;
-        const float* gcb = p.gc + ch * CHUNK;
-        Frag<T> Wf[4][KS];
+        for (int tt = 0; tt < TPW; ++tt)
+            store4(Hb + 16 * (w * TPW + tt) + 4 * grp, S[tt][0], S[tt][1], S[tt][2], S[tt][3]);
+        // X = U - W S for positions 16 w .. 16 w + 15
+        f32x4 X = raw4_to_f32(uf);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) load8(Wf[mt][ks], Wb + (size_t)(16 * mt + r16) * D + 32 * ks + 8 * grp);
-        f32x4 X[4];
-        float gcv[4][4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            float u0, u1, u2, u3;
-            load4(Ub + 16 * mt + 4 * grp, u0, u1, u2, u3);
-            X[mt] = f32x4{u0, u1, u2, u3};
-            const float4 gg = *reinterpret_cast<const float4*>(gcb + 16 * mt + 4 * grp);
-            gcv[mt][0] = gg.x; gcv[mt][1] = gg.y; gcv[mt][2] = gg.z; gcv[mt][3] = gg.w;
-        }
-        const float gl = gcb[ell - 1];
-
-        // X = U - W S.
-        Frag<T> Sb[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) Sb[ks] = pack_perm32<T>(S[2 * ks], S[2 * ks + 1], -1.f);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) X[mt] = mma(Wf[mt][ks], Sb[ks], X[mt]);
-
-        // Store (U - W S)^T with perm32 positions; zero past the valid length.
+        for (int ks = 0; ks < KS; ++ks) X = mma(wf[ks], sb[ks], X);
         T* Xb = reinterpret_cast<T*>(p.Xt) + (ch * D + col) * CHUNK;
+        store4(Xb + perm32(16 * w + 4 * grp), X[0], X[1], X[2], X[3]);
+        lds_put4(LX[w >> 1][lane], w & 1, X, 1.f);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int tt = 0; tt < TPW; ++tt) S[tt] *= eg;
+        __syncthreads();  // B2(c): all of X in LX
+        const Frag<T> xb0 = LX[0][lane], xb1 = LX[1][lane];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (16 * mt + 4 * grp + i >= ell) X[mt][i] = 0.f;
-            store4(Xb + perm32(16 * mt + 4 * grp), X[mt][0], X[mt][1], X[mt][2], X[mt][3]);
+        for (int tt = 0; tt < TPW; ++tt) {
+            S[tt] = mma(kf[tt][0], xb0, S[tt]);
+            S[tt] = mma(kf[tt][1], xb1, S[tt]);
         }
-
-        // S <- gamma_l S + K^T diag(gamma_l / gamma_r) (U - W S).
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) X[mt][i] *= __expf(gl - gcv[mt][i]);
-        Frag<T> Xf[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) Xf[ks] = pack_perm32<T>(X[2 * ks], X[2 * ks + 1], 1.f);
-        const float eg = __expf(gl);
-#pragma unroll
-        for (int mt = 0; mt < NT; ++mt) {
-            S[mt] *= eg;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                Frag<T> kf;
-                load8(kf, Kb + (size_t)(16 * mt + r16) * CHUNK + 32 * ks + 8 * grp);
-                S[mt] = mma(kf, Xf[ks], S[mt]);
-            }
+        for (int tt = 0; tt < TPW; ++tt) {
+            const int m = w * TPW + tt;
+            lds_put4(LS[m >> 1][lane], m & 1, S[tt], -1.f);
         }
     }
     if (p.sfinal) {
 #pragma unroll
-        for (int mt = 0; mt < NT; ++mt)
+        for (int tt = 0; tt < TPW; ++tt) {
+            const int m = w * TPW + tt;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p.sfinal[state_off + (size_t)(16 * mt + 4 * grp + i) * D + col] = S[mt][i];
+            for (int i = 0; i < 4; ++i) p.sfinal[state_off + (size_t)(16 * m + 4 * grp + i) * D + col] = S[tt][i];
+        }
     }
 }
 
@@ -564,7 +676,7 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
         hipLaunchKernelGGL((recompute_w_u_kernel<T, D>), dim3(grid_ch), dim3(256), 0, stream, p, grid_ch);
     mark(2);
     if (work_st > 0)
-        hipLaunchKernelGGL((chunk_state_h_kernel<T, D>), dim3(grid_st), dim3(64), 0, stream, p, grid_st);
+        hipLaunchKernelGGL((chunk_state_h_kernel<T, D>), dim3(grid_st), dim3(320), 0, stream, p, grid_st);
     mark(3);
     if (work_ch > 0)
         hipLaunchKernelGGL((chunk_output_o_kernel<T, D>), dim3(grid_ch), dim3(256), 0, stream, p, grid_ch);

@@ -113,6 +113,11 @@ __device__ __forceinline__ Frag<T> pack_perm32(const f32x4& lo, const f32x4& hi,
     return f;
 }
 
+// Four fp32 values times s, rounded to T (vector conversion: packed cvt for bf16).
+__device__ __forceinline__ bf16x4 cvt4_bf16(const f32x4& v, float s) {
+    return __builtin_convertvector(v * s, bf16x4);
+}
+
 // ---- stores of 4 consecutive values --------------------------------------
 __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
     bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
@@ -129,6 +134,24 @@ __device__ __forceinline__ void load4(const float* p, float& a, float& b, float&
     const float4 v = *reinterpret_cast<const float4*>(p);
     a = v.x; b = v.y; c = v.z; d = v.w;
 }
+
+// Four raw elements (kept unconverted so that a prefetch does not force a wait).
+template <typename T>
+struct Raw4;
+template <>
+struct Raw4<bf16> {
+    bf16x4 v;
+};
+template <>
+struct Raw4<float> {
+    float4 v;
+};
+__device__ __forceinline__ void load_raw4(Raw4<bf16>& r, const bf16* p) { r.v = *reinterpret_cast<const bf16x4*>(p); }
+__device__ __forceinline__ void load_raw4(Raw4<float>& r, const float* p) { r.v = *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ f32x4 raw4_to_f32(const Raw4<bf16>& r) {
+    return f32x4{(float)r.v[0], (float)r.v[1], (float)r.v[2], (float)r.v[3]};
+}
+__device__ __forceinline__ f32x4 raw4_to_f32(const Raw4<float>& r) { return f32x4{r.v.x, r.v.y, r.v.z, r.v.w}; }
 
 // perm32 storage offset of logical index i.
 __host__ __device__ __forceinline__ int perm32(int i) {

@@ -45,6 +45,37 @@ def unperm32(stored: np.ndarray) -> np.ndarray:
     return stored[..., perm32_index(stored.shape[-1])]
 
 
+def _split32(i):
+    s, r = i // 32, i % 32
+    return s, r // 16, (r % 16) // 4, r % 4
+
+
+def frag_w_to_logical(flat, d_k):
+    """W [..., 64*d_k] in fragment order -> [..., 64, d_k]."""
+    pos = np.arange(64)[:, None]
+    k = np.arange(d_k)[None, :]
+    s, h, a, b = _split32(k)
+    off = ((pos // 16 * (d_k // 32) + s) * 64 + 16 * a + pos % 16) * 8 + 4 * h + b
+    return flat[..., off]
+
+
+def frag_kd_to_logical(flat, d_k):
+    """Kd [..., d_k*64] in fragment order -> [..., d_k, 64]."""
+    k = np.arange(d_k)[:, None]
+    pos = np.arange(64)[None, :]
+    s, h, a, b = _split32(pos)
+    off = ((k // 16 * 2 + s) * 64 + 16 * a + k % 16) * 8 + 4 * h + b
+    return flat[..., off]
+
+
+def frag_u_to_logical(flat, d_v):
+    """U [..., 64*d_v] in accumulator order -> [..., 64, d_v]."""
+    pos = np.arange(64)[:, None]
+    j = np.arange(d_v)[None, :]
+    off = ((j // 16 * 4 + pos // 16) * 64 + 16 * ((pos % 16) // 4) + j % 16) * 4 + pos % 4
+    return flat[..., off]
+
+
 def chunk_fwd_device(inp, device="cuda", initial_state="from_inputs", return_ws=False):
     """Run gdn_chunk_fwd on seeded inputs; returns (out, final, workspace-or-None) as host arrays / tensor."""
     import torch

@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 
 import gdn_inputs
-from tests.gpu_helpers import chunk_fwd_device, f32_dev, rel_err, to_dev, to_host, unperm32
+from tests.gpu_helpers import (chunk_fwd_device, f32_dev, frag_kd_to_logical, frag_u_to_logical, frag_w_to_logical,
+                               rel_err, to_dev, to_host, unperm32)
 
 pytestmark = pytest.mark.gpu
 
@@ -154,7 +155,6 @@ def test_chunk_intermediates_match_chunk_form(torch_cuda, dtype, d, tol):
     lay = gdn.workspace_layout(inp.T, inp.cu_seqlens, H_q, H_v, d, d, dtype)
     nc = lay["n_chunks"]
     assert nc == 2 + 1 + 1
-    wsb = ws.cpu().numpy()
 
     def region(off, shape, is_f32=False):
         import torch
@@ -164,12 +164,11 @@ def test_chunk_intermediates_match_chunk_form(torch_cuda, dtype, d, tol):
         t = raw.view(torch.float32) if (is_f32 or dtype == "f32") else raw.view(torch.bfloat16)
         return t.float().cpu().numpy().astype(np.float64).reshape(shape)
 
-    del wsb
     gc = region(lay["off_gc"], (nc, H_v, 64), is_f32=True)
     A = region(lay["off_A"], (nc, H_v, 64, 64))
-    W = unperm32(region(lay["off_W"], (nc, H_v, 64, d)))
-    U = np.swapaxes(region(lay["off_Ut"], (nc, H_v, d, 64)), -1, -2)
-    Kt = unperm32(region(lay["off_Kt"], (nc, H_q, d, 64)))
+    W = frag_w_to_logical(region(lay["off_W"], (nc, H_v, 64 * d)), d)
+    U = frag_u_to_logical(region(lay["off_U"], (nc, H_v, 64 * d)), d)
+    Kt = frag_kd_to_logical(region(lay["off_Kd"], (nc, H_v, d * 64)), d)
     Hs = np.swapaxes(region(lay["off_Ht"], (nc, H_v, d, d)), -1, -2)
     X = np.swapaxes(unperm32(region(lay["off_Xt"], (nc, H_v, d, 64))), -1, -2)
 
@@ -192,8 +191,11 @@ def test_chunk_intermediates_match_chunk_form(torch_cuda, dtype, d, tol):
                 assert rel_err(Hs[ci, h], r["h"]) < tol
                 assert rel_err(X[ci, h, :ell], r["X"]) < 3 * tol
                 assert np.all(W[ci, h, ell:] == 0) and np.all(X[ci, h, ell:] == 0)
-            for hq in range(H_q):
-                assert np.array_equal(Kt[ci, hq, :, :ell], k32[t0:t0 + ell, hq, :].T)
+                # keys of the state update carry the decay to the chunk end: gamma_l / gamma_r
+                hq = h // (H_v // H_q)
+                kd = np.exp(r["gc"][-1] - r["gc"])[:, None] * k32[t0:t0 + ell, hq, :].astype(np.float64)
+                assert rel_err(Kt[ci, h, :, :ell], kd.T) < tol
+                assert np.all(Kt[ci, h, :, ell:] == 0)
             ci += 1
 
 
