@@ -4,7 +4,7 @@
 One step = one gdn_chunk_fwd over the headline prefill workload (one sequence
 of T = 4096 tokens, H_q = 16 query/key heads, H_v = 32 value heads,
 d_k = d_v = 128, bf16 q/k/v, fp32 gates and states, nonzero initial state),
-all four kernels, inputs resident in HBM.  The batched decode step (256
+all three kernels, inputs resident in HBM.  The batched decode step (256
 sequences x 1 token, 537 MB of fp32 state updated in place, fresh seeded tokens
 each step) is measured in the same run and reported under "decode".
 
@@ -36,10 +36,7 @@ METRIC = "GDN prefill tokens/s (Hv=32,d=128,T=4096) + MFMA util; decode state GB
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 FP32_MFMA_PEAK_TFLOPS = 157.3
-STAGES = ["kkt_solve", "recompute_w_u", "chunk_state_h", "chunk_output_o"]
-KERNEL_SYMBOL = {"kkt_solve": "kkt_solve_kernel", "recompute_w_u": "recompute_w_u_kernel",
-                 "chunk_state_h": "chunk_state_h_kernel", "chunk_output_o": "chunk_output_o_kernel",
-                 "recurrent_step": "recurrent_step_kernel"}
+STAGES = ["chunk_prep", "chunk_state_h", "chunk_output_o"]
 CHUNK = 64
 
 
@@ -50,6 +47,12 @@ CHUNK = 64
 # ---------------------------------------------------------------------------
 
 def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True):
+    """Algorithmic bytes and flops of each kernel of one gdn_chunk_fwd.
+
+    Bytes: every distinct input read once, every output and intermediate written
+    once and read once per consuming kernel (K is read once per key head).
+    Flops: 2 x multiply-adds of the chunk form at full chunks, triangles exploited.
+    """
     C = CHUNK
     chv, chq = n_chunks * H_v, n_chunks * H_q
     q_b = k_b = T * H_q * d * es
@@ -57,22 +60,19 @@ def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True):
     gate_b = T * H_v * 4  # g or beta
     gc_b = chv * C * 4
     A_b = chv * C * C * es
-    W_b = U_b = X_b = chv * C * d * es
-    Kt_b = chq * d * C * es
+    W_b = U_b = X_b = Kd_b = chv * C * d * es
     H_b = chv * d * d * es
     S_b = N * H_v * d * d * 4
     tri = C * (C - 1) // 2   # strictly lower entries
     tri1 = C * (C + 1) // 2  # lower incl. diagonal
-    per = {  # multiply-adds per (chunk, value head) at full chunks
-        "kkt_solve": tri * d + C ** 3 // 6,
-        "recompute_w_u": 2 * tri1 * d,
-        "chunk_state_h": 2 * C * d * d,
-        "chunk_output_o": C * d * d + 2 * tri1 * d,
+    per = {  # multiply-adds per (chunk, value head)
+        "chunk_prep": tri * d + C ** 3 // 6 + 2 * tri1 * d,   # K K^T, solve, W, U
+        "chunk_state_h": 2 * C * d * d,                      # W S, Kd^T X
+        "chunk_output_o": C * d * d + 2 * tri1 * d,          # Q S, Q K^T, P X
     }
     bytes_ = {
-        "kkt_solve": k_b + 2 * gate_b + gc_b + A_b,
-        "recompute_w_u": A_b + k_b + v_b + gate_b + gc_b + W_b + U_b + Kt_b,
-        "chunk_state_h": W_b + U_b + Kt_b + gc_b + (S_b if has_s0 else 0) + H_b + X_b + S_b,
+        "chunk_prep": k_b + v_b + 2 * gate_b + gc_b + A_b + W_b + U_b + Kd_b,
+        "chunk_state_h": W_b + U_b + Kd_b + gc_b + (S_b if has_s0 else 0) + H_b + X_b + S_b,
         "chunk_output_o": q_b + k_b + gc_b + H_b + X_b + o_b,
     }
     flops = {k: 2 * v * chv for k, v in per.items()}
@@ -177,12 +177,13 @@ def bench_prefill(args, torch, gdn, hip, device):
     sptr = stream.cuda_stream
     code = gdn.DTYPE_BF16 if dt == "bf16" else gdn.DTYPE_F32
     K = args.steps
-    ev = [[hip.event() for _ in range(5)] for _ in range(max(K, 1))]
+    NEV = len(STAGES) + 1
+    ev = [[hip.event() for _ in range(NEV)] for _ in range(max(K, 1))]
 
     def step(events=None):
         arr = None
         if events is not None:
-            arr = (ctypes.c_void_p * 5)(*[e.value for e in events])
+            arr = (ctypes.c_void_p * NEV)(*[e.value for e in events])
         rc = lib.gdn_chunk_fwd_timed(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), cu,
                                      inp.N, None if s0 is None else s0.data_ptr(), out.data_ptr(), fin.data_ptr(),
                                      inp.T, inp.H_q, inp.H_v, inp.d_k, inp.d_v, inp.scale, code, ws.data_ptr(),

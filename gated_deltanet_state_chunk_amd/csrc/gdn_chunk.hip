@@ -1,15 +1,16 @@
 // Chunk-wise Gated DeltaNet prefill for gfx950.
 //
-// Four kernels, one per stage of the chunk form in "实验三：GDN Prefill 前向优化"
-// (section "计算过程描述"):
-//   1. kkt_solve     g^cumsum and A = (I + StrictLower(B Gamma K K^T Gamma^-1))^-1
-//   2. recompute_w_u W = A B Gamma K, U = A B V
-//   3. chunk_state_h S_{c+1} = gamma_l S_c + gamma_l K^T Gamma^-1 (U - W S_c), serial over chunks
-//   4. chunk_output_o O = scale [Gamma Q S_c + Gamma Lower(Q K^T) Gamma^-1 (U - W S_c)]
-// Stage names follow the Prefill-GDN kernel graph of the "Qwen3.5-397B-A17B"
-// trace page (nodes chunk_gate_cumsum, chunk_kkt_solve, chunk_recompute_w_u,
-// chunk_state_h, chunk_output_o), whose zero-init nodes are folded in here:
-// every workspace entry and output row is written exactly once.
+// The four stages of the chunk form in "实验三：GDN Prefill 前向优化" (section
+// "计算过程描述") in three kernels:
+//   1. chunk_prep     g^cumsum, A = (I + StrictLower(B Gamma K K^T Gamma^-1))^-1,
+//                     W = A B Gamma K, U = A B V          (stages 1 and 2)
+//   2. chunk_state_h  S_{c+1} = gamma_l S_c + gamma_l K^T Gamma^-1 (U - W S_c), serial over chunks
+//   3. chunk_output_o O = scale [Gamma Q S_c + Gamma Lower(Q K^T) Gamma^-1 (U - W S_c)]
+// The Prefill-GDN kernel graph of the "Qwen3.5-397B-A17B" trace page runs the
+// first kernel as three (chunk_gate_cumsum, chunk_kkt_solve,
+// chunk_recompute_w_u); here they share one pass over the chunk's keys, which
+// saves re-reading K and the round trip of A.  Its zero-init nodes are folded
+// in: every workspace entry and output row is written exactly once.
 //
 // Every ratio gamma_i / gamma_j is formed as exp(gc_i - gc_j) with i >= j, so
 // nothing overflows however strong the decay (Gamma^-1 alone would).
@@ -48,32 +49,32 @@ __device__ __forceinline__ ChunkPos locate_chunk(const SeqTable& tab, int ci) {
     return c;
 }
 
-constexpr int LPAD = 65;  // fp32 64x64 LDS matrices, padded row
+constexpr int LPAD = 68;  // fp32 64x64 LDS matrices: padded row, 16-byte aligned
 
-// acc += X[xr:xr+16, xc:xc+16] @ Y[yr:yr+16, yc:yc+16], fp32 operands in LDS,
-// four v_mfma_f32_16x16x4_f32 (lane (m, a) supplies X[m][4s+a] and Y[4s+a][m]).
-__device__ __forceinline__ f32x4 mm16_lds(const float (*X)[LPAD], int xr, int xc, const float (*Y)[LPAD], int yr,
-                                          int yc, f32x4 acc, int r16, int grp) {
+// acc += X[0:16, 0:16] @ Y[0:16, 0:16] for fp32 blocks in LDS with row strides
+// XS and YS: four v_mfma_f32_16x16x4_f32 (lane (m, a) supplies X[m][4s+a] and Y[4s+a][m]).
+template <int XS, int YS>
+__device__ __forceinline__ f32x4 mm16_lds(const float* X, const float* Y, f32x4 acc, int r16, int grp) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        const float a = X[xr + r16][xc + 4 * s + grp];
-        const float b = Y[yr + 4 * s + grp][yc + r16];
+        const float a = X[r16 * XS + 4 * s + grp];
+        const float b = Y[(4 * s + grp) * YS + r16];
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
     }
     return acc;
 }
 
-// Store a D tile (lane: column r16, rows 4*grp + i) into an LDS matrix at (r0, c0), times s.
-__device__ __forceinline__ void tile_to_lds(float (*M)[LPAD], int r0, int c0, const f32x4& t, float s, int r16,
-                                            int grp) {
+// Store a D tile (lane: column r16, rows 4*grp + i) into an LDS block with row stride MS, times s.
+template <int MS>
+__device__ __forceinline__ void tile_to_lds(float* M, const f32x4& t, float s, int r16, int grp) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) M[r0 + 4 * grp + i][c0 + r16] = s * t[i];
+    for (int i = 0; i < 4; ++i) M[(4 * grp + i) * MS + r16] = s * t[i];
 }
 
 }  // namespace
 
 // Fragment-order offsets (in elements) of the per-(chunk, value head) blocks
-// written by recompute_w_u and read by chunk_state_h.  A fragment holds 8
+// written by chunk_prep and read by chunk_state_h.  A fragment holds 8
 // values per lane; lane = 16 a + r with r the row (A operand) and a the lane
 // group; "perm32" slot 4 h + b stands for contraction index 16 h + 4 a + b.
 //   W  (rows pos, contraction d_k): fragment (pos / 16, K-step), lane, slot
@@ -92,10 +93,36 @@ __host__ __device__ __forceinline__ int frag_u_offset(int col_tile, int pos_tile
 }
 
 // ---------------------------------------------------------------------------
-// 1. kkt_solve: one workgroup (4 waves) per (chunk, value head).
+// 1. chunk_prep: one workgroup (4 waves) per (chunk, value head); the first two
+//    stages of the chunk form in one pass over the chunk's keys and values:
+//      gc = in-chunk inclusive cumsum of g          ("输入输出定义")
+//      L  = StrictLower(B Gamma K K^T Gamma^-1),  A = (I + L)^-1   (fp32)
+//      W  = A B Gamma K,  U = A B V,  Kd = diag(gamma_l / gamma) K
+//    K is staged in LDS once and serves K K^T, W and Kd; V is prefetched into
+//    registers and staged after the solve (in the space L occupied).  gc and A
+//    are also written to the workspace (for inspection); W, U and Kd are
+//    written in the fragment order chunk_state_h streams into LDS
+//    (frag_w_offset / frag_u_offset / frag_k_offset).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(256) void kkt_solve_kernel(const ChunkParams p, int padded) {
+struct PrepLds {
+    static constexpr int KP = D + 16 / (int)sizeof(T);  // padded row, 16-byte aligned
+    T K[CHUNK][KP];
+    union {
+        float L[CHUNK][LPAD];  // during the solve
+        T V[CHUNK][KP];        // after it
+    } lv;
+    float A[CHUNK][LPAD];
+    float Tm[4][16][20];
+    float gc[CHUNK], beta[CHUNK], sk[CHUNK], sv[CHUNK], kd[CHUNK];
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, int padded) {
+    using PL = PrepLds<T, D>;
+    constexpr int KP = PL::KP;
+    constexpr int VEC = 16 / (int)sizeof(T);                  // elements per 16-byte access
+    constexpr int NV = CHUNK * D / VEC / 256;                 // 16-byte pieces per thread
     const int wid = xcd_remap(blockIdx.x, padded);
     if (wid >= p.tab.n_chunks * p.H_v) return;
     const int h = wid % p.H_v;
@@ -104,13 +131,26 @@ __global__ __launch_bounds__(256) void kkt_solve_kernel(const ChunkParams p, int
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
     const int ell = cp.ell;
+    const size_t ch = (size_t)cp.ci * p.H_v + h;
 
-    __shared__ float s_gc[CHUNK], s_beta[CHUNK];
-    __shared__ float s_L[CHUNK][LPAD];
-    __shared__ float s_A[CHUNK][LPAD];
-    __shared__ float s_T[4][16][LPAD];
+    __shared__ __attribute__((aligned(16))) PL s;
 
-    // In-chunk inclusive cumsum of the log gate ("输入输出定义": restarts every chunk).
+    // V rows into registers now (staged in LDS after the solve); K rows into LDS.
+    const T* kb = reinterpret_cast<const T*>(p.k) + (size_t)cp.t0 * p.H_q * D + (size_t)hq * D;
+    const T* vb = reinterpret_cast<const T*>(p.v) + (size_t)cp.t0 * p.H_v * D + (size_t)h * D;
+    float4 vreg[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
+        vreg[j] = r < ell ? *reinterpret_cast<const float4*>(vb + (size_t)r * p.H_v * D + c) : make_float4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
+        *reinterpret_cast<float4*>(&s.K[r][c]) =
+            r < ell ? *reinterpret_cast<const float4*>(kb + (size_t)r * p.H_q * D + c) : make_float4(0, 0, 0, 0);
+    }
+    // In-chunk inclusive cumsum of the log gate.
     if (w == 0) {
         const size_t gi = (size_t)(cp.t0 + lane) * p.H_v + h;
         float gv = lane < ell ? p.g[gi] : 0.f;
@@ -120,38 +160,40 @@ __global__ __launch_bounds__(256) void kkt_solve_kernel(const ChunkParams p, int
             const float o = __shfl_up(gv, off, 64);
             if (lane >= off) gv += o;
         }
-        s_gc[lane] = gv;
-        s_beta[lane] = bv;
-        p.gc[((size_t)cp.ci * p.H_v + h) * CHUNK + lane] = lane < ell ? gv : 0.f;
-    }
-
-    // K K^T: wave w forms row block w against all four column blocks.
-    const T* kb = reinterpret_cast<const T*>(p.k) + (size_t)cp.t0 * p.H_q * D + (size_t)hq * D;
-    const size_t kstride = (size_t)p.H_q * D;
-    f32x4 acc[4];
-#pragma unroll
-    for (int J = 0; J < 4; ++J) acc[J] = zero4();
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-        Frag<T> a;
-        const int ra = 16 * w + r16;
-        load8_masked(a, kb + (size_t)ra * kstride + 32 * ks + 8 * grp, ra < ell);
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            Frag<T> b;
-            const int rb = 16 * J + r16;
-            load8_masked(b, kb + (size_t)rb * kstride + 32 * ks + 8 * grp, rb < ell);
-            acc[J] = mma(a, b, acc[J]);
-        }
+        const float gl = __shfl(gv, ell - 1, 64);
+        s.gc[lane] = gv;
+        s.beta[lane] = bv;
+        s.sk[lane] = bv * __expf(gv);                          // beta gamma
+        s.sv[lane] = bv;                                        // beta
+        s.kd[lane] = lane < ell ? __expf(gl - gv) : 0.f;        // gamma_l / gamma
+        p.gc[ch * CHUNK + lane] = lane < ell ? gv : 0.f;
     }
     __syncthreads();
-    // L_ij = beta_i exp(gc_i - gc_j) (k_i . k_j) for i > j; zero elsewhere.
+
+    // K K^T: wave w forms row block w against all four column blocks (fragments from LDS).
+    {
+        f32x4 acc[4];
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
+        for (int J = 0; J < 4; ++J) acc[J] = zero4();
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-            const int i = 16 * w + 4 * grp + i4, j = 16 * J + r16;
-            s_L[i][j] = (i > j) ? s_beta[i] * __expf(s_gc[i] - s_gc[j]) * acc[J][i4] : 0.f;
+        for (int ks = 0; ks < D / 32; ++ks) {
+            Frag<T> a;
+            load8(a, &s.K[16 * w + r16][32 * ks + 8 * grp]);
+#pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                Frag<T> b;
+                load8(b, &s.K[16 * J + r16][32 * ks + 8 * grp]);
+                acc[J] = mma(a, b, acc[J]);
+            }
+        }
+        // L_ij = beta_i exp(gc_i - gc_j) (k_i . k_j) for i > j; zero elsewhere.
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int i = 16 * w + 4 * grp + i4, j = 16 * J + r16;
+                s.lv.L[i][j] = (i > j) ? s.beta[i] * __expf(s.gc[i] - s.gc[j]) * acc[J][i4] : 0.f;
+            }
         }
     }
     __syncthreads();
@@ -162,28 +204,28 @@ __global__ __launch_bounds__(256) void kkt_solve_kernel(const ChunkParams p, int
         float a[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            float s = (r == c) ? 1.f : 0.f;
+            float acc = (r == c) ? 1.f : 0.f;
 #pragma unroll
-            for (int kk = 0; kk < r; ++kk) s -= s_L[base + r][base + kk] * a[kk];
-            a[r] = s;
+            for (int kk = 0; kk < r; ++kk) acc -= s.lv.L[base + r][base + kk] * a[kk];
+            a[r] = acc;
         }
         if (grp == 0) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s_A[base + r][base + c] = a[r];
+            for (int r = 0; r < 16; ++r) s.A[base + r][base + c] = a[r];
         }
     }
     __syncthreads();
     // 32x32 diagonal blocks: A10 = -A11 L10 A00 (wave 0), A32 = -A33 L32 A22 (wave 1).
     if (w < 2) {
         const int o = 32 * w;
-        const f32x4 t = mm16_lds(s_L, o + 16, o, s_A, o, o, zero4(), r16, grp);
-        tile_to_lds(s_T[w], 0, 0, t, 1.f, r16, grp);
+        const f32x4 t = mm16_lds<LPAD, LPAD>(&s.lv.L[o + 16][o], &s.A[o][o], zero4(), r16, grp);
+        tile_to_lds<20>(&s.Tm[w][0][0], t, 1.f, r16, grp);
     }
     __syncthreads();
     if (w < 2) {
         const int o = 32 * w;
-        const f32x4 t = mm16_lds(s_A, o + 16, o + 16, s_T[w], 0, 0, zero4(), r16, grp);
-        tile_to_lds(s_A, o + 16, o, t, -1.f, r16, grp);
+        const f32x4 t = mm16_lds<LPAD, 20>(&s.A[o + 16][o + 16], &s.Tm[w][0][0], zero4(), r16, grp);
+        tile_to_lds<LPAD>(&s.A[o + 16][o], t, -1.f, r16, grp);
     }
     __syncthreads();
     // Lower-left 32x32 block: A_LL = -A_hi (L_LL A_lo).  Wave w owns block (I, J) =
@@ -191,22 +233,29 @@ __global__ __launch_bounds__(256) void kkt_solve_kernel(const ChunkParams p, int
     {
         const int I = 2 + (w >> 1), J = w & 1;
         f32x4 t = zero4();
-        for (int K = J; K <= 1; ++K) t = mm16_lds(s_L, 16 * I, 16 * K, s_A, 16 * K, 16 * J, t, r16, grp);
-        tile_to_lds(s_T[w], 0, 0, t, 1.f, r16, grp);
+        for (int K = J; K <= 1; ++K)
+            t = mm16_lds<LPAD, LPAD>(&s.lv.L[16 * I][16 * K], &s.A[16 * K][16 * J], t, r16, grp);
+        tile_to_lds<20>(&s.Tm[w][0][0], t, 1.f, r16, grp);
     }
     __syncthreads();
-    // ... then A_IJ = -sum_{K=2..I} A_IK T_KJ (T_KJ sits in s_T[2*(K-2) + J]).
+    // ... then A_IJ = -sum_{K=2..I} A_IK T_KJ (T_KJ sits in Tm[2*(K-2) + J]).
     {
         const int I = 2 + (w >> 1), J = w & 1;
         f32x4 t = zero4();
-        for (int K = 2; K <= I; ++K) t = mm16_lds(s_A, 16 * I, 16 * K, s_T[2 * (K - 2) + J], 0, 0, t, r16, grp);
-        tile_to_lds(s_A, 16 * I, 16 * J, t, -1.f, r16, grp);
+        for (int K = 2; K <= I; ++K)
+            t = mm16_lds<LPAD, 20>(&s.A[16 * I][16 * K], &s.Tm[2 * (K - 2) + J][0][0], t, r16, grp);
+        tile_to_lds<LPAD>(&s.A[16 * I][16 * J], t, -1.f, r16, grp);
     }
     __syncthreads();
 
-    // Write A, zero outside the valid lower triangle: thread -> row tid/4, 16 columns.
+    // V into LDS (L is dead now); A to the workspace, zero outside the valid lower triangle.
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
+        *reinterpret_cast<float4*>(&s.lv.V[r][c]) = vreg[j];
+    }
     {
-        T* Ab = reinterpret_cast<T*>(p.A) + ((size_t)cp.ci * p.H_v + h) * CHUNK * CHUNK;
+        T* Ab = reinterpret_cast<T*>(p.A) + ch * CHUNK * CHUNK;
         const int i = tid >> 2, j0 = (tid & 3) * 16;
 #pragma unroll
         for (int j4 = 0; j4 < 16; j4 += 4) {
@@ -214,85 +263,34 @@ __global__ __launch_bounds__(256) void kkt_solve_kernel(const ChunkParams p, int
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int j = j0 + j4 + e;
-                v4[e] = (j <= i && i < ell) ? s_A[i][j] : 0.f;
+                v4[e] = (j <= i && i < ell) ? s.A[i][j] : 0.f;
             }
             store4(Ab + (size_t)i * CHUNK + j0 + j4, v4[0], v4[1], v4[2], v4[3]);
         }
     }
-}
-
-// ---------------------------------------------------------------------------
-// 2. recompute_w_u: one workgroup per (chunk, value head).
-//    W^T = (B Gamma K)^T A^T,  U = A (B V),  Kd^T = (diag(gamma_l / gamma_r) K)^T
-//    (the keys of the state update, already carrying the decay to the end of
-//    the chunk).  All three are written in the MFMA fragment order in which
-//    chunk_state_h consumes them (frag_w / frag_k / frag_u below), so that
-//    stage can copy each chunk's block into LDS with contiguous 1 KiB loads.
-// ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(256) void recompute_w_u_kernel(const ChunkParams p, int padded) {
-    const int wid = xcd_remap(blockIdx.x, padded);
-    if (wid >= p.tab.n_chunks * p.H_v) return;
-    const int h = wid % p.H_v;
-    const ChunkPos cp = locate_chunk(p.tab, p.tab.chunk_begin + wid / p.H_v);
-    const int hq = h / p.G;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int r16 = lane & 15, grp = lane >> 4;
-    const int ell = cp.ell;
-    constexpr int SP = D + 2;  // padded LDS row
-
-    __shared__ T s_K[CHUNK][SP];
-    __shared__ T s_V[CHUNK][SP];
-    __shared__ float s_sk[CHUNK], s_sv[CHUNK], s_kd[CHUNK];
-
-    if (tid < CHUNK) {
-        const size_t gi = (size_t)(cp.t0 + tid) * p.H_v + h;
-        const float* gcb = p.gc + ((size_t)cp.ci * p.H_v + h) * CHUNK;
-        const float b = tid < ell ? p.beta[gi] : 0.f;
-        const float gcv = gcb[tid];
-        s_sk[tid] = b * __expf(gcv);
-        s_sv[tid] = b;
-        s_kd[tid] = tid < ell ? __expf(gcb[ell - 1] - gcv) : 0.f;  // gamma_l / gamma_r
-    }
-    // Stage the chunk's K and V rows (zeros past the valid length).
-    {
-        const T* kb = reinterpret_cast<const T*>(p.k) + (size_t)cp.t0 * p.H_q * D + (size_t)hq * D;
-        const T* vb = reinterpret_cast<const T*>(p.v) + (size_t)cp.t0 * p.H_v * D + (size_t)h * D;
-        constexpr int PER_ROW = D / 4;  // 4-element groups per row
-        for (int e = tid; e < CHUNK * PER_ROW; e += 256) {
-            const int r = e / PER_ROW, c4 = (e % PER_ROW) * 4;
-            float k0 = 0.f, k1 = 0.f, k2 = 0.f, k3 = 0.f, v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
-            if (r < ell) {
-                load4(kb + (size_t)r * p.H_q * D + c4, k0, k1, k2, k3);
-                load4(vb + (size_t)r * p.H_v * D + c4, v0, v1, v2, v3);
-            }
-            s_K[r][c4 + 0] = from_f32<T>(k0);
-            s_K[r][c4 + 1] = from_f32<T>(k1);
-            s_K[r][c4 + 2] = from_f32<T>(k2);
-            s_K[r][c4 + 3] = from_f32<T>(k3);
-            s_V[r][c4 + 0] = from_f32<T>(v0);
-            s_V[r][c4 + 1] = from_f32<T>(v1);
-            s_V[r][c4 + 2] = from_f32<T>(v2);
-            s_V[r][c4 + 3] = from_f32<T>(v3);
-        }
-    }
     __syncthreads();
 
-    // Fragments of A (rows pos, contiguous columns), shared by both products:
-    // Af[mt][ks] is the A operand of U = A (B V) for row tile mt and the B
-    // operand of W^T = (B Gamma K)^T A^T for column tile mt.
-    const T* Ab = reinterpret_cast<const T*>(p.A) + ((size_t)cp.ci * p.H_v + h) * CHUNK * CHUNK;
+    // Fragments of A (rows pos, contiguous columns), masked to the valid triangle:
+    // Af[mt][ks] is the A operand of U = A (B V) for row tile mt and the B operand
+    // of W^T = (B Gamma K)^T A^T for column tile mt.
     Frag<T> Af[4][2];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) load8(Af[mt][ks], Ab + (size_t)(16 * mt + r16) * CHUNK + 32 * ks + 8 * grp);
+        for (int ks = 0; ks < 2; ++ks) {
+            const int i = 16 * mt + r16;
+#pragma unroll
+            for (int j8 = 0; j8 < 8; ++j8) {
+                const int j = 32 * ks + 8 * grp + j8;
+                frag_set(Af[mt][ks], j8, (j <= i && i < ell) ? s.A[i][j] : 0.f);
+            }
+        }
 
     constexpr int TPW = D / 64;  // 16-wide tiles of d_k (or d_v) per wave
     constexpr int KS = D / 32;
     // W^T tiles: rows d_k (this wave's tiles), columns pos.  A is lower triangular,
     // so column tile nt only needs contraction steps ks with 32 ks <= 16 nt + 15.
-    T* Wb = reinterpret_cast<T*>(p.W) + ((size_t)cp.ci * p.H_v + h) * CHUNK * D;
+    T* Wb = reinterpret_cast<T*>(p.W) + ch * CHUNK * D;
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
         const int mt = w * TPW + tt;
@@ -303,7 +301,7 @@ __global__ __launch_bounds__(256) void recompute_w_u_kernel(const ChunkParams p,
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int r = 32 * ks + 8 * grp + j;
-                frag_set(kf[ks], j, s_sk[r] * to_f32<T>(s_K[r][dk]));
+                frag_set(kf[ks], j, s.sk[r] * to_f32<T>(s.K[r][dk]));
             }
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
@@ -316,8 +314,7 @@ __global__ __launch_bounds__(256) void recompute_w_u_kernel(const ChunkParams p,
         }
     }
     // U tiles: rows pos, columns d_v (this wave's tiles).
-    T* Ub = reinterpret_cast<T*>(p.Ut) + ((size_t)cp.ci * p.H_v + h) * D * CHUNK;
-    (void)KS;
+    T* Ub = reinterpret_cast<T*>(p.Ut) + ch * D * CHUNK;
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
         const int nt = w * TPW + tt;
@@ -328,7 +325,7 @@ __global__ __launch_bounds__(256) void recompute_w_u_kernel(const ChunkParams p,
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int r = 32 * ks + 8 * grp + j;
-                frag_set(vf[ks], j, s_sv[r] * to_f32<T>(s_V[r][dv]));
+                frag_set(vf[ks], j, s.sv[r] * to_f32<T>(s.lv.V[r][dv]));
             }
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
@@ -341,14 +338,15 @@ __global__ __launch_bounds__(256) void recompute_w_u_kernel(const ChunkParams p,
     }
     // Decayed keys of the state update, transposed.
     {
-        T* Kb = reinterpret_cast<T*>(p.Kt) + ((size_t)cp.ci * p.H_v + h) * D * CHUNK;
+        T* Kb = reinterpret_cast<T*>(p.Kt) + ch * D * CHUNK;
         for (int e = tid; e < D * (CHUNK / 4); e += 256) {
             const int dk = e / (CHUNK / 4), r4 = (e % (CHUNK / 4)) * 4;
-            store4(Kb + frag_k_offset(dk, r4), s_kd[r4] * to_f32<T>(s_K[r4][dk]),
-                   s_kd[r4 + 1] * to_f32<T>(s_K[r4 + 1][dk]), s_kd[r4 + 2] * to_f32<T>(s_K[r4 + 2][dk]),
-                   s_kd[r4 + 3] * to_f32<T>(s_K[r4 + 3][dk]));
+            store4(Kb + frag_k_offset(dk, r4), s.kd[r4] * to_f32<T>(s.K[r4][dk]),
+                   s.kd[r4 + 1] * to_f32<T>(s.K[r4 + 1][dk]), s.kd[r4 + 2] * to_f32<T>(s.K[r4 + 2][dk]),
+                   s.kd[r4 + 3] * to_f32<T>(s.K[r4 + 3][dk]));
         }
     }
+    (void)KS;
 }
 
 // ---------------------------------------------------------------------------
@@ -365,7 +363,7 @@ __global__ __launch_bounds__(256) void recompute_w_u_kernel(const ChunkParams p,
 //    chunk, and read their operands from the LDS stage of that chunk.
 //
 //    Producer wave.  Streams each chunk's W, Kd, U and gate blocks (stored by
-//    recompute_w_u in exactly the LDS stage order) into a ring of stages with
+//    chunk_prep in exactly the LDS stage order) into a ring of stages with
 //    direct global->LDS loads, NST - 1 chunks ahead, so the compute waves never
 //    issue a global load: the per-chunk operands (about 34 KiB) would otherwise
 //    stall their instruction stream on the CU's vector-memory path.
@@ -670,17 +668,14 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
         if (events) (void)hipEventRecord(events[i], stream);
     };
     mark(0);
-    if (work_ch > 0) hipLaunchKernelGGL((kkt_solve_kernel<T, D>), dim3(grid_ch), dim3(256), 0, stream, p, grid_ch);
+    if (work_ch > 0) hipLaunchKernelGGL((chunk_prep_kernel<T, D>), dim3(grid_ch), dim3(256), 0, stream, p, grid_ch);
     mark(1);
-    if (work_ch > 0)
-        hipLaunchKernelGGL((recompute_w_u_kernel<T, D>), dim3(grid_ch), dim3(256), 0, stream, p, grid_ch);
-    mark(2);
     if (work_st > 0)
         hipLaunchKernelGGL((chunk_state_h_kernel<T, D>), dim3(grid_st), dim3(320), 0, stream, p, grid_st);
-    mark(3);
+    mark(2);
     if (work_ch > 0)
         hipLaunchKernelGGL((chunk_output_o_kernel<T, D>), dim3(grid_ch), dim3(256), 0, stream, p, grid_ch);
-    mark(4);
+    mark(3);
     return hipGetLastError();
 }
 

@@ -138,12 +138,12 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
 
 /*
  * gdn_chunk_fwd with stage timing, for profiling and benchmarks.  Same
- * arguments, same results.  `stage_events` is NULL or an array of five
+ * arguments, same results.  `stage_events` is NULL or an array of four
  * hipEvent_t created by the caller; they are recorded on `stream` before the
- * first kernel and after each of the four kernels (kkt_solve, recompute_w_u,
- * chunk_state_h, chunk_output_o) of the first launch (a launch covers up to 64
- * sequences; larger batches take several).  Event k+1 minus event k is then the
- * device time of kernel k.
+ * first kernel and after each of the three kernels (chunk_prep: gate cumsum,
+ * A, W, U; chunk_state_h: the serial state scan; chunk_output_o) of the first
+ * launch (a launch covers up to 64 sequences; larger batches take several).
+ * Event k+1 minus event k is then the device time of kernel k.
  */
 int gdn_chunk_fwd_timed(const void *q, const void *k, const void *v, const float *g, const float *beta,
                         const int32_t *cu_seqlens_host, int32_t num_seqs, const float *initial_state, void *out,
