@@ -49,8 +49,6 @@ __device__ __forceinline__ ChunkPos locate_chunk(const SeqTable& tab, int ci) {
     return c;
 }
 
-constexpr int LPAD = 68;  // fp32 64x64 LDS matrices: padded row, 16-byte aligned
-
 // acc += X[0:16, 0:16] @ Y[0:16, 0:16] for fp32 blocks in LDS with row strides
 // XS and YS: four v_mfma_f32_16x16x4_f32 (lane (m, a) supplies X[m][4s+a] and Y[4s+a][m]).
 template <int XS, int YS>
@@ -104,23 +102,30 @@ __host__ __device__ __forceinline__ int frag_u_offset(int col_tile, int pos_tile
 //    written in the fragment order chunk_state_h streams into LDS
 //    (frag_w_offset / frag_u_offset / frag_k_offset).
 // ---------------------------------------------------------------------------
+// Lower-triangular 64x64 fp32 matrices are kept as their ten 16x16 blocks
+// (I >= J), block (I, J) at index I (I + 1) / 2 + J, rows padded to BS floats.
+constexpr int BS = 20;
+constexpr int BLK = 16 * BS;
+__host__ __device__ constexpr int blk(int I, int J) { return (I * (I + 1) / 2 + J) * BLK; }
+
 template <typename T, int D>
 struct PrepLds {
     static constexpr int KP = D + 16 / (int)sizeof(T);  // padded row, 16-byte aligned
     T K[CHUNK][KP];
     union {
-        float L[CHUNK][LPAD];  // during the solve
-        T V[CHUNK][KP];        // after it
-    } lv;
-    float A[CHUNK][LPAD];
-    float Tm[4][16][20];
-    float gc[CHUNK], beta[CHUNK], sk[CHUNK], sv[CHUNK], kd[CHUNK];
+        struct {
+            float L[10 * BLK];  // strictly lower part of B Gamma K K^T Gamma^-1
+            float Tm[4 * BLK];  // products of the block solve
+        } sv;                   // during the solve
+        T V[CHUNK][KP];         // after it
+    } u;
+    float A[10 * BLK];          // (I + L)^-1
+    float gc[CHUNK], beta[CHUNK], sk[CHUNK], svb[CHUNK], kd[CHUNK];
 };
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, int padded) {
     using PL = PrepLds<T, D>;
-    constexpr int KP = PL::KP;
     constexpr int VEC = 16 / (int)sizeof(T);                  // elements per 16-byte access
     constexpr int NV = CHUNK * D / VEC / 256;                 // 16-byte pieces per thread
     const int wid = xcd_remap(blockIdx.x, padded);
@@ -134,6 +139,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
     const size_t ch = (size_t)cp.ci * p.H_v + h;
 
     __shared__ __attribute__((aligned(16))) PL s;
+    float* const Ls = s.u.sv.L;
+    float* const Tm = s.u.sv.Tm;
+    float* const As = s.A;
 
     // V rows into registers now (staged in LDS after the solve); K rows into LDS.
     const T* kb = reinterpret_cast<const T*>(p.k) + (size_t)cp.t0 * p.H_q * D + (size_t)hq * D;
@@ -164,68 +172,62 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
         s.gc[lane] = gv;
         s.beta[lane] = bv;
         s.sk[lane] = bv * __expf(gv);                          // beta gamma
-        s.sv[lane] = bv;                                        // beta
+        s.svb[lane] = bv;                                       // beta
         s.kd[lane] = lane < ell ? __expf(gl - gv) : 0.f;        // gamma_l / gamma
         p.gc[ch * CHUNK + lane] = lane < ell ? gv : 0.f;
     }
     __syncthreads();
 
-    // K K^T: wave w forms row block w against all four column blocks (fragments from LDS).
-    {
-        f32x4 acc[4];
-#pragma unroll
-        for (int J = 0; J < 4; ++J) acc[J] = zero4();
+    // K K^T: wave w forms row block w against column blocks J <= w (fragments from LDS);
+    // L_ij = beta_i exp(gc_i - gc_j) (k_i . k_j) for i > j, zero elsewhere.
+    for (int J = 0; J <= w; ++J) {
+        f32x4 acc = zero4();
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
-            Frag<T> a;
+            Frag<T> a, b;
             load8(a, &s.K[16 * w + r16][32 * ks + 8 * grp]);
-#pragma unroll
-            for (int J = 0; J < 4; ++J) {
-                Frag<T> b;
-                load8(b, &s.K[16 * J + r16][32 * ks + 8 * grp]);
-                acc[J] = mma(a, b, acc[J]);
-            }
+            load8(b, &s.K[16 * J + r16][32 * ks + 8 * grp]);
+            acc = mma(a, b, acc);
         }
-        // L_ij = beta_i exp(gc_i - gc_j) (k_i . k_j) for i > j; zero elsewhere.
+        float* Lb = Ls + blk(w, J);
 #pragma unroll
-        for (int J = 0; J < 4; ++J) {
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const int i = 16 * w + 4 * grp + i4, j = 16 * J + r16;
-                s.lv.L[i][j] = (i > j) ? s.beta[i] * __expf(s.gc[i] - s.gc[j]) * acc[J][i4] : 0.f;
-            }
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const int i = 16 * w + 4 * grp + i4, j = 16 * J + r16;
+            Lb[(4 * grp + i4) * BS + r16] = (i > j) ? s.beta[i] * __expf(s.gc[i] - s.gc[j]) * acc[i4] : 0.f;
         }
     }
     __syncthreads();
 
     // (I + L)^-1 by blocks of 16.  Diagonal blocks: forward substitution, lane owns column c.
     {
-        const int base = 16 * w, c = r16;
+        const float* Lb = Ls + blk(w, w);
+        const int c = r16;
         float a[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float acc = (r == c) ? 1.f : 0.f;
 #pragma unroll
-            for (int kk = 0; kk < r; ++kk) acc -= s.lv.L[base + r][base + kk] * a[kk];
+            for (int kk = 0; kk < r; ++kk) acc -= Lb[r * BS + kk] * a[kk];
             a[r] = acc;
         }
         if (grp == 0) {
+            float* Ab = As + blk(w, w);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s.A[base + r][base + c] = a[r];
+            for (int r = 0; r < 16; ++r) Ab[r * BS + c] = a[r];
         }
     }
     __syncthreads();
     // 32x32 diagonal blocks: A10 = -A11 L10 A00 (wave 0), A32 = -A33 L32 A22 (wave 1).
     if (w < 2) {
-        const int o = 32 * w;
-        const f32x4 t = mm16_lds<LPAD, LPAD>(&s.lv.L[o + 16][o], &s.A[o][o], zero4(), r16, grp);
-        tile_to_lds<20>(&s.Tm[w][0][0], t, 1.f, r16, grp);
+        const int o = 2 * w;
+        const f32x4 t = mm16_lds<BS, BS>(Ls + blk(o + 1, o), As + blk(o, o), zero4(), r16, grp);
+        tile_to_lds<BS>(Tm + w * BLK, t, 1.f, r16, grp);
     }
     __syncthreads();
     if (w < 2) {
-        const int o = 32 * w;
-        const f32x4 t = mm16_lds<LPAD, 20>(&s.A[o + 16][o + 16], &s.Tm[w][0][0], zero4(), r16, grp);
-        tile_to_lds<LPAD>(&s.A[o + 16][o], t, -1.f, r16, grp);
+        const int o = 2 * w;
+        const f32x4 t = mm16_lds<BS, BS>(As + blk(o + 1, o + 1), Tm + w * BLK, zero4(), r16, grp);
+        tile_to_lds<BS>(As + blk(o + 1, o), t, -1.f, r16, grp);
     }
     __syncthreads();
     // Lower-left 32x32 block: A_LL = -A_hi (L_LL A_lo).  Wave w owns block (I, J) =
@@ -233,18 +235,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
     {
         const int I = 2 + (w >> 1), J = w & 1;
         f32x4 t = zero4();
-        for (int K = J; K <= 1; ++K)
-            t = mm16_lds<LPAD, LPAD>(&s.lv.L[16 * I][16 * K], &s.A[16 * K][16 * J], t, r16, grp);
-        tile_to_lds<20>(&s.Tm[w][0][0], t, 1.f, r16, grp);
+        for (int K = J; K <= 1; ++K) t = mm16_lds<BS, BS>(Ls + blk(I, K), As + blk(K, J), t, r16, grp);
+        tile_to_lds<BS>(Tm + w * BLK, t, 1.f, r16, grp);
     }
     __syncthreads();
-    // ... then A_IJ = -sum_{K=2..I} A_IK T_KJ (T_KJ sits in Tm[2*(K-2) + J]).
+    // ... then A_IJ = -sum_{K=2..I} A_IK T_KJ (T_KJ sits in Tm block 2*(K-2) + J).
     {
         const int I = 2 + (w >> 1), J = w & 1;
         f32x4 t = zero4();
-        for (int K = 2; K <= I; ++K)
-            t = mm16_lds<LPAD, 20>(&s.A[16 * I][16 * K], &s.Tm[2 * (K - 2) + J][0][0], t, r16, grp);
-        tile_to_lds<LPAD>(&s.A[16 * I][16 * J], t, -1.f, r16, grp);
+        for (int K = 2; K <= I; ++K) t = mm16_lds<BS, BS>(As + blk(I, K), Tm + (2 * (K - 2) + J) * BLK, t, r16, grp);
+        tile_to_lds<BS>(As + blk(I, J), t, -1.f, r16, grp);
     }
     __syncthreads();
 
@@ -252,42 +252,49 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
-        *reinterpret_cast<float4*>(&s.lv.V[r][c]) = vreg[j];
+        *reinterpret_cast<float4*>(&s.u.V[r][c]) = vreg[j];
     }
     {
         T* Ab = reinterpret_cast<T*>(p.A) + ch * CHUNK * CHUNK;
-        const int i = tid >> 2, j0 = (tid & 3) * 16;
+        const int i = tid >> 2, jb = tid & 3;  // row i, column block jb
+        const float* src = As + blk(i >> 4, jb) + (i & 15) * BS;
 #pragma unroll
         for (int j4 = 0; j4 < 16; j4 += 4) {
             float v4[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int j = j0 + j4 + e;
-                v4[e] = (j <= i && i < ell) ? s.A[i][j] : 0.f;
+                const int j = 16 * jb + j4 + e;
+                v4[e] = (jb <= (i >> 4) && j <= i && i < ell) ? src[j4 + e] : 0.f;
             }
-            store4(Ab + (size_t)i * CHUNK + j0 + j4, v4[0], v4[1], v4[2], v4[3]);
+            store4(Ab + (size_t)i * CHUNK + 16 * jb + j4, v4[0], v4[1], v4[2], v4[3]);
         }
     }
     __syncthreads();
 
-    // Fragments of A (rows pos, contiguous columns), masked to the valid triangle:
-    // Af[mt][ks] is the A operand of U = A (B V) for row tile mt and the B operand
-    // of W^T = (B Gamma K)^T A^T for column tile mt.
+    // Fragments of A (rows pos, contiguous columns): Af[mt][ks] is the A operand of
+    // U = A (B V) for row tile mt and the B operand of W^T = (B Gamma K)^T A^T for
+    // column tile mt.  Blocks above the diagonal are zero; rows past the valid
+    // length are unit rows e_i, which meet zero rows of B Gamma K and B V, so W and
+    // U vanish there without masking.
     Frag<T> Af[4][2];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const int i = 16 * mt + r16;
-#pragma unroll
-            for (int j8 = 0; j8 < 8; ++j8) {
-                const int j = 32 * ks + 8 * grp + j8;
-                frag_set(Af[mt][ks], j8, (j <= i && i < ell) ? s.A[i][j] : 0.f);
+            const int J = 2 * ks + (grp >> 1);  // column block of this lane's 8 columns
+            float4 lo = make_float4(0, 0, 0, 0), hi = lo;
+            if (J <= mt) {
+                const float4* src = reinterpret_cast<const float4*>(As + blk(mt, J) + r16 * BS + 8 * (grp & 1));
+                lo = src[0];
+                hi = src[1];
             }
+            frag_set(Af[mt][ks], 0, lo.x); frag_set(Af[mt][ks], 1, lo.y);
+            frag_set(Af[mt][ks], 2, lo.z); frag_set(Af[mt][ks], 3, lo.w);
+            frag_set(Af[mt][ks], 4, hi.x); frag_set(Af[mt][ks], 5, hi.y);
+            frag_set(Af[mt][ks], 6, hi.z); frag_set(Af[mt][ks], 7, hi.w);
         }
 
     constexpr int TPW = D / 64;  // 16-wide tiles of d_k (or d_v) per wave
-    constexpr int KS = D / 32;
     // W^T tiles: rows d_k (this wave's tiles), columns pos.  A is lower triangular,
     // so column tile nt only needs contraction steps ks with 32 ks <= 16 nt + 15.
     T* Wb = reinterpret_cast<T*>(p.W) + ch * CHUNK * D;
@@ -325,7 +332,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int r = 32 * ks + 8 * grp + j;
-                frag_set(vf[ks], j, s.sv[r] * to_f32<T>(s.lv.V[r][dv]));
+                frag_set(vf[ks], j, s.svb[r] * to_f32<T>(s.u.V[r][dv]));
             }
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
@@ -346,7 +353,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
                    s.kd[r4 + 3] * to_f32<T>(s.K[r4 + 3][dk]));
         }
     }
-    (void)KS;
 }
 
 // ---------------------------------------------------------------------------
