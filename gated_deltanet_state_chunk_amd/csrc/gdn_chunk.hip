@@ -552,12 +552,29 @@ __global__ __launch_bounds__(320) void chunk_state_h_kernel(const ChunkParams p,
 }
 
 // ---------------------------------------------------------------------------
-// 4. chunk_output_o: one workgroup per (chunk, value head).  Computes
+// 4. chunk_output_o: one workgroup (4 waves) per (chunk, value head).  Computes
 //    O^T = scale [ (H^T Q^T) diag(gamma) + (U - W S)^T P^T ],
 //    P^T[j][i] = (k_j . q_i) exp(gc_i - gc_j) for j <= i  (Lower keeps the diagonal).
+//    Q and K are staged in LDS once; wave w forms the P^T tiles of query block w
+//    and publishes them in operand order; then each wave produces its 16-row
+//    tiles of O^T (d_v rows) for all 64 positions.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
+struct OutLds {
+    static constexpr int KP = D + 16 / (int)sizeof(T);
+    T Q[CHUNK][KP];
+    T K[CHUNK][KP];
+    Frag<T> P[4][2][64];  // B operand of (U - W S)^T P^T: [query tile][K-step][lane]
+    float gc[CHUNK];
+};
+
+template <typename T, int D>
 __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p, int padded) {
+    using OL = OutLds<T, D>;
+    constexpr int KS = D / 32;
+    constexpr int TPW = D / 64;
+    constexpr int VEC = 16 / (int)sizeof(T);
+    constexpr int NV = CHUNK * D / VEC / 256;
     const int wid = xcd_remap(blockIdx.x, padded);
     if (wid >= p.tab.n_chunks * p.H_v) return;
     const int h = wid % p.H_v;
@@ -566,94 +583,95 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
     const int ell = cp.ell;
-    constexpr int KS = D / 32;
-    constexpr int TPW = D / 64;
-    constexpr int PP = CHUNK + 2;
-
-    __shared__ float s_gc[CHUNK];
-    __shared__ T s_Pt[CHUNK][PP];  // P^T [pos'][pos]
-
     const size_t ch = (size_t)cp.ci * p.H_v + h;
-    if (tid < CHUNK) s_gc[tid] = p.gc[ch * CHUNK + tid];
 
+    __shared__ __attribute__((aligned(16))) OL s;
+
+    // This wave's operand fragments of H^T and (U - W S)^T (rows d_v), straight to registers.
+    const T* Hb = reinterpret_cast<const T*>(p.Ht) + ch * D * D;
+    const T* Xb = reinterpret_cast<const T*>(p.Xt) + ch * D * CHUNK;
+    Frag<T> hf[TPW][KS], xf[TPW][2];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+        const int dv = 16 * (w * TPW + tt) + r16;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) load8(hf[tt][ks], Hb + (size_t)dv * D + 32 * ks + 8 * grp);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) load8(xf[tt][ks], Xb + (size_t)dv * CHUNK + 32 * ks + 8 * grp);
+    }
+    // Q and K rows into LDS (zeros past the valid length), gates.
     const T* qb = reinterpret_cast<const T*>(p.q) + (size_t)cp.t0 * p.H_q * D + (size_t)hq * D;
     const T* kb = reinterpret_cast<const T*>(p.k) + (size_t)cp.t0 * p.H_q * D + (size_t)hq * D;
-    const size_t qstride = (size_t)p.H_q * D;
-
-    // Q fragments (B operand, rows pos): Qf[nt][ks].
-    Frag<T> Qf[4][KS];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int r = 16 * nt + r16;
-            load8_masked(Qf[nt][ks], qb + (size_t)r * qstride + 32 * ks + 8 * grp, r < ell);
-        }
-    __syncthreads();  // s_gc
-
-    // P^T tiles (I, J = w) for I <= w: rows pos' (keys), columns pos (queries).
-    Frag<T> qw[KS];  // query fragments of column tile w (runtime index: load, do not index Qf)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const int r = 16 * w + r16;
-        load8_masked(qw[ks], qb + (size_t)r * qstride + 32 * ks + 8 * grp, r < ell);
+    for (int j = 0; j < NV; ++j) {
+        const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
+        const bool ok = r < ell;
+        const size_t off = (size_t)r * p.H_q * D + c;
+        *reinterpret_cast<float4*>(&s.Q[r][c]) = ok ? *reinterpret_cast<const float4*>(qb + off) : make_float4(0, 0, 0, 0);
+        *reinterpret_cast<float4*>(&s.K[r][c]) = ok ? *reinterpret_cast<const float4*>(kb + off) : make_float4(0, 0, 0, 0);
     }
-    for (int I = 0; I < 4; ++I) {
-        f32x4 c = zero4();
-        if (I <= w) {
+    if (tid < CHUNK) s.gc[tid] = p.gc[ch * CHUNK + tid];
+    __syncthreads();
+
+    // P^T tiles (I, J = w) for I <= w, published as B fragments for query tile w.
+    {
+        Frag<T> qw[KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                Frag<T> kf;
-                const int r = 16 * I + r16;
-                load8_masked(kf, kb + (size_t)r * qstride + 32 * ks + 8 * grp, r < ell);
-                c = mma(kf, qw[ks], c);
-            }
-        }
+        for (int ks = 0; ks < KS; ++ks) load8(qw[ks], &s.Q[16 * w + r16][32 * ks + 8 * grp]);
         const int pos = 16 * w + r16;
+        const float gq = s.gc[pos];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int pj = 16 * I + 4 * grp + i;
-            const float val = (pj <= pos && pos < ell) ? c[i] * __expf(s_gc[pos] - s_gc[pj]) : 0.f;
-            s_Pt[pj][pos] = from_f32<T>(val);
+        for (int I = 0; I < 4; ++I) {
+            f32x4 c = zero4();
+            if (I <= w) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    Frag<T> kf;
+                    load8(kf, &s.K[16 * I + r16][32 * ks + 8 * grp]);
+                    c = mma(kf, qw[ks], c);
+                }
+            }
+            f32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int pj = 16 * I + 4 * grp + i;
+                v[i] = (pj <= pos && pos < ell) ? c[i] * __expf(gq - s.gc[pj]) : 0.f;
+            }
+            // rows pos' 16 I + 4 grp + i: K-step I / 2, slots 4 (I % 2) + i
+            if constexpr (sizeof(T) == 2) {
+                *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(&s.P[w][I >> 1][lane]) + 4 * (I & 1)) =
+                    cvt4_bf16(v, 1.f);
+            } else {
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(&s.P[w][I >> 1][lane]) + 4 * (I & 1)) =
+                    make_float4(v[0], v[1], v[2], v[3]);
+            }
         }
     }
     __syncthreads();
 
     // Output tiles: rows d_v (this wave's tiles), columns pos.
-    const T* Hb = reinterpret_cast<const T*>(p.Ht) + ch * D * D;
-    const T* Xb = reinterpret_cast<const T*>(p.Xt) + ch * D * CHUNK;
     T* ob = reinterpret_cast<T*>(p.out) + (size_t)cp.t0 * p.H_v * D + (size_t)h * D;
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-        const int mt = w * TPW + tt;
-        const int dv = 16 * mt + r16;
-        Frag<T> hf[KS], xf[2];
+    for (int nt = 0; nt < 4; ++nt) {
+        Frag<T> qf[KS], pf[2];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) load8(hf[ks], Hb + (size_t)dv * D + 32 * ks + 8 * grp);
+        for (int ks = 0; ks < KS; ++ks) load8(qf[ks], &s.Q[16 * nt + r16][32 * ks + 8 * grp]);
+        pf[0] = s.P[nt][0][lane];
+        pf[1] = s.P[nt][1][lane];
+        const int pos = 16 * nt + r16;
+        const float eg = __expf(s.gc[pos]);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) load8(xf[ks], Xb + (size_t)dv * CHUNK + 32 * ks + 8 * grp);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int tt = 0; tt < TPW; ++tt) {
             f32x4 inter = zero4(), intra = zero4();
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) inter = mma(hf[ks], Qf[nt][ks], inter);
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                if (32 * ks > 16 * nt + 15) continue;  // P^T rows all beyond this column tile
-                Frag<T> pf;  // perm32 slots: pos' = 32 ks + 16 hh + 4 grp + b
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) pf.v[4 * hh + b] = s_Pt[32 * ks + 16 * hh + 4 * grp + b][16 * nt + r16];
-                intra = mma(xf[ks], pf, intra);
-            }
-            const int pos = 16 * nt + r16;
+            for (int ks = 0; ks < KS; ++ks) inter = mma(hf[tt][ks], qf[ks], inter);
+            intra = mma(xf[tt][0], pf[0], intra);
+            if (nt >= 2) intra = mma(xf[tt][1], pf[1], intra);  // P^T rows 32..63 vanish for queries < 32
             if (pos < ell) {
-                const float eg = __expf(s_gc[pos]);
                 float o4[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o4[i] = p.scale * (eg * inter[i] + intra[i]);
-                store4(ob + (size_t)pos * p.H_v * D + 16 * mt + 4 * grp, o4[0], o4[1], o4[2], o4[3]);
+                store4(ob + (size_t)pos * p.H_v * D + 16 * (w * TPW + tt) + 4 * grp, o4[0], o4[1], o4[2], o4[3]);
             }
         }
     }
