@@ -12,7 +12,8 @@
 //
 // One 256-thread workgroup per (sequence, value head).  Thread t owns a 16-byte
 // column group cg = t % (d/4) of rows rg + RG*m (RG = 1024/d row groups), so
-// each wave reads whole contiguous rows with 128-bit loads.  Column sums are
+// each wave reads whole contiguous rows with 128-bit loads; the updated state
+// goes back with non-temporal 128-bit stores.  Column sums are
 // reduced across row groups with lane shuffles inside a wave and through LDS
 // across the four waves.
 #include "gdn_device.h"
@@ -97,7 +98,9 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(const DecodeParams 
         t.y = alpha * t.y + kr[m] * dl[1];
         t.z = alpha * t.z + kr[m] * dl[2];
         t.w = alpha * t.w + kr[m] * dl[3];
-        Sp[row * CPR + cg] = t;
+        // non-temporal: the state is not touched again by this step, and keeping
+        // it out of the caches measurably raises the read/write stream rate
+        __builtin_nontemporal_store(f32x4{t.x, t.y, t.z, t.w}, reinterpret_cast<f32x4*>(&Sp[row * CPR + cg]));
     }
     if (rg == 0) store4(reinterpret_cast<T*>(p.out) + (size_t)nh * D + 4 * cg, o[0], o[1], o[2], o[3]);
 }
