@@ -9,8 +9,8 @@ sequences x 1 token, 537 MB of fp32 state updated in place, fresh seeded tokens
 each step) is measured in the same run and reported under "decode".
 
 Prints ONE JSON line.  Timing: W untimed warm-up steps, then K timed steps
-between two device synchronisations, with HIP events recorded by the library
-on the launch stream before/after each kernel (per-kernel durations) and around
+between two device synchronisations, with start/stop HIP events stamped by each
+kernel's own dispatch (per-kernel durations, no launch gaps) and events around
 the whole step.  "roofline" reports the slowest kernel of the step against the
 HBM roofline on its algorithmic bytes; "cpu_baseline" times the fp64 oracle on
 the host cores over a bounded prefix of the same workload.
@@ -177,7 +177,7 @@ def bench_prefill(args, torch, gdn, hip, device):
     sptr = stream.cuda_stream
     code = gdn.DTYPE_BF16 if dt == "bf16" else gdn.DTYPE_F32
     K = args.steps
-    NEV = len(STAGES) + 1
+    NEV = 2 * len(STAGES)
     ev = [[hip.event() for _ in range(NEV)] for _ in range(max(K, 1))]
 
     def step(events=None):
@@ -204,7 +204,8 @@ def bench_prefill(args, torch, gdn, hip, device):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
-    stage_ms = {s: sum(hip.elapsed_ms(ev[i][j], ev[i][j + 1]) for i in range(K)) / K for j, s in enumerate(STAGES)}
+    stage_ms = {s: sum(hip.elapsed_ms(ev[i][2 * j], ev[i][2 * j + 1]) for i in range(K)) / K
+                for j, s in enumerate(STAGES)}
     ms_step = total_ms / K
     es = 2 if dt == "bf16" else 4
     bytes_, flops = prefill_work(inp.T, inp.N, lay["n_chunks"], inp.H_q, inp.H_v, inp.d_k, es,
@@ -241,32 +242,38 @@ def bench_decode(args, torch, gdn, hip, device):
     return dict(N=N, ms_step=ms, bytes=nbytes, flops=nflops, steps=K)
 
 
-def cpu_baseline(inp, target_s=12.0):
-    """fp64 oracle on the host cores over a prefix of the prefill workload (all heads)."""
+def cpu_baseline(inp, target_s=10.0):
+    """fp64 oracle on the host cores over the prefill workload (all heads): a prefix
+    sized to about target_s seconds, or the whole workload repeated until then."""
     import oracle
 
     threads = oracle.max_threads()
+    s0 = None if inp.initial_state is None else inp.initial_state[:1].astype("float64")
 
     def run(Tp):
         t = time.perf_counter()
         oracle.forward(inp.q32()[:Tp], inp.k32()[:Tp], inp.v32()[:Tp], inp.g[:Tp], inp.beta[:Tp], [0, Tp],
-                       inp.H_q, inp.H_v, inp.scale,
-                       initial_state=None if inp.initial_state is None else inp.initial_state[:1].astype("float64"))
+                       inp.H_q, inp.H_v, inp.scale, initial_state=s0)
         return time.perf_counter() - t
 
     probe_T = min(256, inp.T)
     tp = run(probe_T)
     Ts = int(min(inp.T, max(probe_T, probe_T * target_s / max(tp, 1e-6))))
     Ts = max(CHUNK, Ts // CHUNK * CHUNK) if inp.T >= CHUNK else inp.T
-    ts = run(Ts)
+    reps, total = 0, 0.0
+    while True:
+        total += run(Ts)
+        reps += 1
+        if total >= target_s or reps >= 1000:
+            break
     try:
         avail = len(os.sched_getaffinity(0))
     except AttributeError:
         avail = os.cpu_count()
-    return dict(value=Ts / ts, unit="tokens/s", cores=threads, kind="oracle",
+    return dict(value=reps * Ts / total, unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"fp64 token recurrence (oracle/gdn_recurrence.c, OpenMP over value heads) on the first "
-                       f"{Ts} of {inp.T} tokens, all {inp.H_v} value heads, {ts:.2f} s wall; "
-                       f"{avail} host cores visible")
+                       f"{Ts} of {inp.T} tokens, all {inp.H_v} value heads, run {reps} times in {total:.2f} s wall; "
+                       f"{avail} host cores visible, {threads} OpenMP threads")
 
 
 def copy_calibration(torch, device, gib=1.0):

@@ -16,6 +16,8 @@
 // nothing overflows however strong the decay (Gamma^-1 alone would).
 // Positions past a tail chunk's valid length carry beta = 0 and zero K/V rows,
 // which makes their rows of A (masked to zero), W, U and U - W S vanish.
+#include <hip/hip_ext.h>
+
 #include "gdn_device.h"
 #include "gdn_params.h"
 
@@ -688,18 +690,19 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
     const int grid_ch = pad8(work_ch);
     const int work_st = p.tab.num_seqs * p.H_v * (D / 16);
     const int grid_st = pad8(work_st);
-    auto mark = [&](int i) {
-        if (events) (void)hipEventRecord(events[i], stream);
+    // With events, each kernel is launched with hipExtLaunchKernelGGL, whose
+    // start/stop events are stamped by the kernel's own dispatch (kernel time
+    // only, no launch gaps).
+    auto launch = [&](int k, auto kernel, int grid, int block) {
+        if (events)
+            hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, stream, events[2 * k], events[2 * k + 1], 0, p,
+                                  grid);
+        else
+            hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, stream, p, grid);
     };
-    mark(0);
-    if (work_ch > 0) hipLaunchKernelGGL((chunk_prep_kernel<T, D>), dim3(grid_ch), dim3(256), 0, stream, p, grid_ch);
-    mark(1);
-    if (work_st > 0)
-        hipLaunchKernelGGL((chunk_state_h_kernel<T, D>), dim3(grid_st), dim3(320), 0, stream, p, grid_st);
-    mark(2);
-    if (work_ch > 0)
-        hipLaunchKernelGGL((chunk_output_o_kernel<T, D>), dim3(grid_ch), dim3(256), 0, stream, p, grid_ch);
-    mark(3);
+    if (work_ch > 0) launch(0, chunk_prep_kernel<T, D>, grid_ch, 256);
+    if (work_st > 0) launch(1, chunk_state_h_kernel<T, D>, grid_st, 320);
+    if (work_ch > 0) launch(2, chunk_output_o_kernel<T, D>, grid_ch, 256);
     return hipGetLastError();
 }
 

@@ -59,8 +59,8 @@ struct DecodeParams {
 };
 
 // Kernel launchers (defined in the .hip translation units).  T is float or
-// __bf16, D is d_k = d_v.  `events` is null or four events recorded before the
-// first and after each of the three chunk kernels.
+// __bf16, D is d_k = d_v.  `events` is null or six events: start and stop of
+// each of the three chunk kernels.
 template <typename T, int D>
 hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEvent_t const* events);
 

@@ -137,13 +137,14 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
                   gdn_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * gdn_chunk_fwd with stage timing, for profiling and benchmarks.  Same
- * arguments, same results.  `stage_events` is NULL or an array of four
- * hipEvent_t created by the caller; they are recorded on `stream` before the
- * first kernel and after each of the three kernels (chunk_prep: gate cumsum,
- * A, W, U; chunk_state_h: the serial state scan; chunk_output_o) of the first
- * launch (a launch covers up to 64 sequences; larger batches take several).
- * Event k+1 minus event k is then the device time of kernel k.
+ * gdn_chunk_fwd with per-kernel timing, for profiling and benchmarks.  Same
+ * arguments, same results.  `stage_events` is NULL or an array of six
+ * hipEvent_t created by the caller: the start and stop events of the three
+ * kernels (chunk_prep: gate cumsum, A, W, U; chunk_state_h: the serial state
+ * scan; chunk_output_o) of the first launch (a launch covers up to 64
+ * sequences; larger batches take several).  They are stamped by the kernels'
+ * own dispatches, so event 2k+1 minus event 2k is the execution time of
+ * kernel k without launch gaps.
  */
 int gdn_chunk_fwd_timed(const void *q, const void *k, const void *v, const float *g, const float *beta,
                         const int32_t *cu_seqlens_host, int32_t num_seqs, const float *initial_state, void *out,
