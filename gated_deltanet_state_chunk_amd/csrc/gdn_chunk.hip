@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
         s.kd[lane] = lane < ell ? __expf(gl - gv) : 0.f;        // gamma_l / gamma
         p.gc[ch * CHUNK + lane] = lane < ell ? gv : 0.f;
     }
-    __syncthreads();
+    lds_sync();
 
     // K K^T: wave w forms row block w against column blocks J <= w (fragments from LDS);
     // L_ij = beta_i exp(gc_i - gc_j) (k_i . k_j) for i > j, zero elsewhere.
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
             Lb[(4 * grp + i4) * BS + r16] = (i > j) ? s.beta[i] * __expf(s.gc[i] - s.gc[j]) * acc[i4] : 0.f;
         }
     }
-    __syncthreads();
+    lds_sync();
 
     // (I + L)^-1 by blocks of 16.  Diagonal blocks: forward substitution, lane owns column c.
     {
@@ -218,20 +218,20 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
             for (int r = 0; r < 16; ++r) Ab[r * BS + c] = a[r];
         }
     }
-    __syncthreads();
+    lds_sync();
     // 32x32 diagonal blocks: A10 = -A11 L10 A00 (wave 0), A32 = -A33 L32 A22 (wave 1).
     if (w < 2) {
         const int o = 2 * w;
         const f32x4 t = mm16_lds<BS, BS>(Ls + blk(o + 1, o), As + blk(o, o), zero4(), r16, grp);
         tile_to_lds<BS>(Tm + w * BLK, t, 1.f, r16, grp);
     }
-    __syncthreads();
+    lds_sync();
     if (w < 2) {
         const int o = 2 * w;
         const f32x4 t = mm16_lds<BS, BS>(As + blk(o + 1, o + 1), Tm + w * BLK, zero4(), r16, grp);
         tile_to_lds<BS>(As + blk(o + 1, o), t, -1.f, r16, grp);
     }
-    __syncthreads();
+    lds_sync();
     // Lower-left 32x32 block: A_LL = -A_hi (L_LL A_lo).  Wave w owns block (I, J) =
     // (2 + w/2, w%2); first T_IJ = sum_{K=J..1} L_IK A_KJ ...
     {
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
         for (int K = J; K <= 1; ++K) t = mm16_lds<BS, BS>(Ls + blk(I, K), As + blk(K, J), t, r16, grp);
         tile_to_lds<BS>(Tm + w * BLK, t, 1.f, r16, grp);
     }
-    __syncthreads();
+    lds_sync();
     // ... then A_IJ = -sum_{K=2..I} A_IK T_KJ (T_KJ sits in Tm block 2*(K-2) + J).
     {
         const int I = 2 + (w >> 1), J = w & 1;
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
         for (int K = 2; K <= I; ++K) t = mm16_lds<BS, BS>(As + blk(I, K), Tm + (2 * (K - 2) + J) * BLK, t, r16, grp);
         tile_to_lds<BS>(As + blk(I, J), t, -1.f, r16, grp);
     }
-    __syncthreads();
+    lds_sync();
 
     // V into LDS (L is dead now); A to the workspace, zero outside the valid lower triangle.
 #pragma unroll
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
             store4(Ab + (size_t)i * CHUNK + 16 * jb + j4, v4[0], v4[1], v4[2], v4[3]);
         }
     }
-    __syncthreads();
+    lds_sync();
 
     // Fragments of A (rows pos, contiguous columns): Af[mt][ks] is the A operand of
     // U = A (B V) for row tile mt and the B operand of W^T = (B Gamma K)^T A^T for
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
 // ---------------------------------------------------------------------------
 // 3. chunk_state_h: one workgroup per (sequence, value head, 16-column tile of
 //    d_v), serial over the sequence's chunks; four compute waves (one per SIMD)
-//    and one producer wave.
+//    and two producer waves.
 //
 //    Compute waves.  The fp32 state slice S[:, tile] (d_k x 16) stays in MFMA
 //    accumulators, split by rows over the waves.  Per chunk:
@@ -370,11 +370,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
 //    operand order (one 16-byte access per lane and fragment), two barriers a
 //    chunk, and read their operands from the LDS stage of that chunk.
 //
-//    Producer wave.  Streams each chunk's W, Kd, U and gate blocks (stored by
-//    chunk_prep in exactly the LDS stage order) into a ring of stages with
-//    direct global->LDS loads, NST - 1 chunks ahead, so the compute waves never
-//    issue a global load: the per-chunk operands (about 34 KiB) would otherwise
-//    stall their instruction stream on the CU's vector-memory path.
+//    Producer waves.  Two waves stream each chunk's W, Kd, U and gate blocks
+//    (stored by chunk_prep in exactly the LDS stage order) into a ring of NST
+//    stages with direct global->LDS loads, up to NST - 1 chunks ahead, so the
+//    compute waves never issue a global load: the per-chunk operands (about
+//    34 KiB) would otherwise stall their instruction stream.  Two producers,
+//    because one wave can keep only 63 memory operations in flight, which caps
+//    its stream at about 26 B/clk; the CU sustains more with more requests out.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct StateStage {
@@ -383,9 +385,16 @@ struct StateStage {
     static constexpr int U_BYTES = 4 * 64 * 4 * (int)sizeof(T);  // one 16-column tile
     static constexpr int G_BYTES = CHUNK * 4;
     static constexpr int BYTES = W_BYTES + K_BYTES + U_BYTES + G_BYTES;
-    static constexpr int NDMA = (W_BYTES + K_BYTES + U_BYTES) / 1024 + 1;  // loads per chunk
+    static constexpr int NPIECE = (W_BYTES + K_BYTES + U_BYTES) / 1024;    // 1 KiB loads per chunk (+ gates)
     static constexpr int EXCH = (D / 32 + 2) * 64 * 8 * (int)sizeof(T);    // -S and X exchange
-    static constexpr int NST = (3 * BYTES + EXCH <= 150 * 1024 && NDMA <= 63) ? 3 : 2;
+    // A wave can keep at most 63 vector-memory operations in flight, so the
+    // stream is split over NPW producer waves, each owning every NPW-th piece,
+    // with one chunk's share (plus the gate load) within that limit.
+    static constexpr int NPW = (NPIECE + 1 + 62) / 63;
+    static constexpr int PER_WAVE = (NPIECE + NPW - 1) / NPW + 1;           // upper bound incl. the gate load
+    // Two LDS stages: the compute waves copy chunk c into registers before
+    // B1(c), so stage c % 2 is refilled with chunk c + 2 from B1(c) on.
+    static constexpr int NST = 2;
 };
 
 typedef __attribute__((address_space(1))) const void* gptr_t;
@@ -404,22 +413,42 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Issue this producer wave's share (pieces j with j % NPW == pw) of one
+// chunk's direct-to-LDS loads; part 0 issues the first half of the share,
+// part 1 the rest and the 256-byte gate block (producer wave 0).
 template <typename T, int D>
-__device__ __forceinline__ void state_issue(char* stage, const ChunkParams& p, size_t ch, int tile, int lane) {
+__device__ __forceinline__ void state_issue(char* stage, const ChunkParams& p, size_t ch, int tile, int lane, int pw,
+                                            int part) {
     using SS = StateStage<T, D>;
     constexpr int NT = D / 16;
+    constexpr int NW = SS::W_BYTES / 1024, NK = SS::K_BYTES / 1024;
+    constexpr int NP = SS::NPIECE;
     const char* wg = reinterpret_cast<const char*>(p.W) + ch * SS::W_BYTES;
     const char* kg = reinterpret_cast<const char*>(p.Kt) + ch * SS::K_BYTES;
     const char* ug = reinterpret_cast<const char*>(p.Ut) + (ch * NT + tile) * SS::U_BYTES;
 #pragma unroll
-    for (int j = 0; j < SS::W_BYTES / 1024; ++j) dma_1k(wg + 1024 * j, stage + 1024 * j, lane);
-#pragma unroll
-    for (int j = 0; j < SS::K_BYTES / 1024; ++j) dma_1k(kg + 1024 * j, stage + SS::W_BYTES + 1024 * j, lane);
-#pragma unroll
-    for (int j = 0; j < SS::U_BYTES / 1024; ++j)
-        dma_1k(ug + 1024 * j, stage + SS::W_BYTES + SS::K_BYTES + 1024 * j, lane);
-    __builtin_amdgcn_global_load_lds((gptr_t)(p.gc + ch * CHUNK + lane),
-                                     (lptr_t)(stage + SS::W_BYTES + SS::K_BYTES + SS::U_BYTES), 4, 0, 0);
+    for (int j = 0; j < NP; ++j) {
+        if (j % SS::NPW != pw) continue;
+        if ((j < NP / 2) != (part == 0)) continue;
+        if (j < NW)
+            dma_1k(wg + 1024 * j, stage + 1024 * j, lane);
+        else if (j < NW + NK)
+            dma_1k(kg + 1024 * (j - NW), stage + SS::W_BYTES + 1024 * (j - NW), lane);
+        else
+            dma_1k(ug + 1024 * (j - NW - NK), stage + SS::W_BYTES + SS::K_BYTES + 1024 * (j - NW - NK), lane);
+    }
+    if (part == 1 && pw == 0)
+        __builtin_amdgcn_global_load_lds((gptr_t)(p.gc + ch * CHUNK + lane),
+                                         (lptr_t)(stage + SS::W_BYTES + SS::K_BYTES + SS::U_BYTES), 4, 0, 0);
+}
+
+// Loads producer wave pw issues in part 0 of a chunk.
+template <typename T, int D>
+__host__ __device__ constexpr int state_part0_loads(int pw) {
+    using SS = StateStage<T, D>;
+    int n = 0;
+    for (int j = 0; j < SS::NPIECE / 2; ++j) n += (j % SS::NPW == pw) ? 1 : 0;
+    return n;
 }
 
 // Write a D tile's four values (rows 4 grp + i of one 16-row tile) into the
@@ -435,7 +464,7 @@ __device__ __forceinline__ void lds_put4(Frag<T>& f, int half, const f32x4& v, f
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(320) void chunk_state_h_kernel(const ChunkParams p, int padded) {
+__global__ __launch_bounds__(384) void chunk_state_h_kernel(const ChunkParams p, int padded) {
     using SS = StateStage<T, D>;
     constexpr int NT = D / 16;   // column tiles of d_v per head
     constexpr int KS = D / 32;   // contraction steps over d_k
@@ -458,27 +487,34 @@ __global__ __launch_bounds__(320) void chunk_state_h_kernel(const ChunkParams p,
     Frag<T>(*LS)[64] = reinterpret_cast<Frag<T>(*)[64]>(smem + NST * SS::BYTES);           // [KS][64]: -S
     Frag<T>(*LX)[64] = reinterpret_cast<Frag<T>(*)[64]>(smem + NST * SS::BYTES + KS * 64 * sizeof(Frag<T>));  // [2][64]: X
 
-    if (w == 4) {
-        // ---------------- producer ----------------
+    if (w >= 4) {
+        // ---------------- producer waves ----------------
+        const int pw = w - 4;
 #pragma unroll
-        for (int b = 0; b < NST - 1; ++b)
-            if (b < nch) state_issue<T, D>(smem + b * SS::BYTES, p, (size_t)(c0 + b) * p.H_v + h, tile, lane);
+        for (int b = 0; b < NST; ++b)
+            if (b < nch) {
+                state_issue<T, D>(smem + b * SS::BYTES, p, (size_t)(c0 + b) * p.H_v + h, tile, lane, pw, 0);
+                state_issue<T, D>(smem + b * SS::BYTES, p, (size_t)(c0 + b) * p.H_v + h, tile, lane, pw, 1);
+            }
         wait_vmcnt<0>();
-        // The producer's barriers are plain s_barrier: a workgroup release fence
+        // The producers' barriers are plain s_barrier: a workgroup release fence
         // would wait for the direct-to-LDS loads just issued, and the whole point
-        // is that they stay in flight.  Visibility is ensured explicitly: chunk c
-        // is complete (vmcnt) before this wave arrives at B1(c).  The asm's memory
-        // clobber keeps the compiler from moving loads across the barrier.
+        // is that they stay in flight.  Visibility is ensured explicitly: a
+        // chunk's loads have completed (vmcnt) before the producer arrives at
+        // the barrier after which the compute waves read it.  The asm's memory
+        // clobber keeps the compiler from moving loads across a barrier.
+        asm volatile("s_barrier" ::: "memory");  // B0: chunks 0 and 1 in LDS
         for (int c = 0; c < nch; ++c) {
-            asm volatile("s_barrier" ::: "memory");  // B1(c): stage c % NST is complete and visible
-            const int cn = c + NST - 1;
-            if (cn < nch) state_issue<T, D>(smem + (cn % NST) * SS::BYTES, p, (size_t)(c0 + cn) * p.H_v + h, tile, lane);
+            asm volatile("s_barrier" ::: "memory");  // B1(c): chunk c is in registers, its stage free
+            const int cn = c + NST;
+            char* stn = smem + (cn % NST) * SS::BYTES;
+            const size_t chn = (size_t)(c0 + cn) * p.H_v + h;
+            // A chunk's loads go out in two halves, one in each phase of a step.
+            // chunk c + 1 is read after B2(c)
+            wait_vmcnt<0>();
+            if (cn < nch) state_issue<T, D>(stn, p, chn, tile, lane, pw, 0);
             asm volatile("s_barrier" ::: "memory");  // B2(c)
-            // chunk c + 1 must be in LDS before B1(c + 1); the chunk issued above may stay in flight
-            if (NST == 3 && cn < nch)
-                wait_vmcnt<(NST == 3 ? SS::NDMA : 0)>();
-            else
-                wait_vmcnt<0>();
+            if (cn < nch) state_issue<T, D>(stn, p, chn, tile, lane, pw, 1);
         }
         return;
     }
@@ -493,34 +529,41 @@ __global__ __launch_bounds__(320) void chunk_state_h_kernel(const ChunkParams p,
             S[tt][i] = p.s0 ? p.s0[state_off + (size_t)(16 * m + 4 * grp + i) * D + col] : 0.f;
         lds_put4(LS[m >> 1][lane], m & 1, S[tt], -1.f);
     }
-    for (int c = 0; c < nch; ++c) {
-        const int ci = c0 + c;
-        const int ell = min(CHUNK, L_n - c * CHUNK);
-        const size_t ch = (size_t)ci * p.H_v + h;
+    // Operand fragments of one chunk, read from its LDS stage.
+    Frag<T> wf[KS], kf[TPW][2];
+    Raw4<T> uf;
+    float gl = 0.f;
+    auto read_stage = [&](int c) {
         const char* st = smem + (c % NST) * SS::BYTES;
         const Frag<T>* Wst = reinterpret_cast<const Frag<T>*>(st);
         const Frag<T>* Kst = reinterpret_cast<const Frag<T>*>(st + SS::W_BYTES);
         const Raw4<T>* Ust = reinterpret_cast<const Raw4<T>*>(st + SS::W_BYTES + SS::K_BYTES);
         const float* Gst = reinterpret_cast<const float*>(st + SS::W_BYTES + SS::K_BYTES + SS::U_BYTES);
-        __syncthreads();  // B1(c): -S in LS, stage c ready
-        Frag<T> wf[KS], sb[KS], kf[TPW][2];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            wf[ks] = Wst[(w * KS + ks) * 64 + lane];
-            sb[ks] = LS[ks][lane];
-        }
+        for (int ks = 0; ks < KS; ++ks) wf[ks] = Wst[(w * KS + ks) * 64 + lane];
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) kf[tt][ks] = Kst[((w * TPW + tt) * 2 + ks) * 64 + lane];
-        const Raw4<T> uf = Ust[w * 64 + lane];
-        const float eg = __expf(Gst[ell - 1]);
-
-        // h_c = S (this wave's rows), stored transposed [d_v][d_k]
-        T* Hb = reinterpret_cast<T*>(p.Ht) + (ch * D + col) * D;
+        uf = Ust[w * 64 + lane];
+        gl = Gst[min(CHUNK, L_n - c * CHUNK) - 1];
+    };
+    auto store_h = [&](int c) {  // chunk-start state h_c = S (this wave's rows), transposed [d_v][d_k]
+        T* Hb = reinterpret_cast<T*>(p.Ht) + (((size_t)(c0 + c) * p.H_v + h) * D + col) * D;
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt)
             store4(Hb + 16 * (w * TPW + tt) + 4 * grp, S[tt][0], S[tt][1], S[tt][2], S[tt][3]);
+    };
+    if (nch > 0) store_h(0);
+    lds_sync();  // B0: stages 0 and 1 ready
+    if (nch > 0) read_stage(0);
+    for (int c = 0; c < nch; ++c) {
+        const int ci = c0 + c;
+        const size_t ch = (size_t)ci * p.H_v + h;
+        lds_sync();  // B1(c): -S in LS; chunk c's stage may be refilled
+        Frag<T> sb[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sb[ks] = LS[ks][lane];
         // X = U - W S for positions 16 w .. 16 w + 15
         f32x4 X = raw4_to_f32(uf);
 #pragma unroll
@@ -528,20 +571,29 @@ __global__ __launch_bounds__(320) void chunk_state_h_kernel(const ChunkParams p,
         T* Xb = reinterpret_cast<T*>(p.Xt) + (ch * D + col) * CHUNK;
         store4(Xb + perm32(16 * w + 4 * grp), X[0], X[1], X[2], X[3]);
         lds_put4(LX[w >> 1][lane], w & 1, X, 1.f);
+        const float eg = __expf(gl);
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) S[tt] *= eg;
-        __syncthreads();  // B2(c): all of X in LX
+        Frag<T> kc[TPW][2];
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+            kc[tt][0] = kf[tt][0];
+            kc[tt][1] = kf[tt][1];
+        }
+        lds_sync();  // B2(c): all of X in LX; stage c + 1 ready
+        if (c + 1 < nch) read_stage(c + 1);
         const Frag<T> xb0 = LX[0][lane], xb1 = LX[1][lane];
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
-            S[tt] = mma(kf[tt][0], xb0, S[tt]);
-            S[tt] = mma(kf[tt][1], xb1, S[tt]);
+            S[tt] = mma(kc[tt][0], xb0, S[tt]);
+            S[tt] = mma(kc[tt][1], xb1, S[tt]);
         }
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
             const int m = w * TPW + tt;
             lds_put4(LS[m >> 1][lane], m & 1, S[tt], -1.f);
         }
+        if (c + 1 < nch) store_h(c + 1);
     }
     if (p.sfinal) {
 #pragma unroll
@@ -613,7 +665,7 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
         *reinterpret_cast<float4*>(&s.K[r][c]) = ok ? *reinterpret_cast<const float4*>(kb + off) : make_float4(0, 0, 0, 0);
     }
     if (tid < CHUNK) s.gc[tid] = p.gc[ch * CHUNK + tid];
-    __syncthreads();
+    lds_sync();
 
     // P^T tiles (I, J = w) for I <= w, published as B fragments for query tile w.
     {
@@ -649,7 +701,7 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
             }
         }
     }
-    __syncthreads();
+    lds_sync();
 
     // Output tiles: rows d_v (this wave's tiles), columns pos.
     T* ob = reinterpret_cast<T*>(p.out) + (size_t)cp.t0 * p.H_v * D + (size_t)h * D;
@@ -701,7 +753,7 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
             hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, stream, p, grid);
     };
     if (work_ch > 0) launch(0, chunk_prep_kernel<T, D>, grid_ch, 256);
-    if (work_st > 0) launch(1, chunk_state_h_kernel<T, D>, grid_st, 320);
+    if (work_st > 0) launch(1, chunk_state_h_kernel<T, D>, grid_st, 64 * (4 + StateStage<T, D>::NPW));
     if (work_ch > 0) launch(2, chunk_output_o_kernel<T, D>, grid_ch, 256);
     return hipGetLastError();
 }

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(const DecodeParams 
 #pragma unroll
         for (int e = 0; e < NV; ++e) s_red[w][lane][e] = red[e];
     }
-    __syncthreads();
+    lds_sync();
 #pragma unroll
     for (int e = 0; e < NV; ++e) red[e] = s_red[0][cg][e] + s_red[1][cg][e] + s_red[2][cg][e] + s_red[3][cg][e];
     (void)RGW;

@@ -168,6 +168,21 @@ __host__ __device__ __forceinline__ int perm32(int i) {
 // L2.  `padded` is the grid size, a multiple of 8.
 __device__ __forceinline__ int xcd_remap(int i, int padded) { return (i & 7) * (padded >> 3) + (i >> 3); }
 
+// ---- workgroup barrier ---------------------------------------------------
+// s_waitcnt lgkmcnt(0): this wave's LDS operations have completed.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+// Workgroup barrier that publishes this wave's LDS writes.  The release fence
+// of __syncthreads() emits no LDS wait when only LDS ordering is at stake (the
+// compiler takes LDS operations of all waves to be performed in one global
+// order); on gfx950, with direct-to-LDS loads streaming into the same LDS, a
+// ds_write issued before s_barrier was observed to be missed by another wave's
+// ds_read issued after it.  Every barrier here therefore waits explicitly.
+__device__ __forceinline__ void lds_sync() {
+    wait_lgkmcnt0();
+    __syncthreads();
+}
+
 // ---- wave helpers --------------------------------------------------------
 __device__ __forceinline__ float wave_shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
 

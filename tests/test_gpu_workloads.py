@@ -70,6 +70,28 @@ def test_long_T65536_sampled_heads(torch_cuda, oracle_mod):
     _check(oracle_mod, inp, out, fin, [0, 17, 31], 1e-2)
 
 
+def test_long_T65536_bitwise_repeatable(torch_cuda):
+    """Two forwards of the 65536-token workload give bit-identical outputs and
+    final states: 1024 serial chunk steps per head make any ordering race
+    between the state kernel's waves show up here (the method is deterministic,
+    so is every kernel: no atomics, fixed reduction orders)."""
+    import gated_deltanet_state_chunk_amd as gdn
+
+    torch = torch_cuda
+    inp = gdn_inputs.make_workload("long_T65536")
+    q, k, v = (to_dev(a, inp.dtype) for a in (inp.q, inp.k, inp.v))
+    g, beta = f32_dev(inp.g), f32_dev(inp.beta)
+    ws = torch.empty(gdn.workspace_size(inp.T, inp.cu_seqlens, inp.H_q, inp.H_v, inp.d_k, inp.d_v, inp.dtype),
+                     dtype=torch.uint8, device="cuda")
+    s0 = None if inp.initial_state is None else f32_dev(inp.initial_state)
+    res = [gdn.chunk_fwd(q, k, v, g, beta, inp.cu_seqlens, initial_state=s0, scale=inp.scale, workspace=ws)
+           for _ in range(3)]
+    torch.cuda.synchronize()
+    for out, fin in res[1:]:
+        assert torch.equal(out, res[0][0])
+        assert torch.equal(fin, res[0][1])
+
+
 def test_decode_256x16_steps(torch_cuda, oracle_mod):
     import gated_deltanet_state_chunk_amd as gdn
 
