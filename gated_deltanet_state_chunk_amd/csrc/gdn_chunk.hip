@@ -359,8 +359,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
 
 // ---------------------------------------------------------------------------
 // 3. chunk_state_h: one workgroup per (sequence, value head, 16-column tile of
-//    d_v), serial over the sequence's chunks; four compute waves (one per SIMD)
-//    and two producer waves.
+//    d_v), serial over the sequence's chunks: four compute waves (one per
+//    SIMD), NPW producer waves (one; two for fp32 at d = 128) and one store
+//    wave.
 //
 //    Compute waves.  The fp32 state slice S[:, tile] (d_k x 16) stays in MFMA
 //    accumulators, split by rows over the waves.  Per chunk:
@@ -368,15 +369,22 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
 //      S = gamma_l S + Kd^T X   wave w: its rows of S, contraction over positions
 //    The two products exchange bf16 copies of -S and X through LDS in MFMA
 //    operand order (one 16-byte access per lane and fragment), two barriers a
-//    chunk, and read their operands from the LDS stage of that chunk.
+//    chunk (B1 before X, B2 before the state update).  A chunk's W, Kd, U and
+//    gate fragments are copied from its LDS stage into registers during the
+//    second half of the previous step.  The compute waves issue no global
+//    memory instruction inside the loop: a vector-memory instruction stalls
+//    its wave whenever the CU's memory pipeline is backed up, and on this
+//    serial path every stall delays the next barrier for all waves.
 //
-//    Producer waves.  Two waves stream each chunk's W, Kd, U and gate blocks
-//    (stored by chunk_prep in exactly the LDS stage order) into a ring of NST
-//    stages with direct global->LDS loads, up to NST - 1 chunks ahead, so the
-//    compute waves never issue a global load: the per-chunk operands (about
-//    34 KiB) would otherwise stall their instruction stream.  Two producers,
-//    because one wave can keep only 63 memory operations in flight, which caps
-//    its stream at about 26 B/clk; the CU sustains more with more requests out.
+//    Producer waves.  Stream each chunk's W, Kd, U and gate blocks (stored by
+//    chunk_prep in exactly the LDS stage order) into a ring of NST stages
+//    (three where they fit) with direct global->LDS loads.  A stage is free
+//    once its chunk is in registers (B1 of that chunk's step); chunk c + NST
+//    goes out in two halves, at B1(c) and B2(c); vmcnt waits make chunk c + 1
+//    land before B2(c) and keep at most 63 loads in flight per wave.
+//
+//    Store wave.  Copies h_c (the sign-flipped -S of LS, between B1(c) and
+//    B2(c)) and X_c (LX, between B2(c) and B1(c + 1)) to HBM.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct StateStage {
@@ -394,7 +402,8 @@ struct StateStage {
     static constexpr int PER_WAVE = (NPIECE + NPW - 1) / NPW + 1;           // upper bound incl. the gate load
     // Two LDS stages: the compute waves copy chunk c into registers before
     // B1(c), so stage c % 2 is refilled with chunk c + 2 from B1(c) on.
-    static constexpr int NST = 2;
+    static constexpr int LDS_CAP = 160 * 1024;
+    static constexpr int NST = (3 * BYTES + EXCH <= LDS_CAP) ? 3 : 2;
 };
 
 typedef __attribute__((address_space(1))) const void* gptr_t;
@@ -411,6 +420,35 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS reads the compiler does not track.  The producer reads the compute
+// waves' exchange buffers while its own direct-to-LDS loads are in flight; a
+// plain LDS load there makes the compiler wait for all of those loads (it
+// cannot tell the buffers apart), so the producer reads with inline asm and
+// waits for the results itself (lds_wait_untracked) before using them.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// N 16-byte reads: piece i of element j at addr + j * stride + 16 * i (n pieces an element).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+template <int N>
+__device__ __forceinline__ void lds_read_untracked(u32x4* r, unsigned addr, unsigned stride, int n) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const unsigned a = addr + (k / n) * stride + 16 * (k % n);
+        asm volatile("ds_read_b128 %0, %1" : "=v"(r[k]) : "v"(a));
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void lds_wait_untracked(u32x4* r) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < N; ++k) asm volatile("" : "+v"(r[k]));  // uses of r stay after the wait
 }
 
 // Issue this producer wave's share (pieces j with j % NPW == pw) of one
@@ -442,15 +480,25 @@ __device__ __forceinline__ void state_issue(char* stage, const ChunkParams& p, s
                                          (lptr_t)(stage + SS::W_BYTES + SS::K_BYTES + SS::U_BYTES), 4, 0, 0);
 }
 
-// Loads producer wave pw issues in part 0 of a chunk.
+// Loads producer wave pw issues in part 0 / part 1 of a chunk (part 1
+// includes the gate load of wave 0).
 template <typename T, int D>
-__host__ __device__ constexpr int state_part0_loads(int pw) {
+__host__ __device__ constexpr int state_part_loads(int pw, int part) {
     using SS = StateStage<T, D>;
     int n = 0;
-    for (int j = 0; j < SS::NPIECE / 2; ++j) n += (j % SS::NPW == pw) ? 1 : 0;
-    return n;
+    for (int j = 0; j < SS::NPIECE; ++j) n += (j % SS::NPW == pw && (j < SS::NPIECE / 2) == (part == 0)) ? 1 : 0;
+    return n + (part == 1 && pw == 0 ? 1 : 0);
 }
 
+// vmcnt bounds of producer wave pw: ops younger than chunk c + 1's last load
+// when part 0 of chunk c + NST has just gone out (chunks c + 2 .. c + NST - 1
+// whole, plus that part 0), and the in-flight ceiling before part 1 goes out.
+template <typename T, int D>
+__host__ __device__ constexpr int state_wait_b2(int pw) {
+    using SS = StateStage<T, D>;
+    return (SS::NST - 2) * (state_part_loads<T, D>(pw, 0) + state_part_loads<T, D>(pw, 1)) +
+           state_part_loads<T, D>(pw, 0);
+}
 // Write a D tile's four values (rows 4 grp + i of one 16-row tile) into the
 // perm32 fragment they belong to: even tile -> slots 0..3, odd -> slots 4..7.
 template <typename T>
@@ -464,7 +512,7 @@ __device__ __forceinline__ void lds_put4(Frag<T>& f, int half, const f32x4& v, f
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(384) void chunk_state_h_kernel(const ChunkParams p, int padded) {
+__global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p, int padded) {
     using SS = StateStage<T, D>;
     constexpr int NT = D / 16;   // column tiles of d_v per head
     constexpr int KS = D / 32;   // contraction steps over d_k
@@ -487,16 +535,73 @@ __global__ __launch_bounds__(384) void chunk_state_h_kernel(const ChunkParams p,
     Frag<T>(*LS)[64] = reinterpret_cast<Frag<T>(*)[64]>(smem + NST * SS::BYTES);           // [KS][64]: -S
     Frag<T>(*LX)[64] = reinterpret_cast<Frag<T>(*)[64]>(smem + NST * SS::BYTES + KS * 64 * sizeof(Frag<T>));  // [2][64]: X
 
+    if (w >= 4 + SS::NPW) {
+        // ---------------- store wave ----------------
+        // Writes the chunk-start states and X to HBM from the compute waves'
+        // exchange buffers, so that no global store sits in the compute waves'
+        // instruction stream: between B1(c) and B2(c) LS holds bf16(-h_c),
+        // between B2(c) and B1(c + 1) LX holds X_c, both in the perm32
+        // fragment order (slots 0..3: rows 4g..4g+3 of a 32-row block, slots
+        // 4..7: rows 16+4g..16+4g+3, g = lane / 16; column lane % 16).
+        constexpr int FQ = sizeof(Frag<T>) / 16;  // 16-byte pieces per fragment
+        const unsigned sgn = sizeof(T) == 2 ? 0x80008000u : 0x80000000u;
+        const unsigned ls_addr = lds_addr(&LS[0][lane]), lx_addr = lds_addr(&LX[0][lane]);
+        asm volatile("s_barrier" ::: "memory");  // B0
+        for (int c = 0; c < nch; ++c) {
+            const size_t ch = (size_t)(c0 + c) * p.H_v + h;
+            asm volatile("s_barrier" ::: "memory");  // B1(c)
+            u32x4 hs[KS][FQ];
+            lds_read_untracked<KS * FQ>(&hs[0][0], ls_addr, 64 * sizeof(Frag<T>), FQ);
+            lds_wait_untracked<KS * FQ>(&hs[0][0]);
+            T* Hb = reinterpret_cast<T*>(p.Ht) + ((ch * D + col) * D);  // h_c = -(LS): a sign flip, exact
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if constexpr (sizeof(T) == 2) {
+                    const u32x4 u = hs[ks][0];
+                    *reinterpret_cast<u32x2*>(Hb + 32 * ks + 4 * grp) = u32x2{u.x ^ sgn, u.y ^ sgn};
+                    *reinterpret_cast<u32x2*>(Hb + 32 * ks + 16 + 4 * grp) = u32x2{u.z ^ sgn, u.w ^ sgn};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+                        *reinterpret_cast<u32x4*>(Hb + 32 * ks + 16 * e + 4 * grp) = hs[ks][e] ^ sgn;
+                }
+            }
+            asm volatile("s_barrier" ::: "memory");  // B2(c)
+            u32x4 xs[2][FQ];
+            lds_read_untracked<2 * FQ>(&xs[0][0], lx_addr, 64 * sizeof(Frag<T>), FQ);
+            lds_wait_untracked<2 * FQ>(&xs[0][0]);
+            T* Xb = reinterpret_cast<T*>(p.Xt) + (ch * D + col) * CHUNK;  // X_c, already in the stored perm32 order
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < FQ; ++e)
+                    *reinterpret_cast<u32x4*>(Xb + 32 * j + 8 * grp + e * (16 / (int)sizeof(T))) = xs[j][e];
+        }
+        return;
+    }
     if (w >= 4) {
         // ---------------- producer waves ----------------
-        const int pw = w - 4;
+        const int pw = __builtin_amdgcn_readfirstlane(w - 4);  // wave-uniform: scalar branches
+        // Outstanding-load bounds (vmcnt counts at most 63): before k loads go
+        // out at most 63 - k may be in flight (R*_), and at B2(c) chunk c + 1
+        // must have landed (WB_).
+        constexpr int WB_0 = state_wait_b2<T, D>(0), WB_1 = state_wait_b2<T, D>(1);
+        constexpr int R0_0 = 63 - state_part_loads<T, D>(0, 0), R0_1 = 63 - state_part_loads<T, D>(1, 0);
+        constexpr int R1_0 = 63 - state_part_loads<T, D>(0, 1), R1_1 = 63 - state_part_loads<T, D>(1, 1);
+        constexpr int RC_0 = R0_0 - state_part_loads<T, D>(0, 1), RC_1 = R0_1 - state_part_loads<T, D>(1, 1);
+        static_assert(WB_0 < 64 && WB_1 < 64 && RC_0 >= 0 && RC_1 >= 0, "producer loads exceed the vmcnt range");
+        // Chunks 0 .. NST-1 up front; chunk 0 lands before B0.
 #pragma unroll
-        for (int b = 0; b < NST; ++b)
+        for (int b = 0; b < NST; ++b) {
+            if (b == 1) wait_vmcnt<0>();
+            if (b == 2) {
+                if (pw == 0) wait_vmcnt<RC_0>(); else wait_vmcnt<RC_1>();
+            }
             if (b < nch) {
                 state_issue<T, D>(smem + b * SS::BYTES, p, (size_t)(c0 + b) * p.H_v + h, tile, lane, pw, 0);
                 state_issue<T, D>(smem + b * SS::BYTES, p, (size_t)(c0 + b) * p.H_v + h, tile, lane, pw, 1);
             }
-        wait_vmcnt<0>();
+        }
         // The producers' barriers are plain s_barrier: a workgroup release fence
         // would wait for the direct-to-LDS loads just issued, and the whole point
         // is that they stay in flight.  Visibility is ensured explicitly: a
@@ -509,12 +614,20 @@ __global__ __launch_bounds__(384) void chunk_state_h_kernel(const ChunkParams p,
             const int cn = c + NST;
             char* stn = smem + (cn % NST) * SS::BYTES;
             const size_t chn = (size_t)(c0 + cn) * p.H_v + h;
-            // A chunk's loads go out in two halves, one in each phase of a step.
-            // chunk c + 1 is read after B2(c)
-            wait_vmcnt<0>();
-            if (cn < nch) state_issue<T, D>(stn, p, chn, tile, lane, pw, 0);
+            // A chunk's loads go out in two halves, one in each phase of a step;
+            // chunk c + 1 is read after B2(c).
+            if (cn < nch) {
+                if (pw == 0) wait_vmcnt<R0_0>(); else wait_vmcnt<R0_1>();
+                state_issue<T, D>(stn, p, chn, tile, lane, pw, 0);
+                if (pw == 0) wait_vmcnt<WB_0>(); else wait_vmcnt<WB_1>();
+            } else {
+                wait_vmcnt<0>();
+            }
             asm volatile("s_barrier" ::: "memory");  // B2(c)
-            if (cn < nch) state_issue<T, D>(stn, p, chn, tile, lane, pw, 1);
+            if (cn < nch) {
+                if (pw == 0) wait_vmcnt<R1_0>(); else wait_vmcnt<R1_1>();
+                state_issue<T, D>(stn, p, chn, tile, lane, pw, 1);
+            }
         }
         return;
     }
@@ -548,18 +661,9 @@ __global__ __launch_bounds__(384) void chunk_state_h_kernel(const ChunkParams p,
         uf = Ust[w * 64 + lane];
         gl = Gst[min(CHUNK, L_n - c * CHUNK) - 1];
     };
-    auto store_h = [&](int c) {  // chunk-start state h_c = S (this wave's rows), transposed [d_v][d_k]
-        T* Hb = reinterpret_cast<T*>(p.Ht) + (((size_t)(c0 + c) * p.H_v + h) * D + col) * D;
-#pragma unroll
-        for (int tt = 0; tt < TPW; ++tt)
-            store4(Hb + 16 * (w * TPW + tt) + 4 * grp, S[tt][0], S[tt][1], S[tt][2], S[tt][3]);
-    };
-    if (nch > 0) store_h(0);
     lds_sync();  // B0: stages 0 and 1 ready
     if (nch > 0) read_stage(0);
     for (int c = 0; c < nch; ++c) {
-        const int ci = c0 + c;
-        const size_t ch = (size_t)ci * p.H_v + h;
         lds_sync();  // B1(c): -S in LS; chunk c's stage may be refilled
         Frag<T> sb[KS];
 #pragma unroll
@@ -568,8 +672,6 @@ __global__ __launch_bounds__(384) void chunk_state_h_kernel(const ChunkParams p,
         f32x4 X = raw4_to_f32(uf);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) X = mma(wf[ks], sb[ks], X);
-        T* Xb = reinterpret_cast<T*>(p.Xt) + (ch * D + col) * CHUNK;
-        store4(Xb + perm32(16 * w + 4 * grp), X[0], X[1], X[2], X[3]);
         lds_put4(LX[w >> 1][lane], w & 1, X, 1.f);
         const float eg = __expf(gl);
 #pragma unroll
@@ -593,7 +695,6 @@ __global__ __launch_bounds__(384) void chunk_state_h_kernel(const ChunkParams p,
             const int m = w * TPW + tt;
             lds_put4(LS[m >> 1][lane], m & 1, S[tt], -1.f);
         }
-        if (c + 1 < nch) store_h(c + 1);
     }
     if (p.sfinal) {
 #pragma unroll
@@ -753,7 +854,7 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
             hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, stream, p, grid);
     };
     if (work_ch > 0) launch(0, chunk_prep_kernel<T, D>, grid_ch, 256);
-    if (work_st > 0) launch(1, chunk_state_h_kernel<T, D>, grid_st, 64 * (4 + StateStage<T, D>::NPW));
+    if (work_st > 0) launch(1, chunk_state_h_kernel<T, D>, grid_st, 64 * (5 + StateStage<T, D>::NPW));
     if (work_ch > 0) launch(2, chunk_output_o_kernel<T, D>, grid_ch, 256);
     return hipGetLastError();
 }
