@@ -10,7 +10,7 @@ each step) is measured in the same run and reported under "decode".
 
 Prints ONE JSON line.  Timing: W untimed warm-up steps, then K timed steps of
 the product entry point between two device synchronisations (value,
-ms_per_step), then the same K steps again through gdn_chunk_fwd_timed, whose
+ms_per_step), then the same K steps again through gdn_chunk_fwd_ex, whose
 start/stop HIP events are stamped by each kernel's own dispatch (per-kernel
 durations for the roofline; the events themselves cost ~15 us a step, so they
 are kept out of the first pass).  "roofline" reports the slowest kernel of the step against the
@@ -52,7 +52,8 @@ def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True):
     """Algorithmic bytes and flops of each kernel of one gdn_chunk_fwd.
 
     Bytes: every distinct input read once, every output and intermediate written
-    once and read once per consuming kernel (K is read once per key head).
+    once and read once per consuming kernel (K is read once per key head); A is
+    consumed inside chunk_prep and never written (gdn_chunk_fwd does not keep it).
     Flops: 2 x multiply-adds of the chunk form at full chunks, triangles exploited.
     """
     C = CHUNK
@@ -61,7 +62,6 @@ def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True):
     v_b = o_b = T * H_v * d * es
     gate_b = T * H_v * 4  # g or beta
     gc_b = chv * C * 4
-    A_b = chv * C * C * es
     W_b = U_b = X_b = Kd_b = chv * C * d * es
     H_b = chv * d * d * es
     S_b = N * H_v * d * d * 4
@@ -73,7 +73,7 @@ def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True):
         "chunk_output_o": C * d * d + 2 * tri1 * d,          # Q S, Q K^T, P X
     }
     bytes_ = {
-        "chunk_prep": k_b + v_b + 2 * gate_b + gc_b + A_b + W_b + U_b + Kd_b,
+        "chunk_prep": k_b + v_b + 2 * gate_b + gc_b + W_b + U_b + Kd_b,   # A stays on chip
         "chunk_state_h": W_b + U_b + Kd_b + gc_b + (S_b if has_s0 else 0) + H_b + X_b + S_b,
         "chunk_output_o": q_b + k_b + gc_b + H_b + X_b + o_b,
     }
@@ -190,12 +190,12 @@ def bench_prefill(args, torch, gdn, hip, device):
         arr = None
         if events is not None:
             arr = (ctypes.c_void_p * NEV)(*[e.value for e in events])
-        rc = lib.gdn_chunk_fwd_timed(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), cu,
-                                     inp.N, None if s0 is None else s0.data_ptr(), out.data_ptr(), fin.data_ptr(),
-                                     inp.T, inp.H_q, inp.H_v, inp.d_k, inp.d_v, inp.scale, code, ws.data_ptr(),
-                                     lay["total_bytes"], ctypes.c_void_p(sptr), arr)
+        rc = lib.gdn_chunk_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), cu,
+                                  inp.N, None if s0 is None else s0.data_ptr(), out.data_ptr(), fin.data_ptr(),
+                                  inp.T, inp.H_q, inp.H_v, inp.d_k, inp.d_v, inp.scale, code, ws.data_ptr(),
+                                  lay["total_bytes"], ctypes.c_void_p(sptr), 0, arr)
         if rc != 0:
-            raise gdn.GdnError(rc, "gdn_chunk_fwd_timed")
+            raise gdn.GdnError(rc, "gdn_chunk_fwd_ex")
 
     for _ in range(args.warmup):
         step()

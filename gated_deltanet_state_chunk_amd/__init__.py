@@ -26,6 +26,7 @@ _lib = None
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+FWD_KEEP_A = 1  # gdn_chunk_fwd_ex flag: also write A to the workspace
 
 _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace", -4: "hip"}
 
@@ -73,8 +74,8 @@ def load_library():
     lib.gdn_chunk_fwd.argtypes = [P, P, P, P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P,
                                   ctypes.c_size_t, P]
     lib.gdn_chunk_fwd.restype = ctypes.c_int
-    lib.gdn_chunk_fwd_timed.argtypes = lib.gdn_chunk_fwd.argtypes + [P]
-    lib.gdn_chunk_fwd_timed.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_ex.argtypes = lib.gdn_chunk_fwd.argtypes + [ctypes.c_uint32, P]
+    lib.gdn_chunk_fwd_ex.restype = ctypes.c_int
     lib.gdn_recurrent_step.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P]
     lib.gdn_recurrent_step.restype = ctypes.c_int
     _lib = lib
@@ -160,14 +161,16 @@ def workspace_size(T: int, cu_seqlens, H_q: int, H_v: int, d_k: int, d_v: int, d
 # ---------------------------------------------------------------------------
 
 def chunk_fwd(q, k, v, g, beta, cu_seqlens: Sequence[int], initial_state=None, scale: Optional[float] = None,
-              out=None, final_state=None, output_final_state: bool = True, workspace=None, stream=None):
-    """Chunk-wise GDN prefill over a packed batch (gdn_chunk_fwd).
+              out=None, final_state=None, output_final_state: bool = True, workspace=None, stream=None,
+              keep_A: bool = False):
+    """Chunk-wise GDN prefill over a packed batch (gdn_chunk_fwd; gdn_chunk_fwd_ex with keep_A).
 
     q, k: [T, H_q, d_k]; v: [T, H_v, d_v] (bf16 or fp32, same dtype); g, beta:
     [T, H_v] fp32 (g = ln alpha per token); cu_seqlens: host int sequence [N+1];
     initial_state: fp32 [N, H_v, d_k, d_v] or None.  Returns (out, final_state)
     with final_state None when output_final_state is False.  ``workspace`` may
-    be a preallocated uint8 device tensor of at least workspace_size() bytes.
+    be a preallocated uint8 device tensor of at least workspace_size() bytes;
+    keep_A also writes the A intermediate into it (GDN_FWD_KEEP_A).
     """
     torch = _torch()
     lib = load_library()
@@ -205,11 +208,15 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens: Sequence[int], initial_state=None, s
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     else:
         _check_dev("workspace", workspace)
-    rc = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), cu, N, _ptr(initial_state), _ptr(out),
-                           _ptr(final_state), T, H_q, H_v, d_k, d_v, float(scale), dt, _ptr(workspace),
-                           workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), cu, N, _ptr(initial_state), _ptr(out),
+            _ptr(final_state), T, H_q, H_v, d_k, d_v, float(scale), dt, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    if keep_A:
+        rc, name = lib.gdn_chunk_fwd_ex(*args, FWD_KEEP_A, None), "gdn_chunk_fwd_ex"
+    else:
+        rc, name = lib.gdn_chunk_fwd(*args), "gdn_chunk_fwd"
     if rc != 0:
-        raise GdnError(rc, "gdn_chunk_fwd")
+        raise GdnError(rc, name)
     return out, final_state
 
 

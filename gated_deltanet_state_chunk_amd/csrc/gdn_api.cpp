@@ -124,15 +124,16 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                   const int32_t* cu_seqlens_host, int32_t num_seqs, const float* initial_state, void* out,
                   float* final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
                   gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
-    return gdn_chunk_fwd_timed(q, k, v, g, beta, cu_seqlens_host, num_seqs, initial_state, out, final_state, T, H_q,
-                               H_v, d_k, d_v, scale, dtype, workspace, workspace_bytes, stream, nullptr);
+    return gdn_chunk_fwd_ex(q, k, v, g, beta, cu_seqlens_host, num_seqs, initial_state, out, final_state, T, H_q, H_v,
+                            d_k, d_v, scale, dtype, workspace, workspace_bytes, stream, 0u, nullptr);
 }
 
-int gdn_chunk_fwd_timed(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                        const int32_t* cu_seqlens_host, int32_t num_seqs, const float* initial_state, void* out,
-                        float* final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v,
-                        float scale, gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream,
-                        void* const* stage_events) {
+int gdn_chunk_fwd_ex(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                     const int32_t* cu_seqlens_host, int32_t num_seqs, const float* initial_state, void* out,
+                     float* final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
+                     gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream, uint32_t flags,
+                     void* const* stage_events) {
+    if (flags & ~(uint32_t)GDN_FWD_KEEP_A) return GDN_ERR_INVALID;
     gdn_workspace_layout L;
     int rc = gdn_chunk_fwd_workspace_layout(T, num_seqs, cu_seqlens_host, H_q, H_v, d_k, d_v, dtype, &L);
     if (rc != GDN_OK) return rc;
@@ -153,6 +154,7 @@ int gdn_chunk_fwd_timed(const void* q, const void* k, const void* v, const float
     p.A = ws + L.off_A; p.W = ws + L.off_W; p.Ut = ws + L.off_U; p.Kt = ws + L.off_Kd;
     p.Ht = ws + L.off_Ht; p.Xt = ws + L.off_Xt;
     p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
+    p.keep_A = (flags & GDN_FWD_KEEP_A) ? 1 : 0;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     // Launch groups of up to MAX_SEQS_PER_LAUNCH sequences, each with its table in the kernel arguments.

@@ -99,8 +99,9 @@ __host__ __device__ __forceinline__ int frag_u_offset(int col_tile, int pos_tile
 //      L  = StrictLower(B Gamma K K^T Gamma^-1),  A = (I + L)^-1   (fp32)
 //      W  = A B Gamma K,  U = A B V,  Kd = diag(gamma_l / gamma) K
 //    K is staged in LDS once and serves K K^T, W and Kd; V is prefetched into
-//    registers and staged after the solve (in the space L occupied).  gc and A
-//    are also written to the workspace (for inspection); W, U and Kd are
+//    registers and staged after the solve (in the space L occupied).  gc is
+//    written to the workspace, and A too when the caller asks for it (it is
+//    for inspection only: nothing downstream reads it); W, U and Kd are
 //    written in the fragment order chunk_state_h streams into LDS
 //    (frag_w_offset / frag_u_offset / frag_k_offset).
 // ---------------------------------------------------------------------------
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
         const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
         *reinterpret_cast<float4*>(&s.u.V[r][c]) = vreg[j];
     }
-    {
+    if (p.keep_A) {
         T* Ab = reinterpret_cast<T*>(p.A) + ch * CHUNK * CHUNK;
         const int i = tid >> 2, jb = tid & 3;  // row i, column block jb
         const float* src = As + blk(i >> 4, jb) + (i & 15) * BS;
@@ -300,11 +301,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
     // W^T tiles: rows d_k (this wave's tiles), columns pos.  A is lower triangular,
     // so column tile nt only needs contraction steps ks with 32 ks <= 16 nt + 15.
     T* Wb = reinterpret_cast<T*>(p.W) + ch * CHUNK * D;
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-        const int mt = w * TPW + tt;
+    auto w_kfrag = [&](Frag<T>(&kf)[2], int mt) {  // (B Gamma K)^T rows of d_k tile mt, contraction pos
         const int dk = 16 * mt + r16;
-        Frag<T> kf[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -312,14 +310,35 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
                 const int r = 32 * ks + 8 * grp + j;
                 frag_set(kf[ks], j, s.sk[r] * to_f32<T>(s.K[r][dk]));
             }
+    };
+    // lane: column pos = 16 nt + r16, rows d_k = 16 mt + 4 grp + i: in fragment
+    // order this is fragment (pos tile nt, K-step mt / 2), same lane, slots 4 (mt % 2) + i
+    if constexpr (TPW == 2) {  // this wave's two d_k tiles fill whole fragments: 16-byte stores
+        Frag<T> k0[2], k1[2];
+        w_kfrag(k0, 2 * w);
+        w_kfrag(k1, 2 * w + 1);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-            f32x4 c = zero4();
-            c = mma(kf[0], Af[nt][0], c);
-            if (nt >= 2) c = mma(kf[1], Af[nt][1], c);
-            // lane: column pos = 16 nt + r16, rows d_k = 16 mt + 4 grp + i: in fragment
-            // order this is fragment (pos tile nt, K-step mt / 2), same lane, slots 4 (mt % 2) + i
-            store4(Wb + frag_w_offset<D>(nt, mt >> 1, lane) + 4 * (mt & 1), c[0], c[1], c[2], c[3]);
+            f32x4 c0 = mma(k0[0], Af[nt][0], zero4()), c1 = mma(k1[0], Af[nt][0], zero4());
+            if (nt >= 2) {
+                c0 = mma(k0[1], Af[nt][1], c0);
+                c1 = mma(k1[1], Af[nt][1], c1);
+            }
+            store8(Wb + frag_w_offset<D>(nt, w, lane), c0, c1);
+        }
+    } else {
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+            const int mt = w * TPW + tt;
+            Frag<T> kf[2];
+            w_kfrag(kf, mt);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                f32x4 c = zero4();
+                c = mma(kf[0], Af[nt][0], c);
+                if (nt >= 2) c = mma(kf[1], Af[nt][1], c);
+                store4(Wb + frag_w_offset<D>(nt, mt >> 1, lane) + 4 * (mt & 1), c[0], c[1], c[2], c[3]);
+            }
         }
     }
     // U tiles: rows pos, columns d_v (this wave's tiles).
@@ -345,14 +364,19 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
             store4(Ub + frag_u_offset(nt, mt, lane), c[0], c[1], c[2], c[3]);
         }
     }
-    // Decayed keys of the state update, transposed.
+    // Decayed keys of the state update, transposed: item (dk, s, a) covers the
+    // 8 positions 32 s + 16 h + 4 a + b (h, b) that are consecutive in fragment order.
     {
         T* Kb = reinterpret_cast<T*>(p.Kt) + ch * D * CHUNK;
-        for (int e = tid; e < D * (CHUNK / 4); e += 256) {
-            const int dk = e / (CHUNK / 4), r4 = (e % (CHUNK / 4)) * 4;
-            store4(Kb + frag_k_offset(dk, r4), s.kd[r4] * to_f32<T>(s.K[r4][dk]),
-                   s.kd[r4 + 1] * to_f32<T>(s.K[r4 + 1][dk]), s.kd[r4 + 2] * to_f32<T>(s.K[r4 + 2][dk]),
-                   s.kd[r4 + 3] * to_f32<T>(s.K[r4 + 3][dk]));
+        for (int e = tid; e < D * 8; e += 256) {
+            const int dk = e >> 3, sa = e & 7, r0 = 32 * (sa >> 2) + 4 * (sa & 3);
+            f32x4 lo, hi;
+#pragma unroll
+            for (int b4 = 0; b4 < 4; ++b4) {
+                lo[b4] = s.kd[r0 + b4] * to_f32<T>(s.K[r0 + b4][dk]);
+                hi[b4] = s.kd[r0 + 16 + b4] * to_f32<T>(s.K[r0 + 16 + b4][dk]);
+            }
+            store8(Kb + frag_k_offset(dk, r0), lo, hi);
         }
     }
 }

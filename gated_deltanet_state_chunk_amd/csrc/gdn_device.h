@@ -126,6 +126,15 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
     *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
+// Two groups of four values to 8 consecutive elements (one 16-byte store for bf16).
+__device__ __forceinline__ void store8(bf16* p, const f32x4& lo, const f32x4& hi) {
+    const bf16x4 a = __builtin_convertvector(lo, bf16x4), b = __builtin_convertvector(hi, bf16x4);
+    *reinterpret_cast<bf16x8*>(p) = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ void store8(float* p, const f32x4& lo, const f32x4& hi) {
+    *reinterpret_cast<float4*>(p) = make_float4(lo[0], lo[1], lo[2], lo[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(hi[0], hi[1], hi[2], hi[3]);
+}
 __device__ __forceinline__ void load4(const bf16* p, float& a, float& b, float& c, float& d) {
     const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
     a = (float)v[0]; b = (float)v[1]; c = (float)v[2]; d = (float)v[3];

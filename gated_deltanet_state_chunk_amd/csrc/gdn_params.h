@@ -43,6 +43,7 @@ struct ChunkParams {
     void* Xt;
     int32_t H_q, H_v, G;
     float scale;
+    int32_t keep_A;  // nonzero: chunk_prep also writes A to the workspace
     SeqTable tab;
 };
 

@@ -83,7 +83,8 @@ enum {
  * 16 h + 4 a + b is stored at offset 8 a + 4 h + b.
  *
  *   gc  fp32  [n_chunks][H_v][64]            inclusive in-chunk cumsum of g
- *   A   dtype [n_chunks][H_v][64][64]        (I + StrictLower(B Gamma K K^T Gamma^-1))^-1
+ *   A   dtype [n_chunks][H_v][64][64]        (I + StrictLower(B Gamma K K^T Gamma^-1))^-1,
+ *                                            written only under GDN_FWD_KEEP_A (gdn_chunk_fwd_ex)
  *   W   dtype [n_chunks][H_v][64 * d_k]      A B Gamma K, fragment order
  *   U   dtype [n_chunks][H_v][64 * d_v]      A B V, fragment order
  *   Kd  dtype [n_chunks][H_v][d_k * 64]      (Diag(gamma_l / gamma) K)^T, fragment order
@@ -136,21 +137,29 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
                   float *final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
                   gdn_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Flags of gdn_chunk_fwd_ex. */
+#define GDN_FWD_KEEP_A 1u /* also write A to its workspace region (otherwise that region is left untouched) */
+
 /*
- * gdn_chunk_fwd with per-kernel timing, for profiling and benchmarks.  Same
- * arguments, same results.  `stage_events` is NULL or an array of six
- * hipEvent_t created by the caller: the start and stop events of the three
- * kernels (chunk_prep: gate cumsum, A, W, U; chunk_state_h: the serial state
- * scan; chunk_output_o) of the first launch (a launch covers up to 64
- * sequences; larger batches take several).  They are stamped by the kernels'
- * own dispatches, so event 2k+1 minus event 2k is the execution time of
- * kernel k without launch gaps.
+ * gdn_chunk_fwd with options, for inspection, profiling and benchmarks.  Same
+ * arguments and results as gdn_chunk_fwd, plus:
+ *   flags  0 or GDN_FWD_KEEP_A.  A is an intermediate nothing downstream reads
+ *          back (W and U are formed from it on chip), so gdn_chunk_fwd does not
+ *          spend the HBM write on it; GDN_FWD_KEEP_A writes it for inspection.
+ *          Unknown bits: GDN_ERR_INVALID.
+ *   stage_events  NULL or an array of six hipEvent_t created by the caller:
+ *          the start and stop events of the three kernels (chunk_prep: gate
+ *          cumsum, A, W, U; chunk_state_h: the serial state scan;
+ *          chunk_output_o) of the first launch (a launch covers up to 64
+ *          sequences; larger batches take several).  They are stamped by the
+ *          kernels' own dispatches, so event 2k+1 minus event 2k is the
+ *          execution time of kernel k without launch gaps.
  */
-int gdn_chunk_fwd_timed(const void *q, const void *k, const void *v, const float *g, const float *beta,
-                        const int32_t *cu_seqlens_host, int32_t num_seqs, const float *initial_state, void *out,
-                        float *final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v,
-                        float scale, gdn_dtype dtype, void *workspace, size_t workspace_bytes, void *stream,
-                        void *const *stage_events);
+int gdn_chunk_fwd_ex(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                     const int32_t *cu_seqlens_host, int32_t num_seqs, const float *initial_state, void *out,
+                     float *final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
+                     gdn_dtype dtype, void *workspace, size_t workspace_bytes, void *stream, uint32_t flags,
+                     void *const *stage_events);
 
 /*
  * One recurrent decode step ("Qwen3.5-397B-A17B" trace page, Decode-GDN node 7,

@@ -133,6 +133,16 @@ def test_chunk_fwd_rejects_before_any_device_work(gdn):
     # empty batch is a no-op that succeeds without launching anything
     assert call(N=0, T=0, cu=_cu([0])) == 0
 
+    def call_ex(flags, **kw):
+        a = dict(good, **kw)
+        return lib.gdn_chunk_fwd_ex(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"], a["s0"], a["out"],
+                                    a["fin"], a["T"], a["H_q"], a["H_v"], a["dk"], a["dv"], a["scale"], a["dt"],
+                                    a["ws"], a["wsb"], a["stream"], flags, None)
+
+    assert call_ex(2) == -1                    # unknown flag bit
+    assert call_ex(gdn.FWD_KEEP_A, q=None) == -1
+    assert call_ex(gdn.FWD_KEEP_A, N=0, T=0, cu=_cu([0])) == 0
+
 
 def test_recurrent_step_rejects_before_any_device_work(gdn):
     lib = gdn.load_library()

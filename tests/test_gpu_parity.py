@@ -140,6 +140,28 @@ def test_prefill_then_decode_continues(torch_cuda, oracle_mod):
     assert rel_err(to_host(fin_pre), to_host(fin_all)) < 1e-5
 
 
+def test_a_region_untouched_without_keep_a(torch_cuda):
+    """gdn_chunk_fwd leaves the A region as it was; gdn_chunk_fwd_ex with
+    GDN_FWD_KEEP_A fills it, and both give the same outputs."""
+    import torch
+
+    import gated_deltanet_state_chunk_amd as gdn
+
+    inp = gdn_inputs.make_prefill(seed=12, seqlens=[70, 64], H_q=1, H_v=2, d_k=64, d_v=64, dtype="bf16")
+    lay = gdn.workspace_layout(inp.T, inp.cu_seqlens, 1, 2, 64, 64, "bf16")
+    a0, a1 = lay["off_A"], lay["off_W"]
+    args = [to_dev(inp.q, "bf16"), to_dev(inp.k, "bf16"), to_dev(inp.v, "bf16"), f32_dev(inp.g), f32_dev(inp.beta),
+            inp.cu_seqlens]
+    ws = torch.full((lay["total_bytes"],), 0xA5, dtype=torch.uint8, device="cuda")
+    out0, fin0 = gdn.chunk_fwd(*args, scale=inp.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert bool((ws[a0:a1] == 0xA5).all())
+    out1, fin1 = gdn.chunk_fwd(*args, scale=inp.scale, workspace=ws, keep_A=True)
+    torch.cuda.synchronize()
+    assert not bool((ws[a0:a1] == 0xA5).all())
+    assert torch.equal(out0, out1) and torch.equal(fin0, fin1)
+
+
 # ---------------------------------------------------------------------------
 # Per-stage intermediates against the chunk-form oracle
 # ---------------------------------------------------------------------------
@@ -151,7 +173,7 @@ def test_chunk_intermediates_match_chunk_form(torch_cuda, dtype, d, tol):
     lens = [100, 64, 30]
     H_q, H_v = 1, 2
     inp = gdn_inputs.make_prefill(seed=9, seqlens=lens, H_q=H_q, H_v=H_v, d_k=d, d_v=d, dtype=dtype)
-    _, _, ws = chunk_fwd_device(inp, return_ws=True)
+    _, _, ws = chunk_fwd_device(inp, return_ws=True, keep_A=True)
     lay = gdn.workspace_layout(inp.T, inp.cu_seqlens, H_q, H_v, d, d, dtype)
     nc = lay["n_chunks"]
     assert nc == 2 + 1 + 1
