@@ -87,9 +87,10 @@ __host__ __device__ __forceinline__ int frag_k_offset(int dk, int pos4) {
     const int m = dk >> 4, r = dk & 15, ks = pos4 >> 5, h = (pos4 >> 4) & 1, a = (pos4 >> 2) & 3;
     return ((m * 2 + ks) * 64 + 16 * a + r) * 8 + 4 * h;
 }
-//   U (accumulator order): column tile of d_v, row tile of pos, lane -> 4 rows
-__host__ __device__ __forceinline__ int frag_u_offset(int col_tile, int pos_tile, int lane) {
-    return ((col_tile * 4 + pos_tile) * 64 + lane) * 4;
+//   U (accumulator order): column tile of d_v, pair of row tiles of pos, lane ->
+//   8 values, the 4 rows of the even tile then the 4 of the odd one
+__host__ __device__ __forceinline__ int frag_u_offset(int col_tile, int pos_pair, int lane) {
+    return ((col_tile * 2 + pos_pair) * 64 + lane) * 8;
 }
 
 // ---------------------------------------------------------------------------
@@ -355,13 +356,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
                 const int r = 32 * ks + 8 * grp + j;
                 frag_set(vf[ks], j, s.svb[r] * to_f32<T>(s.u.V[r][dv]));
             }
+        // lane: column d_v = 16 nt + r16, rows pos = 16 mt + 4 grp + i (accumulator
+        // order); row tiles 2 m and 2 m + 1 share one 16-byte store
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            f32x4 c = zero4();
-            c = mma(Af[mt][0], vf[0], c);
-            if (mt >= 2) c = mma(Af[mt][1], vf[1], c);
-            // lane: column d_v = 16 nt + r16, rows pos = 16 mt + 4 grp + i (accumulator order)
-            store4(Ub + frag_u_offset(nt, mt, lane), c[0], c[1], c[2], c[3]);
+        for (int m = 0; m < 2; ++m) {
+            f32x4 c0 = mma(Af[2 * m][0], vf[0], zero4()), c1 = mma(Af[2 * m + 1][0], vf[0], zero4());
+            if (m == 1) {
+                c0 = mma(Af[2][1], vf[1], c0);
+                c1 = mma(Af[3][1], vf[1], c1);
+            }
+            store8(Ub + frag_u_offset(nt, m, lane), c0, c1);
         }
     }
     // Decayed keys of the state update, transposed: item (dk, s, a) covers the
@@ -682,7 +686,7 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) kf[tt][ks] = Kst[((w * TPW + tt) * 2 + ks) * 64 + lane];
-        uf = Ust[w * 64 + lane];
+        uf = Ust[((w >> 1) * 64 + lane) * 2 + (w & 1)];
         gl = Gst[min(CHUNK, L_n - c * CHUNK) - 1];
     };
     lds_sync();  // B0: stages 0 and 1 ready

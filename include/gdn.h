@@ -78,7 +78,7 @@ enum {
  * wave; for an index i let i = 32 s + 16 h + 4 a + b with a, b in 0..3):
  *   W   element (pos, k):  ((pos/16 * (d_k/32) + s(k)) * 64 + 16 a(k) + pos%16) * 8 + 4 h(k) + b(k)
  *   Kd  element (k, pos):  ((k/16 * 2 + s(pos)) * 64 + 16 a(pos) + k%16) * 8 + 4 h(pos) + b(pos)
- *   U   element (pos, j):  ((j/16 * 4 + pos/16) * 64 + 16 ((pos%16)/4) + j%16) * 4 + pos%4
+ *   U   element (pos, j):  ((j/16 * 2 + pos/32) * 64 + 16 ((pos%16)/4) + j%16) * 8 + 4 ((pos/16)%2) + pos%4
  * "perm32" means: within every block of 32 consecutive indices, index
  * 16 h + 4 a + b is stored at offset 8 a + 4 h + b.
  *

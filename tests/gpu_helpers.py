@@ -72,7 +72,7 @@ def frag_u_to_logical(flat, d_v):
     """U [..., 64*d_v] in accumulator order -> [..., 64, d_v]."""
     pos = np.arange(64)[:, None]
     j = np.arange(d_v)[None, :]
-    off = ((j // 16 * 4 + pos // 16) * 64 + 16 * ((pos % 16) // 4) + j % 16) * 4 + pos % 4
+    off = ((j // 16 * 2 + pos // 32) * 64 + 16 * ((pos % 16) // 4) + j % 16) * 8 + 4 * ((pos // 16) % 2) + pos % 4
     return flat[..., off]
 
 
