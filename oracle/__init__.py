@@ -22,6 +22,14 @@ forms of the update agree; alpha = 1 reduces to DeltaNet; outputs are affine
 in the initial state and linear in V when S0 = 0; GVA equals explicit head
 repetition; splitting a sequence and passing the state equals running it whole;
 a hand-derived d = 2 worked example (tests/golden/).
+
+``decode_step_fused`` adds the decode front end (q/k L2 norm, gate from a,
+A_log, dt_bias, beta from b).  Pins: softplus(x) - softplus(-x) = x and
+softplus(0) = ln 2 through the returned gate, the overflow branches against
+the exact softplus, sigmoid's logit identity and exact bf16 representability
+of the rounded beta, invariance of the step under scaling q or k (L2 norm),
+zero keys reducing to pure decay, and the page's merged update
+S' = alpha (I - beta k^T k) S + beta k^T v evaluated with numpy matrices.
 """
 from __future__ import annotations
 
@@ -54,6 +62,9 @@ def _load():
     lib.gdn_oracle_decode_step.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_double, P, P, P, I64,
                                            ctypes.c_int]
     lib.gdn_oracle_decode_step.restype = ctypes.c_int
+    lib.gdn_oracle_decode_step_fused.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, I64, I64, I64, I64, I64,
+                                                 ctypes.c_double, P, P, P, P, P, I64, ctypes.c_int]
+    lib.gdn_oracle_decode_step_fused.restype = ctypes.c_int
     lib.gdn_oracle_max_threads.argtypes = []
     lib.gdn_oracle_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -101,6 +112,32 @@ def forward(q, k, v, g, beta, cu_seqlens, H_q, H_v, scale, initial_state=None, h
     if want_delta:
         return out, fin, delta
     return out, fin
+
+
+def decode_step_fused(q, k, v, a, b, A_log, dt_bias, state, H_q, H_v, scale, beta_round_bf16, heads=None,
+                      num_threads=0):
+    """Decode step with the gate / beta / q-k normalisation front end
+    (gdn_oracle_decode_step_fused).  q, k raw [N, H_q, d_k]; v [N, H_v, d_v];
+    a, b [N, H_v]; A_log, dt_bias [H_v]; ``state`` float64 [N, H_v, d_k, d_v]
+    updated in place.  Returns (out [N, H_v, d_v], g [N, H_v], beta [N, H_v])."""
+    lib = _load()
+    f32 = lambda x: np.ascontiguousarray(x, dtype=np.float32)
+    q, k, v, a, b, A_log, dt_bias = map(f32, (q, k, v, a, b, A_log, dt_bias))
+    if state.dtype != np.float64 or not state.flags["C_CONTIGUOUS"]:
+        raise ValueError("state must be C-contiguous float64")
+    N, _, d_k = k.shape
+    d_v = v.shape[2]
+    out = np.zeros((N, H_v, d_v))
+    g = np.zeros((N, H_v))
+    beta = np.zeros((N, H_v))
+    hs = None if heads is None else np.ascontiguousarray(heads, dtype=np.int32)
+    rc = lib.gdn_oracle_decode_step_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+                                          int(bool(beta_round_bf16)), N, H_q, H_v, d_k, d_v, float(scale),
+                                          _ptr(state), _ptr(out), _ptr(g), _ptr(beta), _ptr(hs),
+                                          0 if hs is None else len(hs), int(num_threads))
+    if rc != 0:
+        raise ValueError("gdn_oracle_decode_step_fused: bad arguments")
+    return out, g, beta
 
 
 def decode_step(q, k, v, g, beta, state, H_q, H_v, scale, heads=None, num_threads=0):

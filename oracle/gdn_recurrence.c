@@ -36,10 +36,10 @@
 #include <omp.h>
 #endif
 
-/* One token of the recurrence on one (sequence, value-head) state. */
-static void gdn_token_update(double *S, const float *q, const float *k, const float *v, double g, double beta,
-                             int64_t dk, int64_t dv, double scale, double *out /* may be NULL */, double *p,
-                             double *delta) {
+/* One token of the recurrence on one (sequence, value-head) state; q and k in fp64. */
+static void gdn_token_update_d(double *S, const double *q, const double *k, const float *v, double g, double beta,
+                               int64_t dk, int64_t dv, double scale, double *out /* may be NULL */, double *p,
+                               double *delta) {
     const double alpha = exp(g);
     /* Sbar = alpha * S */
     for (int64_t i = 0; i < dk; ++i)
@@ -47,25 +47,36 @@ static void gdn_token_update(double *S, const float *q, const float *k, const fl
     /* prediction p = k Sbar  (p_j = sum_i k_i Sbar_ij) */
     for (int64_t j = 0; j < dv; ++j) p[j] = 0.0;
     for (int64_t i = 0; i < dk; ++i) {
-        const double ki = (double)k[i];
+        const double ki = k[i];
         for (int64_t j = 0; j < dv; ++j) p[j] += ki * S[i * dv + j];
     }
     /* delta = beta (v - p) */
     for (int64_t j = 0; j < dv; ++j) delta[j] = beta * ((double)v[j] - p[j]);
     /* S = Sbar + k^T delta */
     for (int64_t i = 0; i < dk; ++i) {
-        const double ki = (double)k[i];
+        const double ki = k[i];
         for (int64_t j = 0; j < dv; ++j) S[i * dv + j] += ki * delta[j];
     }
     /* o = scale * q S */
     if (out) {
         for (int64_t j = 0; j < dv; ++j) p[j] = 0.0;
         for (int64_t i = 0; i < dk; ++i) {
-            const double qi = (double)q[i];
+            const double qi = q[i];
             for (int64_t j = 0; j < dv; ++j) p[j] += qi * S[i * dv + j];
         }
         for (int64_t j = 0; j < dv; ++j) out[j] = scale * p[j];
     }
+}
+
+/* The same with the q, k values the device receives (upcast exactly). */
+static void gdn_token_update(double *S, const float *q, const float *k, const float *v, double g, double beta,
+                             int64_t dk, int64_t dv, double scale, double *out, double *p, double *delta) {
+    double qd[1024], kd[1024];
+    for (int64_t i = 0; i < dk; ++i) {
+        qd[i] = (double)q[i];
+        kd[i] = (double)k[i];
+    }
+    gdn_token_update_d(S, qd, kd, v, g, beta, dk, dv, scale, out, p, delta);
 }
 
 /*
@@ -86,7 +97,7 @@ int gdn_oracle_forward(const float *q, const float *k, const float *v, const flo
                        const int64_t *cu_seqlens, int64_t num_seqs, int64_t H_q, int64_t H_v, int64_t dk,
                        int64_t dv, double scale, const double *initial_state, double *out, double *final_state,
                        const int32_t *heads, int64_t n_heads, double *delta_out, int num_threads) {
-    if (num_seqs < 0 || H_q <= 0 || H_v <= 0 || dk <= 0 || dv <= 0 || H_v % H_q != 0) return -1;
+    if (num_seqs < 0 || H_q <= 0 || H_v <= 0 || dk <= 0 || dv <= 0 || H_v % H_q != 0 || dk > 1024) return -1;
     if (!heads) n_heads = H_v;
     const int64_t G = H_v / H_q;
     const int64_t npairs = num_seqs * n_heads;
@@ -133,7 +144,7 @@ int gdn_oracle_forward(const float *q, const float *k, const float *v, const flo
 int gdn_oracle_decode_step(const float *q, const float *k, const float *v, const float *g, const float *beta,
                            int64_t N, int64_t H_q, int64_t H_v, int64_t dk, int64_t dv, double scale,
                            double *state, double *out, const int32_t *heads, int64_t n_heads, int num_threads) {
-    if (N < 0 || H_q <= 0 || H_v <= 0 || dk <= 0 || dv <= 0 || H_v % H_q != 0) return -1;
+    if (N < 0 || H_q <= 0 || H_v <= 0 || dk <= 0 || dv <= 0 || H_v % H_q != 0 || dk > 1024) return -1;
     if (!heads) n_heads = H_v;
     const int64_t G = H_v / H_q;
     const int64_t npairs = N * n_heads;
@@ -158,6 +169,85 @@ int gdn_oracle_decode_step(const float *q, const float *k, const float *v, const
         gdn_token_update(state + (n * H_v + h) * dk * dv, q + (n * H_q + hq) * dk, k + (n * H_q + hq) * dk,
                          v + (n * H_v + h) * dv, (double)g[n * H_v + h], (double)beta[n * H_v + h], dk, dv, scale,
                          out + (n * H_v + h) * dv, p, delta);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Decode step with the front end of the same node (trace page, Decode-GDN
+ * node 7, its first two steps), in fp64:
+ *   k_bar = k / sqrt(sum_j k_j^2 + 1e-6),  q_bar = scale * q / sqrt(sum_j q_j^2 + 1e-6)
+ *     (an L2 norm over the sum of squares, not an RMS norm; the query scale
+ *     multiplies once, after the norm)
+ *   g = -exp(A_log[h]) * softplus(a + dt_bias[h]),  alpha = exp(g)
+ *     softplus with the overflow branches of the "Kestrel_VLLM - 24" page,
+ *     section 三 (its beta/g kernel): x if x > 20, exp(x) if x < -20, else
+ *     log1p(exp(x))
+ *   beta = sigmoid(b), rounded to bf16 and back when beta_round_bf16 (the
+ *     trace page keeps that rounding when b is bf16); sigmoid is taken in fp64
+ *     and rounded to fp32 first, the precision the pages' kernels work in
+ * then the update of gdn_token_update with q_bar (scale already applied), k_bar.
+ *   a, b: [N, H_v] (exact values the device receives); A_log, dt_bias: [H_v]
+ *   g_out, beta_out: [N, H_v] double or NULL (the gate and beta used)
+ */
+static double softplus_branchy(double x) {
+    if (x > 20.0) return x;
+    if (x < -20.0) return exp(x);
+    return log1p(exp(x));
+}
+
+/* fp32 -> bf16 (round to nearest even) -> fp32; inputs here are finite. */
+static float round_bf16(float x) {
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    u &= 0xFFFF0000u;
+    memcpy(&x, &u, 4);
+    return x;
+}
+
+int gdn_oracle_decode_step_fused(const float *q, const float *k, const float *v, const float *a, const float *b,
+                                 const float *A_log, const float *dt_bias, int beta_round_bf16, int64_t N,
+                                 int64_t H_q, int64_t H_v, int64_t dk, int64_t dv, double scale, double *state,
+                                 double *out, double *g_out, double *beta_out, const int32_t *heads, int64_t n_heads,
+                                 int num_threads) {
+    if (N < 0 || H_q <= 0 || H_v <= 0 || dk <= 0 || dv <= 0 || H_v % H_q != 0 || dk > 1024 || dv > 1024) return -1;
+    if (!heads) n_heads = H_v;
+    const int64_t G = H_v / H_q;
+    const int64_t npairs = N * n_heads;
+#ifdef _OPENMP
+    if (num_threads > 0) omp_set_num_threads(num_threads);
+#endif
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t pi = 0; pi < npairs; ++pi) {
+        const int64_t n = pi / n_heads;
+        const int64_t h = heads ? (int64_t)heads[pi % n_heads] : (pi % n_heads);
+        if (h < 0 || h >= H_v) {
+            bad |= 1;
+            continue;
+        }
+        const int64_t hq = h / G;
+        const float *qr = q + (n * H_q + hq) * dk, *kr = k + (n * H_q + hq) * dk;
+        double qn[1024], kn[1024], p[1024], delta[1024];
+        double sq = 0.0, sk = 0.0;
+        for (int64_t i = 0; i < dk; ++i) {
+            sq += (double)qr[i] * (double)qr[i];
+            sk += (double)kr[i] * (double)kr[i];
+        }
+        const double rq = scale / sqrt(sq + 1e-6), rk = 1.0 / sqrt(sk + 1e-6);
+        for (int64_t i = 0; i < dk; ++i) {
+            qn[i] = (double)qr[i] * rq;
+            kn[i] = (double)kr[i] * rk;
+        }
+        const double g = -exp((double)A_log[h]) * softplus_branchy((double)a[n * H_v + h] + (double)dt_bias[h]);
+        float sig = (float)(1.0 / (1.0 + exp(-(double)b[n * H_v + h])));
+        if (beta_round_bf16) sig = round_bf16(sig);
+        const double beta = (double)sig;
+        if (g_out) g_out[n * H_v + h] = g;
+        if (beta_out) beta_out[n * H_v + h] = beta;
+        gdn_token_update_d(state + (n * H_v + h) * dk * dv, qn, kn, v + (n * H_v + h) * dv, g, beta, dk, dv, 1.0,
+                           out + (n * H_v + h) * dv, p, delta);
     }
     return bad ? -1 : 0;
 }

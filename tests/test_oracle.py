@@ -362,3 +362,132 @@ def test_bad_arguments_rejected(oracle_mod):
     with pytest.raises(ValueError):
         oracle_mod.forward(q, q, np.zeros((2, 4, 4), np.float32), np.zeros((2, 4), np.float32),
                            np.zeros((2, 4), np.float32), [0, 2], 3, 4, 1.0)
+
+
+# ---------------------------------------------------------------------------
+# Decode front end ("Qwen3.5-397B-A17B" trace page, Decode-GDN node 7, steps 1
+# and 2; softplus branches of the "Kestrel_VLLM - 24" page, section 三)
+# ---------------------------------------------------------------------------
+def _fused_inputs(rng, N, H_q, H_v, d, a_scale=2.0):
+    q = rng.standard_normal((N, H_q, d)).astype(np.float32)
+    k = rng.standard_normal((N, H_q, d)).astype(np.float32)
+    v = rng.standard_normal((N, H_v, d)).astype(np.float32)
+    a = (a_scale * rng.standard_normal((N, H_v))).astype(np.float32)
+    b = (2.0 * rng.standard_normal((N, H_v))).astype(np.float32)
+    A_log = rng.uniform(-1.0, 1.0, H_v).astype(np.float32)
+    dt_bias = rng.uniform(-0.5, 0.5, H_v).astype(np.float32)
+    S = 0.1 * rng.standard_normal((N, H_v, d, d))
+    return q, k, v, a, b, A_log, dt_bias, S
+
+
+def _fused(oracle_mod, q, k, v, a, b, A_log, dt_bias, S, H_q, H_v, scale=0.125, rnd=False):
+    S = np.ascontiguousarray(S, dtype=np.float64).copy()
+    out, g, beta = oracle_mod.decode_step_fused(q, k, v, a, b, A_log, dt_bias, S, H_q, H_v, scale, rnd)
+    return out, g, beta, S
+
+
+def test_fused_gate_softplus_identities(oracle_mod):
+    """With A_log = 0 the gate is -softplus(a + dt_bias): softplus(x) - softplus(-x) = x,
+    softplus(0) = ln 2, and the +-20 overflow branches stay within 1e-8 of the exact value."""
+    x = np.concatenate([np.linspace(-19.5, 19.5, 79), [0.0]]).astype(np.float32)
+    N, H = len(x), 1
+    zeros = np.zeros(1, np.float32)
+    q = np.ones((N, 1, 2), np.float32)
+    k = np.ones((N, 1, 2), np.float32)
+    v = np.ones((N, 1, 2), np.float32)
+    S = np.zeros((N, 1, 2, 2))
+    _, gp, _, _ = _fused(oracle_mod, q, k, v, x[:, None], np.zeros((N, H), np.float32), zeros, zeros, S, 1, 1)
+    _, gm, _, _ = _fused(oracle_mod, q, k, v, -x[:, None], np.zeros((N, H), np.float32), zeros, zeros, S, 1, 1)
+    np.testing.assert_allclose(-gp[:, 0] + gm[:, 0], x.astype(np.float64), rtol=0, atol=1e-12)
+    assert abs(-gp[-1, 0] - np.log(2.0)) < 1e-15
+    big = np.array([20.5, 30.0, 60.0, -20.5, -30.0, -60.0], np.float32)
+    M = len(big)
+    _, gb, _, _ = _fused(oracle_mod, q[:M], k[:M], v[:M], big[:, None], np.zeros((M, H), np.float32), zeros, zeros,
+                         S[:M], 1, 1)
+    exact = np.logaddexp(0.0, big.astype(np.float64))
+    np.testing.assert_allclose(-gb[:, 0], exact, rtol=1e-8, atol=0)
+    # the learned scale multiplies: A_log = ln 3 triples the gate
+    _, g3, _, _ = _fused(oracle_mod, q, k, v, x[:, None], np.zeros((N, H), np.float32),
+                         np.array([np.log(3.0)], np.float32), zeros, S, 1, 1)
+    np.testing.assert_allclose(g3[:, 0], 3.0 * gp[:, 0] * np.exp(np.float64(np.float32(np.log(3.0)))) / 3.0,
+                               rtol=1e-12)
+    assert np.all(gp <= 0)
+
+
+def test_fused_beta_sigmoid_and_bf16_rounding(oracle_mod):
+    """beta = sigmoid(b): logit(beta) = b without rounding; with the bf16 rounding
+    beta is exactly representable in bf16 and within half a bf16 ulp of sigmoid(b)."""
+    rng = np.random.default_rng(2)
+    N = 64
+    b = (3.0 * rng.standard_normal((N, 1))).astype(np.float32)
+    b[0, 0] = 0.0
+    q = np.ones((N, 1, 2), np.float32)
+    zeros = np.zeros(1, np.float32)
+    S = np.zeros((N, 1, 2, 2))
+    _, _, beta, _ = _fused(oracle_mod, q, q, q, np.zeros((N, 1), np.float32), b, zeros, zeros, S, 1, 1)
+    # beta is sigmoid rounded to fp32 (relative error <= 2^-24), which moves the
+    # logit by at most 2^-24 / (1 - beta) + 2^-24 / beta ... use twice that
+    bnd = 2.0 ** -23 * (1 / (1 - beta) + 1 / beta)
+    assert np.all(np.abs(np.log(beta / (1 - beta)) - b.astype(np.float64)) <= bnd)
+    assert beta[0, 0] == 0.5
+    _, _, br, _ = _fused(oracle_mod, q, q, q, np.zeros((N, 1), np.float32), b, zeros, zeros, S, 1, 1, rnd=True)
+    bits = br.astype(np.float32).view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0)
+    assert np.all(np.abs(br - beta) <= beta * 2.0 ** -8 + 1e-12)   # half a bf16 ulp (8 significant bits)
+    assert br[0, 0] == 0.5
+
+
+def test_fused_l2_norm_scale_invariance_and_zero_keys(oracle_mod):
+    """The q/k normalisation is an L2 norm: scaling q or k by c > 0 changes nothing
+    (beyond the 1e-6 eps); zero keys leave only the decay (S' = alpha S) and the read."""
+    rng = np.random.default_rng(3)
+    N, H_q, H_v, d = 3, 2, 4, 16
+    q, k, v, a, b, A_log, dt_bias, S = _fused_inputs(rng, N, H_q, H_v, d)
+    o1, g1, _, S1 = _fused(oracle_mod, q, k, v, a, b, A_log, dt_bias, S, H_q, H_v)
+    o2, _, _, S2 = _fused(oracle_mod, (7.0 * q).astype(np.float32), (0.25 * k).astype(np.float32), v, a, b, A_log,
+                          dt_bias, S, H_q, H_v)
+    assert _rel(o2, o1) < 1e-6 and _rel(S2, S1) < 1e-6
+    kz = np.zeros_like(k)
+    o0, g0, _, S0 = _fused(oracle_mod, q, kz, v, a, b, A_log, dt_bias, S, H_q, H_v)
+    alpha = np.exp(g0)[:, :, None, None]
+    assert _rel(S0, alpha * S) < 1e-14
+    qn = q.astype(np.float64) / np.sqrt((q.astype(np.float64) ** 2).sum(-1, keepdims=True) + 1e-6)
+    G = H_v // H_q
+    ref = 0.125 * np.einsum("nhi,nhij->nhj", np.repeat(qn, G, axis=1), alpha * S)
+    assert _rel(o0, ref) < 1e-12
+
+
+def test_fused_matches_merged_update_formula(oracle_mod):
+    """The page's merged form of the step, S' = alpha S (I - beta k k^T) + beta v k^T
+    (column convention; here S' = alpha (I - beta k^T k) S + beta k^T v), with the
+    norms from numpy and the gate from logaddexp, read as o = scale q_bar S'."""
+    rng = np.random.default_rng(4)
+    N, H_q, H_v, d = 2, 2, 4, 12
+    q, k, v, a, b, A_log, dt_bias, S = _fused_inputs(rng, N, H_q, H_v, d)
+    out, _, _, S1 = _fused(oracle_mod, q, k, v, a, b, A_log, dt_bias, S, H_q, H_v, scale=0.3)
+    G = H_v // H_q
+    for n in range(N):
+        for h in range(H_v):
+            kk = k[n, h // G].astype(np.float64)
+            qq = q[n, h // G].astype(np.float64)
+            kb = kk / np.linalg.norm(kk)
+            qb = 0.3 * qq / np.linalg.norm(qq)
+            alpha = np.exp(-np.exp(np.float64(A_log[h])) * np.logaddexp(0.0, np.float64(a[n, h]) + dt_bias[h]))
+            beta = 1.0 / (1.0 + np.exp(-np.float64(b[n, h])))
+            M = alpha * (np.eye(d) - beta * np.outer(kb, kb))
+            Sn = M @ S[n, h] + beta * np.outer(kb, v[n, h].astype(np.float64))
+            assert _rel(S1[n, h], Sn) < 1e-6   # eps 1e-6 inside the norm, fp32 sigmoid
+            assert _rel(out[n, h], qb @ Sn) < 1e-6
+
+
+def test_fused_front_end_then_plain_step(oracle_mod):
+    """Feeding the normalised q, k and the returned gate and beta to the plain
+    decode step reproduces the fused step (up to the fp32 rounding of q_bar, k_bar)."""
+    rng = np.random.default_rng(5)
+    N, H_q, H_v, d = 2, 1, 2, 32
+    q, k, v, a, b, A_log, dt_bias, S = _fused_inputs(rng, N, H_q, H_v, d)
+    out, g, beta, S1 = _fused(oracle_mod, q, k, v, a, b, A_log, dt_bias, S, H_q, H_v, scale=0.2)
+    nrm = lambda x: x.astype(np.float64) / np.sqrt((x.astype(np.float64) ** 2).sum(-1, keepdims=True) + 1e-6)
+    S2 = np.ascontiguousarray(S.copy())
+    o2 = oracle_mod.decode_step(nrm(q), nrm(k), v, g, beta, S2, H_q, H_v, 0.2)
+    assert _rel(o2, out) < 1e-6 and _rel(S2, S1) < 1e-6
