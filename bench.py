@@ -6,7 +6,9 @@ of T = 4096 tokens, H_q = 16 query/key heads, H_v = 32 value heads,
 d_k = d_v = 128, bf16 q/k/v, fp32 gates and states, nonzero initial state),
 all three kernels, inputs resident in HBM.  The batched decode step (256
 sequences x 1 token, 537 MB of fp32 state updated in place, fresh seeded tokens
-each step) is measured in the same run and reported under "decode".
+each step) is measured in the same run and reported under "decode", and the
+same step taken from the raw inputs (q/k L2 norm, gate and beta computed inside
+the step) under "decode_fused".
 
 Prints ONE JSON line.  Timing: W untimed warm-up steps, then K timed steps of
 the product entry point between two device synchronisations (value,
@@ -81,9 +83,12 @@ def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True):
     return bytes_, flops
 
 
-def decode_work(N, H_q, H_v, d, es):
+def decode_work(N, H_q, H_v, d, es, fused=False):
+    """Bytes and flops of one decode step: the fp32 state read and written once,
+    q, k, v, o, and g, beta (plain) or a, b and the per-head A_log, dt_bias (fused)."""
     state = N * H_v * d * d * 4
-    io = 2 * N * H_q * d * es + 2 * N * H_v * d * es + 2 * N * H_v * 4
+    gates = 2 * N * H_v * es + 2 * H_v * 4 if fused else 2 * N * H_v * 4
+    io = 2 * N * H_q * d * es + 2 * N * H_v * d * es + gates
     return 2 * state + io, N * H_v * d * d * 8
 
 
@@ -228,7 +233,9 @@ def bench_prefill(args, torch, gdn, hip, device):
                 ms_step_with_events=timed_ms)
 
 
-def bench_decode(args, torch, gdn, hip, device):
+def bench_decode(args, torch, gdn, hip, device, fused=False):
+    """Decode steps on the 256 x 32-head batch: the plain step (normalised q, k and
+    final g, beta) or, with fused, the step from raw q, k, a, b (front end inside)."""
     import gdn_inputs
 
     cfg = gdn_inputs.DECODE_WORKLOAD
@@ -236,14 +243,20 @@ def bench_decode(args, torch, gdn, hip, device):
     state = _dev(gdn_inputs.make_decode_state(cfg["seed"], N, H_v, d, d, cfg["state_std"]), "f32", torch, device)
     toks = []
     for s in range(cfg["steps"]):
-        t = gdn_inputs.make_decode_token(gdn_inputs.decode_step_seed(s), N, H_q, H_v, d, d, dt)
-        toks.append(tuple(_dev(x, dt, torch, device) for x in (t.q, t.k, t.v)) +
-                    (_dev(t.g, "f32", torch, device), _dev(t.beta, "f32", torch, device)))
+        if fused:
+            t = gdn_inputs.make_decode_raw_token(gdn_inputs.decode_step_seed(s), N, H_q, H_v, d, d, dt)
+            toks.append(tuple(_dev(x, dt, torch, device) for x in (t.q, t.k, t.v, t.a, t.b)) +
+                        (_dev(t.A_log, "f32", torch, device), _dev(t.dt_bias, "f32", torch, device)))
+        else:
+            t = gdn_inputs.make_decode_token(gdn_inputs.decode_step_seed(s), N, H_q, H_v, d, d, dt)
+            toks.append(tuple(_dev(x, dt, torch, device) for x in (t.q, t.k, t.v)) +
+                        (_dev(t.g, "f32", torch, device), _dev(t.beta, "f32", torch, device)))
+    step_fn = gdn.recurrent_step_fused if fused else gdn.recurrent_step
     out = torch.empty((N, H_v, d), dtype=toks[0][0].dtype, device=device)
     scale = 1.0 / math.sqrt(d)
     K = max(args.steps, cfg["steps"])
     for i in range(args.warmup):
-        gdn.recurrent_step(*toks[i % len(toks)], state, scale=scale, out=out)
+        step_fn(*toks[i % len(toks)], state, scale=scale, out=out)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     # Pass 1: back-to-back steps, no per-kernel events.
@@ -251,7 +264,7 @@ def bench_decode(args, torch, gdn, hip, device):
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for i in range(K):
-        gdn.recurrent_step(*toks[i % len(toks)], state, scale=scale, out=out)
+        step_fn(*toks[i % len(toks)], state, scale=scale, out=out)
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / K
@@ -259,11 +272,11 @@ def bench_decode(args, torch, gdn, hip, device):
     evs = [(hip.event(), hip.event()) for _ in range(K)]
     for i in range(K):
         hip.record(evs[i][0], stream.cuda_stream)
-        gdn.recurrent_step(*toks[i % len(toks)], state, scale=scale, out=out)
+        step_fn(*toks[i % len(toks)], state, scale=scale, out=out)
         hip.record(evs[i][1], stream.cuda_stream)
     torch.cuda.synchronize()
     kms = sum(hip.elapsed_ms(a, b) for a, b in evs) / K
-    nbytes, nflops = decode_work(N, H_q, H_v, d, 2 if dt == "bf16" else 4)
+    nbytes, nflops = decode_work(N, H_q, H_v, d, 2 if dt == "bf16" else 4, fused=fused)
     return dict(N=N, ms_step=ms, kernel_ms=kms, bytes=nbytes, flops=nflops, steps=K)
 
 
@@ -343,7 +356,7 @@ def main():
         return
 
     res = {}
-    pre = dec = None
+    pre = dec = decf = None
     if args.only in ("all", "prefill"):
         pre = bench_prefill(args, torch, gdn, hip, device)
         print(f"[bench] prefill {args.workload}: {pre['ms_step']:.4f} ms/step, stages "
@@ -351,6 +364,8 @@ def main():
     if args.only in ("all", "decode"):
         dec = bench_decode(args, torch, gdn, hip, device)
         print(f"[bench] decode: {dec['ms_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+        decf = bench_decode(args, torch, gdn, hip, device, fused=True)
+        print(f"[bench] decode (fused front end): {decf['ms_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
     if pre is not None:
         inp = pre["inp"]
@@ -405,6 +420,15 @@ def main():
                         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
                         "config": {"workload": "decode_256x1"}, "roofline": decode["roofline"]})
         res["decode"] = decode
+    if decf is not None:
+        kgbs = decf["bytes"] / (decf["kernel_ms"] * 1e-3) / 1e9
+        res["decode_fused"] = {
+            "workload": "decode_256x1 from raw q, k, a, b (q/k L2 norm, gate and beta inside the step)",
+            "us_per_step": decf["ms_step"] * 1e3, "kernel_us": decf["kernel_ms"] * 1e3,
+            "state_gb_per_s": decf["bytes"] / (decf["ms_step"] * 1e-3) / 1e9,
+            "tokens_per_s": decf["N"] / (decf["ms_step"] * 1e-3), "steps": decf["steps"],
+            "roofline": {"bound": "hbm", "kernel": "recurrent_step_fused", "achieved": kgbs, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": kgbs / HBM_PEAK_GBS, "traffic": None}}
     if pre is not None and args.only == "all" and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(pre["inp"])
     res["source_sha"] = _source_sha()

@@ -78,6 +78,8 @@ def load_library():
     lib.gdn_chunk_fwd_ex.restype = ctypes.c_int
     lib.gdn_recurrent_step.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P]
     lib.gdn_recurrent_step.restype = ctypes.c_int
+    lib.gdn_recurrent_step_fused.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P]
+    lib.gdn_recurrent_step_fused.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -249,4 +251,41 @@ def recurrent_step(q, k, v, g, beta, state, scale: Optional[float] = None, out=N
                                 d_k, d_v, float(scale), dt, _stream_ptr(stream))
     if rc != 0:
         raise GdnError(rc, "gdn_recurrent_step")
+    return out
+
+
+def recurrent_step_fused(q, k, v, a, b, A_log, dt_bias, state, scale: Optional[float] = None, out=None,
+                         stream=None):
+    """One decode step from the raw inputs (gdn_recurrent_step_fused): q/k L2 norm,
+    gate from a, A_log, dt_bias, beta from b, then the state update; ``state`` is
+    updated in place.
+
+    q, k: [N, H_q, d_k] (not normalised); v: [N, H_v, d_v]; a, b: [N, H_v] (q's
+    dtype); A_log, dt_bias: fp32 [H_v]; state: fp32 [N, H_v, d_k, d_v].  Returns
+    out [N, H_v, d_v] in q's dtype.  scale defaults to 1/sqrt(d_k).
+    """
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("a", a), ("b", b)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("A_log", A_log, torch.float32)
+    _check_dev("dt_bias", dt_bias, torch.float32)
+    _check_dev("state", state, torch.float32)
+    N, H_q, d_k = q.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    if k.shape != q.shape or v.shape[0] != N or a.shape != (N, H_v) or b.shape != (N, H_v) or \
+            A_log.shape != (H_v,) or dt_bias.shape != (H_v,) or tuple(state.shape) != (N, H_v, d_k, d_v):
+        raise ValueError("inconsistent decode shapes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    if out is None:
+        out = torch.empty((N, H_v, d_v), dtype=q.dtype, device=q.device)
+    else:
+        _check_dev("out", out, q.dtype)
+    rc = lib.gdn_recurrent_step_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+                                      _ptr(state), _ptr(out), N, H_q, H_v, d_k, d_v, float(scale), dt,
+                                      _stream_ptr(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_recurrent_step_fused")
     return out

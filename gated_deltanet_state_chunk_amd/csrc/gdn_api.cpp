@@ -55,10 +55,13 @@ hipError_t run_chunk(const gdn::ChunkParams& p, gdn_dtype dt, int d, hipStream_t
     return d == 128 ? gdn::launch_chunk_pipeline<float, 128>(p, s, ev) : gdn::launch_chunk_pipeline<float, 64>(p, s, ev);
 }
 
+template <bool FUSED>
 hipError_t run_decode(const gdn::DecodeParams& p, gdn_dtype dt, int d, hipStream_t s) {
     if (dt == GDN_DTYPE_BF16)
-        return d == 128 ? gdn::launch_recurrent_step<gdn::bf16, 128>(p, s) : gdn::launch_recurrent_step<gdn::bf16, 64>(p, s);
-    return d == 128 ? gdn::launch_recurrent_step<float, 128>(p, s) : gdn::launch_recurrent_step<float, 64>(p, s);
+        return d == 128 ? gdn::launch_recurrent_step<gdn::bf16, 128, FUSED>(p, s)
+                        : gdn::launch_recurrent_step<gdn::bf16, 64, FUSED>(p, s);
+    return d == 128 ? gdn::launch_recurrent_step<float, 128, FUSED>(p, s)
+                    : gdn::launch_recurrent_step<float, 64, FUSED>(p, s);
 }
 
 int hip_fail(hipError_t e) {
@@ -193,10 +196,38 @@ int gdn_recurrent_step(const void* q, const void* k, const void* v, const float*
     for (const void* ptr : ptrs)
         if (!aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
     if (!(scale == scale)) return GDN_ERR_INVALID;
-    gdn::DecodeParams p;
+    gdn::DecodeParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.state = state; p.out = out;
     p.N = N; p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
-    const hipError_t e = run_decode(p, dtype, d_k, static_cast<hipStream_t>(stream));
+    const hipError_t e = run_decode<false>(p, dtype, d_k, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+    return GDN_OK;
+}
+
+int gdn_recurrent_step_fused(const void* q, const void* k, const void* v, const void* a, const void* b,
+                             const float* A_log, const float* dt_bias, float* state, void* out, int32_t N,
+                             int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale, gdn_dtype dtype,
+                             void* stream) {
+    int rc = check_shapes(H_q, H_v, d_k, d_v, dtype);
+    if (rc != GDN_OK) return rc;
+    if (N < 0) return GDN_ERR_INVALID;
+    if (N == 0) return GDN_OK;
+    if ((int64_t)N * H_v > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !state || !out) return GDN_ERR_INVALID;
+    const void* ptrs[] = {q, k, v, state, out};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
+    // per-head scalars: natural alignment of their element type
+    const size_t es = elem_size(dtype);
+    if ((reinterpret_cast<uintptr_t>(a) % es) || (reinterpret_cast<uintptr_t>(b) % es) ||
+        (reinterpret_cast<uintptr_t>(A_log) & 3u) || (reinterpret_cast<uintptr_t>(dt_bias) & 3u))
+        return GDN_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return GDN_ERR_INVALID;
+    gdn::DecodeParams p{};
+    p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.A_log = A_log; p.dt_bias = dt_bias;
+    p.state = state; p.out = out;
+    p.N = N; p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
+    const hipError_t e = run_decode<true>(p, dtype, d_k, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e);
     return GDN_OK;
 }

@@ -10,6 +10,15 @@
 // taken from the values read once, and S' is written once.  The pass is bound
 // by HBM bandwidth (64 KiB read + 64 KiB written per head at d = 128).
 //
+// The fused variant takes the raw inputs of that node instead (its first two
+// steps): k_bar = k / sqrt(sum k^2 + 1e-6), q_bar = scale q / sqrt(sum q^2 +
+// 1e-6), g = -exp(A_log) softplus(a + dt_bias) (softplus with the +-20 overflow
+// branches of the "Kestrel_VLLM - 24" page, section 三), beta = sigmoid(b)
+// rounded to the input dtype (bf16 keeps that rounding, as the trace page
+// notes).  The two sums of squares ride along with the column reductions, and
+// the norms are applied as scalars afterwards, so the state is still read
+// and written once.
+//
 // One 256-thread workgroup per (sequence, value head).  Thread t owns a 16-byte
 // column group cg = t % (d/4) of rows rg + RG*m (RG = 1024/d row groups), so
 // each wave reads whole contiguous rows with 128-bit loads; the updated state
@@ -21,13 +30,13 @@
 
 namespace gdn {
 
-template <typename T, int D>
+template <typename T, int D, bool FUSED>
 __global__ __launch_bounds__(256) void recurrent_step_kernel(const DecodeParams p) {
     constexpr int CPR = D / 4;      // float4 column groups per row
     constexpr int RG = 256 / CPR;   // row groups
     constexpr int RPT = D / RG;     // rows per thread
     constexpr int RGW = 64 / CPR;   // row groups per wave
-    constexpr int NV = 9;           // reduced values: k S (4), q S (4), q . k
+    constexpr int NV = FUSED ? 11 : 9;  // reduced values: k S (4), q S (4), q . k [, k . k, q . q]
     const int nh = blockIdx.x;
     const int n = nh / p.H_v, h = nh % p.H_v;
     const int hq = h / p.G;
@@ -41,8 +50,17 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(const DecodeParams 
     const T* qp = reinterpret_cast<const T*>(p.q) + ((size_t)n * p.H_q + hq) * D;
     const T* kp = reinterpret_cast<const T*>(p.k) + ((size_t)n * p.H_q + hq) * D;
     const T* vp = reinterpret_cast<const T*>(p.v) + (size_t)nh * D;
-    const float alpha = __expf(p.g[nh]);
-    const float beta = p.beta[nh];
+    float alpha, beta;
+    if constexpr (FUSED) {
+        const float xa = to_f32<T>(reinterpret_cast<const T*>(p.a)[nh]) + p.dt_bias[h];
+        const float sp = xa > 20.f ? xa : (xa < -20.f ? expf(xa) : log1pf(expf(xa)));
+        alpha = expf(-expf(p.A_log[h]) * sp);
+        const float sg = 1.f / (1.f + expf(-to_f32<T>(reinterpret_cast<const T*>(p.b)[nh])));
+        beta = to_f32<T>(from_f32<T>(sg));  // rounded to the input dtype (RNE)
+    } else {
+        alpha = __expf(p.g[nh]);
+        beta = p.beta[nh];
+    }
 
     float4 s[RPT];
     float kr[RPT], qr[RPT];
@@ -67,6 +85,10 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(const DecodeParams 
         red[6] += qr[m] * s[m].z;
         red[7] += qr[m] * s[m].w;
         red[8] += qr[m] * kr[m];
+        if constexpr (FUSED) {
+            red[9] += kr[m] * kr[m];
+            red[10] += qr[m] * qr[m];
+        }
     }
     // Row groups inside a wave differ in the lane bits above log2(CPR).
 #pragma unroll
@@ -84,20 +106,27 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(const DecodeParams 
 
     float vv[4];
     load4(vp + 4 * cg, vv[0], vv[1], vv[2], vv[3]);
+    // Norm factors (1 and scale for the plain step, whose q, k arrive normalised).
+    float rk = 1.f, rq = p.scale;
+    if constexpr (FUSED) {
+        rk = 1.f / sqrtf(red[9] + 1e-6f);
+        rq = p.scale / sqrtf(red[10] + 1e-6f);
+    }
     float dl[4], o[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        dl[c] = beta * (vv[c] - alpha * red[c]);
-        o[c] = p.scale * (alpha * red[4 + c] + red[8] * dl[c]);
+        dl[c] = beta * (vv[c] - alpha * rk * red[c]);
+        o[c] = rq * (alpha * red[4 + c] + rk * red[8] * dl[c]);
     }
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int row = rg + RG * m;
         float4 t = s[m];
-        t.x = alpha * t.x + kr[m] * dl[0];
-        t.y = alpha * t.y + kr[m] * dl[1];
-        t.z = alpha * t.z + kr[m] * dl[2];
-        t.w = alpha * t.w + kr[m] * dl[3];
+        const float kn = rk * kr[m];
+        t.x = alpha * t.x + kn * dl[0];
+        t.y = alpha * t.y + kn * dl[1];
+        t.z = alpha * t.z + kn * dl[2];
+        t.w = alpha * t.w + kn * dl[3];
         // non-temporal: the state is not touched again by this step, and keeping
         // it out of the caches measurably raises the read/write stream rate
         __builtin_nontemporal_store(f32x4{t.x, t.y, t.z, t.w}, reinterpret_cast<f32x4*>(&Sp[row * CPR + cg]));
@@ -105,16 +134,20 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(const DecodeParams 
     if (rg == 0) store4(reinterpret_cast<T*>(p.out) + (size_t)nh * D + 4 * cg, o[0], o[1], o[2], o[3]);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool FUSED>
 hipError_t launch_recurrent_step(const DecodeParams& p, hipStream_t stream) {
     const int nwg = p.N * p.H_v;
-    if (nwg > 0) hipLaunchKernelGGL((recurrent_step_kernel<T, D>), dim3(nwg), dim3(256), 0, stream, p);
+    if (nwg > 0) hipLaunchKernelGGL((recurrent_step_kernel<T, D, FUSED>), dim3(nwg), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
-template hipError_t launch_recurrent_step<bf16, 128>(const DecodeParams&, hipStream_t);
-template hipError_t launch_recurrent_step<bf16, 64>(const DecodeParams&, hipStream_t);
-template hipError_t launch_recurrent_step<float, 128>(const DecodeParams&, hipStream_t);
-template hipError_t launch_recurrent_step<float, 64>(const DecodeParams&, hipStream_t);
+template hipError_t launch_recurrent_step<bf16, 128, false>(const DecodeParams&, hipStream_t);
+template hipError_t launch_recurrent_step<bf16, 64, false>(const DecodeParams&, hipStream_t);
+template hipError_t launch_recurrent_step<float, 128, false>(const DecodeParams&, hipStream_t);
+template hipError_t launch_recurrent_step<float, 64, false>(const DecodeParams&, hipStream_t);
+template hipError_t launch_recurrent_step<bf16, 128, true>(const DecodeParams&, hipStream_t);
+template hipError_t launch_recurrent_step<bf16, 64, true>(const DecodeParams&, hipStream_t);
+template hipError_t launch_recurrent_step<float, 128, true>(const DecodeParams&, hipStream_t);
+template hipError_t launch_recurrent_step<float, 64, true>(const DecodeParams&, hipStream_t);
 
 }  // namespace gdn

@@ -51,8 +51,12 @@ struct DecodeParams {
     const void* q;
     const void* k;
     const void* v;
-    const float* g;
-    const float* beta;
+    const float* g;       // plain step: per (n, h) log gate
+    const float* beta;    // plain step: per (n, h) beta
+    const void* a;        // fused step: per (n, h) gate input, dtype of q
+    const void* b;        // fused step: per (n, h) beta input, dtype of q
+    const float* A_log;   // fused step: per value head
+    const float* dt_bias; // fused step: per value head
     float* state;
     void* out;
     int32_t N, H_q, H_v, G;
@@ -65,7 +69,7 @@ struct DecodeParams {
 template <typename T, int D>
 hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEvent_t const* events);
 
-template <typename T, int D>
+template <typename T, int D, bool FUSED>
 hipError_t launch_recurrent_step(const DecodeParams& p, hipStream_t stream);
 
 }  // namespace gdn

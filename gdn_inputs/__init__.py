@@ -204,6 +204,40 @@ def make_decode_token(seed: int, N: int, H_q: int, H_v: int, d_k: int, d_v: int,
     return DecodeToken(dtype, q, k, v, g, beta)
 
 
+@dataclasses.dataclass
+class DecodeRawToken:
+    """Raw inputs of one fused decode step: q, k [N, H_q, d_k] (not normalised),
+    v [N, H_v, d_v], a, b [N, H_v] in the storage dtype; A_log, dt_bias [H_v] float32."""
+
+    dtype: str
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    a: np.ndarray
+    b: np.ndarray
+    A_log: np.ndarray
+    dt_bias: np.ndarray
+
+    def f32(self, name):
+        return storage_to_f32(getattr(self, name), self.dtype)
+
+
+def make_decode_raw_token(seed: int, N: int, H_q: int, H_v: int, d_k: int, d_v: int,
+                          dtype: str = "bf16") -> DecodeRawToken:
+    """q, k, v, a, b ~ N(0, 1) (projection / convolution outputs, unnormalised);
+    per value head A_log = ln U(1, 16) and dt_bias ~ U(-7, -2.3) (so the gate input
+    a + dt_bias sits around the range of softplus used by decay rates)."""
+    rng = np.random.default_rng(seed)
+    q = round_to(rng.standard_normal((N, H_q, d_k), dtype=np.float32), dtype)
+    k = round_to(rng.standard_normal((N, H_q, d_k), dtype=np.float32), dtype)
+    v = round_to(rng.standard_normal((N, H_v, d_v), dtype=np.float32), dtype)
+    a = round_to(rng.standard_normal((N, H_v), dtype=np.float32), dtype)
+    b = round_to(rng.standard_normal((N, H_v), dtype=np.float32), dtype)
+    A_log = np.log(rng.uniform(1.0, 16.0, size=H_v)).astype(np.float32)
+    dt_bias = rng.uniform(-7.0, -2.3, size=H_v).astype(np.float32)
+    return DecodeRawToken(dtype, q, k, v, a, b, A_log, dt_bias)
+
+
 def make_decode_state(seed: int, N: int, H_v: int, d_k: int, d_v: int, std: float = 0.02) -> np.ndarray:
     rng = np.random.default_rng(seed)
     return (rng.standard_normal((N, H_v, d_k, d_v), dtype=np.float32) * np.float32(std)).astype(np.float32)

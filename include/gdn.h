@@ -180,6 +180,30 @@ int gdn_recurrent_step(const void *q, const void *k, const void *v, const float 
                        void *out, int32_t N, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
                        gdn_dtype dtype, void *stream);
 
+/*
+ * One recurrent decode step with its front end fused in ("Qwen3.5-397B-A17B"
+ * trace page, Decode-GDN node 7, gdn_packed_recurrent_qk_norm_gating_state_update,
+ * all four steps).  Takes the raw per-token inputs of that node; for every
+ * sequence n and value head h (query/key head h / (H_v / H_q)):
+ *     k_bar = k / sqrt(sum_j k_j^2 + 1e-6),   q_bar = scale * q / sqrt(sum_j q_j^2 + 1e-6)
+ *     g = -exp(A_log[h]) * softplus(a[n,h] + dt_bias[h]),   alpha = exp(g)
+ *         (softplus(x) = x for x > 20, exp(x) for x < -20, log1p(exp(x)) otherwise)
+ *     beta = sigmoid(b[n,h]) rounded to `dtype` (the bf16 rounding the page keeps)
+ *     S = alpha S;  delta = beta (v - k_bar S);  S = S + k_bar^T delta;  o = q_bar S
+ * in fp32, one pass over S.  The model's query scale is 1 / sqrt(d_k).
+ *
+ *   q, k     dtype [N, H_q, d_k]   (not normalised)    v dtype [N, H_v, d_v]
+ *   a, b     dtype [N, H_v]        A_log, dt_bias fp32 [H_v]
+ *   state    fp32 [N, H_v, d_k, d_v], updated IN PLACE
+ *   out      dtype [N, H_v, d_v]
+ * q, k, v, state, out 16-byte aligned; a, b, A_log, dt_bias aligned to their
+ * element size.  Errors as gdn_recurrent_step.  N == 0 is a no-op returning GDN_OK.
+ */
+int gdn_recurrent_step_fused(const void *q, const void *k, const void *v, const void *a, const void *b,
+                             const float *A_log, const float *dt_bias, float *state, void *out, int32_t N,
+                             int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale, gdn_dtype dtype,
+                             void *stream);
+
 /* Static string naming a status code. */
 const char *gdn_status_string(int status);
 

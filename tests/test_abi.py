@@ -162,6 +162,29 @@ def test_recurrent_step_rejects_before_any_device_work(gdn):
     assert call(N=0) == 0
 
 
+def test_recurrent_step_fused_rejects_before_any_device_work(gdn):
+    lib = gdn.load_library()
+    keep, p = _fake()
+    good = dict(q=p, k=p, v=p, a=p, b=p, A=p, dtb=p, st=p, out=p, N=4, H_q=2, H_v=4, dk=128, dv=128, scale=0.1,
+                dt=1, stream=None)
+
+    def call(**kw):
+        x = dict(good, **kw)
+        return lib.gdn_recurrent_step_fused(x["q"], x["k"], x["v"], x["a"], x["b"], x["A"], x["dtb"], x["st"],
+                                            x["out"], x["N"], x["H_q"], x["H_v"], x["dk"], x["dv"], x["scale"],
+                                            x["dt"], x["stream"])
+
+    assert call(a=None) == -1
+    assert call(dtb=None) == -1
+    assert call(q=p + 8) == -2                 # misaligned tensor
+    assert call(a=p + 1) == -2                 # bf16 scalar off its 2-byte alignment
+    assert call(A=p + 2) == -2                 # fp32 parameter off its 4-byte alignment
+    assert call(H_q=3) == -2
+    assert call(N=-1) == -1
+    assert call(scale=float("nan")) == -1
+    assert call(N=0) == 0
+
+
 def test_binding_refuses_host_tensors(gdn):
     torch = pytest.importorskip("torch")
     q = torch.zeros(4, 2, 64)
