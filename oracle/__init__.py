@@ -30,6 +30,11 @@ the exact softplus, sigmoid's logit identity and exact bf16 representability
 of the rounded beta, invariance of the step under scaling q or k (L2 norm),
 zero keys reducing to pure decay, and the page's merged update
 S' = alpha (I - beta k^T k) S + beta k^T v evaluated with numpy matrices.
+
+``gated_rmsnorm`` is the read-out epilogue (oracle/gated_norm.py).  Pins:
+invariance under scaling o (eps = 0), zero gate gives zero, the unit RMS of
+the normalised read-out under a saturated gate, silu(z) - silu(-z) = z, and
+linearity in the weight.
 """
 from __future__ import annotations
 
@@ -39,6 +44,7 @@ import os
 import numpy as np
 
 from . import chunk_form  # noqa: F401
+from .gated_norm import gated_rmsnorm  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdn_oracle.so")

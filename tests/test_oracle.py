@@ -491,3 +491,31 @@ def test_fused_front_end_then_plain_step(oracle_mod):
     S2 = np.ascontiguousarray(S.copy())
     o2 = oracle_mod.decode_step(nrm(q), nrm(k), v, g, beta, S2, H_q, H_v, 0.2)
     assert _rel(o2, out) < 1e-6 and _rel(S2, S1) < 1e-6
+
+
+# ---------------------------------------------------------------------------
+# Gated RMSNorm epilogue ("Qwen3.5-397B-A17B" trace page, node 8)
+# ---------------------------------------------------------------------------
+def test_gated_rmsnorm_pins():
+    from oracle import gated_rmsnorm
+
+    rng = np.random.default_rng(6)
+    o = rng.standard_normal((5, 3, 64))
+    z = 2.0 * rng.standard_normal((5, 3, 64))
+    w = rng.uniform(0.5, 1.5, 64)
+    y = gated_rmsnorm(o, z, w, 0.0)
+    # an RMS norm: scaling the read-out changes nothing (eps = 0)
+    assert _rel(gated_rmsnorm(7.5 * o, z, w, 0.0), y) < 1e-14
+    # a closed gate (z = 0) gives zero; silu(z) - silu(-z) = z
+    assert np.all(gated_rmsnorm(o, np.zeros_like(z), w, 1e-6) == 0)
+    diff = gated_rmsnorm(o, z, w, 0.0) - gated_rmsnorm(o, -z, w, 0.0)
+    unit = gated_rmsnorm(o, np.ones_like(z), np.ones_like(w), 0.0) / (1 / (1 + np.exp(-1.0)))
+    assert _rel(diff, unit * w * z) < 1e-13
+    # saturated gate (silu(40) = 40 to double precision), unit weight: mean of squares
+    # of y / 40 equals ms / (ms + eps) with ms the read-out's mean square
+    eps = 1e-3
+    y40 = gated_rmsnorm(o, np.full_like(z, 40.0), np.ones_like(w), eps) / 40.0
+    ms = np.mean(o * o, axis=-1)
+    assert _rel(np.mean(y40 * y40, axis=-1), ms / (ms + eps)) < 1e-12
+    # linear in the weight
+    assert _rel(gated_rmsnorm(o, z, 3.0 * w, 1e-6), 3.0 * gated_rmsnorm(o, z, w, 1e-6)) < 1e-14
