@@ -50,7 +50,7 @@ CHUNK = 64
 # exploited)
 # ---------------------------------------------------------------------------
 
-def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True):
+def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True, gated=False):
     """Algorithmic bytes and flops of each kernel of one gdn_chunk_fwd.
 
     Bytes: every distinct input read once, every output and intermediate written
@@ -77,7 +77,7 @@ def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True):
     bytes_ = {
         "chunk_prep": k_b + v_b + 2 * gate_b + gc_b + W_b + U_b + Kd_b,   # A stays on chip
         "chunk_state_h": W_b + U_b + Kd_b + gc_b + (S_b if has_s0 else 0) + H_b + X_b + S_b,
-        "chunk_output_o": q_b + k_b + gc_b + H_b + X_b + o_b,
+        "chunk_output_o": q_b + k_b + gc_b + H_b + X_b + o_b + ((o_b + d * 4) if gated else 0),  # z, weight
     }
     flops = {k: 2 * v * chv for k, v in per.items()}
     return bytes_, flops
@@ -170,7 +170,9 @@ def _traffic_from_profiles(kernel: str, workload: str):
 # measurements
 # ---------------------------------------------------------------------------
 
-def bench_prefill(args, torch, gdn, hip, device):
+def bench_prefill(args, torch, gdn, hip, device, gated=False):
+    """The prefill step; with gated, out also passes through the gated RMSNorm
+    read-out epilogue (z and weight seeded, eps 1e-6)."""
     import gdn_inputs
 
     inp = gdn_inputs.make_workload(args.workload)
@@ -187,6 +189,12 @@ def bench_prefill(args, torch, gdn, hip, device):
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
     code = gdn.DTYPE_BF16 if dt == "bf16" else gdn.DTYPE_F32
+    gate_ref = None
+    if gated:
+        z, w = gdn_inputs.make_gate(93, inp.T, inp.H_v, inp.d_v, dt)
+        zt, wt = _dev(z, dt, torch, device), _dev(w, "f32", torch, device)
+        gate_obj = gdn.OutputGate(zt.data_ptr(), wt.data_ptr(), 1e-6)
+        gate_ref = ctypes.byref(gate_obj)
     K = args.steps
     NEV = 2 * len(STAGES)
     ev = [[hip.event() for _ in range(NEV)] for _ in range(max(K, 1))]
@@ -195,10 +203,18 @@ def bench_prefill(args, torch, gdn, hip, device):
         arr = None
         if events is not None:
             arr = (ctypes.c_void_p * NEV)(*[e.value for e in events])
+        if events is None and gate_ref is None:
+            rc = lib.gdn_chunk_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), cu,
+                                   inp.N, None if s0 is None else s0.data_ptr(), out.data_ptr(), fin.data_ptr(),
+                                   inp.T, inp.H_q, inp.H_v, inp.d_k, inp.d_v, inp.scale, code, ws.data_ptr(),
+                                   lay["total_bytes"], ctypes.c_void_p(sptr))
+            if rc != 0:
+                raise gdn.GdnError(rc, "gdn_chunk_fwd")
+            return
         rc = lib.gdn_chunk_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), cu,
                                   inp.N, None if s0 is None else s0.data_ptr(), out.data_ptr(), fin.data_ptr(),
                                   inp.T, inp.H_q, inp.H_v, inp.d_k, inp.d_v, inp.scale, code, ws.data_ptr(),
-                                  lay["total_bytes"], ctypes.c_void_p(sptr), 0, arr)
+                                  lay["total_bytes"], ctypes.c_void_p(sptr), 0, gate_ref, arr)
         if rc != 0:
             raise gdn.GdnError(rc, "gdn_chunk_fwd_ex")
 
@@ -228,12 +244,12 @@ def bench_prefill(args, torch, gdn, hip, device):
     ms_step = total_ms / K
     es = 2 if dt == "bf16" else 4
     bytes_, flops = prefill_work(inp.T, inp.N, lay["n_chunks"], inp.H_q, inp.H_v, inp.d_k, es,
-                                 has_s0=s0 is not None)
+                                 has_s0=s0 is not None, gated=gated)
     return dict(inp=inp, lay=lay, ms_step=ms_step, wall_s=wall, stage_ms=stage_ms, bytes=bytes_, flops=flops,
                 ms_step_with_events=timed_ms)
 
 
-def bench_decode(args, torch, gdn, hip, device, fused=False):
+def bench_decode(args, torch, gdn, hip, device, fused=False, gated=False):
     """Decode steps on the 256 x 32-head batch: the plain step (normalised q, k and
     final g, beta) or, with fused, the step from raw q, k, a, b (front end inside)."""
     import gdn_inputs
@@ -252,6 +268,11 @@ def bench_decode(args, torch, gdn, hip, device, fused=False):
             toks.append(tuple(_dev(x, dt, torch, device) for x in (t.q, t.k, t.v)) +
                         (_dev(t.g, "f32", torch, device), _dev(t.beta, "f32", torch, device)))
     step_fn = gdn.recurrent_step_fused if fused else gdn.recurrent_step
+    if gated:
+        z, w = gdn_inputs.make_gate(97, N, H_v, d, dt)
+        gate = (_dev(z, dt, torch, device), _dev(w, "f32", torch, device), 1e-6)
+        plain_fn = step_fn
+        step_fn = lambda *a, **kw: plain_fn(*a, gate=gate, **kw)  # noqa: E731
     out = torch.empty((N, H_v, d), dtype=toks[0][0].dtype, device=device)
     scale = 1.0 / math.sqrt(d)
     K = max(args.steps, cfg["steps"])
@@ -277,6 +298,8 @@ def bench_decode(args, torch, gdn, hip, device, fused=False):
     torch.cuda.synchronize()
     kms = sum(hip.elapsed_ms(a, b) for a, b in evs) / K
     nbytes, nflops = decode_work(N, H_q, H_v, d, 2 if dt == "bf16" else 4, fused=fused)
+    if gated:
+        nbytes += N * H_v * d * (2 if dt == "bf16" else 4) + d * 4  # z, weight
     return dict(N=N, ms_step=ms, kernel_ms=kms, bytes=nbytes, flops=nflops, steps=K)
 
 
@@ -356,16 +379,22 @@ def main():
         return
 
     res = {}
-    pre = dec = decf = None
+    pre = pre_g = dec = decf = decg = None
     if args.only in ("all", "prefill"):
         pre = bench_prefill(args, torch, gdn, hip, device)
         print(f"[bench] prefill {args.workload}: {pre['ms_step']:.4f} ms/step, stages "
               + ", ".join(f"{s} {pre['stage_ms'][s] * 1e3:.1f} us" for s in STAGES), file=sys.stderr, flush=True)
+        pre_g = bench_prefill(args, torch, gdn, hip, device, gated=True)
+        print(f"[bench] prefill {args.workload} + gated read-out: {pre_g['ms_step']:.4f} ms/step, chunk_output_o "
+              f"{pre_g['stage_ms']['chunk_output_o'] * 1e3:.1f} us", file=sys.stderr, flush=True)
     if args.only in ("all", "decode"):
         dec = bench_decode(args, torch, gdn, hip, device)
         print(f"[bench] decode: {dec['ms_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
         decf = bench_decode(args, torch, gdn, hip, device, fused=True)
         print(f"[bench] decode (fused front end): {decf['ms_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+        decg = bench_decode(args, torch, gdn, hip, device, fused=True, gated=True)
+        print(f"[bench] decode (front end + gated read-out): {decg['ms_step'] * 1e3:.1f} us/step", file=sys.stderr,
+              flush=True)
 
     if pre is not None:
         inp = pre["inp"]
@@ -420,6 +449,21 @@ def main():
                         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
                         "config": {"workload": "decode_256x1"}, "roofline": decode["roofline"]})
         res["decode"] = decode
+    if pre_g is not None:
+        og = pre_g["stage_ms"]["chunk_output_o"] * 1e-3
+        res["prefill_gated"] = {
+            "workload": args.workload + " with the gated RMSNorm read-out epilogue in chunk_output_o",
+            "ms_per_step": pre_g["ms_step"], "tokens_per_s": pre_g["inp"].T / (pre_g["ms_step"] * 1e-3),
+            "stages_us": {s: pre_g["stage_ms"][s] * 1e3 for s in STAGES},
+            "chunk_output_o_hbm_frac": pre_g["bytes"]["chunk_output_o"] / og / 1e9 / HBM_PEAK_GBS}
+    if decg is not None:
+        kg = decg["bytes"] / (decg["kernel_ms"] * 1e-3) / 1e9
+        res["decode_fused_gated"] = {
+            "workload": "decode_256x1 from raw inputs, with the gated RMSNorm read-out (nodes 7 and 8 in one pass)",
+            "us_per_step": decg["ms_step"] * 1e3, "kernel_us": decg["kernel_ms"] * 1e3,
+            "tokens_per_s": decg["N"] / (decg["ms_step"] * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": kg, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": kg / HBM_PEAK_GBS, "traffic": None}}
     if decf is not None:
         kgbs = decf["bytes"] / (decf["kernel_ms"] * 1e-3) / 1e9
         res["decode_fused"] = {

@@ -46,6 +46,25 @@ class WorkspaceLayout(ctypes.Structure):
                 ("off_Ht", ctypes.c_size_t), ("off_Xt", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t)]
 
 
+class OutputGate(ctypes.Structure):
+    """gdn_output_gate: read-out epilogue out = rmsnorm(o) * weight * silu(z)."""
+    _fields_ = [("z", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
+def _gate_arg(gate, dtype, rows, H_v, d_v):
+    """(z, weight, eps) -> (ctypes pointer or None, keep-alive)."""
+    if gate is None:
+        return None, None
+    torch = _torch()
+    z, weight, eps = gate
+    _check_dev("z", z, dtype)
+    _check_dev("gate weight", weight, torch.float32)
+    if tuple(z.shape) != (rows, H_v, d_v) or tuple(weight.shape) != (d_v,):
+        raise ValueError("gate: z must be [rows, H_v, d_v] and weight [d_v]")
+    g = OutputGate(_ptr(z), _ptr(weight), float(eps))
+    return ctypes.byref(g), g
+
+
 def lib_path() -> str:
     return _LIB_PATH
 
@@ -74,11 +93,12 @@ def load_library():
     lib.gdn_chunk_fwd.argtypes = [P, P, P, P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P,
                                   ctypes.c_size_t, P]
     lib.gdn_chunk_fwd.restype = ctypes.c_int
-    lib.gdn_chunk_fwd_ex.argtypes = lib.gdn_chunk_fwd.argtypes + [ctypes.c_uint32, P]
+    lib.gdn_chunk_fwd_ex.argtypes = lib.gdn_chunk_fwd.argtypes + [ctypes.c_uint32, P, P]
     lib.gdn_chunk_fwd_ex.restype = ctypes.c_int
     lib.gdn_recurrent_step.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P]
     lib.gdn_recurrent_step.restype = ctypes.c_int
-    lib.gdn_recurrent_step_fused.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P]
+    lib.gdn_recurrent_step_fused.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P,
+                                             P]
     lib.gdn_recurrent_step_fused.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -164,7 +184,7 @@ def workspace_size(T: int, cu_seqlens, H_q: int, H_v: int, d_k: int, d_v: int, d
 
 def chunk_fwd(q, k, v, g, beta, cu_seqlens: Sequence[int], initial_state=None, scale: Optional[float] = None,
               out=None, final_state=None, output_final_state: bool = True, workspace=None, stream=None,
-              keep_A: bool = False):
+              keep_A: bool = False, gate=None):
     """Chunk-wise GDN prefill over a packed batch (gdn_chunk_fwd; gdn_chunk_fwd_ex with keep_A).
 
     q, k: [T, H_q, d_k]; v: [T, H_v, d_v] (bf16 or fp32, same dtype); g, beta:
@@ -172,7 +192,9 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens: Sequence[int], initial_state=None, s
     initial_state: fp32 [N, H_v, d_k, d_v] or None.  Returns (out, final_state)
     with final_state None when output_final_state is False.  ``workspace`` may
     be a preallocated uint8 device tensor of at least workspace_size() bytes;
-    keep_A also writes the A intermediate into it (GDN_FWD_KEEP_A).
+    keep_A also writes the A intermediate into it (GDN_FWD_KEEP_A).  ``gate`` =
+    (z [T, H_v, d_v] in q's dtype, weight fp32 [d_v], eps) applies the gated
+    RMSNorm read-out epilogue to out (gdn_chunk_fwd_ex).
     """
     torch = _torch()
     lib = load_library()
@@ -213,8 +235,9 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens: Sequence[int], initial_state=None, s
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), cu, N, _ptr(initial_state), _ptr(out),
             _ptr(final_state), T, H_q, H_v, d_k, d_v, float(scale), dt, _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream_ptr(stream))
-    if keep_A:
-        rc, name = lib.gdn_chunk_fwd_ex(*args, FWD_KEEP_A, None), "gdn_chunk_fwd_ex"
+    gptr, _keep = _gate_arg(gate, q.dtype, T, H_v, d_v)
+    if keep_A or gate is not None:
+        rc, name = lib.gdn_chunk_fwd_ex(*args, FWD_KEEP_A if keep_A else 0, gptr, None), "gdn_chunk_fwd_ex"
     else:
         rc, name = lib.gdn_chunk_fwd(*args), "gdn_chunk_fwd"
     if rc != 0:
@@ -255,14 +278,15 @@ def recurrent_step(q, k, v, g, beta, state, scale: Optional[float] = None, out=N
 
 
 def recurrent_step_fused(q, k, v, a, b, A_log, dt_bias, state, scale: Optional[float] = None, out=None,
-                         stream=None):
+                         stream=None, gate=None):
     """One decode step from the raw inputs (gdn_recurrent_step_fused): q/k L2 norm,
     gate from a, A_log, dt_bias, beta from b, then the state update; ``state`` is
     updated in place.
 
     q, k: [N, H_q, d_k] (not normalised); v: [N, H_v, d_v]; a, b: [N, H_v] (q's
     dtype); A_log, dt_bias: fp32 [H_v]; state: fp32 [N, H_v, d_k, d_v].  Returns
-    out [N, H_v, d_v] in q's dtype.  scale defaults to 1/sqrt(d_k).
+    out [N, H_v, d_v] in q's dtype.  scale defaults to 1/sqrt(d_k).  ``gate`` =
+    (z [N, H_v, d_v], weight fp32 [d_v], eps) adds the gated RMSNorm read-out.
     """
     torch = _torch()
     lib = load_library()
@@ -283,8 +307,9 @@ def recurrent_step_fused(q, k, v, a, b, A_log, dt_bias, state, scale: Optional[f
         out = torch.empty((N, H_v, d_v), dtype=q.dtype, device=q.device)
     else:
         _check_dev("out", out, q.dtype)
+    gptr, _keep = _gate_arg(gate, q.dtype, N, H_v, d_v)
     rc = lib.gdn_recurrent_step_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
-                                      _ptr(state), _ptr(out), N, H_q, H_v, d_k, d_v, float(scale), dt,
+                                      _ptr(state), _ptr(out), N, H_q, H_v, d_k, d_v, float(scale), dt, gptr,
                                       _stream_ptr(stream))
     if rc != 0:
         raise GdnError(rc, "gdn_recurrent_step_fused")

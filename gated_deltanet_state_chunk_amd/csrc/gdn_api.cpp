@@ -3,6 +3,7 @@
 // nothing and never touches the device (all-or-nothing entry points).
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <string>
 
 #include "gdn.h"
@@ -24,6 +25,14 @@ int check_shapes(int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype d
     if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
     if (d_k != d_v || (d_k != 64 && d_k != 128)) return GDN_ERR_UNSUPPORTED;
     if (H_v % H_q != 0) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+// Read-out epilogue arguments: z and weight present and 16-byte aligned, eps > 0.
+int check_gate(const gdn_output_gate* gate, bool need_z) {
+    if (!(gate->eps > 0.f) || !(gate->eps < INFINITY)) return GDN_ERR_INVALID;
+    if (need_z && (!gate->z || !gate->weight)) return GDN_ERR_INVALID;
+    if ((gate->z && !aligned16(gate->z)) || (gate->weight && !aligned16(gate->weight))) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }
 
@@ -128,15 +137,19 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                   float* final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
                   gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
     return gdn_chunk_fwd_ex(q, k, v, g, beta, cu_seqlens_host, num_seqs, initial_state, out, final_state, T, H_q, H_v,
-                            d_k, d_v, scale, dtype, workspace, workspace_bytes, stream, 0u, nullptr);
+                            d_k, d_v, scale, dtype, workspace, workspace_bytes, stream, 0u, nullptr, nullptr);
 }
 
 int gdn_chunk_fwd_ex(const void* q, const void* k, const void* v, const float* g, const float* beta,
                      const int32_t* cu_seqlens_host, int32_t num_seqs, const float* initial_state, void* out,
                      float* final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
                      gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream, uint32_t flags,
-                     void* const* stage_events) {
+                     const gdn_output_gate* gate, void* const* stage_events) {
     if (flags & ~(uint32_t)GDN_FWD_KEEP_A) return GDN_ERR_INVALID;
+    if (gate) {
+        const int grc = check_gate(gate, T > 0);
+        if (grc != GDN_OK) return grc;
+    }
     gdn_workspace_layout L;
     int rc = gdn_chunk_fwd_workspace_layout(T, num_seqs, cu_seqlens_host, H_q, H_v, d_k, d_v, dtype, &L);
     if (rc != GDN_OK) return rc;
@@ -158,6 +171,9 @@ int gdn_chunk_fwd_ex(const void* q, const void* k, const void* v, const float* g
     p.Ht = ws + L.off_Ht; p.Xt = ws + L.off_Xt;
     p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
     p.keep_A = (flags & GDN_FWD_KEEP_A) ? 1 : 0;
+    p.gz = gate ? gate->z : nullptr;
+    p.gw = gate ? gate->weight : nullptr;
+    p.geps = gate ? gate->eps : 0.f;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     // Launch groups of up to MAX_SEQS_PER_LAUNCH sequences, each with its table in the kernel arguments.
@@ -207,7 +223,7 @@ int gdn_recurrent_step(const void* q, const void* k, const void* v, const float*
 int gdn_recurrent_step_fused(const void* q, const void* k, const void* v, const void* a, const void* b,
                              const float* A_log, const float* dt_bias, float* state, void* out, int32_t N,
                              int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale, gdn_dtype dtype,
-                             void* stream) {
+                             const gdn_output_gate* gate, void* stream) {
     int rc = check_shapes(H_q, H_v, d_k, d_v, dtype);
     if (rc != GDN_OK) return rc;
     if (N < 0) return GDN_ERR_INVALID;
@@ -223,8 +239,15 @@ int gdn_recurrent_step_fused(const void* q, const void* k, const void* v, const 
         (reinterpret_cast<uintptr_t>(A_log) & 3u) || (reinterpret_cast<uintptr_t>(dt_bias) & 3u))
         return GDN_ERR_UNSUPPORTED;
     if (!(scale == scale)) return GDN_ERR_INVALID;
+    if (gate) {
+        const int grc = check_gate(gate, true);
+        if (grc != GDN_OK) return grc;
+    }
     gdn::DecodeParams p{};
     p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.A_log = A_log; p.dt_bias = dt_bias;
+    p.gz = gate ? gate->z : nullptr;
+    p.gw = gate ? gate->weight : nullptr;
+    p.geps = gate ? gate->eps : 0.f;
     p.state = state; p.out = out;
     p.N = N; p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
     const hipError_t e = run_decode<true>(p, dtype, d_k, static_cast<hipStream_t>(stream));

@@ -740,7 +740,11 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
 //    P^T[j][i] = (k_j . q_i) exp(gc_i - gc_j) for j <= i  (Lower keeps the diagonal).
 //    Q and K are staged in LDS once; wave w forms the P^T tiles of query block w
 //    and publishes them in operand order; then each wave produces its 16-row
-//    tiles of O^T (d_v rows) for all 64 positions.
+//    tiles of O^T (d_v rows) for all 64 positions.  With the read-out
+//    epilogue (trace page, Decode-GDN node 8; node 18 of the prefill graph)
+//    the tiles stay in registers until each position's sum of squares over
+//    d_v has been reduced across the lanes and waves, then
+//    out = o / sqrt(mean o^2 + eps) * weight * silu(z) is stored instead of o.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct OutLds {
@@ -749,9 +753,10 @@ struct OutLds {
     T K[CHUNK][KP];
     Frag<T> P[4][2][64];  // B operand of (U - W S)^T P^T: [query tile][K-step][lane]
     float gc[CHUNK];
+    float ss[4][CHUNK];   // gated read-out: per-wave sums of o^2 per position
 };
 
-template <typename T, int D>
+template <typename T, int D, bool GATED>
 __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p, int padded) {
     using OL = OutLds<T, D>;
     constexpr int KS = D / 32;
@@ -795,6 +800,24 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
     }
     if (tid < CHUNK) s.gc[tid] = p.gc[ch * CHUNK + tid];
     lds_sync();
+    // Gated read-out: this lane's z values (rows past the valid length re-read the
+    // last valid row; they are never stored) and norm weights, fetched after the Q/K staging
+    // (so those loads are not queued behind them).
+    Raw4<T> zr[GATED ? 4 : 1][GATED ? TPW : 1];
+    float4 wv[GATED ? TPW : 1];
+    if constexpr (GATED) {
+        const T* zb = reinterpret_cast<const T*>(p.gz) + (size_t)cp.t0 * p.H_v * D + (size_t)h * D;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                const int pos = min(16 * nt + r16, ell - 1);
+                load_raw4(zr[nt][tt], zb + (size_t)pos * p.H_v * D + 16 * (w * TPW + tt) + 4 * grp);
+            }
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+            wv[tt] = *reinterpret_cast<const float4*>(p.gw + 16 * (w * TPW + tt) + 4 * grp);
+    }
 
     // P^T tiles (I, J = w) for I <= w, published as B fragments for query tile w.
     {
@@ -834,6 +857,7 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
 
     // Output tiles: rows d_v (this wave's tiles), columns pos.
     T* ob = reinterpret_cast<T*>(p.out) + (size_t)cp.t0 * p.H_v * D + (size_t)h * D;
+    f32x4 ov[GATED ? 4 : 1][TPW];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
         Frag<T> qf[KS], pf[2];
@@ -850,11 +874,47 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
             for (int ks = 0; ks < KS; ++ks) inter = mma(hf[tt][ks], qf[ks], inter);
             intra = mma(xf[tt][0], pf[0], intra);
             if (nt >= 2) intra = mma(xf[tt][1], pf[1], intra);  // P^T rows 32..63 vanish for queries < 32
-            if (pos < ell) {
-                float o4[4];
+            f32x4 o4;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o4[i] = p.scale * (eg * inter[i] + intra[i]);
+            for (int i = 0; i < 4; ++i) o4[i] = p.scale * (eg * inter[i] + intra[i]);
+            if constexpr (GATED) {
+                ov[nt][tt] = o4;
+            } else if (pos < ell) {
                 store4(ob + (size_t)pos * p.H_v * D + 16 * (w * TPW + tt) + 4 * grp, o4[0], o4[1], o4[2], o4[3]);
+            }
+        }
+    }
+    if constexpr (GATED) {
+        // Head-wise RMS over d_v: this lane's values, the four lanes sharing a
+        // position (grp), then the four waves through LDS.
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            float ssq = 0.f;
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ssq += ov[nt][tt][i] * ov[nt][tt][i];
+            ssq += wave_shfl_xor(ssq, 16);
+            ssq += wave_shfl_xor(ssq, 32);
+            if (grp == 0) s.ss[w][16 * nt + r16] = ssq;
+        }
+        lds_sync();
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int pos = 16 * nt + r16;
+            const float rstd =
+                1.f / sqrtf((s.ss[0][pos] + s.ss[1][pos] + s.ss[2][pos] + s.ss[3][pos]) * (1.f / D) + p.geps);
+            if (pos < ell) {
+#pragma unroll
+                for (int tt = 0; tt < TPW; ++tt) {
+                    const f32x4 zf = raw4_to_f32(zr[nt][tt]);
+                    const float wf[4] = {wv[tt].x, wv[tt].y, wv[tt].z, wv[tt].w};
+                    float y[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        y[i] = ov[nt][tt][i] * rstd * wf[i] * (zf[i] / (1.f + __expf(-zf[i])));
+                    store4(ob + (size_t)pos * p.H_v * D + 16 * (w * TPW + tt) + 4 * grp, y[0], y[1], y[2], y[3]);
+                }
             }
         }
     }
@@ -883,7 +943,12 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
     };
     if (work_ch > 0) launch(0, chunk_prep_kernel<T, D>, grid_ch, 256);
     if (work_st > 0) launch(1, chunk_state_h_kernel<T, D>, grid_st, 64 * (5 + StateStage<T, D>::NPW));
-    if (work_ch > 0) launch(2, chunk_output_o_kernel<T, D>, grid_ch, 256);
+    if (work_ch > 0) {
+        if (p.gz)
+            launch(2, chunk_output_o_kernel<T, D, true>, grid_ch, 256);
+        else
+            launch(2, chunk_output_o_kernel<T, D, false>, grid_ch, 256);
+    }
     return hipGetLastError();
 }
 

@@ -131,6 +131,22 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(const DecodeParams 
         // it out of the caches measurably raises the read/write stream rate
         __builtin_nontemporal_store(f32x4{t.x, t.y, t.z, t.w}, reinterpret_cast<f32x4*>(&Sp[row * CPR + cg]));
     }
+    if constexpr (FUSED) {
+        if (p.gz) {
+            // Gated read-out (trace page, Decode-GDN node 8): every group of CPR
+            // consecutive lanes holds the head's d_v outputs, 4 per lane.
+            float ssq = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
+#pragma unroll
+            for (int msk = 1; msk < CPR; msk <<= 1) ssq += wave_shfl_xor(ssq, msk);
+            const float rstd = 1.f / sqrtf(ssq * (1.f / D) + p.geps);
+            float zv[4];
+            load4(reinterpret_cast<const T*>(p.gz) + (size_t)nh * D + 4 * cg, zv[0], zv[1], zv[2], zv[3]);
+            const float4 wv = *reinterpret_cast<const float4*>(p.gw + 4 * cg);
+            const float wf[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) o[c] = o[c] * rstd * wf[c] * (zv[c] / (1.f + __expf(-zv[c])));
+        }
+    }
     if (rg == 0) store4(reinterpret_cast<T*>(p.out) + (size_t)nh * D + 4 * cg, o[0], o[1], o[2], o[3]);
 }
 

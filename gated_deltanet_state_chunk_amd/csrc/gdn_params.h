@@ -44,6 +44,10 @@ struct ChunkParams {
     int32_t H_q, H_v, G;
     float scale;
     int32_t keep_A;  // nonzero: chunk_prep also writes A to the workspace
+    // optional read-out epilogue out = rmsnorm(o) * gw * silu(gz) (gz null: none)
+    const void* gz;
+    const float* gw;
+    float geps;
     SeqTable tab;
 };
 
@@ -59,6 +63,9 @@ struct DecodeParams {
     const float* dt_bias; // fused step: per value head
     float* state;
     void* out;
+    const void* gz;  // optional read-out epilogue (fused step only), as in ChunkParams
+    const float* gw;
+    float geps;
     int32_t N, H_q, H_v, G;
     float scale;
 };

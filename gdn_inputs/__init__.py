@@ -238,6 +238,15 @@ def make_decode_raw_token(seed: int, N: int, H_q: int, H_v: int, d_k: int, d_v: 
     return DecodeRawToken(dtype, q, k, v, a, b, A_log, dt_bias)
 
 
+def make_gate(seed: int, rows: int, H_v: int, d_v: int, dtype: str = "bf16"):
+    """Inputs of the gated RMSNorm read-out: z [rows, H_v, d_v] ~ N(0, 1) in the
+    storage dtype, weight [d_v] ~ U(0.5, 1.5) float32."""
+    rng = np.random.default_rng(seed)
+    z = round_to(rng.standard_normal((rows, H_v, d_v), dtype=np.float32), dtype)
+    w = rng.uniform(0.5, 1.5, size=d_v).astype(np.float32)
+    return z, w
+
+
 def make_decode_state(seed: int, N: int, H_v: int, d_k: int, d_v: int, std: float = 0.02) -> np.ndarray:
     rng = np.random.default_rng(seed)
     return (rng.standard_normal((N, H_v, d_k, d_v), dtype=np.float32) * np.float32(std)).astype(np.float32)

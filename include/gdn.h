@@ -137,6 +137,25 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
                   float *final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
                   gdn_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Optional read-out epilogue of gdn_chunk_fwd_ex and gdn_recurrent_step_fused:
+ * the head-wise gated RMSNorm that follows the GDN read-out ("Qwen3.5-397B-A17B"
+ * trace page, Decode-GDN node 8, output_rmsnorm_silu_gate; node 18 of the
+ * prefill graph):
+ *     out[t, h, :] = o / sqrt(mean_j o_j^2 + eps) * weight * silu(z[t, h, :]),
+ *     silu(x) = x * sigmoid(x),
+ * over the d_v channels of one value head, norm before gate, computed on the
+ * fp32 read-out o and rounded once to the output dtype.
+ *   z       dtype [T or N, H_v, d_v], 16-byte aligned
+ *   weight  fp32 [d_v] (multiplies directly), 16-byte aligned
+ *   eps     the model's norm epsilon (> 0)
+ */
+typedef struct gdn_output_gate {
+    const void *z;
+    const float *weight;
+    float eps;
+} gdn_output_gate;
+
 /* Flags of gdn_chunk_fwd_ex. */
 #define GDN_FWD_KEEP_A 1u /* also write A to its workspace region (otherwise that region is left untouched) */
 
@@ -147,6 +166,7 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
  *          back (W and U are formed from it on chip), so gdn_chunk_fwd does not
  *          spend the HBM write on it; GDN_FWD_KEEP_A writes it for inspection.
  *          Unknown bits: GDN_ERR_INVALID.
+ *   gate   NULL, or the read-out epilogue above applied to `out`.
  *   stage_events  NULL or an array of six hipEvent_t created by the caller:
  *          the start and stop events of the three kernels (chunk_prep: gate
  *          cumsum, A, W, U; chunk_state_h: the serial state scan;
@@ -159,7 +179,7 @@ int gdn_chunk_fwd_ex(const void *q, const void *k, const void *v, const float *g
                      const int32_t *cu_seqlens_host, int32_t num_seqs, const float *initial_state, void *out,
                      float *final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
                      gdn_dtype dtype, void *workspace, size_t workspace_bytes, void *stream, uint32_t flags,
-                     void *const *stage_events);
+                     const gdn_output_gate *gate, void *const *stage_events);
 
 /*
  * One recurrent decode step ("Qwen3.5-397B-A17B" trace page, Decode-GDN node 7,
@@ -196,13 +216,15 @@ int gdn_recurrent_step(const void *q, const void *k, const void *v, const float 
  *   a, b     dtype [N, H_v]        A_log, dt_bias fp32 [H_v]
  *   state    fp32 [N, H_v, d_k, d_v], updated IN PLACE
  *   out      dtype [N, H_v, d_v]
+ *   gate     NULL, or the read-out epilogue (gdn_output_gate) applied to out:
+ *            the whole of nodes 7 and 8 in one pass.
  * q, k, v, state, out 16-byte aligned; a, b, A_log, dt_bias aligned to their
  * element size.  Errors as gdn_recurrent_step.  N == 0 is a no-op returning GDN_OK.
  */
 int gdn_recurrent_step_fused(const void *q, const void *k, const void *v, const void *a, const void *b,
                              const float *A_log, const float *dt_bias, float *state, void *out, int32_t N,
                              int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale, gdn_dtype dtype,
-                             void *stream);
+                             const gdn_output_gate *gate, void *stream);
 
 /* Static string naming a status code. */
 const char *gdn_status_string(int status);

@@ -137,9 +137,21 @@ def test_chunk_fwd_rejects_before_any_device_work(gdn):
         a = dict(good, **kw)
         return lib.gdn_chunk_fwd_ex(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"], a["s0"], a["out"],
                                     a["fin"], a["T"], a["H_q"], a["H_v"], a["dk"], a["dv"], a["scale"], a["dt"],
-                                    a["ws"], a["wsb"], a["stream"], flags, None)
+                                    a["ws"], a["wsb"], a["stream"], flags, None, None)
 
     assert call_ex(2) == -1                    # unknown flag bit
+
+    def call_gate(z, w, eps):
+        g = gdn.OutputGate(z, w, eps)
+        a = good
+        return lib.gdn_chunk_fwd_ex(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"], a["s0"], a["out"],
+                                    a["fin"], a["T"], a["H_q"], a["H_v"], a["dk"], a["dv"], a["scale"], a["dt"],
+                                    a["ws"], a["wsb"], a["stream"], 0, ctypes.byref(g), None)
+
+    assert call_gate(p, p, 0.0) == -1          # eps must be > 0
+    assert call_gate(p, p, float("nan")) == -1
+    assert call_gate(None, p, 1e-6) == -1      # z missing
+    assert call_gate(p + 8, p, 1e-6) == -2     # z misaligned
     assert call_ex(gdn.FWD_KEEP_A, q=None) == -1
     assert call_ex(gdn.FWD_KEEP_A, N=0, T=0, cu=_cu([0])) == 0
 
@@ -172,7 +184,7 @@ def test_recurrent_step_fused_rejects_before_any_device_work(gdn):
         x = dict(good, **kw)
         return lib.gdn_recurrent_step_fused(x["q"], x["k"], x["v"], x["a"], x["b"], x["A"], x["dtb"], x["st"],
                                             x["out"], x["N"], x["H_q"], x["H_v"], x["dk"], x["dv"], x["scale"],
-                                            x["dt"], x["stream"])
+                                            x["dt"], None, x["stream"])
 
     assert call(a=None) == -1
     assert call(dtb=None) == -1
