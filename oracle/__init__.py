@@ -35,6 +35,12 @@ S' = alpha (I - beta k^T k) S + beta k^T v evaluated with numpy matrices.
 invariance under scaling o (eps = 0), zero gate gives zero, the unit RMS of
 the normalised read-out under a saturated gate, silu(z) - silu(-z) = z, and
 linearity in the weight.
+
+``conv_silu_varlen`` / ``conv_silu_step`` are the short causal convolution +
+SiLU with its input history (oracle/conv.py).  Pins: numpy's convolve and
+torch's grouped conv1d per channel, SiLU alone under the identity kernel,
+splitting a sequence and passing the history, and the decode step against the
+prefill of the same tokens.
 """
 from __future__ import annotations
 
@@ -45,6 +51,7 @@ import numpy as np
 
 from . import chunk_form  # noqa: F401
 from .gated_norm import gated_rmsnorm  # noqa: F401
+from .conv import conv_silu_step, conv_silu_varlen  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdn_oracle.so")

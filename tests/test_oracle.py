@@ -519,3 +519,72 @@ def test_gated_rmsnorm_pins():
     assert _rel(np.mean(y40 * y40, axis=-1), ms / (ms + eps)) < 1e-12
     # linear in the weight
     assert _rel(gated_rmsnorm(o, z, 3.0 * w, 1e-6), 3.0 * gated_rmsnorm(o, z, w, 1e-6)) < 1e-14
+
+
+# ---------------------------------------------------------------------------
+# Causal conv1d + SiLU with its input history (trace page node 6; "Kestrel_VLLM
+# - 24" page, section 三)
+# ---------------------------------------------------------------------------
+def _silu64(x):
+    import torch
+
+    return torch.nn.functional.silu(torch.from_numpy(np.asarray(x, dtype=np.float64))).numpy()
+
+
+def test_conv_matches_numpy_convolve_and_torch_conv1d():
+    import torch
+
+    from oracle import conv_silu_varlen
+
+    rng = np.random.default_rng(10)
+    T, C, K = 37, 6, 4
+    x = rng.standard_normal((T, C))
+    w = rng.standard_normal((C, K))
+    b = rng.standard_normal(C)
+    y, fin = conv_silu_varlen(x, [0, T], w, b)
+    for c in range(C):
+        pre = np.convolve(x[:, c], w[c, ::-1])[:T] + b[c]   # causal: zeros before the start
+        assert _rel(y[:, c], _silu64(pre)) < 1e-13
+    tc = torch.nn.functional.conv1d(torch.from_numpy(x.T[None]), torch.from_numpy(w[:, None, :]),
+                                    torch.from_numpy(b), padding=K - 1, groups=C)[0, :, :T].T
+    assert _rel(y, _silu64(tc.numpy())) < 1e-13
+    assert np.array_equal(fin[0], x[T - (K - 1):])
+
+
+def test_conv_identity_kernel_is_silu_and_short_sequences():
+    from oracle import conv_silu_varlen
+
+    rng = np.random.default_rng(11)
+    T, C, K = 9, 5, 4
+    x = rng.standard_normal((T, C))
+    w = np.zeros((C, K))
+    w[:, K - 1] = 1.0
+    y, _ = conv_silu_varlen(x, [0, T], w)
+    assert _rel(y, _silu64(x)) < 1e-15
+    # a 2-token sequence: its final history reaches into the initial one
+    s0 = rng.standard_normal((1, K - 1, C))
+    _, fin = conv_silu_varlen(x[:2], [0, 2], w, None, s0)
+    assert np.array_equal(fin[0], np.concatenate([s0[0, 2:], x[:2]]))
+
+
+def test_conv_split_and_decode_agree():
+    from oracle import conv_silu_step, conv_silu_varlen
+
+    rng = np.random.default_rng(12)
+    T, C, K = 23, 7, 4
+    x = rng.standard_normal((T, C))
+    w = rng.standard_normal((C, K))
+    b = rng.standard_normal(C)
+    s0 = rng.standard_normal((1, K - 1, C))
+    y, fin = conv_silu_varlen(x, [0, T], w, b, s0)
+    # split at 10: pass the history
+    y1, f1 = conv_silu_varlen(x[:10], [0, 10], w, b, s0)
+    y2, f2 = conv_silu_varlen(x[10:], [0, T - 10], w, b, f1)
+    assert _rel(np.concatenate([y1, y2]), y) < 1e-15 and np.array_equal(f2, fin)
+    # packed: two sequences in one call equal two calls
+    yp, fp = conv_silu_varlen(x, [0, 10, T], w, b, np.concatenate([s0, f1]))
+    assert np.array_equal(yp[:10], y1) and np.array_equal(yp[10:], y2) and np.array_equal(fp[1], fin[0])
+    # decode: token by token from the same history
+    st = s0.copy()
+    yd = np.stack([conv_silu_step(x[t:t + 1], w, b, st)[0] for t in range(T)])
+    assert _rel(yd, y) < 1e-15 and np.array_equal(st, fin)
