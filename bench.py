@@ -303,6 +303,48 @@ def bench_decode(args, torch, gdn, hip, device, fused=False, gated=False):
     return dict(N=N, ms_step=ms, kernel_ms=kms, bytes=nbytes, flops=nflops, steps=K)
 
 
+def bench_conv(args, torch, gdn, device):
+    """Causal conv1d + SiLU at the model's shapes: the prefill over T = 4096
+    tokens of C = 8192 channels (q, k, v of 16 + 16 + 32 heads at d = 128), K = 4,
+    bf16, with a history in and out; and the decode step for 256 sequences."""
+    import gdn_inputs
+
+    T, C, K, N = 4096, 8192, 4, 256
+    x, s0, w, b = gdn_inputs.make_conv(80, T, C, K, 1, "bf16")
+    xd, s0d, wd, bd = (_dev(x, "bf16", torch, device), _dev(s0, "bf16", torch, device),
+                       _dev(w, "f32", torch, device), _dev(b, "f32", torch, device))
+    out = torch.empty_like(xd)
+    fin = torch.empty_like(s0d)
+    cu = [0, T]
+    xs, ss, _, _ = gdn_inputs.make_conv(81, N, C, K, N, "bf16")
+    xsd, ssd = _dev(xs, "bf16", torch, device), _dev(ss, "bf16", torch, device)
+    outs = torch.empty_like(xsd)
+
+    def timed(fn, K_):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(K_):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / K_
+
+    steps = max(args.steps, 20)
+    ms_p = timed(lambda: gdn.conv1d_silu(xd, cu, wd, bd, initial_state=s0d, final_state=fin, out=out), steps)
+    ms_s = timed(lambda: gdn.conv1d_silu_step(xsd, wd, bd, ssd, out=outs), steps)
+    bytes_p = 2 * T * C * 2 + C * K * 4 + C * 4 + 2 * (K - 1) * C * 2
+    bytes_s = 2 * N * C * 2 + 2 * N * (K - 1) * C * 2 + C * K * 4 + C * 4
+    return {"prefill": {"workload": f"T={T}, C={C}, K={K}, bf16", "us": ms_p * 1e3,
+                        "gb_per_s": bytes_p / (ms_p * 1e-3) / 1e9,
+                        "hbm_frac": bytes_p / (ms_p * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            "decode_step": {"workload": f"N={N}, C={C}, K={K}, bf16", "us": ms_s * 1e3,
+                            "gb_per_s": bytes_s / (ms_s * 1e-3) / 1e9,
+                            "hbm_frac": bytes_s / (ms_s * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+
+
 def cpu_baseline(inp, target_s=10.0):
     """fp64 oracle on the host cores over the prefill workload (all heads): a prefix
     sized to about target_s seconds, or the whole workload repeated until then."""
@@ -473,6 +515,11 @@ def main():
             "tokens_per_s": decf["N"] / (decf["ms_step"] * 1e-3), "steps": decf["steps"],
             "roofline": {"bound": "hbm", "kernel": "recurrent_step_fused", "achieved": kgbs, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": kgbs / HBM_PEAK_GBS, "traffic": None}}
+    if args.only == "all":
+        conv = bench_conv(args, torch, gdn, device)
+        print(f"[bench] conv1d+SiLU: prefill {conv['prefill']['us']:.1f} us, decode step "
+              f"{conv['decode_step']['us']:.1f} us", file=sys.stderr, flush=True)
+        res["conv1d_silu"] = conv
     if pre is not None and args.only == "all" and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(pre["inp"])
     res["source_sha"] = _source_sha()

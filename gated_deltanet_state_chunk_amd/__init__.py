@@ -100,6 +100,10 @@ def load_library():
     lib.gdn_recurrent_step_fused.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P,
                                              P]
     lib.gdn_recurrent_step_fused.restype = ctypes.c_int
+    lib.gdn_conv1d_silu_fwd.argtypes = [P, P, I32, I32, I32, I32, P, P, P, P, P, ctypes.c_int, P]
+    lib.gdn_conv1d_silu_fwd.restype = ctypes.c_int
+    lib.gdn_conv1d_silu_step.argtypes = [P, I32, I32, I32, P, P, P, P, ctypes.c_int, P]
+    lib.gdn_conv1d_silu_step.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -313,4 +317,65 @@ def recurrent_step_fused(q, k, v, a, b, A_log, dt_bias, state, scale: Optional[f
                                       _stream_ptr(stream))
     if rc != 0:
         raise GdnError(rc, "gdn_recurrent_step_fused")
+    return out
+
+
+def conv1d_silu(x, cu_seqlens: Sequence[int], weight, bias=None, initial_state=None, final_state=None,
+                output_final_state: bool = True, out=None, stream=None):
+    """Causal depthwise conv1d + SiLU over a packed batch (gdn_conv1d_silu_fwd).
+
+    x: [T, C] (bf16 or fp32); weight: fp32 [C, K] (oldest tap first); bias: fp32
+    [C] or None; initial_state: [N, K-1, C] in x's dtype or None.  Returns
+    (out [T, C], final_state [N, K-1, C] or None).
+    """
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(x)
+    _check_dev("x", x, x.dtype)
+    _check_dev("weight", weight, torch.float32)
+    T, C = x.shape
+    K = weight.shape[1]
+    if tuple(weight.shape) != (C, K):
+        raise ValueError("weight must be [C, K]")
+    if bias is not None:
+        _check_dev("bias", bias, torch.float32)
+    cu = _host_cu(cu_seqlens)
+    N = len(cu) - 1
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None:
+            _check_dev(name, t, x.dtype)
+            if tuple(t.shape) != (N, K - 1, C):
+                raise ValueError(f"{name} must be [N, K-1, C]")
+    if out is None:
+        out = torch.empty_like(x)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, K - 1, C), dtype=x.dtype, device=x.device)
+    rc = lib.gdn_conv1d_silu_fwd(_ptr(x), cu, N, T, C, K, _ptr(weight), _ptr(bias), _ptr(initial_state), _ptr(out),
+                                 _ptr(final_state), dt, _stream_ptr(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_conv1d_silu_fwd")
+    return out, final_state
+
+
+def conv1d_silu_step(x, weight, bias, state, out=None, stream=None):
+    """One decode token of the convolution (gdn_conv1d_silu_step): x [N, C];
+    state [N, K-1, C] updated in place.  Returns out [N, C]."""
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(x)
+    _check_dev("x", x, x.dtype)
+    _check_dev("weight", weight, torch.float32)
+    _check_dev("state", state, x.dtype)
+    N, C = x.shape
+    K = weight.shape[1]
+    if tuple(state.shape) != (N, K - 1, C) or tuple(weight.shape) != (C, K):
+        raise ValueError("inconsistent conv step shapes")
+    if bias is not None:
+        _check_dev("bias", bias, torch.float32)
+    if out is None:
+        out = torch.empty_like(x)
+    rc = lib.gdn_conv1d_silu_step(_ptr(x), N, C, K, _ptr(weight), _ptr(bias), _ptr(state), _ptr(out), dt,
+                                  _stream_ptr(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_conv1d_silu_step")
     return out

@@ -64,6 +64,25 @@ hipError_t run_chunk(const gdn::ChunkParams& p, gdn_dtype dt, int d, hipStream_t
     return d == 128 ? gdn::launch_chunk_pipeline<float, 128>(p, s, ev) : gdn::launch_chunk_pipeline<float, 64>(p, s, ev);
 }
 
+template <typename T>
+hipError_t run_conv(const gdn::ConvParams& p, int K, int N_step, hipStream_t s) {
+    // N_step < 0: prefill; else a decode step over N_step sequences
+    switch (K) {
+        case 2: return N_step < 0 ? gdn::launch_conv_prefill<T, 2>(p, s) : gdn::launch_conv_step<T, 2>(p, N_step, s);
+        case 3: return N_step < 0 ? gdn::launch_conv_prefill<T, 3>(p, s) : gdn::launch_conv_step<T, 3>(p, N_step, s);
+        default: return N_step < 0 ? gdn::launch_conv_prefill<T, 4>(p, s) : gdn::launch_conv_step<T, 4>(p, N_step, s);
+    }
+}
+
+int check_conv(int32_t C, int32_t K, gdn_dtype dtype, const float* weight, const float* bias) {
+    if (C <= 0 || K <= 0 || !weight) return GDN_ERR_INVALID;
+    if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
+    if (K < 2 || K > 4) return GDN_ERR_UNSUPPORTED;
+    if (C % (int32_t)(16 / elem_size(dtype)) != 0) return GDN_ERR_UNSUPPORTED;
+    if (!aligned16(weight) || (bias && !aligned16(bias))) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
 template <bool FUSED>
 hipError_t run_decode(const gdn::DecodeParams& p, gdn_dtype dt, int d, hipStream_t s) {
     if (dt == GDN_DTYPE_BF16)
@@ -83,6 +102,63 @@ int hip_fail(hipError_t e) {
 extern "C" {
 
 const char* gdn_version(void) { return "0.1.0"; }
+
+int gdn_conv1d_silu_fwd(const void* x, const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t T, int32_t C,
+                        int32_t K, const float* weight, const float* bias, const void* initial_state, void* out,
+                        void* final_state, gdn_dtype dtype, void* stream) {
+    int rc = check_conv(C, K, dtype, weight, bias);
+    if (rc != GDN_OK) return rc;
+    int64_t n_chunks = 0;
+    rc = check_seqlens(T, num_seqs, cu_seqlens_host, &n_chunks);
+    if (rc != GDN_OK) return rc;
+    if (num_seqs == 0) return GDN_OK;
+    if ((int64_t)T * C > INT32_MAX * (int64_t)16) return GDN_ERR_UNSUPPORTED;
+    if (T > 0 && (!x || !out)) return GDN_ERR_INVALID;
+    const void* ptrs[] = {x, out, initial_state, final_state};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
+    gdn::ConvParams p{};
+    p.x = x; p.y = out; p.w = weight; p.b = bias; p.s_in = initial_state; p.s_out = final_state; p.C = C;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t chunk_base = 0;
+    for (int32_t s0 = 0; s0 < num_seqs; s0 += gdn::MAX_SEQS_PER_LAUNCH) {
+        const int32_t ns = std::min<int32_t>(gdn::MAX_SEQS_PER_LAUNCH, num_seqs - s0);
+        gdn::SeqTable& tab = p.tab;
+        tab.num_seqs = ns;
+        tab.seq_base = s0;
+        tab.chunk_begin = chunk_base;
+        int32_t c = chunk_base;
+        for (int32_t i = 0; i <= ns; ++i) {
+            tab.cu[i] = cu_seqlens_host[s0 + i];
+            tab.choff[i] = c;
+            if (i < ns) c += (cu_seqlens_host[s0 + i + 1] - cu_seqlens_host[s0 + i] + GDN_CHUNK - 1) / GDN_CHUNK;
+        }
+        tab.n_chunks = c - chunk_base;
+        chunk_base = c;
+        const hipError_t e =
+            dtype == GDN_DTYPE_BF16 ? run_conv<gdn::bf16>(p, K, -1, s) : run_conv<float>(p, K, -1, s);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return GDN_OK;
+}
+
+int gdn_conv1d_silu_step(const void* x, int32_t N, int32_t C, int32_t K, const float* weight, const float* bias,
+                         void* state, void* out, gdn_dtype dtype, void* stream) {
+    int rc = check_conv(C, K, dtype, weight, bias);
+    if (rc != GDN_OK) return rc;
+    if (N < 0) return GDN_ERR_INVALID;
+    if (N == 0) return GDN_OK;
+    if (!x || !state || !out) return GDN_ERR_INVALID;
+    const void* ptrs[] = {x, state, out};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
+    gdn::ConvParams p{};
+    p.x = x; p.y = out; p.w = weight; p.b = bias; p.s_in = state; p.s_out = state; p.C = C;
+    const hipError_t e = dtype == GDN_DTYPE_BF16 ? run_conv<gdn::bf16>(p, K, N, static_cast<hipStream_t>(stream))
+                                                 : run_conv<float>(p, K, N, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+    return GDN_OK;
+}
 
 const char* gdn_status_string(int status) {
     switch (status) {

@@ -70,6 +70,21 @@ struct DecodeParams {
     float scale;
 };
 
+// Causal conv1d + SiLU (gdn_conv.hip).  Prefill: x, y [T, C]; s_in, s_out
+// [num_seqs, K-1, C] (either may be null).  Step: x, y [N, C]; s_out is the
+// history, updated in place.  w [C, K] fp32 (oldest tap first), b [C] or null.
+struct ConvParams {
+    const void* x;
+    void* y;
+    const float* w;
+    const float* b;
+    const void* s_in;
+    void* s_out;
+    int32_t C;
+    int32_t q0;    // prefill: first quarter-chunk of this launch
+    SeqTable tab;  // prefill only
+};
+
 // Kernel launchers (defined in the .hip translation units).  T is float or
 // __bf16, D is d_k = d_v.  `events` is null or six events: start and stop of
 // each of the three chunk kernels.
@@ -78,5 +93,10 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
 
 template <typename T, int D, bool FUSED>
 hipError_t launch_recurrent_step(const DecodeParams& p, hipStream_t stream);
+
+template <typename T, int K>
+hipError_t launch_conv_prefill(const ConvParams& p, hipStream_t stream);
+template <typename T, int K>
+hipError_t launch_conv_step(const ConvParams& p, int N, hipStream_t stream);
 
 }  // namespace gdn

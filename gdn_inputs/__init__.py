@@ -247,6 +247,18 @@ def make_gate(seed: int, rows: int, H_v: int, d_v: int, dtype: str = "bf16"):
     return z, w
 
 
+def make_conv(seed: int, T: int, C: int, K: int, N: int, dtype: str = "bf16", with_state: bool = True):
+    """Inputs of the short causal convolution: x [T, C] ~ N(0, 1) and, if asked,
+    histories [N, K-1, C] ~ N(0, 1) in the storage dtype; weight [C, K] ~ N(0, 1/K)
+    and bias [C] ~ N(0, 0.1^2) float32."""
+    rng = np.random.default_rng(seed)
+    x = round_to(rng.standard_normal((T, C), dtype=np.float32), dtype)
+    s0 = round_to(rng.standard_normal((N, K - 1, C), dtype=np.float32), dtype) if with_state else None
+    w = (rng.standard_normal((C, K)) / np.sqrt(K)).astype(np.float32)
+    b = (0.1 * rng.standard_normal(C)).astype(np.float32)
+    return x, s0, w, b
+
+
 def make_decode_state(seed: int, N: int, H_v: int, d_k: int, d_v: int, std: float = 0.02) -> np.ndarray:
     rng = np.random.default_rng(seed)
     return (rng.standard_normal((N, H_v, d_k, d_v), dtype=np.float32) * np.float32(std)).astype(np.float32)

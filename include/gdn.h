@@ -226,6 +226,37 @@ int gdn_recurrent_step_fused(const void *q, const void *k, const void *v, const 
                              int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale, gdn_dtype dtype,
                              const gdn_output_gate *gate, void *stream);
 
+/*
+ * Short causal depthwise convolution + SiLU with its input history over a
+ * packed batch ("Qwen3.5-397B-A17B" trace page, Decode-GDN node 6,
+ * qkvzba_unpack_causal_conv1d_silu; the window order of the "Kestrel_VLLM - 24"
+ * page, section 三).  For every sequence n, token t and channel c:
+ *     out[t, c] = SiLU(sum_{k=0}^{K-1} weight[c, k] * x_{t-(K-1)+k, c} + bias[c])
+ * taps oldest first (weight[c, K-1] multiplies the current input); inputs
+ * before a sequence's first token come from its history initial_state[n]
+ * (rows oldest first) or are zero.  final_state[n] receives the sequence's
+ * last K-1 raw inputs (reaching into its history when it is shorter).
+ *
+ *   x, out      dtype [T, C]   (out rounded to dtype; must not overlap x)
+ *   weight      fp32 [C, K]    bias fp32 [C] or NULL
+ *   initial_state, final_state  dtype [num_seqs, K-1, C] or NULL; may be equal
+ *   cu_seqlens_host  as for gdn_chunk_fwd
+ * K in {2, 3, 4}; C a multiple of 8 (bf16) or 4 (fp32); every pointer
+ * 16-byte aligned.
+ * num_seqs == 0 is a no-op returning GDN_OK.
+ */
+int gdn_conv1d_silu_fwd(const void *x, const int32_t *cu_seqlens_host, int32_t num_seqs, int32_t T, int32_t C,
+                        int32_t K, const float *weight, const float *bias, const void *initial_state, void *out,
+                        void *final_state, gdn_dtype dtype, void *stream);
+
+/*
+ * One decode token of the same convolution for N sequences: x, out dtype
+ * [N, C]; state dtype [N, K-1, C], the history, updated IN PLACE (shifted by
+ * one, x appended).  Same constraints as gdn_conv1d_silu_fwd; N == 0 is a no-op.
+ */
+int gdn_conv1d_silu_step(const void *x, int32_t N, int32_t C, int32_t K, const float *weight, const float *bias,
+                         void *state, void *out, gdn_dtype dtype, void *stream);
+
 /* Static string naming a status code. */
 const char *gdn_status_string(int status);
 

@@ -197,6 +197,36 @@ def test_recurrent_step_fused_rejects_before_any_device_work(gdn):
     assert call(N=0) == 0
 
 
+def test_conv_entry_points_reject_before_any_device_work(gdn):
+    lib = gdn.load_library()
+    keep, p = _fake()
+    cu = _cu([0, 10])
+
+    def fwd(**kw):
+        a = dict(x=p, cu=cu, N=1, T=10, C=64, K=4, w=p, b=None, s0=None, out=p, fin=None, dt=1)
+        a.update(kw)
+        return lib.gdn_conv1d_silu_fwd(a["x"], a["cu"], a["N"], a["T"], a["C"], a["K"], a["w"], a["b"], a["s0"],
+                                       a["out"], a["fin"], a["dt"], None)
+
+    assert fwd(K=5) == -2 and fwd(K=1) == -2   # taps outside 2..4
+    assert fwd(C=60) == -2                     # not whole 16-byte channel groups (bf16)
+    assert fwd(w=None) == -1
+    assert fwd(x=p + 8) == -2
+    assert fwd(cu=_cu([0, 11])) == -1
+    assert fwd(N=0, T=0, cu=_cu([0])) == 0
+
+    def step(**kw):
+        a = dict(x=p, N=3, C=64, K=4, w=p, b=None, st=p, out=p, dt=0)
+        a.update(kw)
+        return lib.gdn_conv1d_silu_step(a["x"], a["N"], a["C"], a["K"], a["w"], a["b"], a["st"], a["out"],
+                                        a["dt"], None)
+
+    assert step(st=None) == -1
+    assert step(C=62) == -2
+    assert step(w=p + 4) == -2                 # weights are read as 16-byte vectors
+    assert step(N=0) == 0
+
+
 def test_binding_refuses_host_tensors(gdn):
     torch = pytest.importorskip("torch")
     q = torch.zeros(4, 2, 64)
