@@ -16,7 +16,9 @@ import math
 import os
 from typing import Optional, Sequence
 
-__all__ = ["chunk_fwd", "recurrent_step", "workspace_layout", "workspace_size", "lib_path", "load_library",
+__all__ = ["chunk_fwd", "recurrent_step", "recurrent_step_fused", "conv1d_silu", "conv1d_silu_step",
+           "chunk_fwd_pooled", "conv1d_silu_pooled", "recurrent_step_fused_pooled", "conv1d_silu_step_pooled",
+           "state_rows_zero", "state_rows_copy", "workspace_layout", "workspace_size", "lib_path", "load_library",
            "GdnError", "CHUNK", "DTYPE_F32", "DTYPE_BF16"]
 
 CHUNK = 64
@@ -49,6 +51,38 @@ class WorkspaceLayout(ctypes.Structure):
 class OutputGate(ctypes.Structure):
     """gdn_output_gate: read-out epilogue out = rmsnorm(o) * weight * silu(z)."""
     _fields_ = [("z", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
+class StateSlots(ctypes.Structure):
+    """gdn_state_slots: host pool rows of a prefill's sequences (-1: none) and which resume."""
+    _fields_ = [("slot", ctypes.POINTER(ctypes.c_int32)), ("has_initial", ctypes.POINTER(ctypes.c_uint8)),
+                ("pool_size", ctypes.c_int32)]
+
+
+def _slots_arg(slots, has_initial, pool_size, N):
+    """(host slots, host has_initial or None, pool rows) -> (StateSlots, keep-alive)."""
+    torch = _torch()
+    vals = [int(x) for x in (slots.tolist() if isinstance(slots, torch.Tensor) else slots)]
+    if len(vals) != N:
+        raise ValueError(f"slots must have one entry per sequence ({N}), got {len(vals)}")
+    sl = (ctypes.c_int32 * max(N, 1))(*vals)
+    hi = None
+    if has_initial is not None:
+        flags = [1 if bool(x) else 0 for x in (has_initial.tolist() if isinstance(has_initial, torch.Tensor)
+                                               else has_initial)]
+        if len(flags) != N:
+            raise ValueError("has_initial must have one entry per sequence")
+        hi = (ctypes.c_uint8 * max(N, 1))(*flags)
+    st = StateSlots(ctypes.cast(sl, ctypes.POINTER(ctypes.c_int32)),
+                    ctypes.cast(hi, ctypes.POINTER(ctypes.c_uint8)) if hi is not None else None, int(pool_size))
+    return st, (sl, hi)
+
+
+def _check_slot_dev(slot, N):
+    torch = _torch()
+    _check_dev("slot", slot, torch.int32)
+    if tuple(slot.shape) != (N,):
+        raise ValueError(f"slot must be int32 [{N}]")
 
 
 def _gate_arg(gate, dtype, rows, H_v, d_v):
@@ -104,6 +138,18 @@ def load_library():
     lib.gdn_conv1d_silu_fwd.restype = ctypes.c_int
     lib.gdn_conv1d_silu_step.argtypes = [P, I32, I32, I32, P, P, P, P, ctypes.c_int, P]
     lib.gdn_conv1d_silu_step.restype = ctypes.c_int
+    SL = ctypes.POINTER(StateSlots)
+    lib.gdn_chunk_fwd_pooled.argtypes = [P, P, P, P, P, P, I32, P, SL, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P,
+                                         ctypes.c_size_t, P, P]
+    lib.gdn_conv1d_silu_fwd_pooled.argtypes = [P, P, I32, I32, I32, I32, P, P, P, SL, P, ctypes.c_int, P]
+    lib.gdn_recurrent_step_fused_pooled.argtypes = [P, P, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, F,
+                                                    ctypes.c_int, P, P]
+    lib.gdn_conv1d_silu_step_pooled.argtypes = [P, I32, I32, I32, P, P, P, P, I32, P, ctypes.c_int, P]
+    lib.gdn_state_rows_zero.argtypes = [P, I32, ctypes.c_size_t, P, I32, P]
+    lib.gdn_state_rows_copy.argtypes = [P, I32, ctypes.c_size_t, P, P, I32, P]
+    for fn in ("gdn_chunk_fwd_pooled", "gdn_conv1d_silu_fwd_pooled", "gdn_recurrent_step_fused_pooled",
+               "gdn_conv1d_silu_step_pooled", "gdn_state_rows_zero", "gdn_state_rows_copy"):
+        getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -379,3 +425,185 @@ def conv1d_silu_step(x, weight, bias, state, out=None, stream=None):
     if rc != 0:
         raise GdnError(rc, "gdn_conv1d_silu_step")
     return out
+
+
+# ---------------------------------------------------------------------------
+# state pools (serving): rows addressed by slot
+# ---------------------------------------------------------------------------
+
+def chunk_fwd_pooled(q, k, v, g, beta, cu_seqlens: Sequence[int], state_pool, slots, has_initial=None,
+                     scale: Optional[float] = None, out=None, workspace=None, stream=None, gate=None):
+    """Chunk-wise prefill reading and writing states in a pool (gdn_chunk_fwd_pooled).
+
+    state_pool: fp32 [P, H_v, d_k, d_v]; slots: host ints [N], the pool row of
+    each sequence (-1: starts from zeros, final state not kept); has_initial:
+    host bools [N] or None (all True) — False starts that sequence from zeros
+    although it has a row (a request without a cached prefix).  Returns out.
+    """
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("g", g, torch.float32)
+    _check_dev("beta", beta, torch.float32)
+    _check_dev("state_pool", state_pool, torch.float32)
+    T, H_q, d_k = q.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    if k.shape != q.shape or v.shape[0] != T or g.shape != (T, H_v) or beta.shape != (T, H_v):
+        raise ValueError("inconsistent q/k/v/g/beta shapes")
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H_v, d_k, d_v):
+        raise ValueError("state_pool must be [P, H_v, d_k, d_v]")
+    cu = _host_cu(cu_seqlens)
+    N = len(cu) - 1
+    st, _keep_slots = _slots_arg(slots, has_initial, state_pool.shape[0], N)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    if out is None:
+        out = torch.empty((T, H_v, d_v), dtype=q.dtype, device=q.device)
+    else:
+        _check_dev("out", out, q.dtype)
+    ws_bytes = lib.gdn_chunk_fwd_workspace_size(T, N, cu, H_q, H_v, d_k, d_v, dt)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _check_dev("workspace", workspace)
+    gptr, _keep = _gate_arg(gate, q.dtype, T, H_v, d_v)
+    rc = lib.gdn_chunk_fwd_pooled(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), cu, N, _ptr(state_pool),
+                                  ctypes.byref(st), _ptr(out), T, H_q, H_v, d_k, d_v, float(scale), dt,
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(), gptr,
+                                  _stream_ptr(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_chunk_fwd_pooled")
+    return out
+
+
+def conv1d_silu_pooled(x, cu_seqlens: Sequence[int], weight, bias, state_pool, slots, has_initial=None, out=None,
+                       stream=None):
+    """Packed conv1d + SiLU reading and writing histories in a pool
+    (gdn_conv1d_silu_fwd_pooled): state_pool [P, K-1, C] in x's dtype; slots and
+    has_initial as for chunk_fwd_pooled.  Returns out [T, C]."""
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(x)
+    _check_dev("x", x, x.dtype)
+    _check_dev("weight", weight, torch.float32)
+    _check_dev("state_pool", state_pool, x.dtype)
+    T, C = x.shape
+    K = weight.shape[1]
+    if tuple(weight.shape) != (C, K) or state_pool.dim() != 3 or tuple(state_pool.shape[1:]) != (K - 1, C):
+        raise ValueError("weight must be [C, K] and state_pool [P, K-1, C]")
+    if bias is not None:
+        _check_dev("bias", bias, torch.float32)
+    cu = _host_cu(cu_seqlens)
+    N = len(cu) - 1
+    st, _keep_slots = _slots_arg(slots, has_initial, state_pool.shape[0], N)
+    if out is None:
+        out = torch.empty_like(x)
+    rc = lib.gdn_conv1d_silu_fwd_pooled(_ptr(x), cu, N, T, C, K, _ptr(weight), _ptr(bias), _ptr(state_pool),
+                                        ctypes.byref(st), _ptr(out), dt, _stream_ptr(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_conv1d_silu_fwd_pooled")
+    return out
+
+
+def recurrent_step_fused_pooled(q, k, v, a, b, A_log, dt_bias, state_pool, slot, scale: Optional[float] = None,
+                                out=None, stream=None, gate=None):
+    """Fused decode step over a state pool (gdn_recurrent_step_fused_pooled).
+
+    state_pool: fp32 [P, H_v, d_k, d_v], updated in place; slot: device int32
+    [N], the pool row of each sequence; a slot outside [0, P) is padding (zero
+    output row, no pool access).  Other arguments as recurrent_step_fused.
+    """
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("a", a), ("b", b)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("A_log", A_log, torch.float32)
+    _check_dev("dt_bias", dt_bias, torch.float32)
+    _check_dev("state_pool", state_pool, torch.float32)
+    N, H_q, d_k = q.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    if k.shape != q.shape or v.shape[0] != N or a.shape != (N, H_v) or b.shape != (N, H_v) or \
+            A_log.shape != (H_v,) or dt_bias.shape != (H_v,) or state_pool.dim() != 4 or \
+            tuple(state_pool.shape[1:]) != (H_v, d_k, d_v):
+        raise ValueError("inconsistent decode shapes")
+    _check_slot_dev(slot, N)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    if out is None:
+        out = torch.empty((N, H_v, d_v), dtype=q.dtype, device=q.device)
+    else:
+        _check_dev("out", out, q.dtype)
+    gptr, _keep = _gate_arg(gate, q.dtype, N, H_v, d_v)
+    rc = lib.gdn_recurrent_step_fused_pooled(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log),
+                                             _ptr(dt_bias), _ptr(state_pool), _ptr(slot), state_pool.shape[0],
+                                             _ptr(out), N, H_q, H_v, d_k, d_v, float(scale), dt, gptr,
+                                             _stream_ptr(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_recurrent_step_fused_pooled")
+    return out
+
+
+def conv1d_silu_step_pooled(x, weight, bias, state_pool, slot, out=None, stream=None):
+    """One decode token of the convolution over a history pool
+    (gdn_conv1d_silu_step_pooled): x [N, C]; state_pool [P, K-1, C] updated in
+    place; slot device int32 [N] (outside [0, P): padding).  Returns out [N, C]."""
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(x)
+    _check_dev("x", x, x.dtype)
+    _check_dev("weight", weight, torch.float32)
+    _check_dev("state_pool", state_pool, x.dtype)
+    N, C = x.shape
+    K = weight.shape[1]
+    if tuple(weight.shape) != (C, K) or state_pool.dim() != 3 or tuple(state_pool.shape[1:]) != (K - 1, C):
+        raise ValueError("inconsistent conv step shapes")
+    if bias is not None:
+        _check_dev("bias", bias, torch.float32)
+    _check_slot_dev(slot, N)
+    if out is None:
+        out = torch.empty_like(x)
+    rc = lib.gdn_conv1d_silu_step_pooled(_ptr(x), N, C, K, _ptr(weight), _ptr(bias), _ptr(state_pool), _ptr(slot),
+                                         state_pool.shape[0], _ptr(out), dt, _stream_ptr(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_conv1d_silu_step_pooled")
+    return out
+
+
+def _pool_rows(pool, src, dst, what, stream):
+    torch = _torch()
+    lib = load_library()
+    _check_dev("pool", pool)
+    _check_dev("rows", dst, torch.int32)
+    if src is not None:
+        _check_dev("src rows", src, torch.int32)
+        if src.shape != dst.shape:
+            raise ValueError("src and dst rows must have the same length")
+    if dst.dim() != 1:
+        raise ValueError("rows must be 1-D")
+    P = pool.shape[0]
+    row_bytes = pool[0].numel() * pool.element_size() if P > 0 else 0
+    if P == 0:
+        return
+    if src is None:
+        rc = lib.gdn_state_rows_zero(_ptr(pool), P, row_bytes, _ptr(dst), dst.numel(), _stream_ptr(stream))
+    else:
+        rc = lib.gdn_state_rows_copy(_ptr(pool), P, row_bytes, _ptr(src), _ptr(dst), dst.numel(),
+                                     _stream_ptr(stream))
+    if rc != 0:
+        raise GdnError(rc, what)
+
+
+def state_rows_zero(pool, rows, stream=None):
+    """Reset pool rows to zero (gdn_state_rows_zero): pool [P, ...] (state or
+    conv history), rows device int32 [n]; rows outside [0, P) are skipped."""
+    _pool_rows(pool, None, rows, "gdn_state_rows_zero", stream)
+
+
+def state_rows_copy(pool, src_rows, dst_rows, stream=None):
+    """Copy pool rows (gdn_state_rows_copy): row dst_rows[i] := row src_rows[i]
+    (e.g. cloning a state for a speculative branch); pairs with a row outside
+    [0, P) are skipped."""
+    _pool_rows(pool, src_rows, dst_rows, "gdn_state_rows_copy", stream)

@@ -3,8 +3,10 @@
 // nothing and never touches the device (all-or-nothing entry points).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <string>
+#include <vector>
 
 #include "gdn.h"
 #include "gdn_params.h"
@@ -57,6 +59,54 @@ int check_seqlens(int32_t T, int32_t num_seqs, const int32_t* cu, int64_t* n_chu
     return GDN_OK;
 }
 
+// Pool addressing of a prefill: row indices inside the pool, no duplicate
+// kept rows (two sequences writing one row would race).
+int check_slots(const gdn_state_slots* sl, int32_t num_seqs, const void* pool) {
+    if (!sl || sl->pool_size < 0) return GDN_ERR_INVALID;
+    if (num_seqs == 0) return GDN_OK;
+    if (!sl->slot) return GDN_ERR_INVALID;
+    std::vector<int32_t> kept;
+    kept.reserve(num_seqs);
+    for (int32_t i = 0; i < num_seqs; ++i) {
+        const int32_t r = sl->slot[i];
+        if (r >= sl->pool_size) return GDN_ERR_INVALID;
+        if (r >= 0) kept.push_back(r);
+    }
+    if (!kept.empty() && !pool) return GDN_ERR_INVALID;
+    std::sort(kept.begin(), kept.end());
+    if (std::adjacent_find(kept.begin(), kept.end()) != kept.end()) return GDN_ERR_INVALID;
+    return GDN_OK;
+}
+
+// Fills the launch table of sequences s0 .. s0+ns-1 (chunk offsets from
+// chunk_base) with their state rows: pool rows from `slots`, else row i of the
+// initial/final arrays when present, -1 for none.  Returns the next chunk base.
+int32_t fill_table(gdn::SeqTable& tab, const int32_t* cu, int32_t s0, int32_t ns, int32_t chunk_base,
+                   const gdn_state_slots* slots, bool have_in, bool have_out) {
+    tab.num_seqs = ns;
+    tab.seq_base = s0;
+    tab.chunk_begin = chunk_base;
+    int32_t c = chunk_base;
+    for (int32_t i = 0; i <= ns; ++i) {
+        tab.cu[i] = cu[s0 + i];
+        tab.choff[i] = c;
+        if (i == ns) break;
+        c += (cu[s0 + i + 1] - cu[s0 + i] + GDN_CHUNK - 1) / GDN_CHUNK;
+        const int32_t gi = s0 + i;
+        if (slots) {
+            const int32_t r = slots->slot[gi];
+            const bool resume = !slots->has_initial || slots->has_initial[gi];
+            tab.s_in[i] = (r >= 0 && resume) ? r : -1;
+            tab.s_out[i] = r >= 0 ? r : -1;
+        } else {
+            tab.s_in[i] = have_in ? gi : -1;
+            tab.s_out[i] = have_out ? gi : -1;
+        }
+    }
+    tab.n_chunks = c - chunk_base;
+    return c;
+}
+
 hipError_t run_chunk(const gdn::ChunkParams& p, gdn_dtype dt, int d, hipStream_t s, hipEvent_t const* ev) {
     if (dt == GDN_DTYPE_BF16)
         return d == 128 ? gdn::launch_chunk_pipeline<gdn::bf16, 128>(p, s, ev)
@@ -97,6 +147,142 @@ int hip_fail(hipError_t e) {
     return GDN_ERR_HIP;
 }
 
+int conv_fwd_impl(const void* x, const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t T, int32_t C, int32_t K,
+                  const float* weight, const float* bias, const void* s_in, void* out, void* s_out,
+                  const gdn_state_slots* slots, gdn_dtype dtype, void* stream) {
+    int rc = check_conv(C, K, dtype, weight, bias);
+    if (rc != GDN_OK) return rc;
+    int64_t n_chunks = 0;
+    rc = check_seqlens(T, num_seqs, cu_seqlens_host, &n_chunks);
+    if (rc != GDN_OK) return rc;
+    if (slots && (rc = check_slots(slots, num_seqs, s_in)) != GDN_OK) return rc;
+    if (num_seqs == 0) return GDN_OK;
+    if ((int64_t)T * C > INT32_MAX * (int64_t)16) return GDN_ERR_UNSUPPORTED;
+    if (T > 0 && (!x || !out)) return GDN_ERR_INVALID;
+    const void* ptrs[] = {x, out, s_in, s_out};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
+    gdn::ConvParams p{};
+    p.x = x; p.y = out; p.w = weight; p.b = bias; p.s_in = s_in; p.s_out = s_out; p.C = C;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t chunk_base = 0;
+    for (int32_t s0 = 0; s0 < num_seqs; s0 += gdn::MAX_SEQS_PER_LAUNCH) {
+        const int32_t ns = std::min<int32_t>(gdn::MAX_SEQS_PER_LAUNCH, num_seqs - s0);
+        chunk_base = fill_table(p.tab, cu_seqlens_host, s0, ns, chunk_base, slots, s_in != nullptr, s_out != nullptr);
+        const hipError_t e =
+            dtype == GDN_DTYPE_BF16 ? run_conv<gdn::bf16>(p, K, -1, s) : run_conv<float>(p, K, -1, s);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return GDN_OK;
+}
+
+int conv_step_impl(const void* x, int32_t N, int32_t C, int32_t K, const float* weight, const float* bias,
+                   void* pool, const int32_t* slot, int32_t pool_size, void* out, gdn_dtype dtype, void* stream) {
+    int rc = check_conv(C, K, dtype, weight, bias);
+    if (rc != GDN_OK) return rc;
+    if (N < 0 || pool_size < 0) return GDN_ERR_INVALID;
+    if (N == 0) return GDN_OK;
+    if (!x || !out || (pool_size > 0 && !pool)) return GDN_ERR_INVALID;
+    const void* ptrs[] = {x, pool, out};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
+    if (slot && (reinterpret_cast<uintptr_t>(slot) & 3u)) return GDN_ERR_UNSUPPORTED;
+    gdn::ConvParams p{};
+    p.x = x; p.y = out; p.w = weight; p.b = bias; p.s_in = pool; p.s_out = pool; p.C = C;
+    p.slot = slot; p.pool = pool_size;
+    const hipError_t e = dtype == GDN_DTYPE_BF16 ? run_conv<gdn::bf16>(p, K, N, static_cast<hipStream_t>(stream))
+                                                 : run_conv<float>(p, K, N, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+    return GDN_OK;
+}
+
+int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                   const int32_t* cu_seqlens_host, int32_t num_seqs, const float* initial_state, void* out,
+                   float* final_state, const gdn_state_slots* slots, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k,
+                   int32_t d_v, float scale, gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream,
+                   uint32_t flags, const gdn_output_gate* gate, void* const* stage_events) {
+    if (flags & ~(uint32_t)GDN_FWD_KEEP_A) return GDN_ERR_INVALID;
+    if (gate) {
+        const int grc = check_gate(gate, T > 0);
+        if (grc != GDN_OK) return grc;
+    }
+    gdn_workspace_layout L;
+    int rc = gdn_chunk_fwd_workspace_layout(T, num_seqs, cu_seqlens_host, H_q, H_v, d_k, d_v, dtype, &L);
+    if (rc != GDN_OK) return rc;
+    if (slots && (rc = check_slots(slots, num_seqs, initial_state)) != GDN_OK) return rc;
+    if (num_seqs == 0) return GDN_OK;
+    // Pointers: tensors with T > 0 rows must be present; all must be 16-byte aligned.
+    if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_INVALID;
+    const void* ptrs[] = {q, k, v, g, beta, out, initial_state, final_state, workspace};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return GDN_ERR_INVALID;  // NaN
+    if (L.n_chunks > 0 && (!workspace || workspace_bytes < L.total_bytes)) return GDN_ERR_WORKSPACE;
+
+    char* ws = static_cast<char*>(workspace);
+    gdn::ChunkParams p;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.s0 = initial_state; p.out = out; p.sfinal = final_state;
+    p.gc = reinterpret_cast<float*>(ws + L.off_gc);
+    p.A = ws + L.off_A; p.W = ws + L.off_W; p.Ut = ws + L.off_U; p.Kt = ws + L.off_Kd;
+    p.Ht = ws + L.off_Ht; p.Xt = ws + L.off_Xt;
+    p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
+    p.keep_A = (flags & GDN_FWD_KEEP_A) ? 1 : 0;
+    p.gz = gate ? gate->z : nullptr;
+    p.gw = gate ? gate->weight : nullptr;
+    p.geps = gate ? gate->eps : 0.f;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // Launch groups of up to MAX_SEQS_PER_LAUNCH sequences, each with its table in the kernel arguments.
+    int32_t chunk_base = 0;
+    for (int32_t s0 = 0; s0 < num_seqs; s0 += gdn::MAX_SEQS_PER_LAUNCH) {
+        const int32_t ns = std::min<int32_t>(gdn::MAX_SEQS_PER_LAUNCH, num_seqs - s0);
+        chunk_base = fill_table(p.tab, cu_seqlens_host, s0, ns, chunk_base, slots, initial_state != nullptr,
+                                final_state != nullptr);
+        hipEvent_t const* ev = (s0 == 0 && stage_events) ? reinterpret_cast<hipEvent_t const*>(stage_events) : nullptr;
+        const hipError_t e = run_chunk(p, dtype, d_k, s, ev);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return GDN_OK;
+}
+
+int step_fused_impl(const void* q, const void* k, const void* v, const void* a, const void* b, const float* A_log,
+                    const float* dt_bias, float* state, const int32_t* slot, int32_t pool_size, void* out, int32_t N,
+                    int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale, gdn_dtype dtype,
+                    const gdn_output_gate* gate, void* stream) {
+    int rc = check_shapes(H_q, H_v, d_k, d_v, dtype);
+    if (rc != GDN_OK) return rc;
+    if (N < 0 || pool_size < 0) return GDN_ERR_INVALID;
+    if (N == 0) return GDN_OK;
+    if ((int64_t)N * H_v > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !out || (pool_size > 0 && !state)) return GDN_ERR_INVALID;
+    const void* ptrs[] = {q, k, v, state, out};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
+    if (slot && (reinterpret_cast<uintptr_t>(slot) & 3u)) return GDN_ERR_UNSUPPORTED;
+    // per-head scalars: natural alignment of their element type
+    const size_t es = elem_size(dtype);
+    if ((reinterpret_cast<uintptr_t>(a) % es) || (reinterpret_cast<uintptr_t>(b) % es) ||
+        (reinterpret_cast<uintptr_t>(A_log) & 3u) || (reinterpret_cast<uintptr_t>(dt_bias) & 3u))
+        return GDN_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return GDN_ERR_INVALID;
+    if (gate) {
+        const int grc = check_gate(gate, true);
+        if (grc != GDN_OK) return grc;
+    }
+    gdn::DecodeParams p{};
+    p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.A_log = A_log; p.dt_bias = dt_bias;
+    p.gz = gate ? gate->z : nullptr;
+    p.gw = gate ? gate->weight : nullptr;
+    p.geps = gate ? gate->eps : 0.f;
+    p.state = state; p.out = out;
+    p.slot = slot; p.pool = pool_size;
+    p.N = N; p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
+    const hipError_t e = run_decode<true>(p, dtype, d_k, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,58 +292,29 @@ const char* gdn_version(void) { return "0.1.0"; }
 int gdn_conv1d_silu_fwd(const void* x, const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t T, int32_t C,
                         int32_t K, const float* weight, const float* bias, const void* initial_state, void* out,
                         void* final_state, gdn_dtype dtype, void* stream) {
-    int rc = check_conv(C, K, dtype, weight, bias);
-    if (rc != GDN_OK) return rc;
-    int64_t n_chunks = 0;
-    rc = check_seqlens(T, num_seqs, cu_seqlens_host, &n_chunks);
-    if (rc != GDN_OK) return rc;
-    if (num_seqs == 0) return GDN_OK;
-    if ((int64_t)T * C > INT32_MAX * (int64_t)16) return GDN_ERR_UNSUPPORTED;
-    if (T > 0 && (!x || !out)) return GDN_ERR_INVALID;
-    const void* ptrs[] = {x, out, initial_state, final_state};
-    for (const void* ptr : ptrs)
-        if (ptr && !aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
-    gdn::ConvParams p{};
-    p.x = x; p.y = out; p.w = weight; p.b = bias; p.s_in = initial_state; p.s_out = final_state; p.C = C;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    int32_t chunk_base = 0;
-    for (int32_t s0 = 0; s0 < num_seqs; s0 += gdn::MAX_SEQS_PER_LAUNCH) {
-        const int32_t ns = std::min<int32_t>(gdn::MAX_SEQS_PER_LAUNCH, num_seqs - s0);
-        gdn::SeqTable& tab = p.tab;
-        tab.num_seqs = ns;
-        tab.seq_base = s0;
-        tab.chunk_begin = chunk_base;
-        int32_t c = chunk_base;
-        for (int32_t i = 0; i <= ns; ++i) {
-            tab.cu[i] = cu_seqlens_host[s0 + i];
-            tab.choff[i] = c;
-            if (i < ns) c += (cu_seqlens_host[s0 + i + 1] - cu_seqlens_host[s0 + i] + GDN_CHUNK - 1) / GDN_CHUNK;
-        }
-        tab.n_chunks = c - chunk_base;
-        chunk_base = c;
-        const hipError_t e =
-            dtype == GDN_DTYPE_BF16 ? run_conv<gdn::bf16>(p, K, -1, s) : run_conv<float>(p, K, -1, s);
-        if (e != hipSuccess) return hip_fail(e);
-    }
-    return GDN_OK;
+    return conv_fwd_impl(x, cu_seqlens_host, num_seqs, T, C, K, weight, bias, initial_state, out, final_state, nullptr,
+                         dtype, stream);
+}
+
+int gdn_conv1d_silu_fwd_pooled(const void* x, const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t T, int32_t C,
+                               int32_t K, const float* weight, const float* bias, void* state_pool,
+                               const gdn_state_slots* slots, void* out, gdn_dtype dtype, void* stream) {
+    if (!slots) return GDN_ERR_INVALID;
+    return conv_fwd_impl(x, cu_seqlens_host, num_seqs, T, C, K, weight, bias, state_pool, out, state_pool, slots,
+                         dtype, stream);
 }
 
 int gdn_conv1d_silu_step(const void* x, int32_t N, int32_t C, int32_t K, const float* weight, const float* bias,
                          void* state, void* out, gdn_dtype dtype, void* stream) {
-    int rc = check_conv(C, K, dtype, weight, bias);
-    if (rc != GDN_OK) return rc;
-    if (N < 0) return GDN_ERR_INVALID;
-    if (N == 0) return GDN_OK;
-    if (!x || !state || !out) return GDN_ERR_INVALID;
-    const void* ptrs[] = {x, state, out};
-    for (const void* ptr : ptrs)
-        if (!aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
-    gdn::ConvParams p{};
-    p.x = x; p.y = out; p.w = weight; p.b = bias; p.s_in = state; p.s_out = state; p.C = C;
-    const hipError_t e = dtype == GDN_DTYPE_BF16 ? run_conv<gdn::bf16>(p, K, N, static_cast<hipStream_t>(stream))
-                                                 : run_conv<float>(p, K, N, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e);
-    return GDN_OK;
+    if (!state && N > 0) return GDN_ERR_INVALID;
+    return conv_step_impl(x, N, C, K, weight, bias, state, nullptr, N, out, dtype, stream);
+}
+
+int gdn_conv1d_silu_step_pooled(const void* x, int32_t N, int32_t C, int32_t K, const float* weight,
+                                const float* bias, void* state_pool, const int32_t* slot, int32_t pool_size, void* out,
+                                gdn_dtype dtype, void* stream) {
+    if (!slot && N > 0) return GDN_ERR_INVALID;
+    return conv_step_impl(x, N, C, K, weight, bias, state_pool, slot, pool_size, out, dtype, stream);
 }
 
 const char* gdn_status_string(int status) {
@@ -221,58 +378,19 @@ int gdn_chunk_fwd_ex(const void* q, const void* k, const void* v, const float* g
                      float* final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
                      gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream, uint32_t flags,
                      const gdn_output_gate* gate, void* const* stage_events) {
-    if (flags & ~(uint32_t)GDN_FWD_KEEP_A) return GDN_ERR_INVALID;
-    if (gate) {
-        const int grc = check_gate(gate, T > 0);
-        if (grc != GDN_OK) return grc;
-    }
-    gdn_workspace_layout L;
-    int rc = gdn_chunk_fwd_workspace_layout(T, num_seqs, cu_seqlens_host, H_q, H_v, d_k, d_v, dtype, &L);
-    if (rc != GDN_OK) return rc;
-    if (num_seqs == 0) return GDN_OK;
-    // Pointers: tensors with T > 0 rows must be present; all must be 16-byte aligned.
-    if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_INVALID;
-    const void* ptrs[] = {q, k, v, g, beta, out, initial_state, final_state, workspace};
-    for (const void* ptr : ptrs)
-        if (ptr && !aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
-    if (!(scale == scale)) return GDN_ERR_INVALID;  // NaN
-    if (L.n_chunks > 0 && (!workspace || workspace_bytes < L.total_bytes)) return GDN_ERR_WORKSPACE;
+    return chunk_fwd_impl(q, k, v, g, beta, cu_seqlens_host, num_seqs, initial_state, out, final_state, nullptr, T,
+                          H_q, H_v, d_k, d_v, scale, dtype, workspace, workspace_bytes, stream, flags, gate,
+                          stage_events);
+}
 
-    char* ws = static_cast<char*>(workspace);
-    gdn::ChunkParams p;
-    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
-    p.s0 = initial_state; p.out = out; p.sfinal = final_state;
-    p.gc = reinterpret_cast<float*>(ws + L.off_gc);
-    p.A = ws + L.off_A; p.W = ws + L.off_W; p.Ut = ws + L.off_U; p.Kt = ws + L.off_Kd;
-    p.Ht = ws + L.off_Ht; p.Xt = ws + L.off_Xt;
-    p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
-    p.keep_A = (flags & GDN_FWD_KEEP_A) ? 1 : 0;
-    p.gz = gate ? gate->z : nullptr;
-    p.gw = gate ? gate->weight : nullptr;
-    p.geps = gate ? gate->eps : 0.f;
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    // Launch groups of up to MAX_SEQS_PER_LAUNCH sequences, each with its table in the kernel arguments.
-    int32_t chunk_base = 0;
-    for (int32_t s0 = 0; s0 < num_seqs; s0 += gdn::MAX_SEQS_PER_LAUNCH) {
-        const int32_t ns = std::min<int32_t>(gdn::MAX_SEQS_PER_LAUNCH, num_seqs - s0);
-        gdn::SeqTable& tab = p.tab;
-        tab.num_seqs = ns;
-        tab.seq_base = s0;
-        tab.chunk_begin = chunk_base;
-        int32_t c = chunk_base;
-        for (int32_t i = 0; i <= ns; ++i) {
-            tab.cu[i] = cu_seqlens_host[s0 + i];
-            tab.choff[i] = c;
-            if (i < ns) c += (cu_seqlens_host[s0 + i + 1] - cu_seqlens_host[s0 + i] + GDN_CHUNK - 1) / GDN_CHUNK;
-        }
-        tab.n_chunks = c - chunk_base;
-        chunk_base = c;
-        hipEvent_t const* ev = (s0 == 0 && stage_events) ? reinterpret_cast<hipEvent_t const*>(stage_events) : nullptr;
-        const hipError_t e = run_chunk(p, dtype, d_k, s, ev);
-        if (e != hipSuccess) return hip_fail(e);
-    }
-    return GDN_OK;
+int gdn_chunk_fwd_pooled(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         const int32_t* cu_seqlens_host, int32_t num_seqs, float* state_pool,
+                         const gdn_state_slots* slots, void* out, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k,
+                         int32_t d_v, float scale, gdn_dtype dtype, void* workspace, size_t workspace_bytes,
+                         const gdn_output_gate* gate, void* stream) {
+    if (!slots) return GDN_ERR_INVALID;
+    return chunk_fwd_impl(q, k, v, g, beta, cu_seqlens_host, num_seqs, state_pool, out, state_pool, slots, T, H_q,
+                          H_v, d_k, d_v, scale, dtype, workspace, workspace_bytes, stream, 0u, gate, nullptr);
 }
 
 int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g, const float* beta, float* state,
@@ -290,6 +408,7 @@ int gdn_recurrent_step(const void* q, const void* k, const void* v, const float*
     if (!(scale == scale)) return GDN_ERR_INVALID;
     gdn::DecodeParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.state = state; p.out = out;
+    p.slot = nullptr; p.pool = N;
     p.N = N; p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
     const hipError_t e = run_decode<false>(p, dtype, d_k, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e);
@@ -300,33 +419,43 @@ int gdn_recurrent_step_fused(const void* q, const void* k, const void* v, const 
                              const float* A_log, const float* dt_bias, float* state, void* out, int32_t N,
                              int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale, gdn_dtype dtype,
                              const gdn_output_gate* gate, void* stream) {
-    int rc = check_shapes(H_q, H_v, d_k, d_v, dtype);
-    if (rc != GDN_OK) return rc;
-    if (N < 0) return GDN_ERR_INVALID;
-    if (N == 0) return GDN_OK;
-    if ((int64_t)N * H_v > INT32_MAX) return GDN_ERR_UNSUPPORTED;
-    if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !state || !out) return GDN_ERR_INVALID;
-    const void* ptrs[] = {q, k, v, state, out};
-    for (const void* ptr : ptrs)
-        if (!aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
-    // per-head scalars: natural alignment of their element type
-    const size_t es = elem_size(dtype);
-    if ((reinterpret_cast<uintptr_t>(a) % es) || (reinterpret_cast<uintptr_t>(b) % es) ||
-        (reinterpret_cast<uintptr_t>(A_log) & 3u) || (reinterpret_cast<uintptr_t>(dt_bias) & 3u))
+    if (!state && N > 0) return GDN_ERR_INVALID;
+    return step_fused_impl(q, k, v, a, b, A_log, dt_bias, state, nullptr, N, out, N, H_q, H_v, d_k, d_v, scale, dtype,
+                           gate, stream);
+}
+
+int gdn_recurrent_step_fused_pooled(const void* q, const void* k, const void* v, const void* a, const void* b,
+                                    const float* A_log, const float* dt_bias, float* state_pool, const int32_t* slot,
+                                    int32_t pool_size, void* out, int32_t N, int32_t H_q, int32_t H_v, int32_t d_k,
+                                    int32_t d_v, float scale, gdn_dtype dtype, const gdn_output_gate* gate,
+                                    void* stream) {
+    if (!slot && N > 0) return GDN_ERR_INVALID;
+    return step_fused_impl(q, k, v, a, b, A_log, dt_bias, state_pool, slot, pool_size, out, N, H_q, H_v, d_k, d_v,
+                           scale, dtype, gate, stream);
+}
+
+int gdn_state_rows_zero(void* pool, int32_t pool_size, size_t row_bytes, const int32_t* rows, int32_t n,
+                        void* stream) {
+    return gdn_state_rows_copy(pool, pool_size, row_bytes, nullptr, rows, n, stream);
+}
+
+int gdn_state_rows_copy(void* pool, int32_t pool_size, size_t row_bytes, const int32_t* src_rows,
+                        const int32_t* dst_rows, int32_t n, void* stream) {
+    if (n < 0 || pool_size < 0 || row_bytes == 0) return GDN_ERR_INVALID;
+    if (row_bytes % 16 != 0) return GDN_ERR_UNSUPPORTED;
+    if (n == 0 || pool_size == 0) return GDN_OK;
+    if (!pool || !dst_rows) return GDN_ERR_INVALID;
+    if (!aligned16(pool) || (reinterpret_cast<uintptr_t>(dst_rows) & 3u) ||
+        (reinterpret_cast<uintptr_t>(src_rows) & 3u))
         return GDN_ERR_UNSUPPORTED;
-    if (!(scale == scale)) return GDN_ERR_INVALID;
-    if (gate) {
-        const int grc = check_gate(gate, true);
-        if (grc != GDN_OK) return grc;
-    }
-    gdn::DecodeParams p{};
-    p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.A_log = A_log; p.dt_bias = dt_bias;
-    p.gz = gate ? gate->z : nullptr;
-    p.gw = gate ? gate->weight : nullptr;
-    p.geps = gate ? gate->eps : 0.f;
-    p.state = state; p.out = out;
-    p.N = N; p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
-    const hipError_t e = run_decode<true>(p, dtype, d_k, static_cast<hipStream_t>(stream));
+    if (row_bytes > SIZE_MAX / (size_t)pool_size) return GDN_ERR_INVALID;
+    gdn::PoolRowsParams p{};
+    p.base = static_cast<char*>(pool);
+    p.src = src_rows;
+    p.dst = dst_rows;
+    p.pool = pool_size;
+    p.row16 = row_bytes / 16;
+    const hipError_t e = gdn::launch_pool_rows(p, n, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e);
     return GDN_OK;
 }

@@ -554,7 +554,9 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
     const int col = 16 * tile + r16;
-    const size_t state_off = ((size_t)(p.tab.seq_base + n) * p.H_v + h) * D * D;
+    const int si = p.tab.s_in[n], so = p.tab.s_out[n];  // state rows (-1: zeros / not kept)
+    const size_t in_off = ((size_t)max(si, 0) * p.H_v + h) * D * D;
+    const size_t out_off = ((size_t)max(so, 0) * p.H_v + h) * D * D;
     const int L_n = p.tab.cu[n + 1] - p.tab.cu[n];
     const int nch = p.tab.choff[n + 1] - p.tab.choff[n];
     const int c0 = p.tab.choff[n];
@@ -667,7 +669,7 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         const int m = w * TPW + tt;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            S[tt][i] = p.s0 ? p.s0[state_off + (size_t)(16 * m + 4 * grp + i) * D + col] : 0.f;
+            S[tt][i] = si >= 0 ? p.s0[in_off + (size_t)(16 * m + 4 * grp + i) * D + col] : 0.f;
         lds_put4(LS[m >> 1][lane], m & 1, S[tt], -1.f);
     }
     // Operand fragments of one chunk, read from its LDS stage.
@@ -724,12 +726,12 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
             lds_put4(LS[m >> 1][lane], m & 1, S[tt], -1.f);
         }
     }
-    if (p.sfinal) {
+    if (so >= 0) {
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
             const int m = w * TPW + tt;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p.sfinal[state_off + (size_t)(16 * m + 4 * grp + i) * D + col] = S[tt][i];
+            for (int i = 0; i < 4; ++i) p.sfinal[out_off + (size_t)(16 * m + 4 * grp + i) * D + col] = S[tt][i];
         }
     }
 }

@@ -131,9 +131,10 @@ template <typename T, int K>
 __device__ __forceinline__ Vec16<T> input_at(const ConvParams& p, int n, int p_tok, int c) {
     const int s0 = p.tab.cu[n];
     if (p_tok >= s0) return ld16(reinterpret_cast<const T*>(p.x) + (size_t)p_tok * p.C + c);
-    if (!p.s_in) return zero16<T>();
+    const int si = p.tab.s_in[n];
+    if (si < 0) return zero16<T>();
     const int j = K - 1 + (p_tok - s0);  // history row, 0 = oldest
-    return ld16(reinterpret_cast<const T*>(p.s_in) + ((size_t)(p.tab.seq_base + n) * (K - 1) + j) * p.C + c);
+    return ld16(reinterpret_cast<const T*>(p.s_in) + ((size_t)si * (K - 1) + j) * p.C + c);
 }
 
 constexpr int CONV_SUB = 16;  // tokens per thread (a quarter of a chunk)
@@ -184,13 +185,15 @@ __global__ __launch_bounds__(256) void conv_final_state_kernel(const ConvParams 
     const int cg = blockIdx.y * 256 + threadIdx.x;
     if (cg * V >= p.C) return;
     const int c = cg * V, n = blockIdx.x;
+    const int so = p.tab.s_out[n];
+    if (so < 0) return;  // this sequence keeps no history (whole workgroup)
     const int end = p.tab.cu[n + 1];
     Vec16<T> last[K - 1];
 #pragma unroll
     for (int j = 0; j < K - 1; ++j) last[j] = input_at<T, K>(p, n, end - (K - 1) + j, c);
 #pragma unroll
     for (int j = 0; j < K - 1; ++j)
-        st16(reinterpret_cast<T*>(p.s_out) + ((size_t)(p.tab.seq_base + n) * (K - 1) + j) * p.C + c, last[j]);
+        st16(reinterpret_cast<T*>(p.s_out) + ((size_t)so * (K - 1) + j) * p.C + c, last[j]);
 }
 
 template <typename T, int K>
@@ -199,7 +202,12 @@ __global__ __launch_bounds__(256) void conv_step_kernel(const ConvParams p) {
     const int cg = blockIdx.y * 256 + threadIdx.x;
     if (cg * V >= p.C) return;
     const int c = cg * V, n = blockIdx.x;
-    T* st = reinterpret_cast<T*>(p.s_out) + (size_t)n * (K - 1) * p.C + c;
+    const int slot = p.slot ? p.slot[n] : n;
+    if (slot < 0 || slot >= p.pool) {  // padding: zero output, history untouched
+        st16(reinterpret_cast<T*>(p.y) + (size_t)n * p.C + c, zero16<T>());
+        return;
+    }
+    T* st = reinterpret_cast<T*>(p.s_out) + (size_t)slot * (K - 1) * p.C + c;
     Vec16<T> win[K];
 #pragma unroll
     for (int k = 0; k < K - 1; ++k) win[k] = ld16(st + (size_t)k * p.C);
@@ -232,7 +240,7 @@ hipError_t launch_conv_prefill(const ConvParams& p, hipStream_t stream) {
         hipLaunchKernelGGL((conv_prefill_kernel<T, K>), dim3(cblocks, min(65535, nq - q0)), dim3(256), 0, stream,
                            pq);
     }
-    if (p.s_out && p.tab.num_seqs > 0)
+    if (p.s_out && p.tab.num_seqs > 0)  // rows with s_out < 0 return at once
         hipLaunchKernelGGL((conv_final_state_kernel<T, K>), dim3(p.tab.num_seqs, cblocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }

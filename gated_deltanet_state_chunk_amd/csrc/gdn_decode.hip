@@ -45,7 +45,14 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(const DecodeParams 
 
     __shared__ float s_red[4][CPR][NV];
 
-    const size_t sidx = (size_t)nh * D * D;
+    // State row of this sequence; padding (negative or out-of-pool slot) reads
+    // and writes no state and yields a zero output row.
+    const int slot = p.slot ? p.slot[n] : n;
+    if (slot < 0 || slot >= p.pool) {
+        if (tid < D / 4) store4(reinterpret_cast<T*>(p.out) + (size_t)nh * D + 4 * tid, 0.f, 0.f, 0.f, 0.f);
+        return;  // whole workgroup
+    }
+    const size_t sidx = ((size_t)slot * p.H_v + h) * D * D;
     float4* Sp = reinterpret_cast<float4*>(p.state + sidx);
     const T* qp = reinterpret_cast<const T*>(p.q) + ((size_t)n * p.H_q + hq) * D;
     const T* kp = reinterpret_cast<const T*>(p.k) + ((size_t)n * p.H_q + hq) * D;

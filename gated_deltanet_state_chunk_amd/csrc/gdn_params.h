@@ -22,6 +22,8 @@ struct SeqTable {
     int32_t n_chunks;     // chunks in this launch
     int32_t cu[MAX_SEQS_PER_LAUNCH + 1];     // global token offsets
     int32_t choff[MAX_SEQS_PER_LAUNCH + 1];  // global chunk offsets, choff[num_seqs] = chunk_begin + n_chunks
+    int32_t s_in[MAX_SEQS_PER_LAUNCH];       // row of the initial-state array a sequence starts from, -1: zeros
+    int32_t s_out[MAX_SEQS_PER_LAUNCH];      // row of the final-state array it ends in, -1: none
 };
 
 struct ChunkParams {
@@ -55,6 +57,8 @@ struct DecodeParams {
     const void* q;
     const void* k;
     const void* v;
+    const int32_t* slot;  // state row of each sequence (null: row n); < 0 or >= pool: padding
+    int32_t pool;         // rows in the state array
     const float* g;       // plain step: per (n, h) log gate
     const float* beta;    // plain step: per (n, h) beta
     const void* a;        // fused step: per (n, h) gate input, dtype of q
@@ -82,7 +86,21 @@ struct ConvParams {
     void* s_out;
     int32_t C;
     int32_t q0;    // prefill: first quarter-chunk of this launch
+    const int32_t* slot;  // step: history row of each sequence (null: row n); < 0 or >= pool: padding
+    int32_t pool;
     SeqTable tab;  // prefill only
+};
+
+// Pool row maintenance (gdn_pool.hip): for each listed entry i, row dst[i] of
+// the pool receives row src[i] (src null: zeros); entries with a row outside
+// [0, pool) are skipped.
+struct PoolRowsParams {
+    char* base;
+    const int32_t* src;
+    const int32_t* dst;
+    int32_t pool;
+    int32_t i0;    // first entry of this launch
+    size_t row16;  // row size in 16-byte units
 };
 
 // Kernel launchers (defined in the .hip translation units).  T is float or
@@ -98,5 +116,7 @@ template <typename T, int K>
 hipError_t launch_conv_prefill(const ConvParams& p, hipStream_t stream);
 template <typename T, int K>
 hipError_t launch_conv_step(const ConvParams& p, int N, hipStream_t stream);
+
+hipError_t launch_pool_rows(PoolRowsParams p, int32_t n, hipStream_t stream);
 
 }  // namespace gdn

@@ -257,6 +257,94 @@ int gdn_conv1d_silu_fwd(const void *x, const int32_t *cu_seqlens_host, int32_t n
 int gdn_conv1d_silu_step(const void *x, int32_t N, int32_t C, int32_t K, const float *weight, const float *bias,
                          void *state, void *out, gdn_dtype dtype, void *stream);
 
+/*
+ * State pools for serving.  In the "Qwen3.5-397B-A17B" trace page the layer
+ * reads and writes its conv and recurrent states through per-request cache
+ * slots (section 1, Prefill-GDN graph: node 5 derives initial_state_mask from
+ * extend_prefix_lens and feeds node 6; section 3.6.5 keeps padding slots,
+ * invalid state indices and graph replays as part of the cache semantics).
+ * A pool holds one row per slot: the recurrent state pool is fp32
+ * [pool_size, H_v, d_k, d_v], the conv history pool dtype [pool_size, K-1, C].
+ *
+ * Prefill addressing (host arrays, read during the call only):
+ *   slot[i]         pool row of sequence i.  In [0, pool_size): the sequence
+ *                   starts from that row when has_initial[i] != 0 (it extends
+ *                   a cached prefix, extend_prefix_len > 0), from zeros
+ *                   otherwise, and its final state is written back to the
+ *                   row.  < 0: starts from zeros, final state not kept.
+ *                   >= pool_size, or a row >= 0 named twice: GDN_ERR_INVALID.
+ *   has_initial     uint8 [num_seqs], or NULL meaning all nonzero.
+ *   pool_size       rows in the pool (>= 0).
+ * Rows that no sequence names are left untouched.
+ */
+typedef struct gdn_state_slots {
+    const int32_t *slot;
+    const uint8_t *has_initial;
+    int32_t pool_size;
+} gdn_state_slots;
+
+/*
+ * gdn_chunk_fwd over a state pool: state_pool (fp32 [pool_size, H_v, d_k, d_v],
+ * 16-byte aligned; may be NULL when no slot is >= 0) takes the place of
+ * initial_state and final_state, addressed by `slots` as described above.
+ * gate as in gdn_chunk_fwd_ex.  Other arguments, results and errors as
+ * gdn_chunk_fwd; slots == NULL: GDN_ERR_INVALID.
+ */
+int gdn_chunk_fwd_pooled(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                         const int32_t *cu_seqlens_host, int32_t num_seqs, float *state_pool,
+                         const gdn_state_slots *slots, void *out, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k,
+                         int32_t d_v, float scale, gdn_dtype dtype, void *workspace, size_t workspace_bytes,
+                         const gdn_output_gate *gate, void *stream);
+
+/*
+ * gdn_conv1d_silu_fwd over a history pool: state_pool dtype [pool_size, K-1, C]
+ * (16-byte aligned) takes the place of initial_state and final_state,
+ * addressed by `slots`.  Otherwise as gdn_conv1d_silu_fwd.
+ */
+int gdn_conv1d_silu_fwd_pooled(const void *x, const int32_t *cu_seqlens_host, int32_t num_seqs, int32_t T, int32_t C,
+                               int32_t K, const float *weight, const float *bias, void *state_pool,
+                               const gdn_state_slots *slots, void *out, gdn_dtype dtype, void *stream);
+
+/*
+ * Decode steps over a state pool.  slot: DEVICE int32 [N] (4-byte aligned),
+ * the pool row of each sequence, read by the kernel (so a captured graph can
+ * replay with new slots).  A slot outside [0, pool_size) marks padding: that
+ * sequence's output row is written as zeros and no pool row is read or
+ * written.  Two sequences naming one row race (undefined result): rows must
+ * be distinct.  Otherwise as gdn_recurrent_step_fused / gdn_conv1d_silu_step,
+ * with state_pool (fp32 [pool_size, H_v, d_k, d_v], resp. dtype
+ * [pool_size, K-1, C]) updated in place.  slot == NULL with N > 0:
+ * GDN_ERR_INVALID.
+ */
+int gdn_recurrent_step_fused_pooled(const void *q, const void *k, const void *v, const void *a, const void *b,
+                                    const float *A_log, const float *dt_bias, float *state_pool, const int32_t *slot,
+                                    int32_t pool_size, void *out, int32_t N, int32_t H_q, int32_t H_v, int32_t d_k,
+                                    int32_t d_v, float scale, gdn_dtype dtype, const gdn_output_gate *gate,
+                                    void *stream);
+
+int gdn_conv1d_silu_step_pooled(const void *x, int32_t N, int32_t C, int32_t K, const float *weight,
+                                const float *bias, void *state_pool, const int32_t *slot, int32_t pool_size,
+                                void *out, gdn_dtype dtype, void *stream);
+
+/*
+ * Pool row maintenance (the "Kestrel_VLLM - 24" page, section 五, resets its
+ * single state mirror for a new sequence and leaves branch cloning for
+ * speculative decoding to later; here both work on any pool).  The pool is
+ * [pool_size][row_bytes], 16-byte aligned, row_bytes a multiple of 16 (a
+ * recurrent state row is H_v*d_k*d_v*4 bytes, a conv history row
+ * (K-1)*C*sizeof(dtype)).  rows, src_rows, dst_rows: DEVICE int32 [n].
+ *   gdn_state_rows_zero   row rows[i] := 0
+ *   gdn_state_rows_copy   row dst_rows[i] := row src_rows[i]
+ * Entries naming a row outside [0, pool_size) are skipped.  Within one call
+ * a destination row must not also be a source row or appear twice (race);
+ * one source may feed many destinations (cloning one state into several
+ * branches).  n == 0 is a no-op.
+ */
+int gdn_state_rows_zero(void *pool, int32_t pool_size, size_t row_bytes, const int32_t *rows, int32_t n,
+                        void *stream);
+int gdn_state_rows_copy(void *pool, int32_t pool_size, size_t row_bytes, const int32_t *src_rows,
+                        const int32_t *dst_rows, int32_t n, void *stream);
+
 /* Static string naming a status code. */
 const char *gdn_status_string(int status);
 

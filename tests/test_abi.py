@@ -227,6 +227,80 @@ def test_conv_entry_points_reject_before_any_device_work(gdn):
     assert step(N=0) == 0
 
 
+def test_pooled_entry_points_reject_before_any_device_work(gdn):
+    lib = gdn.load_library()
+    keep, p = _fake()
+    cu2 = _cu([0, 10, 30])
+
+    def slots(vals, pool, has=None):
+        st, ka = gdn._slots_arg(vals, has, pool, len(vals))
+        return st, ka
+
+    def chunk(sl, **kw):
+        a = dict(q=p, k=p, v=p, g=p, beta=p, cu=cu2, N=2, pool=p, out=p, T=30, H_q=2, H_v=4, dk=128, dv=128,
+                 scale=0.1, dt=1, ws=p, wsb=1 << 40)
+        a.update(kw)
+        return lib.gdn_chunk_fwd_pooled(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"], a["pool"],
+                                        ctypes.byref(sl[0]) if sl is not None else None, a["out"], a["T"], a["H_q"],
+                                        a["H_v"], a["dk"], a["dv"], a["scale"], a["dt"], a["ws"], a["wsb"], None,
+                                        None)
+
+    assert chunk(None) == -1                          # slots are required
+    assert chunk(slots([3, 3], 8)) == -1              # one row kept by two sequences
+    assert chunk(slots([0, 8], 8)) == -1              # row past the pool
+    assert chunk(slots([0, 1], -1)) == -1             # negative pool size
+    assert chunk(slots([0, 1], 8), pool=None) == -1   # rows named but no pool
+    assert chunk(slots([0, 1], 8), pool=p + 8) == -2  # misaligned pool
+    assert chunk(slots([1, 2], 8), dk=64) == -2       # shape checks still apply
+    assert chunk(slots([], 8), N=0, T=0, cu=_cu([0])) == 0
+
+    def conv(sl, **kw):
+        a = dict(x=p, cu=cu2, N=2, T=30, C=64, K=4, w=p, pool=p, out=p, dt=1)
+        a.update(kw)
+        return lib.gdn_conv1d_silu_fwd_pooled(a["x"], a["cu"], a["N"], a["T"], a["C"], a["K"], a["w"], None,
+                                              a["pool"], ctypes.byref(sl[0]) if sl is not None else None,
+                                              a["out"], a["dt"], None)
+
+    assert conv(None) == -1
+    assert conv(slots([5, 5], 8)) == -1
+    assert conv(slots([-1, 9], 8)) == -1
+    assert conv(slots([0, 1], 8), K=5) == -2
+
+    def step(**kw):
+        x = dict(q=p, k=p, v=p, a=p, b=p, A=p, dtb=p, pool=p, slot=p, P=8, out=p, N=4, H_q=2, H_v=4, dk=128,
+                 dv=128, scale=0.1, dt=1)
+        x.update(kw)
+        return lib.gdn_recurrent_step_fused_pooled(x["q"], x["k"], x["v"], x["a"], x["b"], x["A"], x["dtb"],
+                                                   x["pool"], x["slot"], x["P"], x["out"], x["N"], x["H_q"],
+                                                   x["H_v"], x["dk"], x["dv"], x["scale"], x["dt"], None, None)
+
+    assert step(slot=None) == -1
+    assert step(P=-1) == -1
+    assert step(pool=None) == -1
+    assert step(slot=p + 2) == -2                     # int32 slots off their alignment
+    assert step(N=0, slot=None) == 0
+
+    def cstep(**kw):
+        a = dict(x=p, N=3, C=64, K=4, w=p, pool=p, slot=p, P=8, out=p, dt=0)
+        a.update(kw)
+        return lib.gdn_conv1d_silu_step_pooled(a["x"], a["N"], a["C"], a["K"], a["w"], None, a["pool"], a["slot"],
+                                               a["P"], a["out"], a["dt"], None)
+
+    assert cstep(slot=None) == -1
+    assert cstep(P=-1) == -1
+    assert cstep(pool=None) == -1
+    assert cstep(C=62) == -2
+
+    assert lib.gdn_state_rows_zero(p, 8, 1024, p, 0, None) == 0    # nothing listed
+    assert lib.gdn_state_rows_zero(p, 0, 1024, p, 4, None) == 0    # empty pool
+    assert lib.gdn_state_rows_zero(p, 8, 1000, p, 4, None) == -2   # rows not whole 16-byte units
+    assert lib.gdn_state_rows_zero(p, 8, 0, p, 4, None) == -1
+    assert lib.gdn_state_rows_zero(p, 8, 1024, None, 4, None) == -1
+    assert lib.gdn_state_rows_zero(p + 8, 8, 1024, p, 4, None) == -2
+    assert lib.gdn_state_rows_copy(p, 8, 1024, p, p, -1, None) == -1
+    assert lib.gdn_state_rows_copy(p, 8, 1024, p + 2, p, 4, None) == -2
+
+
 def test_binding_refuses_host_tensors(gdn):
     torch = pytest.importorskip("torch")
     q = torch.zeros(4, 2, 64)
