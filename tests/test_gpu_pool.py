@@ -277,3 +277,55 @@ def test_serving_sequence(torch_cuda, oracle_mod):
     ref_o = oracle_mod.decode_step_fused(tok.f32("q"), tok.f32("k"), tok.f32("v"), tok.f32("a"), tok.f32("b"),
                                          tok.A_log, tok.dt_bias, ref1, H_q, H_v, scale, True)[0]
     assert rel_err(to_host(o)[0], ref_o[0]) < 1e-2
+
+
+def test_decode_graph_replay_with_new_slots(torch_cuda):
+    """The pooled decode steps read their slots from device memory, so a
+    captured graph replays with new slots and inputs; every replay must equal
+    the same calls made eagerly on a second copy of the pools, bit for bit."""
+    import gated_deltanet_state_chunk_amd as gdn
+
+    torch = torch_cuda
+    dtype, N, H_q, H_v, d, P, C, K = "bf16", 4, 2, 4, 128, 6, 128, 4
+    scale = 1.0 / np.sqrt(d)
+    pool_g = f32_dev(gdn_inputs.make_decode_state(101, P, H_v, d, d))
+    pool_e = pool_g.clone()
+    _, cp0, w, b = gdn_inputs.make_conv(102, 1, C, K, P, dtype)
+    cpool_g = to_dev(cp0, dtype)
+    cpool_e = cpool_g.clone()
+    wd, bd = f32_dev(w), f32_dev(b)
+    tok0 = gdn_inputs.make_decode_raw_token(103, N, H_q, H_v, d, d, dtype)
+    A_log, dt_bias = f32_dev(tok0.A_log), f32_dev(tok0.dt_bias)
+    names = ("q", "k", "v", "a", "b")
+    bufs = {m: to_dev(getattr(tok0, m), dtype) for m in names}
+    x_b = to_dev(gdn_inputs.make_conv(104, N, C, K, 1, dtype, with_state=False)[0], dtype)
+    slot_b = torch.zeros(N, dtype=torch.int32, device="cuda")
+    o_b = torch.empty((N, H_v, d), dtype=torch.bfloat16, device="cuda")
+    y_b = torch.empty((N, C), dtype=torch.bfloat16, device="cuda")
+
+    def calls(pool, cpool, o, y):
+        gdn.recurrent_step_fused_pooled(*[bufs[m] for m in names], A_log, dt_bias, pool, slot_b, scale=scale, out=o)
+        gdn.conv1d_silu_step_pooled(x_b, wd, bd, cpool, slot_b, out=y)
+
+    # warm-up outside capture on throwaway pools
+    calls(pool_g.clone(), cpool_g.clone(), torch.empty_like(o_b), torch.empty_like(y_b))
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls(pool_g, cpool_g, o_b, y_b)
+    torch.cuda.synchronize()
+
+    for r, slots in enumerate([[5, 1, -1, 3], [1, 5, 3, 7], [0, -1, 2, 4]]):
+        tok = gdn_inputs.make_decode_raw_token(110 + r, N, H_q, H_v, d, d, dtype)
+        for m in names:
+            bufs[m].copy_(to_dev(getattr(tok, m), dtype))
+        x_b.copy_(to_dev(gdn_inputs.make_conv(120 + r, N, C, K, 1, dtype, with_state=False)[0], dtype))
+        slot_b.copy_(torch.tensor(slots, dtype=torch.int32))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o_e, y_e = torch.empty_like(o_b), torch.empty_like(y_b)
+        calls(pool_e, cpool_e, o_e, y_e)
+        torch.cuda.synchronize()
+        assert torch.equal(o_b, o_e) and torch.equal(y_b, y_e), f"replay {r}"
+        assert torch.equal(pool_g, pool_e) and torch.equal(cpool_g, cpool_e), f"replay {r}"
