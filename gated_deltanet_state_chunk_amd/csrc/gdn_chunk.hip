@@ -118,12 +118,13 @@ struct PrepLds {
     T K[CHUNK][KP];
     union {
         struct {
-            float L[10 * BLK];  // strictly lower part of B Gamma K K^T Gamma^-1
+            // Strictly lower part of B Gamma K K^T Gamma^-1, overwritten block by
+            // block with (I + L)^-1 as the solve finishes with each L block.
+            float LA[10 * BLK];
             float Tm[4 * BLK];  // products of the block solve
         } sv;                   // during the solve
-        T V[CHUNK][KP];         // after it
+        T V[CHUNK][KP];         // after it (once A is in registers)
     } u;
-    float A[10 * BLK];          // (I + L)^-1
     float gc[CHUNK], beta[CHUNK], sk[CHUNK], svb[CHUNK], kd[CHUNK];
 };
 
@@ -143,9 +144,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
     const size_t ch = (size_t)cp.ci * p.H_v + h;
 
     __shared__ __attribute__((aligned(16))) PL s;
-    float* const Ls = s.u.sv.L;
+    float* const Ls = s.u.sv.LA;
     float* const Tm = s.u.sv.Tm;
-    float* const As = s.A;
+    float* const As = s.u.sv.LA;  // block (I, J) of A replaces block (I, J) of L
 
     // V rows into registers now (staged in LDS after the solve); K rows into LDS.
     const T* kb = reinterpret_cast<const T*>(p.k) + (size_t)cp.t0 * p.H_q * D + (size_t)hq * D;
@@ -202,7 +203,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
     }
     lds_sync();
 
-    // (I + L)^-1 by blocks of 16.  Diagonal blocks: forward substitution, lane owns column c.
+    // (I + L)^-1 by blocks of 16, each A block stored over the L block of the same
+    // index once no later step reads that L block.  Diagonal blocks: forward
+    // substitution, lane owns column c (the wave reads all of L_ww before writing A_ww).
     {
         const float* Lb = Ls + blk(w, w);
         const int c = r16;
@@ -252,12 +255,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
     }
     lds_sync();
 
-    // V into LDS (L is dead now); A to the workspace, zero outside the valid lower triangle.
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
-        *reinterpret_cast<float4*>(&s.u.V[r][c]) = vreg[j];
-    }
+    // A to the workspace on request, zero outside the valid lower triangle.
     if (p.keep_A) {
         T* Ab = reinterpret_cast<T*>(p.A) + ch * CHUNK * CHUNK;
         const int i = tid >> 2, jb = tid & 3;  // row i, column block jb
@@ -273,7 +271,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
             store4(Ab + (size_t)i * CHUNK + 16 * jb + j4, v4[0], v4[1], v4[2], v4[3]);
         }
     }
-    lds_sync();
 
     // Fragments of A (rows pos, contiguous columns): Af[mt][ks] is the A operand of
     // U = A (B V) for row tile mt and the B operand of W^T = (B Gamma K)^T A^T for
@@ -297,6 +294,12 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
             frag_set(Af[mt][ks], 4, hi.x); frag_set(Af[mt][ks], 5, hi.y);
             frag_set(Af[mt][ks], 6, hi.z); frag_set(Af[mt][ks], 7, hi.w);
         }
+    lds_sync();  // A is in registers: its LDS takes V (read after W is done)
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
+        *reinterpret_cast<float4*>(&s.u.V[r][c]) = vreg[j];
+    }
 
     constexpr int TPW = D / 64;  // 16-wide tiles of d_k (or d_v) per wave
     // W^T tiles: rows d_k (this wave's tiles), columns pos.  A is lower triangular,
@@ -342,6 +345,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
             }
         }
     }
+    lds_sync();  // V staged
     // U tiles: rows pos, columns d_v (this wave's tiles).
     T* Ub = reinterpret_cast<T*>(p.Ut) + ch * D * CHUNK;
 #pragma unroll
