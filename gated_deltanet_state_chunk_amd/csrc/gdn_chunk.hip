@@ -756,10 +756,14 @@ template <typename T, int D>
 struct OutLds {
     static constexpr int KP = D + 16 / (int)sizeof(T);
     T Q[CHUNK][KP];
-    T K[CHUNK][KP];
-    Frag<T> P[4][2][64];  // B operand of (U - W S)^T P^T: [query tile][K-step][lane]
+    union {
+        T K[CHUNK][KP];  // until the P tiles are formed
+        struct {
+            Frag<T> P[4][2][64];  // B operand of (U - W S)^T P^T: [query tile][K-step][lane]
+            float ss[4][CHUNK];   // gated read-out: per-wave sums of o^2 per position
+        } pr;
+    } u;
     float gc[CHUNK];
-    float ss[4][CHUNK];   // gated read-out: per-wave sums of o^2 per position
 };
 
 template <typename T, int D, bool GATED>
@@ -802,7 +806,7 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
         const bool ok = r < ell;
         const size_t off = (size_t)r * p.H_q * D + c;
         *reinterpret_cast<float4*>(&s.Q[r][c]) = ok ? *reinterpret_cast<const float4*>(qb + off) : make_float4(0, 0, 0, 0);
-        *reinterpret_cast<float4*>(&s.K[r][c]) = ok ? *reinterpret_cast<const float4*>(kb + off) : make_float4(0, 0, 0, 0);
+        *reinterpret_cast<float4*>(&s.u.K[r][c]) = ok ? *reinterpret_cast<const float4*>(kb + off) : make_float4(0, 0, 0, 0);
     }
     if (tid < CHUNK) s.gc[tid] = p.gc[ch * CHUNK + tid];
     lds_sync();
@@ -825,7 +829,9 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
             wv[tt] = *reinterpret_cast<const float4*>(p.gw + 16 * (w * TPW + tt) + 4 * grp);
     }
 
-    // P^T tiles (I, J = w) for I <= w, published as B fragments for query tile w.
+    // P^T tiles (I, J = w) for I <= w, held in registers until every wave is
+    // done with K, then published over K as B fragments for query tile w.
+    f32x4 pt[4];
     {
         Frag<T> qw[KS];
 #pragma unroll
@@ -839,24 +845,27 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     Frag<T> kf;
-                    load8(kf, &s.K[16 * I + r16][32 * ks + 8 * grp]);
+                    load8(kf, &s.u.K[16 * I + r16][32 * ks + 8 * grp]);
                     c = mma(kf, qw[ks], c);
                 }
             }
-            f32x4 v;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int pj = 16 * I + 4 * grp + i;
-                v[i] = (pj <= pos && pos < ell) ? c[i] * __expf(gq - s.gc[pj]) : 0.f;
+                pt[I][i] = (pj <= pos && pos < ell) ? c[i] * __expf(gq - s.gc[pj]) : 0.f;
             }
-            // rows pos' 16 I + 4 grp + i: K-step I / 2, slots 4 (I % 2) + i
-            if constexpr (sizeof(T) == 2) {
-                *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(&s.P[w][I >> 1][lane]) + 4 * (I & 1)) =
-                    cvt4_bf16(v, 1.f);
-            } else {
-                *reinterpret_cast<float4*>(reinterpret_cast<float*>(&s.P[w][I >> 1][lane]) + 4 * (I & 1)) =
-                    make_float4(v[0], v[1], v[2], v[3]);
-            }
+        }
+    }
+    lds_sync();  // K is dead
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        // rows pos' 16 I + 4 grp + i: K-step I / 2, slots 4 (I % 2) + i
+        if constexpr (sizeof(T) == 2) {
+            *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(&s.u.pr.P[w][I >> 1][lane]) + 4 * (I & 1)) =
+                cvt4_bf16(pt[I], 1.f);
+        } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(&s.u.pr.P[w][I >> 1][lane]) + 4 * (I & 1)) =
+                make_float4(pt[I][0], pt[I][1], pt[I][2], pt[I][3]);
         }
     }
     lds_sync();
@@ -869,8 +878,8 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
         Frag<T> qf[KS], pf[2];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) load8(qf[ks], &s.Q[16 * nt + r16][32 * ks + 8 * grp]);
-        pf[0] = s.P[nt][0][lane];
-        pf[1] = s.P[nt][1][lane];
+        pf[0] = s.u.pr.P[nt][0][lane];
+        pf[1] = s.u.pr.P[nt][1][lane];
         const int pos = 16 * nt + r16;
         const float eg = __expf(s.gc[pos]);
 #pragma unroll
@@ -902,14 +911,15 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
                 for (int i = 0; i < 4; ++i) ssq += ov[nt][tt][i] * ov[nt][tt][i];
             ssq += wave_shfl_xor(ssq, 16);
             ssq += wave_shfl_xor(ssq, 32);
-            if (grp == 0) s.ss[w][16 * nt + r16] = ssq;
+            if (grp == 0) s.u.pr.ss[w][16 * nt + r16] = ssq;
         }
         lds_sync();
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             const int pos = 16 * nt + r16;
             const float rstd =
-                1.f / sqrtf((s.ss[0][pos] + s.ss[1][pos] + s.ss[2][pos] + s.ss[3][pos]) * (1.f / D) + p.geps);
+                1.f / sqrtf((s.u.pr.ss[0][pos] + s.u.pr.ss[1][pos] + s.u.pr.ss[2][pos] + s.u.pr.ss[3][pos]) * (1.f / D) +
+                            p.geps);
             if (pos < ell) {
 #pragma unroll
                 for (int tt = 0; tt < TPW; ++tt) {
