@@ -18,6 +18,8 @@
 // which makes their rows of A (masked to zero), W, U and U - W S vanish.
 #include <hip/hip_ext.h>
 
+#include <algorithm>
+
 #include "gdn_device.h"
 #include "gdn_params.h"
 
@@ -129,45 +131,82 @@ struct PrepLds {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, int padded) {
+__global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const ChunkParams p, int padded) {
     using PL = PrepLds<T, D>;
     constexpr int VEC = 16 / (int)sizeof(T);                  // elements per 16-byte access
     constexpr int NV = CHUNK * D / VEC / 256;                 // 16-byte pieces per thread
-    const int wid = xcd_remap(blockIdx.x, padded);
-    if (wid >= p.tab.n_chunks * p.H_v) return;
-    const int h = wid % p.H_v;
-    const ChunkPos cp = locate_chunk(p.tab, p.tab.chunk_begin + wid / p.H_v);
-    const int hq = h / p.G;
+    const int work = p.tab.n_chunks * p.H_v;
+    // Items (chunk, value head) of this workgroup: virtual indices blockIdx.x,
+    // blockIdx.x + gridDim.x, ... mapped XCD-aware (gridDim.x is a multiple of 8,
+    // so every item of a workgroup stays on its XCD).  The next item's K, V and
+    // gate rows are loaded into registers while this item's W, U and Kd are formed.
+    int v = blockIdx.x;
+    int wid = xcd_remap(v, padded);
+    if (wid >= work) return;  // padding items come last, so all later ones are padding too
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
-    const int ell = cp.ell;
-    const size_t ch = (size_t)cp.ci * p.H_v + h;
 
     __shared__ __attribute__((aligned(16))) PL s;
     float* const Ls = s.u.sv.LA;
     float* const Tm = s.u.sv.Tm;
     float* const As = s.u.sv.LA;  // block (I, J) of A replaces block (I, J) of L
 
-    // V rows into registers now (staged in LDS after the solve); K rows into LDS.
-    const T* kb = reinterpret_cast<const T*>(p.k) + (size_t)cp.t0 * p.H_q * D + (size_t)hq * D;
-    const T* vb = reinterpret_cast<const T*>(p.v) + (size_t)cp.t0 * p.H_v * D + (size_t)h * D;
-    float4 vreg[NV];
+    // Rows of K and V (zero past the valid length) and wave 0's gate inputs, in
+    // registers.  K and the gates of the next item are fetched ahead (they are
+    // needed first); V is fetched at the start of its own item, since it is not
+    // read before the solve is done.
+    float4 kreg[NV], vreg[NV];
+    float graw = 0.f, braw = 0.f;
+    auto load_k = [&](int it) {
+        const int hh = it % p.H_v;
+        const ChunkPos c = locate_chunk(p.tab, p.tab.chunk_begin + it / p.H_v);
+        const T* kb = reinterpret_cast<const T*>(p.k) + (size_t)c.t0 * p.H_q * D + (size_t)(hh / p.G) * D;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
-        vreg[j] = r < ell ? *reinterpret_cast<const float4*>(vb + (size_t)r * p.H_v * D + c) : make_float4(0, 0, 0, 0);
+        for (int j = 0; j < NV; ++j) {
+            const int e = tid + 256 * j, r = e / (D / VEC), cc = (e % (D / VEC)) * VEC;
+            kreg[j] = r < c.ell ? *reinterpret_cast<const float4*>(kb + (size_t)r * p.H_q * D + cc)
+                                : make_float4(0, 0, 0, 0);
+        }
+        if (w == 0) {
+            const size_t gi = (size_t)(c.t0 + lane) * p.H_v + hh;
+            graw = lane < c.ell ? p.g[gi] : 0.f;
+            braw = lane < c.ell ? p.beta[gi] : 0.f;
+        }
+    };
+    load_k(wid);
+
+    for (;;) {
+    // Thread indices re-read per item: the empty asm hides that they do not change,
+    // so the address arithmetic of the body is not hoisted out of the loop (where it
+    // would stay live in registers across the whole item).
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, grp = lane >> 4;
+    const int h = wid % p.H_v;
+    const ChunkPos cp = locate_chunk(p.tab, p.tab.chunk_begin + wid / p.H_v);
+    const int ell = cp.ell;
+    const size_t ch = (size_t)cp.ci * p.H_v + h;
+
+    // V rows into registers (staged in LDS after the solve); K rows into LDS.
+    {
+        const T* vb = reinterpret_cast<const T*>(p.v) + (size_t)cp.t0 * p.H_v * D + (size_t)h * D;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
+            vreg[j] = r < ell ? *reinterpret_cast<const float4*>(vb + (size_t)r * p.H_v * D + c)
+                              : make_float4(0, 0, 0, 0);
+        }
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
-        *reinterpret_cast<float4*>(&s.K[r][c]) =
-            r < ell ? *reinterpret_cast<const float4*>(kb + (size_t)r * p.H_q * D + c) : make_float4(0, 0, 0, 0);
+        *reinterpret_cast<float4*>(&s.K[r][c]) = kreg[j];
     }
     // In-chunk inclusive cumsum of the log gate.
     if (w == 0) {
-        const size_t gi = (size_t)(cp.t0 + lane) * p.H_v + h;
-        float gv = lane < ell ? p.g[gi] : 0.f;
-        const float bv = lane < ell ? p.beta[gi] : 0.f;
+        float gv = graw;
+        const float bv = braw;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float o = __shfl_up(gv, off, 64);
@@ -300,6 +339,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
         const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
         *reinterpret_cast<float4*>(&s.u.V[r][c]) = vreg[j];
     }
+    // The next item's K and gate loads go out now; they land while W, U and Kd are formed.
+    v += gridDim.x;
+    const int next = v < padded ? xcd_remap(v, padded) : work;
+    if (next < work) load_k(next);
 
     constexpr int TPW = D / 64;  // 16-wide tiles of d_k (or d_v) per wave
     // W^T tiles: rows d_k (this wave's tiles), columns pos.  A is lower triangular,
@@ -386,6 +429,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const ChunkParams p, in
             }
             store8(Kb + frag_k_offset(dk, r0), lo, hi);
         }
+    }
+    if (next >= work) break;
+    lds_sync();  // every read of this item's LDS is done before the next item's K lands
+    wid = next;
     }
 }
 
@@ -941,6 +988,20 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
 // ---------------------------------------------------------------------------
 static inline int pad8(int x) { return (x + 7) & ~7; }
 
+// Compute units of the current device (cached per device), a multiple of 8 on
+// this chip (eight XCDs).
+static int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = pad8(n);
+    }
+    return cached[dev];
+}
+
 template <typename T, int D>
 hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEvent_t const* events) {
     const int work_ch = p.tab.n_chunks * p.H_v;
@@ -950,20 +1011,23 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
     // With events, each kernel is launched with hipExtLaunchKernelGGL, whose
     // start/stop events are stamped by the kernel's own dispatch (kernel time
     // only, no launch gaps).
-    auto launch = [&](int k, auto kernel, int grid, int block) {
+    auto launch = [&](int k, auto kernel, int grid, int block, int padded) {
         if (events)
             hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, stream, events[2 * k], events[2 * k + 1], 0, p,
-                                  grid);
+                                  padded);
         else
-            hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, stream, p, grid);
+            hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, stream, p, padded);
     };
-    if (work_ch > 0) launch(0, chunk_prep_kernel<T, D>, grid_ch, 256);
-    if (work_st > 0) launch(1, chunk_state_h_kernel<T, D>, grid_st, 64 * (5 + StateStage<T, D>::NPW));
+    // chunk_prep runs as many workgroups as fit on the chip at once (four per CU)
+    // and loops over the rest, prefetching each next item.
+    const int prep_slots = 4 * cu_count();
+    if (work_ch > 0) launch(0, chunk_prep_kernel<T, D>, std::min(grid_ch, prep_slots), 256, grid_ch);
+    if (work_st > 0) launch(1, chunk_state_h_kernel<T, D>, grid_st, 64 * (5 + StateStage<T, D>::NPW), grid_st);
     if (work_ch > 0) {
         if (p.gz)
-            launch(2, chunk_output_o_kernel<T, D, true>, grid_ch, 256);
+            launch(2, chunk_output_o_kernel<T, D, true>, grid_ch, 256, grid_ch);
         else
-            launch(2, chunk_output_o_kernel<T, D, false>, grid_ch, 256);
+            launch(2, chunk_output_o_kernel<T, D, false>, grid_ch, 256, grid_ch);
     }
     return hipGetLastError();
 }
