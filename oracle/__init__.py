@@ -36,6 +36,14 @@ invariance under scaling o (eps = 0), zero gate gives zero, the unit RMS of
 the normalised read-out under a saturated gate, silu(z) - silu(-z) = z, and
 linearity in the weight.
 
+``prefill_front_end`` / ``forward_fused`` add the prefill front end (q/k L2
+norm, gate and beta from the raw projections; oracle/front_end.py) before
+``forward``.  Pins: the gate and beta equal those of the independent C decode
+oracle (``decode_step_fused``) across the softplus branches; with fp32 inputs
+``forward_fused`` over a sequence equals the C fused decode step applied token
+by token; normalised rows have unit norm, are invariant under scaling the raw
+row and keep zero rows zero; bf16-rounded results are exactly representable.
+
 ``conv_silu_varlen`` / ``conv_silu_step`` are the short causal convolution +
 SiLU with its input history (oracle/conv.py).  Pins: numpy's convolve and
 torch's grouped conv1d per channel, SiLU alone under the identity kernel,
@@ -52,6 +60,7 @@ import numpy as np
 from . import chunk_form  # noqa: F401
 from .gated_norm import gated_rmsnorm  # noqa: F401
 from .conv import conv_silu_step, conv_silu_varlen  # noqa: F401
+from .front_end import prefill_front_end  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdn_oracle.so")
@@ -125,6 +134,16 @@ def forward(q, k, v, g, beta, cu_seqlens, H_q, H_v, scale, initial_state=None, h
     if want_delta:
         return out, fin, delta
     return out, fin
+
+
+def forward_fused(q, k, v, a, b, A_log, dt_bias, cu_seqlens, H_q, H_v, scale, round_to_bf16, initial_state=None,
+                  heads=None, num_threads=0):
+    """Prefill from the raw inputs: prefill_front_end, then forward (which takes
+    its inputs as fp32, so q_bar, k_bar and g pass through one fp32 rounding).
+    Returns (out, final) as forward does."""
+    qn, kn, g, beta = prefill_front_end(q, k, a, b, A_log, dt_bias, round_to_bf16)
+    return forward(qn, kn, v, g, beta, cu_seqlens, H_q, H_v, scale, initial_state=initial_state, heads=heads,
+                   num_threads=num_threads)
 
 
 def decode_step_fused(q, k, v, a, b, A_log, dt_bias, state, H_q, H_v, scale, beta_round_bf16, heads=None,

@@ -494,6 +494,85 @@ def test_fused_front_end_then_plain_step(oracle_mod):
 
 
 # ---------------------------------------------------------------------------
+# Prefill front end ("Qwen3.5-397B-A17B" trace page, section 1: nodes 8-10)
+# ---------------------------------------------------------------------------
+def _front_inputs(rng, T, H_q, H_v, d):
+    q = rng.standard_normal((T, H_q, d)).astype(np.float32)
+    k = rng.standard_normal((T, H_q, d)).astype(np.float32)
+    v = rng.standard_normal((T, H_v, d)).astype(np.float32)
+    a = rng.standard_normal((T, H_v)).astype(np.float32)
+    b = rng.standard_normal((T, H_v)).astype(np.float32)
+    A_log = np.log(rng.uniform(1.0, 16.0, H_v)).astype(np.float32)
+    dt_bias = rng.uniform(-7.0, -2.3, H_v).astype(np.float32)
+    return q, k, v, a, b, A_log, dt_bias
+
+
+def test_front_end_gate_and_beta_match_c_decode_oracle(oracle_mod):
+    """The numpy front end's gate and beta equal those the independent C decode
+    oracle derives from the same a, b, A_log, dt_bias, over both softplus
+    overflow branches and the middle, with and without the bf16 rounding of beta."""
+    rng = np.random.default_rng(21)
+    T, H = 40, 2
+    a = np.concatenate([np.linspace(-45, 45, T // 2), 3 * rng.standard_normal(T - T // 2)]).astype(np.float32)
+    a = np.stack([a, -a], axis=1)
+    b = (4 * rng.standard_normal((T, H))).astype(np.float32)
+    A_log = np.array([0.3, 1.7], np.float32)
+    dt_bias = np.array([-4.0, 2.5], np.float32)
+    q = np.ones((T, 1, 2), np.float32)
+    for rnd in (False, True):
+        _, g_c, beta_c, _ = _fused(oracle_mod, q, q, q, a, b, A_log, dt_bias, np.zeros((T, H, 2, 2)), 1, H, rnd=rnd)
+        _, _, g, beta = oracle_mod.prefill_front_end(q, q, a, b, A_log, dt_bias, rnd)
+        np.testing.assert_allclose(g, g_c, rtol=1e-15, atol=0)
+        assert np.array_equal(beta, beta_c)
+
+
+def test_front_end_rows_unit_norm_scale_invariant_and_rounded():
+    """q_bar, k_bar rows have unit L2 norm (up to the 1e-6 inside the root), do
+    not change when the raw row is scaled (norm per row and head, over d_k: a
+    wrong axis breaks this), keep zero rows zero, and with the bf16 rounding are
+    exactly representable and within half a bf16 ulp of the unrounded value."""
+    from oracle.front_end import prefill_front_end
+    rng = np.random.default_rng(22)
+    T, H_q, H_v, d = 9, 2, 4, 64
+    q, k, v, a, b, A_log, dt_bias = _front_inputs(rng, T, H_q, H_v, d)
+    k[3, 1] = 0.0
+    scale = rng.uniform(0.5, 20.0, (T, H_q, 1)).astype(np.float32)
+    qn, kn, _, _ = prefill_front_end(q, k, a, b, A_log, dt_bias, False)
+    qs, ks, _, _ = prefill_front_end(q * scale, k * scale, a, b, A_log, dt_bias, False)
+    nr = np.linalg.norm(qn, axis=-1)
+    assert np.all(np.abs(nr - 1.0) < 1e-6)
+    assert _rel(qs, qn) < 1e-6 and _rel(ks, kn) < 1e-6
+    assert not kn[3, 1].any()
+    qr, kr, _, br = prefill_front_end(q, k, a, b, A_log, dt_bias, True)
+    for x in (qr, kr, br):
+        assert np.all(x.astype(np.float32).view(np.uint32) & 0xFFFF == 0)
+    assert np.all(np.abs(qr - qn) <= np.abs(qn) * 2.0 ** -8 + 1e-30)
+
+
+def test_forward_fused_equals_fused_decode_token_by_token(oracle_mod):
+    """With fp32 inputs the prefill from raw inputs (front end, then the packed
+    recurrence) equals the independent C fused decode step applied token by
+    token from the same initial state (outputs and final state), for a packed
+    batch of two sequences with grouped value heads."""
+    rng = np.random.default_rng(23)
+    H_q, H_v, d = 2, 4, 16
+    lens = [7, 12]
+    T = sum(lens)
+    q, k, v, a, b, A_log, dt_bias = _front_inputs(rng, T, H_q, H_v, d)
+    cu = np.array([0, lens[0], T], np.int64)
+    s0 = (0.1 * rng.standard_normal((2, H_v, d, d))).astype(np.float64)
+    out, fin = oracle_mod.forward_fused(q, k, v, a, b, A_log, dt_bias, cu, H_q, H_v, 0.25, False, initial_state=s0)
+    for n in range(2):
+        S = s0[n:n + 1].copy()
+        for t in range(cu[n], cu[n + 1]):
+            sl = slice(t, t + 1)
+            o, _, _ = oracle_mod.decode_step_fused(q[sl], k[sl], v[sl], a[sl], b[sl], A_log, dt_bias, S, H_q, H_v,
+                                                   0.25, False)
+            assert _rel(out[t], o[0]) < 2e-6, (n, t)
+        assert _rel(fin[n], S[0]) < 2e-6
+
+
+# ---------------------------------------------------------------------------
 # Gated RMSNorm epilogue ("Qwen3.5-397B-A17B" trace page, node 8)
 # ---------------------------------------------------------------------------
 def test_gated_rmsnorm_pins():
