@@ -249,6 +249,59 @@ def bench_prefill(args, torch, gdn, hip, device, gated=False):
                 ms_step_with_events=timed_ms)
 
 
+def bench_prefill_serving(args, torch, gdn, device):
+    """The prefill as a serving layer calls it: raw q, k, a, b (L2 norm, gate and
+    beta inside the kernels, gdn_chunk_fwd_fused) and the gated read-out, at the
+    shapes of the prefill workload."""
+    import gdn_inputs
+
+    base = gdn_inputs.make_workload(args.workload)
+    seqlens = [int(x) for x in (base.cu_seqlens[1:] - base.cu_seqlens[:-1])]
+    inp = gdn_inputs.make_prefill_raw(71, seqlens, base.H_q, base.H_v, base.d_k, base.d_v, base.dtype)
+    dt = inp.dtype
+    q, k, v, a, b = (_dev(getattr(inp, n), dt, torch, device) for n in ("q", "k", "v", "a", "b"))
+    A_log, dt_bias = _dev(inp.A_log, "f32", torch, device), _dev(inp.dt_bias, "f32", torch, device)
+    s0 = _dev(inp.initial_state, "f32", torch, device)
+    z, w = gdn_inputs.make_gate(72, inp.T, inp.H_v, inp.d_v, dt)
+    gate = (_dev(z, dt, torch, device), _dev(w, "f32", torch, device), 1e-6)
+    ws = torch.empty(gdn.workspace_size(inp.T, inp.cu_seqlens, inp.H_q, inp.H_v, inp.d_k, inp.d_v, dt),
+                     dtype=torch.uint8, device=device)
+    out = torch.empty((inp.T, inp.H_v, inp.d_v), dtype=q.dtype, device=device)
+    fin = torch.empty((inp.N, inp.H_v, inp.d_k, inp.d_v), dtype=torch.float32, device=device)
+
+    # Arguments marshalled once (as a serving loop would), so the timed loop is
+    # the library call alone.
+    lib = gdn.load_library()
+    cu = (ctypes.c_int32 * (inp.N + 1))(*[int(x) for x in inp.cu_seqlens])
+    fe = gdn.FrontEnd(a.data_ptr(), b.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr())
+    gate_obj = gdn.OutputGate(gate[0].data_ptr(), gate[1].data_ptr(), gate[2])
+    code = gdn.DTYPE_BF16 if dt == "bf16" else gdn.DTYPE_F32
+    sptr = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    args_c = (q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(fe), cu, inp.N, s0.data_ptr(), out.data_ptr(),
+              fin.data_ptr(), None, inp.T, inp.H_q, inp.H_v, inp.d_k, inp.d_v, inp.scale, code, ws.data_ptr(),
+              ws.numel(), ctypes.byref(gate_obj), sptr)
+
+    def step():
+        rc = lib.gdn_chunk_fwd_fused(*args_c)
+        if rc != 0:
+            raise gdn.GdnError(rc, "gdn_chunk_fwd_fused")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    return {"workload": args.workload + " from raw q, k, a, b (front end in the kernels) with the gated read-out",
+            "ms_per_step": ms, "tokens_per_s": inp.T / (ms * 1e-3)}
+
+
 def bench_decode(args, torch, gdn, hip, device, fused=False, gated=False):
     """Decode steps on the 256 x 32-head batch: the plain step (normalised q, k and
     final g, beta) or, with fused, the step from raw q, k, a, b (front end inside)."""
@@ -429,6 +482,10 @@ def main():
         pre_g = bench_prefill(args, torch, gdn, hip, device, gated=True)
         print(f"[bench] prefill {args.workload} + gated read-out: {pre_g['ms_step']:.4f} ms/step, chunk_output_o "
               f"{pre_g['stage_ms']['chunk_output_o'] * 1e3:.1f} us", file=sys.stderr, flush=True)
+        pre_s = bench_prefill_serving(args, torch, gdn, device)
+        print(f"[bench] prefill {args.workload} from raw inputs + gated read-out: {pre_s['ms_per_step']:.4f} ms/step",
+              file=sys.stderr, flush=True)
+        res["prefill_serving"] = pre_s
     if args.only in ("all", "decode"):
         dec = bench_decode(args, torch, gdn, hip, device)
         print(f"[bench] decode: {dec['ms_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)

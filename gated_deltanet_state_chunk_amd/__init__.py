@@ -17,7 +17,7 @@ import os
 from typing import Optional, Sequence
 
 __all__ = ["chunk_fwd", "recurrent_step", "recurrent_step_fused", "conv1d_silu", "conv1d_silu_step",
-           "chunk_fwd_pooled", "conv1d_silu_pooled", "recurrent_step_fused_pooled", "conv1d_silu_step_pooled",
+           "chunk_fwd_fused", "chunk_fwd_pooled", "conv1d_silu_pooled", "recurrent_step_fused_pooled", "conv1d_silu_step_pooled",
            "state_rows_zero", "state_rows_copy", "workspace_layout", "workspace_size", "lib_path", "load_library",
            "GdnError", "CHUNK", "DTYPE_F32", "DTYPE_BF16"]
 
@@ -51,6 +51,12 @@ class WorkspaceLayout(ctypes.Structure):
 class OutputGate(ctypes.Structure):
     """gdn_output_gate: read-out epilogue out = rmsnorm(o) * weight * silu(z)."""
     _fields_ = [("z", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
+class FrontEnd(ctypes.Structure):
+    """gdn_front_end: raw gate inputs a, b and the per-head A_log, dt_bias."""
+    _fields_ = [("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("A_log", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p)]
 
 
 class StateSlots(ctypes.Structure):
@@ -145,6 +151,9 @@ def load_library():
     lib.gdn_recurrent_step_fused_pooled.argtypes = [P, P, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, F,
                                                     ctypes.c_int, P, P]
     lib.gdn_conv1d_silu_step_pooled.argtypes = [P, I32, I32, I32, P, P, P, P, I32, P, ctypes.c_int, P]
+    lib.gdn_chunk_fwd_fused.argtypes = [P, P, P, ctypes.POINTER(FrontEnd), P, I32, P, P, P, SL, I32, I32, I32, I32,
+                                        I32, F, ctypes.c_int, P, ctypes.c_size_t, P, P]
+    lib.gdn_chunk_fwd_fused.restype = ctypes.c_int
     lib.gdn_state_rows_zero.argtypes = [P, I32, ctypes.c_size_t, P, I32, P]
     lib.gdn_state_rows_copy.argtypes = [P, I32, ctypes.c_size_t, P, P, I32, P]
     for fn in ("gdn_chunk_fwd_pooled", "gdn_conv1d_silu_fwd_pooled", "gdn_recurrent_step_fused_pooled",
@@ -476,6 +485,73 @@ def chunk_fwd_pooled(q, k, v, g, beta, cu_seqlens: Sequence[int], state_pool, sl
     if rc != 0:
         raise GdnError(rc, "gdn_chunk_fwd_pooled")
     return out
+
+
+def chunk_fwd_fused(q, k, v, a, b, A_log, dt_bias, cu_seqlens: Sequence[int], initial_state=None,
+                    scale: Optional[float] = None, out=None, final_state=None, output_final_state: bool = True,
+                    workspace=None, stream=None, gate=None, slots=None, has_initial=None):
+    """Chunk-wise prefill from the raw inputs (gdn_chunk_fwd_fused): q, k are
+    L2-normalised and g, beta formed from a, b, A_log, dt_bias inside the kernels.
+
+    q, k: [T, H_q, d_k] (not normalised); v: [T, H_v, d_v]; a, b: [T, H_v] in q's
+    dtype; A_log, dt_bias: fp32 [H_v].  Without ``slots``: initial_state fp32
+    [N, H_v, d_k, d_v] or None, returns (out, final_state) as chunk_fwd.  With
+    ``slots`` (host ints [N]) and ``has_initial``: ``initial_state`` is a state
+    pool [P, H_v, d_k, d_v] read and written by slot; returns (out, None).
+    ``gate`` as for chunk_fwd.
+    """
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("a", a), ("b", b)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("A_log", A_log, torch.float32)
+    _check_dev("dt_bias", dt_bias, torch.float32)
+    T, H_q, d_k = q.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    if k.shape != q.shape or v.shape[0] != T or a.shape != (T, H_v) or b.shape != (T, H_v) or \
+            A_log.shape != (H_v,) or dt_bias.shape != (H_v,):
+        raise ValueError("inconsistent q/k/v/a/b/A_log/dt_bias shapes")
+    cu = _host_cu(cu_seqlens)
+    N = len(cu) - 1
+    st, keep_slots = None, None
+    if slots is not None:
+        if initial_state is None:
+            raise ValueError("with slots, initial_state is the state pool")
+        _check_dev("state pool", initial_state, torch.float32)
+        if initial_state.dim() != 4 or tuple(initial_state.shape[1:]) != (H_v, d_k, d_v):
+            raise ValueError("state pool must be [P, H_v, d_k, d_v]")
+        st, keep_slots = _slots_arg(slots, has_initial, initial_state.shape[0], N)
+        final_state = None
+    else:
+        if initial_state is not None:
+            _check_dev("initial_state", initial_state, torch.float32)
+            if tuple(initial_state.shape) != (N, H_v, d_k, d_v):
+                raise ValueError("initial_state must be [N, H_v, d_k, d_v]")
+        if final_state is None and output_final_state:
+            final_state = torch.empty((N, H_v, d_k, d_v), dtype=torch.float32, device=q.device)
+        elif final_state is not None:
+            _check_dev("final_state", final_state, torch.float32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    if out is None:
+        out = torch.empty((T, H_v, d_v), dtype=q.dtype, device=q.device)
+    else:
+        _check_dev("out", out, q.dtype)
+    ws_bytes = lib.gdn_chunk_fwd_workspace_size(T, N, cu, H_q, H_v, d_k, d_v, dt)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _check_dev("workspace", workspace)
+    fe = FrontEnd(_ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias))
+    gptr, _keep = _gate_arg(gate, q.dtype, T, H_v, d_v)
+    rc = lib.gdn_chunk_fwd_fused(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(fe), cu, N, _ptr(initial_state), _ptr(out),
+                                 _ptr(final_state), ctypes.byref(st) if st is not None else None, T, H_q, H_v, d_k,
+                                 d_v, float(scale), dt, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 gptr, _stream_ptr(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_chunk_fwd_fused")
+    return out, final_state
 
 
 def conv1d_silu_pooled(x, cu_seqlens: Sequence[int], weight, bias, state_pool, slots, has_initial=None, out=None,

@@ -200,7 +200,8 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, 
                    const int32_t* cu_seqlens_host, int32_t num_seqs, const float* initial_state, void* out,
                    float* final_state, const gdn_state_slots* slots, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k,
                    int32_t d_v, float scale, gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream,
-                   uint32_t flags, const gdn_output_gate* gate, void* const* stage_events) {
+                   uint32_t flags, const gdn_output_gate* gate, void* const* stage_events,
+                   const gdn_front_end* front = nullptr) {
     if (flags & ~(uint32_t)GDN_FWD_KEEP_A) return GDN_ERR_INVALID;
     if (gate) {
         const int grc = check_gate(gate, T > 0);
@@ -212,7 +213,17 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, 
     if (slots && (rc = check_slots(slots, num_seqs, initial_state)) != GDN_OK) return rc;
     if (num_seqs == 0) return GDN_OK;
     // Pointers: tensors with T > 0 rows must be present; all must be 16-byte aligned.
-    if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_INVALID;
+    if (T > 0 && (!q || !k || !v || !out)) return GDN_ERR_INVALID;
+    if (front) {
+        if (g || beta) return GDN_ERR_INVALID;
+        if (T > 0 && (!front->a || !front->b || !front->A_log || !front->dt_bias)) return GDN_ERR_INVALID;
+        const size_t es = elem_size(dtype);
+        if ((reinterpret_cast<uintptr_t>(front->a) % es) || (reinterpret_cast<uintptr_t>(front->b) % es) ||
+            (reinterpret_cast<uintptr_t>(front->A_log) & 3u) || (reinterpret_cast<uintptr_t>(front->dt_bias) & 3u))
+            return GDN_ERR_UNSUPPORTED;
+    } else if (T > 0 && (!g || !beta)) {
+        return GDN_ERR_INVALID;
+    }
     const void* ptrs[] = {q, k, v, g, beta, out, initial_state, final_state, workspace};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
@@ -231,6 +242,10 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, 
     p.gz = gate ? gate->z : nullptr;
     p.gw = gate ? gate->weight : nullptr;
     p.geps = gate ? gate->eps : 0.f;
+    p.fa = front ? front->a : nullptr;
+    p.fb = front ? front->b : nullptr;
+    p.A_log = front ? front->A_log : nullptr;
+    p.dt_bias = front ? front->dt_bias : nullptr;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     // Launch groups of up to MAX_SEQS_PER_LAUNCH sequences, each with its table in the kernel arguments.
@@ -391,6 +406,21 @@ int gdn_chunk_fwd_pooled(const void* q, const void* k, const void* v, const floa
     if (!slots) return GDN_ERR_INVALID;
     return chunk_fwd_impl(q, k, v, g, beta, cu_seqlens_host, num_seqs, state_pool, out, state_pool, slots, T, H_q,
                           H_v, d_k, d_v, scale, dtype, workspace, workspace_bytes, stream, 0u, gate, nullptr);
+}
+
+int gdn_chunk_fwd_fused(const void* q, const void* k, const void* v, const gdn_front_end* front,
+                        const int32_t* cu_seqlens_host, int32_t num_seqs, float* initial_state, void* out,
+                        float* final_state, const gdn_state_slots* slots, int32_t T, int32_t H_q, int32_t H_v,
+                        int32_t d_k, int32_t d_v, float scale, gdn_dtype dtype, void* workspace,
+                        size_t workspace_bytes, const gdn_output_gate* gate, void* stream) {
+    if (!front) return GDN_ERR_INVALID;
+    if (slots) {  // initial_state is the pool; final_state NULL or the same pool
+        if (final_state && final_state != initial_state) return GDN_ERR_INVALID;
+        final_state = initial_state;
+    }
+    return chunk_fwd_impl(q, k, v, nullptr, nullptr, cu_seqlens_host, num_seqs, initial_state, out, final_state,
+                          slots, T, H_q, H_v, d_k, d_v, scale, dtype, workspace, workspace_bytes, stream, 0u, gate,
+                          nullptr, front);
 }
 
 int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g, const float* beta, float* state,

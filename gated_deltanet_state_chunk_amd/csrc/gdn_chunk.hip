@@ -169,8 +169,13 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const ChunkParams p,
         }
         if (w == 0) {
             const size_t gi = (size_t)(c.t0 + lane) * p.H_v + hh;
-            graw = lane < c.ell ? p.g[gi] : 0.f;
-            braw = lane < c.ell ? p.beta[gi] : 0.f;
+            if (p.fa) {  // raw gate inputs (front end)
+                graw = lane < c.ell ? to_f32<T>(reinterpret_cast<const T*>(p.fa)[gi]) : 0.f;
+                braw = lane < c.ell ? to_f32<T>(reinterpret_cast<const T*>(p.fb)[gi]) : 0.f;
+            } else {
+                graw = lane < c.ell ? p.g[gi] : 0.f;
+                braw = lane < c.ell ? p.beta[gi] : 0.f;
+            }
         }
     };
     load_k(wid);
@@ -198,15 +203,21 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const ChunkParams p,
                               : make_float4(0, 0, 0, 0);
         }
     }
+    // With the front end, each K row is L2-normalised on the way (rows past the
+    // valid length are zero and stay zero).
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
-        *reinterpret_cast<float4*>(&s.K[r][c]) = kreg[j];
+        *reinterpret_cast<float4*>(&s.K[r][c]) = p.fa ? l2norm_piece<T, D>(kreg[j]) : kreg[j];
     }
-    // In-chunk inclusive cumsum of the log gate.
+    // In-chunk inclusive cumsum of the log gate (front end: g and beta from the
+    // raw inputs first).
     if (w == 0) {
-        float gv = graw;
-        const float bv = braw;
+        float gv = graw, bv = braw;
+        if (p.fa) {
+            gv = lane < ell ? front_gate(gv, p.A_log[h], p.dt_bias[h]) : 0.f;
+            bv = lane < ell ? front_beta<T>(bv) : 0.f;
+        }
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float o = __shfl_up(gv, off, 64);
@@ -847,13 +858,20 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
     // Q and K rows into LDS (zeros past the valid length), gates.
     const T* qb = reinterpret_cast<const T*>(p.q) + (size_t)cp.t0 * p.H_q * D + (size_t)hq * D;
     const T* kb = reinterpret_cast<const T*>(p.k) + (size_t)cp.t0 * p.H_q * D + (size_t)hq * D;
+    // (With the front end, rows L2-normalised on the way, as in chunk_prep.)
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
         const bool ok = r < ell;
         const size_t off = (size_t)r * p.H_q * D + c;
-        *reinterpret_cast<float4*>(&s.Q[r][c]) = ok ? *reinterpret_cast<const float4*>(qb + off) : make_float4(0, 0, 0, 0);
-        *reinterpret_cast<float4*>(&s.u.K[r][c]) = ok ? *reinterpret_cast<const float4*>(kb + off) : make_float4(0, 0, 0, 0);
+        float4 qv = ok ? *reinterpret_cast<const float4*>(qb + off) : make_float4(0, 0, 0, 0);
+        float4 kv = ok ? *reinterpret_cast<const float4*>(kb + off) : make_float4(0, 0, 0, 0);
+        if (p.fa) {
+            qv = l2norm_piece<T, D>(qv);
+            kv = l2norm_piece<T, D>(kv);
+        }
+        *reinterpret_cast<float4*>(&s.Q[r][c]) = qv;
+        *reinterpret_cast<float4*>(&s.u.K[r][c]) = kv;
     }
     if (tid < CHUNK) s.gc[tid] = p.gc[ch * CHUNK + tid];
     lds_sync();

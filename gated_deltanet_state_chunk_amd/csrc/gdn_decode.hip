@@ -59,11 +59,8 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(const DecodeParams 
     const T* vp = reinterpret_cast<const T*>(p.v) + (size_t)nh * D;
     float alpha, beta;
     if constexpr (FUSED) {
-        const float xa = to_f32<T>(reinterpret_cast<const T*>(p.a)[nh]) + p.dt_bias[h];
-        const float sp = xa > 20.f ? xa : (xa < -20.f ? expf(xa) : log1pf(expf(xa)));
-        alpha = expf(-expf(p.A_log[h]) * sp);
-        const float sg = 1.f / (1.f + expf(-to_f32<T>(reinterpret_cast<const T*>(p.b)[nh])));
-        beta = to_f32<T>(from_f32<T>(sg));  // rounded to the input dtype (RNE)
+        alpha = expf(front_gate(to_f32<T>(reinterpret_cast<const T*>(p.a)[nh]), p.A_log[h], p.dt_bias[h]));
+        beta = front_beta<T>(to_f32<T>(reinterpret_cast<const T*>(p.b)[nh]));  // rounded to the input dtype (RNE)
     } else {
         alpha = __expf(p.g[nh]);
         beta = p.beta[nh];

@@ -195,4 +195,52 @@ __device__ __forceinline__ void lds_sync() {
 // ---- wave helpers --------------------------------------------------------
 __device__ __forceinline__ float wave_shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
 
+// ---- row L2 normalisation of staged rows ---------------------------------
+// A D-element row held as 16-byte pieces by D / (16 / sizeof(T)) consecutive
+// lanes (aligned groups inside one wave): each lane returns its piece times
+// 1 / sqrt(sum over the row of x^2 + 1e-6), rounded to T.  All lanes of the
+// wave must take part (the sum is reduced with lane shuffles).
+template <typename T, int D>
+__device__ __forceinline__ float4 l2norm_piece(float4 raw) {
+    constexpr int VEC = 16 / (int)sizeof(T);
+    constexpr int LPR = D / VEC;  // lanes per row
+    static_assert(LPR <= 64 && (LPR & (LPR - 1)) == 0, "row must fit a power-of-two lane group");
+    if constexpr (sizeof(T) == 2) {
+        const bf16x8 v = __builtin_bit_cast(bf16x8, raw);
+        float x[8];
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            x[i] = (float)v[i];
+            ss += x[i] * x[i];
+        }
+#pragma unroll
+        for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m, 64);
+        const float r = 1.f / sqrtf(ss + 1e-6f);
+        bf16x8 o;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = (bf16)(x[i] * r);
+        return __builtin_bit_cast(float4, o);
+    } else {
+        float ss = raw.x * raw.x + raw.y * raw.y + raw.z * raw.z + raw.w * raw.w;
+#pragma unroll
+        for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m, 64);
+        const float r = 1.f / sqrtf(ss + 1e-6f);
+        return make_float4(raw.x * r, raw.y * r, raw.z * r, raw.w * r);
+    }
+}
+
+// ---- gate transform of the front end ---------------------------------------
+// g = -exp(A_log) softplus(a + dt_bias), softplus(x) = x for x > 20, exp(x)
+// for x < -20, log1p(exp(x)) otherwise; beta = sigmoid(b) rounded to T.
+__device__ __forceinline__ float front_gate(float a, float A_log, float dt_bias) {
+    const float xa = a + dt_bias;
+    const float sp = xa > 20.f ? xa : (xa < -20.f ? expf(xa) : log1pf(expf(xa)));
+    return -expf(A_log) * sp;
+}
+template <typename T>
+__device__ __forceinline__ float front_beta(float b) {
+    return to_f32<T>(from_f32<T>(1.f / (1.f + expf(-b))));
+}
+
 }  // namespace gdn

@@ -50,6 +50,12 @@ struct ChunkParams {
     const void* gz;
     const float* gw;
     float geps;
+    // optional front end (fa null: none): q, k are raw and L2-normalised in the
+    // kernels; g, beta come from fa, fb (dtype [T, H_v]) with A_log, dt_bias [H_v]
+    const void* fa;
+    const void* fb;
+    const float* A_log;
+    const float* dt_bias;
     SeqTable tab;
 };
 

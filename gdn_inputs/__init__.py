@@ -238,6 +238,67 @@ def make_decode_raw_token(seed: int, N: int, H_q: int, H_v: int, d_k: int, d_v: 
     return DecodeRawToken(dtype, q, k, v, a, b, A_log, dt_bias)
 
 
+@dataclasses.dataclass
+class PrefillRawInputs:
+    """Raw inputs of the prefill with its front end: q, k [T, H_q, d_k] (not
+    normalised), v [T, H_v, d_v], a, b [T, H_v] in the storage dtype; A_log,
+    dt_bias [H_v] float32; cu_seqlens int32 [N+1]; initial_state float32
+    [N, H_v, d_k, d_v] or None."""
+
+    dtype: str
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    a: np.ndarray
+    b: np.ndarray
+    A_log: np.ndarray
+    dt_bias: np.ndarray
+    cu_seqlens: np.ndarray
+    initial_state: Optional[np.ndarray]
+    H_q: int
+    H_v: int
+    d_k: int
+    d_v: int
+
+    @property
+    def T(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def N(self) -> int:
+        return len(self.cu_seqlens) - 1
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d_k))
+
+    def f32(self, name):
+        return storage_to_f32(getattr(self, name), self.dtype)
+
+
+def make_prefill_raw(seed: int, seqlens, H_q: int, H_v: int, d_k: int, d_v: int, dtype: str = "bf16",
+                     state_std: Optional[float] = 0.02) -> PrefillRawInputs:
+    """The decode raw-token recipe over a packed batch: q, k, v, a, b ~ N(0, 1)
+    rounded to the storage dtype, A_log = ln U(1, 16), dt_bias ~ U(-7, -2.3) per
+    value head, initial states ~ N(0, state_std^2)."""
+    rng = np.random.default_rng(seed)
+    seqlens = np.asarray(seqlens, dtype=np.int64)
+    cu = np.zeros(len(seqlens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(seqlens)
+    T, N = int(cu[-1]), len(seqlens)
+    q = round_to(rng.standard_normal((T, H_q, d_k), dtype=np.float32), dtype)
+    k = round_to(rng.standard_normal((T, H_q, d_k), dtype=np.float32), dtype)
+    v = round_to(rng.standard_normal((T, H_v, d_v), dtype=np.float32), dtype)
+    a = round_to(rng.standard_normal((T, H_v), dtype=np.float32), dtype)
+    b = round_to(rng.standard_normal((T, H_v), dtype=np.float32), dtype)
+    A_log = np.log(rng.uniform(1.0, 16.0, size=H_v)).astype(np.float32)
+    dt_bias = rng.uniform(-7.0, -2.3, size=H_v).astype(np.float32)
+    s0 = None
+    if state_std is not None:
+        s0 = (rng.standard_normal((N, H_v, d_k, d_v), dtype=np.float32) * np.float32(state_std)).astype(np.float32)
+    return PrefillRawInputs(dtype, q, k, v, a, b, A_log, dt_bias, cu, s0, H_q, H_v, d_k, d_v)
+
+
 def make_gate(seed: int, rows: int, H_v: int, d_v: int, dtype: str = "bf16"):
     """Inputs of the gated RMSNorm read-out: z [rows, H_v, d_v] ~ N(0, 1) in the
     storage dtype, weight [d_v] ~ U(0.5, 1.5) float32."""

@@ -327,6 +327,43 @@ int gdn_conv1d_silu_step_pooled(const void *x, int32_t N, int32_t C, int32_t K, 
                                 void *out, gdn_dtype dtype, void *stream);
 
 /*
+ * Front end of the prefill ("Qwen3.5-397B-A17B" trace page, section 1,
+ * Prefill-GDN graph: node 8 gdn_gating turns a, b into g, beta; nodes 9 and 10
+ * L2-normalise q and k), done inside the chunk kernels as rows are staged:
+ *     k_bar = k / sqrt(sum_j k_j^2 + 1e-6),  q_bar = q / sqrt(sum_j q_j^2 + 1e-6)
+ *             (each rounded to dtype, as the normalisation nodes write them)
+ *     g     = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h])   (the +-20 branches
+ *             of gdn_recurrent_step_fused)
+ *     beta  = sigmoid(b[t,h]) rounded to dtype
+ * then the chunk form of gdn_chunk_fwd on (q_bar, k_bar, v, g, beta); the output
+ * scale is the `scale` argument (the model's 1 / sqrt(d_k)).
+ *   a, b      dtype [T, H_v], aligned to their element size
+ *   A_log, dt_bias  fp32 [H_v], 4-byte aligned
+ */
+typedef struct gdn_front_end {
+    const void *a;
+    const void *b;
+    const float *A_log;
+    const float *dt_bias;
+} gdn_front_end;
+
+/*
+ * Chunk-wise prefill from the raw per-token inputs: q, k not normalised, and
+ * the gdn_front_end inputs in place of g and beta.  Other arguments as
+ * gdn_chunk_fwd, plus
+ *   slots   NULL: initial_state / final_state as in gdn_chunk_fwd.  Non-NULL:
+ *           initial_state is a state pool addressed by slots (see
+ *           gdn_state_slots) and final_state must be NULL or the same pointer.
+ *   gate    NULL, or the read-out epilogue (gdn_output_gate) applied to out.
+ * front == NULL: GDN_ERR_INVALID.  The workspace is gdn_chunk_fwd's.
+ */
+int gdn_chunk_fwd_fused(const void *q, const void *k, const void *v, const gdn_front_end *front,
+                        const int32_t *cu_seqlens_host, int32_t num_seqs, float *initial_state, void *out,
+                        float *final_state, const gdn_state_slots *slots, int32_t T, int32_t H_q, int32_t H_v,
+                        int32_t d_k, int32_t d_v, float scale, gdn_dtype dtype, void *workspace,
+                        size_t workspace_bytes, const gdn_output_gate *gate, void *stream);
+
+/*
  * Pool row maintenance (the "Kestrel_VLLM - 24" page, section 五, resets its
  * single state mirror for a new sequence and leaves branch cloning for
  * speculative decoding to later; here both work on any pool).  The pool is

@@ -301,6 +301,34 @@ def test_pooled_entry_points_reject_before_any_device_work(gdn):
     assert lib.gdn_state_rows_copy(p, 8, 1024, p + 2, p, 4, None) == -2
 
 
+def test_fused_prefill_rejects_before_any_device_work(gdn):
+    lib = gdn.load_library()
+    keep, p = _fake()
+    cu = _cu([0, 10])
+
+    def call(front, slots=None, **kw):
+        a = dict(q=p, k=p, v=p, cu=cu, N=1, s0=p, out=p, fin=p, T=10, H_q=2, H_v=4, dk=128, dv=128, scale=0.1, dt=1,
+                 ws=p, wsb=1 << 40)
+        a.update(kw)
+        return lib.gdn_chunk_fwd_fused(a["q"], a["k"], a["v"], ctypes.byref(front) if front is not None else None,
+                                       a["cu"], a["N"], a["s0"], a["out"], a["fin"],
+                                       ctypes.byref(slots[0]) if slots is not None else None, a["T"], a["H_q"],
+                                       a["H_v"], a["dk"], a["dv"], a["scale"], a["dt"], a["ws"], a["wsb"], None, None)
+
+    fe = gdn.FrontEnd(p, p, p, p)
+    assert call(None) == -1                                   # the front end is required
+    assert call(gdn.FrontEnd(None, p, p, p)) == -1            # a missing
+    assert call(gdn.FrontEnd(p, p, None, p)) == -1            # A_log missing
+    assert call(gdn.FrontEnd(p + 1, p, p, p)) == -2           # bf16 a off its 2-byte alignment
+    assert call(gdn.FrontEnd(p, p, p, p + 2)) == -2           # fp32 dt_bias off its 4-byte alignment
+    assert call(fe, dk=64) == -2
+    assert call(fe, ws=None) == -3
+    sl = gdn._slots_arg([0], None, 4, 1)
+    assert call(fe, slots=sl, fin=p + 256) == -1              # with slots, final_state is the pool or NULL
+    assert call(fe, slots=gdn._slots_arg([4], None, 4, 1)) == -1   # slot past the pool
+    assert call(fe, N=0, T=0, cu=_cu([0])) == 0
+
+
 def test_binding_refuses_host_tensors(gdn):
     torch = pytest.importorskip("torch")
     q = torch.zeros(4, 2, 64)
