@@ -875,20 +875,21 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
     }
     if (tid < CHUNK) s.gc[tid] = p.gc[ch * CHUNK + tid];
     lds_sync();
-    // Gated read-out: this lane's z values (rows past the valid length re-read the
-    // last valid row; they are never stored) and norm weights, fetched after the Q/K staging
-    // (so those loads are not queued behind them).
-    Raw4<T> zr[GATED ? 4 : 1][GATED ? TPW : 1];
+    // Gated read-out: this lane's z values of one position tile (rows past the
+    // valid length re-read the last valid row; they are never stored) and the
+    // norm weights.  Tile 0's z goes out after the Q/K staging (so those loads are
+    // not queued behind it); each later tile's while the previous one is computed.
+    Raw4<T> zc[GATED ? TPW : 1], zn[GATED ? TPW : 1];
     float4 wv[GATED ? TPW : 1];
+    const T* zb = GATED ? reinterpret_cast<const T*>(p.gz) + (size_t)cp.t0 * p.H_v * D + (size_t)h * D : nullptr;
+    auto load_z = [&](Raw4<T>(&zz)[GATED ? TPW : 1], int nt) {
+        const int pos = min(16 * nt + r16, ell - 1);
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+            load_raw4(zz[tt], zb + (size_t)pos * p.H_v * D + 16 * (w * TPW + tt) + 4 * grp);
+    };
     if constexpr (GATED) {
-        const T* zb = reinterpret_cast<const T*>(p.gz) + (size_t)cp.t0 * p.H_v * D + (size_t)h * D;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-            for (int tt = 0; tt < TPW; ++tt) {
-                const int pos = min(16 * nt + r16, ell - 1);
-                load_raw4(zr[nt][tt], zb + (size_t)pos * p.H_v * D + 16 * (w * TPW + tt) + 4 * grp);
-            }
+        load_z(zc, 0);
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt)
             wv[tt] = *reinterpret_cast<const float4*>(p.gw + 16 * (w * TPW + tt) + 4 * grp);
@@ -935,11 +936,17 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
     }
     lds_sync();
 
-    // Output tiles: rows d_v (this wave's tiles), columns pos.
+    // Output tiles: rows d_v (this wave's tiles), columns pos.  With the read-out
+    // epilogue, each position tile is normalised as soon as it is complete: its
+    // sums of o^2 over this lane's values, the four lanes sharing a position
+    // (grp), then the four waves through LDS (one barrier per tile), so only one
+    // tile of o is held in registers.
     T* ob = reinterpret_cast<T*>(p.out) + (size_t)cp.t0 * p.H_v * D + (size_t)h * D;
-    f32x4 ov[GATED ? 4 : 1][TPW];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
+        if constexpr (GATED) {
+            if (nt + 1 < 4) load_z(zn, nt + 1);
+        }
         Frag<T> qf[KS], pf[2];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) load8(qf[ks], &s.Q[16 * nt + r16][32 * ks + 8 * grp]);
@@ -947,6 +954,7 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
         pf[1] = s.u.pr.P[nt][1][lane];
         const int pos = 16 * nt + r16;
         const float eg = __expf(s.gc[pos]);
+        f32x4 ov[TPW];
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
             f32x4 inter = zero4(), intra = zero4();
@@ -954,49 +962,40 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
             for (int ks = 0; ks < KS; ++ks) inter = mma(hf[tt][ks], qf[ks], inter);
             intra = mma(xf[tt][0], pf[0], intra);
             if (nt >= 2) intra = mma(xf[tt][1], pf[1], intra);  // P^T rows 32..63 vanish for queries < 32
-            f32x4 o4;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o4[i] = p.scale * (eg * inter[i] + intra[i]);
-            if constexpr (GATED) {
-                ov[nt][tt] = o4;
-            } else if (pos < ell) {
-                store4(ob + (size_t)pos * p.H_v * D + 16 * (w * TPW + tt) + 4 * grp, o4[0], o4[1], o4[2], o4[3]);
+            for (int i = 0; i < 4; ++i) ov[tt][i] = p.scale * (eg * inter[i] + intra[i]);
+            if constexpr (!GATED) {
+                if (pos < ell)
+                    store4(ob + (size_t)pos * p.H_v * D + 16 * (w * TPW + tt) + 4 * grp, ov[tt][0], ov[tt][1],
+                           ov[tt][2], ov[tt][3]);
             }
         }
-    }
-    if constexpr (GATED) {
-        // Head-wise RMS over d_v: this lane's values, the four lanes sharing a
-        // position (grp), then the four waves through LDS.
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        if constexpr (GATED) {
             float ssq = 0.f;
 #pragma unroll
             for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ssq += ov[nt][tt][i] * ov[nt][tt][i];
+                for (int i = 0; i < 4; ++i) ssq += ov[tt][i] * ov[tt][i];
             ssq += wave_shfl_xor(ssq, 16);
             ssq += wave_shfl_xor(ssq, 32);
-            if (grp == 0) s.u.pr.ss[w][16 * nt + r16] = ssq;
-        }
-        lds_sync();
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            const int pos = 16 * nt + r16;
+            if (grp == 0) s.u.pr.ss[w][pos] = ssq;
+            lds_sync();
             const float rstd =
                 1.f / sqrtf((s.u.pr.ss[0][pos] + s.u.pr.ss[1][pos] + s.u.pr.ss[2][pos] + s.u.pr.ss[3][pos]) * (1.f / D) +
                             p.geps);
             if (pos < ell) {
 #pragma unroll
                 for (int tt = 0; tt < TPW; ++tt) {
-                    const f32x4 zf = raw4_to_f32(zr[nt][tt]);
+                    const f32x4 zf = raw4_to_f32(zc[tt]);
                     const float wf[4] = {wv[tt].x, wv[tt].y, wv[tt].z, wv[tt].w};
                     float y[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        y[i] = ov[nt][tt][i] * rstd * wf[i] * (zf[i] / (1.f + __expf(-zf[i])));
+                    for (int i = 0; i < 4; ++i) y[i] = ov[tt][i] * rstd * wf[i] * (zf[i] / (1.f + __expf(-zf[i])));
                     store4(ob + (size_t)pos * p.H_v * D + 16 * (w * TPW + tt) + 4 * grp, y[0], y[1], y[2], y[3]);
                 }
             }
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) zc[tt] = zn[tt];
         }
     }
 }
