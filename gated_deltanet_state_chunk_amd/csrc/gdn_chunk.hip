@@ -990,7 +990,7 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
                     const float wf[4] = {wv[tt].x, wv[tt].y, wv[tt].z, wv[tt].w};
                     float y[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) y[i] = ov[tt][i] * rstd * wf[i] * (zf[i] / (1.f + __expf(-zf[i])));
+                    for (int i = 0; i < 4; ++i) y[i] = ov[tt][i] * rstd * wf[i] * silu_f32(zf[i]);
                     store4(ob + (size_t)pos * p.H_v * D + 16 * (w * TPW + tt) + 4 * grp, y[0], y[1], y[2], y[3]);
                 }
             }

@@ -82,7 +82,7 @@ __device__ __forceinline__ Vec16<T> from_floats(const float* f) {
     return r;
 }
 
-__device__ __forceinline__ float silu(float a) { return a / (1.f + __expf(-a)); }
+__device__ __forceinline__ float silu(float a) { return silu_f32(a); }
 
 // The weights [C][K] of a thread's V channels are K*V consecutive floats
 // starting 16-byte aligned (c is a multiple of V): load them as float4s.

@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(const DecodeParams 
             const float4 wv = *reinterpret_cast<const float4*>(p.gw + 4 * cg);
             const float wf[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-            for (int c = 0; c < 4; ++c) o[c] = o[c] * rstd * wf[c] * (zv[c] / (1.f + __expf(-zv[c])));
+            for (int c = 0; c < 4; ++c) o[c] = o[c] * rstd * wf[c] * silu_f32(zv[c]);
         }
     }
     if (rg == 0) store4(reinterpret_cast<T*>(p.out) + (size_t)nh * D + 4 * cg, o[0], o[1], o[2], o[3]);

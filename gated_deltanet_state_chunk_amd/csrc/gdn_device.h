@@ -230,6 +230,12 @@ __device__ __forceinline__ float4 l2norm_piece(float4 raw) {
     }
 }
 
+// ---- SiLU ------------------------------------------------------------------
+// x * sigmoid(x) with the hardware reciprocal (v_rcp_f32, about 1 ulp) rather
+// than an IEEE division sequence, which dominated the VALU time where SiLU is
+// applied per element (the convolution, the gated read-out).
+__device__ __forceinline__ float silu_f32(float x) { return x * __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+
 // ---- gate transform of the front end ---------------------------------------
 // g = -exp(A_log) softplus(a + dt_bias), softplus(x) = x for x > 20, exp(x)
 // for x < -20, log1p(exp(x)) otherwise; beta = sigmoid(b) rounded to T.
