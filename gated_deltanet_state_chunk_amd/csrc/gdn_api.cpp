@@ -104,6 +104,12 @@ int32_t fill_table(gdn::SeqTable& tab, const int32_t* cu, int32_t s0, int32_t ns
         }
     }
     tab.n_chunks = c - chunk_base;
+    // Longest sequences first (stable): the serial state scan then starts its
+    // longest chains earliest.
+    for (int32_t i = 0; i < ns; ++i) tab.order[i] = i;
+    std::stable_sort(tab.order, tab.order + ns, [&](int32_t a, int32_t b) {
+        return tab.choff[a + 1] - tab.choff[a] > tab.choff[b + 1] - tab.choff[b];
+    });
     return c;
 }
 

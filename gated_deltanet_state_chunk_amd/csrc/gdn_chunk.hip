@@ -608,11 +608,16 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
     constexpr int KS = D / 32;   // contraction steps over d_k
     constexpr int TPW = D / 64;  // S row tiles per compute wave
     constexpr int NST = SS::NST;
-    const int wid = xcd_remap(blockIdx.x, padded);
-    if (wid >= p.tab.num_seqs * p.H_v * NT) return;
-    const int tile = wid % NT;
-    const int u = wid / NT;
-    const int h = u % p.H_v, n = u / p.H_v;
+    // Work groups of NT tiles, one per (sequence, value head), longest sequences
+    // first; group g runs on XCD g % 8 (workgroup i lands on XCD i % 8) with its
+    // tiles in consecutive slots, so the tiles of a head share an L2 and every
+    // XCD gets an even share of long and short sequences.
+    (void)padded;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int gi = (slot / NT) * 8 + xcd;
+    if (gi >= p.tab.num_seqs * p.H_v) return;
+    const int tile = slot % NT;
+    const int h = gi % p.H_v, n = p.tab.order[gi / p.H_v];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
     const int col = 16 * tile + r16;
@@ -1024,7 +1029,7 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
     const int work_ch = p.tab.n_chunks * p.H_v;
     const int grid_ch = pad8(work_ch);
     const int work_st = p.tab.num_seqs * p.H_v * (D / 16);
-    const int grid_st = pad8(work_st);
+    const int grid_st = pad8(p.tab.num_seqs * p.H_v) * (D / 16);  // whole groups of tiles on each XCD
     // With events, each kernel is launched with hipExtLaunchKernelGGL, whose
     // start/stop events are stamped by the kernel's own dispatch (kernel time
     // only, no launch gaps).

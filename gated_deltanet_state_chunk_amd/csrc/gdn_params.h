@@ -24,6 +24,7 @@ struct SeqTable {
     int32_t choff[MAX_SEQS_PER_LAUNCH + 1];  // global chunk offsets, choff[num_seqs] = chunk_begin + n_chunks
     int32_t s_in[MAX_SEQS_PER_LAUNCH];       // row of the initial-state array a sequence starts from, -1: zeros
     int32_t s_out[MAX_SEQS_PER_LAUNCH];      // row of the final-state array it ends in, -1: none
+    int32_t order[MAX_SEQS_PER_LAUNCH];      // sequences by decreasing chunk count (state scan dispatch order)
 };
 
 struct ChunkParams {
