@@ -131,7 +131,7 @@ struct PrepLds {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const ChunkParams p, int padded) {
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel(const ChunkParams p, int padded) {
     using PL = PrepLds<T, D>;
     constexpr int VEC = 16 / (int)sizeof(T);                  // elements per 16-byte access
     constexpr int NV = CHUNK * D / VEC / 256;                 // 16-byte pieces per thread
@@ -144,7 +144,6 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const ChunkParams p,
     int wid = xcd_remap(v, padded);
     if (wid >= work) return;  // padding items come last, so all later ones are padding too
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int r16 = lane & 15, grp = lane >> 4;
 
     __shared__ __attribute__((aligned(16))) PL s;
     float* const Ls = s.u.sv.LA;
@@ -493,7 +492,7 @@ struct StateStage {
     // Two LDS stages: the compute waves copy chunk c into registers before
     // B1(c), so stage c % 2 is refilled with chunk c + 2 from B1(c) on.
     static constexpr int LDS_CAP = 160 * 1024;
-    static constexpr int NST = (3 * BYTES + EXCH <= LDS_CAP) ? 3 : 2;
+    static constexpr int NST = (3 * BYTES + EXCH + 256 <= LDS_CAP) ? 3 : 2;  // + the L2-prefetch sink
 };
 
 typedef __attribute__((address_space(1))) const void* gptr_t;
@@ -628,7 +627,7 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
     const int nch = p.tab.choff[n + 1] - p.tab.choff[n];
     const int c0 = p.tab.choff[n];
 
-    __shared__ __attribute__((aligned(16))) char smem[NST * SS::BYTES + SS::EXCH];
+    __shared__ __attribute__((aligned(16))) char smem[NST * SS::BYTES + SS::EXCH + 256];  // + L2-prefetch sink
     Frag<T>(*LS)[64] = reinterpret_cast<Frag<T>(*)[64]>(smem + NST * SS::BYTES);           // [KS][64]: -S
     Frag<T>(*LX)[64] = reinterpret_cast<Frag<T>(*)[64]>(smem + NST * SS::BYTES + KS * 64 * sizeof(Frag<T>));  // [2][64]: X
 
@@ -643,10 +642,26 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         constexpr int FQ = sizeof(Frag<T>) / 16;  // 16-byte pieces per fragment
         const unsigned sgn = sizeof(T) == 2 ? 0x80008000u : 0x80000000u;
         const unsigned ls_addr = lds_addr(&LS[0][lane]), lx_addr = lds_addr(&LX[0][lane]);
+        // L2 prefetch: once a step, this tile's share of the W and Kd lines of
+        // chunk c + PF (4 bytes per line, into a sink nobody reads).  The tiles of
+        // a head together touch every line, so by the time the producers stream
+        // that chunk it is in L2.  It pays where the stream comes from HBM rather
+        // than from the Infinity Cache (long or many sequences).
+        constexpr int PF = 6;
+        constexpr int LPT = SS::W_BYTES / 128 / NT;  // lines of W (and of Kd) per tile
+        static_assert(2 * LPT <= 64, "one line per lane");
+        const int li = tile * LPT + lane % LPT;
+        const bool kd_line = (lane / LPT) & 1;
         asm volatile("s_barrier" ::: "memory");  // B0
         for (int c = 0; c < nch; ++c) {
             const size_t ch = (size_t)(c0 + c) * p.H_v + h;
             asm volatile("s_barrier" ::: "memory");  // B1(c)
+            if (c + PF < nch) {
+                const size_t chp = (size_t)(c0 + c + PF) * p.H_v + h;
+                const char* a = kd_line ? reinterpret_cast<const char*>(p.Kt) + chp * SS::K_BYTES + li * 128
+                                        : reinterpret_cast<const char*>(p.W) + chp * SS::W_BYTES + li * 128;
+                __builtin_amdgcn_global_load_lds((gptr_t)a, (lptr_t)(smem + NST * SS::BYTES + SS::EXCH), 4, 0, 0);
+            }
             u32x4 hs[KS][FQ];
             lds_read_untracked<KS * FQ>(&hs[0][0], ls_addr, 64 * sizeof(Frag<T>), FQ);
             lds_wait_untracked<KS * FQ>(&hs[0][0]);
@@ -674,6 +689,7 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
                 for (int e = 0; e < FQ; ++e)
                     *reinterpret_cast<u32x4*>(Xb + 32 * j + 8 * grp + e * (16 / (int)sizeof(T))) = xs[j][e];
         }
+        wait_vmcnt<0>();  // no prefetch may land in LDS after the workgroup has ended
         return;
     }
     if (w >= 4) {
