@@ -237,7 +237,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, 
     if (L.n_chunks > 0 && (!workspace || workspace_bytes < L.total_bytes)) return GDN_ERR_WORKSPACE;
 
     char* ws = static_cast<char*>(workspace);
-    gdn::ChunkParams p;
+    gdn::ChunkParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
     p.s0 = initial_state; p.out = out; p.sfinal = final_state;
     p.gc = reinterpret_cast<float*>(ws + L.off_gc);

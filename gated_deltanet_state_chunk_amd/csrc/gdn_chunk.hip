@@ -646,7 +646,8 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         // chunk c + PF (4 bytes per line, into a sink nobody reads).  The tiles of
         // a head together touch every line, so by the time the producers stream
         // that chunk it is in L2.  It pays where the stream comes from HBM rather
-        // than from the Infinity Cache (long or many sequences).
+        // than from the Infinity Cache (long or many sequences), and costs a few
+        // per cent where it does not, so the launcher enables it by size.
         constexpr int PF = 6;
         constexpr int LPT = SS::W_BYTES / 128 / NT;  // lines of W (and of Kd) per tile
         static_assert(2 * LPT <= 64, "one line per lane");
@@ -656,7 +657,7 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         for (int c = 0; c < nch; ++c) {
             const size_t ch = (size_t)(c0 + c) * p.H_v + h;
             asm volatile("s_barrier" ::: "memory");  // B1(c)
-            if (c + PF < nch) {
+            if (p.l2_prefetch && c + PF < nch) {
                 const size_t chp = (size_t)(c0 + c + PF) * p.H_v + h;
                 const char* a = kd_line ? reinterpret_cast<const char*>(p.Kt) + chp * SS::K_BYTES + li * 128
                                         : reinterpret_cast<const char*>(p.W) + chp * SS::W_BYTES + li * 128;
@@ -1049,23 +1050,28 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
     // With events, each kernel is launched with hipExtLaunchKernelGGL, whose
     // start/stop events are stamped by the kernel's own dispatch (kernel time
     // only, no launch gaps).
-    auto launch = [&](int k, auto kernel, int grid, int block, int padded) {
+    auto launch = [&](int k, auto kernel, int grid, int block, int padded, const ChunkParams& kp) {
         if (events)
-            hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, stream, events[2 * k], events[2 * k + 1], 0, p,
+            hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, stream, events[2 * k], events[2 * k + 1], 0, kp,
                                   padded);
         else
-            hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, stream, p, padded);
+            hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, stream, kp, padded);
     };
+    // The state scan's L2 prefetch pays when its W / Kd / U stream no longer
+    // fits in the 256 MB Infinity Cache next to the layer's other tensors: on
+    // above 128 MiB of stream.
+    ChunkParams pl = p;
+    pl.l2_prefetch = (size_t)work_ch * StateStage<T, D>::BYTES > (size_t(128) << 20) ? 1 : 0;
     // chunk_prep runs as many workgroups as fit on the chip at once (four per CU)
     // and loops over the rest, prefetching each next item.
     const int prep_slots = 4 * cu_count();
-    if (work_ch > 0) launch(0, chunk_prep_kernel<T, D>, std::min(grid_ch, prep_slots), 256, grid_ch);
-    if (work_st > 0) launch(1, chunk_state_h_kernel<T, D>, grid_st, 64 * (5 + StateStage<T, D>::NPW), grid_st);
+    if (work_ch > 0) launch(0, chunk_prep_kernel<T, D>, std::min(grid_ch, prep_slots), 256, grid_ch, pl);
+    if (work_st > 0) launch(1, chunk_state_h_kernel<T, D>, grid_st, 64 * (5 + StateStage<T, D>::NPW), grid_st, pl);
     if (work_ch > 0) {
         if (p.gz)
-            launch(2, chunk_output_o_kernel<T, D, true>, grid_ch, 256, grid_ch);
+            launch(2, chunk_output_o_kernel<T, D, true>, grid_ch, 256, grid_ch, pl);
         else
-            launch(2, chunk_output_o_kernel<T, D, false>, grid_ch, 256, grid_ch);
+            launch(2, chunk_output_o_kernel<T, D, false>, grid_ch, 256, grid_ch, pl);
     }
     return hipGetLastError();
 }

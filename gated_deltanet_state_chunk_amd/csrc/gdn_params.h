@@ -47,6 +47,7 @@ struct ChunkParams {
     int32_t H_q, H_v, G;
     float scale;
     int32_t keep_A;  // nonzero: chunk_prep also writes A to the workspace
+    int32_t l2_prefetch;  // nonzero: chunk_state_h prefetches W / Kd into L2 (set by the launcher)
     // optional read-out epilogue out = rmsnorm(o) * gw * silu(gz) (gz null: none)
     const void* gz;
     const float* gw;
