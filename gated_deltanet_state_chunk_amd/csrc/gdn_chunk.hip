@@ -358,15 +358,27 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
     // W^T tiles: rows d_k (this wave's tiles), columns pos.  A is lower triangular,
     // so column tile nt only needs contraction steps ks with 32 ks <= 16 nt + 15.
     T* Wb = reinterpret_cast<T*>(p.W) + ch * CHUNK * D;
-    auto w_kfrag = [&](Frag<T>(&kf)[2], int mt) {  // (B Gamma K)^T rows of d_k tile mt, contraction pos
-        const int dk = 16 * mt + r16;
+    // A fragment of 8 consecutive positions (32 ks + 8 grp ..) of one column of a
+    // staged [pos][col] matrix, each value scaled by its position's factor.  For
+    // bf16 the columns come from LDS with transposed reads (two per fragment);
+    // for fp32 element by element.
+    auto col_frag = [&](Frag<T>& f, const T* M, const float* sc, int ks, int c) {
+        const int r0 = 32 * ks + 8 * grp;
+        if constexpr (sizeof(T) == 2) {
+            const bf16x4 lo = lds_col4<PL::KP>(M, r0, c & ~15, lane), hi = lds_col4<PL::KP>(M, r0 + 4, c & ~15, lane);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int r = 32 * ks + 8 * grp + j;
-                frag_set(kf[ks], j, s.sk[r] * to_f32<T>(s.K[r][dk]));
+            for (int j = 0; j < 4; ++j) {
+                frag_set(f, j, sc[r0 + j] * (float)lo[j]);
+                frag_set(f, 4 + j, sc[r0 + 4 + j] * (float)hi[j]);
             }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) frag_set(f, j, sc[r0 + j] * to_f32<T>(M[(r0 + j) * PL::KP + c]));
+        }
+    };
+    auto w_kfrag = [&](Frag<T>(&kf)[2], int mt) {  // (B Gamma K)^T rows of d_k tile mt, contraction pos
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) col_frag(kf[ks], &s.K[0][0], s.sk, ks, 16 * mt + r16);
     };
     // lane: column pos = 16 nt + r16, rows d_k = 16 mt + 4 grp + i: in fragment
     // order this is fragment (pos tile nt, K-step mt / 2), same lane, slots 4 (mt % 2) + i
@@ -407,12 +419,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
         const int dv = 16 * nt + r16;
         Frag<T> vf[2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int r = 32 * ks + 8 * grp + j;
-                frag_set(vf[ks], j, s.svb[r] * to_f32<T>(s.u.V[r][dv]));
-            }
+        for (int ks = 0; ks < 2; ++ks) col_frag(vf[ks], &s.u.V[0][0], s.svb, ks, dv);
         // lane: column d_v = 16 nt + r16, rows pos = 16 mt + 4 grp + i (accumulator
         // order); row tiles 2 m and 2 m + 1 share one 16-byte store
 #pragma unroll
@@ -427,15 +434,28 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
     }
     // Decayed keys of the state update, transposed: item (dk, s, a) covers the
     // 8 positions 32 s + 16 h + 4 a + b (h, b) that are consecutive in fragment order.
+    // Items run over dk fastest, so each group of 16 lanes covers 16 consecutive
+    // columns at one (s, a) (as the transposed reads need).
     {
         T* Kb = reinterpret_cast<T*>(p.Kt) + ch * D * CHUNK;
-        for (int e = tid; e < D * 8; e += 256) {
-            const int dk = e >> 3, sa = e & 7, r0 = 32 * (sa >> 2) + 4 * (sa & 3);
-            f32x4 lo, hi;
 #pragma unroll
-            for (int b4 = 0; b4 < 4; ++b4) {
-                lo[b4] = s.kd[r0 + b4] * to_f32<T>(s.K[r0 + b4][dk]);
-                hi[b4] = s.kd[r0 + 16 + b4] * to_f32<T>(s.K[r0 + 16 + b4][dk]);
+        for (int e = tid; e < D * 8; e += 256) {
+            const int dk = e % D, sa = e / D, r0 = 32 * (sa >> 2) + 4 * (sa & 3);
+            f32x4 lo, hi;
+            if constexpr (sizeof(T) == 2) {
+                const bf16x4 kl = lds_col4<PL::KP>(&s.K[0][0], r0, dk & ~15, lane);
+                const bf16x4 kh = lds_col4<PL::KP>(&s.K[0][0], r0 + 16, dk & ~15, lane);
+#pragma unroll
+                for (int b4 = 0; b4 < 4; ++b4) {
+                    lo[b4] = s.kd[r0 + b4] * (float)kl[b4];
+                    hi[b4] = s.kd[r0 + 16 + b4] * (float)kh[b4];
+                }
+            } else {
+#pragma unroll
+                for (int b4 = 0; b4 < 4; ++b4) {
+                    lo[b4] = s.kd[r0 + b4] * to_f32<T>(s.K[r0 + b4][dk]);
+                    hi[b4] = s.kd[r0 + 16 + b4] * to_f32<T>(s.K[r0 + 16 + b4][dk]);
+                }
             }
             store8(Kb + frag_k_offset(dk, r0), lo, hi);
         }

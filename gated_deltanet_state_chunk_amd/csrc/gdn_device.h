@@ -195,6 +195,23 @@ __device__ __forceinline__ void lds_sync() {
 // ---- wave helpers --------------------------------------------------------
 __device__ __forceinline__ float wave_shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
 
+// ---- transposed LDS reads (gfx950 ds_read_b64_tr_b16) ----------------------
+// Rows r0 .. r0+3 of column c0 + (lane % 16) of a row-major bf16 matrix in LDS
+// (row stride RS elements; r0 uniform within each group of 16 lanes, c0 a
+// multiple of 16, 8-byte aligned addresses).  In one ds_read_b64_tr_b16, lane j
+// of a 16-lane group supplies the address of 4 elements (8 bytes) and lane i
+// receives element i % 4 of the chunks of lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12,
+// in that order (layout checked on the device); so lane j points at row
+// r0 + j/4, columns c0 + 4 (j % 4) .. + 3, and lane i gets column c0 + i.
+template <int RS>
+__device__ __forceinline__ bf16x4 lds_col4(const bf16* base, int r0, int c0, int lane) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const int j = lane & 15;
+    const bf16* a = base + (r0 + (j >> 2)) * RS + c0 + 4 * (j & 3);
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)a);
+    return __builtin_bit_cast(bf16x4, r);
+}
+
 // ---- row L2 normalisation of staged rows ---------------------------------
 // A D-element row held as 16-byte pieces by D / (16 / sizeof(T)) consecutive
 // lanes (aligned groups inside one wave): each lane returns its piece times
