@@ -17,7 +17,7 @@ import os
 from typing import Optional, Sequence
 
 __all__ = ["chunk_fwd", "recurrent_step", "recurrent_step_fused", "conv1d_silu", "conv1d_silu_step",
-           "chunk_fwd_fused", "chunk_fwd_pooled", "conv1d_silu_pooled", "recurrent_step_fused_pooled", "conv1d_silu_step_pooled",
+           "chunk_fwd_fused", "chunk_fwd_dev", "chunk_fwd_pooled", "conv1d_silu_pooled", "recurrent_step_fused_pooled", "conv1d_silu_step_pooled",
            "state_rows_zero", "state_rows_copy", "workspace_layout", "workspace_size", "lib_path", "load_library",
            "GdnError", "CHUNK", "DTYPE_F32", "DTYPE_BF16"]
 
@@ -154,6 +154,11 @@ def load_library():
     lib.gdn_chunk_fwd_fused.argtypes = [P, P, P, ctypes.POINTER(FrontEnd), P, I32, P, P, P, SL, I32, I32, I32, I32,
                                         I32, F, ctypes.c_int, P, ctypes.c_size_t, P, P]
     lib.gdn_chunk_fwd_fused.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_dev_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, ctypes.c_int]
+    lib.gdn_chunk_fwd_dev_workspace_size.restype = ctypes.c_size_t
+    lib.gdn_chunk_fwd_dev.argtypes = [P, P, P, P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P,
+                                      ctypes.c_size_t, P, P]
+    lib.gdn_chunk_fwd_dev.restype = ctypes.c_int
     lib.gdn_state_rows_zero.argtypes = [P, I32, ctypes.c_size_t, P, I32, P]
     lib.gdn_state_rows_copy.argtypes = [P, I32, ctypes.c_size_t, P, P, I32, P]
     for fn in ("gdn_chunk_fwd_pooled", "gdn_conv1d_silu_fwd_pooled", "gdn_recurrent_step_fused_pooled",
@@ -552,6 +557,63 @@ def chunk_fwd_fused(q, k, v, a, b, A_log, dt_bias, cu_seqlens: Sequence[int], in
     if rc != 0:
         raise GdnError(rc, "gdn_chunk_fwd_fused")
     return out, final_state
+
+
+def chunk_fwd_dev(q, k, v, g, beta, cu_seqlens_dev, initial_state=None, scale: Optional[float] = None, out=None,
+                  final_state=None, output_final_state: bool = True, workspace=None, stream=None, gate=None):
+    """gdn_chunk_fwd with cu_seqlens in device memory (gdn_chunk_fwd_dev): the
+    call depends on T and the number of sequences only, so it can be captured
+    in a graph and replayed with new boundaries.  cu_seqlens_dev: device int32
+    [N+1].  Other arguments and results as chunk_fwd (workspace sized by
+    dev_workspace_size)."""
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("g", g, torch.float32)
+    _check_dev("beta", beta, torch.float32)
+    _check_dev("cu_seqlens_dev", cu_seqlens_dev, torch.int32)
+    T, H_q, d_k = q.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    if k.shape != q.shape or v.shape[0] != T or g.shape != (T, H_v) or beta.shape != (T, H_v) or \
+            cu_seqlens_dev.dim() != 1:
+        raise ValueError("inconsistent q/k/v/g/beta/cu_seqlens shapes")
+    N = cu_seqlens_dev.numel() - 1
+    if initial_state is not None:
+        _check_dev("initial_state", initial_state, torch.float32)
+        if tuple(initial_state.shape) != (N, H_v, d_k, d_v):
+            raise ValueError("initial_state must be [N, H_v, d_k, d_v]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    if out is None:
+        out = torch.empty((T, H_v, d_v), dtype=q.dtype, device=q.device)
+    else:
+        _check_dev("out", out, q.dtype)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H_v, d_k, d_v), dtype=torch.float32, device=q.device)
+    elif final_state is not None:
+        _check_dev("final_state", final_state, torch.float32)
+    if workspace is None:
+        workspace = torch.empty(max(dev_workspace_size(T, N, H_q, H_v, d_k, d_v, q.dtype), 1), dtype=torch.uint8,
+                                device=q.device)
+    else:
+        _check_dev("workspace", workspace)
+    gptr, _keep = _gate_arg(gate, q.dtype, T, H_v, d_v)
+    rc = lib.gdn_chunk_fwd_dev(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens_dev), N,
+                               _ptr(initial_state), _ptr(out), _ptr(final_state), T, H_q, H_v, d_k, d_v, float(scale),
+                               dt, _ptr(workspace), workspace.numel() * workspace.element_size(), gptr,
+                               _stream_ptr(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_chunk_fwd_dev")
+    return out, final_state
+
+
+def dev_workspace_size(T: int, num_seqs: int, H_q: int, H_v: int, d_k: int, d_v: int, dtype) -> int:
+    """Workspace bytes of chunk_fwd_dev (gdn_chunk_fwd_dev_workspace_size)."""
+    lib = load_library()
+    code = dtype if isinstance(dtype, int) else _dtype_code_from(dtype)
+    return lib.gdn_chunk_fwd_dev_workspace_size(T, num_seqs, H_q, H_v, d_k, d_v, code)
 
 
 def conv1d_silu_pooled(x, cu_seqlens: Sequence[int], weight, bias, state_pool, slots, has_initial=None, out=None,

@@ -148,6 +148,9 @@ hipError_t run_decode(const gdn::DecodeParams& p, gdn_dtype dt, int d, hipStream
                     : gdn::launch_recurrent_step<float, 64, FUSED>(p, s);
 }
 
+int layout_for_chunks(int64_t nc, int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype,
+                      gdn_workspace_layout* layout);
+
 int hip_fail(hipError_t e) {
     g_last_hip_error = hipGetErrorString(e);
     return GDN_ERR_HIP;
@@ -360,6 +363,16 @@ int gdn_chunk_fwd_workspace_layout(int32_t T, int32_t num_seqs, const int32_t* c
     int64_t nc = 0;
     rc = check_seqlens(T, num_seqs, cu_seqlens_host, &nc);
     if (rc != GDN_OK) return rc;
+    return layout_for_chunks(nc, H_v, d_k, d_v, dtype, layout);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Region offsets for n_chunks chunks (sizes are per chunk and value head).
+int layout_for_chunks(int64_t nc, int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype,
+                      gdn_workspace_layout* layout) {
     const size_t es = elem_size(dtype);
     const size_t C = GDN_CHUNK;
     const size_t chv = (size_t)nc * (size_t)H_v;
@@ -377,6 +390,30 @@ int gdn_chunk_fwd_workspace_layout(int32_t T, int32_t num_seqs, const int32_t* c
     *layout = L;
     return GDN_OK;
 }
+
+// Chunk-count bound for a device cu_seqlens: sum_i ceil(len_i / 64) <= T / 64 + num_seqs.
+int64_t chunk_bound(int32_t T, int32_t num_seqs) { return ((int64_t)T + GDN_CHUNK - 1) / GDN_CHUNK + num_seqs; }
+
+// Workspace of the device-table path: the regions for the chunk bound, then one
+// sequence table per launch group.
+int dev_layout(int32_t T, int32_t num_seqs, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype,
+               gdn_workspace_layout* L, size_t* tab_off, size_t* total) {
+    int rc = check_shapes(H_q, H_v, d_k, d_v, dtype);
+    if (rc != GDN_OK) return rc;
+    if (T < 0 || num_seqs < 0) return GDN_ERR_INVALID;
+    const int64_t nb = chunk_bound(T, num_seqs);
+    if (nb > (int64_t)INT32_MAX / 1024) return GDN_ERR_UNSUPPORTED;
+    rc = layout_for_chunks(nb, H_v, d_k, d_v, dtype, L);
+    if (rc != GDN_OK) return rc;
+    const int64_t groups = ((int64_t)num_seqs + gdn::MAX_SEQS_PER_LAUNCH - 1) / gdn::MAX_SEQS_PER_LAUNCH;
+    *tab_off = L->total_bytes;
+    *total = align_up(L->total_bytes + (size_t)groups * sizeof(gdn::SeqTable));
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
 
 size_t gdn_chunk_fwd_workspace_size(int32_t T, int32_t num_seqs, const int32_t* cu_seqlens_host, int32_t H_q,
                                     int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype) {
@@ -412,6 +449,66 @@ int gdn_chunk_fwd_pooled(const void* q, const void* k, const void* v, const floa
     if (!slots) return GDN_ERR_INVALID;
     return chunk_fwd_impl(q, k, v, g, beta, cu_seqlens_host, num_seqs, state_pool, out, state_pool, slots, T, H_q,
                           H_v, d_k, d_v, scale, dtype, workspace, workspace_bytes, stream, 0u, gate, nullptr);
+}
+
+size_t gdn_chunk_fwd_dev_workspace_size(int32_t T, int32_t num_seqs, int32_t H_q, int32_t H_v, int32_t d_k,
+                                        int32_t d_v, gdn_dtype dtype) {
+    gdn_workspace_layout L;
+    size_t tab_off = 0, total = 0;
+    if (dev_layout(T, num_seqs, H_q, H_v, d_k, d_v, dtype, &L, &tab_off, &total) != GDN_OK) return 0;
+    return total;
+}
+
+int gdn_chunk_fwd_dev(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                      const int32_t* cu_seqlens_dev, int32_t num_seqs, const float* initial_state, void* out,
+                      float* final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
+                      gdn_dtype dtype, void* workspace, size_t workspace_bytes, const gdn_output_gate* gate,
+                      void* stream) {
+    if (gate) {
+        const int grc = check_gate(gate, T > 0);
+        if (grc != GDN_OK) return grc;
+    }
+    gdn_workspace_layout L;
+    size_t tab_off = 0, total = 0;
+    int rc = dev_layout(T, num_seqs, H_q, H_v, d_k, d_v, dtype, &L, &tab_off, &total);
+    if (rc != GDN_OK) return rc;
+    if (num_seqs == 0 || T == 0) return GDN_OK;
+    if (!cu_seqlens_dev || !q || !k || !v || !g || !beta || !out) return GDN_ERR_INVALID;
+    const void* ptrs[] = {q, k, v, g, beta, out, initial_state, final_state, workspace};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(cu_seqlens_dev) & 3u) return GDN_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return GDN_ERR_INVALID;
+    if (!workspace || workspace_bytes < total) return GDN_ERR_WORKSPACE;
+
+    char* ws = static_cast<char*>(workspace);
+    gdn::SeqTable* tabs = reinterpret_cast<gdn::SeqTable*>(ws + tab_off);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = gdn::launch_build_tables(cu_seqlens_dev, num_seqs, T, initial_state != nullptr,
+                                            final_state != nullptr, tabs, s);
+    if (e != hipSuccess) return hip_fail(e);
+    gdn::ChunkParams p{};
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.s0 = initial_state; p.out = out; p.sfinal = final_state;
+    p.gc = reinterpret_cast<float*>(ws + L.off_gc);
+    p.A = ws + L.off_A; p.W = ws + L.off_W; p.Ut = ws + L.off_U; p.Kt = ws + L.off_Kd;
+    p.Ht = ws + L.off_Ht; p.Xt = ws + L.off_Xt;
+    p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
+    p.gz = gate ? gate->z : nullptr;
+    p.gw = gate ? gate->weight : nullptr;
+    p.geps = gate ? gate->eps : 0.f;
+    // Per launch group: the host table carries only the grid bounds (sequence
+    // count, a chunk-count bound); the kernels read the device table.
+    const int64_t nb = chunk_bound(T, num_seqs);
+    for (int32_t s0 = 0; s0 < num_seqs; s0 += gdn::MAX_SEQS_PER_LAUNCH) {
+        const int32_t ns = std::min<int32_t>(gdn::MAX_SEQS_PER_LAUNCH, num_seqs - s0);
+        p.tab.num_seqs = ns;
+        p.tab.n_chunks = (int32_t)std::min<int64_t>(nb, ((int64_t)T + GDN_CHUNK - 1) / GDN_CHUNK + ns);
+        p.dtab = tabs + s0 / gdn::MAX_SEQS_PER_LAUNCH;
+        e = run_chunk(p, dtype, d_k, s, nullptr);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return GDN_OK;
 }
 
 int gdn_chunk_fwd_fused(const void* q, const void* k, const void* v, const gdn_front_end* front,

@@ -19,6 +19,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "gdn_device.h"
 #include "gdn_params.h"
@@ -130,17 +131,22 @@ struct PrepLds {
     float gc[CHUNK], beta[CHUNK], sk[CHUNK], svb[CHUNK], kd[CHUNK];
 };
 
-template <typename T, int D>
+// DEV: the sequence table is read from device memory (p.dtab) instead of the
+// kernel arguments (same for the two kernels below).
+template <typename T, int D, bool DEV>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel(const ChunkParams p, int padded) {
     using PL = PrepLds<T, D>;
     constexpr int VEC = 16 / (int)sizeof(T);                  // elements per 16-byte access
     constexpr int NV = CHUNK * D / VEC / 256;                 // 16-byte pieces per thread
-    const int work = p.tab.n_chunks * p.H_v;
+    const SeqTable& tab = DEV ? *p.dtab : p.tab;
+    const int work = tab.n_chunks * p.H_v;
+    if constexpr (DEV) padded = (work + 7) & ~7;  // the grid was sized by a bound
     // Items (chunk, value head) of this workgroup: virtual indices blockIdx.x,
     // blockIdx.x + gridDim.x, ... mapped XCD-aware (gridDim.x is a multiple of 8,
     // so every item of a workgroup stays on its XCD).  The next item's K, V and
     // gate rows are loaded into registers while this item's W, U and Kd are formed.
     int v = blockIdx.x;
+    if (v >= padded) return;
     int wid = xcd_remap(v, padded);
     if (wid >= work) return;  // padding items come last, so all later ones are padding too
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -158,7 +164,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
     float graw = 0.f, braw = 0.f;
     auto load_k = [&](int it) {
         const int hh = it % p.H_v;
-        const ChunkPos c = locate_chunk(p.tab, p.tab.chunk_begin + it / p.H_v);
+        const ChunkPos c = locate_chunk(tab, tab.chunk_begin + it / p.H_v);
         const T* kb = reinterpret_cast<const T*>(p.k) + (size_t)c.t0 * p.H_q * D + (size_t)(hh / p.G) * D;
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
@@ -188,7 +194,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, grp = lane >> 4;
     const int h = wid % p.H_v;
-    const ChunkPos cp = locate_chunk(p.tab, p.tab.chunk_begin + wid / p.H_v);
+    const ChunkPos cp = locate_chunk(tab, tab.chunk_begin + wid / p.H_v);
     const int ell = cp.ell;
     const size_t ch = (size_t)cp.ci * p.H_v + h;
 
@@ -620,7 +626,7 @@ __device__ __forceinline__ void lds_put4(Frag<T>& f, int half, const f32x4& v, f
     }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool DEV>
 __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p, int padded) {
     using SS = StateStage<T, D>;
     constexpr int NT = D / 16;   // column tiles of d_v per head
@@ -634,18 +640,19 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
     (void)padded;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int gi = (slot / NT) * 8 + xcd;
-    if (gi >= p.tab.num_seqs * p.H_v) return;
+    const SeqTable& tab = DEV ? *p.dtab : p.tab;
+    if (gi >= tab.num_seqs * p.H_v) return;
     const int tile = slot % NT;
-    const int h = gi % p.H_v, n = p.tab.order[gi / p.H_v];
+    const int h = gi % p.H_v, n = tab.order[gi / p.H_v];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
     const int col = 16 * tile + r16;
-    const int si = p.tab.s_in[n], so = p.tab.s_out[n];  // state rows (-1: zeros / not kept)
+    const int si = tab.s_in[n], so = tab.s_out[n];  // state rows (-1: zeros / not kept)
     const size_t in_off = ((size_t)max(si, 0) * p.H_v + h) * D * D;
     const size_t out_off = ((size_t)max(so, 0) * p.H_v + h) * D * D;
-    const int L_n = p.tab.cu[n + 1] - p.tab.cu[n];
-    const int nch = p.tab.choff[n + 1] - p.tab.choff[n];
-    const int c0 = p.tab.choff[n];
+    const int L_n = tab.cu[n + 1] - tab.cu[n];
+    const int nch = tab.choff[n + 1] - tab.choff[n];
+    const int c0 = tab.choff[n];
 
     __shared__ __attribute__((aligned(16))) char smem[NST * SS::BYTES + SS::EXCH + 256];  // + L2-prefetch sink
     Frag<T>(*LS)[64] = reinterpret_cast<Frag<T>(*)[64]>(smem + NST * SS::BYTES);           // [KS][64]: -S
@@ -866,17 +873,21 @@ struct OutLds {
     float gc[CHUNK];
 };
 
-template <typename T, int D, bool GATED>
+template <typename T, int D, bool GATED, bool DEV>
 __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p, int padded) {
     using OL = OutLds<T, D>;
     constexpr int KS = D / 32;
     constexpr int TPW = D / 64;
     constexpr int VEC = 16 / (int)sizeof(T);
     constexpr int NV = CHUNK * D / VEC / 256;
+    const SeqTable& tab = DEV ? *p.dtab : p.tab;
+    const int work = tab.n_chunks * p.H_v;
+    if constexpr (DEV) padded = (work + 7) & ~7;  // the grid was sized by a bound
+    if ((int)blockIdx.x >= padded) return;
     const int wid = xcd_remap(blockIdx.x, padded);
-    if (wid >= p.tab.n_chunks * p.H_v) return;
+    if (wid >= work) return;
     const int h = wid % p.H_v;
-    const ChunkPos cp = locate_chunk(p.tab, p.tab.chunk_begin + wid / p.H_v);
+    const ChunkPos cp = locate_chunk(tab, tab.chunk_begin + wid / p.H_v);
     const int hq = h / p.G;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
@@ -1043,6 +1054,72 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
 }
 
 // ---------------------------------------------------------------------------
+// Sequence tables from a device-resident cu_seqlens (one wave).  Per group of
+// up to 64 sequences: sequence ends clamped to [0, T] and made non-decreasing
+// (a running maximum, so every length is >= 0 and every index stays inside the
+// buffers whatever the input holds), chunk offsets by a prefix sum over the
+// lanes, state rows, and the longest-first order the state scan dispatches by.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void build_tables_kernel(const int32_t* __restrict__ cu, int num_seqs, int T,
+                                                         int has_in, int has_out, SeqTable* tabs) {
+    const int lane = threadIdx.x;
+    int chunk_base = 0, prev_end = 0;
+    for (int s0 = 0; s0 < num_seqs; s0 += MAX_SEQS_PER_LAUNCH) {
+        const int ns = min(MAX_SEQS_PER_LAUNCH, num_seqs - s0);
+        SeqTable* tb = tabs + s0 / MAX_SEQS_PER_LAUNCH;
+        int end = lane < ns ? min(max(cu[s0 + lane + 1], 0), T) : 0;
+        end = max(end, prev_end);
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {  // inclusive running maximum
+            const int o = __shfl_up(end, off, 64);
+            if (lane >= off) end = max(end, o);
+        }
+        const int up = __shfl_up(end, 1, 64);
+        const int start = lane == 0 ? prev_end : up;
+        const int len = lane < ns ? end - start : 0;
+        const int nc = (len + CHUNK - 1) / CHUNK;
+        int incl = nc;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {  // inclusive prefix sum of chunk counts
+            const int o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
+        }
+        const int total = __shfl(incl, ns - 1, 64);
+        const int last_end = __shfl(end, ns - 1, 64);
+        int rank = 0;  // stable, longest first
+        for (int j = 0; j < ns; ++j) {
+            const int ncj = __shfl(nc, j, 64);
+            rank += (ncj > nc || (ncj == nc && j < lane)) ? 1 : 0;
+        }
+        if (lane < ns) {
+            tb->cu[lane] = start;
+            tb->choff[lane] = chunk_base + incl - nc;
+            tb->s_in[lane] = has_in ? s0 + lane : -1;
+            tb->s_out[lane] = has_out ? s0 + lane : -1;
+            tb->order[rank] = lane;
+        }
+        if (lane == 0) {
+            tb->cu[ns] = last_end;
+            tb->choff[ns] = chunk_base + total;
+            tb->num_seqs = ns;
+            tb->seq_base = s0;
+            tb->chunk_begin = chunk_base;
+            tb->n_chunks = total;
+        }
+        chunk_base += total;
+        prev_end = last_end;
+    }
+}
+
+hipError_t launch_build_tables(const int32_t* cu_dev, int num_seqs, int T, int has_in, int has_out, SeqTable* tabs,
+                               hipStream_t stream) {
+    if (num_seqs > 0)
+        hipLaunchKernelGGL(build_tables_kernel, dim3(1), dim3(64), 0, stream, cu_dev, num_seqs, T, has_in, has_out,
+                           tabs);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Pipeline launcher: the four stages in stream order.
 // ---------------------------------------------------------------------------
 static inline int pad8(int x) { return (x + 7) & ~7; }
@@ -1085,14 +1162,22 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
     // chunk_prep runs as many workgroups as fit on the chip at once (four per CU)
     // and loops over the rest, prefetching each next item.
     const int prep_slots = 4 * cu_count();
-    if (work_ch > 0) launch(0, chunk_prep_kernel<T, D>, std::min(grid_ch, prep_slots), 256, grid_ch, pl);
-    if (work_st > 0) launch(1, chunk_state_h_kernel<T, D>, grid_st, 64 * (5 + StateStage<T, D>::NPW), grid_st, pl);
-    if (work_ch > 0) {
-        if (p.gz)
-            launch(2, chunk_output_o_kernel<T, D, true>, grid_ch, 256, grid_ch, pl);
-        else
-            launch(2, chunk_output_o_kernel<T, D, false>, grid_ch, 256, grid_ch, pl);
-    }
+    auto run = [&](auto dev) {
+        constexpr bool DEV = decltype(dev)::value;
+        if (work_ch > 0) launch(0, chunk_prep_kernel<T, D, DEV>, std::min(grid_ch, prep_slots), 256, grid_ch, pl);
+        if (work_st > 0)
+            launch(1, chunk_state_h_kernel<T, D, DEV>, grid_st, 64 * (5 + StateStage<T, D>::NPW), grid_st, pl);
+        if (work_ch > 0) {
+            if (p.gz)
+                launch(2, chunk_output_o_kernel<T, D, true, DEV>, grid_ch, 256, grid_ch, pl);
+            else
+                launch(2, chunk_output_o_kernel<T, D, false, DEV>, grid_ch, 256, grid_ch, pl);
+        }
+    };
+    if (p.dtab)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
     return hipGetLastError();
 }
 

@@ -59,6 +59,10 @@ struct ChunkParams {
     const float* A_log;
     const float* dt_bias;
     SeqTable tab;
+    // Device-resident copy of the table (built from a device cu_seqlens by
+    // build_tables_kernel); when set, the kernels read it instead of tab, and
+    // tab.num_seqs / tab.n_chunks only bound the grids.
+    const SeqTable* dtab;
 };
 
 struct DecodeParams {
@@ -119,6 +123,12 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
 
 template <typename T, int D, bool FUSED>
 hipError_t launch_recurrent_step(const DecodeParams& p, hipStream_t stream);
+
+// Sequence tables from a device cu_seqlens (gdn_chunk.hip): one SeqTable per
+// group of up to MAX_SEQS_PER_LAUNCH sequences, boundaries clamped to [0, T]
+// and made non-decreasing so that no kernel can index out of bounds.
+hipError_t launch_build_tables(const int32_t* cu_dev, int num_seqs, int T, int has_in, int has_out, SeqTable* tabs,
+                               hipStream_t stream);
 
 template <typename T, int K>
 hipError_t launch_conv_prefill(const ConvParams& p, hipStream_t stream);

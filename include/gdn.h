@@ -182,6 +182,33 @@ int gdn_chunk_fwd_ex(const void *q, const void *k, const void *v, const float *g
                      const gdn_output_gate *gate, void *const *stage_events);
 
 /*
+ * gdn_chunk_fwd with cu_seqlens in DEVICE memory, for callers that capture the
+ * prefill in a graph and replay it with new sequence boundaries (the trace
+ * page's serving path keeps its sequence offsets on the device).  A small
+ * kernel builds the per-launch sequence tables in the workspace from
+ * cu_seqlens_dev; the grids are sized from T and num_seqs alone, so nothing in
+ * the call depends on the boundaries' values.
+ *   cu_seqlens_dev  DEVICE int32 [num_seqs + 1], 4-byte aligned, read by the
+ *           kernels on the stream.  It should satisfy gdn_chunk_fwd's rules
+ *           (0 = c[0] <= ... <= c[num_seqs] = T); it cannot be checked on the
+ *           host.  Values that break them are clamped into [0, T] and made
+ *           non-decreasing before use (no access leaves the buffers), with
+ *           unspecified results; tokens past the last boundary are not written.
+ *   workspace  >= gdn_chunk_fwd_dev_workspace_size(T, num_seqs, ...) bytes (the
+ *           intermediates for the chunk-count bound T/64 + num_seqs, then the
+ *           tables).
+ *   gate    NULL, or the read-out epilogue (gdn_output_gate).
+ * Other arguments and errors as gdn_chunk_fwd.
+ */
+size_t gdn_chunk_fwd_dev_workspace_size(int32_t T, int32_t num_seqs, int32_t H_q, int32_t H_v, int32_t d_k,
+                                        int32_t d_v, gdn_dtype dtype);
+int gdn_chunk_fwd_dev(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                      const int32_t *cu_seqlens_dev, int32_t num_seqs, const float *initial_state, void *out,
+                      float *final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
+                      gdn_dtype dtype, void *workspace, size_t workspace_bytes, const gdn_output_gate *gate,
+                      void *stream);
+
+/*
  * One recurrent decode step ("Qwen3.5-397B-A17B" trace page, Decode-GDN node 7,
  * gdn_packed_recurrent_qk_norm_gating_state_update — its decay, delta update and
  * read; the Q/K normalisation and gate transform of that node are not part of

@@ -329,6 +329,30 @@ def test_fused_prefill_rejects_before_any_device_work(gdn):
     assert call(fe, N=0, T=0, cu=_cu([0])) == 0
 
 
+def test_dev_seqlens_prefill_rejects_before_any_device_work(gdn):
+    lib = gdn.load_library()
+    keep, p = _fake()
+    assert lib.gdn_chunk_fwd_dev_workspace_size(4096, 1, 16, 32, 128, 128, 1) > \
+        lib.gdn_chunk_fwd_workspace_size(4096, 1, _cu([0, 4096]), 16, 32, 128, 128, 1)
+    assert lib.gdn_chunk_fwd_dev_workspace_size(100, 1, 3, 4, 64, 64, 1) == 0     # H_v % H_q != 0
+
+    def call(**kw):
+        a = dict(q=p, k=p, v=p, g=p, beta=p, cu=p, N=2, s0=None, out=p, fin=None, T=100, H_q=2, H_v=4, dk=64, dv=64,
+                 scale=0.1, dt=1, ws=p, wsb=1 << 40)
+        a.update(kw)
+        return lib.gdn_chunk_fwd_dev(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"], a["s0"], a["out"],
+                                     a["fin"], a["T"], a["H_q"], a["H_v"], a["dk"], a["dv"], a["scale"], a["dt"],
+                                     a["ws"], a["wsb"], None, None)
+
+    assert call(cu=None) == -1
+    assert call(cu=p + 2) == -2               # int32 boundaries off their alignment
+    assert call(g=None) == -1
+    assert call(dk=32, dv=32) == -2
+    assert call(wsb=1024) == -3
+    assert call(N=-1) == -1
+    assert call(T=0) == 0 and call(N=0) == 0
+
+
 def test_binding_refuses_host_tensors(gdn):
     torch = pytest.importorskip("torch")
     q = torch.zeros(4, 2, 64)
