@@ -896,18 +896,6 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
 
     __shared__ __attribute__((aligned(16))) OL s;
 
-    // This wave's operand fragments of H^T and (U - W S)^T (rows d_v), straight to registers.
-    const T* Hb = reinterpret_cast<const T*>(p.Ht) + ch * D * D;
-    const T* Xb = reinterpret_cast<const T*>(p.Xt) + ch * D * CHUNK;
-    Frag<T> hf[TPW][KS], xf[TPW][2];
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-        const int dv = 16 * (w * TPW + tt) + r16;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) load8(hf[tt][ks], Hb + (size_t)dv * D + 32 * ks + 8 * grp);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) load8(xf[tt][ks], Xb + (size_t)dv * CHUNK + 32 * ks + 8 * grp);
-    }
     // Q and K rows into LDS (zeros past the valid length), gates.
     const T* qb = reinterpret_cast<const T*>(p.q) + (size_t)cp.t0 * p.H_q * D + (size_t)hq * D;
     const T* kb = reinterpret_cast<const T*>(p.k) + (size_t)cp.t0 * p.H_q * D + (size_t)hq * D;
@@ -928,6 +916,20 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
     }
     if (tid < CHUNK) s.gc[tid] = p.gc[ch * CHUNK + tid];
     lds_sync();
+    // This wave's operand fragments of H^T and (U - W S)^T (rows d_v), straight to
+    // registers; issued after the Q/K staging (needed first, by the P tiles), so
+    // they land while the P tiles are formed (36.6 -> 35 us at T = 4096).
+    const T* Hb = reinterpret_cast<const T*>(p.Ht) + ch * D * D;
+    const T* Xb = reinterpret_cast<const T*>(p.Xt) + ch * D * CHUNK;
+    Frag<T> hf[TPW][KS], xf[TPW][2];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+        const int dv = 16 * (w * TPW + tt) + r16;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) load8(hf[tt][ks], Hb + (size_t)dv * D + 32 * ks + 8 * grp);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) load8(xf[tt][ks], Xb + (size_t)dv * CHUNK + 32 * ks + 8 * grp);
+    }
     // Gated read-out: this lane's z values of one position tile (rows past the
     // valid length re-read the last valid row; they are never stored) and the
     // norm weights.  Tile 0's z goes out after the Q/K staging (so those loads are
