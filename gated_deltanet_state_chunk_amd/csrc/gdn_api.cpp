@@ -472,8 +472,10 @@ int gdn_chunk_fwd_dev(const void* q, const void* k, const void* v, const float* 
     size_t tab_off = 0, total = 0;
     int rc = dev_layout(T, num_seqs, H_q, H_v, d_k, d_v, dtype, &L, &tab_off, &total);
     if (rc != GDN_OK) return rc;
-    if (num_seqs == 0 || T == 0) return GDN_OK;
-    if (!cu_seqlens_dev || !q || !k || !v || !g || !beta || !out) return GDN_ERR_INVALID;
+    if (num_seqs == 0) return GDN_OK;
+    // T == 0 still runs: every sequence is empty and its final state is its
+    // initial state (or zero), as in gdn_chunk_fwd.
+    if (!cu_seqlens_dev || (T > 0 && (!q || !k || !v || !g || !beta || !out))) return GDN_ERR_INVALID;
     const void* ptrs[] = {q, k, v, g, beta, out, initial_state, final_state, workspace};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return GDN_ERR_UNSUPPORTED;

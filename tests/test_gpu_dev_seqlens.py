@@ -87,3 +87,26 @@ def test_dev_seqlens_graph_replay_with_new_boundaries(torch_cuda):
         torch.cuda.synchronize()
         assert torch.equal(out, ref_o), cu
         assert torch.equal(fin, ref_f), cu
+
+
+@pytest.mark.parametrize("with_initial", [True, False])
+def test_dev_seqlens_all_sequences_empty(torch_cuda, with_initial):
+    """T = 0 with three (empty) sequences: every final state is the initial
+    state (zero without one), as on the host-boundary path."""
+    import gated_deltanet_state_chunk_amd as gdn
+
+    torch = torch_cuda
+    N, H_q, H_v, d = 3, 2, 4, 128
+    q = torch.empty((0, H_q, d), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty((0, H_v, d), dtype=torch.bfloat16, device="cuda")
+    g = torch.empty((0, H_v), dtype=torch.float32, device="cuda")
+    s0 = f32_dev(gdn_inputs.make_decode_state(85, N, H_v, d, d)) if with_initial else None
+    cu_dev = torch.zeros(N + 1, dtype=torch.int32, device="cuda")
+    fin = torch.full((N, H_v, d, d), float("nan"), dtype=torch.float32, device="cuda")
+    out_d, fin_d = gdn.chunk_fwd_dev(q, q, v, g, g, cu_dev, initial_state=s0, final_state=fin)
+    out_h, fin_h = gdn.chunk_fwd(q, q, v, g, g, [0] * (N + 1), initial_state=s0)
+    torch.cuda.synchronize()
+    assert out_d.shape == (0, H_v, d)
+    ref = s0 if with_initial else torch.zeros_like(fin)
+    assert torch.equal(fin_d, ref)
+    assert torch.equal(fin_h, ref)
