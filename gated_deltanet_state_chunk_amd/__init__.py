@@ -194,6 +194,9 @@ def _ptr(t) -> Optional[int]:
 def _check_dev(name, t, dtype=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    # the library launches on the calling thread's current device
+    if t.device.index != _torch().cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, not on the current device")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
