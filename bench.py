@@ -64,19 +64,21 @@ def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True, gated=False):
     v_b = o_b = T * H_v * d * es
     gate_b = T * H_v * 4  # g or beta
     gc_b = chv * C * 4
-    W_b = U_b = X_b = Kd_b = chv * C * d * es
+    W_b = U_b = X_b = chv * C * d * es
+    kf_b = chv * C * 4      # per-position factor of the state update's keys
+    Kc_b = chq * C * d * es  # the state update's copy of the keys, one per key head
     H_b = chv * d * d * es
     S_b = N * H_v * d * d * 4
     tri = C * (C - 1) // 2   # strictly lower entries
     tri1 = C * (C + 1) // 2  # lower incl. diagonal
     per = {  # multiply-adds per (chunk, value head)
         "chunk_prep": tri * d + C ** 3 // 6 + 2 * tri1 * d,   # K K^T, solve, W, U
-        "chunk_state_h": 2 * C * d * d,                      # W S, Kd^T X
+        "chunk_state_h": 2 * C * d * d,                      # W S, Kc^T (kf X)
         "chunk_output_o": C * d * d + 2 * tri1 * d,          # Q S, Q K^T, P X
     }
     bytes_ = {
-        "chunk_prep": k_b + v_b + 2 * gate_b + gc_b + W_b + U_b + Kd_b,   # A stays on chip
-        "chunk_state_h": W_b + U_b + Kd_b + gc_b + (S_b if has_s0 else 0) + H_b + X_b + S_b,
+        "chunk_prep": k_b + v_b + 2 * gate_b + gc_b + W_b + U_b + kf_b + Kc_b,   # A stays on chip
+        "chunk_state_h": W_b + U_b + Kc_b + kf_b + gc_b + (S_b if has_s0 else 0) + H_b + X_b + S_b,
         "chunk_output_o": q_b + k_b + gc_b + H_b + X_b + o_b + ((o_b + d * 4) if gated else 0),  # z, weight
     }
     flops = {k: 2 * v * chv for k, v in per.items()}
@@ -181,7 +183,8 @@ def bench_prefill(args, torch, gdn, hip, device, gated=False):
     g, beta = _dev(inp.g, "f32", torch, device), _dev(inp.beta, "f32", torch, device)
     s0 = _dev(inp.initial_state, "f32", torch, device) if inp.initial_state is not None else None
     lay = gdn.workspace_layout(inp.T, inp.cu_seqlens, inp.H_q, inp.H_v, inp.d_k, inp.d_v, dt)
-    ws = torch.empty(lay["total_bytes"], dtype=torch.uint8, device=device)
+    ws_bytes = gdn.workspace_size(inp.T, inp.cu_seqlens, inp.H_q, inp.H_v, inp.d_k, inp.d_v, dt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
     out = torch.empty((inp.T, inp.H_v, inp.d_v), dtype=q.dtype, device=device)
     fin = torch.empty((inp.N, inp.H_v, inp.d_k, inp.d_v), dtype=torch.float32, device=device)
     lib = gdn.load_library()
@@ -207,14 +210,14 @@ def bench_prefill(args, torch, gdn, hip, device, gated=False):
             rc = lib.gdn_chunk_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), cu,
                                    inp.N, None if s0 is None else s0.data_ptr(), out.data_ptr(), fin.data_ptr(),
                                    inp.T, inp.H_q, inp.H_v, inp.d_k, inp.d_v, inp.scale, code, ws.data_ptr(),
-                                   lay["total_bytes"], ctypes.c_void_p(sptr))
+                                   ws_bytes, ctypes.c_void_p(sptr))
             if rc != 0:
                 raise gdn.GdnError(rc, "gdn_chunk_fwd")
             return
         rc = lib.gdn_chunk_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), cu,
                                   inp.N, None if s0 is None else s0.data_ptr(), out.data_ptr(), fin.data_ptr(),
                                   inp.T, inp.H_q, inp.H_v, inp.d_k, inp.d_v, inp.scale, code, ws.data_ptr(),
-                                  lay["total_bytes"], ctypes.c_void_p(sptr), 0, gate_ref, arr)
+                                  ws_bytes, ctypes.c_void_p(sptr), 0, gate_ref, arr)
         if rc != 0:
             raise gdn.GdnError(rc, "gdn_chunk_fwd_ex")
 

@@ -44,8 +44,9 @@ class GdnError(RuntimeError):
 
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [("n_chunks", ctypes.c_int64), ("off_gc", ctypes.c_size_t), ("off_A", ctypes.c_size_t),
-                ("off_W", ctypes.c_size_t), ("off_U", ctypes.c_size_t), ("off_Kd", ctypes.c_size_t),
-                ("off_Ht", ctypes.c_size_t), ("off_Xt", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t)]
+                ("off_W", ctypes.c_size_t), ("off_U", ctypes.c_size_t), ("off_kf", ctypes.c_size_t),
+                ("off_Kc", ctypes.c_size_t), ("off_Ht", ctypes.c_size_t), ("off_Xt", ctypes.c_size_t),
+                ("total_bytes", ctypes.c_size_t)]
 
 
 class OutputGate(ctypes.Structure):
@@ -242,7 +243,11 @@ def _dtype_code_from(dtype) -> int:
 
 
 def workspace_size(T: int, cu_seqlens, H_q: int, H_v: int, d_k: int, d_v: int, dtype) -> int:
-    return workspace_layout(T, cu_seqlens, H_q, H_v, d_k, d_v, dtype)["total_bytes"]
+    """Workspace bytes of chunk_fwd (gdn_chunk_fwd_workspace_size); raises on invalid arguments."""
+    workspace_layout(T, cu_seqlens, H_q, H_v, d_k, d_v, dtype)  # validates
+    code = dtype if isinstance(dtype, int) else _dtype_code_from(dtype)
+    return load_library().gdn_chunk_fwd_workspace_size(T, len(cu_seqlens) - 1, _host_cu(cu_seqlens), H_q, H_v, d_k,
+                                                       d_v, code)
 
 
 # ---------------------------------------------------------------------------

@@ -148,7 +148,7 @@ hipError_t run_decode(const gdn::DecodeParams& p, gdn_dtype dt, int d, hipStream
                     : gdn::launch_recurrent_step<float, 64, FUSED>(p, s);
 }
 
-int layout_for_chunks(int64_t nc, int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype,
+int layout_for_chunks(int64_t nc, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype,
                       gdn_workspace_layout* layout);
 
 int hip_fail(hipError_t e) {
@@ -244,7 +244,8 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, 
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
     p.s0 = initial_state; p.out = out; p.sfinal = final_state;
     p.gc = reinterpret_cast<float*>(ws + L.off_gc);
-    p.A = ws + L.off_A; p.W = ws + L.off_W; p.Ut = ws + L.off_U; p.Kt = ws + L.off_Kd;
+    p.A = ws + L.off_A; p.W = ws + L.off_W; p.Ut = ws + L.off_U;
+    p.kf = reinterpret_cast<float*>(ws + L.off_kf); p.Kc = ws + L.off_Kc;
     p.Ht = ws + L.off_Ht; p.Xt = ws + L.off_Xt;
     p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
     p.keep_A = (flags & GDN_FWD_KEEP_A) ? 1 : 0;
@@ -363,7 +364,7 @@ int gdn_chunk_fwd_workspace_layout(int32_t T, int32_t num_seqs, const int32_t* c
     int64_t nc = 0;
     rc = check_seqlens(T, num_seqs, cu_seqlens_host, &nc);
     if (rc != GDN_OK) return rc;
-    return layout_for_chunks(nc, H_v, d_k, d_v, dtype, layout);
+    return layout_for_chunks(nc, H_q, H_v, d_k, d_v, dtype, layout);
 }
 
 }  // extern "C"
@@ -371,11 +372,12 @@ int gdn_chunk_fwd_workspace_layout(int32_t T, int32_t num_seqs, const int32_t* c
 namespace {
 
 // Region offsets for n_chunks chunks (sizes are per chunk and value head).
-int layout_for_chunks(int64_t nc, int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype,
+int layout_for_chunks(int64_t nc, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype,
                       gdn_workspace_layout* layout) {
     const size_t es = elem_size(dtype);
     const size_t C = GDN_CHUNK;
     const size_t chv = (size_t)nc * (size_t)H_v;
+    const size_t chq = (size_t)nc * (size_t)H_q;
     size_t off = 0;
     gdn_workspace_layout L;
     L.n_chunks = nc;
@@ -383,7 +385,8 @@ int layout_for_chunks(int64_t nc, int32_t H_v, int32_t d_k, int32_t d_v, gdn_dty
     L.off_A = off;  off = align_up(off + chv * C * C * es);
     L.off_W = off;  off = align_up(off + chv * C * (size_t)d_k * es);
     L.off_U = off; off = align_up(off + chv * (size_t)d_v * C * es);
-    L.off_Kd = off; off = align_up(off + chv * (size_t)d_k * C * es);
+    L.off_kf = off; off = align_up(off + chv * C * sizeof(float));
+    L.off_Kc = off; off = align_up(off + chq * C * (size_t)d_k * es);
     L.off_Ht = off; off = align_up(off + chv * (size_t)d_v * (size_t)d_k * es);
     L.off_Xt = off; off = align_up(off + chv * (size_t)d_v * C * es);
     L.total_bytes = off;
@@ -403,7 +406,7 @@ int dev_layout(int32_t T, int32_t num_seqs, int32_t H_q, int32_t H_v, int32_t d_
     if (T < 0 || num_seqs < 0) return GDN_ERR_INVALID;
     const int64_t nb = chunk_bound(T, num_seqs);
     if (nb > (int64_t)INT32_MAX / 1024) return GDN_ERR_UNSUPPORTED;
-    rc = layout_for_chunks(nb, H_v, d_k, d_v, dtype, L);
+    rc = layout_for_chunks(nb, H_q, H_v, d_k, d_v, dtype, L);
     if (rc != GDN_OK) return rc;
     const int64_t groups = ((int64_t)num_seqs + gdn::MAX_SEQS_PER_LAUNCH - 1) / gdn::MAX_SEQS_PER_LAUNCH;
     *tab_off = L->total_bytes;
@@ -493,7 +496,8 @@ int gdn_chunk_fwd_dev(const void* q, const void* k, const void* v, const float* 
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
     p.s0 = initial_state; p.out = out; p.sfinal = final_state;
     p.gc = reinterpret_cast<float*>(ws + L.off_gc);
-    p.A = ws + L.off_A; p.W = ws + L.off_W; p.Ut = ws + L.off_U; p.Kt = ws + L.off_Kd;
+    p.A = ws + L.off_A; p.W = ws + L.off_W; p.Ut = ws + L.off_U;
+    p.kf = reinterpret_cast<float*>(ws + L.off_kf); p.Kc = ws + L.off_Kc;
     p.Ht = ws + L.off_Ht; p.Xt = ws + L.off_Xt;
     p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
     p.gz = gate ? gate->z : nullptr;

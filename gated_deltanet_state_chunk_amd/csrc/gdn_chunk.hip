@@ -85,29 +85,39 @@ template <int D>
 __host__ __device__ __forceinline__ int frag_w_offset(int pos_tile, int ks, int lane) {
     return ((pos_tile * (D / 32) + ks) * 64 + lane) * 8;
 }
-//   Kd^T (rows d_k, contraction pos): element (dk, pos) with pos a multiple of 4
-__host__ __device__ __forceinline__ int frag_k_offset(int dk, int pos4) {
-    const int m = dk >> 4, r = dk & 15, ks = pos4 >> 5, h = (pos4 >> 4) & 1, a = (pos4 >> 2) & 3;
-    return ((m * 2 + ks) * 64 + 16 * a + r) * 8 + 4 * h;
-}
 //   U (accumulator order): column tile of d_v, pair of row tiles of pos, lane ->
 //   8 values, the 4 rows of the even tile then the 4 of the odd one
 __host__ __device__ __forceinline__ int frag_u_offset(int col_tile, int pos_pair, int lane) {
     return ((col_tile * 2 + pos_pair) * 64 + lane) * 8;
 }
 
+// Permutation of the 16-byte pieces of K row `row` in Kc and in a state-scan
+// stage: piece i is stored at i ^ kswz(row), so that the column reads of the
+// state update hit distinct LDS banks.  bf16: the 32-byte window of 16
+// columns that one transposed read covers moves with row % (pieces / 2);
+// fp32: the 64-byte window moves with (row / 4) % (pieces / 4), the rows 4
+// apart that one scalar column read touches.
+template <typename T, int D>
+__host__ __device__ constexpr int kswz(int row) {
+    constexpr int CPR = D * (int)sizeof(T) / 16;
+    return sizeof(T) == 2 ? (row & (CPR / 2 - 1)) * 2 : ((row >> 2) & (CPR / 4 - 1)) * 4;
+}
+
+
 // ---------------------------------------------------------------------------
 // 1. chunk_prep: one workgroup (4 waves) per (chunk, value head); the first two
 //    stages of the chunk form in one pass over the chunk's keys and values:
 //      gc = in-chunk inclusive cumsum of g          ("输入输出定义")
 //      L  = StrictLower(B Gamma K K^T Gamma^-1),  A = (I + L)^-1   (fp32)
-//      W  = A B Gamma K,  U = A B V,  Kd = diag(gamma_l / gamma) K
-//    K is staged in LDS once and serves K K^T, W and Kd; V is prefetched into
-//    registers and staged after the solve (in the space L occupied).  gc is
-//    written to the workspace, and A too when the caller asks for it (it is
-//    for inspection only: nothing downstream reads it); W, U and Kd are
+//      W  = A B Gamma K,  U = A B V,  kf = gamma_l / gamma  (per position)
+//    K is staged in LDS once and serves K K^T and W; V is prefetched into
+//    registers and staged after the solve (in the space L occupied).  gc and
+//    kf are written to the workspace, and A too when the caller asks for it
+//    (it is for inspection only: nothing downstream reads it); W and U are
 //    written in the fragment order chunk_state_h streams into LDS
-//    (frag_w_offset / frag_u_offset / frag_k_offset).
+//    (frag_w_offset / frag_u_offset).  The state update's keys are not
+//    written: chunk_state_h reads K itself and applies kf to X instead
+//    (Diag(kf) K)^T X = K^T (Diag(kf) X).
 // ---------------------------------------------------------------------------
 // Lower-triangular 64x64 fp32 matrices are kept as their ten 16x16 blocks
 // (I >= J), block (I, J) at index I (I + 1) / 2 + J, rows padded to BS floats.
@@ -144,7 +154,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
     // Items (chunk, value head) of this workgroup: virtual indices blockIdx.x,
     // blockIdx.x + gridDim.x, ... mapped XCD-aware (gridDim.x is a multiple of 8,
     // so every item of a workgroup stays on its XCD).  The next item's K, V and
-    // gate rows are loaded into registers while this item's W, U and Kd are formed.
+    // gate rows are loaded into registers while this item's W and U are formed.
     int v = blockIdx.x;
     if (v >= padded) return;
     int wid = xcd_remap(v, padded);
@@ -209,11 +219,17 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
         }
     }
     // With the front end, each K row is L2-normalised on the way (rows past the
-    // valid length are zero and stay zero).
+    // valid length are zero and stay zero).  The first value head of each key
+    // head also writes the rows to Kc, the state scan's copy of the chunk's keys
+    // (contiguous, 16-byte pieces in the stage order of kswz).
+    const bool write_kc = h % p.G == 0;
+    T* Kcb = reinterpret_cast<T*>(p.Kc) + ((size_t)cp.ci * p.H_q + h / p.G) * CHUNK * D;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
-        *reinterpret_cast<float4*>(&s.K[r][c]) = p.fa ? l2norm_piece<T, D>(kreg[j]) : kreg[j];
+        const float4 kv = p.fa ? l2norm_piece<T, D>(kreg[j]) : kreg[j];
+        *reinterpret_cast<float4*>(&s.K[r][c]) = kv;
+        if (write_kc) *reinterpret_cast<float4*>(Kcb + r * D + VEC * ((c / VEC) ^ kswz<T, D>(r))) = kv;
     }
     // In-chunk inclusive cumsum of the log gate (front end: g and beta from the
     // raw inputs first).
@@ -355,7 +371,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
         const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
         *reinterpret_cast<float4*>(&s.u.V[r][c]) = vreg[j];
     }
-    // The next item's K and gate loads go out now; they land while W, U and Kd are formed.
+    // The next item's K and gate loads go out now; they land while W and U are formed.
     v += gridDim.x;
     const int next = v < padded ? xcd_remap(v, padded) : work;
     if (next < work) load_k(next);
@@ -438,34 +454,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
             store8(Ub + frag_u_offset(nt, m, lane), c0, c1);
         }
     }
-    // Decayed keys of the state update, transposed: item (dk, s, a) covers the
-    // 8 positions 32 s + 16 h + 4 a + b (h, b) that are consecutive in fragment order.
-    // Items run over dk fastest, so each group of 16 lanes covers 16 consecutive
-    // columns at one (s, a) (as the transposed reads need).
-    {
-        T* Kb = reinterpret_cast<T*>(p.Kt) + ch * D * CHUNK;
-#pragma unroll
-        for (int e = tid; e < D * 8; e += 256) {
-            const int dk = e % D, sa = e / D, r0 = 32 * (sa >> 2) + 4 * (sa & 3);
-            f32x4 lo, hi;
-            if constexpr (sizeof(T) == 2) {
-                const bf16x4 kl = lds_col4<PL::KP>(&s.K[0][0], r0, dk & ~15, lane);
-                const bf16x4 kh = lds_col4<PL::KP>(&s.K[0][0], r0 + 16, dk & ~15, lane);
-#pragma unroll
-                for (int b4 = 0; b4 < 4; ++b4) {
-                    lo[b4] = s.kd[r0 + b4] * (float)kl[b4];
-                    hi[b4] = s.kd[r0 + 16 + b4] * (float)kh[b4];
-                }
-            } else {
-#pragma unroll
-                for (int b4 = 0; b4 < 4; ++b4) {
-                    lo[b4] = s.kd[r0 + b4] * to_f32<T>(s.K[r0 + b4][dk]);
-                    hi[b4] = s.kd[r0 + 16 + b4] * to_f32<T>(s.K[r0 + 16 + b4][dk]);
-                }
-            }
-            store8(Kb + frag_k_offset(dk, r0), lo, hi);
-        }
-    }
+    // Per-position factor of the state update's keys: gamma_l / gamma_r (zero
+    // past the valid length).
+    if (tid < CHUNK) p.kf[ch * CHUNK + tid] = s.kd[tid];
     if (next >= work) break;
     lds_sync();  // every read of this item's LDS is done before the next item's K lands
     wid = next;
@@ -480,19 +471,23 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
 //
 //    Compute waves.  The fp32 state slice S[:, tile] (d_k x 16) stays in MFMA
 //    accumulators, split by rows over the waves.  Per chunk:
-//      X = U - W S          wave w: positions 16w..16w+15, contraction over d_k
-//      S = gamma_l S + Kd^T X   wave w: its rows of S, contraction over positions
-//    The two products exchange bf16 copies of -S and X through LDS in MFMA
+//      X = U - W S                 wave w: positions 16w..16w+15, contraction over d_k
+//      S = gamma_l S + K^T (kf X)  wave w: its rows of S, contraction over positions
+//    (kf = gamma_l / gamma per position, with the front end also 1 / |k|: the
+//    decayed keys of the chunk form, applied to X rather than to K).  The two
+//    products exchange bf16 copies of -S, X and kf X through LDS in MFMA
 //    operand order (one 16-byte access per lane and fragment), two barriers a
-//    chunk (B1 before X, B2 before the state update).  A chunk's W, Kd, U and
+//    chunk (B1 before X, B2 before the state update).  A chunk's W, K, U and
 //    gate fragments are copied from its LDS stage into registers during the
-//    second half of the previous step.  The compute waves issue no global
+//    second half of the previous step (K's column fragments with transposed
+//    reads).  The compute waves issue no global
 //    memory instruction inside the loop: a vector-memory instruction stalls
 //    its wave whenever the CU's memory pipeline is backed up, and on this
 //    serial path every stall delays the next barrier for all waves.
 //
-//    Producer waves.  Stream each chunk's W, Kd, U and gate blocks (stored by
-//    chunk_prep in exactly the LDS stage order) into a ring of NST stages
+//    Producer waves.  Stream each chunk's W, K (Kc, one copy per key head),
+//    U, gc and kf blocks (stored by chunk_prep in exactly the LDS stage
+//    order) into a ring of NST stages
 //    (three where they fit) with direct global->LDS loads.  A stage is free
 //    once its chunk is in registers (B1 of that chunk's step); chunk c + NST
 //    goes out in two halves, at B1(c) and B2(c); vmcnt waits make chunk c + 1
@@ -504,19 +499,18 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
 template <typename T, int D>
 struct StateStage {
     static constexpr int W_BYTES = CHUNK * D * (int)sizeof(T);
-    static constexpr int K_BYTES = D * CHUNK * (int)sizeof(T);
+    static constexpr int K_BYTES = CHUNK * D * (int)sizeof(T);   // K rows, row-major (pieces permuted by kswz)
     static constexpr int U_BYTES = 4 * 64 * 4 * (int)sizeof(T);  // one 16-column tile
-    static constexpr int G_BYTES = CHUNK * 4;
+    static constexpr int G_BYTES = 2 * CHUNK * 4;                // gc, then kf
     static constexpr int BYTES = W_BYTES + K_BYTES + U_BYTES + G_BYTES;
     static constexpr int NPIECE = (W_BYTES + K_BYTES + U_BYTES) / 1024;    // 1 KiB loads per chunk (+ gates)
-    static constexpr int EXCH = (D / 32 + 2) * 64 * 8 * (int)sizeof(T);    // -S and X exchange
+    static constexpr int EXCH = (D / 32 + 4) * 64 * 8 * (int)sizeof(T);    // -S, X and kf X exchange
     // A wave can keep at most 63 vector-memory operations in flight, so the
     // stream is split over NPW producer waves, each owning every NPW-th piece,
-    // with one chunk's share (plus the gate load) within that limit.
-    static constexpr int NPW = (NPIECE + 1 + 62) / 63;
-    static constexpr int PER_WAVE = (NPIECE + NPW - 1) / NPW + 1;           // upper bound incl. the gate load
-    // Two LDS stages: the compute waves copy chunk c into registers before
-    // B1(c), so stage c % 2 is refilled with chunk c + 2 from B1(c) on.
+    // with one chunk's share (plus the two gate loads) within that limit.
+    static constexpr int NPW = (NPIECE + 2 + 62) / 63;
+    // The compute waves copy chunk c into registers before B1(c), so stage
+    // c % NST is refilled with chunk c + NST from B1(c) on.
     static constexpr int LDS_CAP = 160 * 1024;
     static constexpr int NST = (3 * BYTES + EXCH + 256 <= LDS_CAP) ? 3 : 2;  // + the L2-prefetch sink
 };
@@ -568,16 +562,17 @@ __device__ __forceinline__ void lds_wait_untracked(u32x4* r) {
 
 // Issue this producer wave's share (pieces j with j % NPW == pw) of one
 // chunk's direct-to-LDS loads; part 0 issues the first half of the share,
-// part 1 the rest and the 256-byte gate block (producer wave 0).
+// part 1 the rest and the two 256-byte gate blocks gc and kf (producer
+// wave 0).  ch: (chunk, value head) index; kch: (chunk, key head) index of Kc.
 template <typename T, int D>
-__device__ __forceinline__ void state_issue(char* stage, const ChunkParams& p, size_t ch, int tile, int lane, int pw,
-                                            int part) {
+__device__ __forceinline__ void state_issue(char* stage, const ChunkParams& p, size_t ch, size_t kch, int tile,
+                                            int lane, int pw, int part) {
     using SS = StateStage<T, D>;
     constexpr int NT = D / 16;
     constexpr int NW = SS::W_BYTES / 1024, NK = SS::K_BYTES / 1024;
     constexpr int NP = SS::NPIECE;
     const char* wg = reinterpret_cast<const char*>(p.W) + ch * SS::W_BYTES;
-    const char* kg = reinterpret_cast<const char*>(p.Kt) + ch * SS::K_BYTES;
+    const char* kg = reinterpret_cast<const char*>(p.Kc) + kch * SS::K_BYTES;
     const char* ug = reinterpret_cast<const char*>(p.Ut) + (ch * NT + tile) * SS::U_BYTES;
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
@@ -590,19 +585,21 @@ __device__ __forceinline__ void state_issue(char* stage, const ChunkParams& p, s
         else
             dma_1k(ug + 1024 * (j - NW - NK), stage + SS::W_BYTES + SS::K_BYTES + 1024 * (j - NW - NK), lane);
     }
-    if (part == 1 && pw == 0)
-        __builtin_amdgcn_global_load_lds((gptr_t)(p.gc + ch * CHUNK + lane),
-                                         (lptr_t)(stage + SS::W_BYTES + SS::K_BYTES + SS::U_BYTES), 4, 0, 0);
+    if (part == 1 && pw == 0) {
+        char* g = stage + SS::W_BYTES + SS::K_BYTES + SS::U_BYTES;
+        __builtin_amdgcn_global_load_lds((gptr_t)(p.gc + ch * CHUNK + lane), (lptr_t)g, 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((gptr_t)(p.kf + ch * CHUNK + lane), (lptr_t)(g + 4 * CHUNK), 4, 0, 0);
+    }
 }
 
 // Loads producer wave pw issues in part 0 / part 1 of a chunk (part 1
-// includes the gate load of wave 0).
+// includes the two gate loads of wave 0).
 template <typename T, int D>
 __host__ __device__ constexpr int state_part_loads(int pw, int part) {
     using SS = StateStage<T, D>;
     int n = 0;
     for (int j = 0; j < SS::NPIECE; ++j) n += (j % SS::NPW == pw && (j < SS::NPIECE / 2) == (part == 0)) ? 1 : 0;
-    return n + (part == 1 && pw == 0 ? 1 : 0);
+    return n + (part == 1 && pw == 0 ? 2 : 0);
 }
 
 // vmcnt bounds of producer wave pw: ops younger than chunk c + 1's last load
@@ -624,6 +621,41 @@ __device__ __forceinline__ void lds_put4(Frag<T>& f, int half, const f32x4& v, f
         *reinterpret_cast<float4*>(reinterpret_cast<float*>(&f) + 4 * half) =
             make_float4(s * v[0], s * v[1], s * v[2], s * v[3]);
     }
+}
+
+// A operand of the state update K^T (kf X) for rows 16 m .. 16 m + 15 of S
+// (columns of K) and contraction step ks (positions 32 ks .. 32 ks + 31 in
+// perm32 slots: slot b <- position 32 ks + 4 g + b, slot 4 + b <- 32 ks + 16 +
+// 4 g + b, g = lane / 16), read from a stage's K rows (pieces permuted by kswz).
+template <typename T, int D>
+__device__ __forceinline__ Frag<T> k_col_frag(const char* kst, int m, int ks, int lane) {
+    constexpr int RB = D * (int)sizeof(T);  // bytes per K row
+    const int g = (lane >> 4) & 3, j = lane & 15;
+    Frag<T> f;
+    if constexpr (sizeof(T) == 2) {
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            // transposed read: lane j names row r0 + j / 4, columns 16 m + 4 (j % 4) .. + 3;
+            // lane i receives column 16 m + i of rows r0 .. r0 + 3
+            const int row = 32 * ks + 16 * half + 4 * g + (j >> 2);
+            const int piece = (2 * m + ((j & 3) >> 1)) ^ kswz<T, D>(row);
+            const char* a = kst + row * RB + 16 * piece + 8 * (j & 1);
+            const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)a);
+            const bf16x4 b = __builtin_bit_cast(bf16x4, r);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f.v[4 * half + i] = b[i];
+        }
+    } else {
+        const int colb = 4 * (16 * m + j);  // byte of column 16 m + j in an unpermuted row
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+            const int row = 32 * ks + (sl < 4 ? 4 * g + sl : 16 + 4 * g + sl - 4);
+            const int piece = (colb >> 4) ^ kswz<T, D>(row);
+            f.v[sl] = *reinterpret_cast<const float*>(kst + row * RB + 16 * piece + (colb & 15));
+        }
+    }
+    return f;
 }
 
 template <typename T, int D, bool DEV>
@@ -653,10 +685,14 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
     const int L_n = tab.cu[n + 1] - tab.cu[n];
     const int nch = tab.choff[n + 1] - tab.choff[n];
     const int c0 = tab.choff[n];
+    // (chunk, key head) index of chunk c of this sequence in Kc
+    const int hq = h / p.G;
+    auto kch = [&](int c) { return (size_t)(c0 + c) * p.H_q + hq; };
 
     __shared__ __attribute__((aligned(16))) char smem[NST * SS::BYTES + SS::EXCH + 256];  // + L2-prefetch sink
     Frag<T>(*LS)[64] = reinterpret_cast<Frag<T>(*)[64]>(smem + NST * SS::BYTES);           // [KS][64]: -S
     Frag<T>(*LX)[64] = reinterpret_cast<Frag<T>(*)[64]>(smem + NST * SS::BYTES + KS * 64 * sizeof(Frag<T>));  // [2][64]: X
+    Frag<T>(*LY)[64] = reinterpret_cast<Frag<T>(*)[64]>(smem + NST * SS::BYTES + (KS + 2) * 64 * sizeof(Frag<T>));  // [2][64]: kf X
 
     if (w >= 4 + SS::NPW) {
         // ---------------- store wave ----------------
@@ -669,25 +705,25 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         constexpr int FQ = sizeof(Frag<T>) / 16;  // 16-byte pieces per fragment
         const unsigned sgn = sizeof(T) == 2 ? 0x80008000u : 0x80000000u;
         const unsigned ls_addr = lds_addr(&LS[0][lane]), lx_addr = lds_addr(&LX[0][lane]);
-        // L2 prefetch: once a step, this tile's share of the W and Kd lines of
+        // L2 prefetch: once a step, this tile's share of the W and K lines of
         // chunk c + PF (4 bytes per line, into a sink nobody reads).  The tiles of
         // a head together touch every line, so by the time the producers stream
         // that chunk it is in L2.  It pays where the stream comes from HBM rather
         // than from the Infinity Cache (long or many sequences), and costs a few
         // per cent where it does not, so the launcher enables it by size.
         constexpr int PF = 6;
-        constexpr int LPT = SS::W_BYTES / 128 / NT;  // lines of W (and of Kd) per tile
+        constexpr int LPT = SS::W_BYTES / 128 / NT;  // lines of W (and of K) per tile
         static_assert(2 * LPT <= 64, "one line per lane");
         const int li = tile * LPT + lane % LPT;
-        const bool kd_line = (lane / LPT) & 1;
+        const bool k_line = (lane / LPT) & 1;
         asm volatile("s_barrier" ::: "memory");  // B0
         for (int c = 0; c < nch; ++c) {
             const size_t ch = (size_t)(c0 + c) * p.H_v + h;
             asm volatile("s_barrier" ::: "memory");  // B1(c)
             if (p.l2_prefetch && c + PF < nch) {
                 const size_t chp = (size_t)(c0 + c + PF) * p.H_v + h;
-                const char* a = kd_line ? reinterpret_cast<const char*>(p.Kt) + chp * SS::K_BYTES + li * 128
-                                        : reinterpret_cast<const char*>(p.W) + chp * SS::W_BYTES + li * 128;
+                const char* a = k_line ? reinterpret_cast<const char*>(p.Kc) + kch(c + PF) * SS::K_BYTES + li * 128
+                                       : reinterpret_cast<const char*>(p.W) + chp * SS::W_BYTES + li * 128;
                 __builtin_amdgcn_global_load_lds((gptr_t)a, (lptr_t)(smem + NST * SS::BYTES + SS::EXCH), 4, 0, 0);
             }
             u32x4 hs[KS][FQ];
@@ -739,8 +775,9 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
                 if (pw == 0) wait_vmcnt<RC_0>(); else wait_vmcnt<RC_1>();
             }
             if (b < nch) {
-                state_issue<T, D>(smem + b * SS::BYTES, p, (size_t)(c0 + b) * p.H_v + h, tile, lane, pw, 0);
-                state_issue<T, D>(smem + b * SS::BYTES, p, (size_t)(c0 + b) * p.H_v + h, tile, lane, pw, 1);
+                const size_t chb = (size_t)(c0 + b) * p.H_v + h;
+                state_issue<T, D>(smem + b * SS::BYTES, p, chb, kch(b), tile, lane, pw, 0);
+                state_issue<T, D>(smem + b * SS::BYTES, p, chb, kch(b), tile, lane, pw, 1);
             }
         }
         // The producers' barriers are plain s_barrier: a workgroup release fence
@@ -759,7 +796,7 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
             // chunk c + 1 is read after B2(c).
             if (cn < nch) {
                 if (pw == 0) wait_vmcnt<R0_0>(); else wait_vmcnt<R0_1>();
-                state_issue<T, D>(stn, p, chn, tile, lane, pw, 0);
+                state_issue<T, D>(stn, p, chn, kch(cn), tile, lane, pw, 0);
                 if (pw == 0) wait_vmcnt<WB_0>(); else wait_vmcnt<WB_1>();
             } else {
                 wait_vmcnt<0>();
@@ -767,7 +804,7 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
             asm volatile("s_barrier" ::: "memory");  // B2(c)
             if (cn < nch) {
                 if (pw == 0) wait_vmcnt<R1_0>(); else wait_vmcnt<R1_1>();
-                state_issue<T, D>(stn, p, chn, tile, lane, pw, 1);
+                state_issue<T, D>(stn, p, chn, kch(cn), tile, lane, pw, 1);
             }
         }
         return;
@@ -784,13 +821,14 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         lds_put4(LS[m >> 1][lane], m & 1, S[tt], -1.f);
     }
     // Operand fragments of one chunk, read from its LDS stage.
-    Frag<T> wf[KS], kf[TPW][2];
+    Frag<T> wf[KS], kfg[TPW][2];
     Raw4<T> uf;
     float gl = 0.f;
+    float4 fx;  // kf of this wave's X rows (positions 16 w + 4 grp + i)
     auto read_stage = [&](int c) {
         const char* st = smem + (c % NST) * SS::BYTES;
         const Frag<T>* Wst = reinterpret_cast<const Frag<T>*>(st);
-        const Frag<T>* Kst = reinterpret_cast<const Frag<T>*>(st + SS::W_BYTES);
+        const char* Kst = st + SS::W_BYTES;
         const Raw4<T>* Ust = reinterpret_cast<const Raw4<T>*>(st + SS::W_BYTES + SS::K_BYTES);
         const float* Gst = reinterpret_cast<const float*>(st + SS::W_BYTES + SS::K_BYTES + SS::U_BYTES);
 #pragma unroll
@@ -798,9 +836,10 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) kf[tt][ks] = Kst[((w * TPW + tt) * 2 + ks) * 64 + lane];
+            for (int ks = 0; ks < 2; ++ks) kfg[tt][ks] = k_col_frag<T, D>(Kst, w * TPW + tt, ks, lane);
         uf = Ust[((w >> 1) * 64 + lane) * 2 + (w & 1)];
         gl = Gst[min(CHUNK, L_n - c * CHUNK) - 1];
+        fx = *reinterpret_cast<const float4*>(Gst + CHUNK + 16 * w + 4 * grp);
     };
     lds_sync();  // B0: stages 0 and 1 ready
     if (nch > 0) read_stage(0);
@@ -814,18 +853,20 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) X = mma(wf[ks], sb[ks], X);
         lds_put4(LX[w >> 1][lane], w & 1, X, 1.f);
+        const f32x4 Y = f32x4{X[0] * fx.x, X[1] * fx.y, X[2] * fx.z, X[3] * fx.w};
+        lds_put4(LY[w >> 1][lane], w & 1, Y, 1.f);
         const float eg = __expf(gl);
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) S[tt] *= eg;
         Frag<T> kc[TPW][2];
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
-            kc[tt][0] = kf[tt][0];
-            kc[tt][1] = kf[tt][1];
+            kc[tt][0] = kfg[tt][0];
+            kc[tt][1] = kfg[tt][1];
         }
-        lds_sync();  // B2(c): all of X in LX; stage c + 1 ready
+        lds_sync();  // B2(c): all of X in LX and kf X in LY; stage c + 1 ready
         if (c + 1 < nch) read_stage(c + 1);
-        const Frag<T> xb0 = LX[0][lane], xb1 = LX[1][lane];
+        const Frag<T> xb0 = LY[0][lane], xb1 = LY[1][lane];
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
             S[tt] = mma(kc[tt][0], xb0, S[tt]);
@@ -896,21 +937,18 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
 
     __shared__ __attribute__((aligned(16))) OL s;
 
-    // Q and K rows into LDS (zeros past the valid length), gates.
+    // Q and K rows into LDS (zeros past the valid length), gates.  K comes from
+    // chunk_prep's contiguous copy Kc (already L2-normalised with the front end,
+    // zero past the valid length); Q rows are L2-normalised on the way with the
+    // front end, as in chunk_prep.
     const T* qb = reinterpret_cast<const T*>(p.q) + (size_t)cp.t0 * p.H_q * D + (size_t)hq * D;
-    const T* kb = reinterpret_cast<const T*>(p.k) + (size_t)cp.t0 * p.H_q * D + (size_t)hq * D;
-    // (With the front end, rows L2-normalised on the way, as in chunk_prep.)
+    const T* kcb = reinterpret_cast<const T*>(p.Kc) + ((size_t)cp.ci * p.H_q + hq) * CHUNK * D;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
-        const bool ok = r < ell;
-        const size_t off = (size_t)r * p.H_q * D + c;
-        float4 qv = ok ? *reinterpret_cast<const float4*>(qb + off) : make_float4(0, 0, 0, 0);
-        float4 kv = ok ? *reinterpret_cast<const float4*>(kb + off) : make_float4(0, 0, 0, 0);
-        if (p.fa) {
-            qv = l2norm_piece<T, D>(qv);
-            kv = l2norm_piece<T, D>(kv);
-        }
+        float4 qv = r < ell ? *reinterpret_cast<const float4*>(qb + (size_t)r * p.H_q * D + c) : make_float4(0, 0, 0, 0);
+        const float4 kv = *reinterpret_cast<const float4*>(kcb + r * D + VEC * ((c / VEC) ^ kswz<T, D>(r)));
+        if (p.fa) qv = l2norm_piece<T, D>(qv);
         *reinterpret_cast<float4*>(&s.Q[r][c]) = qv;
         *reinterpret_cast<float4*>(&s.u.K[r][c]) = kv;
     }
@@ -1156,7 +1194,7 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
         else
             hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, stream, kp, padded);
     };
-    // The state scan's L2 prefetch pays when its W / Kd / U stream no longer
+    // The state scan's L2 prefetch pays when its W / K / U stream no longer
     // fits in the 256 MB Infinity Cache next to the layer's other tensors: on
     // above 128 MiB of stream.
     ChunkParams pl = p;

@@ -215,10 +215,11 @@ __device__ __forceinline__ bf16x4 lds_col4(const bf16* base, int r0, int c0, int
 // ---- row L2 normalisation of staged rows ---------------------------------
 // A D-element row held as 16-byte pieces by D / (16 / sizeof(T)) consecutive
 // lanes (aligned groups inside one wave): each lane returns its piece times
-// 1 / sqrt(sum over the row of x^2 + 1e-6), rounded to T.  All lanes of the
-// wave must take part (the sum is reduced with lane shuffles).
+// 1 / sqrt(sum over the row of x^2 + 1e-6), rounded to T, and that factor in
+// rnorm.  All lanes of the wave must take part (the sum is reduced with lane
+// shuffles).
 template <typename T, int D>
-__device__ __forceinline__ float4 l2norm_piece(float4 raw) {
+__device__ __forceinline__ float4 l2norm_piece(float4 raw, float& rnorm) {
     constexpr int VEC = 16 / (int)sizeof(T);
     constexpr int LPR = D / VEC;  // lanes per row
     static_assert(LPR <= 64 && (LPR & (LPR - 1)) == 0, "row must fit a power-of-two lane group");
@@ -234,6 +235,7 @@ __device__ __forceinline__ float4 l2norm_piece(float4 raw) {
 #pragma unroll
         for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m, 64);
         const float r = 1.f / sqrtf(ss + 1e-6f);
+        rnorm = r;
         bf16x8 o;
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[i] = (bf16)(x[i] * r);
@@ -243,8 +245,14 @@ __device__ __forceinline__ float4 l2norm_piece(float4 raw) {
 #pragma unroll
         for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m, 64);
         const float r = 1.f / sqrtf(ss + 1e-6f);
+        rnorm = r;
         return make_float4(raw.x * r, raw.y * r, raw.z * r, raw.w * r);
     }
+}
+template <typename T, int D>
+__device__ __forceinline__ float4 l2norm_piece(float4 raw) {
+    float r;
+    return l2norm_piece<T, D>(raw, r);
 }
 
 // ---- SiLU ------------------------------------------------------------------

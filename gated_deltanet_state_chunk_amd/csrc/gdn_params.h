@@ -41,13 +41,14 @@ struct ChunkParams {
     void* A;
     void* W;
     void* Ut;
-    void* Kt;
+    float* kf;  // per (chunk, value head, position): factor of the state update's keys
+    void* Kc;   // per (chunk, key head): the chunk's key rows for the state update
     void* Ht;
     void* Xt;
     int32_t H_q, H_v, G;
     float scale;
     int32_t keep_A;  // nonzero: chunk_prep also writes A to the workspace
-    int32_t l2_prefetch;  // nonzero: chunk_state_h prefetches W / Kd into L2 (set by the launcher)
+    int32_t l2_prefetch;  // nonzero: chunk_state_h prefetches W / K into L2 (set by the launcher)
     // optional read-out epilogue out = rmsnorm(o) * gw * silu(gz) (gz null: none)
     const void* gz;
     const float* gw;

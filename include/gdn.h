@@ -73,11 +73,10 @@ enum {
  * numbered in sequence order, each sequence's chunks starting at its own first
  * token, so chunk c of sequence n has global index chunk_offset(n) + c where
  * chunk_offset(n) = sum_{m<n} ceil(L_m / 64).  Positions beyond a tail chunk's
- * valid length hold zeros.  Three regions are kept in the order in which the
+ * valid length hold zeros.  Two regions are kept in the order in which the
  * MFMA units consume them ("fragment order", 8 values per lane of a 64-lane
  * wave; for an index i let i = 32 s + 16 h + 4 a + b with a, b in 0..3):
  *   W   element (pos, k):  ((pos/16 * (d_k/32) + s(k)) * 64 + 16 a(k) + pos%16) * 8 + 4 h(k) + b(k)
- *   Kd  element (k, pos):  ((k/16 * 2 + s(pos)) * 64 + 16 a(pos) + k%16) * 8 + 4 h(pos) + b(pos)
  *   U   element (pos, j):  ((j/16 * 2 + pos/32) * 64 + 16 ((pos%16)/4) + j%16) * 8 + 4 ((pos/16)%2) + pos%4
  * "perm32" means: within every block of 32 consecutive indices, index
  * 16 h + 4 a + b is stored at offset 8 a + 4 h + b.
@@ -87,13 +86,22 @@ enum {
  *                                            written only under GDN_FWD_KEEP_A (gdn_chunk_fwd_ex)
  *   W   dtype [n_chunks][H_v][64 * d_k]      A B Gamma K, fragment order
  *   U   dtype [n_chunks][H_v][64 * d_v]      A B V, fragment order
- *   Kd  dtype [n_chunks][H_v][d_k * 64]      (Diag(gamma_l / gamma) K)^T, fragment order
+ *   kf  fp32  [n_chunks][H_v][64]            gamma_l / gamma per position (the decay of a
+ *                                            key to the chunk end), zero past the valid
+ *                                            length: the state update is
+ *                                            S <- gamma_l S + Kc^T Diag(kf) X
+ *   Kc  dtype [n_chunks][H_q][64][d_k]       the chunk's key rows (L2-normalised with
+ *                                            gdn_chunk_fwd_fused), the 16-byte pieces of row
+ *                                            r permuted: piece i stored at i ^ p(r), where
+ *                                            with P = d_k * sizeof(dtype) / 16 pieces a row
+ *                                            p(r) = 2 (r mod P/2) for bf16 and
+ *                                            4 ((r / 4) mod P/4) for fp32
  *   Ht  dtype [n_chunks][H_v][d_v][d_k]      (state at chunk start)^T
  *   Xt  dtype [n_chunks][H_v][d_v][64]       (U - W S)^T, last index perm32
  */
 typedef struct gdn_workspace_layout {
     int64_t n_chunks;
-    size_t off_gc, off_A, off_W, off_U, off_Kd, off_Ht, off_Xt; /* byte offsets */
+    size_t off_gc, off_A, off_W, off_U, off_kf, off_Kc, off_Ht, off_Xt; /* byte offsets */
     size_t total_bytes;
 } gdn_workspace_layout;
 

@@ -59,15 +59,6 @@ def frag_w_to_logical(flat, d_k):
     return flat[..., off]
 
 
-def frag_kd_to_logical(flat, d_k):
-    """Kd [..., d_k*64] in fragment order -> [..., d_k, 64]."""
-    k = np.arange(d_k)[:, None]
-    pos = np.arange(64)[None, :]
-    s, h, a, b = _split32(pos)
-    off = ((k // 16 * 2 + s) * 64 + 16 * a + k % 16) * 8 + 4 * h + b
-    return flat[..., off]
-
-
 def frag_u_to_logical(flat, d_v):
     """U [..., 64*d_v] in accumulator order -> [..., 64, d_v]."""
     pos = np.arange(64)[:, None]

@@ -66,11 +66,13 @@ def _cu(vals):
 def test_workspace_layout(gdn):
     lay = gdn.workspace_layout(4096, [0, 4096], 16, 32, 128, 128, "bf16")
     assert lay["n_chunks"] == 64
-    offs = [lay[k] for k in ("off_gc", "off_A", "off_W", "off_U", "off_Kd", "off_Ht", "off_Xt", "total_bytes")]
+    offs = [lay[k] for k in ("off_gc", "off_A", "off_W", "off_U", "off_kf", "off_Kc", "off_Ht", "off_Xt",
+                             "total_bytes")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     chv = 64 * 32
     assert lay["off_A"] - lay["off_gc"] == chv * 64 * 4
-    assert lay["off_Ht"] - lay["off_Kd"] == chv * 128 * 64 * 2
+    assert lay["off_Kc"] - lay["off_kf"] == chv * 64 * 4
+    assert lay["off_Ht"] - lay["off_Kc"] == 64 * 16 * 64 * 128 * 2  # chunks x key heads x rows x d_k
     assert lay["off_Xt"] - lay["off_Ht"] == chv * 128 * 128 * 2
     # chunks are counted per sequence: ceil(100/64) + 0 + ceil(1/64) + ceil(128/64)
     lay2 = gdn.workspace_layout(229, [0, 100, 100, 101, 229], 2, 4, 64, 64, "f32")

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import gdn_inputs
-from tests.gpu_helpers import (chunk_fwd_device, f32_dev, frag_kd_to_logical, frag_u_to_logical, frag_w_to_logical,
+from tests.gpu_helpers import (chunk_fwd_device, f32_dev, frag_u_to_logical, frag_w_to_logical,
                                rel_err, to_dev, to_host, unperm32)
 
 pytestmark = pytest.mark.gpu
@@ -190,18 +190,30 @@ def test_chunk_intermediates_match_chunk_form(torch_cuda, dtype, d, tol):
     A = region(lay["off_A"], (nc, H_v, 64, 64))
     W = frag_w_to_logical(region(lay["off_W"], (nc, H_v, 64 * d)), d)
     U = frag_u_to_logical(region(lay["off_U"], (nc, H_v, 64 * d)), d)
-    Kt = frag_kd_to_logical(region(lay["off_Kd"], (nc, H_v, d * 64)), d)
+    kf = region(lay["off_kf"], (nc, H_v, 64), is_f32=True)
+    # Kc: each row's 16-byte pieces stored permuted (piece i at i ^ p(r), as include/gdn.h states)
+    es = 4 if dtype == "f32" else 2
+    P = d * es // 16
+    Kc_st = region(lay["off_Kc"], (nc, H_q, 64, P, 16 // es))
+    Kc = np.empty_like(Kc_st)
+    for r in range(64):
+        pr = 2 * (r % (P // 2)) if es == 2 else 4 * ((r // 4) % (P // 4))
+        Kc[:, :, r, np.arange(P) ^ pr] = Kc_st[:, :, r]
+    Kc = Kc.reshape(nc, H_q, 64, d)
+    k_in = inp.k32()
     Hs = np.swapaxes(region(lay["off_Ht"], (nc, H_v, d, d)), -1, -2)
     X = np.swapaxes(unperm32(region(lay["off_Xt"], (nc, H_v, d, 64))), -1, -2)
 
     ref = chunk_form.chunk_forward(inp.q32(), inp.k32(), inp.v32(), inp.g, inp.beta, inp.cu_seqlens, H_q, H_v,
                                    inp.scale, initial_state=inp.initial_state, keep_intermediates=True)
     ci = 0
-    k32 = inp.k32()
     for n, L in enumerate(lens):
         for c in range((L + 63) // 64):
             ell = min(64, L - 64 * c)
             t0 = int(inp.cu_seqlens[n]) + 64 * c
+            for hq in range(H_q):  # the chunk's key rows, exactly, and zeros past the valid length
+                assert np.array_equal(Kc[ci, hq, :ell], k_in[t0:t0 + ell, hq].astype(np.float64))
+                assert np.all(Kc[ci, hq, ell:] == 0)
             for h in range(H_v):
                 r = ref["chunks"][(n, h)][c]
                 assert rel_err(gc[ci, h, :ell], r["gc"]) < 1e-5
@@ -214,10 +226,8 @@ def test_chunk_intermediates_match_chunk_form(torch_cuda, dtype, d, tol):
                 assert rel_err(X[ci, h, :ell], r["X"]) < 3 * tol
                 assert np.all(W[ci, h, ell:] == 0) and np.all(X[ci, h, ell:] == 0)
                 # keys of the state update carry the decay to the chunk end: gamma_l / gamma_r
-                hq = h // (H_v // H_q)
-                kd = np.exp(r["gc"][-1] - r["gc"])[:, None] * k32[t0:t0 + ell, hq, :].astype(np.float64)
-                assert rel_err(Kt[ci, h, :, :ell], kd.T) < tol
-                assert np.all(Kt[ci, h, :, ell:] == 0)
+                assert rel_err(kf[ci, h, :ell], np.exp(r["gc"][-1] - r["gc"])) < 1e-5
+                assert np.all(kf[ci, h, ell:] == 0)
             ci += 1
 
 
