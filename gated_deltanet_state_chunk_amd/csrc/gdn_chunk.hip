@@ -504,7 +504,11 @@ struct StateStage {
     static constexpr int G_BYTES = 2 * CHUNK * 4;                // gc, then kf
     static constexpr int BYTES = W_BYTES + K_BYTES + U_BYTES + G_BYTES;
     static constexpr int NPIECE = (W_BYTES + K_BYTES + U_BYTES) / 1024;    // 1 KiB loads per chunk (+ gates)
-    static constexpr int EXCH = (D / 32 + 4) * 64 * 8 * (int)sizeof(T);    // -S, X and kf X exchange
+    // Exchange blocks (-S, X and kf X): one fragment per lane, 16 bytes of
+    // padding after every 16 lanes so that the store wave's column gathers
+    // spread over the LDS banks.
+    static constexpr int XBLK = 64 * 8 * (int)sizeof(T) + 4 * 16;
+    static constexpr int EXCH = (D / 32 + 4) * XBLK;
     // A wave can keep at most 63 vector-memory operations in flight, so the
     // stream is split over NPW producer waves, each owning every NPW-th piece,
     // with one chunk's share (plus the two gate loads) within that limit.
@@ -690,9 +694,13 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
     auto kch = [&](int c) { return (size_t)(c0 + c) * p.H_q + hq; };
 
     __shared__ __attribute__((aligned(16))) char smem[NST * SS::BYTES + SS::EXCH + 256];  // + L2-prefetch sink
-    Frag<T>(*LS)[64] = reinterpret_cast<Frag<T>(*)[64]>(smem + NST * SS::BYTES);           // [KS][64]: -S
-    Frag<T>(*LX)[64] = reinterpret_cast<Frag<T>(*)[64]>(smem + NST * SS::BYTES + KS * 64 * sizeof(Frag<T>));  // [2][64]: X
-    Frag<T>(*LY)[64] = reinterpret_cast<Frag<T>(*)[64]>(smem + NST * SS::BYTES + (KS + 2) * 64 * sizeof(Frag<T>));  // [2][64]: kf X
+    char* const LS = smem + NST * SS::BYTES;  // KS blocks: -S
+    char* const LX = LS + KS * SS::XBLK;      // 2 blocks: X
+    char* const LY = LX + 2 * SS::XBLK;       // 2 blocks: kf X
+    // fragment of lane ln in block b of an exchange buffer
+    auto xf = [](char* buf, int b, int ln) -> Frag<T>& {
+        return *reinterpret_cast<Frag<T>*>(buf + b * SS::XBLK + ln * (int)sizeof(Frag<T>) + (ln >> 4) * 16);
+    };
 
     if (w >= 4 + SS::NPW) {
         // ---------------- store wave ----------------
@@ -704,7 +712,38 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         // 4..7: rows 16+4g..16+4g+3, g = lane / 16; column lane % 16).
         constexpr int FQ = sizeof(Frag<T>) / 16;  // 16-byte pieces per fragment
         const unsigned sgn = sizeof(T) == 2 ? 0x80008000u : 0x80000000u;
-        const unsigned ls_addr = lds_addr(&LS[0][lane]), lx_addr = lds_addr(&LX[0][lane]);
+        // Every store writes whole 16-byte pieces, and the 64 lanes of one store
+        // instruction cover consecutive rows of Ht (h^T: a tile's 16 rows of d_k
+        // values) or of Xt, so each instruction writes complete cache lines; the
+        // pieces are gathered from the fragment-ordered exchange buffers by
+        // lane-permuted LDS reads (bf16: two 8-byte halves of a piece come from
+        // the lanes of groups 2a and 2a + 1).
+        constexpr int EB = (int)sizeof(T);
+        constexpr int HPR = D * EB / 16, HPL = 16 * HPR / 64;          // Ht pieces per row / per lane
+        constexpr int XPR = CHUNK * EB / 16, XPL = 16 * XPR / 64;      // Xt pieces per row / per lane
+        const unsigned ls0 = lds_addr(LS), lx0 = lds_addr(LX);
+        auto xoff = [](int b, int ln) { return (unsigned)(b * SS::XBLK + ln * (int)sizeof(Frag<T>) + (ln >> 4) * 16); };
+        unsigned hla[HPL], xla[XPL];  // LDS byte addresses
+        unsigned hgo[HPL], xgo[XPL];  // byte offsets in the chunk-head's Ht / Xt block
+#pragma unroll
+        for (int t = 0; t < HPL; ++t) {
+            const int q = lane + 64 * t, cl = q / HPR, pc = q % HPR;
+            if constexpr (EB == 2) {  // piece pc: d_k 8 pc .. 8 pc + 7
+                const int ks = pc >> 2, a = pc & 3;
+                hla[t] = ls0 + xoff(ks, 32 * (a & 1) + cl) + 8 * (a >> 1);
+            } else {  // piece pc: d_k 4 pc .. 4 pc + 3
+                const int ks = pc >> 3, hh = (pc >> 2) & 1, g = pc & 3;
+                hla[t] = ls0 + xoff(ks, 16 * g + cl) + 16 * hh;
+            }
+            hgo[t] = (unsigned)((16 * tile + cl) * D * EB + 16 * pc);
+        }
+#pragma unroll
+        for (int t = 0; t < XPL; ++t) {
+            const int q = lane + 64 * t, cl = q / XPR, pc = q % XPR;
+            const int j = pc / (4 * FQ), g = (pc / FQ) % 4, e = pc % FQ;
+            xla[t] = lx0 + xoff(j, 16 * g + cl) + 16 * e;
+            xgo[t] = (unsigned)((16 * tile + cl) * CHUNK * EB + 16 * pc);
+        }
         // L2 prefetch: once a step, this tile's share of the W and K lines of
         // chunk c + PF (4 bytes per line, into a sink nobody reads).  The tiles of
         // a head together touch every line, so by the time the producers stream
@@ -726,32 +765,27 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
                                        : reinterpret_cast<const char*>(p.W) + chp * SS::W_BYTES + li * 128;
                 __builtin_amdgcn_global_load_lds((gptr_t)a, (lptr_t)(smem + NST * SS::BYTES + SS::EXCH), 4, 0, 0);
             }
-            u32x4 hs[KS][FQ];
-            lds_read_untracked<KS * FQ>(&hs[0][0], ls_addr, 64 * sizeof(Frag<T>), FQ);
-            lds_wait_untracked<KS * FQ>(&hs[0][0]);
-            T* Hb = reinterpret_cast<T*>(p.Ht) + ((ch * D + col) * D);  // h_c = -(LS): a sign flip, exact
+            // h_c = -(LS): a sign flip, exact
+            u32x4 hv[HPL];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                if constexpr (sizeof(T) == 2) {
-                    const u32x4 u = hs[ks][0];
-                    *reinterpret_cast<u32x2*>(Hb + 32 * ks + 4 * grp) = u32x2{u.x ^ sgn, u.y ^ sgn};
-                    *reinterpret_cast<u32x2*>(Hb + 32 * ks + 16 + 4 * grp) = u32x2{u.z ^ sgn, u.w ^ sgn};
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 2; ++e)
-                        *reinterpret_cast<u32x4*>(Hb + 32 * ks + 16 * e + 4 * grp) = hs[ks][e] ^ sgn;
-                }
+            for (int t = 0; t < HPL; ++t) {
+                if constexpr (EB == 2)  // the two halves, 16 lanes (272 bytes) apart, in one read
+                    asm volatile("ds_read2_b64 %0, %1 offset1:34" : "=v"(hv[t]) : "v"(hla[t]));
+                else
+                    asm volatile("ds_read_b128 %0, %1" : "=v"(hv[t]) : "v"(hla[t]));
             }
+            lds_wait_untracked<HPL>(hv);
+            char* Hb = reinterpret_cast<char*>(p.Ht) + ch * D * D * EB;
+#pragma unroll
+            for (int t = 0; t < HPL; ++t) *reinterpret_cast<u32x4*>(Hb + hgo[t]) = hv[t] ^ sgn;
             asm volatile("s_barrier" ::: "memory");  // B2(c)
-            u32x4 xs[2][FQ];
-            lds_read_untracked<2 * FQ>(&xs[0][0], lx_addr, 64 * sizeof(Frag<T>), FQ);
-            lds_wait_untracked<2 * FQ>(&xs[0][0]);
-            T* Xb = reinterpret_cast<T*>(p.Xt) + (ch * D + col) * CHUNK;  // X_c, already in the stored perm32 order
+            u32x4 xv[XPL];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int t = 0; t < XPL; ++t) asm volatile("ds_read_b128 %0, %1" : "=v"(xv[t]) : "v"(xla[t]));
+            lds_wait_untracked<XPL>(xv);
+            char* Xb = reinterpret_cast<char*>(p.Xt) + ch * D * CHUNK * EB;  // X_c, already in the stored perm32 order
 #pragma unroll
-                for (int e = 0; e < FQ; ++e)
-                    *reinterpret_cast<u32x4*>(Xb + 32 * j + 8 * grp + e * (16 / (int)sizeof(T))) = xs[j][e];
+            for (int t = 0; t < XPL; ++t) *reinterpret_cast<u32x4*>(Xb + xgo[t]) = xv[t];
         }
         wait_vmcnt<0>();  // no prefetch may land in LDS after the workgroup has ended
         return;
@@ -818,7 +852,7 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             S[tt][i] = si >= 0 ? p.s0[in_off + (size_t)(16 * m + 4 * grp + i) * D + col] : 0.f;
-        lds_put4(LS[m >> 1][lane], m & 1, S[tt], -1.f);
+        lds_put4(xf(LS, m >> 1, lane), m & 1, S[tt], -1.f);
     }
     // Operand fragments of one chunk, read from its LDS stage.
     Frag<T> wf[KS], kfg[TPW][2];
@@ -847,14 +881,14 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         lds_sync();  // B1(c): -S in LS; chunk c's stage may be refilled
         Frag<T> sb[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sb[ks] = LS[ks][lane];
+        for (int ks = 0; ks < KS; ++ks) sb[ks] = xf(LS, ks, lane);
         // X = U - W S for positions 16 w .. 16 w + 15
         f32x4 X = raw4_to_f32(uf);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) X = mma(wf[ks], sb[ks], X);
-        lds_put4(LX[w >> 1][lane], w & 1, X, 1.f);
+        lds_put4(xf(LX, w >> 1, lane), w & 1, X, 1.f);
         const f32x4 Y = f32x4{X[0] * fx.x, X[1] * fx.y, X[2] * fx.z, X[3] * fx.w};
-        lds_put4(LY[w >> 1][lane], w & 1, Y, 1.f);
+        lds_put4(xf(LY, w >> 1, lane), w & 1, Y, 1.f);
         const float eg = __expf(gl);
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) S[tt] *= eg;
@@ -866,7 +900,7 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         }
         lds_sync();  // B2(c): all of X in LX and kf X in LY; stage c + 1 ready
         if (c + 1 < nch) read_stage(c + 1);
-        const Frag<T> xb0 = LY[0][lane], xb1 = LY[1][lane];
+        const Frag<T> xb0 = xf(LY, 0, lane), xb1 = xf(LY, 1, lane);
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
             S[tt] = mma(kc[tt][0], xb0, S[tt]);
@@ -875,7 +909,7 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
             const int m = w * TPW + tt;
-            lds_put4(LS[m >> 1][lane], m & 1, S[tt], -1.f);
+            lds_put4(xf(LS, m >> 1, lane), m & 1, S[tt], -1.f);
         }
     }
     if (so >= 0) {
