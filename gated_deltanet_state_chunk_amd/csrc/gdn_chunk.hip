@@ -712,37 +712,35 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         // 4..7: rows 16+4g..16+4g+3, g = lane / 16; column lane % 16).
         constexpr int FQ = sizeof(Frag<T>) / 16;  // 16-byte pieces per fragment
         const unsigned sgn = sizeof(T) == 2 ? 0x80008000u : 0x80000000u;
-        // Every store writes whole 16-byte pieces, and the 64 lanes of one store
-        // instruction cover consecutive rows of Ht (h^T: a tile's 16 rows of d_k
-        // values) or of Xt, so each instruction writes complete cache lines; the
-        // pieces are gathered from the fragment-ordered exchange buffers by
-        // lane-permuted LDS reads (bf16: two 8-byte halves of a piece come from
-        // the lanes of groups 2a and 2a + 1).
+        // Ht and Xt are written in the fragment order chunk_output_o reads them
+        // in (its A operands H^T and X^T, rows d_v: block (d_v tile, K-step),
+        // lane 16 g + r holding row r, contraction indices 8 g .. 8 g + 7 of the
+        // block), so every store instruction writes 1 KiB of consecutive bytes
+        // (whole cache lines) and every load of chunk_output_o reads them the
+        // same way.  The pieces are gathered from the fragment-ordered exchange
+        // buffers (perm32 contraction order) by lane-permuted LDS reads; bf16:
+        // the two 8-byte halves of a piece come from lanes 16 apart, one
+        // ds_read2_b64.
         constexpr int EB = (int)sizeof(T);
-        constexpr int HPR = D * EB / 16, HPL = 16 * HPR / 64;          // Ht pieces per row / per lane
-        constexpr int XPR = CHUNK * EB / 16, XPL = 16 * XPR / 64;      // Xt pieces per row / per lane
+        constexpr int HPL = KS * FQ, XPL = 2 * FQ;  // 16-byte pieces per lane per chunk
         const unsigned ls0 = lds_addr(LS), lx0 = lds_addr(LX);
         auto xoff = [](int b, int ln) { return (unsigned)(b * SS::XBLK + ln * (int)sizeof(Frag<T>) + (ln >> 4) * 16); };
         unsigned hla[HPL], xla[XPL];  // LDS byte addresses
         unsigned hgo[HPL], xgo[XPL];  // byte offsets in the chunk-head's Ht / Xt block
 #pragma unroll
         for (int t = 0; t < HPL; ++t) {
-            const int q = lane + 64 * t, cl = q / HPR, pc = q % HPR;
-            if constexpr (EB == 2) {  // piece pc: d_k 8 pc .. 8 pc + 7
-                const int ks = pc >> 2, a = pc & 3;
-                hla[t] = ls0 + xoff(ks, 32 * (a & 1) + cl) + 8 * (a >> 1);
-            } else {  // piece pc: d_k 4 pc .. 4 pc + 3
-                const int ks = pc >> 3, hh = (pc >> 2) & 1, g = pc & 3;
-                hla[t] = ls0 + xoff(ks, 16 * g + cl) + 16 * hh;
-            }
-            hgo[t] = (unsigned)((16 * tile + cl) * D * EB + 16 * pc);
+            const int ks = t / FQ, e = t % FQ;  // piece: d_k 32 ks + 8 grp + 4 e .. (bf16: 8 values, e = 0)
+            if constexpr (EB == 2)
+                hla[t] = ls0 + xoff(ks, 32 * (grp & 1) + r16) + 8 * (grp >> 1);
+            else
+                hla[t] = ls0 + xoff(ks, 16 * (2 * (grp & 1) + e) + r16) + 16 * (grp >> 1);
+            hgo[t] = (unsigned)(((tile * KS + ks) * 64 + lane) * 8 * EB + 16 * e);
         }
 #pragma unroll
         for (int t = 0; t < XPL; ++t) {
-            const int q = lane + 64 * t, cl = q / XPR, pc = q % XPR;
-            const int j = pc / (4 * FQ), g = (pc / FQ) % 4, e = pc % FQ;
-            xla[t] = lx0 + xoff(j, 16 * g + cl) + 16 * e;
-            xgo[t] = (unsigned)((16 * tile + cl) * CHUNK * EB + 16 * pc);
+            const int j = t / FQ, e = t % FQ;  // piece: stored positions 32 j + 8 grp + 4 e ..
+            xla[t] = lx0 + xoff(j, 16 * grp + r16) + 16 * e;
+            xgo[t] = (unsigned)(((tile * 2 + j) * 64 + lane) * 8 * EB + 16 * e);
         }
         // L2 prefetch: once a step, this tile's share of the W and K lines of
         // chunk c + PF (4 bytes per line, into a sink nobody reads).  The tiles of
@@ -996,11 +994,11 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
     Frag<T> hf[TPW][KS], xf[TPW][2];
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
-        const int dv = 16 * (w * TPW + tt) + r16;
+        const int m = w * TPW + tt;  // d_v tile
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) load8(hf[tt][ks], Hb + (size_t)dv * D + 32 * ks + 8 * grp);
+        for (int ks = 0; ks < KS; ++ks) load8(hf[tt][ks], Hb + ((size_t)(m * KS + ks) * 64 + lane) * 8);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) load8(xf[tt][ks], Xb + (size_t)dv * CHUNK + 32 * ks + 8 * grp);
+        for (int ks = 0; ks < 2; ++ks) load8(xf[tt][ks], Xb + ((size_t)(m * 2 + ks) * 64 + lane) * 8);
     }
     // Gated read-out: this lane's z values of one position tile (rows past the
     // valid length re-read the last valid row; they are never stored) and the

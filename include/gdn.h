@@ -73,7 +73,7 @@ enum {
  * numbered in sequence order, each sequence's chunks starting at its own first
  * token, so chunk c of sequence n has global index chunk_offset(n) + c where
  * chunk_offset(n) = sum_{m<n} ceil(L_m / 64).  Positions beyond a tail chunk's
- * valid length hold zeros.  Two regions are kept in the order in which the
+ * valid length hold zeros.  W, U, Ht and Xt are kept in the order in which the
  * MFMA units consume them ("fragment order", 8 values per lane of a 64-lane
  * wave; for an index i let i = 32 s + 16 h + 4 a + b with a, b in 0..3):
  *   W   element (pos, k):  ((pos/16 * (d_k/32) + s(k)) * 64 + 16 a(k) + pos%16) * 8 + 4 h(k) + b(k)
@@ -96,8 +96,10 @@ enum {
  *                                            with P = d_k * sizeof(dtype) / 16 pieces a row
  *                                            p(r) = 2 (r mod P/2) for bf16 and
  *                                            4 ((r / 4) mod P/4) for fp32
- *   Ht  dtype [n_chunks][H_v][d_v][d_k]      (state at chunk start)^T
- *   Xt  dtype [n_chunks][H_v][d_v][64]       (U - W S)^T, last index perm32
+ *   Ht  dtype [n_chunks][H_v][d_v * d_k]     (state at chunk start)^T, element (j, k) at
+ *                                            ((j/16 * (d_k/32) + k/32) * 64 + 16 ((k%32)/8) + j%16) * 8 + k%8
+ *   Xt  dtype [n_chunks][H_v][d_v * 64]      (U - W S)^T, element (j, pos) at the same place
+ *                                            with d_k -> 64 and k -> perm32(pos)
  */
 typedef struct gdn_workspace_layout {
     int64_t n_chunks;

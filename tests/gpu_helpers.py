@@ -59,6 +59,15 @@ def frag_w_to_logical(flat, d_k):
     return flat[..., off]
 
 
+def frag_rows_to_logical(flat, rows, cols):
+    """[..., rows*cols] in the row-operand fragment order of Ht / Xt (block (row/16,
+    col/32), lane 16 ((col%32)/8) + row%16, slot col%8) -> [..., rows, cols]."""
+    r = np.arange(rows)[:, None]
+    c = np.arange(cols)[None, :]
+    off = ((r // 16 * (cols // 32) + c // 32) * 64 + 16 * ((c % 32) // 8) + r % 16) * 8 + c % 8
+    return flat[..., off]
+
+
 def frag_u_to_logical(flat, d_v):
     """U [..., 64*d_v] in accumulator order -> [..., 64, d_v]."""
     pos = np.arange(64)[:, None]

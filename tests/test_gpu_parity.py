@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import gdn_inputs
-from tests.gpu_helpers import (chunk_fwd_device, f32_dev, frag_u_to_logical, frag_w_to_logical,
+from tests.gpu_helpers import (chunk_fwd_device, f32_dev, frag_rows_to_logical, frag_u_to_logical, frag_w_to_logical,
                                rel_err, to_dev, to_host, unperm32)
 
 pytestmark = pytest.mark.gpu
@@ -201,8 +201,8 @@ def test_chunk_intermediates_match_chunk_form(torch_cuda, dtype, d, tol):
         Kc[:, :, r, np.arange(P) ^ pr] = Kc_st[:, :, r]
     Kc = Kc.reshape(nc, H_q, 64, d)
     k_in = inp.k32()
-    Hs = np.swapaxes(region(lay["off_Ht"], (nc, H_v, d, d)), -1, -2)
-    X = np.swapaxes(unperm32(region(lay["off_Xt"], (nc, H_v, d, 64))), -1, -2)
+    Hs = np.swapaxes(frag_rows_to_logical(region(lay["off_Ht"], (nc, H_v, d * d)), d, d), -1, -2)
+    X = np.swapaxes(unperm32(frag_rows_to_logical(region(lay["off_Xt"], (nc, H_v, d * 64)), d, 64)), -1, -2)
 
     ref = chunk_form.chunk_forward(inp.q32(), inp.k32(), inp.v32(), inp.g, inp.beta, inp.cu_seqlens, H_q, H_v,
                                    inp.scale, initial_state=inp.initial_state, keep_intermediates=True)
