@@ -941,6 +941,8 @@ struct OutLds {
         struct {
             Frag<T> P[4][2][64];  // B operand of (U - W S)^T P^T: [query tile][K-step][lane]
             float ss[4][CHUNK];   // gated read-out: per-wave sums of o^2 per position
+            T os[2][16][D];       // one position tile of O (rows: positions), two buffers;
+                                  // 16-byte piece i of row r stored at i ^ (r % pieces)
         } pr;
     } u;
     float gc[CHUNK];
@@ -1000,24 +1002,36 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) load8(xf[tt][ks], Xb + ((size_t)(m * 2 + ks) * 64 + lane) * 8);
     }
-    // Gated read-out: this lane's z values of one position tile (rows past the
-    // valid length re-read the last valid row; they are never stored) and the
-    // norm weights.  Tile 0's z goes out after the Q/K staging (so those loads are
-    // not queued behind it); each later tile's while the previous one is computed.
-    Raw4<T> zc[GATED ? TPW : 1], zn[GATED ? TPW : 1];
-    float4 wv[GATED ? TPW : 1];
+    // Read-out: each position tile of O is staged in LDS and leaves as whole
+    // 16-byte pieces of rows, wave w storing rows 4 w .. 4 w + 3 (piece q of
+    // the wave: row 4 w + q / PPR, piece q % PPR), so a store instruction
+    // writes consecutive bytes of a row.  With the gated read-out the same
+    // lanes load the matching pieces of z (rows past the valid length re-read
+    // the last valid row; they are never stored) and apply the norm there; a
+    // lane's pieces all have the same columns, so its norm weights are loaded
+    // once.  Tile 0's z goes out after the Q/K staging (so those loads are not
+    // queued behind it); each later tile's while the previous one is computed.
+    constexpr int VE = 16 / (int)sizeof(T);         // elements per piece
+    constexpr int PPR = D / VE;                     // pieces per row
+    constexpr int PL = (4 * PPR + 63) / 64;         // pieces per lane
+    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+    u32x4_t zc[GATED ? PL : 1], zn[GATED ? PL : 1];
+    float wvp[GATED ? VE : 1];
     const T* zb = GATED ? reinterpret_cast<const T*>(p.gz) + (size_t)cp.t0 * p.H_v * D + (size_t)h * D : nullptr;
-    auto load_z = [&](Raw4<T>(&zz)[GATED ? TPW : 1], int nt) {
-        const int pos = min(16 * nt + r16, ell - 1);
+    auto load_z = [&](u32x4_t(&zz)[GATED ? PL : 1], int nt) {
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt)
-            load_raw4(zz[tt], zb + (size_t)pos * p.H_v * D + 16 * (w * TPW + tt) + 4 * grp);
+        for (int u = 0; u < PL; ++u) {
+            const int q = lane + 64 * u;
+            if (q < 4 * PPR) {
+                const int pos = min(16 * nt + 4 * w + q / PPR, ell - 1);
+                zz[u] = *reinterpret_cast<const u32x4_t*>(zb + (size_t)pos * p.H_v * D + (q % PPR) * VE);
+            }
+        }
     };
     if constexpr (GATED) {
         load_z(zc, 0);
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt)
-            wv[tt] = *reinterpret_cast<const float4*>(p.gw + 16 * (w * TPW + tt) + 4 * grp);
+        for (int e = 0; e < VE; ++e) wvp[e] = p.gw[(lane % PPR) * VE + e];
     }
 
     // P^T tiles (I, J = w) for I <= w, held in registers until every wave is
@@ -1079,7 +1093,7 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
         pf[1] = s.u.pr.P[nt][1][lane];
         const int pos = 16 * nt + r16;
         const float eg = __expf(s.gc[pos]);
-        f32x4 ov[TPW];
+        float ssq = 0.f;
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
             f32x4 inter = zero4(), intra = zero4();
@@ -1087,40 +1101,67 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
             for (int ks = 0; ks < KS; ++ks) inter = mma(hf[tt][ks], qf[ks], inter);
             intra = mma(xf[tt][0], pf[0], intra);
             if (nt >= 2) intra = mma(xf[tt][1], pf[1], intra);  // P^T rows 32..63 vanish for queries < 32
+            f32x4 ov;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ov[tt][i] = p.scale * (eg * inter[i] + intra[i]);
-            if constexpr (!GATED) {
-                if (pos < ell)
-                    store4(ob + (size_t)pos * p.H_v * D + 16 * (w * TPW + tt) + 4 * grp, ov[tt][0], ov[tt][1],
-                           ov[tt][2], ov[tt][3]);
+            for (int i = 0; i < 4; ++i) ov[i] = p.scale * (eg * inter[i] + intra[i]);
+            if constexpr (GATED) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ssq += ov[i] * ov[i];
             }
+            // 4 values of row r16 (position), columns 16 (w TPW + tt) + 4 grp ..
+            const int col = 16 * (w * TPW + tt) + 4 * grp;
+            store4(&s.u.pr.os[nt & 1][r16][((col / VE) ^ (r16 % PPR)) * VE + col % VE], ov[0], ov[1], ov[2], ov[3]);
         }
-        if constexpr (GATED) {
-            float ssq = 0.f;
-#pragma unroll
-            for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ssq += ov[tt][i] * ov[tt][i];
+        if constexpr (GATED) {  // this wave's share of each position's sum of o^2 over d_v
             ssq += wave_shfl_xor(ssq, 16);
             ssq += wave_shfl_xor(ssq, 32);
             if (grp == 0) s.u.pr.ss[w][pos] = ssq;
-            lds_sync();
-            const float rstd =
-                1.f / sqrtf((s.u.pr.ss[0][pos] + s.u.pr.ss[1][pos] + s.u.pr.ss[2][pos] + s.u.pr.ss[3][pos]) * (1.f / D) +
-                            p.geps);
-            if (pos < ell) {
+        }
+        // One barrier a tile: buffer nt & 1 is rewritten two tiles later, after
+        // the next tile's barrier.
+        lds_sync();
 #pragma unroll
-                for (int tt = 0; tt < TPW; ++tt) {
-                    const f32x4 zf = raw4_to_f32(zc[tt]);
-                    const float wf[4] = {wv[tt].x, wv[tt].y, wv[tt].z, wv[tt].w};
-                    float y[4];
+        for (int u = 0; u < PL; ++u) {
+            const int q = lane + 64 * u;
+            if (q < 4 * PPR) {
+                const int row = 4 * w + q / PPR, pc = q % PPR, pr = 16 * nt + row;
+                const float4 raw = *reinterpret_cast<const float4*>(&s.u.pr.os[nt & 1][row][(pc ^ (row % PPR)) * VE]);
+                float4 outv = raw;
+                if constexpr (GATED) {
+                    const float rstd =
+                        1.f / sqrtf((s.u.pr.ss[0][pr] + s.u.pr.ss[1][pr] + s.u.pr.ss[2][pr] + s.u.pr.ss[3][pr]) *
+                                        (1.f / D) + p.geps);
+                    float o[VE], zf[VE];
+                    if constexpr (sizeof(T) == 2) {
+                        const bf16x8 ob8 = __builtin_bit_cast(bf16x8, raw), zb8 = __builtin_bit_cast(bf16x8, zc[u]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) y[i] = ov[tt][i] * rstd * wf[i] * silu_f32(zf[i]);
-                    store4(ob + (size_t)pos * p.H_v * D + 16 * (w * TPW + tt) + 4 * grp, y[0], y[1], y[2], y[3]);
+                        for (int e = 0; e < VE; ++e) {
+                            o[e] = (float)ob8[e];
+                            zf[e] = (float)zb8[e];
+                        }
+                    } else {
+                        const float4 zz = __builtin_bit_cast(float4, zc[u]);
+                        o[0] = raw.x; o[1] = raw.y; o[2] = raw.z; o[3] = raw.w;
+                        zf[0] = zz.x; zf[1] = zz.y; zf[2] = zz.z; zf[3] = zz.w;
+                    }
+                    float y[VE];
+#pragma unroll
+                    for (int e = 0; e < VE; ++e) y[e] = o[e] * rstd * wvp[e] * silu_f32(zf[e]);
+                    if constexpr (sizeof(T) == 2) {
+                        bf16x8 yb;
+#pragma unroll
+                        for (int e = 0; e < VE; ++e) yb[e] = (bf16)y[e];
+                        outv = __builtin_bit_cast(float4, yb);
+                    } else {
+                        outv = make_float4(y[0], y[1], y[2], y[3]);
+                    }
                 }
+                if (pr < ell) *reinterpret_cast<float4*>(ob + (size_t)pr * p.H_v * D + pc * VE) = outv;
             }
+        }
+        if constexpr (GATED) {
 #pragma unroll
-            for (int tt = 0; tt < TPW; ++tt) zc[tt] = zn[tt];
+            for (int u = 0; u < PL; ++u) zc[u] = zn[u];
         }
     }
 }
