@@ -127,7 +127,7 @@ __host__ __device__ constexpr int blk(int I, int J) { return (I * (I + 1) / 2 + 
 
 template <typename T, int D>
 struct PrepLds {
-    static constexpr int KP = D + 16 / (int)sizeof(T);  // padded row, 16-byte aligned
+    static constexpr int KP = D + 32 / (int)sizeof(T);  // padded row (32 bytes: the transposed column reads hit distinct banks)
     T K[CHUNK][KP];
     union {
         struct {
