@@ -496,11 +496,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
 //    Store wave.  Copies h_c (the sign-flipped -S of LS, between B1(c) and
 //    B2(c)) and X_c (LX, between B2(c) and B1(c + 1)) to HBM.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, int CT = 1>
 struct StateStage {
     static constexpr int W_BYTES = CHUNK * D * (int)sizeof(T);
     static constexpr int K_BYTES = CHUNK * D * (int)sizeof(T);   // K rows, row-major (pieces permuted by kswz)
-    static constexpr int U_BYTES = 4 * 64 * 4 * (int)sizeof(T);  // one 16-column tile
+    static constexpr int U1_BYTES = 4 * 64 * 4 * (int)sizeof(T); // one 16-column tile of U
+    static constexpr int U_BYTES = CT * U1_BYTES;                // the workgroup's CT tiles
     static constexpr int G_BYTES = 2 * CHUNK * 4;                // gc, then kf
     static constexpr int BYTES = W_BYTES + K_BYTES + U_BYTES + G_BYTES;
     static constexpr int NPIECE = (W_BYTES + K_BYTES + U_BYTES) / 1024;    // 1 KiB loads per chunk (+ gates)
@@ -508,7 +509,7 @@ struct StateStage {
     // padding after every 16 lanes so that the store wave's column gathers
     // spread over the LDS banks.
     static constexpr int XBLK = 64 * 8 * (int)sizeof(T) + 4 * 16;
-    static constexpr int EXCH = (D / 32 + 4) * XBLK;
+    static constexpr int EXCH = (D / 32 + 4) * CT * XBLK;
     // A wave can keep at most 63 vector-memory operations in flight, so the
     // stream is split over NPW producer waves, each owning every NPW-th piece,
     // with one chunk's share (plus the two gate loads) within that limit.
@@ -573,16 +574,16 @@ __device__ __forceinline__ void lds_wait_untracked(u32x4* r) {
 // chunk's direct-to-LDS loads; part 0 issues the first half of the share,
 // part 1 the rest and the two 256-byte gate blocks gc and kf (producer
 // wave 0).  ch: (chunk, value head) index; kch: (chunk, key head) index of Kc.
-template <typename T, int D>
+template <typename T, int D, int CT>
 __device__ __forceinline__ void state_issue(char* stage, const ChunkParams& p, size_t ch, size_t kch, int tile,
                                             int lane, int pw, int part) {
-    using SS = StateStage<T, D>;
+    using SS = StateStage<T, D, CT>;
     constexpr int NT = D / 16;
     constexpr int NW = SS::W_BYTES / 1024, NK = SS::K_BYTES / 1024;
     constexpr int NP = SS::NPIECE;
     const char* wg = reinterpret_cast<const char*>(p.W) + ch * SS::W_BYTES;
     const char* kg = reinterpret_cast<const char*>(p.Kc) + kch * SS::K_BYTES;
-    const char* ug = reinterpret_cast<const char*>(p.Ut) + (ch * NT + tile) * SS::U_BYTES;
+    const char* ug = reinterpret_cast<const char*>(p.Ut) + (ch * NT + CT * tile) * SS::U1_BYTES;
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
         if (j % SS::NPW != pw) continue;
@@ -603,9 +604,9 @@ __device__ __forceinline__ void state_issue(char* stage, const ChunkParams& p, s
 
 // Loads producer wave pw issues in part 0 / part 1 of a chunk (part 1
 // includes the two gate loads of wave 0).
-template <typename T, int D>
+template <typename T, int D, int CT>
 __host__ __device__ constexpr int state_part_loads(int pw, int part) {
-    using SS = StateStage<T, D>;
+    using SS = StateStage<T, D, CT>;
     int n = 0;
     for (int j = 0; j < SS::NPIECE; ++j) n += (j % SS::NPW == pw && (j < SS::NPIECE / 2) == (part == 0)) ? 1 : 0;
     return n + (part == 1 && pw == 0 ? 2 : 0);
@@ -614,11 +615,11 @@ __host__ __device__ constexpr int state_part_loads(int pw, int part) {
 // vmcnt bounds of producer wave pw: ops younger than chunk c + 1's last load
 // when part 0 of chunk c + NST has just gone out (chunks c + 2 .. c + NST - 1
 // whole, plus that part 0), and the in-flight ceiling before part 1 goes out.
-template <typename T, int D>
+template <typename T, int D, int CT>
 __host__ __device__ constexpr int state_wait_b2(int pw) {
-    using SS = StateStage<T, D>;
-    return (SS::NST - 2) * (state_part_loads<T, D>(pw, 0) + state_part_loads<T, D>(pw, 1)) +
-           state_part_loads<T, D>(pw, 0);
+    using SS = StateStage<T, D, CT>;
+    return (SS::NST - 2) * (state_part_loads<T, D, CT>(pw, 0) + state_part_loads<T, D, CT>(pw, 1)) +
+           state_part_loads<T, D, CT>(pw, 0);
 }
 // Write a D tile's four values (rows 4 grp + i of one 16-row tile) into the
 // perm32 fragment they belong to: even tile -> slots 0..3, odd -> slots 4..7.
@@ -667,10 +668,11 @@ __device__ __forceinline__ Frag<T> k_col_frag(const char* kst, int m, int ks, in
     return f;
 }
 
-template <typename T, int D, bool DEV>
+template <typename T, int D, bool DEV, int CT>
 __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p, int padded) {
-    using SS = StateStage<T, D>;
+    using SS = StateStage<T, D, CT>;
     constexpr int NT = D / 16;   // column tiles of d_v per head
+    constexpr int NTW = NT / CT; // workgroups per head (CT column tiles each)
     constexpr int KS = D / 32;   // contraction steps over d_k
     constexpr int TPW = D / 64;  // S row tiles per compute wave
     constexpr int NST = SS::NST;
@@ -680,14 +682,13 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
     // XCD gets an even share of long and short sequences.
     (void)padded;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int gi = (slot / NT) * 8 + xcd;
+    const int gi = (slot / NTW) * 8 + xcd;
     const SeqTable& tab = DEV ? *p.dtab : p.tab;
     if (gi >= tab.num_seqs * p.H_v) return;
-    const int tile = slot % NT;
+    const int tile = slot % NTW;  // column tiles CT tile .. CT tile + CT - 1
     const int h = gi % p.H_v, n = tab.order[gi / p.H_v];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
-    const int col = 16 * tile + r16;
     const int si = tab.s_in[n], so = tab.s_out[n];  // state rows (-1: zeros / not kept)
     const size_t in_off = ((size_t)max(si, 0) * p.H_v + h) * D * D;
     const size_t out_off = ((size_t)max(so, 0) * p.H_v + h) * D * D;
@@ -699,9 +700,9 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
     auto kch = [&](int c) { return (size_t)(c0 + c) * p.H_q + hq; };
 
     __shared__ __attribute__((aligned(16))) char smem[NST * SS::BYTES + SS::EXCH + 256];  // + L2-prefetch sink
-    char* const LS = smem + NST * SS::BYTES;  // KS blocks: -S
-    char* const LX = LS + KS * SS::XBLK;      // 2 blocks: X
-    char* const LY = LX + 2 * SS::XBLK;       // 2 blocks: kf X
+    char* const LS = smem + NST * SS::BYTES;  // KS x CT blocks: -S (block ks CT + ct)
+    char* const LX = LS + KS * CT * SS::XBLK; // 2 x CT blocks: X (block j CT + ct)
+    char* const LY = LX + 2 * CT * SS::XBLK;  // 2 x CT blocks: kf X
     // fragment of lane ln in block b of an exchange buffer
     auto xf = [](char* buf, int b, int ln) -> Frag<T>& {
         return *reinterpret_cast<Frag<T>*>(buf + b * SS::XBLK + ln * (int)sizeof(Frag<T>) + (ln >> 4) * 16);
@@ -730,22 +731,26 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         constexpr int HPL = KS * FQ, XPL = 2 * FQ;  // 16-byte pieces per lane per chunk
         const unsigned ls0 = lds_addr(LS), lx0 = lds_addr(LX);
         auto xoff = [](int b, int ln) { return (unsigned)(b * SS::XBLK + ln * (int)sizeof(Frag<T>) + (ln >> 4) * 16); };
-        unsigned hla[HPL], xla[XPL];  // LDS byte addresses
-        unsigned hgo[HPL], xgo[XPL];  // byte offsets in the chunk-head's Ht / Xt block
+        unsigned hla[CT][HPL], xla[CT][XPL];  // LDS byte addresses
+        unsigned hgo[CT][HPL], xgo[CT][XPL];  // byte offsets in the chunk-head's Ht / Xt block
 #pragma unroll
-        for (int t = 0; t < HPL; ++t) {
-            const int ks = t / FQ, e = t % FQ;  // piece: d_k 32 ks + 8 grp + 4 e .. (bf16: 8 values, e = 0)
-            if constexpr (EB == 2)
-                hla[t] = ls0 + xoff(ks, 32 * (grp & 1) + r16) + 8 * (grp >> 1);
-            else
-                hla[t] = ls0 + xoff(ks, 16 * (2 * (grp & 1) + e) + r16) + 16 * (grp >> 1);
-            hgo[t] = (unsigned)(((tile * KS + ks) * 64 + lane) * 8 * EB + 16 * e);
-        }
+        for (int ct = 0; ct < CT; ++ct) {
+            const int ctile = CT * tile + ct;  // d_v tile
 #pragma unroll
-        for (int t = 0; t < XPL; ++t) {
-            const int j = t / FQ, e = t % FQ;  // piece: stored positions 32 j + 8 grp + 4 e ..
-            xla[t] = lx0 + xoff(j, 16 * grp + r16) + 16 * e;
-            xgo[t] = (unsigned)(((tile * 2 + j) * 64 + lane) * 8 * EB + 16 * e);
+            for (int t = 0; t < HPL; ++t) {
+                const int ks = t / FQ, e = t % FQ;  // piece: d_k 32 ks + 8 grp + 4 e .. (bf16: 8 values, e = 0)
+                if constexpr (EB == 2)
+                    hla[ct][t] = ls0 + xoff(ks * CT + ct, 32 * (grp & 1) + r16) + 8 * (grp >> 1);
+                else
+                    hla[ct][t] = ls0 + xoff(ks * CT + ct, 16 * (2 * (grp & 1) + e) + r16) + 16 * (grp >> 1);
+                hgo[ct][t] = (unsigned)(((ctile * KS + ks) * 64 + lane) * 8 * EB + 16 * e);
+            }
+#pragma unroll
+            for (int t = 0; t < XPL; ++t) {
+                const int j = t / FQ, e = t % FQ;  // piece: stored positions 32 j + 8 grp + 4 e ..
+                xla[ct][t] = lx0 + xoff(j * CT + ct, 16 * grp + r16) + 16 * e;
+                xgo[ct][t] = (unsigned)(((ctile * 2 + j) * 64 + lane) * 8 * EB + 16 * e);
+            }
         }
         // L2 prefetch: once a step, this tile's share of the W and K lines of
         // chunk c + PF (4 bytes per line, into a sink nobody reads).  The tiles of
@@ -754,41 +759,57 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         // than from the Infinity Cache (long or many sequences), and costs a few
         // per cent where it does not, so the launcher enables it by size.
         constexpr int PF = 6;
-        constexpr int LPT = SS::W_BYTES / 128 / NT;  // lines of W (and of K) per tile
-        static_assert(2 * LPT <= 64, "one line per lane");
-        const int li = tile * LPT + lane % LPT;
-        const bool k_line = (lane / LPT) & 1;
+        constexpr int LPT = SS::W_BYTES / 128 / NTW;  // lines of W (and of K) per workgroup
+        constexpr int NPL = (2 * LPT + 63) / 64;      // prefetch loads per lane (W lines, then K lines)
         asm volatile("s_barrier" ::: "memory");  // B0
         for (int c = 0; c < nch; ++c) {
             const size_t ch = (size_t)(c0 + c) * p.H_v + h;
             asm volatile("s_barrier" ::: "memory");  // B1(c)
             if (p.l2_prefetch && c + PF < nch) {
                 const size_t chp = (size_t)(c0 + c + PF) * p.H_v + h;
-                const char* a = k_line ? reinterpret_cast<const char*>(p.Kc) + kch(c + PF) * SS::K_BYTES + li * 128
-                                       : reinterpret_cast<const char*>(p.W) + chp * SS::W_BYTES + li * 128;
-                __builtin_amdgcn_global_load_lds((gptr_t)a, (lptr_t)(smem + NST * SS::BYTES + SS::EXCH), 4, 0, 0);
+#pragma unroll
+                for (int q = 0; q < NPL; ++q) {
+                    const int L = lane + 64 * q;
+                    if (L < 2 * LPT) {
+                        const int li = tile * LPT + L % LPT;
+                        const char* a = L >= LPT
+                                            ? reinterpret_cast<const char*>(p.Kc) + kch(c + PF) * SS::K_BYTES + li * 128
+                                            : reinterpret_cast<const char*>(p.W) + chp * SS::W_BYTES + li * 128;
+                        __builtin_amdgcn_global_load_lds((gptr_t)a, (lptr_t)(smem + NST * SS::BYTES + SS::EXCH), 4, 0,
+                                                         0);
+                    }
+                }
             }
             // h_c = -(LS): a sign flip, exact
-            u32x4 hv[HPL];
+            u32x4 hv[CT * HPL];
 #pragma unroll
-            for (int t = 0; t < HPL; ++t) {
-                if constexpr (EB == 2)  // the two halves, 16 lanes (272 bytes) apart, in one read
-                    asm volatile("ds_read2_b64 %0, %1 offset1:34" : "=v"(hv[t]) : "v"(hla[t]));
-                else
-                    asm volatile("ds_read_b128 %0, %1" : "=v"(hv[t]) : "v"(hla[t]));
-            }
-            lds_wait_untracked<HPL>(hv);
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int t = 0; t < HPL; ++t) {
+                    if constexpr (EB == 2)  // the two halves, 16 lanes (272 bytes) apart, in one read
+                        asm volatile("ds_read2_b64 %0, %1 offset1:34" : "=v"(hv[ct * HPL + t]) : "v"(hla[ct][t]));
+                    else
+                        asm volatile("ds_read_b128 %0, %1" : "=v"(hv[ct * HPL + t]) : "v"(hla[ct][t]));
+                }
+            lds_wait_untracked<CT * HPL>(hv);
             char* Hb = reinterpret_cast<char*>(p.Ht) + ch * D * D * EB;
 #pragma unroll
-            for (int t = 0; t < HPL; ++t) *reinterpret_cast<u32x4*>(Hb + hgo[t]) = hv[t] ^ sgn;
-            asm volatile("s_barrier" ::: "memory");  // B2(c)
-            u32x4 xv[XPL];
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int t = 0; t < XPL; ++t) asm volatile("ds_read_b128 %0, %1" : "=v"(xv[t]) : "v"(xla[t]));
-            lds_wait_untracked<XPL>(xv);
+                for (int t = 0; t < HPL; ++t) *reinterpret_cast<u32x4*>(Hb + hgo[ct][t]) = hv[ct * HPL + t] ^ sgn;
+            asm volatile("s_barrier" ::: "memory");  // B2(c)
+            u32x4 xv[CT * XPL];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int t = 0; t < XPL; ++t)
+                    asm volatile("ds_read_b128 %0, %1" : "=v"(xv[ct * XPL + t]) : "v"(xla[ct][t]));
+            lds_wait_untracked<CT * XPL>(xv);
             char* Xb = reinterpret_cast<char*>(p.Xt) + ch * D * CHUNK * EB;  // X_c, already in the stored perm32 order
 #pragma unroll
-            for (int t = 0; t < XPL; ++t) *reinterpret_cast<u32x4*>(Xb + xgo[t]) = xv[t];
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int t = 0; t < XPL; ++t) *reinterpret_cast<u32x4*>(Xb + xgo[ct][t]) = xv[ct * XPL + t];
         }
         wait_vmcnt<0>();  // no prefetch may land in LDS after the workgroup has ended
         return;
@@ -799,10 +820,10 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         // Outstanding-load bounds (vmcnt counts at most 63): before k loads go
         // out at most 63 - k may be in flight (R*_), and at B2(c) chunk c + 1
         // must have landed (WB_).
-        constexpr int WB_0 = state_wait_b2<T, D>(0), WB_1 = state_wait_b2<T, D>(1);
-        constexpr int R0_0 = 63 - state_part_loads<T, D>(0, 0), R0_1 = 63 - state_part_loads<T, D>(1, 0);
-        constexpr int R1_0 = 63 - state_part_loads<T, D>(0, 1), R1_1 = 63 - state_part_loads<T, D>(1, 1);
-        constexpr int RC_0 = R0_0 - state_part_loads<T, D>(0, 1), RC_1 = R0_1 - state_part_loads<T, D>(1, 1);
+        constexpr int WB_0 = state_wait_b2<T, D, CT>(0), WB_1 = state_wait_b2<T, D, CT>(1);
+        constexpr int R0_0 = 63 - state_part_loads<T, D, CT>(0, 0), R0_1 = 63 - state_part_loads<T, D, CT>(1, 0);
+        constexpr int R1_0 = 63 - state_part_loads<T, D, CT>(0, 1), R1_1 = 63 - state_part_loads<T, D, CT>(1, 1);
+        constexpr int RC_0 = R0_0 - state_part_loads<T, D, CT>(0, 1), RC_1 = R0_1 - state_part_loads<T, D, CT>(1, 1);
         static_assert(WB_0 < 64 && WB_1 < 64 && RC_0 >= 0 && RC_1 >= 0, "producer loads exceed the vmcnt range");
         // Chunks 0 .. NST-1 up front; chunk 0 lands before B0.
 #pragma unroll
@@ -813,8 +834,8 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
             }
             if (b < nch) {
                 const size_t chb = (size_t)(c0 + b) * p.H_v + h;
-                state_issue<T, D>(smem + b * SS::BYTES, p, chb, kch(b), tile, lane, pw, 0);
-                state_issue<T, D>(smem + b * SS::BYTES, p, chb, kch(b), tile, lane, pw, 1);
+                state_issue<T, D, CT>(smem + b * SS::BYTES, p, chb, kch(b), tile, lane, pw, 0);
+                state_issue<T, D, CT>(smem + b * SS::BYTES, p, chb, kch(b), tile, lane, pw, 1);
             }
         }
         // The producers' barriers are plain s_barrier: a workgroup release fence
@@ -833,7 +854,7 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
             // chunk c + 1 is read after B2(c).
             if (cn < nch) {
                 if (pw == 0) wait_vmcnt<R0_0>(); else wait_vmcnt<R0_1>();
-                state_issue<T, D>(stn, p, chn, kch(cn), tile, lane, pw, 0);
+                state_issue<T, D, CT>(stn, p, chn, kch(cn), tile, lane, pw, 0);
                 if (pw == 0) wait_vmcnt<WB_0>(); else wait_vmcnt<WB_1>();
             } else {
                 wait_vmcnt<0>();
@@ -841,25 +862,29 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
             asm volatile("s_barrier" ::: "memory");  // B2(c)
             if (cn < nch) {
                 if (pw == 0) wait_vmcnt<R1_0>(); else wait_vmcnt<R1_1>();
-                state_issue<T, D>(stn, p, chn, kch(cn), tile, lane, pw, 1);
+                state_issue<T, D, CT>(stn, p, chn, kch(cn), tile, lane, pw, 1);
             }
         }
         return;
     }
 
     // ---------------- compute waves ----------------
-    f32x4 S[TPW];
+    f32x4 S[TPW][CT];
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
         const int m = w * TPW + tt;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[tt][i] = si >= 0 ? p.s0[in_off + (size_t)(16 * m + 4 * grp + i) * D + col] : 0.f;
-        lds_put4(xf(LS, m >> 1, lane), m & 1, S[tt], -1.f);
+        for (int ct = 0; ct < CT; ++ct) {
+            const int col = 16 * (CT * tile + ct) + r16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[tt][ct][i] = si >= 0 ? p.s0[in_off + (size_t)(16 * m + 4 * grp + i) * D + col] : 0.f;
+            lds_put4(xf(LS, (m >> 1) * CT + ct, lane), m & 1, S[tt][ct], -1.f);
+        }
     }
     // Operand fragments of one chunk, read from its LDS stage.
     Frag<T> wf[KS], kfg[TPW][2];
-    Raw4<T> uf;
+    Raw4<T> uf[CT];
     float gl = 0.f;
     float4 fx;  // kf of this wave's X rows (positions 16 w + 4 grp + i)
     auto read_stage = [&](int c) {
@@ -874,7 +899,8 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) kfg[tt][ks] = k_col_frag<T, D>(Kst, w * TPW + tt, ks, lane);
-        uf = Ust[((w >> 1) * 64 + lane) * 2 + (w & 1)];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) uf[ct] = Ust[ct * (SS::U1_BYTES / (int)sizeof(Raw4<T>)) + ((w >> 1) * 64 + lane) * 2 + (w & 1)];
         gl = Gst[min(CHUNK, L_n - c * CHUNK) - 1];
         fx = *reinterpret_cast<const float4*>(Gst + CHUNK + 16 * w + 4 * grp);
     };
@@ -882,19 +908,30 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
     if (nch > 0) read_stage(0);
     for (int c = 0; c < nch; ++c) {
         lds_sync();  // B1(c): -S in LS; chunk c's stage may be refilled
-        Frag<T> sb[KS];
+        Frag<T> sb[CT][KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sb[ks] = xf(LS, ks, lane);
-        // X = U - W S for positions 16 w .. 16 w + 15
-        f32x4 X = raw4_to_f32(uf);
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) X = mma(wf[ks], sb[ks], X);
-        lds_put4(xf(LX, w >> 1, lane), w & 1, X, 1.f);
-        const f32x4 Y = f32x4{X[0] * fx.x, X[1] * fx.y, X[2] * fx.z, X[3] * fx.w};
-        lds_put4(xf(LY, w >> 1, lane), w & 1, Y, 1.f);
+            for (int ks = 0; ks < KS; ++ks) sb[ct][ks] = xf(LS, ks * CT + ct, lane);
+        // X = U - W S for positions 16 w .. 16 w + 15 (one independent chain per column tile)
+        f32x4 X[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) X[ct] = raw4_to_f32(uf[ct]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) X[ct] = mma(wf[ks], sb[ct][ks], X[ct]);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            lds_put4(xf(LX, (w >> 1) * CT + ct, lane), w & 1, X[ct], 1.f);
+            const f32x4 Y = f32x4{X[ct][0] * fx.x, X[ct][1] * fx.y, X[ct][2] * fx.z, X[ct][3] * fx.w};
+            lds_put4(xf(LY, (w >> 1) * CT + ct, lane), w & 1, Y, 1.f);
+        }
         const float eg = __expf(gl);
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) S[tt] *= eg;
+        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) S[tt][ct] *= eg;
         Frag<T> kc[TPW][2];
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
@@ -903,16 +940,20 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         }
         lds_sync();  // B2(c): all of X in LX and kf X in LY; stage c + 1 ready
         if (c + 1 < nch) read_stage(c + 1);
-        const Frag<T> xb0 = xf(LY, 0, lane), xb1 = xf(LY, 1, lane);
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            S[tt] = mma(kc[tt][0], xb0, S[tt]);
-            S[tt] = mma(kc[tt][1], xb1, S[tt]);
+        for (int ct = 0; ct < CT; ++ct) {
+            const Frag<T> xb0 = xf(LY, ct, lane), xb1 = xf(LY, CT + ct, lane);
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                S[tt][ct] = mma(kc[tt][0], xb0, S[tt][ct]);
+                S[tt][ct] = mma(kc[tt][1], xb1, S[tt][ct]);
+            }
         }
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
             const int m = w * TPW + tt;
-            lds_put4(xf(LS, m >> 1, lane), m & 1, S[tt], -1.f);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) lds_put4(xf(LS, (m >> 1) * CT + ct, lane), m & 1, S[tt][ct], -1.f);
         }
     }
     if (so >= 0) {
@@ -920,7 +961,12 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         for (int tt = 0; tt < TPW; ++tt) {
             const int m = w * TPW + tt;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p.sfinal[out_off + (size_t)(16 * m + 4 * grp + i) * D + col] = S[tt][i];
+            for (int ct = 0; ct < CT; ++ct) {
+                const int col = 16 * (CT * tile + ct) + r16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    p.sfinal[out_off + (size_t)(16 * m + 4 * grp + i) * D + col] = S[tt][ct][i];
+            }
         }
     }
 }
@@ -1260,8 +1306,13 @@ template <typename T, int D>
 hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEvent_t const* events) {
     const int work_ch = p.tab.n_chunks * p.H_v;
     const int grid_ch = pad8(work_ch);
-    const int work_st = p.tab.num_seqs * p.H_v * (D / 16);
-    const int grid_st = pad8(p.tab.num_seqs * p.H_v) * (D / 16);  // whole groups of tiles on each XCD
+    const int groups = p.tab.num_seqs * p.H_v;  // (sequence, value head) pairs of the state scan
+    // Column tiles per state-scan workgroup (bf16): one while the chip has a CU
+    // for every 16-column tile (the shortest serial step: T = 4096, 32 heads),
+    // two up to two tiles a CU, four beyond: a step's W and K stream then
+    // serves 2 or 4 tiles (packed 8-sequence batch: 444 -> 311 -> 287 us).
+    const int tiles = groups * (D / 16), cus = cu_count();
+    const int ct = sizeof(T) != 2 ? 1 : tiles <= cus ? 1 : tiles <= 2 * cus ? 2 : 4;
     // With events, each kernel is launched with hipExtLaunchKernelGGL, whose
     // start/stop events are stamped by the kernel's own dispatch (kernel time
     // only, no launch gaps).
@@ -1283,8 +1334,24 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
     auto run = [&](auto dev) {
         constexpr bool DEV = decltype(dev)::value;
         if (work_ch > 0) launch(0, chunk_prep_kernel<T, D, DEV>, std::min(grid_ch, prep_slots), 256, grid_ch, pl);
-        if (work_st > 0)
-            launch(1, chunk_state_h_kernel<T, D, DEV>, grid_st, 64 * (5 + StateStage<T, D>::NPW), grid_st, pl);
+        // grids: whole groups of workgroups on each XCD
+        auto state = [&](auto ctc) {
+            constexpr int CT = decltype(ctc)::value;
+            const int grid = pad8(groups) * (D / 16 / CT);
+            launch(1, chunk_state_h_kernel<T, D, DEV, CT>, grid, 64 * (5 + StateStage<T, D, CT>::NPW), grid, pl);
+        };
+        if (groups > 0) {
+            if constexpr (sizeof(T) == 2) {
+                if (ct == 4)
+                    state(std::integral_constant<int, 4>{});
+                else if (ct == 2)
+                    state(std::integral_constant<int, 2>{});
+                else
+                    state(std::integral_constant<int, 1>{});
+            } else {
+                state(std::integral_constant<int, 1>{});
+            }
+        }
         if (work_ch > 0) {
             if (p.gz)
                 launch(2, chunk_output_o_kernel<T, D, true, DEV>, grid_ch, 256, grid_ch, pl);
