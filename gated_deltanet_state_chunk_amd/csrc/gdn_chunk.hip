@@ -977,11 +977,12 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
 //    P^T[j][i] = (k_j . q_i) exp(gc_i - gc_j) for j <= i  (Lower keeps the diagonal).
 //    Q and K are staged in LDS once; wave w forms the P^T tiles of query block w
 //    and publishes them in operand order; then each wave produces its 16-row
-//    tiles of O^T (d_v rows) for all 64 positions.  With the read-out
+//    tiles of O^T (d_v rows) for all 64 positions, one 16-position tile at a
+//    time, which goes through LDS and leaves as rows of O.  With the read-out
 //    epilogue (trace page, Decode-GDN node 8; node 18 of the prefill graph)
-//    the tiles stay in registers until each position's sum of squares over
-//    d_v has been reduced across the lanes and waves, then
-//    out = o / sqrt(mean o^2 + eps) * weight * silu(z) is stored instead of o.
+//    each position's sum of squares over d_v is reduced across the lanes and
+//    waves on the way, and out = o / sqrt(mean o^2 + eps) * weight * silu(z)
+//    is stored instead of o.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct OutLds {
@@ -1126,11 +1127,10 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
     }
     lds_sync();
 
-    // Output tiles: rows d_v (this wave's tiles), columns pos.  With the read-out
-    // epilogue, each position tile is normalised as soon as it is complete: its
-    // sums of o^2 over this lane's values, the four lanes sharing a position
-    // (grp), then the four waves through LDS (one barrier per tile), so only one
-    // tile of o is held in registers.
+    // Output tiles: rows d_v (this wave's tiles), columns pos, one position tile
+    // at a time.  With the read-out epilogue, each position's sum of o^2 is
+    // reduced over this lane's values, the four lanes sharing a position (grp)
+    // and the four waves (through LDS, behind the tile's one barrier).
     T* ob = reinterpret_cast<T*>(p.out) + (size_t)cp.t0 * p.H_v * D + (size_t)h * D;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
