@@ -29,6 +29,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -142,10 +143,15 @@ def _dev(arr, dtype, torch, device):
 
 
 def _source_sha() -> str:
+    """Hash of the kernel sources with comments and blank space removed, so that
+    counter summaries stay tied to the code they were taken on, not its prose."""
     h = hashlib.sha256()
     for f in ("gdn_chunk.hip", "gdn_decode.hip", "gdn_device.h", "gdn_params.h"):
-        with open(os.path.join(ROOT, "gated_deltanet_state_chunk_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "gated_deltanet_state_chunk_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                # line comments (no string in these sources holds //)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
