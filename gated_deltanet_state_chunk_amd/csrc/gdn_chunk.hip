@@ -487,8 +487,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
 //
 //    Producer waves.  Stream each chunk's W, K (Kc, one copy per key head),
 //    U, gc and kf blocks (stored by chunk_prep in exactly the LDS stage
-//    order) into a ring of NST = 2 stages with direct global->LDS loads.
-//    A stage is free
+//    order) into a ring of NST stages (three where they fit) with direct
+//    global->LDS loads.  A stage is free
 //    once its chunk is in registers (B1 of that chunk's step); chunk c + NST
 //    goes out in two halves, at B1(c) and B2(c); vmcnt waits make chunk c + 1
 //    land before B2(c) and keep at most 63 loads in flight per wave.
@@ -516,13 +516,12 @@ struct StateStage {
     static constexpr int NPW = (NPIECE + 2 + 62) / 63;
     // The compute waves copy chunk c into registers before B1(c), so stage
     // c % NST is refilled with chunk c + NST from B1(c) on.
-    // Two stages: a chunk is issued a step and a half before it is read (the
-    // third stage of earlier versions bought nothing measurable), and at bf16
-    // d = 128 two workgroups then fit on a CU (2 x 78 KiB), which large batches
-    // use (packed batch: state scan 463 -> 444 us).
+    // Three stages where they fit (a chunk is issued two steps and a half
+    // before it is read), else two.  The third stage pays where the stream
+    // comes from HBM (T = 65536: 991 -> 902 us) and costs nothing at T = 4096;
+    // the launcher runs one workgroup per CU anyway once tiles outnumber CUs.
     static constexpr int LDS_CAP = 160 * 1024;
-    static constexpr int NST = 2;
-    static_assert(NST * BYTES + EXCH + 256 <= LDS_CAP, "stages exceed LDS");  // + the L2-prefetch sink
+    static constexpr int NST = (3 * BYTES + EXCH + 256 <= LDS_CAP) ? 3 : 2;  // + the L2-prefetch sink
 };
 
 typedef __attribute__((address_space(1))) const void* gptr_t;
