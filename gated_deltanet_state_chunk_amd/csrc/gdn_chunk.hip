@@ -19,6 +19,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -1290,15 +1291,17 @@ static inline int pad8(int x) { return (x + 7) & ~7; }
 // Compute units of the current device (cached per device), a multiple of 8 on
 // this chip (eight XCDs).
 static int cu_count() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];  // zero-initialised; concurrent callers store the same value
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
+    int c = cached[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = pad8(n);
+        c = pad8(n);
+        cached[dev].store(c, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return c;
 }
 
 template <typename T, int D>
