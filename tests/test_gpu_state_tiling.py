@@ -54,3 +54,18 @@ def test_state_scan_tiling_bitwise_consistent(torch_cuda):
         res.append((out[:197], fin[0]))
     for o, f in res[1:]:
         assert np.array_equal(o, res[0][0]) and np.array_equal(f, res[0][1])
+
+
+@pytest.mark.parametrize("n_seq,d", [(8, 128), (40, 128), (40, 64)])
+def test_state_scan_tiling_odd_heads_many_sequences(torch_cuda, oracle_mod, n_seq, d):
+    """Five value heads on five key heads (groups not a multiple of 8, so the
+    per-XCD grid is padded) over many short ragged sequences: 8 sequences at
+    d = 128 give 320 tiles (two a workgroup), 40 sequences four a workgroup."""
+    lens = [int(x) for x in np.random.default_rng(702 + n_seq + d).integers(0, 140, n_seq)]
+    inp = gdn_inputs.make_prefill(seed=703 + n_seq, seqlens=lens, H_q=5, H_v=5, d_k=d, d_v=d, dtype="bf16",
+                                  state_std=0.02)
+    out, fin = chunk_fwd_device(inp)
+    ref_o, ref_s = oracle_mod.forward(inp.q32(), inp.k32(), inp.v32(), inp.g, inp.beta, inp.cu_seqlens, 5, 5,
+                                      inp.scale, initial_state=inp.initial_state.astype(np.float64))
+    assert rel_err(out, ref_o) < 1e-2
+    assert rel_err(fin, ref_s) < 1e-2
