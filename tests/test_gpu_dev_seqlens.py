@@ -51,6 +51,33 @@ def test_dev_seqlens_equals_host_seqlens(torch_cuda, oracle_mod, dtype, lens):
         assert rel_err(to_host(out_d), ref_o) < tol and rel_err(to_host(fin_d), ref_f) < tol
 
 
+def test_dev_seqlens_many_items(torch_cuda, oracle_mod):
+    """A batch with over eight (chunk, value head) items per chunk_prep slot of
+    a 256-CU part (291 chunks x 32 value heads), where chunk_prep runs one
+    workgroup an item instead of looping: device and host boundaries agree bit
+    for bit, and sampled heads match the oracle (bf16 bar, 1e-2)."""
+    import gated_deltanet_state_chunk_amd as gdn
+
+    torch = torch_cuda
+    lens = [9000, 5000, 3000, 1500]
+    inp = gdn_inputs.make_prefill(86, lens, 16, 32, 128, 128, "bf16")
+    assert sum(-(-n // 64) for n in lens) * 32 > 8 * 4 * 256
+    args = _dev_args(inp)
+    s0 = f32_dev(inp.initial_state)
+    cu_dev = torch.tensor(inp.cu_seqlens, dtype=torch.int32, device="cuda")
+    out_h, fin_h = gdn.chunk_fwd(*args, inp.cu_seqlens, initial_state=s0)
+    out_d, fin_d = gdn.chunk_fwd_dev(*args, cu_dev, initial_state=s0)
+    torch.cuda.synchronize()
+    assert torch.equal(out_h, out_d)
+    assert torch.equal(fin_h, fin_d)
+    heads = [0, 13, 31]
+    ref_o, ref_f = oracle_mod.forward(inp.q32(), inp.k32(), inp.v32(), inp.g, inp.beta, inp.cu_seqlens, 16, 32,
+                                      inp.scale, initial_state=inp.initial_state.astype(np.float64), heads=heads)
+    out, fin = to_host(out_d), to_host(fin_d)
+    assert rel_err(out[:, heads], ref_o[:, heads]) < 1e-2
+    assert rel_err(fin[:, heads], ref_f[:, heads]) < 1e-2
+
+
 def test_dev_seqlens_graph_replay_with_new_boundaries(torch_cuda):
     """One captured call, replayed with three different splits of the same T
     tokens into four sequences (written into the captured cu_seqlens buffer);
