@@ -311,9 +311,13 @@ def bench_prefill_serving(args, torch, gdn, device):
             "ms_per_step": ms, "tokens_per_s": inp.T / (ms * 1e-3)}
 
 
-def bench_decode(args, torch, gdn, hip, device, fused=False, gated=False):
+def bench_decode(args, torch, gdn, hip, device, fused=False, gated=False, pooled=False):
     """Decode steps on the 256 x 32-head batch: the plain step (normalised q, k and
-    final g, beta) or, with fused, the step from raw q, k, a, b (front end inside)."""
+    final g, beta) or, with fused, the step from raw q, k, a, b (front end inside);
+    with pooled (fused only), the states live in a pool of twice as many rows and
+    each sequence's row comes from a seeded permutation (the serving form)."""
+    import numpy as np
+
     import gdn_inputs
 
     cfg = gdn_inputs.DECODE_WORKLOAD
@@ -335,6 +339,17 @@ def bench_decode(args, torch, gdn, hip, device, fused=False, gated=False):
         gate = (_dev(z, dt, torch, device), _dev(w, "f32", torch, device), 1e-6)
         plain_fn = step_fn
         step_fn = lambda *a, **kw: plain_fn(*a, gate=gate, **kw)  # noqa: E731
+    if pooled:
+        assert fused
+        P = 2 * N
+        slot = torch.tensor(np.random.default_rng(cfg["seed"] + 1).permutation(P)[:N].astype(np.int32),
+                            device=device)
+        pool = torch.zeros((P, H_v, d, d), dtype=torch.float32, device=device)
+        pool[slot.long()] = state
+        state = pool
+        unpooled_fn = step_fn
+        step_fn = lambda *a, **kw: gdn.recurrent_step_fused_pooled(*a, slot, **kw)  # noqa: E731
+        assert unpooled_fn is gdn.recurrent_step_fused
     out = torch.empty((N, H_v, d), dtype=toks[0][0].dtype, device=device)
     scale = 1.0 / math.sqrt(d)
     K = max(args.steps, cfg["steps"])
@@ -483,7 +498,7 @@ def main():
         return
 
     res = {}
-    pre = pre_g = dec = decf = decg = None
+    pre = pre_g = dec = decf = decg = decp = None
     if args.only in ("all", "prefill"):
         pre = bench_prefill(args, torch, gdn, hip, device)
         print(f"[bench] prefill {args.workload}: {pre['ms_step']:.4f} ms/step, stages "
@@ -500,6 +515,9 @@ def main():
         print(f"[bench] decode: {dec['ms_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
         decf = bench_decode(args, torch, gdn, hip, device, fused=True)
         print(f"[bench] decode (fused front end): {decf['ms_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+        decp = bench_decode(args, torch, gdn, hip, device, fused=True, pooled=True)
+        print(f"[bench] decode (fused front end, state pool): {decp['ms_step'] * 1e3:.1f} us/step", file=sys.stderr,
+              flush=True)
         decg = bench_decode(args, torch, gdn, hip, device, fused=True, gated=True)
         print(f"[bench] decode (front end + gated read-out): {decg['ms_step'] * 1e3:.1f} us/step", file=sys.stderr,
               flush=True)
@@ -581,6 +599,15 @@ def main():
             "tokens_per_s": decf["N"] / (decf["ms_step"] * 1e-3), "steps": decf["steps"],
             "roofline": {"bound": "hbm", "kernel": "recurrent_step_fused", "achieved": kgbs, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": kgbs / HBM_PEAK_GBS, "traffic": None}}
+    if decp is not None:
+        kp = decp["bytes"] / (decp["kernel_ms"] * 1e-3) / 1e9
+        res["decode_fused_pooled"] = {
+            "workload": "decode_256x1 from raw q, k, a, b over a 512-row state pool, each sequence's row from a "
+                        "seeded permutation (gdn_recurrent_step_fused_pooled)",
+            "us_per_step": decp["ms_step"] * 1e3, "kernel_us": decp["kernel_ms"] * 1e3,
+            "tokens_per_s": decp["N"] / (decp["ms_step"] * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": kp, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": kp / HBM_PEAK_GBS, "traffic": None}}
     if args.only == "all":
         conv = bench_conv(args, torch, gdn, device)
         print(f"[bench] conv1d+SiLU: prefill {conv['prefill']['us']:.1f} us, decode step "
