@@ -480,7 +480,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported (the GDN core shards over "
-              f"sequences and value heads with no exchange; see the design notes).", file=sys.stderr)
+              f"sequences and value heads with no exchange between GPUs).", file=sys.stderr)
         sys.exit(2)
 
     import torch
