@@ -1,0 +1,15 @@
+"""Host-side checks of bench.py's command line (no GPU): more than one GPU is
+refused with a message and a non-zero status before anything touches a device."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "single GPU" in r.stderr and "--gpus 2" in r.stderr
+    assert r.stdout == ""
