@@ -36,9 +36,8 @@ _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace", 
 class GdnError(RuntimeError):
     def __init__(self, status: int, what: str):
         lib = load_library()
-        msg = lib.gdn_status_string(status).decode()
-        hip = lib.gdn_last_hip_error().decode() if status == -4 else ""
-        super().__init__(f"{what}: {msg} ({status}){' — ' + hip if hip else ''}")
+        msg = lib.gdn_strerror(status).decode()  # names the HIP error too for a failed launch
+        super().__init__(f"{what}: {msg} ({status})")
         self.status = status
 
 
@@ -125,11 +124,13 @@ def load_library():
     lib.gdn_version.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_strerror.argtypes = [ctypes.c_int]
+    lib.gdn_strerror.restype = ctypes.c_char_p
     lib.gdn_last_hip_error.restype = ctypes.c_char_p
     lib.gdn_chunk_fwd_workspace_layout.argtypes = [I32, I32, P, I32, I32, I32, I32, ctypes.c_int,
                                                    ctypes.POINTER(WorkspaceLayout)]
     lib.gdn_chunk_fwd_workspace_layout.restype = ctypes.c_int
-    lib.gdn_chunk_fwd_workspace_size.argtypes = [I32, I32, P, I32, I32, I32, I32, ctypes.c_int]
+    lib.gdn_chunk_fwd_workspace_size.argtypes = [P, I32, I32, I32, I32, I32, ctypes.c_int]
     lib.gdn_chunk_fwd_workspace_size.restype = ctypes.c_size_t
     lib.gdn_chunk_fwd.argtypes = [P, P, P, P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P,
                                   ctypes.c_size_t, P]
@@ -204,6 +205,15 @@ def _check_dev(name, t, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _check_buf(name, t, dtype, shape):
+    """A caller-supplied output buffer: on the current device, contiguous, of the
+    given dtype and exactly the given shape (the kernels write every element of
+    that shape, so a smaller buffer would be overrun)."""
+    _check_dev(name, t, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def _host_cu(cu_seqlens) -> "ctypes.Array":
     torch = _torch()
     if isinstance(cu_seqlens, torch.Tensor):
@@ -246,7 +256,7 @@ def workspace_size(T: int, cu_seqlens, H_q: int, H_v: int, d_k: int, d_v: int, d
     """Workspace bytes of chunk_fwd (gdn_chunk_fwd_workspace_size); raises on invalid arguments."""
     workspace_layout(T, cu_seqlens, H_q, H_v, d_k, d_v, dtype)  # validates
     code = dtype if isinstance(dtype, int) else _dtype_code_from(dtype)
-    return load_library().gdn_chunk_fwd_workspace_size(T, len(cu_seqlens) - 1, _host_cu(cu_seqlens), H_q, H_v, d_k,
+    return load_library().gdn_chunk_fwd_workspace_size(_host_cu(cu_seqlens), len(cu_seqlens) - 1, H_q, H_v, d_k,
                                                        d_v, code)
 
 
@@ -290,12 +300,12 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens: Sequence[int], initial_state=None, s
     if out is None:
         out = torch.empty((T, H_v, d_v), dtype=q.dtype, device=q.device)
     else:
-        _check_dev("out", out, q.dtype)
+        _check_buf("out", out, q.dtype, (T, H_v, d_v))
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H_v, d_k, d_v), dtype=torch.float32, device=q.device)
     elif final_state is not None:
-        _check_dev("final_state", final_state, torch.float32)
-    ws_bytes = lib.gdn_chunk_fwd_workspace_size(T, N, cu, H_q, H_v, d_k, d_v, dt)
+        _check_buf("final_state", final_state, torch.float32, (N, H_v, d_k, d_v))
+    ws_bytes = lib.gdn_chunk_fwd_workspace_size(cu, N, H_q, H_v, d_k, d_v, dt)
     if ws_bytes == 0 and N > 0 and T > 0:
         lay = WorkspaceLayout()
         rc = lib.gdn_chunk_fwd_workspace_layout(T, N, cu, H_q, H_v, d_k, d_v, dt, ctypes.byref(lay))
@@ -341,7 +351,7 @@ def recurrent_step(q, k, v, g, beta, state, scale: Optional[float] = None, out=N
     if out is None:
         out = torch.empty((N, H_v, d_v), dtype=q.dtype, device=q.device)
     else:
-        _check_dev("out", out, q.dtype)
+        _check_buf("out", out, q.dtype, (N, H_v, d_v))
     rc = lib.gdn_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out), N, H_q, H_v,
                                 d_k, d_v, float(scale), dt, _stream_ptr(stream))
     if rc != 0:
@@ -378,7 +388,7 @@ def recurrent_step_fused(q, k, v, a, b, A_log, dt_bias, state, scale: Optional[f
     if out is None:
         out = torch.empty((N, H_v, d_v), dtype=q.dtype, device=q.device)
     else:
-        _check_dev("out", out, q.dtype)
+        _check_buf("out", out, q.dtype, (N, H_v, d_v))
     gptr, _keep = _gate_arg(gate, q.dtype, N, H_v, d_v)
     rc = lib.gdn_recurrent_step_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
                                       _ptr(state), _ptr(out), N, H_q, H_v, d_k, d_v, float(scale), dt, gptr,
@@ -416,6 +426,8 @@ def conv1d_silu(x, cu_seqlens: Sequence[int], weight, bias=None, initial_state=N
                 raise ValueError(f"{name} must be [N, K-1, C]")
     if out is None:
         out = torch.empty_like(x)
+    else:
+        _check_buf("out", out, x.dtype, tuple(x.shape))
     if final_state is None and output_final_state:
         final_state = torch.empty((N, K - 1, C), dtype=x.dtype, device=x.device)
     rc = lib.gdn_conv1d_silu_fwd(_ptr(x), cu, N, T, C, K, _ptr(weight), _ptr(bias), _ptr(initial_state), _ptr(out),
@@ -442,6 +454,8 @@ def conv1d_silu_step(x, weight, bias, state, out=None, stream=None):
         _check_dev("bias", bias, torch.float32)
     if out is None:
         out = torch.empty_like(x)
+    else:
+        _check_buf("out", out, x.dtype, tuple(x.shape))
     rc = lib.gdn_conv1d_silu_step(_ptr(x), N, C, K, _ptr(weight), _ptr(bias), _ptr(state), _ptr(out), dt,
                                   _stream_ptr(stream))
     if rc != 0:
@@ -484,8 +498,8 @@ def chunk_fwd_pooled(q, k, v, g, beta, cu_seqlens: Sequence[int], state_pool, sl
     if out is None:
         out = torch.empty((T, H_v, d_v), dtype=q.dtype, device=q.device)
     else:
-        _check_dev("out", out, q.dtype)
-    ws_bytes = lib.gdn_chunk_fwd_workspace_size(T, N, cu, H_q, H_v, d_k, d_v, dt)
+        _check_buf("out", out, q.dtype, (T, H_v, d_v))
+    ws_bytes = lib.gdn_chunk_fwd_workspace_size(cu, N, H_q, H_v, d_k, d_v, dt)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     else:
@@ -544,14 +558,14 @@ def chunk_fwd_fused(q, k, v, a, b, A_log, dt_bias, cu_seqlens: Sequence[int], in
         if final_state is None and output_final_state:
             final_state = torch.empty((N, H_v, d_k, d_v), dtype=torch.float32, device=q.device)
         elif final_state is not None:
-            _check_dev("final_state", final_state, torch.float32)
+            _check_buf("final_state", final_state, torch.float32, (N, H_v, d_k, d_v))
     if scale is None:
         scale = 1.0 / math.sqrt(d_k)
     if out is None:
         out = torch.empty((T, H_v, d_v), dtype=q.dtype, device=q.device)
     else:
-        _check_dev("out", out, q.dtype)
-    ws_bytes = lib.gdn_chunk_fwd_workspace_size(T, N, cu, H_q, H_v, d_k, d_v, dt)
+        _check_buf("out", out, q.dtype, (T, H_v, d_v))
+    ws_bytes = lib.gdn_chunk_fwd_workspace_size(cu, N, H_q, H_v, d_k, d_v, dt)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     else:
@@ -597,11 +611,11 @@ def chunk_fwd_dev(q, k, v, g, beta, cu_seqlens_dev, initial_state=None, scale: O
     if out is None:
         out = torch.empty((T, H_v, d_v), dtype=q.dtype, device=q.device)
     else:
-        _check_dev("out", out, q.dtype)
+        _check_buf("out", out, q.dtype, (T, H_v, d_v))
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H_v, d_k, d_v), dtype=torch.float32, device=q.device)
     elif final_state is not None:
-        _check_dev("final_state", final_state, torch.float32)
+        _check_buf("final_state", final_state, torch.float32, (N, H_v, d_k, d_v))
     if workspace is None:
         workspace = torch.empty(max(dev_workspace_size(T, N, H_q, H_v, d_k, d_v, q.dtype), 1), dtype=torch.uint8,
                                 device=q.device)
@@ -646,6 +660,8 @@ def conv1d_silu_pooled(x, cu_seqlens: Sequence[int], weight, bias, state_pool, s
     st, _keep_slots = _slots_arg(slots, has_initial, state_pool.shape[0], N)
     if out is None:
         out = torch.empty_like(x)
+    else:
+        _check_buf("out", out, x.dtype, tuple(x.shape))
     rc = lib.gdn_conv1d_silu_fwd_pooled(_ptr(x), cu, N, T, C, K, _ptr(weight), _ptr(bias), _ptr(state_pool),
                                         ctypes.byref(st), _ptr(out), dt, _stream_ptr(stream))
     if rc != 0:
@@ -681,7 +697,7 @@ def recurrent_step_fused_pooled(q, k, v, a, b, A_log, dt_bias, state_pool, slot,
     if out is None:
         out = torch.empty((N, H_v, d_v), dtype=q.dtype, device=q.device)
     else:
-        _check_dev("out", out, q.dtype)
+        _check_buf("out", out, q.dtype, (N, H_v, d_v))
     gptr, _keep = _gate_arg(gate, q.dtype, N, H_v, d_v)
     rc = lib.gdn_recurrent_step_fused_pooled(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log),
                                              _ptr(dt_bias), _ptr(state_pool), _ptr(slot), state_pool.shape[0],
@@ -711,6 +727,8 @@ def conv1d_silu_step_pooled(x, weight, bias, state_pool, slot, out=None, stream=
     _check_slot_dev(slot, N)
     if out is None:
         out = torch.empty_like(x)
+    else:
+        _check_buf("out", out, x.dtype, tuple(x.shape))
     rc = lib.gdn_conv1d_silu_step_pooled(_ptr(x), N, C, K, _ptr(weight), _ptr(bias), _ptr(state_pool), _ptr(slot),
                                          state_pool.shape[0], _ptr(out), dt, _stream_ptr(stream))
     if rc != 0:

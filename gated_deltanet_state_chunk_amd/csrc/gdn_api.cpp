@@ -20,41 +20,41 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-inline size_t elem_size(gdn_dtype dt) { return dt == GDN_DTYPE_BF16 ? 2 : 4; }
+inline size_t elem_size(gdn_dtype dt) { return dt == GDN_BF16 ? 2 : 4; }
 
 int check_shapes(int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype) {
-    if (H_q <= 0 || H_v <= 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_INVALID;
-    if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
-    if (d_k != d_v || (d_k != 64 && d_k != 128)) return GDN_ERR_UNSUPPORTED;
-    if (H_v % H_q != 0) return GDN_ERR_UNSUPPORTED;
+    if (H_q <= 0 || H_v <= 0 || d_k <= 0 || d_v <= 0) return GDN_EINVAL;
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_EUNSUPPORTED;
+    if (d_k != d_v || (d_k != 64 && d_k != 128)) return GDN_EUNSUPPORTED;
+    if (H_v % H_q != 0) return GDN_EUNSUPPORTED;
     return GDN_OK;
 }
 
 // Read-out epilogue arguments: z and weight present and 16-byte aligned, eps > 0.
 int check_gate(const gdn_output_gate* gate, bool need_z) {
-    if (!(gate->eps > 0.f) || !(gate->eps < INFINITY)) return GDN_ERR_INVALID;
-    if (need_z && (!gate->z || !gate->weight)) return GDN_ERR_INVALID;
-    if ((gate->z && !aligned16(gate->z)) || (gate->weight && !aligned16(gate->weight))) return GDN_ERR_UNSUPPORTED;
+    if (!(gate->eps > 0.f) || !(gate->eps < INFINITY)) return GDN_EINVAL;
+    if (need_z && (!gate->z || !gate->weight)) return GDN_EINVAL;
+    if ((gate->z && !aligned16(gate->z)) || (gate->weight && !aligned16(gate->weight))) return GDN_EUNSUPPORTED;
     return GDN_OK;
 }
 
 // Validates cu_seqlens and counts chunks (each sequence chunked from its own start).
 int check_seqlens(int32_t T, int32_t num_seqs, const int32_t* cu, int64_t* n_chunks) {
-    if (T < 0 || num_seqs < 0) return GDN_ERR_INVALID;
+    if (T < 0 || num_seqs < 0) return GDN_EINVAL;
     if (num_seqs == 0) {
-        if (T != 0) return GDN_ERR_INVALID;
+        if (T != 0) return GDN_EINVAL;
         *n_chunks = 0;
         return GDN_OK;
     }
-    if (!cu) return GDN_ERR_INVALID;
-    if (cu[0] != 0 || cu[num_seqs] != T) return GDN_ERR_INVALID;
+    if (!cu) return GDN_EINVAL;
+    if (cu[0] != 0 || cu[num_seqs] != T) return GDN_EINVAL;
     int64_t nc = 0;
     for (int32_t i = 0; i < num_seqs; ++i) {
         const int64_t len = (int64_t)cu[i + 1] - cu[i];
-        if (len < 0) return GDN_ERR_INVALID;
+        if (len < 0) return GDN_EINVAL;
         nc += (len + GDN_CHUNK - 1) / GDN_CHUNK;
     }
-    if (nc > (int64_t)INT32_MAX / 1024) return GDN_ERR_UNSUPPORTED;
+    if (nc > (int64_t)INT32_MAX / 1024) return GDN_EUNSUPPORTED;
     *n_chunks = nc;
     return GDN_OK;
 }
@@ -62,19 +62,19 @@ int check_seqlens(int32_t T, int32_t num_seqs, const int32_t* cu, int64_t* n_chu
 // Pool addressing of a prefill: row indices inside the pool, no duplicate
 // kept rows (two sequences writing one row would race).
 int check_slots(const gdn_state_slots* sl, int32_t num_seqs, const void* pool) {
-    if (!sl || sl->pool_size < 0) return GDN_ERR_INVALID;
+    if (!sl || sl->pool_size < 0) return GDN_EINVAL;
     if (num_seqs == 0) return GDN_OK;
-    if (!sl->slot) return GDN_ERR_INVALID;
+    if (!sl->slot) return GDN_EINVAL;
     std::vector<int32_t> kept;
     kept.reserve(num_seqs);
     for (int32_t i = 0; i < num_seqs; ++i) {
         const int32_t r = sl->slot[i];
-        if (r >= sl->pool_size) return GDN_ERR_INVALID;
+        if (r >= sl->pool_size) return GDN_EINVAL;
         if (r >= 0) kept.push_back(r);
     }
-    if (!kept.empty() && !pool) return GDN_ERR_INVALID;
+    if (!kept.empty() && !pool) return GDN_EINVAL;
     std::sort(kept.begin(), kept.end());
-    if (std::adjacent_find(kept.begin(), kept.end()) != kept.end()) return GDN_ERR_INVALID;
+    if (std::adjacent_find(kept.begin(), kept.end()) != kept.end()) return GDN_EINVAL;
     return GDN_OK;
 }
 
@@ -114,7 +114,7 @@ int32_t fill_table(gdn::SeqTable& tab, const int32_t* cu, int32_t s0, int32_t ns
 }
 
 hipError_t run_chunk(const gdn::ChunkParams& p, gdn_dtype dt, int d, hipStream_t s, hipEvent_t const* ev) {
-    if (dt == GDN_DTYPE_BF16)
+    if (dt == GDN_BF16)
         return d == 128 ? gdn::launch_chunk_pipeline<gdn::bf16, 128>(p, s, ev)
                         : gdn::launch_chunk_pipeline<gdn::bf16, 64>(p, s, ev);
     return d == 128 ? gdn::launch_chunk_pipeline<float, 128>(p, s, ev) : gdn::launch_chunk_pipeline<float, 64>(p, s, ev);
@@ -131,17 +131,17 @@ hipError_t run_conv(const gdn::ConvParams& p, int K, int N_step, hipStream_t s) 
 }
 
 int check_conv(int32_t C, int32_t K, gdn_dtype dtype, const float* weight, const float* bias) {
-    if (C <= 0 || K <= 0 || !weight) return GDN_ERR_INVALID;
-    if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
-    if (K < 2 || K > 4) return GDN_ERR_UNSUPPORTED;
-    if (C % (int32_t)(16 / elem_size(dtype)) != 0) return GDN_ERR_UNSUPPORTED;
-    if (!aligned16(weight) || (bias && !aligned16(bias))) return GDN_ERR_UNSUPPORTED;
+    if (C <= 0 || K <= 0 || !weight) return GDN_EINVAL;
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_EUNSUPPORTED;
+    if (K < 2 || K > 4) return GDN_EUNSUPPORTED;
+    if (C % (int32_t)(16 / elem_size(dtype)) != 0) return GDN_EUNSUPPORTED;
+    if (!aligned16(weight) || (bias && !aligned16(bias))) return GDN_EUNSUPPORTED;
     return GDN_OK;
 }
 
 template <bool FUSED>
 hipError_t run_decode(const gdn::DecodeParams& p, gdn_dtype dt, int d, hipStream_t s) {
-    if (dt == GDN_DTYPE_BF16)
+    if (dt == GDN_BF16)
         return d == 128 ? gdn::launch_recurrent_step<gdn::bf16, 128, FUSED>(p, s)
                         : gdn::launch_recurrent_step<gdn::bf16, 64, FUSED>(p, s);
     return d == 128 ? gdn::launch_recurrent_step<float, 128, FUSED>(p, s)
@@ -153,12 +153,12 @@ int layout_for_chunks(int64_t nc, int32_t H_q, int32_t H_v, int32_t d_k, int32_t
 
 int hip_fail(hipError_t e) {
     g_last_hip_error = hipGetErrorString(e);
-    return GDN_ERR_HIP;
+    return GDN_ELAUNCH;
 }
 
 int conv_fwd_impl(const void* x, const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t T, int32_t C, int32_t K,
                   const float* weight, const float* bias, const void* s_in, void* out, void* s_out,
-                  const gdn_state_slots* slots, gdn_dtype dtype, void* stream) {
+                  const gdn_state_slots* slots, gdn_dtype dtype, hipStream_t stream) {
     int rc = check_conv(C, K, dtype, weight, bias);
     if (rc != GDN_OK) return rc;
     int64_t n_chunks = 0;
@@ -166,41 +166,40 @@ int conv_fwd_impl(const void* x, const int32_t* cu_seqlens_host, int32_t num_seq
     if (rc != GDN_OK) return rc;
     if (slots && (rc = check_slots(slots, num_seqs, s_in)) != GDN_OK) return rc;
     if (num_seqs == 0) return GDN_OK;
-    if ((int64_t)T * C > INT32_MAX * (int64_t)16) return GDN_ERR_UNSUPPORTED;
-    if (T > 0 && (!x || !out)) return GDN_ERR_INVALID;
+    if ((int64_t)T * C > INT32_MAX * (int64_t)16) return GDN_EUNSUPPORTED;
+    if (T > 0 && (!x || !out)) return GDN_EINVAL;
     const void* ptrs[] = {x, out, s_in, s_out};
     for (const void* ptr : ptrs)
-        if (ptr && !aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
+        if (ptr && !aligned16(ptr)) return GDN_EUNSUPPORTED;
     gdn::ConvParams p{};
     p.x = x; p.y = out; p.w = weight; p.b = bias; p.s_in = s_in; p.s_out = s_out; p.C = C;
-    hipStream_t s = static_cast<hipStream_t>(stream);
     int32_t chunk_base = 0;
     for (int32_t s0 = 0; s0 < num_seqs; s0 += gdn::MAX_SEQS_PER_LAUNCH) {
         const int32_t ns = std::min<int32_t>(gdn::MAX_SEQS_PER_LAUNCH, num_seqs - s0);
         chunk_base = fill_table(p.tab, cu_seqlens_host, s0, ns, chunk_base, slots, s_in != nullptr, s_out != nullptr);
         const hipError_t e =
-            dtype == GDN_DTYPE_BF16 ? run_conv<gdn::bf16>(p, K, -1, s) : run_conv<float>(p, K, -1, s);
+            dtype == GDN_BF16 ? run_conv<gdn::bf16>(p, K, -1, stream) : run_conv<float>(p, K, -1, stream);
         if (e != hipSuccess) return hip_fail(e);
     }
     return GDN_OK;
 }
 
 int conv_step_impl(const void* x, int32_t N, int32_t C, int32_t K, const float* weight, const float* bias,
-                   void* pool, const int32_t* slot, int32_t pool_size, void* out, gdn_dtype dtype, void* stream) {
+                   void* pool, const int32_t* slot, int32_t pool_size, void* out, gdn_dtype dtype,
+                   hipStream_t stream) {
     int rc = check_conv(C, K, dtype, weight, bias);
     if (rc != GDN_OK) return rc;
-    if (N < 0 || pool_size < 0) return GDN_ERR_INVALID;
+    if (N < 0 || pool_size < 0) return GDN_EINVAL;
     if (N == 0) return GDN_OK;
-    if (!x || !out || (pool_size > 0 && !pool)) return GDN_ERR_INVALID;
+    if (!x || !out || (pool_size > 0 && !pool)) return GDN_EINVAL;
     const void* ptrs[] = {x, pool, out};
     for (const void* ptr : ptrs)
-        if (ptr && !aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
-    if (slot && (reinterpret_cast<uintptr_t>(slot) & 3u)) return GDN_ERR_UNSUPPORTED;
+        if (ptr && !aligned16(ptr)) return GDN_EUNSUPPORTED;
+    if (slot && (reinterpret_cast<uintptr_t>(slot) & 3u)) return GDN_EUNSUPPORTED;
     gdn::ConvParams p{};
     p.x = x; p.y = out; p.w = weight; p.b = bias; p.s_in = pool; p.s_out = pool; p.C = C;
     p.slot = slot; p.pool = pool_size;
-    const hipError_t e = dtype == GDN_DTYPE_BF16 ? run_conv<gdn::bf16>(p, K, N, static_cast<hipStream_t>(stream))
-                                                 : run_conv<float>(p, K, N, static_cast<hipStream_t>(stream));
+    const hipError_t e = dtype == GDN_BF16 ? run_conv<gdn::bf16>(p, K, N, stream) : run_conv<float>(p, K, N, stream);
     if (e != hipSuccess) return hip_fail(e);
     return GDN_OK;
 }
@@ -208,10 +207,11 @@ int conv_step_impl(const void* x, int32_t N, int32_t C, int32_t K, const float* 
 int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
                    const int32_t* cu_seqlens_host, int32_t num_seqs, const float* initial_state, void* out,
                    float* final_state, const gdn_state_slots* slots, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k,
-                   int32_t d_v, float scale, gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream,
+                   int32_t d_v, float scale, gdn_dtype dtype, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream,
                    uint32_t flags, const gdn_output_gate* gate, void* const* stage_events,
                    const gdn_front_end* front = nullptr) {
-    if (flags & ~(uint32_t)GDN_FWD_KEEP_A) return GDN_ERR_INVALID;
+    if (flags & ~(uint32_t)GDN_FWD_KEEP_A) return GDN_EINVAL;
     if (gate) {
         const int grc = check_gate(gate, T > 0);
         if (grc != GDN_OK) return grc;
@@ -222,22 +222,22 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, 
     if (slots && (rc = check_slots(slots, num_seqs, initial_state)) != GDN_OK) return rc;
     if (num_seqs == 0) return GDN_OK;
     // Pointers: tensors with T > 0 rows must be present; all must be 16-byte aligned.
-    if (T > 0 && (!q || !k || !v || !out)) return GDN_ERR_INVALID;
+    if (T > 0 && (!q || !k || !v || !out)) return GDN_EINVAL;
     if (front) {
-        if (g || beta) return GDN_ERR_INVALID;
-        if (T > 0 && (!front->a || !front->b || !front->A_log || !front->dt_bias)) return GDN_ERR_INVALID;
+        if (g || beta) return GDN_EINVAL;
+        if (T > 0 && (!front->a || !front->b || !front->A_log || !front->dt_bias)) return GDN_EINVAL;
         const size_t es = elem_size(dtype);
         if ((reinterpret_cast<uintptr_t>(front->a) % es) || (reinterpret_cast<uintptr_t>(front->b) % es) ||
             (reinterpret_cast<uintptr_t>(front->A_log) & 3u) || (reinterpret_cast<uintptr_t>(front->dt_bias) & 3u))
-            return GDN_ERR_UNSUPPORTED;
+            return GDN_EUNSUPPORTED;
     } else if (T > 0 && (!g || !beta)) {
-        return GDN_ERR_INVALID;
+        return GDN_EINVAL;
     }
     const void* ptrs[] = {q, k, v, g, beta, out, initial_state, final_state, workspace};
     for (const void* ptr : ptrs)
-        if (ptr && !aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
-    if (!(scale == scale)) return GDN_ERR_INVALID;  // NaN
-    if (L.n_chunks > 0 && (!workspace || workspace_bytes < L.total_bytes)) return GDN_ERR_WORKSPACE;
+        if (ptr && !aligned16(ptr)) return GDN_EUNSUPPORTED;
+    if (!(scale == scale)) return GDN_EINVAL;  // NaN
+    if (L.n_chunks > 0 && (!workspace || workspace_bytes < L.total_bytes)) return GDN_EWORKSPACE;
 
     char* ws = static_cast<char*>(workspace);
     gdn::ChunkParams p{};
@@ -257,7 +257,6 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, 
     p.A_log = front ? front->A_log : nullptr;
     p.dt_bias = front ? front->dt_bias : nullptr;
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
     // Launch groups of up to MAX_SEQS_PER_LAUNCH sequences, each with its table in the kernel arguments.
     int32_t chunk_base = 0;
     for (int32_t s0 = 0; s0 < num_seqs; s0 += gdn::MAX_SEQS_PER_LAUNCH) {
@@ -265,7 +264,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, 
         chunk_base = fill_table(p.tab, cu_seqlens_host, s0, ns, chunk_base, slots, initial_state != nullptr,
                                 final_state != nullptr);
         hipEvent_t const* ev = (s0 == 0 && stage_events) ? reinterpret_cast<hipEvent_t const*>(stage_events) : nullptr;
-        const hipError_t e = run_chunk(p, dtype, d_k, s, ev);
+        const hipError_t e = run_chunk(p, dtype, d_k, stream, ev);
         if (e != hipSuccess) return hip_fail(e);
     }
     return GDN_OK;
@@ -274,23 +273,23 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, 
 int step_fused_impl(const void* q, const void* k, const void* v, const void* a, const void* b, const float* A_log,
                     const float* dt_bias, float* state, const int32_t* slot, int32_t pool_size, void* out, int32_t N,
                     int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale, gdn_dtype dtype,
-                    const gdn_output_gate* gate, void* stream) {
+                    const gdn_output_gate* gate, hipStream_t stream) {
     int rc = check_shapes(H_q, H_v, d_k, d_v, dtype);
     if (rc != GDN_OK) return rc;
-    if (N < 0 || pool_size < 0) return GDN_ERR_INVALID;
+    if (N < 0 || pool_size < 0) return GDN_EINVAL;
     if (N == 0) return GDN_OK;
-    if ((int64_t)N * H_v > INT32_MAX) return GDN_ERR_UNSUPPORTED;
-    if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !out || (pool_size > 0 && !state)) return GDN_ERR_INVALID;
+    if ((int64_t)N * H_v > INT32_MAX) return GDN_EUNSUPPORTED;
+    if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !out || (pool_size > 0 && !state)) return GDN_EINVAL;
     const void* ptrs[] = {q, k, v, state, out};
     for (const void* ptr : ptrs)
-        if (ptr && !aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
-    if (slot && (reinterpret_cast<uintptr_t>(slot) & 3u)) return GDN_ERR_UNSUPPORTED;
+        if (ptr && !aligned16(ptr)) return GDN_EUNSUPPORTED;
+    if (slot && (reinterpret_cast<uintptr_t>(slot) & 3u)) return GDN_EUNSUPPORTED;
     // per-head scalars: natural alignment of their element type
     const size_t es = elem_size(dtype);
     if ((reinterpret_cast<uintptr_t>(a) % es) || (reinterpret_cast<uintptr_t>(b) % es) ||
         (reinterpret_cast<uintptr_t>(A_log) & 3u) || (reinterpret_cast<uintptr_t>(dt_bias) & 3u))
-        return GDN_ERR_UNSUPPORTED;
-    if (!(scale == scale)) return GDN_ERR_INVALID;
+        return GDN_EUNSUPPORTED;
+    if (!(scale == scale)) return GDN_EINVAL;
     if (gate) {
         const int grc = check_gate(gate, true);
         if (grc != GDN_OK) return grc;
@@ -303,7 +302,7 @@ int step_fused_impl(const void* q, const void* k, const void* v, const void* a, 
     p.state = state; p.out = out;
     p.slot = slot; p.pool = pool_size;
     p.N = N; p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
-    const hipError_t e = run_decode<true>(p, dtype, d_k, static_cast<hipStream_t>(stream));
+    const hipError_t e = run_decode<true>(p, dtype, d_k, stream);
     if (e != hipSuccess) return hip_fail(e);
     return GDN_OK;
 }
@@ -316,49 +315,56 @@ const char* gdn_version(void) { return "0.1.0"; }
 
 int gdn_conv1d_silu_fwd(const void* x, const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t T, int32_t C,
                         int32_t K, const float* weight, const float* bias, const void* initial_state, void* out,
-                        void* final_state, gdn_dtype dtype, void* stream) {
+                        void* final_state, gdn_dtype dtype, hipStream_t stream) {
     return conv_fwd_impl(x, cu_seqlens_host, num_seqs, T, C, K, weight, bias, initial_state, out, final_state, nullptr,
                          dtype, stream);
 }
 
 int gdn_conv1d_silu_fwd_pooled(const void* x, const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t T, int32_t C,
                                int32_t K, const float* weight, const float* bias, void* state_pool,
-                               const gdn_state_slots* slots, void* out, gdn_dtype dtype, void* stream) {
-    if (!slots) return GDN_ERR_INVALID;
+                               const gdn_state_slots* slots, void* out, gdn_dtype dtype, hipStream_t stream) {
+    if (!slots) return GDN_EINVAL;
     return conv_fwd_impl(x, cu_seqlens_host, num_seqs, T, C, K, weight, bias, state_pool, out, state_pool, slots,
                          dtype, stream);
 }
 
 int gdn_conv1d_silu_step(const void* x, int32_t N, int32_t C, int32_t K, const float* weight, const float* bias,
-                         void* state, void* out, gdn_dtype dtype, void* stream) {
-    if (!state && N > 0) return GDN_ERR_INVALID;
+                         void* state, void* out, gdn_dtype dtype, hipStream_t stream) {
+    if (!state && N > 0) return GDN_EINVAL;
     return conv_step_impl(x, N, C, K, weight, bias, state, nullptr, N, out, dtype, stream);
 }
 
 int gdn_conv1d_silu_step_pooled(const void* x, int32_t N, int32_t C, int32_t K, const float* weight,
                                 const float* bias, void* state_pool, const int32_t* slot, int32_t pool_size, void* out,
-                                gdn_dtype dtype, void* stream) {
-    if (!slot && N > 0) return GDN_ERR_INVALID;
+                                gdn_dtype dtype, hipStream_t stream) {
+    if (!slot && N > 0) return GDN_EINVAL;
     return conv_step_impl(x, N, C, K, weight, bias, state_pool, slot, pool_size, out, dtype, stream);
 }
 
 const char* gdn_status_string(int status) {
     switch (status) {
         case GDN_OK: return "ok";
-        case GDN_ERR_INVALID: return "invalid argument";
-        case GDN_ERR_UNSUPPORTED: return "unsupported shape, dtype or alignment";
-        case GDN_ERR_WORKSPACE: return "workspace missing or too small";
-        case GDN_ERR_HIP: return "HIP launch failed";
+        case GDN_EINVAL: return "invalid argument";
+        case GDN_EUNSUPPORTED: return "unsupported shape, dtype or alignment";
+        case GDN_EWORKSPACE: return "workspace missing or too small";
+        case GDN_ELAUNCH: return "HIP launch failed";
         default: return "unknown status";
     }
 }
 
 const char* gdn_last_hip_error(void) { return g_last_hip_error.c_str(); }
 
+const char* gdn_strerror(int status) {
+    if (status != GDN_ELAUNCH || g_last_hip_error.empty()) return gdn_status_string(status);
+    thread_local std::string text;
+    text = std::string(gdn_status_string(status)) + ": " + g_last_hip_error;
+    return text.c_str();
+}
+
 int gdn_chunk_fwd_workspace_layout(int32_t T, int32_t num_seqs, const int32_t* cu_seqlens_host, int32_t H_q,
                                    int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype,
                                    gdn_workspace_layout* layout) {
-    if (!layout) return GDN_ERR_INVALID;
+    if (!layout) return GDN_EINVAL;
     int rc = check_shapes(H_q, H_v, d_k, d_v, dtype);
     if (rc != GDN_OK) return rc;
     int64_t nc = 0;
@@ -403,9 +409,9 @@ int dev_layout(int32_t T, int32_t num_seqs, int32_t H_q, int32_t H_v, int32_t d_
                gdn_workspace_layout* L, size_t* tab_off, size_t* total) {
     int rc = check_shapes(H_q, H_v, d_k, d_v, dtype);
     if (rc != GDN_OK) return rc;
-    if (T < 0 || num_seqs < 0) return GDN_ERR_INVALID;
+    if (T < 0 || num_seqs < 0) return GDN_EINVAL;
     const int64_t nb = chunk_bound(T, num_seqs);
-    if (nb > (int64_t)INT32_MAX / 1024) return GDN_ERR_UNSUPPORTED;
+    if (nb > (int64_t)INT32_MAX / 1024) return GDN_EUNSUPPORTED;
     rc = layout_for_chunks(nb, H_q, H_v, d_k, d_v, dtype, L);
     if (rc != GDN_OK) return rc;
     const int64_t groups = ((int64_t)num_seqs + gdn::MAX_SEQS_PER_LAUNCH - 1) / gdn::MAX_SEQS_PER_LAUNCH;
@@ -418,8 +424,10 @@ int dev_layout(int32_t T, int32_t num_seqs, int32_t H_q, int32_t H_v, int32_t d_
 
 extern "C" {
 
-size_t gdn_chunk_fwd_workspace_size(int32_t T, int32_t num_seqs, const int32_t* cu_seqlens_host, int32_t H_q,
-                                    int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype) {
+size_t gdn_chunk_fwd_workspace_size(const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H_q, int32_t H_v,
+                                    int32_t d_k, int32_t d_v, gdn_dtype dtype) {
+    if (num_seqs < 0 || (num_seqs > 0 && !cu_seqlens_host)) return 0;
+    const int32_t T = num_seqs > 0 ? cu_seqlens_host[num_seqs] : 0;
     gdn_workspace_layout L;
     if (gdn_chunk_fwd_workspace_layout(T, num_seqs, cu_seqlens_host, H_q, H_v, d_k, d_v, dtype, &L) != GDN_OK)
         return 0;
@@ -429,7 +437,7 @@ size_t gdn_chunk_fwd_workspace_size(int32_t T, int32_t num_seqs, const int32_t* 
 int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                   const int32_t* cu_seqlens_host, int32_t num_seqs, const float* initial_state, void* out,
                   float* final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
-                  gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                  gdn_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return gdn_chunk_fwd_ex(q, k, v, g, beta, cu_seqlens_host, num_seqs, initial_state, out, final_state, T, H_q, H_v,
                             d_k, d_v, scale, dtype, workspace, workspace_bytes, stream, 0u, nullptr, nullptr);
 }
@@ -437,7 +445,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
 int gdn_chunk_fwd_ex(const void* q, const void* k, const void* v, const float* g, const float* beta,
                      const int32_t* cu_seqlens_host, int32_t num_seqs, const float* initial_state, void* out,
                      float* final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
-                     gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream, uint32_t flags,
+                     gdn_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream, uint32_t flags,
                      const gdn_output_gate* gate, void* const* stage_events) {
     return chunk_fwd_impl(q, k, v, g, beta, cu_seqlens_host, num_seqs, initial_state, out, final_state, nullptr, T,
                           H_q, H_v, d_k, d_v, scale, dtype, workspace, workspace_bytes, stream, flags, gate,
@@ -448,8 +456,8 @@ int gdn_chunk_fwd_pooled(const void* q, const void* k, const void* v, const floa
                          const int32_t* cu_seqlens_host, int32_t num_seqs, float* state_pool,
                          const gdn_state_slots* slots, void* out, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k,
                          int32_t d_v, float scale, gdn_dtype dtype, void* workspace, size_t workspace_bytes,
-                         const gdn_output_gate* gate, void* stream) {
-    if (!slots) return GDN_ERR_INVALID;
+                         const gdn_output_gate* gate, hipStream_t stream) {
+    if (!slots) return GDN_EINVAL;
     return chunk_fwd_impl(q, k, v, g, beta, cu_seqlens_host, num_seqs, state_pool, out, state_pool, slots, T, H_q,
                           H_v, d_k, d_v, scale, dtype, workspace, workspace_bytes, stream, 0u, gate, nullptr);
 }
@@ -466,7 +474,7 @@ int gdn_chunk_fwd_dev(const void* q, const void* k, const void* v, const float* 
                       const int32_t* cu_seqlens_dev, int32_t num_seqs, const float* initial_state, void* out,
                       float* final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
                       gdn_dtype dtype, void* workspace, size_t workspace_bytes, const gdn_output_gate* gate,
-                      void* stream) {
+                      hipStream_t stream) {
     if (gate) {
         const int grc = check_gate(gate, T > 0);
         if (grc != GDN_OK) return grc;
@@ -478,19 +486,18 @@ int gdn_chunk_fwd_dev(const void* q, const void* k, const void* v, const float* 
     if (num_seqs == 0) return GDN_OK;
     // T == 0 still runs: every sequence is empty and its final state is its
     // initial state (or zero), as in gdn_chunk_fwd.
-    if (!cu_seqlens_dev || (T > 0 && (!q || !k || !v || !g || !beta || !out))) return GDN_ERR_INVALID;
+    if (!cu_seqlens_dev || (T > 0 && (!q || !k || !v || !g || !beta || !out))) return GDN_EINVAL;
     const void* ptrs[] = {q, k, v, g, beta, out, initial_state, final_state, workspace};
     for (const void* ptr : ptrs)
-        if (ptr && !aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
-    if (reinterpret_cast<uintptr_t>(cu_seqlens_dev) & 3u) return GDN_ERR_UNSUPPORTED;
-    if (!(scale == scale)) return GDN_ERR_INVALID;
-    if (!workspace || workspace_bytes < total) return GDN_ERR_WORKSPACE;
+        if (ptr && !aligned16(ptr)) return GDN_EUNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(cu_seqlens_dev) & 3u) return GDN_EUNSUPPORTED;
+    if (!(scale == scale)) return GDN_EINVAL;
+    if (!workspace || workspace_bytes < total) return GDN_EWORKSPACE;
 
     char* ws = static_cast<char*>(workspace);
     gdn::SeqTable* tabs = reinterpret_cast<gdn::SeqTable*>(ws + tab_off);
-    hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = gdn::launch_build_tables(cu_seqlens_dev, num_seqs, T, initial_state != nullptr,
-                                            final_state != nullptr, tabs, s);
+                                            final_state != nullptr, tabs, stream);
     if (e != hipSuccess) return hip_fail(e);
     gdn::ChunkParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
@@ -511,7 +518,7 @@ int gdn_chunk_fwd_dev(const void* q, const void* k, const void* v, const float* 
         p.tab.num_seqs = ns;
         p.tab.n_chunks = (int32_t)std::min<int64_t>(nb, ((int64_t)T + GDN_CHUNK - 1) / GDN_CHUNK + ns);
         p.dtab = tabs + s0 / gdn::MAX_SEQS_PER_LAUNCH;
-        e = run_chunk(p, dtype, d_k, s, nullptr);
+        e = run_chunk(p, dtype, d_k, stream, nullptr);
         if (e != hipSuccess) return hip_fail(e);
     }
     return GDN_OK;
@@ -521,10 +528,10 @@ int gdn_chunk_fwd_fused(const void* q, const void* k, const void* v, const gdn_f
                         const int32_t* cu_seqlens_host, int32_t num_seqs, float* initial_state, void* out,
                         float* final_state, const gdn_state_slots* slots, int32_t T, int32_t H_q, int32_t H_v,
                         int32_t d_k, int32_t d_v, float scale, gdn_dtype dtype, void* workspace,
-                        size_t workspace_bytes, const gdn_output_gate* gate, void* stream) {
-    if (!front) return GDN_ERR_INVALID;
+                        size_t workspace_bytes, const gdn_output_gate* gate, hipStream_t stream) {
+    if (!front) return GDN_EINVAL;
     if (slots) {  // initial_state is the pool; final_state NULL or the same pool
-        if (final_state && final_state != initial_state) return GDN_ERR_INVALID;
+        if (final_state && final_state != initial_state) return GDN_EINVAL;
         final_state = initial_state;
     }
     return chunk_fwd_impl(q, k, v, nullptr, nullptr, cu_seqlens_host, num_seqs, initial_state, out, final_state,
@@ -534,22 +541,22 @@ int gdn_chunk_fwd_fused(const void* q, const void* k, const void* v, const gdn_f
 
 int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g, const float* beta, float* state,
                        void* out, int32_t N, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
-                       gdn_dtype dtype, void* stream) {
+                       gdn_dtype dtype, hipStream_t stream) {
     int rc = check_shapes(H_q, H_v, d_k, d_v, dtype);
     if (rc != GDN_OK) return rc;
-    if (N < 0) return GDN_ERR_INVALID;
+    if (N < 0) return GDN_EINVAL;
     if (N == 0) return GDN_OK;
-    if ((int64_t)N * H_v > INT32_MAX) return GDN_ERR_UNSUPPORTED;
-    if (!q || !k || !v || !g || !beta || !state || !out) return GDN_ERR_INVALID;
+    if ((int64_t)N * H_v > INT32_MAX) return GDN_EUNSUPPORTED;
+    if (!q || !k || !v || !g || !beta || !state || !out) return GDN_EINVAL;
     const void* ptrs[] = {q, k, v, g, beta, state, out};
     for (const void* ptr : ptrs)
-        if (!aligned16(ptr)) return GDN_ERR_UNSUPPORTED;
-    if (!(scale == scale)) return GDN_ERR_INVALID;
+        if (!aligned16(ptr)) return GDN_EUNSUPPORTED;
+    if (!(scale == scale)) return GDN_EINVAL;
     gdn::DecodeParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.state = state; p.out = out;
     p.slot = nullptr; p.pool = N;
     p.N = N; p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
-    const hipError_t e = run_decode<false>(p, dtype, d_k, static_cast<hipStream_t>(stream));
+    const hipError_t e = run_decode<false>(p, dtype, d_k, stream);
     if (e != hipSuccess) return hip_fail(e);
     return GDN_OK;
 }
@@ -557,8 +564,8 @@ int gdn_recurrent_step(const void* q, const void* k, const void* v, const float*
 int gdn_recurrent_step_fused(const void* q, const void* k, const void* v, const void* a, const void* b,
                              const float* A_log, const float* dt_bias, float* state, void* out, int32_t N,
                              int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale, gdn_dtype dtype,
-                             const gdn_output_gate* gate, void* stream) {
-    if (!state && N > 0) return GDN_ERR_INVALID;
+                             const gdn_output_gate* gate, hipStream_t stream) {
+    if (!state && N > 0) return GDN_EINVAL;
     return step_fused_impl(q, k, v, a, b, A_log, dt_bias, state, nullptr, N, out, N, H_q, H_v, d_k, d_v, scale, dtype,
                            gate, stream);
 }
@@ -567,34 +574,34 @@ int gdn_recurrent_step_fused_pooled(const void* q, const void* k, const void* v,
                                     const float* A_log, const float* dt_bias, float* state_pool, const int32_t* slot,
                                     int32_t pool_size, void* out, int32_t N, int32_t H_q, int32_t H_v, int32_t d_k,
                                     int32_t d_v, float scale, gdn_dtype dtype, const gdn_output_gate* gate,
-                                    void* stream) {
-    if (!slot && N > 0) return GDN_ERR_INVALID;
+                                    hipStream_t stream) {
+    if (!slot && N > 0) return GDN_EINVAL;
     return step_fused_impl(q, k, v, a, b, A_log, dt_bias, state_pool, slot, pool_size, out, N, H_q, H_v, d_k, d_v,
                            scale, dtype, gate, stream);
 }
 
 int gdn_state_rows_zero(void* pool, int32_t pool_size, size_t row_bytes, const int32_t* rows, int32_t n,
-                        void* stream) {
+                        hipStream_t stream) {
     return gdn_state_rows_copy(pool, pool_size, row_bytes, nullptr, rows, n, stream);
 }
 
 int gdn_state_rows_copy(void* pool, int32_t pool_size, size_t row_bytes, const int32_t* src_rows,
-                        const int32_t* dst_rows, int32_t n, void* stream) {
-    if (n < 0 || pool_size < 0 || row_bytes == 0) return GDN_ERR_INVALID;
-    if (row_bytes % 16 != 0) return GDN_ERR_UNSUPPORTED;
+                        const int32_t* dst_rows, int32_t n, hipStream_t stream) {
+    if (n < 0 || pool_size < 0 || row_bytes == 0) return GDN_EINVAL;
+    if (row_bytes % 16 != 0) return GDN_EUNSUPPORTED;
     if (n == 0 || pool_size == 0) return GDN_OK;
-    if (!pool || !dst_rows) return GDN_ERR_INVALID;
+    if (!pool || !dst_rows) return GDN_EINVAL;
     if (!aligned16(pool) || (reinterpret_cast<uintptr_t>(dst_rows) & 3u) ||
         (reinterpret_cast<uintptr_t>(src_rows) & 3u))
-        return GDN_ERR_UNSUPPORTED;
-    if (row_bytes > SIZE_MAX / (size_t)pool_size) return GDN_ERR_INVALID;
+        return GDN_EUNSUPPORTED;
+    if (row_bytes > SIZE_MAX / (size_t)pool_size) return GDN_EINVAL;
     gdn::PoolRowsParams p{};
     p.base = static_cast<char*>(pool);
     p.src = src_rows;
     p.dst = dst_rows;
     p.pool = pool_size;
     p.row16 = row_bytes / 16;
-    const hipError_t e = gdn::launch_pool_rows(p, n, static_cast<hipStream_t>(stream));
+    const hipError_t e = gdn::launch_pool_rows(p, n, stream);
     if (e != hipSuccess) return hip_fail(e);
     return GDN_OK;
 }

@@ -50,17 +50,21 @@ extern "C" {
 #endif
 
 typedef enum gdn_dtype {
-    GDN_DTYPE_F32 = 0,  /* IEEE binary32 */
-    GDN_DTYPE_BF16 = 1, /* bfloat16, round-to-nearest-even on output */
+    GDN_F32 = 0,  /* IEEE binary32 */
+    GDN_BF16 = 1, /* bfloat16, round-to-nearest-even on output */
 } gdn_dtype;
 
 enum {
     GDN_OK = 0,
-    GDN_ERR_INVALID = -1,     /* NULL / inconsistent arguments, bad cu_seqlens */
-    GDN_ERR_UNSUPPORTED = -2, /* d_k != d_v, d not in {64,128}, H_v % H_q != 0, misaligned pointer */
-    GDN_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than gdn_chunk_fwd_workspace_size() */
-    GDN_ERR_HIP = -4,         /* a HIP launch failed; gdn_last_hip_error() names it */
+    GDN_EINVAL = -1,       /* NULL / inconsistent arguments, bad cu_seqlens */
+    GDN_EUNSUPPORTED = -2, /* d_k != d_v, d not in {64,128}, H_v % H_q != 0, misaligned pointer */
+    GDN_EWORKSPACE = -3,   /* workspace NULL or smaller than gdn_chunk_fwd_workspace_size() */
+    GDN_ELAUNCH = -4,      /* a HIP launch failed; gdn_strerror() names the HIP error */
 };
+
+/* The HIP runtime's stream handle, declared here as the runtime declares it so
+ * that callers need not include the HIP headers to use this one. */
+typedef struct ihipStream_t *hipStream_t;
 
 /* Chunk length of the prefill (fixed; section "Chunk-wise Parallel"). */
 #define GDN_CHUNK 64
@@ -110,15 +114,18 @@ typedef struct gdn_workspace_layout {
 /*
  * Host-only.  Validates the batch description and fills `layout`.
  * cu_seqlens_host: HOST int32 [num_seqs + 1], 0 = c[0] <= c[1] <= ... <= c[num_seqs] = T.
- * Returns GDN_OK or GDN_ERR_INVALID / GDN_ERR_UNSUPPORTED.
+ * Returns GDN_OK or GDN_EINVAL / GDN_EUNSUPPORTED.
  */
 int gdn_chunk_fwd_workspace_layout(int32_t T, int32_t num_seqs, const int32_t *cu_seqlens_host, int32_t H_q,
                                    int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype,
                                    gdn_workspace_layout *layout);
 
-/* Host-only.  Bytes of workspace gdn_chunk_fwd needs, or 0 if the arguments are invalid. */
-size_t gdn_chunk_fwd_workspace_size(int32_t T, int32_t num_seqs, const int32_t *cu_seqlens_host, int32_t H_q,
-                                    int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype);
+/* Host-only.  Bytes of workspace gdn_chunk_fwd needs for the batch described by
+ * cu_seqlens_host (T = cu_seqlens_host[num_seqs]; may be NULL when num_seqs == 0),
+ * or 0 if the arguments are invalid (an empty batch needs 0 bytes too;
+ * gdn_chunk_fwd_workspace_layout tells the two cases apart). */
+size_t gdn_chunk_fwd_workspace_size(const int32_t *cu_seqlens_host, int32_t num_seqs, int32_t H_q, int32_t H_v,
+                                    int32_t d_k, int32_t d_v, gdn_dtype dtype);
 
 /*
  * Chunk-wise prefill ("实验三：GDN Prefill 前向优化", sections "计算过程描述" and
@@ -145,7 +152,7 @@ size_t gdn_chunk_fwd_workspace_size(int32_t T, int32_t num_seqs, const int32_t *
 int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
                   const int32_t *cu_seqlens_host, int32_t num_seqs, const float *initial_state, void *out,
                   float *final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
-                  gdn_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
+                  gdn_dtype dtype, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Optional read-out epilogue of gdn_chunk_fwd_ex and gdn_recurrent_step_fused:
@@ -175,7 +182,7 @@ typedef struct gdn_output_gate {
  *   flags  0 or GDN_FWD_KEEP_A.  A is an intermediate nothing downstream reads
  *          back (W and U are formed from it on chip), so gdn_chunk_fwd does not
  *          spend the HBM write on it; GDN_FWD_KEEP_A writes it for inspection.
- *          Unknown bits: GDN_ERR_INVALID.
+ *          Unknown bits: GDN_EINVAL.
  *   gate   NULL, or the read-out epilogue above applied to `out`.
  *   stage_events  NULL or an array of six hipEvent_t created by the caller:
  *          the start and stop events of the three kernels (chunk_prep: gate
@@ -188,7 +195,7 @@ typedef struct gdn_output_gate {
 int gdn_chunk_fwd_ex(const void *q, const void *k, const void *v, const float *g, const float *beta,
                      const int32_t *cu_seqlens_host, int32_t num_seqs, const float *initial_state, void *out,
                      float *final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
-                     gdn_dtype dtype, void *workspace, size_t workspace_bytes, void *stream, uint32_t flags,
+                     gdn_dtype dtype, void *workspace, size_t workspace_bytes, hipStream_t stream, uint32_t flags,
                      const gdn_output_gate *gate, void *const *stage_events);
 
 /*
@@ -216,7 +223,7 @@ int gdn_chunk_fwd_dev(const void *q, const void *k, const void *v, const float *
                       const int32_t *cu_seqlens_dev, int32_t num_seqs, const float *initial_state, void *out,
                       float *final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
                       gdn_dtype dtype, void *workspace, size_t workspace_bytes, const gdn_output_gate *gate,
-                      void *stream);
+                      hipStream_t stream);
 
 /*
  * One recurrent decode step ("Qwen3.5-397B-A17B" trace page, Decode-GDN node 7,
@@ -235,7 +242,7 @@ int gdn_chunk_fwd_dev(const void *q, const void *k, const void *v, const float *
  */
 int gdn_recurrent_step(const void *q, const void *k, const void *v, const float *g, const float *beta, float *state,
                        void *out, int32_t N, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,
-                       gdn_dtype dtype, void *stream);
+                       gdn_dtype dtype, hipStream_t stream);
 
 /*
  * One recurrent decode step with its front end fused in ("Qwen3.5-397B-A17B"
@@ -244,7 +251,7 @@ int gdn_recurrent_step(const void *q, const void *k, const void *v, const float 
  * sequence n and value head h (query/key head h / (H_v / H_q)):
  *     k_bar = k / sqrt(sum_j k_j^2 + 1e-6),   q_bar = scale * q / sqrt(sum_j q_j^2 + 1e-6)
  *     g = -exp(A_log[h]) * softplus(a[n,h] + dt_bias[h]),   alpha = exp(g)
- *         (softplus(x) = x for x > 20, exp(x) for x < -20, log1p(exp(x)) otherwise)
+ *         (softplus(x) = ln(1 + e^x), evaluated without overflow for any x)
  *     beta = sigmoid(b[n,h]) rounded to `dtype` (the bf16 rounding the page keeps)
  *     S = alpha S;  delta = beta (v - k_bar S);  S = S + k_bar^T delta;  o = q_bar S
  * in fp32, one pass over S.  The model's query scale is 1 / sqrt(d_k).
@@ -261,7 +268,7 @@ int gdn_recurrent_step(const void *q, const void *k, const void *v, const float 
 int gdn_recurrent_step_fused(const void *q, const void *k, const void *v, const void *a, const void *b,
                              const float *A_log, const float *dt_bias, float *state, void *out, int32_t N,
                              int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale, gdn_dtype dtype,
-                             const gdn_output_gate *gate, void *stream);
+                             const gdn_output_gate *gate, hipStream_t stream);
 
 /*
  * Short causal depthwise convolution + SiLU with its input history over a
@@ -284,7 +291,7 @@ int gdn_recurrent_step_fused(const void *q, const void *k, const void *v, const 
  */
 int gdn_conv1d_silu_fwd(const void *x, const int32_t *cu_seqlens_host, int32_t num_seqs, int32_t T, int32_t C,
                         int32_t K, const float *weight, const float *bias, const void *initial_state, void *out,
-                        void *final_state, gdn_dtype dtype, void *stream);
+                        void *final_state, gdn_dtype dtype, hipStream_t stream);
 
 /*
  * One decode token of the same convolution for N sequences: x, out dtype
@@ -292,7 +299,7 @@ int gdn_conv1d_silu_fwd(const void *x, const int32_t *cu_seqlens_host, int32_t n
  * one, x appended).  Same constraints as gdn_conv1d_silu_fwd; N == 0 is a no-op.
  */
 int gdn_conv1d_silu_step(const void *x, int32_t N, int32_t C, int32_t K, const float *weight, const float *bias,
-                         void *state, void *out, gdn_dtype dtype, void *stream);
+                         void *state, void *out, gdn_dtype dtype, hipStream_t stream);
 
 /*
  * State pools for serving.  In the "Qwen3.5-397B-A17B" trace page the layer
@@ -309,7 +316,7 @@ int gdn_conv1d_silu_step(const void *x, int32_t N, int32_t C, int32_t K, const f
  *                   a cached prefix, extend_prefix_len > 0), from zeros
  *                   otherwise, and its final state is written back to the
  *                   row.  < 0: starts from zeros, final state not kept.
- *                   >= pool_size, or a row >= 0 named twice: GDN_ERR_INVALID.
+ *                   >= pool_size, or a row >= 0 named twice: GDN_EINVAL.
  *   has_initial     uint8 [num_seqs], or NULL meaning all nonzero.
  *   pool_size       rows in the pool (>= 0).
  * Rows that no sequence names are left untouched.
@@ -325,13 +332,13 @@ typedef struct gdn_state_slots {
  * 16-byte aligned; may be NULL when no slot is >= 0) takes the place of
  * initial_state and final_state, addressed by `slots` as described above.
  * gate as in gdn_chunk_fwd_ex.  Other arguments, results and errors as
- * gdn_chunk_fwd; slots == NULL: GDN_ERR_INVALID.
+ * gdn_chunk_fwd; slots == NULL: GDN_EINVAL.
  */
 int gdn_chunk_fwd_pooled(const void *q, const void *k, const void *v, const float *g, const float *beta,
                          const int32_t *cu_seqlens_host, int32_t num_seqs, float *state_pool,
                          const gdn_state_slots *slots, void *out, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k,
                          int32_t d_v, float scale, gdn_dtype dtype, void *workspace, size_t workspace_bytes,
-                         const gdn_output_gate *gate, void *stream);
+                         const gdn_output_gate *gate, hipStream_t stream);
 
 /*
  * gdn_conv1d_silu_fwd over a history pool: state_pool dtype [pool_size, K-1, C]
@@ -340,7 +347,7 @@ int gdn_chunk_fwd_pooled(const void *q, const void *k, const void *v, const floa
  */
 int gdn_conv1d_silu_fwd_pooled(const void *x, const int32_t *cu_seqlens_host, int32_t num_seqs, int32_t T, int32_t C,
                                int32_t K, const float *weight, const float *bias, void *state_pool,
-                               const gdn_state_slots *slots, void *out, gdn_dtype dtype, void *stream);
+                               const gdn_state_slots *slots, void *out, gdn_dtype dtype, hipStream_t stream);
 
 /*
  * Decode steps over a state pool.  slot: DEVICE int32 [N] (4-byte aligned),
@@ -351,17 +358,17 @@ int gdn_conv1d_silu_fwd_pooled(const void *x, const int32_t *cu_seqlens_host, in
  * be distinct.  Otherwise as gdn_recurrent_step_fused / gdn_conv1d_silu_step,
  * with state_pool (fp32 [pool_size, H_v, d_k, d_v], resp. dtype
  * [pool_size, K-1, C]) updated in place.  slot == NULL with N > 0:
- * GDN_ERR_INVALID.
+ * GDN_EINVAL.
  */
 int gdn_recurrent_step_fused_pooled(const void *q, const void *k, const void *v, const void *a, const void *b,
                                     const float *A_log, const float *dt_bias, float *state_pool, const int32_t *slot,
                                     int32_t pool_size, void *out, int32_t N, int32_t H_q, int32_t H_v, int32_t d_k,
                                     int32_t d_v, float scale, gdn_dtype dtype, const gdn_output_gate *gate,
-                                    void *stream);
+                                    hipStream_t stream);
 
 int gdn_conv1d_silu_step_pooled(const void *x, int32_t N, int32_t C, int32_t K, const float *weight,
                                 const float *bias, void *state_pool, const int32_t *slot, int32_t pool_size,
-                                void *out, gdn_dtype dtype, void *stream);
+                                void *out, gdn_dtype dtype, hipStream_t stream);
 
 /*
  * Front end of the prefill ("Qwen3.5-397B-A17B" trace page, section 1,
@@ -369,8 +376,8 @@ int gdn_conv1d_silu_step_pooled(const void *x, int32_t N, int32_t C, int32_t K, 
  * L2-normalise q and k), done inside the chunk kernels as rows are staged:
  *     k_bar = k / sqrt(sum_j k_j^2 + 1e-6),  q_bar = q / sqrt(sum_j q_j^2 + 1e-6)
  *             (each rounded to dtype, as the normalisation nodes write them)
- *     g     = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h])   (the +-20 branches
- *             of gdn_recurrent_step_fused)
+ *     g     = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h])   (as in
+ *             gdn_recurrent_step_fused)
  *     beta  = sigmoid(b[t,h]) rounded to dtype
  * then the chunk form of gdn_chunk_fwd on (q_bar, k_bar, v, g, beta); the output
  * scale is the `scale` argument (the model's 1 / sqrt(d_k)).
@@ -392,13 +399,13 @@ typedef struct gdn_front_end {
  *           initial_state is a state pool addressed by slots (see
  *           gdn_state_slots) and final_state must be NULL or the same pointer.
  *   gate    NULL, or the read-out epilogue (gdn_output_gate) applied to out.
- * front == NULL: GDN_ERR_INVALID.  The workspace is gdn_chunk_fwd's.
+ * front == NULL: GDN_EINVAL.  The workspace is gdn_chunk_fwd's.
  */
 int gdn_chunk_fwd_fused(const void *q, const void *k, const void *v, const gdn_front_end *front,
                         const int32_t *cu_seqlens_host, int32_t num_seqs, float *initial_state, void *out,
                         float *final_state, const gdn_state_slots *slots, int32_t T, int32_t H_q, int32_t H_v,
                         int32_t d_k, int32_t d_v, float scale, gdn_dtype dtype, void *workspace,
-                        size_t workspace_bytes, const gdn_output_gate *gate, void *stream);
+                        size_t workspace_bytes, const gdn_output_gate *gate, hipStream_t stream);
 
 /*
  * Pool row maintenance (the "Kestrel_VLLM - 24" page, section 五, resets its
@@ -415,11 +422,17 @@ int gdn_chunk_fwd_fused(const void *q, const void *k, const void *v, const gdn_f
  * branches).  n == 0 is a no-op.
  */
 int gdn_state_rows_zero(void *pool, int32_t pool_size, size_t row_bytes, const int32_t *rows, int32_t n,
-                        void *stream);
+                        hipStream_t stream);
 int gdn_state_rows_copy(void *pool, int32_t pool_size, size_t row_bytes, const int32_t *src_rows,
-                        const int32_t *dst_rows, int32_t n, void *stream);
+                        const int32_t *dst_rows, int32_t n, hipStream_t stream);
 
-/* Static string naming a status code. */
+/* Text naming a status code.  For GDN_ELAUNCH it also names the last HIP error
+ * this thread saw inside the library (the text is then thread-local and valid
+ * until the next call into the library from this thread); otherwise, and for
+ * codes it does not know, a static string. */
+const char *gdn_strerror(int status);
+
+/* Static string naming a status code (gdn_strerror without the HIP error). */
 const char *gdn_status_string(int status);
 
 /* Text of the last HIP error seen by this thread inside the library ("" if none). */

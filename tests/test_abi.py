@@ -33,7 +33,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(gdn):
     names = _declared()
-    assert {"gdn_chunk_fwd", "gdn_recurrent_step", "gdn_chunk_fwd_workspace_size"} <= set(names)
+    assert {"gdn_chunk_fwd", "gdn_recurrent_step", "gdn_chunk_fwd_workspace_size", "gdn_strerror"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", gdn.lib_path()], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT (gdn_\w+)", out))
@@ -57,6 +57,42 @@ def test_status_strings(gdn):
     assert lib.gdn_status_string(-3).startswith(b"workspace")
     assert lib.gdn_version().startswith(b"0.")
     assert lib.gdn_last_hip_error() == b""
+    # gdn_strerror: the same texts while no HIP error has been recorded
+    for status in (0, -1, -2, -3, -4, -99, 5):
+        assert lib.gdn_strerror(status) == lib.gdn_status_string(status)
+
+
+def test_contract_names_compile(tmp_path):
+    # The names and signatures a caller coded to the documented boundary uses
+    # (status and dtype enums, hipStream_t, the workspace query on cu_seqlens).
+    src = tmp_path / "c.c"
+    src.write_text(r'''
+#include "gdn.h"
+int main(void) {
+    const int32_t cu[3] = {0, 100, 164};
+    size_t ws = gdn_chunk_fwd_workspace_size(cu, 2, 16, 32, 128, 128, GDN_BF16);
+    hipStream_t s = 0;
+    int (*fwd)(const void *, const void *, const void *, const float *, const float *, const int32_t *, int32_t,
+               const float *, void *, float *, int32_t, int32_t, int32_t, int32_t, int32_t, float, gdn_dtype,
+               void *, size_t, hipStream_t) = gdn_chunk_fwd;
+    int (*step)(const void *, const void *, const void *, const float *, const float *, float *, void *, int32_t,
+                int32_t, int32_t, int32_t, int32_t, float, gdn_dtype, hipStream_t) = gdn_recurrent_step;
+    const char *(*err)(int) = gdn_strerror;
+    int codes[] = {GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_ELAUNCH, GDN_F32};
+    return (ws == 0) + (s != 0) + (fwd == 0) + (step == 0) + (err == 0) + codes[0];
+}
+''')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), "-c", str(src), "-o",
+                    str(tmp_path / "c.o")], check=True)
+
+
+def test_workspace_size_contract(gdn):
+    lib = gdn.load_library()
+    assert lib.gdn_chunk_fwd_workspace_size(_cu([0, 100, 164]), 2, 16, 32, 128, 128, 1) == \
+        gdn.workspace_layout(164, [0, 100, 164], 16, 32, 128, 128, "bf16")["total_bytes"]
+    assert lib.gdn_chunk_fwd_workspace_size(None, 0, 16, 32, 128, 128, 1) == 0  # empty batch: nothing needed
+    assert lib.gdn_chunk_fwd_workspace_size(None, 2, 16, 32, 128, 128, 1) == 0  # missing cu_seqlens
+    assert lib.gdn_chunk_fwd_workspace_size(_cu([0, 5, 3]), 2, 16, 32, 128, 128, 1) == 0
 
 
 def _cu(vals):
@@ -98,8 +134,12 @@ def test_layout_validation(gdn, args, status):
     lay = gdn.WorkspaceLayout()
     rc = lib.gdn_chunk_fwd_workspace_layout(T, len(cu) - 1, _cu(cu), H_q, H_v, dk, dv, dt, ctypes.byref(lay))
     assert rc == status
-    size = lib.gdn_chunk_fwd_workspace_size(T, len(cu) - 1, _cu(cu), H_q, H_v, dk, dv, dt)
-    assert (size > 0) == (status == 0)
+    # the size query takes T from cu_seqlens itself, so a cu[N] != T batch is a
+    # valid batch of cu[N] tokens there
+    size = lib.gdn_chunk_fwd_workspace_size(_cu(cu), len(cu) - 1, H_q, H_v, dk, dv, dt)
+    assert (size > 0) == (status == 0 or cu[-1] != T)
+    if status == 0:
+        assert size == lay.total_bytes
 
 
 def _fake(n=1):
@@ -335,7 +375,7 @@ def test_dev_seqlens_prefill_rejects_before_any_device_work(gdn):
     lib = gdn.load_library()
     keep, p = _fake()
     assert lib.gdn_chunk_fwd_dev_workspace_size(4096, 1, 16, 32, 128, 128, 1) > \
-        lib.gdn_chunk_fwd_workspace_size(4096, 1, _cu([0, 4096]), 16, 32, 128, 128, 1)
+        lib.gdn_chunk_fwd_workspace_size(_cu([0, 4096]), 1, 16, 32, 128, 128, 1)
     assert lib.gdn_chunk_fwd_dev_workspace_size(100, 1, 3, 4, 64, 64, 1) == 0     # H_v % H_q != 0
 
     def call(**kw):
