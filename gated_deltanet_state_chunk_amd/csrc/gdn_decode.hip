@@ -12,8 +12,8 @@
 //
 // The fused variant takes the raw inputs of that node instead (its first two
 // steps): k_bar = k / sqrt(sum k^2 + 1e-6), q_bar = scale q / sqrt(sum q^2 +
-// 1e-6), g = -exp(A_log) softplus(a + dt_bias) (softplus with the +-20 overflow
-// branches of the "Kestrel_VLLM - 24" page, section 三), beta = sigmoid(b)
+// 1e-6), g = -exp(A_log) softplus(a + dt_bias) (softplus(x) = ln(1 + e^x) in
+// an overflow-free form, front_gate), beta = sigmoid(b)
 // rounded to the input dtype (bf16 keeps that rounding, as the trace page
 // notes).  The two sums of squares ride along with the column reductions, and
 // the norms are applied as scalars afterwards, so the state is still read

@@ -262,13 +262,15 @@ __device__ __forceinline__ float4 l2norm_piece(float4 raw) {
 __device__ __forceinline__ float silu_f32(float x) { return x * __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 // ---- gate transform of the front end ---------------------------------------
-// g = -exp(A_log) softplus(a + dt_bias), softplus(x) = x for x > 20, exp(x)
-// for x < -20, log1p(exp(x)) otherwise; beta = sigmoid(b) rounded to T.
+// g = -exp(A_log) softplus(a + dt_bias), with softplus(x) = ln(1 + e^x) taken
+// as max(x, 0) + ln(1 + e^-|x|): the exponential never overflows, and where |x|
+// is large the correction term drops below rounding of its own accord (above
+// x = 17 it is under half an fp32 ulp of x; below x = -88 e^x underflows).
 __device__ __forceinline__ float front_gate(float a, float A_log, float dt_bias) {
-    const float xa = a + dt_bias;
-    const float sp = xa > 20.f ? xa : (xa < -20.f ? expf(xa) : log1pf(expf(xa)));
-    return -expf(A_log) * sp;
+    const float x = a + dt_bias;
+    return -expf(A_log) * (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))));
 }
+// beta = sigmoid(b) rounded to T (the activation dtype the gating hands on).
 template <typename T>
 __device__ __forceinline__ float front_beta(float b) {
     return to_f32<T>(from_f32<T>(1.f / (1.f + expf(-b))));

@@ -25,8 +25,8 @@ a hand-derived d = 2 worked example (tests/golden/).
 
 ``decode_step_fused`` adds the decode front end (q/k L2 norm, gate from a,
 A_log, dt_bias, beta from b).  Pins: softplus(x) - softplus(-x) = x and
-softplus(0) = ln 2 through the returned gate, the overflow branches against
-the exact softplus, sigmoid's logit identity and exact bf16 representability
+softplus(0) = ln 2 through the returned gate (over |x| up to 60, where a
+naive exponential would overflow), softplus(x) -> x and -> e^x in its tails, sigmoid's logit identity and exact bf16 representability
 of the rounded beta, invariance of the step under scaling q or k (L2 norm),
 zero keys reducing to pure decay, and the page's merged update
 S' = alpha (I - beta k^T k) S + beta k^T v evaluated with numpy matrices.
@@ -39,7 +39,7 @@ linearity in the weight.
 ``prefill_front_end`` / ``forward_fused`` add the prefill front end (q/k L2
 norm, gate and beta from the raw projections; oracle/front_end.py) before
 ``forward``.  Pins: the gate and beta equal those of the independent C decode
-oracle (``decode_step_fused``) across the softplus branches; with fp32 inputs
+oracle (``decode_step_fused``) over gate inputs from -60 to 60; with fp32 inputs
 ``forward_fused`` over a sequence equals the C fused decode step applied token
 by token; normalised rows have unit norm, are invariant under scaling the raw
 row and keep zero rows zero; bf16-rounded results are exactly representable.

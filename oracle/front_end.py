@@ -6,8 +6,7 @@ and beta; nodes 9 and 10 L2-normalise q and k), in fp64:
 
     q_bar = q / sqrt(sum_j q_j^2 + 1e-6)       (per token and head, over d_k)
     k_bar = k / sqrt(sum_j k_j^2 + 1e-6)
-    g     = -exp(A_log[h]) * softplus(a[t, h] + dt_bias[h])
-            softplus(x) = x for x > 20, exp(x) for x < -20, log1p(exp(x)) otherwise
+    g     = -exp(A_log[h]) * softplus(a[t, h] + dt_bias[h]),  softplus(x) = ln(1 + e^x)
     beta  = sigmoid(b[t, h])
 
 The normalisation and gating nodes hand their results to the chunk kernels in
@@ -28,10 +27,10 @@ def round_bf16(x):
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
-def softplus_branchy(x):
+def softplus(x):
+    """ln(1 + e^x), elementwise, as max(x, 0) + ln(1 + e^-|x|) so that nothing overflows."""
     x = np.asarray(x, dtype=np.float64)
-    mid = np.log1p(np.exp(np.clip(x, -20.0, 20.0)))
-    return np.where(x > 20.0, x, np.where(x < -20.0, np.exp(x), mid))
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
 
 
 def l2_normalise(x):
@@ -48,7 +47,7 @@ def prefill_front_end(q, k, a, b, A_log, dt_bias, round_to_bf16):
     b = np.asarray(b, dtype=np.float64)
     A_log = np.asarray(A_log, dtype=np.float64)
     dt_bias = np.asarray(dt_bias, dtype=np.float64)
-    g = -np.exp(A_log)[None, :] * softplus_branchy(a + dt_bias[None, :])
+    g = -np.exp(A_log)[None, :] * softplus(a + dt_bias[None, :])
     sig = (1.0 / (1.0 + np.exp(-b))).astype(np.float32).astype(np.float64)
     if round_to_bf16:
         return round_bf16(qn), round_bf16(kn), g, round_bf16(sig)

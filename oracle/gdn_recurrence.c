@@ -179,10 +179,12 @@ int gdn_oracle_decode_step(const float *q, const float *k, const float *v, const
  *   k_bar = k / sqrt(sum_j k_j^2 + 1e-6),  q_bar = scale * q / sqrt(sum_j q_j^2 + 1e-6)
  *     (an L2 norm over the sum of squares, not an RMS norm; the query scale
  *     multiplies once, after the norm)
- *   g = -exp(A_log[h]) * softplus(a + dt_bias[h]),  alpha = exp(g)
- *     softplus with the overflow branches of the "Kestrel_VLLM - 24" page,
- *     section 三 (its beta/g kernel): x if x > 20, exp(x) if x < -20, else
- *     log1p(exp(x))
+ *   g = -exp(A_log[h]) * softplus(a + dt_bias[h]),  alpha = exp(g),
+ *     softplus(x) = ln(1 + e^x) (the gate of the trace page's node 7; the
+ *     "Kestrel_VLLM - 24" page, section 三, guards its exponential against
+ *     overflow with branches at +-20, which change the value by less than
+ *     fp32 rounding; here the overflow-free form max(x, 0) + ln(1 + e^-|x|)
+ *     gives the exact value)
  *   beta = sigmoid(b), rounded to bf16 and back when beta_round_bf16 (the
  *     trace page keeps that rounding when b is bf16); sigmoid is taken in fp64
  *     and rounded to fp32 first, the precision the pages' kernels work in
@@ -190,11 +192,7 @@ int gdn_oracle_decode_step(const float *q, const float *k, const float *v, const
  *   a, b: [N, H_v] (exact values the device receives); A_log, dt_bias: [H_v]
  *   g_out, beta_out: [N, H_v] double or NULL (the gate and beta used)
  */
-static double softplus_branchy(double x) {
-    if (x > 20.0) return x;
-    if (x < -20.0) return exp(x);
-    return log1p(exp(x));
-}
+static double softplus(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
 
 /* fp32 -> bf16 (round to nearest even) -> fp32; inputs here are finite. */
 static float round_bf16(float x) {
@@ -240,7 +238,7 @@ int gdn_oracle_decode_step_fused(const float *q, const float *k, const float *v,
             qn[i] = (double)qr[i] * rq;
             kn[i] = (double)kr[i] * rk;
         }
-        const double g = -exp((double)A_log[h]) * softplus_branchy((double)a[n * H_v + h] + (double)dt_bias[h]);
+        const double g = -exp((double)A_log[h]) * softplus((double)a[n * H_v + h] + (double)dt_bias[h]);
         float sig = (float)(1.0 / (1.0 + exp(-(double)b[n * H_v + h])));
         if (beta_round_bf16) sig = round_bf16(sig);
         const double beta = (double)sig;
