@@ -165,6 +165,31 @@ def test_a_region_untouched_without_keep_a(torch_cuda):
 # ---------------------------------------------------------------------------
 # Per-stage intermediates against the chunk-form oracle
 # ---------------------------------------------------------------------------
+def _x_bound(r, inp, n, h, c, d, dtype, tol_h):
+    """Worst-case error of the stored X = U - W S of one chunk, relative to max|X|,
+    from the roundings on its path: the A and B V (B Gamma K) operands of U (W),
+    U and W themselves, the S operand, X itself (unit u each: 2^-9 for bf16,
+    2^-24 for fp32), fp32 accumulation over the 64 positions or d_k rows
+    (2^-24 per term), and the chunk-start state's own error, taken at the
+    tolerance h is held to (tol_h max|h|).  Each product term is bounded by the
+    sums of |a| |b| (no cancellation assumed), so this is a bound, not an
+    estimate; it depends on the inputs, not on the device result."""
+    u = 2.0 ** -9 if dtype == "bf16" else 2.0 ** -24
+    ua = 2.0 ** -24
+    ell = r["U"].shape[0]
+    t0 = int(inp.cu_seqlens[n]) + 64 * c
+    hq = h // (inp.H_v // inp.H_q)
+    V = inp.v32()[t0:t0 + ell, h].astype(np.float64)
+    K = inp.k32()[t0:t0 + ell, hq].astype(np.float64)
+    b = inp.beta[t0:t0 + ell, h].astype(np.float64)
+    A, S, W, U, X = (np.abs(r[key]) for key in ("A", "h", "W", "U", "X"))
+    BV, BGK = np.abs(b[:, None] * V), np.abs((b * np.exp(r["gc"]))[:, None] * K)
+    dU = (2 * u + 64 * ua) * (A @ BV) + u * U
+    dW = (2 * u + 64 * ua) * (A @ BGK) + u * W
+    dX = dU + dW @ S + (u + d * ua) * (W @ S) + W.sum(1, keepdims=True) * tol_h * S.max() + u * X
+    return float(dX.max() / X.max())
+
+
 @pytest.mark.parametrize("dtype,d,tol", [("f32", 64, 1e-4), ("bf16", 128, 1e-2)])
 def test_chunk_intermediates_match_chunk_form(torch_cuda, dtype, d, tol):
     import gated_deltanet_state_chunk_amd as gdn
@@ -223,7 +248,9 @@ def test_chunk_intermediates_match_chunk_form(torch_cuda, dtype, d, tol):
                 assert rel_err(W[ci, h, :ell], r["W"]) < tol
                 assert rel_err(U[ci, h, :ell], r["U"]) < tol
                 assert rel_err(Hs[ci, h], r["h"]) < tol
-                assert rel_err(X[ci, h, :ell], r["X"]) < 3 * tol
+                x_tol = max(tol, _x_bound(r, inp, n, h, c, d, dtype, tol)) if dtype == "f32" else \
+                    _x_bound(r, inp, n, h, c, d, dtype, tol)
+                assert rel_err(X[ci, h, :ell], r["X"]) < x_tol, (n, h, c, x_tol)
                 assert np.all(W[ci, h, ell:] == 0) and np.all(X[ci, h, ell:] == 0)
                 # keys of the state update carry the decay to the chunk end: gamma_l / gamma_r
                 assert rel_err(kf[ci, h, :ell], np.exp(r["gc"][-1] - r["gc"])) < 1e-5
