@@ -16,7 +16,7 @@ import math
 import os
 from typing import Optional, Sequence
 
-__all__ = ["chunk_fwd", "recurrent_step", "recurrent_step_fused", "conv1d_silu", "conv1d_silu_step",
+__all__ = ["chunk_fwd", "chunk_fwd_scratch", "SCRATCH_BYTES", "recurrent_step", "recurrent_step_fused", "conv1d_silu", "conv1d_silu_step",
            "chunk_fwd_fused", "chunk_fwd_dev", "chunk_fwd_pooled", "conv1d_silu_pooled", "recurrent_step_fused_pooled", "conv1d_silu_step_pooled",
            "state_rows_zero", "state_rows_copy", "workspace_layout", "workspace_size", "lib_path", "load_library",
            "GdnError", "CHUNK", "DTYPE_F32", "DTYPE_BF16"]
@@ -29,6 +29,7 @@ _lib = None
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 FWD_KEEP_A = 1  # gdn_chunk_fwd_ex flag: also write A to the workspace
+SCRATCH_BYTES = 256 << 20  # GDN_SCRATCH_BYTES: the static workspace of gdn_chunk_fwd_scratch
 
 _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace", -4: "hip"}
 
@@ -136,6 +137,8 @@ def load_library():
                                   ctypes.c_size_t, P]
     lib.gdn_chunk_fwd.restype = ctypes.c_int
     lib.gdn_chunk_fwd_ex.argtypes = lib.gdn_chunk_fwd.argtypes + [ctypes.c_uint32, P, P]
+    lib.gdn_chunk_fwd_scratch.argtypes = [P, P, P, P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P]
+    lib.gdn_chunk_fwd_scratch.restype = ctypes.c_int
     lib.gdn_chunk_fwd_ex.restype = ctypes.c_int
     lib.gdn_recurrent_step.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P]
     lib.gdn_recurrent_step.restype = ctypes.c_int
@@ -324,6 +327,47 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens: Sequence[int], initial_state=None, s
         rc, name = lib.gdn_chunk_fwd(*args), "gdn_chunk_fwd"
     if rc != 0:
         raise GdnError(rc, name)
+    return out, final_state
+
+
+def chunk_fwd_scratch(q, k, v, g, beta, cu_seqlens: Sequence[int], initial_state=None,
+                      scale: Optional[float] = None, out=None, final_state=None, stream=None):
+    """chunk_fwd whose workspace is the library's static device array
+    (gdn_chunk_fwd_scratch): the C call allocates nothing.  ``out`` and
+    ``final_state`` must be preallocated by callers that cannot allocate (this
+    wrapper allocates them only when they are None).  Batches needing more than
+    SCRATCH_BYTES of workspace are refused (GdnError, workspace).  Calls that
+    overlap in time on one GPU share the array and race."""
+    torch = _torch()
+    lib = load_library()
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("g", g, torch.float32)
+    _check_dev("beta", beta, torch.float32)
+    T, H_q, d_k = q.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    if k.shape != q.shape or v.shape[0] != T or g.shape != (T, H_v) or beta.shape != (T, H_v):
+        raise ValueError("inconsistent q/k/v/g/beta shapes")
+    cu = _host_cu(cu_seqlens)
+    N = len(cu) - 1
+    if initial_state is not None:
+        _check_buf("initial_state", initial_state, torch.float32, (N, H_v, d_k, d_v))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    if out is None:
+        out = torch.empty((T, H_v, d_v), dtype=q.dtype, device=q.device)
+    else:
+        _check_buf("out", out, q.dtype, (T, H_v, d_v))
+    if final_state is None:
+        final_state = torch.empty((N, H_v, d_k, d_v), dtype=torch.float32, device=q.device)
+    else:
+        _check_buf("final_state", final_state, torch.float32, (N, H_v, d_k, d_v))
+    rc = lib.gdn_chunk_fwd_scratch(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), cu, N, _ptr(initial_state),
+                                   _ptr(out), _ptr(final_state), T, H_q, H_v, d_k, d_v, float(scale), dt,
+                                   _stream_ptr(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_chunk_fwd_scratch")
     return out, final_state
 
 

@@ -151,10 +151,8 @@ hipError_t run_decode(const gdn::DecodeParams& p, gdn_dtype dt, int d, hipStream
 int layout_for_chunks(int64_t nc, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, gdn_dtype dtype,
                       gdn_workspace_layout* layout);
 
-int hip_fail(hipError_t e) {
-    g_last_hip_error = hipGetErrorString(e);
-    return GDN_ELAUNCH;
-}
+using gdn::hip_fail;
+
 
 int conv_fwd_impl(const void* x, const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t T, int32_t C, int32_t K,
                   const float* weight, const float* bias, const void* s_in, void* out, void* s_out,
@@ -308,6 +306,11 @@ int step_fused_impl(const void* q, const void* k, const void* v, const void* a, 
 }
 
 }  // namespace
+
+int gdn::hip_fail(hipError_t e) {
+    g_last_hip_error = hipGetErrorString(e);
+    return GDN_ELAUNCH;
+}
 
 extern "C" {
 

@@ -138,4 +138,8 @@ hipError_t launch_conv_step(const ConvParams& p, int N, hipStream_t stream);
 
 hipError_t launch_pool_rows(PoolRowsParams p, int32_t n, hipStream_t stream);
 
+// Records e as this thread's last HIP error (named by gdn_strerror) and returns
+// GDN_ELAUNCH (gdn_api.cpp).
+int hip_fail(hipError_t e);
+
 }  // namespace gdn

@@ -226,6 +226,31 @@ int gdn_chunk_fwd_dev(const void *q, const void *k, const void *v, const float *
                       hipStream_t stream);
 
 /*
+ * gdn_chunk_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and results, with the workspace taken from a static device
+ * array of GDN_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * (placed when its code object is loaded; kept until the process ends).  The
+ * first call on a device looks up that device's copy (no allocation); the call
+ * allocates nothing.  Arguments, results and errors as gdn_chunk_fwd, except:
+ *   - a batch whose workspace (gdn_chunk_fwd_workspace_size) exceeds
+ *     GDN_SCRATCH_BYTES returns GDN_EWORKSPACE before any HIP call (256 MiB:
+ *     one 4096-token sequence at H_v = 32, d = 128, bf16 needs 193 MiB);
+ *   - the workspace contents after the call are those of gdn_chunk_fwd, in the
+ *     library's array, and are overwritten by the next call.
+ * All calls on one GPU share its array: calls that overlap in time on one GPU
+ * (on different streams, or from several host threads without ordering) race
+ * and give undefined results.  Calls in stream order on one stream are safe:
+ * every region a call reads is written earlier in the same call, so nothing
+ * left by a previous call needs clearing.
+ */
+#define GDN_SCRATCH_BYTES (256u << 20)
+int gdn_chunk_fwd_scratch(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                          const int32_t *cu_seqlens_host, int32_t num_seqs, const float *initial_state, void *out,
+                          float *final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v,
+                          float scale, gdn_dtype dtype, hipStream_t stream);
+
+/*
  * One recurrent decode step ("Qwen3.5-397B-A17B" trace page, Decode-GDN node 7,
  * gdn_packed_recurrent_qk_norm_gating_state_update — its decay, delta update and
  * read; the Q/K normalisation and gate transform of that node are not part of

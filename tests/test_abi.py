@@ -405,3 +405,25 @@ def test_binding_refuses_host_tensors(gdn):
         gdn.chunk_fwd(q, q, torch.zeros(4, 4, 64), torch.zeros(4, 4), torch.zeros(4, 4), [0, 4])
     with pytest.raises(TypeError):
         gdn.chunk_fwd(q.to(torch.float16), q, q, q, q, [0, 4])
+
+
+def test_scratch_prefill_refuses_before_any_device_work(gdn):
+    """gdn_chunk_fwd_scratch: an invalid batch, or one whose workspace exceeds
+    the static array, is refused on the host (no GPU here: any HIP call would
+    fail with GDN_ELAUNCH instead)."""
+    lib = gdn.load_library()
+    keep, p = _fake()
+    assert gdn.SCRATCH_BYTES == 256 << 20
+
+    def call(cu, T, H_q=16, H_v=32, d=128, dt=1, **kw):
+        a = dict(q=p, k=p, v=p, g=p, beta=p, s0=None, out=p, fin=p, scale=0.1)
+        a.update(kw)
+        return lib.gdn_chunk_fwd_scratch(a["q"], a["k"], a["v"], a["g"], a["beta"], _cu(cu), len(cu) - 1, a["s0"],
+                                         a["out"], a["fin"], T, H_q, H_v, d, d, a["scale"], dt, None)
+
+    need = lambda T: lib.gdn_chunk_fwd_workspace_size(_cu([0, T]), 1, 16, 32, 128, 128, 1)  # noqa: E731
+    assert need(4096) <= gdn.SCRATCH_BYTES < need(8192)
+    assert call([0, 8192], 8192) == -3          # 8192 tokens at 32 heads: beyond the array
+    assert call([0, 4096], 4000) == -1          # cu[N] != T
+    assert call([0, 100], 100, H_q=3) == -2
+    assert call([0], 0) == 0                    # empty batch: no-op
