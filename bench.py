@@ -41,7 +41,15 @@ METRIC = "GDN prefill tokens/s (Hv=32,d=128,T=4096) + MFMA util; decode state GB
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 FP32_MFMA_PEAK_TFLOPS = 157.3
-STAGES = ["chunk_prep", "chunk_state_h", "chunk_output_o"]
+# Kernels of one prefill launch, in stream order.  bf16: the output is formed
+# inside the state scan and the third slot is the gated read-out pass (empty
+# without the read-out); fp32: the separate output kernel.
+STAGES_BF16 = ["chunk_prep", "chunk_state_o", "gated_readout"]
+STAGES_F32 = ["chunk_prep", "chunk_state_h", "chunk_output_o"]
+
+
+def stages_for(dtype):
+    return STAGES_BF16 if dtype == "bf16" else STAGES_F32
 CHUNK = 64
 
 
@@ -55,9 +63,14 @@ def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True, gated=False):
     """Algorithmic bytes and flops of each kernel of one gdn_chunk_fwd.
 
     Bytes: every distinct input read once, every output and intermediate written
-    once and read once per consuming kernel (K is read once per key head); A is
-    consumed inside chunk_prep and never written (gdn_chunk_fwd does not keep it).
-    Flops: 2 x multiply-adds of the chunk form at full chunks, triangles exploited.
+    once and read once per consuming kernel (K and Q are read once per key
+    head); A is consumed inside chunk_prep and never written.  bf16 (es = 2):
+    chunk_prep also forms P (the masked, decayed Q K^T, six 1 KiB fragments per
+    chunk and value head), the state scan forms the output from P, q and its
+    own on-chip h and U - W S, and the gated read-out (when asked for) is a
+    pass over the output.  fp32: the chunk-start states h and U - W S go
+    through HBM to a separate output kernel.  Flops: 2 x multiply-adds of the
+    chunk form at full chunks, triangles exploited.
     """
     C = CHUNK
     chv, chq = n_chunks * H_v, n_chunks * H_q
@@ -70,18 +83,25 @@ def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True, gated=False):
     Kc_b = chq * C * d * es  # the state update's copy of the keys, one per key head
     H_b = chv * d * d * es
     S_b = N * H_v * d * d * 4
+    P_b = chv * 6 * 1024
     tri = C * (C - 1) // 2   # strictly lower entries
     tri1 = C * (C + 1) // 2  # lower incl. diagonal
-    per = {  # multiply-adds per (chunk, value head)
-        "chunk_prep": tri * d + C ** 3 // 6 + 2 * tri1 * d,   # K K^T, solve, W, U
-        "chunk_state_h": 2 * C * d * d,                      # W S, Kc^T (kf X)
-        "chunk_output_o": C * d * d + 2 * tri1 * d,          # Q S, Q K^T, P X
-    }
-    bytes_ = {
-        "chunk_prep": k_b + v_b + 2 * gate_b + gc_b + W_b + U_b + kf_b + Kc_b,   # A stays on chip
-        "chunk_state_h": W_b + U_b + Kc_b + kf_b + gc_b + (S_b if has_s0 else 0) + H_b + X_b + S_b,
-        "chunk_output_o": q_b + k_b + gc_b + H_b + X_b + o_b + ((o_b + d * 4) if gated else 0),  # z, weight
-    }
+    prep = tri * d + C ** 3 // 6 + 2 * tri1 * d          # K K^T, solve, W, U
+    s0 = S_b if has_s0 else 0
+    if es == 2:
+        per = {"chunk_prep": prep + tri1 * d,                              # + Q K^T
+               "chunk_state_o": 2 * C * d * d + C * d * d + tri1 * d,      # W S, Kc^T (kf X), Q S, P X
+               "gated_readout": 0}
+        bytes_ = {"chunk_prep": k_b + v_b + 2 * gate_b + gc_b + W_b + U_b + kf_b + Kc_b + q_b + P_b,
+                  "chunk_state_o": W_b + U_b + Kc_b + kf_b + gc_b + P_b + q_b + s0 + S_b + o_b,
+                  "gated_readout": (3 * o_b + d * 4) if gated else 0}      # o read, z read, out written
+    else:
+        per = {"chunk_prep": prep,
+               "chunk_state_h": 2 * C * d * d,                             # W S, Kc^T (kf X)
+               "chunk_output_o": C * d * d + 2 * tri1 * d}                 # Q S, Q K^T, P X
+        bytes_ = {"chunk_prep": k_b + v_b + 2 * gate_b + gc_b + W_b + U_b + kf_b + Kc_b,
+                  "chunk_state_h": W_b + U_b + Kc_b + kf_b + gc_b + s0 + H_b + X_b + S_b,
+                  "chunk_output_o": q_b + k_b + gc_b + H_b + X_b + o_b + ((o_b + d * 4) if gated else 0)}
     flops = {k: 2 * v * chv for k, v in per.items()}
     return bytes_, flops
 
@@ -205,6 +225,7 @@ def bench_prefill(args, torch, gdn, hip, device, gated=False):
         gate_obj = gdn.OutputGate(zt.data_ptr(), wt.data_ptr(), 1e-6)
         gate_ref = ctypes.byref(gate_obj)
     K = args.steps
+    STAGES = stages_for(dt)
     NEV = 2 * len(STAGES)
     ev = [[hip.event() for _ in range(NEV)] for _ in range(max(K, 1))]
 
@@ -255,6 +276,7 @@ def bench_prefill(args, torch, gdn, hip, device, gated=False):
     bytes_, flops = prefill_work(inp.T, inp.N, lay["n_chunks"], inp.H_q, inp.H_v, inp.d_k, es,
                                  has_s0=s0 is not None, gated=gated)
     return dict(inp=inp, lay=lay, ms_step=ms_step, wall_s=wall, stage_ms=stage_ms, bytes=bytes_, flops=flops,
+                stages=STAGES,
                 ms_step_with_events=timed_ms)
 
 
@@ -502,10 +524,12 @@ def main():
     if args.only in ("all", "prefill"):
         pre = bench_prefill(args, torch, gdn, hip, device)
         print(f"[bench] prefill {args.workload}: {pre['ms_step']:.4f} ms/step, stages "
-              + ", ".join(f"{s} {pre['stage_ms'][s] * 1e3:.1f} us" for s in STAGES), file=sys.stderr, flush=True)
+              + ", ".join(f"{s} {pre['stage_ms'][s] * 1e3:.1f} us" for s in pre["stages"]), file=sys.stderr,
+              flush=True)
         pre_g = bench_prefill(args, torch, gdn, hip, device, gated=True)
-        print(f"[bench] prefill {args.workload} + gated read-out: {pre_g['ms_step']:.4f} ms/step, chunk_output_o "
-              f"{pre_g['stage_ms']['chunk_output_o'] * 1e3:.1f} us", file=sys.stderr, flush=True)
+        print(f"[bench] prefill {args.workload} + gated read-out: {pre_g['ms_step']:.4f} ms/step, "
+              + ", ".join(f"{s} {pre_g['stage_ms'][s] * 1e3:.1f} us" for s in pre_g["stages"]), file=sys.stderr,
+              flush=True)
         pre_s = bench_prefill_serving(args, torch, gdn, device)
         print(f"[bench] prefill {args.workload} from raw inputs + gated read-out: {pre_s['ms_per_step']:.4f} ms/step",
               file=sys.stderr, flush=True)
@@ -526,6 +550,7 @@ def main():
         inp = pre["inp"]
         ms = pre["ms_step"]
         tokens = inp.T
+        STAGES = pre["stages"]
         dom = max(STAGES, key=lambda s: pre["stage_ms"][s])
         dom_s = pre["stage_ms"][dom] * 1e-3
         achieved = pre["bytes"][dom] / dom_s / 1e9
@@ -555,9 +580,10 @@ def main():
             "stages_us": {s: pre["stage_ms"][s] * 1e3 for s in STAGES},
             "ms_per_step_with_kernel_events": pre["ms_step_with_events"],
             "stage_hbm_frac": {s: pre["bytes"][s] / (pre["stage_ms"][s] * 1e-3) / 1e9 / HBM_PEAK_GBS
-                               for s in STAGES},
+                               for s in STAGES if pre["bytes"][s] > 0},
             "mfma_util": {"whole_step": total_flops / (ms * 1e-3) / 1e12 / mfma_peak,
-                          **{s: pre["flops"][s] / (pre["stage_ms"][s] * 1e-3) / 1e12 / mfma_peak for s in STAGES}},
+                          **{s: pre["flops"][s] / (pre["stage_ms"][s] * 1e-3) / 1e12 / mfma_peak for s in STAGES
+                             if pre["flops"][s] > 0}},
             "algorithmic": {"gflop": total_flops / 1e9, "mbytes": {s: pre["bytes"][s] / 1e6 for s in STAGES}},
         })
     if dec is not None:
@@ -576,12 +602,13 @@ def main():
                         "config": {"workload": "decode_256x1"}, "roofline": decode["roofline"]})
         res["decode"] = decode
     if pre_g is not None:
-        og = pre_g["stage_ms"]["chunk_output_o"] * 1e-3
+        ro = pre_g["stages"][2]  # the kernel that applies the read-out
+        og = pre_g["stage_ms"][ro] * 1e-3
         res["prefill_gated"] = {
-            "workload": args.workload + " with the gated RMSNorm read-out epilogue in chunk_output_o",
+            "workload": args.workload + " with the gated RMSNorm read-out",
             "ms_per_step": pre_g["ms_step"], "tokens_per_s": pre_g["inp"].T / (pre_g["ms_step"] * 1e-3),
-            "stages_us": {s: pre_g["stage_ms"][s] * 1e3 for s in STAGES},
-            "chunk_output_o_hbm_frac": pre_g["bytes"]["chunk_output_o"] / og / 1e9 / HBM_PEAK_GBS}
+            "stages_us": {s: pre_g["stage_ms"][s] * 1e3 for s in pre_g["stages"]},
+            "readout_kernel": ro, "readout_hbm_frac": pre_g["bytes"][ro] / og / 1e9 / HBM_PEAK_GBS}
     if decg is not None:
         kg = decg["bytes"] / (decg["kernel_ms"] * 1e-3) / 1e9
         res["decode_fused_gated"] = {

@@ -29,6 +29,7 @@ _lib = None
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 FWD_KEEP_A = 1  # gdn_chunk_fwd_ex flag: also write A to the workspace
+FWD_KEEP_HX = 2  # gdn_chunk_fwd_ex flag: also write Ht and Xt (bf16 forms the output on chip)
 SCRATCH_BYTES = 256 << 20  # GDN_SCRATCH_BYTES: the static workspace of gdn_chunk_fwd_scratch
 
 _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace", -4: "hip"}
@@ -46,6 +47,7 @@ class WorkspaceLayout(ctypes.Structure):
     _fields_ = [("n_chunks", ctypes.c_int64), ("off_gc", ctypes.c_size_t), ("off_A", ctypes.c_size_t),
                 ("off_W", ctypes.c_size_t), ("off_U", ctypes.c_size_t), ("off_kf", ctypes.c_size_t),
                 ("off_Kc", ctypes.c_size_t), ("off_Ht", ctypes.c_size_t), ("off_Xt", ctypes.c_size_t),
+                ("off_P", ctypes.c_size_t),
                 ("total_bytes", ctypes.c_size_t)]
 
 
@@ -269,7 +271,7 @@ def workspace_size(T: int, cu_seqlens, H_q: int, H_v: int, d_k: int, d_v: int, d
 
 def chunk_fwd(q, k, v, g, beta, cu_seqlens: Sequence[int], initial_state=None, scale: Optional[float] = None,
               out=None, final_state=None, output_final_state: bool = True, workspace=None, stream=None,
-              keep_A: bool = False, gate=None):
+              keep_A: bool = False, gate=None, keep_hx: bool = False):
     """Chunk-wise GDN prefill over a packed batch (gdn_chunk_fwd; gdn_chunk_fwd_ex with keep_A).
 
     q, k: [T, H_q, d_k]; v: [T, H_v, d_v] (bf16 or fp32, same dtype); g, beta:
@@ -277,7 +279,8 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens: Sequence[int], initial_state=None, s
     initial_state: fp32 [N, H_v, d_k, d_v] or None.  Returns (out, final_state)
     with final_state None when output_final_state is False.  ``workspace`` may
     be a preallocated uint8 device tensor of at least workspace_size() bytes;
-    keep_A also writes the A intermediate into it (GDN_FWD_KEEP_A).  ``gate`` =
+    keep_A also writes the A intermediate into it (GDN_FWD_KEEP_A), keep_hx the
+    chunk-start states and U - W S (GDN_FWD_KEEP_HX).  ``gate`` =
     (z [T, H_v, d_v] in q's dtype, weight fp32 [d_v], eps) applies the gated
     RMSNorm read-out epilogue to out (gdn_chunk_fwd_ex).
     """
@@ -321,8 +324,9 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens: Sequence[int], initial_state=None, s
             _ptr(final_state), T, H_q, H_v, d_k, d_v, float(scale), dt, _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream_ptr(stream))
     gptr, _keep = _gate_arg(gate, q.dtype, T, H_v, d_v)
-    if keep_A or gate is not None:
-        rc, name = lib.gdn_chunk_fwd_ex(*args, FWD_KEEP_A if keep_A else 0, gptr, None), "gdn_chunk_fwd_ex"
+    flags = (FWD_KEEP_A if keep_A else 0) | (FWD_KEEP_HX if keep_hx else 0)
+    if flags or gate is not None:
+        rc, name = lib.gdn_chunk_fwd_ex(*args, flags, gptr, None), "gdn_chunk_fwd_ex"
     else:
         rc, name = lib.gdn_chunk_fwd(*args), "gdn_chunk_fwd"
     if rc != 0:

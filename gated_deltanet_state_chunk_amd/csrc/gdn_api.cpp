@@ -209,7 +209,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, 
                    hipStream_t stream,
                    uint32_t flags, const gdn_output_gate* gate, void* const* stage_events,
                    const gdn_front_end* front = nullptr) {
-    if (flags & ~(uint32_t)GDN_FWD_KEEP_A) return GDN_EINVAL;
+    if (flags & ~(uint32_t)(GDN_FWD_KEEP_A | GDN_FWD_KEEP_HX)) return GDN_EINVAL;
     if (gate) {
         const int grc = check_gate(gate, T > 0);
         if (grc != GDN_OK) return grc;
@@ -245,8 +245,11 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, 
     p.A = ws + L.off_A; p.W = ws + L.off_W; p.Ut = ws + L.off_U;
     p.kf = reinterpret_cast<float*>(ws + L.off_kf); p.Kc = ws + L.off_Kc;
     p.Ht = ws + L.off_Ht; p.Xt = ws + L.off_Xt;
+    p.Pf = dtype == GDN_BF16 ? ws + L.off_P : nullptr;
     p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
     p.keep_A = (flags & GDN_FWD_KEEP_A) ? 1 : 0;
+    p.keep_hx = (flags & GDN_FWD_KEEP_HX) ? 1 : 0;
+    p.T = T;
     p.gz = gate ? gate->z : nullptr;
     p.gw = gate ? gate->weight : nullptr;
     p.geps = gate ? gate->eps : 0.f;
@@ -398,6 +401,8 @@ int layout_for_chunks(int64_t nc, int32_t H_q, int32_t H_v, int32_t d_k, int32_t
     L.off_Kc = off; off = align_up(off + chq * C * (size_t)d_k * es);
     L.off_Ht = off; off = align_up(off + chv * (size_t)d_v * (size_t)d_k * es);
     L.off_Xt = off; off = align_up(off + chv * (size_t)d_v * C * es);
+    // P (bf16 only: the output is formed inside the state scan): six 1 KiB fragments
+    L.off_P = off; off = align_up(off + (dtype == GDN_BF16 ? chv * 6 * 64 * 8 * es : 0));
     L.total_bytes = off;
     *layout = L;
     return GDN_OK;
@@ -509,7 +514,9 @@ int gdn_chunk_fwd_dev(const void* q, const void* k, const void* v, const float* 
     p.A = ws + L.off_A; p.W = ws + L.off_W; p.Ut = ws + L.off_U;
     p.kf = reinterpret_cast<float*>(ws + L.off_kf); p.Kc = ws + L.off_Kc;
     p.Ht = ws + L.off_Ht; p.Xt = ws + L.off_Xt;
+    p.Pf = dtype == GDN_BF16 ? ws + L.off_P : nullptr;
     p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
+    p.T = T;
     p.gz = gate ? gate->z : nullptr;
     p.gw = gate ? gate->weight : nullptr;
     p.geps = gate ? gate->eps : 0.f;

@@ -105,6 +105,11 @@ __host__ __device__ constexpr int kswz(int row) {
 }
 
 
+// P, the masked and decayed Q K^T of a (chunk, value head), is kept as the six
+// B-operand fragments of X^T P^T its query tiles need: (tile, K-step) =
+// (0,0), (1,0), (2,0), (2,1), (3,0), (3,1) (query tiles 0 and 1 see keys < 32 only).
+constexpr int P_FRAGS = 6;
+
 // ---------------------------------------------------------------------------
 // 1. chunk_prep: one workgroup (4 waves) per (chunk, value head); the first two
 //    stages of the chunk form in one pass over the chunk's keys and values:
@@ -219,6 +224,33 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
                               : make_float4(0, 0, 0, 0);
         }
     }
+    // Query fragments of this wave's 16 positions for P (bf16): rows 16 w + r16,
+    // contraction indices 32 ks + 8 grp .. + 7 (zero past the valid length;
+    // L2-normalised with the front end, the row spread over the four lanes of
+    // lane % 16).
+    Frag<T> qw[D / 32];
+    if constexpr (sizeof(T) == 2) {
+        if (p.Pf) {
+            const int row = 16 * w + r16;
+            const T* qb = reinterpret_cast<const T*>(p.q) + ((size_t)(cp.t0 + row) * p.H_q + h / p.G) * D + 8 * grp;
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) load8_masked(qw[ks], qb + 32 * ks, row < ell);
+            if (p.fa) {
+                float ss = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) ss += frag_get(qw[ks], j) * frag_get(qw[ks], j);
+                ss += __shfl_xor(ss, 16, 64);
+                ss += __shfl_xor(ss, 32, 64);
+                const float r = 1.f / sqrtf(ss + 1e-6f);
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) frag_set(qw[ks], j, frag_get(qw[ks], j) * r);
+            }
+        }
+    }
     // With the front end, each K row is L2-normalised on the way (rows past the
     // valid length are zero and stay zero).  The first value head of each key
     // head also writes the rows to Kc, the state scan's copy of the chunk's keys
@@ -257,20 +289,47 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
 
     // K K^T: wave w forms row block w against column blocks J <= w (fragments from LDS);
     // L_ij = beta_i exp(gc_i - gc_j) (k_i . k_j) for i > j, zero elsewhere.
-    for (int J = 0; J <= w; ++J) {
-        f32x4 acc = zero4();
+    // With P requested (bf16), the same K fragments also give the P^T tiles
+    // (J, w) = K_J Q_w^T of this wave's query positions i = 16 w + r16:
+    // P^T[j][i] = (k_j . q_i) exp(gc_i - gc_j) for j <= i < ell (Lower keeps the diagonal).
+    f32x4 pt[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+        if (J > w) break;
+        f32x4 acc = zero4(), pacc = zero4();
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
             Frag<T> a, b;
             load8(a, &s.K[16 * w + r16][32 * ks + 8 * grp]);
             load8(b, &s.K[16 * J + r16][32 * ks + 8 * grp]);
             acc = mma(a, b, acc);
+            if constexpr (sizeof(T) == 2) {
+                if (p.Pf) pacc = mma(b, qw[ks], pacc);
+            }
         }
         float* Lb = Ls + blk(w, J);
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             const int i = 16 * w + 4 * grp + i4, j = 16 * J + r16;
             Lb[(4 * grp + i4) * BS + r16] = (i > j) ? s.beta[i] * __expf(s.gc[i] - s.gc[j]) * acc[i4] : 0.f;
+        }
+        if constexpr (sizeof(T) == 2) {
+            const int i = 16 * w + r16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 16 * J + 4 * grp + e;
+                pt[J][e] = (j <= i && i < ell) ? pacc[e] * __expf(s.gc[i] - s.gc[j]) : 0.f;
+            }
+        }
+    }
+    // P to the workspace as the B operands of X^T P^T: query tile w, K-steps
+    // s = 0 (and 1 for w >= 2), two stacked P^T tiles per fragment (perm32).
+    if constexpr (sizeof(T) == 2) {
+        if (p.Pf) {
+            T* Pb = reinterpret_cast<T*>(p.Pf) + ch * P_FRAGS * 512;
+            const int f0 = w < 2 ? w : 2 * w - 2;
+            *reinterpret_cast<Frag<T>*>(Pb + (f0 * 64 + lane) * 8) = pack_perm32<T>(pt[0], pt[1], 1.f);
+            if (w >= 2) *reinterpret_cast<Frag<T>*>(Pb + ((f0 + 1) * 64 + lane) * 8) = pack_perm32<T>(pt[2], pt[3], 1.f);
         }
     }
     lds_sync();
@@ -497,32 +556,74 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
 //    Store wave.  Copies h_c (the sign-flipped -S of LS, between B1(c) and
 //    B2(c)) and X_c (LX, between B2(c) and B1(c + 1)) to HBM.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int CT = 1>
+// Loads producer wave pw of NPW issues in part 0 / part 1 of a chunk of NPIECE
+// 1 KiB pieces (part 1 includes the two 256-byte gate loads of wave 0).
+__host__ __device__ constexpr int stage_part_loads(int npiece, int npw, int pw, int part) {
+    int n = 0;
+    for (int j = 0; j < npiece; ++j) n += (j % npw == pw && (j < npiece / 2) == (part == 0)) ? 1 : 0;
+    return n + (part == 1 && pw == 0 ? 2 : 0);
+}
+// Producer waves' vmcnt bound at B2(c) (chunks c + 2 .. c + nst - 1 whole plus
+// part 0 of chunk c + nst issued after chunk c + 1's last load) for wave pw.
+__host__ __device__ constexpr int stage_wait_b2(int npiece, int npw, int nst, int pw) {
+    return (nst - 2) * (stage_part_loads(npiece, npw, pw, 0) + stage_part_loads(npiece, npw, pw, 1)) +
+           stage_part_loads(npiece, npw, pw, 0);
+}
+// Fewest producer waves (1, 2 or 4) whose outstanding loads stay within the
+// 63 a wave's vmcnt can count.
+__host__ __device__ constexpr int stage_producers(int npiece, int nst) {
+    for (int npw = 1; npw < 4; npw *= 2) {
+        bool ok = true;
+        for (int pw = 0; pw < npw; ++pw) {
+            const int r0 = 63 - stage_part_loads(npiece, npw, pw, 0);
+            ok = ok && stage_wait_b2(npiece, npw, nst, pw) < 64 && r0 - stage_part_loads(npiece, npw, pw, 1) >= 0;
+        }
+        if (ok) return npw;
+    }
+    return 4;
+}
+
+// FO: the output is formed in the scan; the stage also carries the chunk's P
+// fragments (for the output waves) and the workgroup keeps an output tile
+// buffer through which the store wave writes O.
+template <typename T, int D, int CT = 1, bool FO = false>
 struct StateStage {
     static constexpr int W_BYTES = CHUNK * D * (int)sizeof(T);
     static constexpr int K_BYTES = CHUNK * D * (int)sizeof(T);   // K rows, row-major (pieces permuted by kswz)
     static constexpr int U1_BYTES = 4 * 64 * 4 * (int)sizeof(T); // one 16-column tile of U
     static constexpr int U_BYTES = CT * U1_BYTES;                // the workgroup's CT tiles
     static constexpr int G_BYTES = 2 * CHUNK * 4;                // gc, then kf
-    static constexpr int BYTES = W_BYTES + K_BYTES + U_BYTES + G_BYTES;
-    static constexpr int NPIECE = (W_BYTES + K_BYTES + U_BYTES) / 1024;    // 1 KiB loads per chunk (+ gates)
+    static constexpr int P_BYTES = FO ? P_FRAGS * 1024 : 0;      // P fragments (bf16)
+    static constexpr int G_OFF = W_BYTES + K_BYTES + U_BYTES;
+    static constexpr int P_OFF = G_OFF + G_BYTES;
+    static constexpr int BYTES = P_OFF + P_BYTES;
+    static constexpr int NPIECE = (W_BYTES + K_BYTES + U_BYTES + P_BYTES) / 1024;  // 1 KiB loads per chunk (+ gates)
     // Exchange blocks (-S, X and kf X): one fragment per lane, 16 bytes of
     // padding after every 16 lanes so that the store wave's column gathers
     // spread over the LDS banks.
-    static constexpr int XBLK = 64 * 8 * (int)sizeof(T) + 4 * 16;
+    static constexpr int XPAD = 16;
+    static constexpr int XBLK = 64 * 8 * (int)sizeof(T) + 4 * XPAD;
     static constexpr int EXCH = (D / 32 + 4) * CT * XBLK;
+    static constexpr int OBUF = FO ? 4 * CT * 64 * 8 : 0;  // output tiles (bf16: 4 values a lane, per wave and tile)
+    static constexpr int QBUF = FO ? 4 * 16 * D * (int)sizeof(T) : 0;  // each output wave's 16 query rows
+    // Three stages where they fit and one producer wave can keep them fed (a
+    // chunk is issued two steps and a half before it is read), else two.  The
+    // third stage pays where the stream comes from HBM (T = 65536: 991 -> 902
+    // us) and costs nothing at T = 4096.  A second producer wave costs more
+    // than it brings (T = 4096: 48.6 -> 61.9 us), so a stage that only two
+    // producers could keep three deep gets two.
+    static constexpr int LDS_CAP = 160 * 1024;
+    static constexpr int NST = (3 * BYTES + EXCH + OBUF + QBUF + 256 <= LDS_CAP &&  // + the L2-prefetch sink
+                                (FO ? stage_producers(NPIECE, 3) == 1 : true))
+                                   ? 3
+                                   : 2;
     // A wave can keep at most 63 vector-memory operations in flight, so the
-    // stream is split over NPW producer waves, each owning every NPW-th piece,
-    // with one chunk's share (plus the two gate loads) within that limit.
-    static constexpr int NPW = (NPIECE + 2 + 62) / 63;
+    // stream is split over NPW producer waves, each owning every NPW-th piece.
     // The compute waves copy chunk c into registers before B1(c), so stage
     // c % NST is refilled with chunk c + NST from B1(c) on.
-    // Three stages where they fit (a chunk is issued two steps and a half
-    // before it is read), else two.  The third stage pays where the stream
-    // comes from HBM (T = 65536: 991 -> 902 us) and costs nothing at T = 4096;
-    // the launcher runs one workgroup per CU anyway once tiles outnumber CUs.
-    static constexpr int LDS_CAP = 160 * 1024;
-    static constexpr int NST = (3 * BYTES + EXCH + 256 <= LDS_CAP) ? 3 : 2;  // + the L2-prefetch sink
+    static constexpr int NPW = stage_producers(NPIECE, NST);
+    static constexpr int NOUT = FO ? 4 : 0;       // output waves
+    static constexpr int WAVES = 5 + NPW + NOUT;  // compute, producers, store, output
 };
 
 typedef __attribute__((address_space(1))) const void* gptr_t;
@@ -574,12 +675,13 @@ __device__ __forceinline__ void lds_wait_untracked(u32x4* r) {
 // chunk's direct-to-LDS loads; part 0 issues the first half of the share,
 // part 1 the rest and the two 256-byte gate blocks gc and kf (producer
 // wave 0).  ch: (chunk, value head) index; kch: (chunk, key head) index of Kc.
-template <typename T, int D, int CT>
+// With the output formed in the scan (FO) the chunk's P fragments follow.
+template <typename T, int D, int CT, bool FO>
 __device__ __forceinline__ void state_issue(char* stage, const ChunkParams& p, size_t ch, size_t kch, int tile,
                                             int lane, int pw, int part) {
-    using SS = StateStage<T, D, CT>;
+    using SS = StateStage<T, D, CT, FO>;
     constexpr int NT = D / 16;
-    constexpr int NW = SS::W_BYTES / 1024, NK = SS::K_BYTES / 1024;
+    constexpr int NW = SS::W_BYTES / 1024, NK = SS::K_BYTES / 1024, NU = SS::U_BYTES / 1024;
     constexpr int NP = SS::NPIECE;
     const char* wg = reinterpret_cast<const char*>(p.W) + ch * SS::W_BYTES;
     const char* kg = reinterpret_cast<const char*>(p.Kc) + kch * SS::K_BYTES;
@@ -588,38 +690,31 @@ __device__ __forceinline__ void state_issue(char* stage, const ChunkParams& p, s
     for (int j = 0; j < NP; ++j) {
         if (j % SS::NPW != pw) continue;
         if ((j < NP / 2) != (part == 0)) continue;
-        if (j < NW)
+        if (j < NW) {
             dma_1k(wg + 1024 * j, stage + 1024 * j, lane);
-        else if (j < NW + NK)
+        } else if (j < NW + NK) {
             dma_1k(kg + 1024 * (j - NW), stage + SS::W_BYTES + 1024 * (j - NW), lane);
-        else
+        } else if (j < NW + NK + NU) {
             dma_1k(ug + 1024 * (j - NW - NK), stage + SS::W_BYTES + SS::K_BYTES + 1024 * (j - NW - NK), lane);
+        } else {
+            const char* pg = reinterpret_cast<const char*>(p.Pf) + ch * SS::P_BYTES;
+            dma_1k(pg + 1024 * (j - NW - NK - NU), stage + SS::P_OFF + 1024 * (j - NW - NK - NU), lane);
+        }
     }
     if (part == 1 && pw == 0) {
-        char* g = stage + SS::W_BYTES + SS::K_BYTES + SS::U_BYTES;
+        char* g = stage + SS::G_OFF;
         __builtin_amdgcn_global_load_lds((gptr_t)(p.gc + ch * CHUNK + lane), (lptr_t)g, 4, 0, 0);
         __builtin_amdgcn_global_load_lds((gptr_t)(p.kf + ch * CHUNK + lane), (lptr_t)(g + 4 * CHUNK), 4, 0, 0);
     }
 }
 
-// Loads producer wave pw issues in part 0 / part 1 of a chunk (part 1
-// includes the two gate loads of wave 0).
-template <typename T, int D, int CT>
+template <typename SS>
 __host__ __device__ constexpr int state_part_loads(int pw, int part) {
-    using SS = StateStage<T, D, CT>;
-    int n = 0;
-    for (int j = 0; j < SS::NPIECE; ++j) n += (j % SS::NPW == pw && (j < SS::NPIECE / 2) == (part == 0)) ? 1 : 0;
-    return n + (part == 1 && pw == 0 ? 2 : 0);
+    return stage_part_loads(SS::NPIECE, SS::NPW, pw, part);
 }
-
-// vmcnt bounds of producer wave pw: ops younger than chunk c + 1's last load
-// when part 0 of chunk c + NST has just gone out (chunks c + 2 .. c + NST - 1
-// whole, plus that part 0), and the in-flight ceiling before part 1 goes out.
-template <typename T, int D, int CT>
+template <typename SS>
 __host__ __device__ constexpr int state_wait_b2(int pw) {
-    using SS = StateStage<T, D, CT>;
-    return (SS::NST - 2) * (state_part_loads<T, D, CT>(pw, 0) + state_part_loads<T, D, CT>(pw, 1)) +
-           state_part_loads<T, D, CT>(pw, 0);
+    return stage_wait_b2(SS::NPIECE, SS::NPW, SS::NST, pw);
 }
 // Write a D tile's four values (rows 4 grp + i of one 16-row tile) into the
 // perm32 fragment they belong to: even tile -> slots 0..3, odd -> slots 4..7.
@@ -668,9 +763,131 @@ __device__ __forceinline__ Frag<T> k_col_frag(const char* kst, int m, int ks, in
     return f;
 }
 
-template <typename T, int D, bool DEV, int CT>
-__global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p, int padded) {
-    using SS = StateStage<T, D, CT>;
+// ---------------------------------------------------------------------------
+// Output waves of chunk_state_h with the output formed in the scan (stage 4 of
+// the chunk form computed beside stage 3).  Wave o forms the outputs of
+// positions 16 o .. 16 o + 15 of every chunk for the workgroup's CT column
+// tiles of d_v:
+//   O^T = scale [ (h^T Q^T) diag(gamma) + X^T P^T ]
+// from the scan's own operands: h_c from LS (which holds -h_c between B1(c)
+// and B2(c)), X_c from LX (between B2(c) and B1(c + 1)), P and the gates from
+// the chunk's stage (read after B2(c - 1), before the stage is released at
+// B1(c)), and this wave's query rows from q, loaded one chunk ahead (L2
+// normalised here with the front end).  LS and LX fragments serve as the A
+// operands h^T and X^T unchanged; the query fragments list d_k in the same
+// (perm32) order.  The bf16 tile goes to LO, from where the store wave writes
+// it after the next barrier, so these waves issue no global store.  Nothing
+// on the serial chain waits for them except the two barriers of a step.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int CT>
+__device__ __forceinline__ void chunk_output_waves(const ChunkParams& p, const char* smem, const char* LS,
+                                                   const char* LX, char* LO, char* LQ, int o, int lane,
+                                                   const SeqTable& tab, int n, int hq, int nch, int L_n) {
+    static_assert(sizeof(T) == 2, "the output waves are bf16");
+    using SS = StateStage<T, D, CT, true>;
+    constexpr int KS = D / 32;
+    constexpr int NST = SS::NST;
+    o = __builtin_amdgcn_readfirstlane(o);
+    const int r16 = lane & 15, grp = lane >> 4;
+    const int pos = 16 * o + r16;  // this lane's query position (column of its O^T tiles)
+    auto xfr = [&](const char* buf, int b) {
+        return *reinterpret_cast<const Frag<T>*>(buf + b * SS::XBLK + lane * (int)sizeof(Frag<T>) +
+                                                 (lane >> 4) * SS::XPAD);
+    };
+    // Query rows: each wave copies its 16 rows of the chunk into its own LDS
+    // buffer with 1 KiB direct-to-LDS loads (four rows each; the 16-byte pieces
+    // of row r permuted by r so that the fragment reads below spread over the
+    // banks), issued a step ahead, right after the previous chunk's fragments
+    // have been read out.  Rows past the valid length re-read the last valid
+    // row; their outputs are never stored.  (Loaded straight into registers,
+    // 8 bytes of 16 rows an instruction, the rows cost the serial chain 45 us
+    // at T = 4096: the CU's vector-memory path is shared with the producers.)
+    constexpr int RB = D * (int)sizeof(T), PPR = RB / 16;  // row bytes, 16-byte pieces a row
+    char* const lq = LQ + o * 16 * RB;
+    auto load_q = [&](int c) {
+        const int ell = min(CHUNK, L_n - c * CHUNK);
+        const char* q0 = reinterpret_cast<const char*>(p.q) + ((size_t)(tab.cu[n] + c * CHUNK) * p.H_q + hq) * RB;
+#pragma unroll
+        for (int i = 0; i < 16 * PPR / 64; ++i) {
+            const int e = 64 * i + lane, r = e / PPR, pc = (e % PPR) ^ (r % PPR);
+            const char* src = q0 + (size_t)min(16 * o + r, ell - 1) * p.H_q * RB + 16 * pc;
+            __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(lq + 1024 * i), 16, 0, 0);
+        }
+    };
+    // fragment ks of this lane's row: slots 0..3 <- d_k 32 ks + 4 grp .. + 3,
+    // slots 4..7 <- 32 ks + 16 + 4 grp .. + 3 (the exchange fragments' d_k order)
+    auto q_frag = [&](int ks) {
+        const char* row = lq + r16 * RB + 8 * (grp & 1);
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 16 * ((4 * ks + (grp >> 1)) ^ (r16 % PPR)));
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 16 * ((4 * ks + 2 + (grp >> 1)) ^ (r16 % PPR)));
+        Frag<T> f;
+        f.v = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return f;
+    };
+    Frag<T> pf0, pf1;
+    float gq = 0.f;
+    auto read_stage = [&](int c) {
+        const char* st = smem + (c % NST) * SS::BYTES;
+        const Frag<T>* P = reinterpret_cast<const Frag<T>*>(st + SS::P_OFF);
+        const int f0 = o < 2 ? o : 2 * o - 2;  // fragments of query tile o (see P_FRAGS)
+        pf0 = P[f0 * 64 + lane];
+        if (o >= 2) pf1 = P[(f0 + 1) * 64 + lane];
+        gq = reinterpret_cast<const float*>(st + SS::G_OFF)[pos];
+    };
+    if (nch > 0) load_q(0);
+    wait_lgkmcnt0();
+    asm volatile("s_barrier" ::: "memory");  // B0
+    if (nch > 0) read_stage(0);
+    for (int c = 0; c < nch; ++c) {
+        wait_lgkmcnt0();
+        asm volatile("s_barrier" ::: "memory");  // B1(c): LS holds -h_c
+        wait_vmcnt<0>();                         // chunk c's query rows (this wave's only loads) are in LQ
+        Frag<T> qf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = q_frag(ks);
+        wait_lgkmcnt0();                         // read out before the next chunk's rows overwrite them
+        if (c + 1 < nch) load_q(c + 1);
+        if (p.fa) {  // front end: q_bar = q / sqrt(sum q^2 + 1e-6), rounded to T; the row is in lanes r16 + 16 g
+            float ss = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) ss += frag_get(qf[ks], j) * frag_get(qf[ks], j);
+            ss += __shfl_xor(ss, 16, 64);
+            ss += __shfl_xor(ss, 32, 64);
+            const float r = 1.f / sqrtf(ss + 1e-6f);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) frag_set(qf[ks], j, frag_get(qf[ks], j) * r);
+        }
+        // -(h^T Q^T) from LS
+        f32x4 inter[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            inter[ct] = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) inter[ct] = mma(xfr(LS, ks * CT + ct), qf[ks], inter[ct]);
+        }
+        const float eg = __expf(gq);
+        wait_lgkmcnt0();
+        asm volatile("s_barrier" ::: "memory");  // B2(c): LX holds X_c
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            f32x4 acc = mma(xfr(LX, ct), pf0, zero4());
+            if (o >= 2) acc = mma(xfr(LX, CT + ct), pf1, acc);  // P^T rows 32..63 vanish for queries < 32
+            *reinterpret_cast<bf16x4*>(LO + ((ct * 4 + o) * 64 + lane) * 8) = cvt4_bf16(acc - eg * inter[ct], p.scale);
+        }
+        if (c + 1 < nch) read_stage(c + 1);
+    }
+    wait_lgkmcnt0();
+    asm volatile("s_barrier" ::: "memory");  // B_end: the last output tile is in LO
+}
+
+template <typename T, int D, bool DEV, int CT, bool FO>
+__global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_state_h_kernel(const ChunkParams p,
+                                                                                            int padded) {
+    using SS = StateStage<T, D, CT, FO>;
     constexpr int NT = D / 16;   // column tiles of d_v per head
     constexpr int NTW = NT / CT; // workgroups per head (CT column tiles each)
     constexpr int KS = D / 32;   // contraction steps over d_k
@@ -699,15 +916,27 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
     const int hq = h / p.G;
     auto kch = [&](int c) { return (size_t)(c0 + c) * p.H_q + hq; };
 
-    __shared__ __attribute__((aligned(16))) char smem[NST * SS::BYTES + SS::EXCH + 256];  // + L2-prefetch sink
+    __shared__ __attribute__((aligned(16))) char smem[NST * SS::BYTES + SS::EXCH + SS::OBUF + SS::QBUF + 256];
     char* const LS = smem + NST * SS::BYTES;  // KS x CT blocks: -S (block ks CT + ct)
     char* const LX = LS + KS * CT * SS::XBLK; // 2 x CT blocks: X (block j CT + ct)
     char* const LY = LX + 2 * CT * SS::XBLK;  // 2 x CT blocks: kf X
+    char* const LO = LY + 2 * CT * SS::XBLK;  // FO: output tiles, 8 bytes per (tile ct, wave, lane)
+    char* const LQ = LO + SS::OBUF;           // FO: each output wave's query rows
+    char* const sink = LQ + SS::QBUF;         // L2-prefetch sink
     // fragment of lane ln in block b of an exchange buffer
     auto xf = [](char* buf, int b, int ln) -> Frag<T>& {
-        return *reinterpret_cast<Frag<T>*>(buf + b * SS::XBLK + ln * (int)sizeof(Frag<T>) + (ln >> 4) * 16);
+        return *reinterpret_cast<Frag<T>*>(buf + b * SS::XBLK + ln * (int)sizeof(Frag<T>) + (ln >> 4) * SS::XPAD);
     };
+    // Whether the store wave writes h and X (always without the output waves;
+    // with them only for inspection).
+    const bool store_hx = !FO || p.keep_hx;
 
+    if constexpr (FO) {
+        if (w > 4 + SS::NPW) {
+            chunk_output_waves<T, D, CT>(p, smem, LS, LX, LO, LQ, w - (5 + SS::NPW), lane, tab, n, hq, nch, L_n);
+            return;
+        }
+    }
     if (w >= 4 + SS::NPW) {
         // ---------------- store wave ----------------
         // Writes the chunk-start states and X to HBM from the compute waves'
@@ -730,7 +959,9 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         constexpr int EB = (int)sizeof(T);
         constexpr int HPL = KS * FQ, XPL = 2 * FQ;  // 16-byte pieces per lane per chunk
         const unsigned ls0 = lds_addr(LS), lx0 = lds_addr(LX);
-        auto xoff = [](int b, int ln) { return (unsigned)(b * SS::XBLK + ln * (int)sizeof(Frag<T>) + (ln >> 4) * 16); };
+        auto xoff = [](int b, int ln) {
+            return (unsigned)(b * SS::XBLK + ln * (int)sizeof(Frag<T>) + (ln >> 4) * SS::XPAD);
+        };
         unsigned hla[CT][HPL], xla[CT][XPL];  // LDS byte addresses
         unsigned hgo[CT][HPL], xgo[CT][XPL];  // byte offsets in the chunk-head's Ht / Xt block
 #pragma unroll
@@ -761,6 +992,33 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         constexpr int PF = 6;
         constexpr int LPT = SS::W_BYTES / 128 / NTW;  // lines of W (and of K) per workgroup
         constexpr int NPL = (2 * LPT + 63) / 64;      // prefetch loads per lane (W lines, then K lines)
+        // Output tile of chunk c (FO) from LO to O: lane L writes row L of the
+        // chunk (output wave L / 16, lane L % 16 of its groups), 16 values of
+        // d_v per column tile as two 16-byte pieces gathered from the lanes of
+        // groups 0, 1 and 2, 3 (128 bytes apart in LO).
+        auto store_o = [&](int c) {
+            if constexpr (FO) {
+                const int ell = min(CHUNK, L_n - c * CHUNK);
+                const unsigned lo0 = lds_addr(LO) + (unsigned)((((lane >> 4) * 64) + (lane & 15)) * 8);
+                u32x4 ov[2 * CT];
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
+                        asm volatile("ds_read2_b64 %0, %1 offset1:16"
+                                     : "=v"(ov[2 * ct + h2])
+                                     : "v"(lo0 + (unsigned)(ct * 4 * 64 * 8 + h2 * 32 * 8)));
+                lds_wait_untracked<2 * CT>(ov);
+                if (lane < ell) {
+                    char* orow = reinterpret_cast<char*>(p.out) +
+                                 (((size_t)(tab.cu[n] + c * CHUNK + lane) * p.H_v + h) * D + 16 * CT * tile) * EB;
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; ++h2) *reinterpret_cast<u32x4*>(orow + 32 * ct + 16 * h2) = ov[2 * ct + h2];
+                }
+            }
+        };
         asm volatile("s_barrier" ::: "memory");  // B0
         for (int c = 0; c < nch; ++c) {
             const size_t ch = (size_t)(c0 + c) * p.H_v + h;
@@ -775,10 +1033,16 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
                         const char* a = L >= LPT
                                             ? reinterpret_cast<const char*>(p.Kc) + kch(c + PF) * SS::K_BYTES + li * 128
                                             : reinterpret_cast<const char*>(p.W) + chp * SS::W_BYTES + li * 128;
-                        __builtin_amdgcn_global_load_lds((gptr_t)a, (lptr_t)(smem + NST * SS::BYTES + SS::EXCH), 4, 0,
-                                                         0);
+                        __builtin_amdgcn_global_load_lds((gptr_t)a, (lptr_t)sink, 4, 0, 0);
                     }
                 }
+            }
+            if constexpr (FO) {
+                if (c > 0) store_o(c - 1);
+            }
+            if (!store_hx) {
+                asm volatile("s_barrier" ::: "memory");  // B2(c)
+                continue;
             }
             // h_c = -(LS): a sign flip, exact
             u32x4 hv[CT * HPL];
@@ -786,8 +1050,10 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int t = 0; t < HPL; ++t) {
-                    if constexpr (EB == 2)  // the two halves, 16 lanes (272 bytes) apart, in one read
+                    if constexpr (EB == 2 && SS::XPAD == 16)  // the two halves, 16 lanes (272 bytes) apart, in one read
                         asm volatile("ds_read2_b64 %0, %1 offset1:34" : "=v"(hv[ct * HPL + t]) : "v"(hla[ct][t]));
+                    else if constexpr (EB == 2)  // unpadded: 256 bytes apart
+                        asm volatile("ds_read2_b64 %0, %1 offset1:32" : "=v"(hv[ct * HPL + t]) : "v"(hla[ct][t]));
                     else
                         asm volatile("ds_read_b128 %0, %1" : "=v"(hv[ct * HPL + t]) : "v"(hla[ct][t]));
                 }
@@ -811,6 +1077,10 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
 #pragma unroll
                 for (int t = 0; t < XPL; ++t) *reinterpret_cast<u32x4*>(Xb + xgo[ct][t]) = xv[ct * XPL + t];
         }
+        if constexpr (FO) {
+            asm volatile("s_barrier" ::: "memory");  // B_end: the last output tile is in LO
+            if (nch > 0) store_o(nch - 1);
+        }
         wait_vmcnt<0>();  // no prefetch may land in LDS after the workgroup has ended
         return;
     }
@@ -820,11 +1090,13 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
         // Outstanding-load bounds (vmcnt counts at most 63): before k loads go
         // out at most 63 - k may be in flight (R*_), and at B2(c) chunk c + 1
         // must have landed (WB_).
-        constexpr int WB_0 = state_wait_b2<T, D, CT>(0), WB_1 = state_wait_b2<T, D, CT>(1);
-        constexpr int R0_0 = 63 - state_part_loads<T, D, CT>(0, 0), R0_1 = 63 - state_part_loads<T, D, CT>(1, 0);
-        constexpr int R1_0 = 63 - state_part_loads<T, D, CT>(0, 1), R1_1 = 63 - state_part_loads<T, D, CT>(1, 1);
-        constexpr int RC_0 = R0_0 - state_part_loads<T, D, CT>(0, 1), RC_1 = R0_1 - state_part_loads<T, D, CT>(1, 1);
+        static_assert(SS::NPW <= 2, "the producer code below handles one or two waves");
+        constexpr int WB_0 = state_wait_b2<SS>(0), WB_1 = state_wait_b2<SS>(1);
+        constexpr int R0_0 = 63 - state_part_loads<SS>(0, 0), R0_1 = 63 - state_part_loads<SS>(1, 0);
+        constexpr int R1_0 = 63 - state_part_loads<SS>(0, 1), R1_1 = 63 - state_part_loads<SS>(1, 1);
+        constexpr int RC_0 = R0_0 - state_part_loads<SS>(0, 1), RC_1 = R0_1 - state_part_loads<SS>(1, 1);
         static_assert(WB_0 < 64 && WB_1 < 64 && RC_0 >= 0 && RC_1 >= 0, "producer loads exceed the vmcnt range");
+
         // Chunks 0 .. NST-1 up front; chunk 0 lands before B0.
 #pragma unroll
         for (int b = 0; b < NST; ++b) {
@@ -834,8 +1106,8 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
             }
             if (b < nch) {
                 const size_t chb = (size_t)(c0 + b) * p.H_v + h;
-                state_issue<T, D, CT>(smem + b * SS::BYTES, p, chb, kch(b), tile, lane, pw, 0);
-                state_issue<T, D, CT>(smem + b * SS::BYTES, p, chb, kch(b), tile, lane, pw, 1);
+                state_issue<T, D, CT, FO>(smem + b * SS::BYTES, p, chb, kch(b), tile, lane, pw, 0);
+                state_issue<T, D, CT, FO>(smem + b * SS::BYTES, p, chb, kch(b), tile, lane, pw, 1);
             }
         }
         // The producers' barriers are plain s_barrier: a workgroup release fence
@@ -854,7 +1126,7 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
             // chunk c + 1 is read after B2(c).
             if (cn < nch) {
                 if (pw == 0) wait_vmcnt<R0_0>(); else wait_vmcnt<R0_1>();
-                state_issue<T, D, CT>(stn, p, chn, kch(cn), tile, lane, pw, 0);
+                state_issue<T, D, CT, FO>(stn, p, chn, kch(cn), tile, lane, pw, 0);
                 if (pw == 0) wait_vmcnt<WB_0>(); else wait_vmcnt<WB_1>();
             } else {
                 wait_vmcnt<0>();
@@ -862,9 +1134,10 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
             asm volatile("s_barrier" ::: "memory");  // B2(c)
             if (cn < nch) {
                 if (pw == 0) wait_vmcnt<R1_0>(); else wait_vmcnt<R1_1>();
-                state_issue<T, D, CT>(stn, p, chn, kch(cn), tile, lane, pw, 1);
+                state_issue<T, D, CT, FO>(stn, p, chn, kch(cn), tile, lane, pw, 1);
             }
         }
+        if constexpr (FO) asm volatile("s_barrier" ::: "memory");  // B_end
         return;
     }
 
@@ -956,6 +1229,7 @@ __global__ __launch_bounds__(448) void chunk_state_h_kernel(const ChunkParams p,
             for (int ct = 0; ct < CT; ++ct) lds_put4(xf(LS, (m >> 1) * CT + ct, lane), m & 1, S[tt][ct], -1.f);
         }
     }
+    if constexpr (FO) lds_sync();  // B_end
     if (so >= 0) {
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
@@ -1218,6 +1492,59 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
 }
 
 // ---------------------------------------------------------------------------
+// Gated read-out after the fused output (trace page, node 18 of the prefill
+// graph; Decode-GDN node 8): in place over the rows of the launch's tokens,
+//     out = o / sqrt(mean o^2 + eps) * weight * silu(z)
+// over the d_v values of one (token, value head) row, o being the output as
+// stored (rounded to the output dtype, the value the unfused pair of nodes
+// hands over).  A row is held by D / 8 (bf16) lanes, 16 bytes each; HBM bound.
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool DEV>
+__global__ __launch_bounds__(256) void chunk_gate_kernel(const ChunkParams p) {
+    constexpr int VE = 16 / (int)sizeof(T);  // elements per lane
+    constexpr int LPR = D / VE;              // lanes per row
+    constexpr int RPB = 256 / LPR;           // rows per workgroup
+    const SeqTable& tab = DEV ? *p.dtab : p.tab;
+    const int tbeg = tab.cu[0], tend = tab.cu[tab.num_seqs];
+    const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;  // (token - tbeg) * H_v + head
+    if (row >= (size_t)(tend - tbeg) * p.H_v) return;                 // whole rows leave together
+    const int li = threadIdx.x % LPR;
+    const size_t off = ((size_t)tbeg * p.H_v + row) * D + (size_t)li * VE;
+    T* const ob = reinterpret_cast<T*>(p.out) + off;
+    const float4 raw = *reinterpret_cast<const float4*>(ob);
+    const float4 zraw = *reinterpret_cast<const float4*>(reinterpret_cast<const T*>(p.gz) + off);
+    float o[VE], z[VE];
+    if constexpr (sizeof(T) == 2) {
+        const bf16x8 ov = __builtin_bit_cast(bf16x8, raw), zv = __builtin_bit_cast(bf16x8, zraw);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+            o[e] = (float)ov[e];
+            z[e] = (float)zv[e];
+        }
+    } else {
+        o[0] = raw.x; o[1] = raw.y; o[2] = raw.z; o[3] = raw.w;
+        z[0] = zraw.x; z[1] = zraw.y; z[2] = zraw.z; z[3] = zraw.w;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) ss += o[e] * o[e];
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m, 64);
+    const float rstd = 1.f / sqrtf(ss * (1.f / D) + p.geps);
+    float y[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) y[e] = o[e] * rstd * p.gw[li * VE + e] * silu_f32(z[e]);
+    if constexpr (sizeof(T) == 2) {
+        bf16x8 yb;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) yb[e] = (bf16)y[e];
+        *reinterpret_cast<float4*>(ob) = __builtin_bit_cast(float4, yb);
+    } else {
+        *reinterpret_cast<float4*>(ob) = make_float4(y[0], y[1], y[2], y[3]);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Sequence tables from a device-resident cu_seqlens (one wave).  Per group of
 // up to 64 sequences: sequence ends clamped to [0, T] and made non-decreasing
 // (a running maximum, so every length is >= 0 and every index stays inside the
@@ -1337,6 +1664,11 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
     // (packed 8-sequence batch, 16 items a slot: 199 against 208 us).
     const int prep_slots = 4 * cu_count();
     const int prep_grid = work_ch > 8 * prep_slots ? grid_ch : std::min(grid_ch, prep_slots);
+    // bf16: chunk_output_o's work runs inside the state scan (output waves), so
+    // the chunk-start states and U - W S never leave the chip; the gated
+    // read-out is then a row pass over the output.  fp32 keeps the separate
+    // output kernel (a stage with the query rows would not fit in LDS twice).
+    constexpr bool FO = sizeof(T) == 2;
     auto run = [&](auto dev) {
         constexpr bool DEV = decltype(dev)::value;
         if (work_ch > 0) launch(0, chunk_prep_kernel<T, D, DEV>, prep_grid, 256, grid_ch, pl);
@@ -1344,7 +1676,7 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
         auto state = [&](auto ctc) {
             constexpr int CT = decltype(ctc)::value;
             const int grid = pad8(groups) * (D / 16 / CT);
-            launch(1, chunk_state_h_kernel<T, D, DEV, CT>, grid, 64 * (5 + StateStage<T, D, CT>::NPW), grid, pl);
+            launch(1, chunk_state_h_kernel<T, D, DEV, CT, FO>, grid, 64 * StateStage<T, D, CT, FO>::WAVES, grid, pl);
         };
         if (groups > 0) {
             if constexpr (sizeof(T) == 2) {
@@ -1359,10 +1691,28 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
             }
         }
         if (work_ch > 0) {
-            if (p.gz)
-                launch(2, chunk_output_o_kernel<T, D, true, DEV>, grid_ch, 256, grid_ch, pl);
-            else
-                launch(2, chunk_output_o_kernel<T, D, false, DEV>, grid_ch, 256, grid_ch, pl);
+            if constexpr (!FO) {
+                if (p.gz)
+                    launch(2, chunk_output_o_kernel<T, D, true, DEV>, grid_ch, 256, grid_ch, pl);
+                else
+                    launch(2, chunk_output_o_kernel<T, D, false, DEV>, grid_ch, 256, grid_ch, pl);
+            } else if (p.gz) {
+                constexpr int RPB = 256 / (D * (int)sizeof(T) / 16);
+                const int64_t rows = (int64_t)(DEV ? p.T : p.tab.cu[p.tab.num_seqs] - p.tab.cu[0]) * p.H_v;
+                const int grid = (int)((rows + RPB - 1) / RPB);
+                auto gate_kernel = chunk_gate_kernel<T, D, DEV>;
+                if (grid > 0 && events)
+                    hipExtLaunchKernelGGL(gate_kernel, dim3(grid), dim3(256), 0, stream, events[4], events[5], 0, pl);
+                else if (grid > 0)
+                    hipLaunchKernelGGL(gate_kernel, dim3(grid), dim3(256), 0, stream, pl);
+                else if (events) {
+                    (void)hipEventRecord(events[4], stream);
+                    (void)hipEventRecord(events[5], stream);
+                }
+            } else if (events) {  // no third kernel: its two events mark the same point
+                (void)hipEventRecord(events[4], stream);
+                (void)hipEventRecord(events[5], stream);
+            }
         }
     };
     if (p.dtab)

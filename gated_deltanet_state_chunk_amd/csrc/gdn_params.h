@@ -45,9 +45,12 @@ struct ChunkParams {
     void* Kc;   // per (chunk, key head): the chunk's key rows for the state update
     void* Ht;
     void* Xt;
+    void* Pf;   // per (chunk, value head): P as the output's B operands (bf16; null: P not formed)
     int32_t H_q, H_v, G;
     float scale;
     int32_t keep_A;  // nonzero: chunk_prep also writes A to the workspace
+    int32_t keep_hx;  // nonzero: the state scan writes Ht, Xt even where the output is formed on chip
+    int32_t T;       // tokens of the whole batch (bounds the gated read-out's rows on the device-table path)
     int32_t l2_prefetch;  // nonzero: chunk_state_h prefetches W / K into L2 (set by the launcher)
     // optional read-out epilogue out = rmsnorm(o) * gw * silu(gz) (gz null: none)
     const void* gz;

@@ -104,10 +104,19 @@ typedef struct ihipStream_t *hipStream_t;
  *                                            ((j/16 * (d_k/32) + k/32) * 64 + 16 ((k%32)/8) + j%16) * 8 + k%8
  *   Xt  dtype [n_chunks][H_v][d_v * 64]      (U - W S)^T, element (j, pos) at the same place
  *                                            with d_k -> 64 and k -> perm32(pos)
+ *   P   bf16  [n_chunks][H_v][6][64][8]      (bf16 only; empty for fp32) P[i][j] =
+ *                                            (q_i . k_j) exp(gc_i - gc_j) for j <= i < valid
+ *                                            length, else 0, as six fragments f = (query
+ *                                            tile t, key step s) = (0,0), (1,0), (2,0), (2,1),
+ *                                            (3,0), (3,1): lane 16 a + r, slot 4 h + b holds
+ *                                            P[16 t + r][32 s + 16 h + 4 a + b]
+ * For bf16 the chunk-start states and U - W S never leave the chip (the output
+ * is formed inside the state scan): Ht and Xt are written only under
+ * GDN_FWD_KEEP_HX (gdn_chunk_fwd_ex).
  */
 typedef struct gdn_workspace_layout {
     int64_t n_chunks;
-    size_t off_gc, off_A, off_W, off_U, off_kf, off_Kc, off_Ht, off_Xt; /* byte offsets */
+    size_t off_gc, off_A, off_W, off_U, off_kf, off_Kc, off_Ht, off_Xt, off_P; /* byte offsets */
     size_t total_bytes;
 } gdn_workspace_layout;
 
@@ -174,7 +183,8 @@ typedef struct gdn_output_gate {
 } gdn_output_gate;
 
 /* Flags of gdn_chunk_fwd_ex. */
-#define GDN_FWD_KEEP_A 1u /* also write A to its workspace region (otherwise that region is left untouched) */
+#define GDN_FWD_KEEP_A 1u  /* also write A to its workspace region (otherwise that region is left untouched) */
+#define GDN_FWD_KEEP_HX 2u /* also write Ht and Xt (bf16 forms the output on chip and leaves them untouched) */
 
 /*
  * gdn_chunk_fwd with options, for inspection, profiling and benchmarks.  Same

@@ -198,7 +198,7 @@ def test_chunk_intermediates_match_chunk_form(torch_cuda, dtype, d, tol):
     lens = [100, 64, 30]
     H_q, H_v = 1, 2
     inp = gdn_inputs.make_prefill(seed=9, seqlens=lens, H_q=H_q, H_v=H_v, d_k=d, d_v=d, dtype=dtype)
-    _, _, ws = chunk_fwd_device(inp, return_ws=True, keep_A=True)
+    _, _, ws = chunk_fwd_device(inp, return_ws=True, keep_A=True, keep_hx=True)
     lay = gdn.workspace_layout(inp.T, inp.cu_seqlens, H_q, H_v, d, d, dtype)
     nc = lay["n_chunks"]
     assert nc == 2 + 1 + 1
