@@ -47,7 +47,7 @@ class WorkspaceLayout(ctypes.Structure):
     _fields_ = [("n_chunks", ctypes.c_int64), ("off_gc", ctypes.c_size_t), ("off_A", ctypes.c_size_t),
                 ("off_W", ctypes.c_size_t), ("off_U", ctypes.c_size_t), ("off_kf", ctypes.c_size_t),
                 ("off_Kc", ctypes.c_size_t), ("off_Ht", ctypes.c_size_t), ("off_Xt", ctypes.c_size_t),
-                ("off_P", ctypes.c_size_t),
+                ("off_P", ctypes.c_size_t), ("off_Qc", ctypes.c_size_t),
                 ("total_bytes", ctypes.c_size_t)]
 
 

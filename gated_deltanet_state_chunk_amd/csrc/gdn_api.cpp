@@ -246,6 +246,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, 
     p.kf = reinterpret_cast<float*>(ws + L.off_kf); p.Kc = ws + L.off_Kc;
     p.Ht = ws + L.off_Ht; p.Xt = ws + L.off_Xt;
     p.Pf = dtype == GDN_BF16 ? ws + L.off_P : nullptr;
+    p.Qc = (dtype == GDN_BF16 && front) ? ws + L.off_Qc : nullptr;
     p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
     p.keep_A = (flags & GDN_FWD_KEEP_A) ? 1 : 0;
     p.keep_hx = (flags & GDN_FWD_KEEP_HX) ? 1 : 0;
@@ -403,6 +404,8 @@ int layout_for_chunks(int64_t nc, int32_t H_q, int32_t H_v, int32_t d_k, int32_t
     L.off_Xt = off; off = align_up(off + chv * (size_t)d_v * C * es);
     // P (bf16 only: the output is formed inside the state scan): six 1 KiB fragments
     L.off_P = off; off = align_up(off + (dtype == GDN_BF16 ? chv * 6 * 64 * 8 * es : 0));
+    // Qc (bf16 only): the front end's normalised query rows, one copy per key head
+    L.off_Qc = off; off = align_up(off + (dtype == GDN_BF16 ? chq * C * (size_t)d_k * es : 0));
     L.total_bytes = off;
     *layout = L;
     return GDN_OK;

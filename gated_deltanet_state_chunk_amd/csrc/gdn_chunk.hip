@@ -241,13 +241,20 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
                 for (int ks = 0; ks < D / 32; ++ks)
 #pragma unroll
                     for (int j = 0; j < 8; ++j) ss += frag_get(qw[ks], j) * frag_get(qw[ks], j);
-                ss += __shfl_xor(ss, 16, 64);
-                ss += __shfl_xor(ss, 32, 64);
-                const float r = 1.f / sqrtf(ss + 1e-6f);
+                const float r = 1.f / sqrtf(sum_over_rows(ss) + 1e-6f);
 #pragma unroll
                 for (int ks = 0; ks < D / 32; ++ks)
 #pragma unroll
                     for (int j = 0; j < 8; ++j) frag_set(qw[ks], j, frag_get(qw[ks], j) * r);
+                // the first value head of each key head keeps the normalised rows (Qc) for the
+                // state scan's output waves, piece i of row r at i ^ (r mod pieces)
+                if (h % p.G == 0) {
+                    constexpr int PPR = D / 8;
+                    T* Qcb = reinterpret_cast<T*>(p.Qc) + (((size_t)cp.ci * p.H_q + h / p.G) * CHUNK + row) * D;
+#pragma unroll
+                    for (int ks = 0; ks < D / 32; ++ks)
+                        *reinterpret_cast<Frag<T>*>(Qcb + 8 * ((4 * ks + grp) ^ (row % PPR))) = qw[ks];
+                }
             }
         }
     }
@@ -772,8 +779,8 @@ __device__ __forceinline__ Frag<T> k_col_frag(const char* kst, int m, int ks, in
 // from the scan's own operands: h_c from LS (which holds -h_c between B1(c)
 // and B2(c)), X_c from LX (between B2(c) and B1(c + 1)), P and the gates from
 // the chunk's stage (read after B2(c - 1), before the stage is released at
-// B1(c)), and this wave's query rows from q, loaded one chunk ahead (L2
-// normalised here with the front end).  LS and LX fragments serve as the A
+// B1(c)), and this wave's query rows, copied into LDS a chunk ahead (with the
+// front end from chunk_prep's normalised copy Qc).  LS and LX fragments serve as the A
 // operands h^T and X^T unchanged; the query fragments list d_k in the same
 // (perm32) order.  The bf16 tile goes to LO, from where the store wave writes
 // it after the next barrier, so these waves issue no global store.  Nothing
@@ -804,7 +811,16 @@ __device__ __forceinline__ void chunk_output_waves(const ChunkParams& p, const c
     // at T = 4096: the CU's vector-memory path is shared with the producers.)
     constexpr int RB = D * (int)sizeof(T), PPR = RB / 16;  // row bytes, 16-byte pieces a row
     char* const lq = LQ + o * 16 * RB;
+    // With the front end the rows come normalised, already in that order, from
+    // chunk_prep's copy Qc (contiguous: the wave's 16 rows are 16 RB bytes).
     auto load_q = [&](int c) {
+        if (p.Qc) {
+            const char* q0 = reinterpret_cast<const char*>(p.Qc) +
+                             (((size_t)(tab.choff[n] + c) * p.H_q + hq) * CHUNK + 16 * o) * RB;
+#pragma unroll
+            for (int i = 0; i < 16 * PPR / 64; ++i) dma_1k(q0 + 1024 * i, lq + 1024 * i, lane);
+            return;
+        }
         const int ell = min(CHUNK, L_n - c * CHUNK);
         const char* q0 = reinterpret_cast<const char*>(p.q) + ((size_t)(tab.cu[n] + c * CHUNK) * p.H_q + hq) * RB;
 #pragma unroll
@@ -847,20 +863,6 @@ __device__ __forceinline__ void chunk_output_waves(const ChunkParams& p, const c
         for (int ks = 0; ks < KS; ++ks) qf[ks] = q_frag(ks);
         wait_lgkmcnt0();                         // read out before the next chunk's rows overwrite them
         if (c + 1 < nch) load_q(c + 1);
-        if (p.fa) {  // front end: q_bar = q / sqrt(sum q^2 + 1e-6), rounded to T; the row is in lanes r16 + 16 g
-            float ss = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) ss += frag_get(qf[ks], j) * frag_get(qf[ks], j);
-            ss += __shfl_xor(ss, 16, 64);
-            ss += __shfl_xor(ss, 32, 64);
-            const float r = 1.f / sqrtf(ss + 1e-6f);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) frag_set(qf[ks], j, frag_get(qf[ks], j) * r);
-        }
         // -(h^T Q^T) from LS
         f32x4 inter[CT];
 #pragma unroll

@@ -195,6 +195,21 @@ __device__ __forceinline__ void lds_sync() {
 // ---- wave helpers --------------------------------------------------------
 __device__ __forceinline__ float wave_shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
 
+// Sum of x over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the same lane of the four
+// 16-lane rows), every one of them receiving the same bits.  gfx950's lane
+// swaps are VALU instructions: v_permlane16_swap exchanges the odd rows of its
+// first operand with the even rows of its second, v_permlane32_swap the upper
+// half of the first with the lower half of the second, so with both operands
+// equal the two results add to the pairwise sums.  A shuffle (ds_bpermute)
+// would travel through the LDS unit and queue behind the LDS traffic of a busy
+// workgroup.
+__device__ __forceinline__ float sum_over_rows(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // ---- transposed LDS reads (gfx950 ds_read_b64_tr_b16) ----------------------
 // Rows r0 .. r0+3 of column c0 + (lane % 16) of a row-major bf16 matrix in LDS
 // (row stride RS elements; r0 uniform within each group of 16 lanes, c0 a

@@ -110,13 +110,17 @@ typedef struct ihipStream_t *hipStream_t;
  *                                            tile t, key step s) = (0,0), (1,0), (2,0), (2,1),
  *                                            (3,0), (3,1): lane 16 a + r, slot 4 h + b holds
  *                                            P[16 t + r][32 s + 16 h + 4 a + b]
+ *   Qc  bf16  [n_chunks][H_q][64][d_k]       (bf16 only; written by gdn_chunk_fwd_fused) the
+ *                                            chunk's L2-normalised query rows, zero past
+ *                                            the valid length, the 16-byte pieces of row r
+ *                                            permuted: piece i at i ^ (r mod P), P as for Kc
  * For bf16 the chunk-start states and U - W S never leave the chip (the output
  * is formed inside the state scan): Ht and Xt are written only under
  * GDN_FWD_KEEP_HX (gdn_chunk_fwd_ex).
  */
 typedef struct gdn_workspace_layout {
     int64_t n_chunks;
-    size_t off_gc, off_A, off_W, off_U, off_kf, off_Kc, off_Ht, off_Xt, off_P; /* byte offsets */
+    size_t off_gc, off_A, off_W, off_U, off_kf, off_Kc, off_Ht, off_Xt, off_P, off_Qc; /* byte offsets */
     size_t total_bytes;
 } gdn_workspace_layout;
 

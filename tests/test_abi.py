@@ -103,18 +103,19 @@ def test_workspace_layout(gdn):
     lay = gdn.workspace_layout(4096, [0, 4096], 16, 32, 128, 128, "bf16")
     assert lay["n_chunks"] == 64
     offs = [lay[k] for k in ("off_gc", "off_A", "off_W", "off_U", "off_kf", "off_Kc", "off_Ht", "off_Xt",
-                             "off_P", "total_bytes")]
+                             "off_P", "off_Qc", "total_bytes")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     chv = 64 * 32
     assert lay["off_A"] - lay["off_gc"] == chv * 64 * 4
     assert lay["off_Kc"] - lay["off_kf"] == chv * 64 * 4
     assert lay["off_Ht"] - lay["off_Kc"] == 64 * 16 * 64 * 128 * 2  # chunks x key heads x rows x d_k
     assert lay["off_Xt"] - lay["off_Ht"] == chv * 128 * 128 * 2
-    assert lay["total_bytes"] - lay["off_P"] == chv * 6 * 1024       # P: six 1 KiB fragments (bf16)
+    assert lay["off_Qc"] - lay["off_P"] == chv * 6 * 1024            # P: six 1 KiB fragments (bf16)
+    assert lay["total_bytes"] - lay["off_Qc"] == 64 * 16 * 64 * 128 * 2  # Qc: as Kc
     # chunks are counted per sequence: ceil(100/64) + 0 + ceil(1/64) + ceil(128/64)
     lay2 = gdn.workspace_layout(229, [0, 100, 100, 101, 229], 2, 4, 64, 64, "f32")
     assert lay2["n_chunks"] == 2 + 0 + 1 + 2
-    assert lay2["total_bytes"] == lay2["off_P"]                       # no P region for fp32
+    assert lay2["total_bytes"] == lay2["off_P"] == lay2["off_Qc"]     # no P or Qc region for fp32
     assert gdn.workspace_size(0, [0], 2, 4, 64, 64, "f32") >= 0
 
 
