@@ -994,30 +994,34 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
         constexpr int PF = 6;
         constexpr int LPT = SS::W_BYTES / 128 / NTW;  // lines of W (and of K) per workgroup
         constexpr int NPL = (2 * LPT + 63) / 64;      // prefetch loads per lane (W lines, then K lines)
-        // Output tile of chunk c (FO) from LO to O: lane L writes row L of the
-        // chunk (output wave L / 16, lane L % 16 of its groups), 16 values of
-        // d_v per column tile as two 16-byte pieces gathered from the lanes of
-        // groups 0, 1 and 2, 3 (128 bytes apart in LO).
+        // Output tile of chunk c (FO) from LO to O.  A row of the tile is 32 CT
+        // contiguous bytes of O, so 2 CT lanes share a row, 16 bytes each (column
+        // tile ct, half hf), and an instruction covers 64 / (2 CT) whole row
+        // pieces: every cache line it touches receives all of the workgroup's
+        // bytes of that line at once.  (Row by row, 16 bytes of 64 rows an
+        // instruction, the stores cost the serial chain about 9 us at T = 4096.)
+        // Each piece is gathered from LO, where output wave o's lane 16 g + r
+        // holds columns 4 g .. 4 g + 3 of row 16 o + r: the lanes of groups 2 hf
+        // and 2 hf + 1, 128 bytes apart.
         auto store_o = [&](int c) {
             if constexpr (FO) {
+                constexpr int LPRW = 2 * CT, RPI = 64 / LPRW;  // lanes per row, rows per instruction
                 const int ell = min(CHUNK, L_n - c * CHUNK);
-                const unsigned lo0 = lds_addr(LO) + (unsigned)((((lane >> 4) * 64) + (lane & 15)) * 8);
-                u32x4 ov[2 * CT];
+                const int pc = lane % LPRW, ct = pc >> 1, hf = pc & 1;
+                u32x4 ov[LPRW];
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
+                for (int i = 0; i < LPRW; ++i) {
+                    const int row = RPI * i + lane / LPRW;
+                    const unsigned a = lds_addr(LO) + (unsigned)((((ct * 4 + (row >> 4)) * 64) + 32 * hf + (row & 15)) * 8);
+                    asm volatile("ds_read2_b64 %0, %1 offset1:16" : "=v"(ov[i]) : "v"(a));
+                }
+                lds_wait_untracked<LPRW>(ov);
+                char* o0 = reinterpret_cast<char*>(p.out) +
+                           (((size_t)(tab.cu[n] + c * CHUNK) * p.H_v + h) * D + 16 * (CT * tile + ct) + 8 * hf) * EB;
 #pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2)
-                        asm volatile("ds_read2_b64 %0, %1 offset1:16"
-                                     : "=v"(ov[2 * ct + h2])
-                                     : "v"(lo0 + (unsigned)(ct * 4 * 64 * 8 + h2 * 32 * 8)));
-                lds_wait_untracked<2 * CT>(ov);
-                if (lane < ell) {
-                    char* orow = reinterpret_cast<char*>(p.out) +
-                                 (((size_t)(tab.cu[n] + c * CHUNK + lane) * p.H_v + h) * D + 16 * CT * tile) * EB;
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                        for (int h2 = 0; h2 < 2; ++h2) *reinterpret_cast<u32x4*>(orow + 32 * ct + 16 * h2) = ov[2 * ct + h2];
+                for (int i = 0; i < LPRW; ++i) {
+                    const int row = RPI * i + lane / LPRW;
+                    if (row < ell) *reinterpret_cast<u32x4*>(o0 + (size_t)row * p.H_v * D * EB) = ov[i];
                 }
             }
         };
