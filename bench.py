@@ -154,6 +154,60 @@ class Hip:
         return float(ms.value)
 
 
+def per_step_ms(hip, stream_ptr, step, K, flush=None):
+    """Milliseconds of each of K steps, each bracketed by its own pair of timing
+    events on the stream: back to back, or with flush() queued before every step
+    outside its events (so the step starts with cold caches)."""
+    evs = [(hip.event(), hip.event()) for _ in range(K)]
+    for i in range(K):
+        if flush is not None:
+            flush()
+        hip.record(evs[i][0], stream_ptr)
+        step()
+        hip.record(evs[i][1], stream_ptr)
+    return sorted(hip.elapsed_ms(a, b) for a, b in evs)
+
+
+def stats(ms):
+    """median / min / mean of a list of per-step milliseconds."""
+    n = len(ms)
+    med = ms[n // 2] if n % 2 else 0.5 * (ms[n // 2 - 1] + ms[n // 2])
+    return {"median_ms": med, "min_ms": min(ms), "mean_ms": sum(ms) / n, "n": n}
+
+
+class CacheFlush:
+    """Evicts the 256 MB Infinity Cache (and L2) between timed steps: a 1 GiB
+    streaming copy (two 512 MiB buffers) through gdn_stream_copy, queued on the
+    stream outside the steps' timing events."""
+
+    def __init__(self, torch, gdn, device, nbytes=512 << 20):
+        self.gdn = gdn
+        self.src = torch.ones(nbytes, dtype=torch.uint8, device=device)
+        self.dst = torch.empty_like(self.src)
+
+    def __call__(self):
+        self.gdn.stream_copy(self.src, self.dst)
+
+
+def hbm_probe(torch, gdn, hip, device, nbytes=1 << 30, reps=20):
+    """Achievable HBM bandwidth: a 1 GiB device-to-device copy through the
+    library's own streaming copy kernel (read once, write once: 2 GiB of traffic,
+    8x the Infinity Cache), median of `reps` event-timed copies."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    sptr = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        gdn.stream_copy(src, dst)
+    torch.cuda.synchronize()
+    st = stats(per_step_ms(hip, sptr, lambda: gdn.stream_copy(src, dst), reps))
+    ok = bool(torch.equal(src[:4096], dst[:4096])) and bool(torch.equal(src[-4096:], dst[-4096:]))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"kernel": "gdn_stream_copy", "bytes_per_copy": 2 * nbytes, "median_us": st["median_ms"] * 1e3,
+            "gb_per_s": 2 * nbytes / (st["median_ms"] * 1e-3) / 1e9,
+            "gb_per_s_best": 2 * nbytes / (st["min_ms"] * 1e-3) / 1e9, "copy_checked": ok}
+
+
 def _dev(arr, dtype, torch, device):
     import numpy as np
 
@@ -272,12 +326,16 @@ def bench_prefill(args, torch, gdn, hip, device, gated=False):
     stage_ms = {s: sum(hip.elapsed_ms(ev[i][2 * j], ev[i][2 * j + 1]) for i in range(K)) / K
                 for j, s in enumerate(STAGES)}
     ms_step = total_ms / K
+    # Pass 3: per-step distribution, back to back; pass 4: each step after a
+    # cache-evicting copy (outside its events), i.e. from HBM-resident data.
+    nstep = max(K, 20)
+    warm = stats(per_step_ms(hip, sptr, step, nstep))
+    cold = stats(per_step_ms(hip, sptr, step, nstep, flush=CacheFlush(torch, gdn, device)))
     es = 2 if dt == "bf16" else 4
     bytes_, flops = prefill_work(inp.T, inp.N, lay["n_chunks"], inp.H_q, inp.H_v, inp.d_k, es,
                                  has_s0=s0 is not None, gated=gated)
     return dict(inp=inp, lay=lay, ms_step=ms_step, wall_s=wall, stage_ms=stage_ms, bytes=bytes_, flops=flops,
-                stages=STAGES,
-                ms_step_with_events=timed_ms)
+                stages=STAGES, ms_step_with_events=timed_ms, warm=warm, cold=cold)
 
 
 def bench_prefill_serving(args, torch, gdn, device):
@@ -331,6 +389,40 @@ def bench_prefill_serving(args, torch, gdn, device):
     ms = t0.elapsed_time(t1) / args.steps
     return {"workload": args.workload + " from raw q, k, a, b (front end in the kernels) with the gated read-out",
             "ms_per_step": ms, "tokens_per_s": inp.T / (ms * 1e-3)}
+
+
+def bench_prefill_many(args, torch, gdn, hip, device):
+    """A serving prefill batch of 256 short requests (many_256req: lengths uniform
+    in [1, 256], 34422 tokens, 32 value heads): gdn_chunk_fwd with host
+    cu_seqlens and gdn_chunk_fwd_dev with device cu_seqlens, per-step medians."""
+    import gdn_inputs
+
+    inp = gdn_inputs.make_workload("many_256req")
+    q, k, v = (_dev(x, inp.dtype, torch, device) for x in (inp.q, inp.k, inp.v))
+    g, beta = _dev(inp.g, "f32", torch, device), _dev(inp.beta, "f32", torch, device)
+    s0 = _dev(inp.initial_state, "f32", torch, device)
+    out = torch.empty((inp.T, inp.H_v, inp.d_v), dtype=q.dtype, device=device)
+    fin = torch.empty((inp.N, inp.H_v, inp.d_k, inp.d_v), dtype=torch.float32, device=device)
+    ws = torch.empty(gdn.workspace_size(inp.T, inp.cu_seqlens, inp.H_q, inp.H_v, inp.d_k, inp.d_v, inp.dtype),
+                     dtype=torch.uint8, device=device)
+    wsd = torch.empty(gdn.dev_workspace_size(inp.T, inp.N, inp.H_q, inp.H_v, inp.d_k, inp.d_v, inp.dtype),
+                      dtype=torch.uint8, device=device)
+    cud = torch.tensor(inp.cu_seqlens, dtype=torch.int32, device=device)
+    sptr = torch.cuda.current_stream().cuda_stream
+    host = lambda: gdn.chunk_fwd(q, k, v, g, beta, inp.cu_seqlens, initial_state=s0, scale=inp.scale,  # noqa: E731
+                                 out=out, final_state=fin, workspace=ws)
+    devp = lambda: gdn.chunk_fwd_dev(q, k, v, g, beta, cud, initial_state=s0, scale=inp.scale,  # noqa: E731
+                                     out=out, final_state=fin, workspace=wsd)
+    res = {"workload": f"many_256req: {inp.N} sequences, lengths uniform in [1, 256], T={inp.T}, H_q={inp.H_q}, "
+                       f"H_v={inp.H_v}, d={inp.d_k}, bf16"}
+    for name, fn in (("gdn_chunk_fwd", host), ("gdn_chunk_fwd_dev", devp)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        st = stats(per_step_ms(hip, sptr, fn, max(args.steps, 20)))
+        res[name] = {"median_us": st["median_ms"] * 1e3, "min_us": st["min_ms"] * 1e3,
+                     "tokens_per_s": inp.T / (st["median_ms"] * 1e-3)}
+    return res
 
 
 def bench_decode(args, torch, gdn, hip, device, fused=False, gated=False, pooled=False):
@@ -395,11 +487,12 @@ def bench_decode(args, torch, gdn, hip, device, fused=False, gated=False, pooled
         step_fn(*toks[i % len(toks)], state, scale=scale, out=out)
         hip.record(evs[i][1], stream.cuda_stream)
     torch.cuda.synchronize()
-    kms = sum(hip.elapsed_ms(a, b) for a, b in evs) / K
+    kst = stats(sorted(hip.elapsed_ms(a, b) for a, b in evs))
+    kms = kst["mean_ms"]
     nbytes, nflops = decode_work(N, H_q, H_v, d, 2 if dt == "bf16" else 4, fused=fused)
     if gated:
         nbytes += N * H_v * d * (2 if dt == "bf16" else 4) + d * 4  # z, weight
-    return dict(N=N, ms_step=ms, kernel_ms=kms, bytes=nbytes, flops=nflops, steps=K)
+    return dict(N=N, ms_step=ms, kernel_ms=kms, kernel_stats=kst, bytes=nbytes, flops=nflops, steps=K)
 
 
 def bench_conv(args, torch, gdn, device):
@@ -472,10 +565,24 @@ def cpu_baseline(inp, target_s=10.0):
         avail = len(os.sched_getaffinity(0))
     except AttributeError:
         avail = os.cpu_count()
-    return dict(value=reps * Ts / total, unit="tokens/s", cores=threads, kind="oracle",
+    return dict(value=reps * Ts / total, unit="tokens/s", cores=threads, kind="oracle", cpu_model=cpu_model(),
                 sample=f"fp64 token recurrence (oracle/gdn_recurrence.c, OpenMP over value heads) on the first "
                        f"{Ts} of {inp.T} tokens, all {inp.H_v} value heads, run {reps} times in {total:.2f} s wall; "
                        f"{avail} host cores visible, {threads} OpenMP threads")
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first processor entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
 
 
 def copy_calibration(torch, device, gib=1.0):
@@ -495,7 +602,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_T4096",
-                    choices=["prefill_T4096", "varlen_8seq", "long_T65536", "tiny_f32_T100"])
+                    choices=["prefill_T4096", "varlen_8seq", "long_T65536", "many_256req", "tiny_f32_T100"])
     ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
                     help="restrict the run (used for counter collection)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -521,6 +628,12 @@ def main():
 
     res = {}
     pre = pre_g = dec = decf = decg = decp = None
+    hbm = None
+    if args.only in ("all", "prefill", "decode"):
+        hbm = hbm_probe(torch, gdn, hip, device)
+        print(f"[bench] achievable HBM (1 GiB streaming copy): {hbm['gb_per_s']:.0f} GB/s median, "
+              f"{hbm['gb_per_s_best']:.0f} best", file=sys.stderr, flush=True)
+        res["achievable_hbm"] = hbm
     if args.only in ("all", "prefill"):
         pre = bench_prefill(args, torch, gdn, hip, device)
         print(f"[bench] prefill {args.workload}: {pre['ms_step']:.4f} ms/step, stages "
@@ -534,6 +647,11 @@ def main():
         print(f"[bench] prefill {args.workload} from raw inputs + gated read-out: {pre_s['ms_per_step']:.4f} ms/step",
               file=sys.stderr, flush=True)
         res["prefill_serving"] = pre_s
+        if args.workload == "prefill_T4096":
+            many = bench_prefill_many(args, torch, gdn, hip, device)
+            print(f"[bench] prefill of 256 short requests: host cu_seqlens {many['gdn_chunk_fwd']['median_us']:.1f} us, "
+                  f"device cu_seqlens {many['gdn_chunk_fwd_dev']['median_us']:.1f} us", file=sys.stderr, flush=True)
+            res["prefill_many"] = many
     if args.only in ("all", "decode"):
         dec = bench_decode(args, torch, gdn, hip, device)
         print(f"[bench] decode: {dec['ms_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
@@ -576,7 +694,15 @@ def main():
                        "chunk": CHUNK, "initial_state": inp.initial_state is not None},
             "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS,
+                         "frac_of_achievable": achieved / hbm["gb_per_s"] if hbm else None,
                          "traffic": traffic},
+            "step_ms": pre["warm"],
+            "step_ms_cold": pre["cold"],
+            "tokens_per_s_median": tokens / (pre["warm"]["median_ms"] * 1e-3),
+            "tokens_per_s_cold_median": tokens / (pre["cold"]["median_ms"] * 1e-3),
+            "whole_step": {"algorithmic_mbytes": sum(pre["bytes"].values()) / 1e6,
+                           "gb_per_s": sum(pre["bytes"].values()) / (ms * 1e-3) / 1e9,
+                           "frac_of_peak": sum(pre["bytes"].values()) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
             "stages_us": {s: pre["stage_ms"][s] * 1e3 for s in STAGES},
             "ms_per_step_with_kernel_events": pre["ms_step_with_events"],
             "stage_hbm_frac": {s: pre["bytes"][s] / (pre["stage_ms"][s] * 1e-3) / 1e9 / HBM_PEAK_GBS
@@ -590,7 +716,8 @@ def main():
         gbs = dec["bytes"] / (dec["ms_step"] * 1e-3) / 1e9
         kgbs = dec["bytes"] / (dec["kernel_ms"] * 1e-3) / 1e9
         decode = {"workload": "decode_256x1", "us_per_step": dec["ms_step"] * 1e3, "state_gb_per_s": gbs,
-                  "kernel_us": dec["kernel_ms"] * 1e3,
+                  "kernel_us": dec["kernel_ms"] * 1e3, "kernel_us_median": dec["kernel_stats"]["median_ms"] * 1e3,
+                  "kernel_us_min": dec["kernel_stats"]["min_ms"] * 1e3,
                   "tokens_per_s": dec["N"] / (dec["ms_step"] * 1e-3), "steps": dec["steps"],
                   "roofline": {"bound": "hbm", "kernel": "recurrent_step", "achieved": kgbs, "peak": HBM_PEAK_GBS,
                                "unit": "GB/s", "frac": kgbs / HBM_PEAK_GBS,

@@ -18,7 +18,7 @@ from typing import Optional, Sequence
 
 __all__ = ["chunk_fwd", "chunk_fwd_scratch", "SCRATCH_BYTES", "recurrent_step", "recurrent_step_fused", "conv1d_silu", "conv1d_silu_step",
            "chunk_fwd_fused", "chunk_fwd_dev", "chunk_fwd_pooled", "conv1d_silu_pooled", "recurrent_step_fused_pooled", "conv1d_silu_step_pooled",
-           "state_rows_zero", "state_rows_copy", "workspace_layout", "workspace_size", "lib_path", "load_library",
+           "state_rows_zero", "state_rows_copy", "stream_copy", "workspace_layout", "workspace_size", "lib_path", "load_library",
            "GdnError", "CHUNK", "DTYPE_F32", "DTYPE_BF16"]
 
 CHUNK = 64
@@ -166,6 +166,8 @@ def load_library():
     lib.gdn_chunk_fwd_dev.argtypes = [P, P, P, P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P,
                                       ctypes.c_size_t, P, P]
     lib.gdn_chunk_fwd_dev.restype = ctypes.c_int
+    lib.gdn_stream_copy.argtypes = [P, P, ctypes.c_size_t, P]
+    lib.gdn_stream_copy.restype = ctypes.c_int
     lib.gdn_state_rows_zero.argtypes = [P, I32, ctypes.c_size_t, P, I32, P]
     lib.gdn_state_rows_copy.argtypes = [P, I32, ctypes.c_size_t, P, P, I32, P]
     for fn in ("gdn_chunk_fwd_pooled", "gdn_conv1d_silu_fwd_pooled", "gdn_recurrent_step_fused_pooled",
@@ -806,6 +808,21 @@ def _pool_rows(pool, src, dst, what, stream):
                                      _stream_ptr(stream))
     if rc != 0:
         raise GdnError(rc, what)
+
+
+def stream_copy(src, dst, stream=None):
+    """Measurement aid (gdn_stream_copy): dst := src as a plain streaming copy,
+    for the achievable-HBM figure.  Contiguous device tensors of equal byte size
+    (a multiple of 16)."""
+    lib = load_library()
+    _check_dev("src", src)
+    _check_dev("dst", dst)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same size in bytes")
+    rc = lib.gdn_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream_ptr(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_stream_copy")
 
 
 def state_rows_zero(pool, rows, stream=None):

@@ -21,7 +21,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libgdn.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["gdn_chunk.hip", "gdn_decode.hip", "gdn_conv.hip", "gdn_pool.hip", "gdn_scratch.hip", "gdn_api.cpp"]
+SOURCES = ["gdn_chunk.hip", "gdn_decode.hip", "gdn_conv.hip", "gdn_pool.hip", "gdn_scratch.hip", "gdn_probe.hip", "gdn_api.cpp"]
 ARCH = "gfx950"
 
 

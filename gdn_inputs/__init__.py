@@ -133,12 +133,13 @@ def make_prefill(
     state_std: Optional[float] = 0.02,
     beta_override: Optional[float] = None,
     g_override: Optional[float] = None,
+    max_len: int = 8192,
 ) -> PrefillInputs:
     """Draw one prefill batch.  ``seqlens`` is a list of sequence lengths, or an int
-    N meaning "draw N lengths uniform in [1, 8192]" (first draw of the stream)."""
+    N meaning "draw N lengths uniform in [1, max_len]" (first draw of the stream)."""
     rng = np.random.default_rng(seed)
     if isinstance(seqlens, (int, np.integer)):
-        seqlens = rng.integers(1, 8193, size=int(seqlens))
+        seqlens = rng.integers(1, max_len + 1, size=int(seqlens))
     seqlens = np.asarray(seqlens, dtype=np.int64)
     cu = np.zeros(len(seqlens) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(seqlens)
@@ -339,6 +340,9 @@ WORKLOADS = {
                         alpha_range=(0.85, 0.999), state_std=0.02),
     "long_T65536": dict(seed=4, seqlens=[65536], H_q=16, H_v=32, d_k=128, d_v=128, dtype="bf16",
                         alpha_range=(0.95, 0.9999), state_std=0.02),
+    # a serving prefill batch of many short requests (lengths uniform in [1, 256])
+    "many_256req": dict(seed=6, seqlens=256, max_len=256, H_q=16, H_v=32, d_k=128, d_v=128, dtype="bf16",
+                        alpha_range=(0.85, 0.999), state_std=0.02),
 }
 
 DECODE_WORKLOAD = dict(seed=5, N=256, H_q=16, H_v=32, d_k=128, d_v=128, dtype="bf16", steps=16,

@@ -465,6 +465,17 @@ int gdn_state_rows_zero(void *pool, int32_t pool_size, size_t row_bytes, const i
 int gdn_state_rows_copy(void *pool, int32_t pool_size, size_t row_bytes, const int32_t *src_rows,
                         const int32_t *dst_rows, int32_t n, hipStream_t stream);
 
+/*
+ * Measurement aid (not part of the GDN computation): dst[0 .. bytes) :=
+ * src[0 .. bytes) with 16-byte vector accesses over the whole chip, a plain
+ * read-once / write-once stream.  Its bandwidth, 2 * bytes / time, is the
+ * achievable HBM figure the library's kernels are compared with, and a copy of
+ * known size calibrates HBM byte counters.  Device buffers, 16-byte aligned,
+ * bytes a multiple of 16, not overlapping (GDN_EINVAL), asynchronous on
+ * `stream`.  bytes == 0 is a no-op.
+ */
+int gdn_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
+
 /* Text naming a status code.  For GDN_ELAUNCH it also names the last HIP error
  * this thread saw inside the library (the text is then thread-local and valid
  * until the next call into the library from this thread); otherwise, and for

@@ -430,3 +430,14 @@ def test_scratch_prefill_refuses_before_any_device_work(gdn):
     assert call([0, 4096], 4000) == -1          # cu[N] != T
     assert call([0, 100], 100, H_q=3) == -2
     assert call([0], 0) == 0                    # empty batch: no-op
+
+
+def test_stream_copy_validation(gdn):
+    """gdn_stream_copy (measurement aid) refuses bad arguments on the host."""
+    lib = gdn.load_library()
+    keep, p = _fake(8)
+    assert lib.gdn_stream_copy(p, p + 4096, 0, None) == 0         # nothing to copy
+    assert lib.gdn_stream_copy(None, p, 256, None) == -1
+    assert lib.gdn_stream_copy(p, p + 8, 256, None) == -2         # misaligned destination
+    assert lib.gdn_stream_copy(p, p + 256, 24, None) == -2        # not a multiple of 16 bytes
+    assert lib.gdn_stream_copy(p, p + 128, 256, None) == -1       # overlapping
