@@ -110,7 +110,80 @@ int32_t fill_table(gdn::SeqTable& tab, const int32_t* cu, int32_t s0, int32_t ns
     std::stable_sort(tab.order, tab.order + ns, [&](int32_t a, int32_t b) {
         return tab.choff[a + 1] - tab.choff[a] > tab.choff[b + 1] - tab.choff[b];
     });
+    // one sequence a state-scan bin until pack_scan_bins says otherwise
+    for (int32_t i = 0; i <= ns; ++i) tab.bin_first[i] = i;
+    tab.n_bins = ns;
+    tab.ct = 0;
     return c;
+}
+
+// Cost model of the state scan on MI355X (bf16, d = 128, all CUs busy), in
+// units of one serial step with one column tile a workgroup (1.15 us): a step
+// with 1, 2 or 4 tiles a workgroup (the MFMA and LDS work grows with the
+// tiles, the W and K loads do not), and the extra cost of moving from one
+// sequence of a bin to the next (final-state stores, initial-state loads).
+// Measured: 4 x 16384 tokens, 1.15 / 1.47 / 2.39 us a step; 64 x 128 tokens,
+// 1.5 / 2.1 / 3.1 us a sequence boundary.
+constexpr double kScanStep[3] = {1.0, 1.28, 2.08};
+constexpr double kScanSeq[3] = {1.3, 1.8, 2.7};
+
+// Longest-processing-time packing of the launch's sequences (tab.order, longest
+// first) into m bins, a sequence of c chunks weighing step c + seq; rewrites
+// order bin by bin, heaviest bin first, and bin_first.  Returns the heaviest
+// bin's weight.
+double lpt_bins(gdn::SeqTable& tab, int32_t m, double step, double seq, bool write) {
+    const int32_t ns = tab.num_seqs;
+    std::vector<double> load(m, 0.0);
+    std::vector<int32_t> bin_of(ns, 0);
+    for (int32_t i = 0; i < ns; ++i) {
+        const int32_t n = tab.order[i];
+        const int32_t b = (int32_t)(std::min_element(load.begin(), load.end()) - load.begin());
+        bin_of[i] = b;
+        load[b] += step * (tab.choff[n + 1] - tab.choff[n]) + seq;
+    }
+    const double heaviest = *std::max_element(load.begin(), load.end());
+    if (!write) return heaviest;
+    std::vector<int32_t> bins(m);
+    for (int32_t b = 0; b < m; ++b) bins[b] = b;
+    std::stable_sort(bins.begin(), bins.end(), [&](int32_t a, int32_t b) { return load[a] > load[b]; });
+    std::vector<int32_t> order(tab.order, tab.order + ns);
+    int32_t k = 0;
+    for (int32_t j = 0; j < m; ++j) {
+        tab.bin_first[j] = k;
+        for (int32_t i = 0; i < ns; ++i)
+            if (bin_of[i] == bins[j]) tab.order[k++] = order[i];
+    }
+    tab.bin_first[m] = k;
+    tab.n_bins = m;
+    return heaviest;
+}
+
+// State-scan work split for a host table: the column tiles per workgroup (ct)
+// and the bins of sequences a workgroup scans one after another.  A workgroup
+// holds a CU (its LDS), so a launch of more workgroups than CUs runs in waves,
+// each paying a workgroup's start-up and drain; instead the sequences are
+// packed into as many bins as there are CUs for them (cus / workgroups a bin),
+// at most one sequence a bin, and ct is the one whose heaviest bin is the
+// cheapest under the cost model.
+void pack_scan_bins(gdn::SeqTable& tab, int32_t H_v, int32_t d, bool bf16, int32_t cus) {
+    const int32_t ns = tab.num_seqs;
+    if (ns <= 0) return;
+    const int32_t nt = d / 16;
+    int32_t best_ci = 0, best_m = 1;
+    double best = 0.0;
+    for (int32_t ci = 0; ci < (bf16 ? 3 : 1); ++ci) {  // ct = 1 << ci
+        const int64_t per_bin = (int64_t)H_v * (nt >> ci);  // workgroups a bin
+        const int32_t m = (int32_t)std::max<int64_t>(1, std::min<int64_t>(ns, cus / per_bin));
+        const int64_t waves = (m * per_bin + cus - 1) / cus;
+        const double cost = lpt_bins(tab, m, kScanStep[ci], kScanSeq[ci], false) * (double)waves;
+        if (ci == 0 || cost < best) {
+            best = cost;
+            best_ci = ci;
+            best_m = m;
+        }
+    }
+    lpt_bins(tab, best_m, kScanStep[best_ci], kScanSeq[best_ci], true);
+    tab.ct = 1 << best_ci;
 }
 
 hipError_t run_chunk(const gdn::ChunkParams& p, gdn_dtype dt, int d, hipStream_t s, hipEvent_t const* ev) {
@@ -265,6 +338,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, 
         const int32_t ns = std::min<int32_t>(gdn::MAX_SEQS_PER_LAUNCH, num_seqs - s0);
         chunk_base = fill_table(p.tab, cu_seqlens_host, s0, ns, chunk_base, slots, initial_state != nullptr,
                                 final_state != nullptr);
+        pack_scan_bins(p.tab, H_v, d_k, dtype == GDN_BF16, gdn::cu_count());
         hipEvent_t const* ev = (s0 == 0 && stage_events) ? reinterpret_cast<hipEvent_t const*>(stage_events) : nullptr;
         const hipError_t e = run_chunk(p, dtype, d_k, stream, ev);
         if (e != hipSuccess) return hip_fail(e);
@@ -529,6 +603,8 @@ int gdn_chunk_fwd_dev(const void* q, const void* k, const void* v, const float* 
     for (int32_t s0 = 0; s0 < num_seqs; s0 += gdn::MAX_SEQS_PER_LAUNCH) {
         const int32_t ns = std::min<int32_t>(gdn::MAX_SEQS_PER_LAUNCH, num_seqs - s0);
         p.tab.num_seqs = ns;
+        p.tab.n_bins = ns;  // one sequence a bin (build_tables)
+        p.tab.ct = 0;
         p.tab.n_chunks = (int32_t)std::min<int64_t>(nb, ((int64_t)T + GDN_CHUNK - 1) / GDN_CHUNK + ns);
         p.dtab = tabs + s0 / gdn::MAX_SEQS_PER_LAUNCH;
         e = run_chunk(p, dtype, d_k, stream, nullptr);

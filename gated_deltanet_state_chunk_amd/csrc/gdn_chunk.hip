@@ -55,6 +55,49 @@ __device__ __forceinline__ ChunkPos locate_chunk(const SeqTable& tab, int ci) {
     return c;
 }
 
+// The chunks of the sequences of one state-scan bin (order[kb .. ke) of the
+// launch table), sequence after sequence, empty sequences skipped.  All its
+// values are uniform across a workgroup.
+struct BinCursor {
+    const SeqTable* tab;
+    int k, ke;      // position in order[], end of the bin
+    int n, c, nch;  // sequence, chunk within it, its chunk count
+    int c0, t0, L;  // its first global chunk, first token and length
+    __device__ void at_seq() {
+        n = tab->order[k];
+        c = 0;
+        c0 = tab->choff[n];
+        nch = tab->choff[n + 1] - c0;
+        t0 = tab->cu[n];
+        L = tab->cu[n + 1] - t0;
+    }
+    __device__ void skip_empty() {
+        while (k < ke && nch == 0)
+            if (++k < ke) at_seq();
+    }
+    __device__ void begin(const SeqTable& t, int kb, int kend) {
+        tab = &t;
+        k = kb;
+        ke = kend;
+        nch = 0;
+        if (k < ke) {
+            at_seq();
+            skip_empty();
+        }
+    }
+    __device__ bool valid() const { return k < ke; }
+    __device__ void next() {
+        if (++c == nch && ++k < ke) {
+            at_seq();
+            skip_empty();
+        }
+    }
+    __device__ int ci() const { return c0 + c; }                      // global chunk index
+    __device__ int ell() const { return min(CHUNK, L - c * CHUNK); }  // valid length
+    __device__ int token() const { return t0 + c * CHUNK; }           // first token
+    __device__ bool last() const { return c + 1 == nch; }
+};
+
 // acc += X[0:16, 0:16] @ Y[0:16, 0:16] for fp32 blocks in LDS with row strides
 // XS and YS: four v_mfma_f32_16x16x4_f32 (lane (m, a) supplies X[m][4s+a] and Y[4s+a][m]).
 template <int XS, int YS>
@@ -789,7 +832,7 @@ __device__ __forceinline__ Frag<T> k_col_frag(const char* kst, int m, int ks, in
 template <typename T, int D, int CT>
 __device__ __forceinline__ void chunk_output_waves(const ChunkParams& p, const char* smem, const char* LS,
                                                    const char* LX, char* LO, char* LQ, int o, int lane,
-                                                   const SeqTable& tab, int n, int hq, int nch, int L_n) {
+                                                   const SeqTable& tab, int kb, int ke, int hq, int nch) {
     static_assert(sizeof(T) == 2, "the output waves are bf16");
     using SS = StateStage<T, D, CT, true>;
     constexpr int KS = D / 32;
@@ -813,22 +856,25 @@ __device__ __forceinline__ void chunk_output_waves(const ChunkParams& p, const c
     char* const lq = LQ + o * 16 * RB;
     // With the front end the rows come normalised, already in that order, from
     // chunk_prep's copy Qc (contiguous: the wave's 16 rows are 16 RB bytes).
-    auto load_q = [&](int c) {
+    BinCursor cq;  // the chunk whose query rows are copied next
+    cq.begin(tab, kb, ke);
+    auto load_q = [&]() {
         if (p.Qc) {
-            const char* q0 = reinterpret_cast<const char*>(p.Qc) +
-                             (((size_t)(tab.choff[n] + c) * p.H_q + hq) * CHUNK + 16 * o) * RB;
+            const char* q0 = reinterpret_cast<const char*>(p.Qc) + (((size_t)cq.ci() * p.H_q + hq) * CHUNK + 16 * o) * RB;
 #pragma unroll
             for (int i = 0; i < 16 * PPR / 64; ++i) dma_1k(q0 + 1024 * i, lq + 1024 * i, lane);
+            cq.next();
             return;
         }
-        const int ell = min(CHUNK, L_n - c * CHUNK);
-        const char* q0 = reinterpret_cast<const char*>(p.q) + ((size_t)(tab.cu[n] + c * CHUNK) * p.H_q + hq) * RB;
+        const int ell = cq.ell();
+        const char* q0 = reinterpret_cast<const char*>(p.q) + ((size_t)cq.token() * p.H_q + hq) * RB;
 #pragma unroll
         for (int i = 0; i < 16 * PPR / 64; ++i) {
             const int e = 64 * i + lane, r = e / PPR, pc = (e % PPR) ^ (r % PPR);
             const char* src = q0 + (size_t)min(16 * o + r, ell - 1) * p.H_q * RB + 16 * pc;
             __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(lq + 1024 * i), 16, 0, 0);
         }
+        cq.next();
     };
     // fragment ks of this lane's row: slots 0..3 <- d_k 32 ks + 4 grp .. + 3,
     // slots 4..7 <- 32 ks + 16 + 4 grp .. + 3 (the exchange fragments' d_k order)
@@ -850,7 +896,7 @@ __device__ __forceinline__ void chunk_output_waves(const ChunkParams& p, const c
         if (o >= 2) pf1 = P[(f0 + 1) * 64 + lane];
         gq = reinterpret_cast<const float*>(st + SS::G_OFF)[pos];
     };
-    if (nch > 0) load_q(0);
+    if (nch > 0) load_q();
     wait_lgkmcnt0();
     asm volatile("s_barrier" ::: "memory");  // B0
     if (nch > 0) read_stage(0);
@@ -862,7 +908,7 @@ __device__ __forceinline__ void chunk_output_waves(const ChunkParams& p, const c
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[ks] = q_frag(ks);
         wait_lgkmcnt0();                         // read out before the next chunk's rows overwrite them
-        if (c + 1 < nch) load_q(c + 1);
+        if (c + 1 < nch) load_q();
         // -(h^T Q^T) from LS
         f32x4 inter[CT];
 #pragma unroll
@@ -895,28 +941,28 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
     constexpr int KS = D / 32;   // contraction steps over d_k
     constexpr int TPW = D / 64;  // S row tiles per compute wave
     constexpr int NST = SS::NST;
-    // Work groups of NT tiles, one per (sequence, value head), longest sequences
-    // first; group g runs on XCD g % 8 (workgroup i lands on XCD i % 8) with its
-    // tiles in consecutive slots, so the tiles of a head share an L2 and every
-    // XCD gets an even share of long and short sequences.
+    // Work groups of NTW workgroups, one per (bin, value head), the bins
+    // heaviest first; group g runs on XCD g % 8 (workgroup i lands on XCD i % 8)
+    // with its tiles in consecutive slots, so the tiles of a head share an L2
+    // and every XCD gets an even share of heavy and light bins.  A bin is a run
+    // of sequences the workgroup scans one after another (one sequence, unless
+    // the launch has more sequences than fit on the chip side by side).
     (void)padded;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int gi = (slot / NTW) * 8 + xcd;
     const SeqTable& tab = DEV ? *p.dtab : p.tab;
-    if (gi >= tab.num_seqs * p.H_v) return;
+    if (gi >= tab.n_bins * p.H_v) return;
     const int tile = slot % NTW;  // column tiles CT tile .. CT tile + CT - 1
-    const int h = gi % p.H_v, n = tab.order[gi / p.H_v];
+    const int h = gi % p.H_v, bin = gi / p.H_v;
+    const int kb = tab.bin_first[bin], ke = tab.bin_first[bin + 1];
+    int nch = 0;  // chunks of the bin
+    for (int k = kb; k < ke; ++k) nch += tab.choff[tab.order[k] + 1] - tab.choff[tab.order[k]];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
-    const int si = tab.s_in[n], so = tab.s_out[n];  // state rows (-1: zeros / not kept)
-    const size_t in_off = ((size_t)max(si, 0) * p.H_v + h) * D * D;
-    const size_t out_off = ((size_t)max(so, 0) * p.H_v + h) * D * D;
-    const int L_n = tab.cu[n + 1] - tab.cu[n];
-    const int nch = tab.choff[n + 1] - tab.choff[n];
-    const int c0 = tab.choff[n];
-    // (chunk, key head) index of chunk c of this sequence in Kc
     const int hq = h / p.G;
-    auto kch = [&](int c) { return (size_t)(c0 + c) * p.H_q + hq; };
+    // (chunk, value head) and (chunk, key head) indices of the chunk a cursor is at
+    auto vch = [&](const BinCursor& cu) { return (size_t)cu.ci() * p.H_v + h; };
+    auto kch = [&](const BinCursor& cu) { return (size_t)cu.ci() * p.H_q + hq; };
 
     __shared__ __attribute__((aligned(16))) char smem[NST * SS::BYTES + SS::EXCH + SS::OBUF + SS::QBUF + 256];
     char* const LS = smem + NST * SS::BYTES;  // KS x CT blocks: -S (block ks CT + ct)
@@ -935,7 +981,7 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
 
     if constexpr (FO) {
         if (w > 4 + SS::NPW) {
-            chunk_output_waves<T, D, CT>(p, smem, LS, LX, LO, LQ, w - (5 + SS::NPW), lane, tab, n, hq, nch, L_n);
+            chunk_output_waves<T, D, CT>(p, smem, LS, LX, LO, LQ, w - (5 + SS::NPW), lane, tab, kb, ke, hq, nch);
             return;
         }
     }
@@ -1003,10 +1049,15 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
         // Each piece is gathered from LO, where output wave o's lane 16 g + r
         // holds columns 4 g .. 4 g + 3 of row 16 o + r: the lanes of groups 2 hf
         // and 2 hf + 1, 128 bytes apart.
-        auto store_o = [&](int c) {
+        BinCursor co, cs, cpf;  // chunks of the next output store, of the step, of the next prefetch
+        co.begin(tab, kb, ke);
+        cs.begin(tab, kb, ke);
+        cpf.begin(tab, kb, ke);
+        for (int i = 0; i < PF; ++i) cpf.next();
+        auto store_o = [&]() {
             if constexpr (FO) {
                 constexpr int LPRW = 2 * CT, RPI = 64 / LPRW;  // lanes per row, rows per instruction
-                const int ell = min(CHUNK, L_n - c * CHUNK);
+                const int ell = co.ell();
                 const int pc = lane % LPRW, ct = pc >> 1, hf = pc & 1;
                 u32x4 ov[LPRW];
 #pragma unroll
@@ -1017,34 +1068,37 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
                 }
                 lds_wait_untracked<LPRW>(ov);
                 char* o0 = reinterpret_cast<char*>(p.out) +
-                           (((size_t)(tab.cu[n] + c * CHUNK) * p.H_v + h) * D + 16 * (CT * tile + ct) + 8 * hf) * EB;
+                           (((size_t)co.token() * p.H_v + h) * D + 16 * (CT * tile + ct) + 8 * hf) * EB;
 #pragma unroll
                 for (int i = 0; i < LPRW; ++i) {
                     const int row = RPI * i + lane / LPRW;
                     if (row < ell) *reinterpret_cast<u32x4*>(o0 + (size_t)row * p.H_v * D * EB) = ov[i];
                 }
+                co.next();
             }
         };
         asm volatile("s_barrier" ::: "memory");  // B0
         for (int c = 0; c < nch; ++c) {
-            const size_t ch = (size_t)(c0 + c) * p.H_v + h;
+            const size_t ch = vch(cs);
+            cs.next();
             asm volatile("s_barrier" ::: "memory");  // B1(c)
-            if (p.l2_prefetch && c + PF < nch) {
-                const size_t chp = (size_t)(c0 + c + PF) * p.H_v + h;
+            if (p.l2_prefetch && cpf.valid()) {
+                const size_t chp = vch(cpf), kchp = kch(cpf);
 #pragma unroll
                 for (int q = 0; q < NPL; ++q) {
                     const int L = lane + 64 * q;
                     if (L < 2 * LPT) {
                         const int li = tile * LPT + L % LPT;
                         const char* a = L >= LPT
-                                            ? reinterpret_cast<const char*>(p.Kc) + kch(c + PF) * SS::K_BYTES + li * 128
+                                            ? reinterpret_cast<const char*>(p.Kc) + kchp * SS::K_BYTES + li * 128
                                             : reinterpret_cast<const char*>(p.W) + chp * SS::W_BYTES + li * 128;
                         __builtin_amdgcn_global_load_lds((gptr_t)a, (lptr_t)sink, 4, 0, 0);
                     }
                 }
             }
+            cpf.next();
             if constexpr (FO) {
-                if (c > 0) store_o(c - 1);
+                if (c > 0) store_o();
             }
             if (!store_hx) {
                 asm volatile("s_barrier" ::: "memory");  // B2(c)
@@ -1085,7 +1139,7 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
         }
         if constexpr (FO) {
             asm volatile("s_barrier" ::: "memory");  // B_end: the last output tile is in LO
-            if (nch > 0) store_o(nch - 1);
+            if (nch > 0) store_o();
         }
         wait_vmcnt<0>();  // no prefetch may land in LDS after the workgroup has ended
         return;
@@ -1103,6 +1157,8 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
         constexpr int RC_0 = R0_0 - state_part_loads<SS>(0, 1), RC_1 = R0_1 - state_part_loads<SS>(1, 1);
         static_assert(WB_0 < 64 && WB_1 < 64 && RC_0 >= 0 && RC_1 >= 0, "producer loads exceed the vmcnt range");
 
+        BinCursor cp;  // the chunk whose loads go out next
+        cp.begin(tab, kb, ke);
         // Chunks 0 .. NST-1 up front; chunk 0 lands before B0.
 #pragma unroll
         for (int b = 0; b < NST; ++b) {
@@ -1111,9 +1167,9 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
                 if (pw == 0) wait_vmcnt<RC_0>(); else wait_vmcnt<RC_1>();
             }
             if (b < nch) {
-                const size_t chb = (size_t)(c0 + b) * p.H_v + h;
-                state_issue<T, D, CT, FO>(smem + b * SS::BYTES, p, chb, kch(b), tile, lane, pw, 0);
-                state_issue<T, D, CT, FO>(smem + b * SS::BYTES, p, chb, kch(b), tile, lane, pw, 1);
+                state_issue<T, D, CT, FO>(smem + b * SS::BYTES, p, vch(cp), kch(cp), tile, lane, pw, 0);
+                state_issue<T, D, CT, FO>(smem + b * SS::BYTES, p, vch(cp), kch(cp), tile, lane, pw, 1);
+                cp.next();
             }
         }
         // The producers' barriers are plain s_barrier: a workgroup release fence
@@ -1127,12 +1183,12 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
             asm volatile("s_barrier" ::: "memory");  // B1(c): chunk c is in registers, its stage free
             const int cn = c + NST;
             char* stn = smem + (cn % NST) * SS::BYTES;
-            const size_t chn = (size_t)(c0 + cn) * p.H_v + h;
+            const size_t chn = vch(cp), kchn = kch(cp);  // chunk cn
             // A chunk's loads go out in two halves, one in each phase of a step;
             // chunk c + 1 is read after B2(c).
             if (cn < nch) {
                 if (pw == 0) wait_vmcnt<R0_0>(); else wait_vmcnt<R0_1>();
-                state_issue<T, D, CT, FO>(stn, p, chn, kch(cn), tile, lane, pw, 0);
+                state_issue<T, D, CT, FO>(stn, p, chn, kchn, tile, lane, pw, 0);
                 if (pw == 0) wait_vmcnt<WB_0>(); else wait_vmcnt<WB_1>();
             } else {
                 wait_vmcnt<0>();
@@ -1140,7 +1196,8 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
             asm volatile("s_barrier" ::: "memory");  // B2(c)
             if (cn < nch) {
                 if (pw == 0) wait_vmcnt<R1_0>(); else wait_vmcnt<R1_1>();
-                state_issue<T, D, CT, FO>(stn, p, chn, kch(cn), tile, lane, pw, 1);
+                state_issue<T, D, CT, FO>(stn, p, chn, kchn, tile, lane, pw, 1);
+                cp.next();
             }
         }
         if constexpr (FO) asm volatile("s_barrier" ::: "memory");  // B_end
@@ -1148,25 +1205,69 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
     }
 
     // ---------------- compute waves ----------------
+    // This wave's rows of S for the workgroup's column tiles: entry i of
+    // [tt][ct] is row 16 (w TPW + tt) + 4 grp + i, column 16 (CT tile + ct) + r16.
+    auto s_index = [&](int tt, int ct, int i) {
+        return (size_t)(16 * (w * TPW + tt) + 4 * grp + i) * D + 16 * (CT * tile + ct) + r16;
+    };
+    // initial state of sequence n (zeros without a row)
+    auto load_s = [&](int n, f32x4 (&dst)[TPW][CT]) {
+        const int si = tab.s_in[n];
+        const float* src = p.s0 + ((size_t)max(si, 0) * p.H_v + h) * D * D;
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                if (si < 0) {
+                    dst[tt][ct] = zero4();
+                    continue;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[tt][ct][i] = src[s_index(tt, ct, i)];
+            }
+    };
+    // final state of sequence n, if it has a row
+    auto store_s = [&](int n, const f32x4 (&src)[TPW][CT]) {
+        const int so = tab.s_out[n];
+        if (so < 0) return;
+        float* dst = p.sfinal + ((size_t)so * p.H_v + h) * D * D;
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[s_index(tt, ct, i)] = src[tt][ct][i];
+    };
     f32x4 S[TPW][CT];
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-        const int m = w * TPW + tt;
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            const int col = 16 * (CT * tile + ct) + r16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[tt][ct][i] = si >= 0 ? p.s0[in_off + (size_t)(16 * m + 4 * grp + i) * D + col] : 0.f;
-            lds_put4(xf(LS, (m >> 1) * CT + ct, lane), m & 1, S[tt][ct], -1.f);
+    // Sequences without tokens end in the state they start from.
+    for (int k = kb; k < ke; ++k) {
+        const int n = tab.order[k];
+        if (tab.choff[n + 1] == tab.choff[n] && tab.s_out[n] >= 0) {
+            f32x4 S0[TPW][CT];
+            load_s(n, S0);
+            store_s(n, S0);
         }
+    }
+    BinCursor rd;  // the chunk whose stage is read next
+    rd.begin(tab, kb, ke);
+    auto put_s = [&]() {  // -S into LS, the operand of the next step
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+            const int m = w * TPW + tt;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) lds_put4(xf(LS, (m >> 1) * CT + ct, lane), m & 1, S[tt][ct], -1.f);
+        }
+    };
+    if (nch > 0) {
+        load_s(rd.n, S);
+        put_s();
     }
     // Operand fragments of one chunk, read from its LDS stage.
     Frag<T> wf[KS], kfg[TPW][2];
     Raw4<T> uf[CT];
     float gl = 0.f;
     float4 fx;  // kf of this wave's X rows (positions 16 w + 4 grp + i)
-    auto read_stage = [&](int c) {
+    auto read_stage = [&](int c) {  // chunk c of the bin, at cursor rd
         const char* st = smem + (c % NST) * SS::BYTES;
         const Frag<T>* Wst = reinterpret_cast<const Frag<T>*>(st);
         const char* Kst = st + SS::W_BYTES;
@@ -1180,75 +1281,89 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
             for (int ks = 0; ks < 2; ++ks) kfg[tt][ks] = k_col_frag<T, D>(Kst, w * TPW + tt, ks, lane);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) uf[ct] = Ust[ct * (SS::U1_BYTES / (int)sizeof(Raw4<T>)) + ((w >> 1) * 64 + lane) * 2 + (w & 1)];
-        gl = Gst[min(CHUNK, L_n - c * CHUNK) - 1];
+        gl = Gst[rd.ell() - 1];
         fx = *reinterpret_cast<const float4*>(Gst + CHUNK + 16 * w + 4 * grp);
+        rd.next();
     };
-    lds_sync();  // B0: stages 0 and 1 ready
+    auto bar = [] {  // the compute waves' LDS traffic is all a barrier waits for
+        wait_lgkmcnt0();
+        asm volatile("s_barrier" ::: "memory");
+    };
+    bar();  // B0: stages 0 and 1 ready
     if (nch > 0) read_stage(0);
-    for (int c = 0; c < nch; ++c) {
-        lds_sync();  // B1(c): -S in LS; chunk c's stage may be refilled
-        Frag<T> sb[CT][KS];
+    // The bin's sequences one after another (the inner loop is one sequence's
+    // chunks; the sequence change stays out of it).  c counts the bin's chunks.
+    int c = 0;
+    for (int k = kb; k < ke; ++k) {
+        const int n = tab.order[k];
+        const int nc = tab.choff[n + 1] - tab.choff[n];
+        for (int j = 0; j < nc; ++j, ++c) {
+            bar();  // B1(c): -S in LS; chunk c's stage may be refilled
+            Frag<T> sb[CT][KS];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) sb[ct][ks] = xf(LS, ks * CT + ct, lane);
-        // X = U - W S for positions 16 w .. 16 w + 15 (one independent chain per column tile)
-        f32x4 X[CT];
+                for (int ks = 0; ks < KS; ++ks) sb[ct][ks] = xf(LS, ks * CT + ct, lane);
+            // X = U - W S for positions 16 w .. 16 w + 15 (one independent chain per column tile)
+            f32x4 X[CT];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) X[ct] = raw4_to_f32(uf[ct]);
+            for (int ct = 0; ct < CT; ++ct) X[ct] = raw4_to_f32(uf[ct]);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) X[ct] = mma(wf[ks], sb[ct][ks], X[ct]);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            lds_put4(xf(LX, (w >> 1) * CT + ct, lane), w & 1, X[ct], 1.f);
-            const f32x4 Y = f32x4{X[ct][0] * fx.x, X[ct][1] * fx.y, X[ct][2] * fx.z, X[ct][3] * fx.w};
-            lds_put4(xf(LY, (w >> 1) * CT + ct, lane), w & 1, Y, 1.f);
-        }
-        const float eg = __expf(gl);
-#pragma unroll
-        for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) S[tt][ct] *= eg;
-        Frag<T> kc[TPW][2];
-#pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            kc[tt][0] = kfg[tt][0];
-            kc[tt][1] = kfg[tt][1];
-        }
-        lds_sync();  // B2(c): all of X in LX and kf X in LY; stage c + 1 ready
-        if (c + 1 < nch) read_stage(c + 1);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            const Frag<T> xb0 = xf(LY, ct, lane), xb1 = xf(LY, CT + ct, lane);
-#pragma unroll
-            for (int tt = 0; tt < TPW; ++tt) {
-                S[tt][ct] = mma(kc[tt][0], xb0, S[tt][ct]);
-                S[tt][ct] = mma(kc[tt][1], xb1, S[tt][ct]);
-            }
-        }
-#pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            const int m = w * TPW + tt;
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) lds_put4(xf(LS, (m >> 1) * CT + ct, lane), m & 1, S[tt][ct], -1.f);
-        }
-    }
-    if constexpr (FO) lds_sync();  // B_end
-    if (so >= 0) {
-#pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            const int m = w * TPW + tt;
+                for (int ct = 0; ct < CT; ++ct) X[ct] = mma(wf[ks], sb[ct][ks], X[ct]);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-                const int col = 16 * (CT * tile + ct) + r16;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    p.sfinal[out_off + (size_t)(16 * m + 4 * grp + i) * D + col] = S[tt][ct][i];
+                lds_put4(xf(LX, (w >> 1) * CT + ct, lane), w & 1, X[ct], 1.f);
+                const f32x4 Y = f32x4{X[ct][0] * fx.x, X[ct][1] * fx.y, X[ct][2] * fx.z, X[ct][3] * fx.w};
+                lds_put4(xf(LY, (w >> 1) * CT + ct, lane), w & 1, Y, 1.f);
             }
+            const float eg = __expf(gl);
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) S[tt][ct] *= eg;
+            Frag<T> kc[TPW][2];
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                kc[tt][0] = kfg[tt][0];
+                kc[tt][1] = kfg[tt][1];
+            }
+            bar();  // B2(c): all of X in LX and kf X in LY; stage c + 1 ready
+            if (c + 1 < nch) read_stage(c + 1);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const Frag<T> xb0 = xf(LY, ct, lane), xb1 = xf(LY, CT + ct, lane);
+#pragma unroll
+                for (int tt = 0; tt < TPW; ++tt) {
+                    S[tt][ct] = mma(kc[tt][0], xb0, S[tt][ct]);
+                    S[tt][ct] = mma(kc[tt][1], xb1, S[tt][ct]);
+                }
+            }
+            if (j + 1 < nc) put_s();
+        }
+        if (nc == 0) continue;  // (its final state was written above)
+        // Sequence end, after B2 of its last chunk: its final state leaves, and
+        // the initial state of the bin's next sequence with tokens becomes S
+        // before B1 of the next step.  Loads go out before the stores: vmcnt
+        // counts stores too, so loads issued after them would also wait for
+        // the stores' acknowledgements.
+        if (c < nch) {
+            int k2 = k + 1;  // exists: chunks remain
+            while (tab.choff[tab.order[k2] + 1] == tab.choff[tab.order[k2]]) ++k2;
+            f32x4 S0[TPW][CT];
+            load_s(tab.order[k2], S0);
+            store_s(n, S);
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) S[tt][ct] = S0[tt][ct];
+            put_s();
+        } else {
+            store_s(n, S);
         }
     }
+    if constexpr (FO) bar();  // B_end
 }
 
 // ---------------------------------------------------------------------------
@@ -1595,7 +1710,11 @@ __global__ __launch_bounds__(64) void build_tables_kernel(const int32_t* __restr
             tb->s_out[lane] = has_out ? s0 + lane : -1;
             tb->order[rank] = lane;
         }
+        if (lane < ns) tb->bin_first[lane] = lane;  // one sequence a bin
         if (lane == 0) {
+            tb->bin_first[ns] = ns;
+            tb->n_bins = ns;
+            tb->ct = 0;
             tb->cu[ns] = last_end;
             tb->choff[ns] = chunk_base + total;
             tb->num_seqs = ns;
@@ -1623,7 +1742,7 @@ static inline int pad8(int x) { return (x + 7) & ~7; }
 
 // Compute units of the current device (cached per device), a multiple of 8 on
 // this chip (eight XCDs).
-static int cu_count() {
+int cu_count() {
     static std::atomic<int> cached[64];  // zero-initialised; concurrent callers store the same value
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -1641,13 +1760,17 @@ template <typename T, int D>
 hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEvent_t const* events) {
     const int work_ch = p.tab.n_chunks * p.H_v;
     const int grid_ch = pad8(work_ch);
-    const int groups = p.tab.num_seqs * p.H_v;  // (sequence, value head) pairs of the state scan
-    // Column tiles per state-scan workgroup (bf16): one while the chip has a CU
-    // for every 16-column tile (the shortest serial step: T = 4096, 32 heads),
-    // two up to two tiles a CU, four beyond: a step's W and K stream then
-    // serves 2 or 4 tiles (packed 8-sequence batch: 444 -> 311 -> 287 us).
+    const int groups = p.tab.n_bins * p.H_v;  // (bin, value head) pairs of the state scan
+    // Column tiles per state-scan workgroup: as the bins were packed for
+    // (host tables); with device tables (one sequence a bin, lengths unknown
+    // here) one while the chip has a CU for every 16-column tile, two up to two
+    // tiles a CU, four beyond: a step's W and K stream then serves 2 or 4 tiles.
     const int tiles = groups * (D / 16), cus = cu_count();
-    const int ct = sizeof(T) != 2 ? 1 : tiles <= cus ? 1 : tiles <= 2 * cus ? 2 : 4;
+    const int ct = sizeof(T) != 2         ? 1
+                   : p.tab.ct > 0         ? p.tab.ct
+                   : tiles <= cus         ? 1
+                   : tiles <= 2 * cus     ? 2
+                                          : 4;
     // With events, each kernel is launched with hipExtLaunchKernelGGL, whose
     // start/stop events are stamped by the kernel's own dispatch (kernel time
     // only, no launch gaps).

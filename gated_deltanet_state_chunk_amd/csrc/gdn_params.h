@@ -24,7 +24,14 @@ struct SeqTable {
     int32_t choff[MAX_SEQS_PER_LAUNCH + 1];  // global chunk offsets, choff[num_seqs] = chunk_begin + n_chunks
     int32_t s_in[MAX_SEQS_PER_LAUNCH];       // row of the initial-state array a sequence starts from, -1: zeros
     int32_t s_out[MAX_SEQS_PER_LAUNCH];      // row of the final-state array it ends in, -1: none
-    int32_t order[MAX_SEQS_PER_LAUNCH];      // sequences by decreasing chunk count (state scan dispatch order)
+    int32_t order[MAX_SEQS_PER_LAUNCH];      // sequences of each state-scan bin, bin by bin (see bin_first)
+    // State-scan bins: a workgroup of the scan walks the sequences of one bin
+    // (order[bin_first[b]] .. order[bin_first[b + 1] - 1]) one after another for
+    // its value head and column tiles.  ct: column tiles per scan workgroup the
+    // bins were packed for (0: the launcher chooses, one sequence per bin).
+    int32_t n_bins;
+    int32_t ct;
+    int32_t bin_first[MAX_SEQS_PER_LAUNCH + 1];
 };
 
 struct ChunkParams {
@@ -145,5 +152,7 @@ hipError_t launch_pool_rows(PoolRowsParams p, int32_t n, hipStream_t stream);
 // Records e as this thread's last HIP error (named by gdn_strerror) and returns
 // GDN_ELAUNCH (gdn_api.cpp).
 int hip_fail(hipError_t e);
+// Compute units of the current device (a multiple of 8).
+int cu_count();
 
 }  // namespace gdn

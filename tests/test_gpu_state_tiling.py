@@ -1,10 +1,12 @@
-"""GPU parity of the state scan's workgroup shapes: one, two or four 16-column
-tiles of d_v per workgroup, which the launcher picks from the number of tiles
-per CU (1 sequence x 32 heads x 8 tiles = one a CU on a 256-CU part; 2
-sequences = two; 5 sequences = more), on bf16 d = 128 with ragged lengths,
-against the fp64 oracle on every head.  The three shapes run the same MFMAs in
-the same order, so the results must also agree bitwise across them (the same
-head, same tokens, in batches of different sizes).
+"""GPU parity of the state scan's work split: one, two or four 16-column tiles
+of d_v per workgroup, and bins of sequences that one workgroup scans one after
+another.  The host picks both from the chunk counts (on a 256-CU part: one
+sequence of 4 chunks x 32 heads -> one tile a workgroup; 4 + 3 chunks -> two
+tiles, one sequence a bin; 4 + 3 + 2 + 1 + 2 chunks -> four tiles, four bins,
+one of them two sequences), checked on bf16 d = 128 with ragged lengths
+against the fp64 oracle on every head.  Every split runs the same MFMAs in
+the same order for a sequence, so the results must also agree bitwise across
+them (the same head, same tokens, in batches of different sizes).
 """
 import dataclasses
 
@@ -12,7 +14,7 @@ import numpy as np
 import pytest
 
 import gdn_inputs
-from tests.gpu_helpers import chunk_fwd_device, rel_err
+from tests.gpu_helpers import chunk_fwd_device, f32_dev, rel_err, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -59,8 +61,8 @@ def test_state_scan_tiling_bitwise_consistent(torch_cuda):
 @pytest.mark.parametrize("n_seq,d", [(8, 128), (40, 128), (40, 64)])
 def test_state_scan_tiling_odd_heads_many_sequences(torch_cuda, oracle_mod, n_seq, d):
     """Five value heads on five key heads (groups not a multiple of 8, so the
-    per-XCD grid is padded) over many short ragged sequences: 8 sequences at
-    d = 128 give 320 tiles (two a workgroup), 40 sequences four a workgroup."""
+    per-XCD grid is padded) over many short ragged sequences, with empty ones:
+    bins of several sequences a workgroup at every tile width."""
     lens = [int(x) for x in np.random.default_rng(702 + n_seq + d).integers(0, 140, n_seq)]
     inp = gdn_inputs.make_prefill(seed=703 + n_seq, seqlens=lens, H_q=5, H_v=5, d_k=d, d_v=d, dtype="bf16",
                                   state_std=0.02)
@@ -69,3 +71,51 @@ def test_state_scan_tiling_odd_heads_many_sequences(torch_cuda, oracle_mod, n_se
                                       inp.scale, initial_state=inp.initial_state.astype(np.float64))
     assert rel_err(out, ref_o) < 1e-2
     assert rel_err(fin, ref_s) < 1e-2
+
+
+def test_state_scan_bins_short_sequences_pool_and_empties(torch_cuda, oracle_mod):
+    """80 requests of 1..199 tokens, every tenth empty, at H_v = 32, d = 128,
+    over a state pool: the first launch group's 64 sequences go four bins of
+    about 16 sequences (four tiles a workgroup), the last 16 into bins of
+    their own shape.  Sampled heads against the oracle; an empty sequence ends
+    in the state it starts from (its cached row, or zeros without one); pool
+    rows no sequence names are untouched."""
+    import gated_deltanet_state_chunk_amd as gdn
+
+    torch = torch_cuda
+    rng = np.random.default_rng(704)
+    lens = [int(x) for x in rng.integers(1, 200, 80)]
+    for i in range(0, 80, 10):
+        lens[i] = 0
+    n, H_q, H_v, d, P = len(lens), 16, 32, 128, 96
+    inp = gdn_inputs.make_prefill(seed=705, seqlens=lens, H_q=H_q, H_v=H_v, d_k=d, d_v=d, dtype="bf16",
+                                  state_std=None)
+    pool0 = gdn_inputs.make_decode_state(706, P, H_v, d, d)
+    slots = [int(x) for x in rng.permutation(P)[:n]]
+    slots[3] = -1  # no row: starts from zeros, final state not kept
+    has = [int(x) for x in rng.integers(0, 2, n)]
+    has[0] = 1   # an empty sequence with a cached prefix keeps its row
+    has[10] = 0  # an empty sequence without one ends in zeros
+    pool = f32_dev(pool0)
+    dev = [to_dev(inp.q, "bf16"), to_dev(inp.k, "bf16"), to_dev(inp.v, "bf16"), f32_dev(inp.g), f32_dev(inp.beta)]
+    print(f"[bins] {n} sequences, T={inp.T}, H_v={H_v}, pool={P}", flush=True)
+    out = gdn.chunk_fwd_pooled(*dev, inp.cu_seqlens, pool, slots, has)
+    torch.cuda.synchronize()
+    init = np.zeros((n, H_v, d, d))
+    for i, (r, hv) in enumerate(zip(slots, has)):
+        if r >= 0 and hv:
+            init[i] = pool0[r]
+    heads = [0, 17, 31]
+    ref_o, ref_s = oracle_mod.forward(inp.q32(), inp.k32(), inp.v32(), inp.g, inp.beta, inp.cu_seqlens, H_q, H_v,
+                                      inp.scale, initial_state=init, heads=heads)
+    oh, ph = to_host(out), to_host(pool)
+    for h in heads:
+        assert rel_err(oh[:, h], ref_o[:, h]) < 1e-2, h
+        fin = np.stack([ph[r, h] if r >= 0 else ref_s[i, h] for i, r in enumerate(slots)])
+        assert rel_err(fin, ref_s[:, h]) < 1e-2, h
+    for i in range(0, n, 10):
+        r = slots[i]
+        if r >= 0:
+            assert np.array_equal(ph[r], init[i]), f"empty sequence {i}"
+    for r in sorted(set(range(P)) - {r for r in slots if r >= 0}):
+        assert np.array_equal(ph[r], pool0[r].astype(np.float64)), f"row {r} touched"

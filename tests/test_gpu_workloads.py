@@ -63,6 +63,17 @@ def test_varlen_8seq_sampled_heads(torch_cuda, oracle_mod):
     _check(oracle_mod, inp, out, fin, [0, 1, 13, 30, 31], 1e-2)
 
 
+def test_many_256req_sampled_heads(torch_cuda, oracle_mod):
+    """The serving prefill batch of 256 requests of 1..256 tokens: four launch
+    groups of 64 sequences, each group's state scan walking its sequences in
+    bins (several sequences one after another per workgroup)."""
+    inp = gdn_inputs.make_workload("many_256req")
+    assert len(inp.cu_seqlens) == 257
+    out, fin = chunk_fwd_device(inp)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(fin))
+    _check(oracle_mod, inp, out, fin, [0, 14, 31], 1e-2)
+
+
 def test_long_T65536_sampled_heads(torch_cuda, oracle_mod):
     inp = gdn_inputs.make_workload("long_T65536")
     out, fin = chunk_fwd_device(inp)
