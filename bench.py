@@ -585,13 +585,14 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
-def copy_calibration(torch, device, gib=1.0):
-    """A plain device copy of known size, run under rocprofv3 --pmc to calibrate HBM byte counters."""
+def copy_calibration(torch, gdn, device, gib=1.0):
+    """The library's streaming copy (gdn_stream_copy, kernel stream_copy_kernel) of
+    known size, run under rocprofv3 --pmc to calibrate the HBM byte counters."""
     n = int(gib * (1 << 30))
     src = torch.empty(n, dtype=torch.uint8, device=device).fill_(1)
     dst = torch.empty_like(src)
     for _ in range(3):
-        dst.copy_(src)
+        gdn.stream_copy(src, dst)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
 
@@ -603,8 +604,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_T4096",
                     choices=["prefill_T4096", "varlen_8seq", "long_T65536", "many_256req", "tiny_f32_T100"])
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
-                    help="restrict the run (used for counter collection)")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy", "many"], default="all",
+                    help="restrict the run (used for counter collection): prefill = the workload's plain and gated "
+                         "steps only; many = the 256-request batch only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -623,7 +625,10 @@ def main():
     gdn.load_library()
     hip = Hip()
     if args.only == "copy":
-        copy_calibration(torch, device)
+        copy_calibration(torch, gdn, device)
+        return
+    if args.only == "many":
+        print(json.dumps({"prefill_many": bench_prefill_many(args, torch, gdn, hip, device)}), flush=True)
         return
 
     res = {}
@@ -643,6 +648,7 @@ def main():
         print(f"[bench] prefill {args.workload} + gated read-out: {pre_g['ms_step']:.4f} ms/step, "
               + ", ".join(f"{s} {pre_g['stage_ms'][s] * 1e3:.1f} us" for s in pre_g["stages"]), file=sys.stderr,
               flush=True)
+    if args.only == "all":
         pre_s = bench_prefill_serving(args, torch, gdn, device)
         print(f"[bench] prefill {args.workload} from raw inputs + gated read-out: {pre_s['ms_per_step']:.4f} ms/step",
               file=sys.stderr, flush=True)

@@ -186,6 +186,24 @@ void pack_scan_bins(gdn::SeqTable& tab, int32_t H_v, int32_t d, bool bf16, int32
     tab.ct = 1 << best_ci;
 }
 
+// The same choice for device tables, whose lengths the host does not see: the
+// cost model on a launch group of equal sequences of the batch's mean length.
+// Returns ct; *bins_cap is the number of bins a group of that ct may use.
+int32_t dev_scan_shape(int32_t num_seqs, int32_t T, int32_t H_v, int32_t d, bool bf16, int32_t cus,
+                       int32_t* bins_cap) {
+    gdn::SeqTable t;
+    const int32_t ns = std::min<int32_t>(gdn::MAX_SEQS_PER_LAUNCH, num_seqs);
+    const int64_t len = num_seqs > 0 ? (int64_t)T / num_seqs : 0;
+    const int32_t c = (int32_t)std::min<int64_t>((len + GDN_CHUNK - 1) / GDN_CHUNK, 1 << 24);
+    t.num_seqs = ns;
+    for (int32_t i = 0; i <= ns; ++i) t.choff[i] = i * c;
+    for (int32_t i = 0; i < ns; ++i) t.order[i] = i;
+    pack_scan_bins(t, H_v, d, bf16, cus);
+    const int64_t per_bin = (int64_t)H_v * ((d / 16) / t.ct);
+    *bins_cap = (int32_t)std::max<int64_t>(1, cus / per_bin);
+    return t.ct;
+}
+
 hipError_t run_chunk(const gdn::ChunkParams& p, gdn_dtype dt, int d, hipStream_t s, hipEvent_t const* ev) {
     if (dt == GDN_BF16)
         return d == 128 ? gdn::launch_chunk_pipeline<gdn::bf16, 128>(p, s, ev)
@@ -581,8 +599,10 @@ int gdn_chunk_fwd_dev(const void* q, const void* k, const void* v, const float* 
 
     char* ws = static_cast<char*>(workspace);
     gdn::SeqTable* tabs = reinterpret_cast<gdn::SeqTable*>(ws + tab_off);
+    int32_t bins_cap = 1;
+    const int32_t ct = dev_scan_shape(num_seqs, T, H_v, d_k, dtype == GDN_BF16, gdn::cu_count(), &bins_cap);
     hipError_t e = gdn::launch_build_tables(cu_seqlens_dev, num_seqs, T, initial_state != nullptr,
-                                            final_state != nullptr, tabs, stream);
+                                            final_state != nullptr, bins_cap, tabs, stream);
     if (e != hipSuccess) return hip_fail(e);
     gdn::ChunkParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
@@ -603,8 +623,8 @@ int gdn_chunk_fwd_dev(const void* q, const void* k, const void* v, const float* 
     for (int32_t s0 = 0; s0 < num_seqs; s0 += gdn::MAX_SEQS_PER_LAUNCH) {
         const int32_t ns = std::min<int32_t>(gdn::MAX_SEQS_PER_LAUNCH, num_seqs - s0);
         p.tab.num_seqs = ns;
-        p.tab.n_bins = ns;  // one sequence a bin (build_tables)
-        p.tab.ct = 0;
+        p.tab.n_bins = std::min(ns, bins_cap);  // as build_tables computes it
+        p.tab.ct = ct;
         p.tab.n_chunks = (int32_t)std::min<int64_t>(nb, ((int64_t)T + GDN_CHUNK - 1) / GDN_CHUNK + ns);
         p.dtab = tabs + s0 / gdn::MAX_SEQS_PER_LAUNCH;
         e = run_chunk(p, dtype, d_k, stream, nullptr);

@@ -950,7 +950,24 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
     (void)padded;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int gi = (slot / NTW) * 8 + xcd;
-    const SeqTable& tab = DEV ? *p.dtab : p.tab;
+    // A device table is copied into LDS first: read from global memory, which
+    // the kernel also writes, its entries would be vector loads, and a vector
+    // load in a producer wave's cursor would count against the vmcnt that
+    // paces the stage loads (its wait would drain the stages in flight).
+    __shared__ __attribute__((aligned(16))) std::conditional_t<DEV, SeqTable, int> dtab_lds;
+    if constexpr (DEV) {
+        static_assert(sizeof(SeqTable) % 4 == 0, "table copied in words");
+        const int32_t* src = reinterpret_cast<const int32_t*>(p.dtab);
+        int32_t* dst = reinterpret_cast<int32_t*>(&dtab_lds);
+        for (int i = threadIdx.x; i < (int)(sizeof(SeqTable) / 4); i += blockDim.x) dst[i] = src[i];
+        __syncthreads();
+    }
+    const SeqTable& tab = [&]() -> const SeqTable& {
+        if constexpr (DEV)
+            return dtab_lds;
+        else
+            return p.tab;
+    }();
     if (gi >= tab.n_bins * p.H_v) return;
     const int tile = slot % NTW;  // column tiles CT tile .. CT tile + CT - 1
     const int h = gi % p.H_v, bin = gi / p.H_v;
@@ -1670,16 +1687,25 @@ __global__ __launch_bounds__(256) void chunk_gate_kernel(const ChunkParams p) {
 // up to 64 sequences: sequence ends clamped to [0, T] and made non-decreasing
 // (a running maximum, so every length is >= 0 and every index stays inside the
 // buffers whatever the input holds), chunk offsets by a prefix sum over the
-// lanes, state rows, and the longest-first order the state scan dispatches by.
+// lanes, state rows, and the state scan's bins: m = min(sequences, bins_cap)
+// bins filled with the sequences longest first in boustrophedon order (round
+// r of m sequences goes to bins 0 .. m-1, the next round back from m-1), so
+// that every bin's position in order[] has a closed form.  The next group's
+// sequence ends are loaded while a group is processed.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void build_tables_kernel(const int32_t* __restrict__ cu, int num_seqs, int T,
-                                                         int has_in, int has_out, SeqTable* tabs) {
+                                                         int has_in, int has_out, int bins_cap, SeqTable* tabs) {
     const int lane = threadIdx.x;
     int chunk_base = 0, prev_end = 0;
+    int raw = lane < min(MAX_SEQS_PER_LAUNCH, num_seqs) ? cu[lane + 1] : 0;
     for (int s0 = 0; s0 < num_seqs; s0 += MAX_SEQS_PER_LAUNCH) {
         const int ns = min(MAX_SEQS_PER_LAUNCH, num_seqs - s0);
         SeqTable* tb = tabs + s0 / MAX_SEQS_PER_LAUNCH;
-        int end = lane < ns ? min(max(cu[s0 + lane + 1], 0), T) : 0;
+        int end = lane < ns ? min(max(raw, 0), T) : 0;
+        {
+            const int s1 = s0 + MAX_SEQS_PER_LAUNCH;  // the next group's ends, in flight meanwhile
+            raw = s1 + lane < num_seqs ? cu[s1 + lane + 1] : 0;
+        }
         end = max(end, prev_end);
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {  // inclusive running maximum
@@ -1703,17 +1729,27 @@ __global__ __launch_bounds__(64) void build_tables_kernel(const int32_t* __restr
             const int ncj = __shfl(nc, j, 64);
             rank += (ncj > nc || (ncj == nc && j < lane)) ? 1 : 0;
         }
+        const int m = min(ns, max(bins_cap, 1));
+        const int rounds = ns / m, rem = ns % m;  // whole rounds, sequences of the last one
+        // first position of bin b in order[]: rounds + 1 sequences for the bins
+        // the last round reaches (the first rem, or the last rem when that round
+        // runs backwards), rounds for the others
+        auto bin_first = [&](int b) {
+            return b * rounds + ((rounds & 1) ? max(0, b - (m - rem)) : min(b, rem));
+        };
         if (lane < ns) {
             tb->cu[lane] = start;
             tb->choff[lane] = chunk_base + incl - nc;
             tb->s_in[lane] = has_in ? s0 + lane : -1;
             tb->s_out[lane] = has_out ? s0 + lane : -1;
-            tb->order[rank] = lane;
+            const int r = rank / m, q = rank % m;
+            const int b = (r & 1) ? m - 1 - q : q;
+            tb->order[bin_first(b) + r] = lane;
         }
-        if (lane < ns) tb->bin_first[lane] = lane;  // one sequence a bin
+        if (lane < m) tb->bin_first[lane] = bin_first(lane);
         if (lane == 0) {
-            tb->bin_first[ns] = ns;
-            tb->n_bins = ns;
+            tb->bin_first[m] = ns;
+            tb->n_bins = m;
             tb->ct = 0;
             tb->cu[ns] = last_end;
             tb->choff[ns] = chunk_base + total;
@@ -1727,11 +1763,11 @@ __global__ __launch_bounds__(64) void build_tables_kernel(const int32_t* __restr
     }
 }
 
-hipError_t launch_build_tables(const int32_t* cu_dev, int num_seqs, int T, int has_in, int has_out, SeqTable* tabs,
-                               hipStream_t stream) {
+hipError_t launch_build_tables(const int32_t* cu_dev, int num_seqs, int T, int has_in, int has_out, int bins_cap,
+                               SeqTable* tabs, hipStream_t stream) {
     if (num_seqs > 0)
         hipLaunchKernelGGL(build_tables_kernel, dim3(1), dim3(64), 0, stream, cu_dev, num_seqs, T, has_in, has_out,
-                           tabs);
+                           bins_cap, tabs);
     return hipGetLastError();
 }
 
@@ -1761,16 +1797,9 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
     const int work_ch = p.tab.n_chunks * p.H_v;
     const int grid_ch = pad8(work_ch);
     const int groups = p.tab.n_bins * p.H_v;  // (bin, value head) pairs of the state scan
-    // Column tiles per state-scan workgroup: as the bins were packed for
-    // (host tables); with device tables (one sequence a bin, lengths unknown
-    // here) one while the chip has a CU for every 16-column tile, two up to two
-    // tiles a CU, four beyond: a step's W and K stream then serves 2 or 4 tiles.
-    const int tiles = groups * (D / 16), cus = cu_count();
-    const int ct = sizeof(T) != 2         ? 1
-                   : p.tab.ct > 0         ? p.tab.ct
-                   : tiles <= cus         ? 1
-                   : tiles <= 2 * cus     ? 2
-                                          : 4;
+    // Column tiles per state-scan workgroup, as the bins were packed for (fp32:
+    // one); a step's W and K stream serves 2 or 4 tiles.
+    const int ct = sizeof(T) != 2 ? 1 : p.tab.ct == 4 ? 4 : p.tab.ct == 2 ? 2 : 1;
     // With events, each kernel is launched with hipExtLaunchKernelGGL, whose
     // start/stop events are stamped by the kernel's own dispatch (kernel time
     // only, no launch gaps).

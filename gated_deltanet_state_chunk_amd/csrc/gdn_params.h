@@ -139,8 +139,9 @@ hipError_t launch_recurrent_step(const DecodeParams& p, hipStream_t stream);
 // Sequence tables from a device cu_seqlens (gdn_chunk.hip): one SeqTable per
 // group of up to MAX_SEQS_PER_LAUNCH sequences, boundaries clamped to [0, T]
 // and made non-decreasing so that no kernel can index out of bounds.
-hipError_t launch_build_tables(const int32_t* cu_dev, int num_seqs, int T, int has_in, int has_out, SeqTable* tabs,
-                               hipStream_t stream);
+// bins_cap: state-scan bins a launch group may use (at most one sequence a bin)
+hipError_t launch_build_tables(const int32_t* cu_dev, int num_seqs, int T, int has_in, int has_out, int bins_cap,
+                               SeqTable* tabs, hipStream_t stream);
 
 template <typename T, int K>
 hipError_t launch_conv_prefill(const ConvParams& p, hipStream_t stream);
