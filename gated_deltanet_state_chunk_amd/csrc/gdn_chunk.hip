@@ -268,9 +268,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
         }
     }
     // Query fragments of this wave's 16 positions for P (bf16): rows 16 w + r16,
-    // contraction indices 32 ks + 8 grp .. + 7 (zero past the valid length;
-    // L2-normalised with the front end, the row spread over the four lanes of
-    // lane % 16).
+    // contraction indices 32 ks + 8 grp .. + 7 (zero past the valid length).
+    // Loaded here, used after the solve, so the load latency overlaps K K^T
+    // and the solve.
     Frag<T> qw[D / 32];
     if constexpr (sizeof(T) == 2) {
         if (p.Pf) {
@@ -278,27 +278,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
             const T* qb = reinterpret_cast<const T*>(p.q) + ((size_t)(cp.t0 + row) * p.H_q + h / p.G) * D + 8 * grp;
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) load8_masked(qw[ks], qb + 32 * ks, row < ell);
-            if (p.fa) {
-                float ss = 0.f;
-#pragma unroll
-                for (int ks = 0; ks < D / 32; ++ks)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) ss += frag_get(qw[ks], j) * frag_get(qw[ks], j);
-                const float r = 1.f / sqrtf(sum_over_rows(ss) + 1e-6f);
-#pragma unroll
-                for (int ks = 0; ks < D / 32; ++ks)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) frag_set(qw[ks], j, frag_get(qw[ks], j) * r);
-                // the first value head of each key head keeps the normalised rows (Qc) for the
-                // state scan's output waves, piece i of row r at i ^ (r mod pieces)
-                if (h % p.G == 0) {
-                    constexpr int PPR = D / 8;
-                    T* Qcb = reinterpret_cast<T*>(p.Qc) + (((size_t)cp.ci * p.H_q + h / p.G) * CHUNK + row) * D;
-#pragma unroll
-                    for (int ks = 0; ks < D / 32; ++ks)
-                        *reinterpret_cast<Frag<T>*>(Qcb + 8 * ((4 * ks + grp) ^ (row % PPR))) = qw[ks];
-                }
-            }
         }
     }
     // With the front end, each K row is L2-normalised on the way (rows past the
@@ -339,47 +318,22 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
 
     // K K^T: wave w forms row block w against column blocks J <= w (fragments from LDS);
     // L_ij = beta_i exp(gc_i - gc_j) (k_i . k_j) for i > j, zero elsewhere.
-    // With P requested (bf16), the same K fragments also give the P^T tiles
-    // (J, w) = K_J Q_w^T of this wave's query positions i = 16 w + r16:
-    // P^T[j][i] = (k_j . q_i) exp(gc_i - gc_j) for j <= i < ell (Lower keeps the diagonal).
-    f32x4 pt[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
         if (J > w) break;
-        f32x4 acc = zero4(), pacc = zero4();
+        f32x4 acc = zero4();
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
             Frag<T> a, b;
             load8(a, &s.K[16 * w + r16][32 * ks + 8 * grp]);
             load8(b, &s.K[16 * J + r16][32 * ks + 8 * grp]);
             acc = mma(a, b, acc);
-            if constexpr (sizeof(T) == 2) {
-                if (p.Pf) pacc = mma(b, qw[ks], pacc);
-            }
         }
         float* Lb = Ls + blk(w, J);
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             const int i = 16 * w + 4 * grp + i4, j = 16 * J + r16;
             Lb[(4 * grp + i4) * BS + r16] = (i > j) ? s.beta[i] * __expf(s.gc[i] - s.gc[j]) * acc[i4] : 0.f;
-        }
-        if constexpr (sizeof(T) == 2) {
-            const int i = 16 * w + r16;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = 16 * J + 4 * grp + e;
-                pt[J][e] = (j <= i && i < ell) ? pacc[e] * __expf(s.gc[i] - s.gc[j]) : 0.f;
-            }
-        }
-    }
-    // P to the workspace as the B operands of X^T P^T: query tile w, K-steps
-    // s = 0 (and 1 for w >= 2), two stacked P^T tiles per fragment (perm32).
-    if constexpr (sizeof(T) == 2) {
-        if (p.Pf) {
-            T* Pb = reinterpret_cast<T*>(p.Pf) + ch * P_FRAGS * 512;
-            const int f0 = w < 2 ? w : 2 * w - 2;
-            *reinterpret_cast<Frag<T>*>(Pb + (f0 * 64 + lane) * 8) = pack_perm32<T>(pt[0], pt[1], 1.f);
-            if (w >= 2) *reinterpret_cast<Frag<T>*>(Pb + ((f0 + 1) * 64 + lane) * 8) = pack_perm32<T>(pt[2], pt[3], 1.f);
         }
     }
     lds_sync();
@@ -435,6 +389,60 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
         tile_to_lds<BS>(As + blk(I, J), t, -1.f, r16, grp);
     }
     lds_sync();
+
+    // P (bf16): the P^T tiles (J, w) = K_J Q_w^T of this wave's query positions
+    // i = 16 w + r16, P^T[j][i] = (k_j . q_i) exp(gc_i - gc_j) for j <= i < ell
+    // (Lower keeps the diagonal), K_J from the staged keys.  With the front end
+    // the query rows are L2-normalised first (the row spread over the four lanes
+    // of lane % 16), and the first value head of each key head keeps them (Qc)
+    // for the state scan's output waves, piece i of row r at i ^ (r mod pieces).
+    if constexpr (sizeof(T) == 2) {
+        if (p.Pf) {
+            const int row = 16 * w + r16;
+            if (p.fa) {
+                float ss = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) ss += frag_get(qw[ks], j) * frag_get(qw[ks], j);
+                const float r = 1.f / sqrtf(sum_over_rows(ss) + 1e-6f);
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) frag_set(qw[ks], j, frag_get(qw[ks], j) * r);
+                if (h % p.G == 0) {
+                    constexpr int PPR = D / 8;
+                    T* Qcb = reinterpret_cast<T*>(p.Qc) + (((size_t)cp.ci * p.H_q + h / p.G) * CHUNK + row) * D;
+#pragma unroll
+                    for (int ks = 0; ks < D / 32; ++ks)
+                        *reinterpret_cast<Frag<T>*>(Qcb + 8 * ((4 * ks + grp) ^ (row % PPR))) = qw[ks];
+                }
+            }
+            f32x4 pt[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                if (J > w) break;
+                f32x4 pacc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks) {
+                    Frag<T> b;
+                    load8(b, &s.K[16 * J + r16][32 * ks + 8 * grp]);
+                    pacc = mma(b, qw[ks], pacc);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 16 * J + 4 * grp + e;
+                    pt[J][e] = (j <= row && row < ell) ? pacc[e] * __expf(s.gc[row] - s.gc[j]) : 0.f;
+                }
+            }
+            // to the workspace as the B operands of X^T P^T: query tile w, K-steps
+            // s = 0 (and 1 for w >= 2), two stacked P^T tiles per fragment (perm32)
+            T* Pb = reinterpret_cast<T*>(p.Pf) + ch * P_FRAGS * 512;
+            const int f0 = w < 2 ? w : 2 * w - 2;
+            *reinterpret_cast<Frag<T>*>(Pb + (f0 * 64 + lane) * 8) = pack_perm32<T>(pt[0], pt[1], 1.f);
+            if (w >= 2) *reinterpret_cast<Frag<T>*>(Pb + ((f0 + 1) * 64 + lane) * 8) = pack_perm32<T>(pt[2], pt[3], 1.f);
+        }
+    }
 
     // A to the workspace on request, zero outside the valid lower triangle.
     if (p.keep_A) {
