@@ -17,7 +17,8 @@
 //                           of its window's loads issued together
 //   conv_final_state_kernel each sequence's last K-1 inputs, launched after it
 //                           (stream order makes final_state == initial_state safe)
-//   conv_step_kernel        one decode token per sequence, history updated in place
+//   conv_step_kernel        one decode token per sequence, four sequences a thread
+//                           (the taps read once for them), history updated in place
 #include "gdn_device.h"
 #include "gdn_params.h"
 
@@ -196,35 +197,58 @@ __global__ __launch_bounds__(256) void conv_final_state_kernel(const ConvParams 
         st16(reinterpret_cast<T*>(p.s_out) + ((size_t)so * (K - 1) + j) * p.C + c, last[j]);
 }
 
+// Decode step: each thread serves STEP_SEQS sequences for its 16 bytes of
+// channels, so its taps are read once for all of them (per workgroup they are
+// 32 KiB, as much as the step's own traffic for one sequence each) and the
+// loads of all its sequences are in flight together.
+constexpr int STEP_SEQS = 4;
+
 template <typename T, int K>
-__global__ __launch_bounds__(256) void conv_step_kernel(const ConvParams p) {
+__global__ __launch_bounds__(256) void conv_step_kernel(const ConvParams p, int N) {
     constexpr int V = Vec16<T>::N;
     const int cg = blockIdx.y * 256 + threadIdx.x;
     if (cg * V >= p.C) return;
-    const int c = cg * V, n = blockIdx.x;
-    const int slot = p.slot ? p.slot[n] : n;
-    if (slot < 0 || slot >= p.pool) {  // padding: zero output, history untouched
-        st16(reinterpret_cast<T*>(p.y) + (size_t)n * p.C + c, zero16<T>());
-        return;
-    }
-    T* st = reinterpret_cast<T*>(p.s_out) + (size_t)slot * (K - 1) * p.C + c;
-    Vec16<T> win[K];
+    const int c = cg * V, n0 = blockIdx.x * STEP_SEQS;
+    // window per sequence: its K-1 history rows, then its input; padding
+    // (slot outside the pool) reads and writes no history, outputs zeros
+    Vec16<T> win[STEP_SEQS][K];
+    T* st[STEP_SEQS];
+    bool live[STEP_SEQS];
 #pragma unroll
-    for (int k = 0; k < K - 1; ++k) win[k] = ld16(st + (size_t)k * p.C);
-    win[K - 1] = ld16(reinterpret_cast<const T*>(p.x) + (size_t)n * p.C + c);
+    for (int j = 0; j < STEP_SEQS; ++j) {
+        const int n = n0 + j;
+        const int slot = n < N ? (p.slot ? p.slot[n] : n) : -1;
+        live[j] = slot >= 0 && slot < p.pool;
+        st[j] = reinterpret_cast<T*>(p.s_out) + (size_t)max(slot, 0) * (K - 1) * p.C + c;
+        if (live[j]) {
+#pragma unroll
+            for (int k = 0; k < K - 1; ++k) win[j][k] = ld16(st[j] + (size_t)k * p.C);
+            win[j][K - 1] = ld16(reinterpret_cast<const T*>(p.x) + (size_t)n * p.C + c);
+        }
+    }
     float wk[K][V], bc[V];
     load_taps<K, V>(p, c, wk, bc);
-    float y[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-        float a = bc[i];
+    for (int j = 0; j < STEP_SEQS; ++j) {
+        const int n = n0 + j;
+        if (n >= N) break;
+        T* yrow = reinterpret_cast<T*>(p.y) + (size_t)n * p.C + c;
+        if (!live[j]) {
+            st16(yrow, zero16<T>());
+            continue;
+        }
+        float y[V];
 #pragma unroll
-        for (int k = 0; k < K; ++k) a += wk[k][i] * get(win[k], i);
-        y[i] = silu(a);
+        for (int i = 0; i < V; ++i) {
+            float a = bc[i];
+#pragma unroll
+            for (int k = 0; k < K; ++k) a += wk[k][i] * get(win[j][k], i);
+            y[i] = silu(a);
+        }
+        st16(yrow, from_floats<T>(y));
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) st16(st[j] + (size_t)k * p.C, win[j][k + 1]);
     }
-    st16(reinterpret_cast<T*>(p.y) + (size_t)n * p.C + c, from_floats<T>(y));
-#pragma unroll
-    for (int k = 0; k < K - 1; ++k) st16(st + (size_t)k * p.C, win[k + 1]);
 }
 
 }  // namespace
@@ -249,7 +273,9 @@ template <typename T, int K>
 hipError_t launch_conv_step(const ConvParams& p, int N, hipStream_t stream) {
     constexpr int V = Vec16<T>::N;
     const int cblocks = (p.C / V + 255) / 256;
-    if (N > 0) hipLaunchKernelGGL((conv_step_kernel<T, K>), dim3(N, cblocks), dim3(256), 0, stream, p);
+    if (N > 0)
+        hipLaunchKernelGGL((conv_step_kernel<T, K>), dim3((N + STEP_SEQS - 1) / STEP_SEQS, cblocks), dim3(256), 0, stream,
+                           p, N);
     return hipGetLastError();
 }
 
