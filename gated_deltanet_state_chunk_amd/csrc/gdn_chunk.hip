@@ -466,7 +466,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
     // column tile mt.  Blocks above the diagonal are zero; rows past the valid
     // length are unit rows e_i, which meet zero rows of B Gamma K and B V, so W and
     // U vanish there without masking.
-    Frag<T> Af[4][2];
+    using PT = ProdT<T>;  // element type of the W and U products' operands
+    Frag<PT> Af[4][2];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -499,10 +500,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
     // so column tile nt only needs contraction steps ks with 32 ks <= 16 nt + 15.
     T* Wb = reinterpret_cast<T*>(p.W) + ch * CHUNK * D;
     // A fragment of 8 consecutive positions (32 ks + 8 grp ..) of one column of a
-    // staged [pos][col] matrix, each value scaled by its position's factor.  For
+    // staged [pos][col] matrix, each value scaled by its position's factor and
+    // rounded to the product type (fp16 for bf16 inputs: rounding the scaled
+    // values B V to bf16 was the largest single error of the output).  For
     // bf16 the columns come from LDS with transposed reads (two per fragment);
     // for fp32 element by element.
-    auto col_frag = [&](Frag<T>& f, const T* M, const float* sc, int ks, int c) {
+    auto col_frag = [&](Frag<PT>& f, const T* M, const float* sc, int ks, int c) {
         const int r0 = 32 * ks + 8 * grp;
         if constexpr (sizeof(T) == 2) {
             const bf16x4 lo = lds_col4<PL::KP>(M, r0, c & ~15, lane), hi = lds_col4<PL::KP>(M, r0 + 4, c & ~15, lane);
@@ -516,14 +519,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
             for (int j = 0; j < 8; ++j) frag_set(f, j, sc[r0 + j] * to_f32<T>(M[(r0 + j) * PL::KP + c]));
         }
     };
-    auto w_kfrag = [&](Frag<T>(&kf)[2], int mt) {  // (B Gamma K)^T rows of d_k tile mt, contraction pos
+    auto w_kfrag = [&](Frag<PT>(&kf)[2], int mt) {  // (B Gamma K)^T rows of d_k tile mt, contraction pos
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) col_frag(kf[ks], &s.K[0][0], s.sk, ks, 16 * mt + r16);
     };
     // lane: column pos = 16 nt + r16, rows d_k = 16 mt + 4 grp + i: in fragment
     // order this is fragment (pos tile nt, K-step mt / 2), same lane, slots 4 (mt % 2) + i
     if constexpr (TPW == 2) {  // this wave's two d_k tiles fill whole fragments: 16-byte stores
-        Frag<T> k0[2], k1[2];
+        Frag<PT> k0[2], k1[2];
         w_kfrag(k0, 2 * w);
         w_kfrag(k1, 2 * w + 1);
 #pragma unroll
@@ -539,7 +542,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
             const int mt = w * TPW + tt;
-            Frag<T> kf[2];
+            Frag<PT> kf[2];
             w_kfrag(kf, mt);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
@@ -550,14 +553,15 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
             }
         }
     }
+
     lds_sync();  // V staged
-    // U tiles: rows pos, columns d_v (this wave's tiles).
-    T* Ub = reinterpret_cast<T*>(p.Ut) + ch * D * CHUNK;
+    // U tiles: rows pos, columns d_v (this wave's tiles), stored in the product type.
+    PT* Ub = reinterpret_cast<PT*>(p.Ut) + ch * D * CHUNK;
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
         const int nt = w * TPW + tt;
         const int dv = 16 * nt + r16;
-        Frag<T> vf[2];
+        Frag<PT> vf[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) col_frag(vf[ks], &s.u.V[0][0], s.svb, ks, dv);
         // lane: column d_v = 16 nt + r16, rows pos = 16 mt + 4 grp + i (accumulator
@@ -1289,14 +1293,14 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
     }
     // Operand fragments of one chunk, read from its LDS stage.
     Frag<T> wf[KS], kfg[TPW][2];
-    Raw4<T> uf[CT];
+    Raw4<ProdT<T>> uf[CT];  // U is stored in the product type (fp16 for bf16 inputs)
     float gl = 0.f;
     float4 fx;  // kf of this wave's X rows (positions 16 w + 4 grp + i)
     auto read_stage = [&](int c) {  // chunk c of the bin, at cursor rd
         const char* st = smem + (c % NST) * SS::BYTES;
         const Frag<T>* Wst = reinterpret_cast<const Frag<T>*>(st);
         const char* Kst = st + SS::W_BYTES;
-        const Raw4<T>* Ust = reinterpret_cast<const Raw4<T>*>(st + SS::W_BYTES + SS::K_BYTES);
+        const Raw4<ProdT<T>>* Ust = reinterpret_cast<const Raw4<ProdT<T>>*>(st + SS::W_BYTES + SS::K_BYTES);
         const float* Gst = reinterpret_cast<const float*>(st + SS::W_BYTES + SS::K_BYTES + SS::U_BYTES);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) wf[ks] = Wst[(w * KS + ks) * 64 + lane];
@@ -1305,7 +1309,7 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) kfg[tt][ks] = k_col_frag<T, D>(Kst, w * TPW + tt, ks, lane);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) uf[ct] = Ust[ct * (SS::U1_BYTES / (int)sizeof(Raw4<T>)) + ((w >> 1) * 64 + lane) * 2 + (w & 1)];
+        for (int ct = 0; ct < CT; ++ct) uf[ct] = Ust[ct * (SS::U1_BYTES / (int)sizeof(Raw4<ProdT<T>>)) + ((w >> 1) * 64 + lane) * 2 + (w & 1)];
         gl = Gst[rd.ell() - 1];
         fx = *reinterpret_cast<const float4*>(Gst + CHUNK + 16 * w + 4 * grp);
         rd.next();

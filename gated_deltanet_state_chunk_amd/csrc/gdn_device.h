@@ -21,6 +21,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 namespace gdn {
@@ -29,6 +31,9 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int CHUNK = 64;
 
@@ -40,12 +45,25 @@ struct Frag<bf16> {
     bf16x8 v;
 };
 template <>
+struct Frag<f16> {
+    f16x8 v;
+};
+template <>
 struct Frag<float> {
     float v[8];
 };
 
+// Element type of chunk_prep's W and U products and of the stored U: fp16 for
+// bf16 inputs (the same two bytes as bf16 and the same MFMA rate, with three
+// more mantissa bits for values well inside its range), fp32 for fp32 inputs.
+template <typename T>
+using ProdT = std::conditional_t<sizeof(T) == 2, f16, float>;
+
 __device__ __forceinline__ f32x4 mma(const Frag<bf16>& a, const Frag<bf16>& b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const Frag<f16>& a, const Frag<f16>& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mma(const Frag<float>& a, const Frag<float>& b, f32x4 c) {
 #pragma unroll
@@ -62,6 +80,8 @@ template <>
 __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ float to_f32<bf16>(bf16 x) { return (float)x; }
+template <>
+__device__ __forceinline__ float to_f32<f16>(f16 x) { return (float)x; }
 
 template <typename T>
 __device__ __forceinline__ T from_f32(float x);
@@ -69,6 +89,8 @@ template <>
 __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // round to nearest even
+template <>
+__device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }  // round to nearest even
 
 // ---- fragment loads ------------------------------------------------------
 // 8 consecutive elements at p (16-byte aligned for bf16, 32-byte for fp32).
@@ -131,6 +153,10 @@ __device__ __forceinline__ void store8(bf16* p, const f32x4& lo, const f32x4& hi
     const bf16x4 a = __builtin_convertvector(lo, bf16x4), b = __builtin_convertvector(hi, bf16x4);
     *reinterpret_cast<bf16x8*>(p) = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
+__device__ __forceinline__ void store8(f16* p, const f32x4& lo, const f32x4& hi) {
+    const f16x4 a = __builtin_convertvector(lo, f16x4), b = __builtin_convertvector(hi, f16x4);
+    *reinterpret_cast<f16x8*>(p) = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
 __device__ __forceinline__ void store8(float* p, const f32x4& lo, const f32x4& hi) {
     *reinterpret_cast<float4*>(p) = make_float4(lo[0], lo[1], lo[2], lo[3]);
     *reinterpret_cast<float4*>(p + 4) = make_float4(hi[0], hi[1], hi[2], hi[3]);
@@ -152,12 +178,19 @@ struct Raw4<bf16> {
     bf16x4 v;
 };
 template <>
+struct Raw4<f16> {
+    f16x4 v;
+};
+template <>
 struct Raw4<float> {
     float4 v;
 };
 __device__ __forceinline__ void load_raw4(Raw4<bf16>& r, const bf16* p) { r.v = *reinterpret_cast<const bf16x4*>(p); }
 __device__ __forceinline__ void load_raw4(Raw4<float>& r, const float* p) { r.v = *reinterpret_cast<const float4*>(p); }
 __device__ __forceinline__ f32x4 raw4_to_f32(const Raw4<bf16>& r) {
+    return f32x4{(float)r.v[0], (float)r.v[1], (float)r.v[2], (float)r.v[3]};
+}
+__device__ __forceinline__ f32x4 raw4_to_f32(const Raw4<f16>& r) {
     return f32x4{(float)r.v[0], (float)r.v[1], (float)r.v[2], (float)r.v[3]};
 }
 __device__ __forceinline__ f32x4 raw4_to_f32(const Raw4<float>& r) { return f32x4{r.v.x, r.v.y, r.v.z, r.v.w}; }

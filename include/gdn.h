@@ -89,7 +89,11 @@ typedef struct ihipStream_t *hipStream_t;
  *   A   dtype [n_chunks][H_v][64][64]        (I + StrictLower(B Gamma K K^T Gamma^-1))^-1,
  *                                            written only under GDN_FWD_KEEP_A (gdn_chunk_fwd_ex)
  *   W   dtype [n_chunks][H_v][64 * d_k]      A B Gamma K, fragment order
- *   U   dtype [n_chunks][H_v][64 * d_v]      A B V, fragment order
+ *   U   utype [n_chunks][H_v][64 * d_v]      A B V, fragment order; utype is IEEE binary16
+ *                                            for bf16 inputs (the same two bytes, three more
+ *                                            mantissa bits; W and U are formed from binary16
+ *                                            operands, so |beta v|, the entries of A and of U
+ *                                            must stay below 65504), fp32 for fp32 inputs
  *   kf  fp32  [n_chunks][H_v][64]            gamma_l / gamma per position (the decay of a
  *                                            key to the chunk end), zero past the valid
  *                                            length: the state update is

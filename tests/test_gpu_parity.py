@@ -203,18 +203,21 @@ def test_chunk_intermediates_match_chunk_form(torch_cuda, dtype, d, tol):
     nc = lay["n_chunks"]
     assert nc == 2 + 1 + 1
 
-    def region(off, shape, is_f32=False):
+    def region(off, shape, is_f32=False, half=False):
         import torch
 
         nbytes = int(np.prod(shape)) * (4 if (is_f32 or dtype == "f32") else 2)
         raw = ws[off:off + nbytes]
-        t = raw.view(torch.float32) if (is_f32 or dtype == "f32") else raw.view(torch.bfloat16)
+        if is_f32 or dtype == "f32":
+            t = raw.view(torch.float32)
+        else:  # bf16 inputs: U is stored as fp16, the rest of the 2-byte regions as bf16
+            t = raw.view(torch.float16) if half else raw.view(torch.bfloat16)
         return t.float().cpu().numpy().astype(np.float64).reshape(shape)
 
     gc = region(lay["off_gc"], (nc, H_v, 64), is_f32=True)
     A = region(lay["off_A"], (nc, H_v, 64, 64))
     W = frag_w_to_logical(region(lay["off_W"], (nc, H_v, 64 * d)), d)
-    U = frag_u_to_logical(region(lay["off_U"], (nc, H_v, 64 * d)), d)
+    U = frag_u_to_logical(region(lay["off_U"], (nc, H_v, 64 * d), half=True), d)
     kf = region(lay["off_kf"], (nc, H_v, 64), is_f32=True)
     # Kc: each row's 16-byte pieces stored permuted (piece i at i ^ p(r), as include/gdn.h states)
     es = 4 if dtype == "f32" else 2
