@@ -10,7 +10,10 @@ each step) is measured in the same run and reported under "decode", and the
 same step taken from the raw inputs (q/k L2 norm, gate and beta computed inside
 the step) under "decode_fused".
 
-Prints ONE JSON line.  Timing: W untimed warm-up steps, then K timed steps of
+Prints ONE JSON line.  Timing: W untimed warm-up steps (default 300: a prefill
+step on MI355X takes about 300 back-to-back steps, ~30 ms, to settle from
+~100 to ~86 us at T = 4096; a streaming copy beforehand does not replace
+them), then K timed steps of
 the product entry point between two device synchronisations (value,
 ms_per_step), then the same K steps again through gdn_chunk_fwd_ex, whose
 start/stop HIP events are stamped by each kernel's own dispatch (per-kernel
@@ -608,8 +611,8 @@ def copy_calibration(torch, gdn, device, gib=1.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="prefill_T4096",
                     choices=["prefill_T4096", "varlen_8seq", "long_T65536", "many_256req", "tiny_f32_T100"])
     ap.add_argument("--only", choices=["all", "prefill", "decode", "copy", "many"], default="all",
