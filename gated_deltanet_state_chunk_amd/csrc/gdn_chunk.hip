@@ -595,14 +595,16 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
 //    accumulators, split by rows over the waves.  Per chunk:
 //      X = U - W S                 wave w: positions 16w..16w+15, contraction over d_k
 //      S = gamma_l S + K^T (kf X)  wave w: its rows of S, contraction over positions
-//    (kf = gamma_l / gamma per position, with the front end also 1 / |k|: the
-//    decayed keys of the chunk form, applied to X rather than to K).  The two
+//    (kf = gamma_l / gamma per position: the decayed keys of the chunk form,
+//    applied to X rather than to K; with the front end the rows of K are the
+//    L2-normalised keys chunk_prep keeps in Kc).  The two
 //    products exchange bf16 copies of -S, X and kf X through LDS in MFMA
 //    operand order (one 16-byte access per lane and fragment), two barriers a
 //    chunk (B1 before X, B2 before the state update).  A chunk's W, K, U and
 //    gate fragments are copied from its LDS stage into registers during the
-//    second half of the previous step (K's column fragments with transposed
-//    reads).  The compute waves issue no global
+//    previous step (K's column fragments with transposed reads): with three
+//    stages in its first half, where the compute waves would otherwise wait
+//    for the output waves at B2, with two in its second.  The compute waves issue no global
 //    memory instruction inside the loop: a vector-memory instruction stalls
 //    its wave whenever the CU's memory pipeline is backed up, and on this
 //    serial path every stall delays the next barrier for all waves.
@@ -613,7 +615,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
 //    global->LDS loads.  A stage is free
 //    once its chunk is in registers (B1 of that chunk's step); chunk c + NST
 //    goes out in two halves, at B1(c) and B2(c); vmcnt waits make chunk c + 1
-//    land before B2(c) and keep at most 63 loads in flight per wave.
+//    land before B1(c) (three stages) or B2(c) (two) and keep at most 63
+//    loads in flight per wave.
 //
 //    Store wave.  Copies h_c (the sign-flipped -S of LS, between B1(c) and
 //    B2(c)) and X_c (LX, between B2(c) and B1(c + 1)) to HBM.
@@ -1208,18 +1211,32 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
         // the barrier after which the compute waves read it.  The asm's memory
         // clobber keeps the compiler from moving loads across a barrier.
         asm volatile("s_barrier" ::: "memory");  // B0: chunks 0 and 1 in LDS
+        // A chunk's loads go out in two halves, one in each phase of a step.
+        // With three stages the compute waves copy chunk c + 1 into registers
+        // between B1(c) and B2(c), so it has landed before B1(c): only chunk
+        // c + 2's loads may then be in flight (LA_).  With two stages it is read
+        // after B2(c) and lands before that barrier (WB_).
+        constexpr int LA_0 = state_part_loads<SS>(0, 0) + state_part_loads<SS>(0, 1);
+        constexpr int LA_1 = state_part_loads<SS>(1, 0) + state_part_loads<SS>(1, 1);
         for (int c = 0; c < nch; ++c) {
+            if constexpr (NST == 3) {
+                if (c + 2 < nch) {
+                    if (pw == 0) wait_vmcnt<LA_0>(); else wait_vmcnt<LA_1>();
+                } else {
+                    wait_vmcnt<0>();
+                }
+            }
             asm volatile("s_barrier" ::: "memory");  // B1(c): chunk c is in registers, its stage free
             const int cn = c + NST;
             char* stn = smem + (cn % NST) * SS::BYTES;
             const size_t chn = vch(cp), kchn = kch(cp);  // chunk cn
-            // A chunk's loads go out in two halves, one in each phase of a step;
-            // chunk c + 1 is read after B2(c).
             if (cn < nch) {
                 if (pw == 0) wait_vmcnt<R0_0>(); else wait_vmcnt<R0_1>();
                 state_issue<T, D, CT, FO>(stn, p, chn, kchn, tile, lane, pw, 0);
-                if (pw == 0) wait_vmcnt<WB_0>(); else wait_vmcnt<WB_1>();
-            } else {
+                if constexpr (NST != 3) {
+                    if (pw == 0) wait_vmcnt<WB_0>(); else wait_vmcnt<WB_1>();
+                }
+            } else if constexpr (NST != 3) {
                 wait_vmcnt<0>();
             }
             asm volatile("s_barrier" ::: "memory");  // B2(c)
@@ -1358,8 +1375,16 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
                 kc[tt][0] = kfg[tt][0];
                 kc[tt][1] = kfg[tt][1];
             }
-            bar();  // B2(c): all of X in LX and kf X in LY; stage c + 1 ready
-            if (c + 1 < nch) read_stage(c + 1);
+            // Three stages: chunk c + 1 has landed before B1(c), and its
+            // fragments are read here, while the output waves still work on
+            // h_c; two stages: after B2(c).
+            if constexpr (NST == 3) {
+                if (c + 1 < nch) read_stage(c + 1);
+            }
+            bar();  // B2(c): all of X in LX and kf X in LY
+            if constexpr (NST != 3) {
+                if (c + 1 < nch) read_stage(c + 1);
+            }
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
                 const Frag<T> xb0 = xf(LY, ct, lane), xb1 = xf(LY, CT + ct, lane);
