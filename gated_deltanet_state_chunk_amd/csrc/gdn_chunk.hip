@@ -1728,10 +1728,15 @@ __global__ __launch_bounds__(256) void chunk_gate_kernel(const ChunkParams p) {
 // bins filled with the sequences longest first in boustrophedon order (round
 // r of m sequences goes to bins 0 .. m-1, the next round back from m-1), so
 // that every bin's position in order[] has a closed form.  The next group's
-// sequence ends are loaded while a group is processed.
+// sequence ends are loaded while a group is processed.  The ranks compare each
+// lane's chunk count with all others, read back from LDS four at a time (all
+// lanes the same address: a broadcast), rather than by one cross-lane shuffle
+// per sequence.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void build_tables_kernel(const int32_t* __restrict__ cu, int num_seqs, int T,
                                                          int has_in, int has_out, int bins_cap, SeqTable* tabs) {
+    static_assert(MAX_SEQS_PER_LAUNCH == 64, "one lane a sequence");
+    __shared__ __attribute__((aligned(16))) int nc_lds[64];
     const int lane = threadIdx.x;
     int chunk_base = 0, prev_end = 0;
     int raw = lane < min(MAX_SEQS_PER_LAUNCH, num_seqs) ? cu[lane + 1] : 0;
@@ -1761,11 +1766,20 @@ __global__ __launch_bounds__(64) void build_tables_kernel(const int32_t* __restr
         }
         const int total = __shfl(incl, ns - 1, 64);
         const int last_end = __shfl(end, ns - 1, 64);
+        nc_lds[lane] = nc;  // zero past ns
+        __syncthreads();
         int rank = 0;  // stable, longest first
-        for (int j = 0; j < ns; ++j) {
-            const int ncj = __shfl(nc, j, 64);
-            rank += (ncj > nc || (ncj == nc && j < lane)) ? 1 : 0;
+#pragma unroll
+        for (int j4 = 0; j4 < 16; ++j4) {
+            const int4 v = reinterpret_cast<const int4*>(nc_lds)[j4];
+            const int vj[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * j4 + e;
+                rank += (j < ns && (vj[e] > nc || (vj[e] == nc && j < lane))) ? 1 : 0;
+            }
         }
+        __syncthreads();  // all reads done before the next group overwrites nc_lds
         const int m = min(ns, max(bins_cap, 1));
         const int rounds = ns / m, rem = ns % m;  // whole rounds, sequences of the last one
         // first position of bin b in order[]: rounds + 1 sequences for the bins
