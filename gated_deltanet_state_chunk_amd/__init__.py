@@ -30,6 +30,7 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 FWD_KEEP_A = 1  # gdn_chunk_fwd_ex flag: also write A to the workspace
 FWD_KEEP_HX = 2  # gdn_chunk_fwd_ex flag: also write Ht and Xt (bf16 forms the output on chip)
+FWD_SCAN_CT = {1: 4, 2: 8, 4: 16}  # gdn_chunk_fwd_ex flags: the state scan's column tiles a workgroup (bf16)
 SCRATCH_BYTES = 256 << 20  # GDN_SCRATCH_BYTES: the static workspace of gdn_chunk_fwd_scratch
 
 _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace", -4: "hip"}
@@ -273,8 +274,8 @@ def workspace_size(T: int, cu_seqlens, H_q: int, H_v: int, d_k: int, d_v: int, d
 
 def chunk_fwd(q, k, v, g, beta, cu_seqlens: Sequence[int], initial_state=None, scale: Optional[float] = None,
               out=None, final_state=None, output_final_state: bool = True, workspace=None, stream=None,
-              keep_A: bool = False, gate=None, keep_hx: bool = False):
-    """Chunk-wise GDN prefill over a packed batch (gdn_chunk_fwd; gdn_chunk_fwd_ex with keep_A).
+              keep_A: bool = False, gate=None, keep_hx: bool = False, scan_ct: Optional[int] = None):
+    """Chunk-wise GDN prefill over a packed batch (gdn_chunk_fwd; gdn_chunk_fwd_ex with options).
 
     q, k: [T, H_q, d_k]; v: [T, H_v, d_v] (bf16 or fp32, same dtype); g, beta:
     [T, H_v] fp32 (g = ln alpha per token); cu_seqlens: host int sequence [N+1];
@@ -284,11 +285,15 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens: Sequence[int], initial_state=None, s
     keep_A also writes the A intermediate into it (GDN_FWD_KEEP_A), keep_hx the
     chunk-start states and U - W S (GDN_FWD_KEEP_HX).  ``gate`` =
     (z [T, H_v, d_v] in q's dtype, weight fp32 [d_v], eps) applies the gated
-    RMSNorm read-out epilogue to out (gdn_chunk_fwd_ex).
+    RMSNorm read-out epilogue to out (gdn_chunk_fwd_ex).  ``scan_ct`` (1, 2 or
+    4) fixes the state scan's column tiles a workgroup (GDN_FWD_SCAN_CT*)
+    instead of the host cost model's choice.
     """
     torch = _torch()
     lib = load_library()
     dt = _dtype_code(q)
+    if scan_ct is not None and scan_ct not in FWD_SCAN_CT:
+        raise ValueError("scan_ct must be 1, 2 or 4")
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_dev(name, t, q.dtype)
     _check_dev("g", g, torch.float32)
@@ -326,7 +331,7 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens: Sequence[int], initial_state=None, s
             _ptr(final_state), T, H_q, H_v, d_k, d_v, float(scale), dt, _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream_ptr(stream))
     gptr, _keep = _gate_arg(gate, q.dtype, T, H_v, d_v)
-    flags = (FWD_KEEP_A if keep_A else 0) | (FWD_KEEP_HX if keep_hx else 0)
+    flags = (FWD_KEEP_A if keep_A else 0) | (FWD_KEEP_HX if keep_hx else 0) | FWD_SCAN_CT.get(scan_ct, 0)
     if flags or gate is not None:
         rc, name = lib.gdn_chunk_fwd_ex(*args, flags, gptr, None), "gdn_chunk_fwd_ex"
     else:

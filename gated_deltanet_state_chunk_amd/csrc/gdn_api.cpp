@@ -165,18 +165,19 @@ double lpt_bins(gdn::SeqTable& tab, int32_t m, double step, double seq, bool wri
 // packed into as many bins as there are CUs for them (cus / workgroups a bin),
 // at most one sequence a bin, and ct is the one whose heaviest bin is the
 // cheapest under the cost model.
-void pack_scan_bins(gdn::SeqTable& tab, int32_t H_v, int32_t d, bool bf16, int32_t cus) {
+void pack_scan_bins(gdn::SeqTable& tab, int32_t H_v, int32_t d, bool bf16, int32_t cus, int32_t force_ct = 0) {
     const int32_t ns = tab.num_seqs;
     if (ns <= 0) return;
     const int32_t nt = d / 16;
     int32_t best_ci = 0, best_m = 1;
     double best = 0.0;
     for (int32_t ci = 0; ci < (bf16 ? 3 : 1); ++ci) {  // ct = 1 << ci
+        if (bf16 && force_ct && (1 << ci) != force_ct) continue;
         const int64_t per_bin = (int64_t)H_v * (nt >> ci);  // workgroups a bin
         const int32_t m = (int32_t)std::max<int64_t>(1, std::min<int64_t>(ns, cus / per_bin));
         const int64_t waves = (m * per_bin + cus - 1) / cus;
         const double cost = lpt_bins(tab, m, kScanStep[ci], kScanSeq[ci], false) * (double)waves;
-        if (ci == 0 || cost < best) {
+        if ((bf16 && force_ct) || ci == 0 || cost < best) {
             best = cost;
             best_ci = ci;
             best_m = m;
@@ -300,7 +301,11 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, 
                    hipStream_t stream,
                    uint32_t flags, const gdn_output_gate* gate, void* const* stage_events,
                    const gdn_front_end* front = nullptr) {
-    if (flags & ~(uint32_t)(GDN_FWD_KEEP_A | GDN_FWD_KEEP_HX)) return GDN_EINVAL;
+    constexpr uint32_t kScanCt = GDN_FWD_SCAN_CT1 | GDN_FWD_SCAN_CT2 | GDN_FWD_SCAN_CT4;
+    if (flags & ~(uint32_t)(GDN_FWD_KEEP_A | GDN_FWD_KEEP_HX | kScanCt)) return GDN_EINVAL;
+    const uint32_t ctf = flags & kScanCt;
+    if (ctf & (ctf - 1)) return GDN_EINVAL;  // more than one tile width
+    const int32_t force_ct = ctf == GDN_FWD_SCAN_CT1 ? 1 : ctf == GDN_FWD_SCAN_CT2 ? 2 : ctf == GDN_FWD_SCAN_CT4 ? 4 : 0;
     if (gate) {
         const int grc = check_gate(gate, T > 0);
         if (grc != GDN_OK) return grc;
@@ -356,7 +361,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, 
         const int32_t ns = std::min<int32_t>(gdn::MAX_SEQS_PER_LAUNCH, num_seqs - s0);
         chunk_base = fill_table(p.tab, cu_seqlens_host, s0, ns, chunk_base, slots, initial_state != nullptr,
                                 final_state != nullptr);
-        pack_scan_bins(p.tab, H_v, d_k, dtype == GDN_BF16, gdn::cu_count());
+        pack_scan_bins(p.tab, H_v, d_k, dtype == GDN_BF16, gdn::cu_count(), force_ct);
         hipEvent_t const* ev = (s0 == 0 && stage_events) ? reinterpret_cast<hipEvent_t const*>(stage_events) : nullptr;
         const hipError_t e = run_chunk(p, dtype, d_k, stream, ev);
         if (e != hipSuccess) return hip_fail(e);

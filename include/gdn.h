@@ -193,14 +193,21 @@ typedef struct gdn_output_gate {
 /* Flags of gdn_chunk_fwd_ex. */
 #define GDN_FWD_KEEP_A 1u  /* also write A to its workspace region (otherwise that region is left untouched) */
 #define GDN_FWD_KEEP_HX 2u /* also write Ht and Xt (bf16 forms the output on chip and leaves them untouched) */
+#define GDN_FWD_SCAN_CT1 4u  /* bf16: the state scan takes 1 / 2 / 4 sixteen-column tiles of d_v a */
+#define GDN_FWD_SCAN_CT2 8u  /* workgroup, with as many bins of sequences as fit on the chip at that */
+#define GDN_FWD_SCAN_CT4 16u /* width, instead of the width the host's cost model picks (at most one) */
 
 /*
  * gdn_chunk_fwd with options, for inspection, profiling and benchmarks.  Same
  * arguments and results as gdn_chunk_fwd, plus:
- *   flags  0 or GDN_FWD_KEEP_A.  A is an intermediate nothing downstream reads
- *          back (W and U are formed from it on chip), so gdn_chunk_fwd does not
- *          spend the HBM write on it; GDN_FWD_KEEP_A writes it for inspection.
- *          Unknown bits: GDN_EINVAL.
+ *   flags  0 or a combination of the GDN_FWD_ bits above.  A is an
+ *          intermediate nothing downstream reads back (W and U are formed from
+ *          it on chip), so gdn_chunk_fwd does not spend the HBM write on it;
+ *          GDN_FWD_KEEP_A writes it for inspection.  A GDN_FWD_SCAN_CT bit fixes
+ *          the state scan's work split (for tests of every split; the results
+ *          are bitwise the same for any split); it is ignored for fp32, which
+ *          always scans one tile a workgroup.  Unknown bits, or more than one
+ *          GDN_FWD_SCAN_CT bit: GDN_EINVAL.
  *   gate   NULL, or the read-out epilogue above applied to `out`.
  *   stage_events  NULL or an array of six hipEvent_t created by the caller:
  *          the start and stop events of the three kernels (chunk_prep: gate

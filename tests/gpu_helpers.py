@@ -76,7 +76,8 @@ def frag_u_to_logical(flat, d_v):
     return flat[..., off]
 
 
-def chunk_fwd_device(inp, device="cuda", initial_state="from_inputs", return_ws=False, keep_A=False, keep_hx=False):
+def chunk_fwd_device(inp, device="cuda", initial_state="from_inputs", return_ws=False, keep_A=False, keep_hx=False,
+                     scan_ct=None):
     """Run gdn_chunk_fwd on seeded inputs; returns (out, final, workspace-or-None) as host arrays / tensor."""
     import torch
 
@@ -93,7 +94,7 @@ def chunk_fwd_device(inp, device="cuda", initial_state="from_inputs", return_ws=
     ws = torch.empty(max(gdn.workspace_size(inp.T, inp.cu_seqlens, inp.H_q, inp.H_v, inp.d_k, inp.d_v,
                                             inp.dtype), 1), dtype=torch.uint8, device=device)
     out, fin = gdn.chunk_fwd(q, k, v, g, beta, inp.cu_seqlens, initial_state=s0, scale=inp.scale, workspace=ws,
-                             keep_A=keep_A, keep_hx=keep_hx)
+                             keep_A=keep_A, keep_hx=keep_hx, scan_ct=scan_ct)
     torch.cuda.synchronize()
     res = (to_host(out), to_host(fin))
     if return_ws:

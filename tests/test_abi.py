@@ -184,7 +184,10 @@ def test_chunk_fwd_rejects_before_any_device_work(gdn):
                                     a["fin"], a["T"], a["H_q"], a["H_v"], a["dk"], a["dv"], a["scale"], a["dt"],
                                     a["ws"], a["wsb"], a["stream"], flags, None, None)
 
-    assert call_ex(4) == -1                    # unknown flag bit
+    assert call_ex(32) == -1                   # unknown flag bit
+    assert call_ex(gdn.FWD_SCAN_CT[1] | gdn.FWD_SCAN_CT[2]) == -1  # two tile widths
+    assert call_ex(gdn.FWD_SCAN_CT[4], q=None) == -1
+    assert call_ex(gdn.FWD_SCAN_CT[2], N=0, T=0, cu=_cu([0])) == 0
 
     def call_gate(z, w, eps):
         g = gdn.OutputGate(z, w, eps)

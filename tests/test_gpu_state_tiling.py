@@ -73,6 +73,33 @@ def test_state_scan_tiling_odd_heads_many_sequences(torch_cuda, oracle_mod, n_se
     assert rel_err(fin, ref_s) < 1e-2
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_state_scan_every_width_bins_bitwise(torch_cuda, oracle_mod, d):
+    """Each work split of the state scan forced on one batch: 1, 2 and 4
+    column tiles a workgroup, each with as many bins as fit on a 256-CU part
+    (H_v = 4, d = 128: 8 / 16 / 32 bins; d = 64: 16 / 32 / 40), so 40 ragged
+    sequences, some empty, make bins of several sequences at every width,
+    including the widths whose three-stage ring reads the next chunk's stage
+    half a step early, across sequence changes.  The three results agree bit
+    for bit, and match the oracle on every head."""
+    lens = [int(x) for x in np.random.default_rng(710 + d).integers(0, 300, 40)]
+    for i in (3, 17, 39):
+        lens[i] = 0
+    inp = gdn_inputs.make_prefill(seed=711 + d, seqlens=lens, H_q=2, H_v=4, d_k=d, d_v=d, dtype="bf16",
+                                  state_std=0.02)
+    res = {}
+    for ct in (1, 2, 4):
+        print(f"[widths] d={d} scan_ct={ct} T={inp.T}", flush=True)
+        res[ct] = chunk_fwd_device(inp, scan_ct=ct)
+    for ct in (2, 4):
+        assert np.array_equal(res[ct][0], res[1][0]), ct
+        assert np.array_equal(res[ct][1], res[1][1]), ct
+    ref_o, ref_s = oracle_mod.forward(inp.q32(), inp.k32(), inp.v32(), inp.g, inp.beta, inp.cu_seqlens, 2, 4,
+                                      inp.scale, initial_state=inp.initial_state.astype(np.float64))
+    assert rel_err(res[1][0], ref_o) < 1e-2
+    assert rel_err(res[1][1], ref_s) < 1e-2
+
+
 def test_state_scan_bins_short_sequences_pool_and_empties(torch_cuda, oracle_mod):
     """80 requests of 1..199 tokens, every tenth empty, at H_v = 32, d = 128,
     over a state pool: the first launch group's 64 sequences go four bins of
