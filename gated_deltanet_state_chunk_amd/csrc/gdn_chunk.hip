@@ -1068,10 +1068,15 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
         // a head together touch every line, so by the time the producers stream
         // that chunk it is in L2.  It pays where the stream comes from HBM rather
         // than from the Infinity Cache (long or many sequences), and costs a few
-        // per cent where it does not, so the launcher enables it by size.
+        // per cent where it does not, so the launcher enables it by size.  With
+        // one tile a workgroup (long sequences) the output waves' query rows are
+        // prefetched too: read only one step ahead, their HBM latency otherwise
+        // holds up the first half of every step (T = 65536: scan 1151 -> 1000
+        // us); with four tiles the extra lines cost more than they save.
         constexpr int PF = 6;
-        constexpr int LPT = SS::W_BYTES / 128 / NTW;  // lines of W (and of K) per workgroup
-        constexpr int NPL = (2 * LPT + 63) / 64;      // prefetch loads per lane (W lines, then K lines)
+        constexpr int LPT = SS::W_BYTES / 128 / NTW;  // lines of W (and of K, and of the query rows) per workgroup
+        constexpr int NPF = FO && CT == 1 ? 3 : 2;     // W, K (and the query rows) of a chunk
+        constexpr int NPL = (NPF * LPT + 63) / 64;    // prefetch loads per lane
         // Output tile of chunk c (FO) from LO to O.  A row of the tile is 32 CT
         // contiguous bytes of O, so 2 CT lanes share a row, 16 bytes each (column
         // tile ct, half hf), and an instruction covers 64 / (2 CT) whole row
@@ -1119,11 +1124,21 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
 #pragma unroll
                 for (int q = 0; q < NPL; ++q) {
                     const int L = lane + 64 * q;
-                    if (L < 2 * LPT) {
+                    if (L < NPF * LPT) {
                         const int li = tile * LPT + L % LPT;
                         const char* a = L >= LPT
                                             ? reinterpret_cast<const char*>(p.Kc) + kchp * SS::K_BYTES + li * 128
                                             : reinterpret_cast<const char*>(p.W) + chp * SS::W_BYTES + li * 128;
+                        if (L >= 2 * LPT) {  // line li of the chunk's query rows
+                            constexpr int QRB = D * (int)sizeof(T), LPR = QRB / 128;
+                            if (p.Qc) {
+                                a = reinterpret_cast<const char*>(p.Qc) + kchp * CHUNK * QRB + li * 128;
+                            } else {
+                                const int row = min(li / LPR, cpf.ell() - 1);
+                                a = reinterpret_cast<const char*>(p.q) +
+                                    ((size_t)(cpf.token() + row) * p.H_q + hq) * QRB + 128 * (li % LPR);
+                            }
+                        }
                         __builtin_amdgcn_global_load_lds((gptr_t)a, (lptr_t)sink, 4, 0, 0);
                     }
                 }
