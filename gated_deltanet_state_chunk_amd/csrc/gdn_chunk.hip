@@ -1072,11 +1072,16 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
         // one tile a workgroup (long sequences) the output waves' query rows are
         // prefetched too: read only one step ahead, their HBM latency otherwise
         // holds up the first half of every step (T = 65536: scan 1151 -> 1000
-        // us); with four tiles the extra lines cost more than they save.
+        // us); so are the tile's share of P, its U block and the gate blocks
+        // (1000 -> 978 us).  With four tiles the extra lines cost more than they
+        // save.
         constexpr int PF = 6;
         constexpr int LPT = SS::W_BYTES / 128 / NTW;  // lines of W (and of K, and of the query rows) per workgroup
         constexpr int NPF = FO && CT == 1 ? 3 : 2;     // W, K (and the query rows) of a chunk
-        constexpr int NPL = (NPF * LPT + 63) / 64;    // prefetch loads per lane
+        constexpr bool XPF = FO && CT == 1;            // also P (this tile's share of lines), its U and the gates
+        constexpr int PLT = SS::P_BYTES / 128 / NTW, ULT = SS::U_BYTES / 128, GL = 4;
+        constexpr int NXL = XPF ? PLT + ULT + GL : 0;
+        constexpr int NPL = (NPF * LPT + NXL + 63) / 64;    // prefetch loads per lane
         // Output tile of chunk c (FO) from LO to O.  A row of the tile is 32 CT
         // contiguous bytes of O, so 2 CT lanes share a row, 16 bytes each (column
         // tile ct, half hf), and an instruction covers 64 / (2 CT) whole row
@@ -1139,6 +1144,18 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
                                     ((size_t)(cpf.token() + row) * p.H_q + hq) * QRB + 128 * (li % LPR);
                             }
                         }
+                        __builtin_amdgcn_global_load_lds((gptr_t)a, (lptr_t)sink, 4, 0, 0);
+                    } else if (L < NPF * LPT + NXL) {
+                        const int x = L - NPF * LPT;
+                        const char* a;
+                        if (x < PLT)
+                            a = reinterpret_cast<const char*>(p.Pf) + chp * SS::P_BYTES + (tile * PLT + x) * 128;
+                        else if (x < PLT + ULT)
+                            a = reinterpret_cast<const char*>(p.Ut) + (chp * NT + CT * tile) * SS::U1_BYTES + (x - PLT) * 128;
+                        else if (x < PLT + ULT + 2)
+                            a = reinterpret_cast<const char*>(p.gc + chp * CHUNK) + (x - PLT - ULT) * 128;
+                        else
+                            a = reinterpret_cast<const char*>(p.kf + chp * CHUNK) + (x - PLT - ULT - 2) * 128;
                         __builtin_amdgcn_global_load_lds((gptr_t)a, (lptr_t)sink, 4, 0, 0);
                     }
                 }
