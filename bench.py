@@ -67,43 +67,48 @@ def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True, gated=False):
 
     Bytes: every distinct input read once, every output and intermediate written
     once and read once per consuming kernel (K and Q are read once per key
-    head); A is consumed inside chunk_prep and never written.  bf16 (es = 2):
+    head).  chunk_prep writes, per (chunk, value head), the gate block (gc, kf,
+    beta, beta gamma) and A as six MFMA fragments, and once per key head the
+    key rows Kc; the state scan forms X = U - W S as A B (V - Gamma K S) from
+    those and the value rows, so W and U are never written.  bf16 (es = 2):
     chunk_prep also forms P (the masked, decayed Q K^T, six 1 KiB fragments per
     chunk and value head), the state scan forms the output from P, q and its
-    own on-chip h and U - W S, and the gated read-out (when asked for) is a
-    pass over the output.  fp32: the chunk-start states h and U - W S go
-    through HBM to a separate output kernel.  Flops: 2 x multiply-adds of the
-    chunk form at full chunks, triangles exploited.
+    own on-chip h and X, and the gated read-out (when asked for) is a pass over
+    the output.  fp32: the chunk-start states h and X go through HBM to a
+    separate output kernel.  Flops: 2 x multiply-adds of the chunk form at full
+    chunks, triangles exploited.
     """
     C = CHUNK
     chv, chq = n_chunks * H_v, n_chunks * H_q
     q_b = k_b = T * H_q * d * es
     v_b = o_b = T * H_v * d * es
-    gate_b = T * H_v * 4  # g or beta
-    gc_b = chv * C * 4
-    W_b = U_b = X_b = chv * C * d * es
-    kf_b = chv * C * 4      # per-position factor of the state update's keys
-    Kc_b = chq * C * d * es  # the state update's copy of the keys, one per key head
+    gate_b = T * H_v * 4     # g or beta
+    G_b = chv * 4 * C * 4    # gate block per (chunk, value head)
+    gc_b = chv * C * 4       # its gc row (what the fp32 output kernel reads)
+    Af_b = chv * 6 * 64 * 8 * es  # A's six fragments
+    X_b = chv * C * d * es
+    Kc_b = chq * C * d * es  # the state scan's copy of the keys, one per key head
     H_b = chv * d * d * es
     S_b = N * H_v * d * d * 4
     P_b = chv * 6 * 1024
     tri = C * (C - 1) // 2   # strictly lower entries
     tri1 = C * (C + 1) // 2  # lower incl. diagonal
-    prep = tri * d + C ** 3 // 6 + 2 * tri1 * d          # K K^T, solve, W, U
+    prep = tri * d + C ** 3 // 6                          # K K^T, solve
+    scan = 2 * C * d * d + tri1 * d                        # K S, A (B Y), Kc^T (kf X)
     s0 = S_b if has_s0 else 0
     if es == 2:
         per = {"chunk_prep": prep + tri1 * d,                              # + Q K^T
-               "chunk_state_o": 2 * C * d * d + C * d * d + tri1 * d,      # W S, Kc^T (kf X), Q S, P X
+               "chunk_state_o": scan + C * d * d + tri1 * d,               # + Q S, P X
                "gated_readout": 0}
-        bytes_ = {"chunk_prep": k_b + v_b + 2 * gate_b + gc_b + W_b + U_b + kf_b + Kc_b + q_b + P_b,
-                  "chunk_state_o": W_b + U_b + Kc_b + kf_b + gc_b + P_b + q_b + s0 + S_b + o_b,
+        bytes_ = {"chunk_prep": k_b + 2 * gate_b + G_b + Af_b + Kc_b + q_b + P_b,
+                  "chunk_state_o": Kc_b + Af_b + G_b + v_b + P_b + q_b + s0 + S_b + o_b,
                   "gated_readout": (3 * o_b + d * 4) if gated else 0}      # o read, z read, out written
     else:
         per = {"chunk_prep": prep,
-               "chunk_state_h": 2 * C * d * d,                             # W S, Kc^T (kf X)
+               "chunk_state_h": scan,
                "chunk_output_o": C * d * d + 2 * tri1 * d}                 # Q S, Q K^T, P X
-        bytes_ = {"chunk_prep": k_b + v_b + 2 * gate_b + gc_b + W_b + U_b + kf_b + Kc_b,
-                  "chunk_state_h": W_b + U_b + Kc_b + kf_b + gc_b + s0 + H_b + X_b + S_b,
+        bytes_ = {"chunk_prep": k_b + 2 * gate_b + G_b + Af_b + Kc_b,
+                  "chunk_state_h": Kc_b + Af_b + G_b + v_b + s0 + H_b + X_b + S_b,
                   "chunk_output_o": q_b + k_b + gc_b + H_b + X_b + o_b + ((o_b + d * 4) if gated else 0)}
     flops = {k: 2 * v * chv for k, v in per.items()}
     return bytes_, flops

@@ -31,6 +31,8 @@ DTYPE_BF16 = 1
 FWD_KEEP_A = 1  # gdn_chunk_fwd_ex flag: also write A to the workspace
 FWD_KEEP_HX = 2  # gdn_chunk_fwd_ex flag: also write Ht and Xt (bf16 forms the output on chip)
 FWD_SCAN_CT = {1: 4, 2: 8, 4: 16}  # gdn_chunk_fwd_ex flags: the state scan's column tiles a workgroup (bf16)
+FWD_KEEP_WU = 32  # gdn_chunk_fwd_ex flag: also form W and U in the workspace
+FWD_FORM = {"W": 64, "A": 128}  # gdn_chunk_fwd_ex flags: the state scan's operand form (bf16)
 SCRATCH_BYTES = 256 << 20  # GDN_SCRATCH_BYTES: the static workspace of gdn_chunk_fwd_scratch
 
 _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace", -4: "hip"}
@@ -45,8 +47,8 @@ class GdnError(RuntimeError):
 
 
 class WorkspaceLayout(ctypes.Structure):
-    _fields_ = [("n_chunks", ctypes.c_int64), ("off_gc", ctypes.c_size_t), ("off_A", ctypes.c_size_t),
-                ("off_W", ctypes.c_size_t), ("off_U", ctypes.c_size_t), ("off_kf", ctypes.c_size_t),
+    _fields_ = [("n_chunks", ctypes.c_int64), ("off_gates", ctypes.c_size_t), ("off_A", ctypes.c_size_t),
+                ("off_Af", ctypes.c_size_t), ("off_W", ctypes.c_size_t), ("off_U", ctypes.c_size_t),
                 ("off_Kc", ctypes.c_size_t), ("off_Ht", ctypes.c_size_t), ("off_Xt", ctypes.c_size_t),
                 ("off_P", ctypes.c_size_t), ("off_Qc", ctypes.c_size_t),
                 ("total_bytes", ctypes.c_size_t)]
@@ -274,7 +276,8 @@ def workspace_size(T: int, cu_seqlens, H_q: int, H_v: int, d_k: int, d_v: int, d
 
 def chunk_fwd(q, k, v, g, beta, cu_seqlens: Sequence[int], initial_state=None, scale: Optional[float] = None,
               out=None, final_state=None, output_final_state: bool = True, workspace=None, stream=None,
-              keep_A: bool = False, gate=None, keep_hx: bool = False, scan_ct: Optional[int] = None):
+              keep_A: bool = False, gate=None, keep_hx: bool = False, scan_ct: Optional[int] = None,
+              keep_wu: bool = False, form: Optional[str] = None):
     """Chunk-wise GDN prefill over a packed batch (gdn_chunk_fwd; gdn_chunk_fwd_ex with options).
 
     q, k: [T, H_q, d_k]; v: [T, H_v, d_v] (bf16 or fp32, same dtype); g, beta:
@@ -282,12 +285,14 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens: Sequence[int], initial_state=None, s
     initial_state: fp32 [N, H_v, d_k, d_v] or None.  Returns (out, final_state)
     with final_state None when output_final_state is False.  ``workspace`` may
     be a preallocated uint8 device tensor of at least workspace_size() bytes;
-    keep_A also writes the A intermediate into it (GDN_FWD_KEEP_A), keep_hx the
-    chunk-start states and U - W S (GDN_FWD_KEEP_HX).  ``gate`` =
+    keep_A also writes the A intermediate into it (GDN_FWD_KEEP_A), keep_wu W
+    and U (GDN_FWD_KEEP_WU), keep_hx the chunk-start states and U - W S
+    (GDN_FWD_KEEP_HX).  ``gate`` =
     (z [T, H_v, d_v] in q's dtype, weight fp32 [d_v], eps) applies the gated
     RMSNorm read-out epilogue to out (gdn_chunk_fwd_ex).  ``scan_ct`` (1, 2 or
     4) fixes the state scan's column tiles a workgroup (GDN_FWD_SCAN_CT*)
-    instead of the host cost model's choice.
+    instead of the host cost model's choice; ``form`` ("W" or "A") the operands
+    the state scan reads (GDN_FWD_FORM_*) instead of the library's choice.
     """
     torch = _torch()
     lib = load_library()
@@ -331,7 +336,10 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens: Sequence[int], initial_state=None, s
             _ptr(final_state), T, H_q, H_v, d_k, d_v, float(scale), dt, _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream_ptr(stream))
     gptr, _keep = _gate_arg(gate, q.dtype, T, H_v, d_v)
-    flags = (FWD_KEEP_A if keep_A else 0) | (FWD_KEEP_HX if keep_hx else 0) | FWD_SCAN_CT.get(scan_ct, 0)
+    if form is not None and form not in FWD_FORM:
+        raise ValueError('form must be "W" or "A"')
+    flags = ((FWD_KEEP_A if keep_A else 0) | (FWD_KEEP_HX if keep_hx else 0) | (FWD_KEEP_WU if keep_wu else 0) |
+             FWD_SCAN_CT.get(scan_ct, 0) | FWD_FORM.get(form, 0))
     if flags or gate is not None:
         rc, name = lib.gdn_chunk_fwd_ex(*args, flags, gptr, None), "gdn_chunk_fwd_ex"
     else:

@@ -190,6 +190,27 @@ void pack_scan_bins(gdn::SeqTable& tab, int32_t H_v, int32_t d, bool bf16, int32
 // The same choice for device tables, whose lengths the host does not see: the
 // cost model on a launch group of equal sequences of the batch's mean length.
 // Returns ct; *bins_cap is the number of bins a group of that ct may use.
+// Form of the chunk operands the state scan reads (bf16; fp32 always reads W
+// and U).  The scan's time is its serial chain, and the A form (X = A B (V -
+// Gamma K S)) adds an exchange to every step of it, while it takes the W and U
+// products and 40 % of the bytes out of chunk_prep.  W and U pay only where
+// chunk_prep is cheap: the batch's tile chains (sequence, value head, 16 columns
+// of d_v) fit on the chip about twice over, and the scan's W-form operand
+// stream fits in the 256 MB Infinity Cache next to the layer's other tensors
+// (at most 128 MiB).  Measured on MI355X (one call, binding included): one
+// sequence of 4096 tokens x 32 heads 105 (W) against 108 us (A); of 8192
+// tokens 227 against 205 us; of 65536 tokens 1.48 against 1.43 ms; 8
+// sequences of about 3800 tokens 554 against 488 us; 256 requests of up to
+// 256 tokens 952 against 844 us.  Decided from the call's token and sequence
+// counts alone, so host and device boundaries take the same form.
+int32_t a_form(int32_t T, int32_t num_seqs, int32_t H_v, int32_t d, gdn_dtype dtype, int32_t cus) {
+    if (dtype != GDN_BF16) return 0;
+    if ((int64_t)num_seqs * H_v * (d / 16) > 2 * (int64_t)cus) return 1;
+    const int64_t chunks = ((int64_t)T + GDN_CHUNK - 1) / GDN_CHUNK + num_seqs;  // bound on the chunk count
+    const int64_t stage = 2 * (int64_t)GDN_CHUNK * d * 2 + GDN_CHUNK * 16 * 2 + 1024 + 6 * 1024;  // W, K, U, gates, P
+    return chunks * H_v * stage > (int64_t(128) << 20) ? 1 : 0;
+}
+
 int32_t dev_scan_shape(int32_t num_seqs, int32_t T, int32_t H_v, int32_t d, bool bf16, int32_t cus,
                        int32_t* bins_cap) {
     gdn::SeqTable t;
@@ -302,9 +323,11 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, 
                    uint32_t flags, const gdn_output_gate* gate, void* const* stage_events,
                    const gdn_front_end* front = nullptr) {
     constexpr uint32_t kScanCt = GDN_FWD_SCAN_CT1 | GDN_FWD_SCAN_CT2 | GDN_FWD_SCAN_CT4;
-    if (flags & ~(uint32_t)(GDN_FWD_KEEP_A | GDN_FWD_KEEP_HX | kScanCt)) return GDN_EINVAL;
+    constexpr uint32_t kForm = GDN_FWD_FORM_W | GDN_FWD_FORM_A;
+    if (flags & ~(uint32_t)(GDN_FWD_KEEP_A | GDN_FWD_KEEP_HX | GDN_FWD_KEEP_WU | kScanCt | kForm)) return GDN_EINVAL;
     const uint32_t ctf = flags & kScanCt;
     if (ctf & (ctf - 1)) return GDN_EINVAL;  // more than one tile width
+    if ((flags & kForm) == kForm) return GDN_EINVAL;  // both forms
     const int32_t force_ct = ctf == GDN_FWD_SCAN_CT1 ? 1 : ctf == GDN_FWD_SCAN_CT2 ? 2 : ctf == GDN_FWD_SCAN_CT4 ? 4 : 0;
     if (gate) {
         const int grc = check_gate(gate, T > 0);
@@ -337,14 +360,16 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, 
     gdn::ChunkParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
     p.s0 = initial_state; p.out = out; p.sfinal = final_state;
-    p.gc = reinterpret_cast<float*>(ws + L.off_gc);
-    p.A = ws + L.off_A; p.W = ws + L.off_W; p.Ut = ws + L.off_U;
-    p.kf = reinterpret_cast<float*>(ws + L.off_kf); p.Kc = ws + L.off_Kc;
+    p.gates = reinterpret_cast<float*>(ws + L.off_gates);
+    p.A = ws + L.off_A; p.Af = ws + L.off_Af; p.W = ws + L.off_W; p.Ut = ws + L.off_U;
+    p.Kc = ws + L.off_Kc;
     p.Ht = ws + L.off_Ht; p.Xt = ws + L.off_Xt;
     p.Pf = dtype == GDN_BF16 ? ws + L.off_P : nullptr;
     p.Qc = (dtype == GDN_BF16 && front) ? ws + L.off_Qc : nullptr;
     p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
     p.keep_A = (flags & GDN_FWD_KEEP_A) ? 1 : 0;
+    p.keep_wu = (flags & GDN_FWD_KEEP_WU) ? 1 : 0;
+    p.aform = (flags & GDN_FWD_FORM_A) ? 1 : (flags & GDN_FWD_FORM_W) ? 0 : a_form(T, num_seqs, H_v, d_k, dtype, gdn::cu_count());
     p.keep_hx = (flags & GDN_FWD_KEEP_HX) ? 1 : 0;
     p.T = T;
     p.gz = gate ? gate->z : nullptr;
@@ -491,11 +516,10 @@ int layout_for_chunks(int64_t nc, int32_t H_q, int32_t H_v, int32_t d_k, int32_t
     size_t off = 0;
     gdn_workspace_layout L;
     L.n_chunks = nc;
-    L.off_gc = off; off = align_up(off + chv * C * sizeof(float));
+    L.off_gates = off; off = align_up(off + chv * 4 * C * sizeof(float));
     L.off_A = off;  off = align_up(off + chv * C * C * es);
     L.off_W = off;  off = align_up(off + chv * C * (size_t)d_k * es);
     L.off_U = off; off = align_up(off + chv * (size_t)d_v * C * es);
-    L.off_kf = off; off = align_up(off + chv * C * sizeof(float));
     L.off_Kc = off; off = align_up(off + chq * C * (size_t)d_k * es);
     L.off_Ht = off; off = align_up(off + chv * (size_t)d_v * (size_t)d_k * es);
     L.off_Xt = off; off = align_up(off + chv * (size_t)d_v * C * es);
@@ -503,6 +527,9 @@ int layout_for_chunks(int64_t nc, int32_t H_q, int32_t H_v, int32_t d_k, int32_t
     L.off_P = off; off = align_up(off + (dtype == GDN_BF16 ? chv * 6 * 64 * 8 * es : 0));
     // Qc (bf16 only): the front end's normalised query rows, one copy per key head
     L.off_Qc = off; off = align_up(off + (dtype == GDN_BF16 ? chq * C * (size_t)d_k * es : 0));
+    // A's six MFMA fragments (64 lanes x 8 values, in the two-byte product type
+    // for bf16 inputs, fp32 for fp32)
+    L.off_Af = off; off = align_up(off + chv * 6 * 64 * 8 * es);
     L.total_bytes = off;
     *layout = L;
     return GDN_OK;
@@ -612,13 +639,14 @@ int gdn_chunk_fwd_dev(const void* q, const void* k, const void* v, const float* 
     gdn::ChunkParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
     p.s0 = initial_state; p.out = out; p.sfinal = final_state;
-    p.gc = reinterpret_cast<float*>(ws + L.off_gc);
-    p.A = ws + L.off_A; p.W = ws + L.off_W; p.Ut = ws + L.off_U;
-    p.kf = reinterpret_cast<float*>(ws + L.off_kf); p.Kc = ws + L.off_Kc;
+    p.gates = reinterpret_cast<float*>(ws + L.off_gates);
+    p.A = ws + L.off_A; p.Af = ws + L.off_Af; p.W = ws + L.off_W; p.Ut = ws + L.off_U;
+    p.Kc = ws + L.off_Kc;
     p.Ht = ws + L.off_Ht; p.Xt = ws + L.off_Xt;
     p.Pf = dtype == GDN_BF16 ? ws + L.off_P : nullptr;
     p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
     p.T = T;
+    p.aform = a_form(T, num_seqs, H_v, d_k, dtype, gdn::cu_count());
     p.gz = gate ? gate->z : nullptr;
     p.gw = gate ? gate->weight : nullptr;
     p.geps = gate ? gate->eps : 0.f;

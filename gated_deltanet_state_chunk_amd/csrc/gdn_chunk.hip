@@ -154,25 +154,32 @@ __host__ __device__ constexpr int kswz(int row) {
 constexpr int P_FRAGS = 6;
 
 // ---------------------------------------------------------------------------
-// 1. chunk_prep: one workgroup (4 waves) per (chunk, value head); the first two
-//    stages of the chunk form in one pass over the chunk's keys and values:
+// 1. chunk_prep: one workgroup (4 waves) per (chunk, value head); the first
+//    stages of the chunk form in one pass over the chunk's keys:
 //      gc = in-chunk inclusive cumsum of g          ("输入输出定义")
 //      L  = StrictLower(B Gamma K K^T Gamma^-1),  A = (I + L)^-1   (fp32)
-//      W  = A B Gamma K,  U = A B V,  kf = gamma_l / gamma  (per position)
-//    K is staged in LDS once and serves K K^T and W; V is prefetched into
-//    registers and staged after the solve (in the space L occupied).  gc and
-//    kf are written to the workspace, and A too when the caller asks for it
-//    (it is for inspection only: nothing downstream reads it); W and U are
-//    written in the fragment order chunk_state_h streams into LDS
-//    (frag_w_offset / frag_u_offset).  The state update's keys are not
-//    written: chunk_state_h reads K itself and applies kf to X instead
-//    (Diag(kf) K)^T X = K^T (Diag(kf) X).
+//    and the per-chunk operands of the state scan: the six fragments of A it
+//    multiplies B (V - Gamma K S) by, the gate block (gc, kf = gamma_l / gamma,
+//    beta and beta gamma per position), the key rows (Kc, once per key head)
+//    and, for bf16, P = masked, decayed Q K^T.  The scan never sees W or U:
+//    U - W S = A B V - A B Gamma K S = A B (V - Gamma K S), so it forms X from
+//    A and the raw K and V rows (section "计算过程描述" gives U and W as
+//    A B V and A B Gamma K; the product is only regrouped).  W and U are
+//    still formed, from the same A, when the caller asks for them
+//    (inspection), and A itself under keep_A.
 // ---------------------------------------------------------------------------
 // Lower-triangular 64x64 fp32 matrices are kept as their ten 16x16 blocks
 // (I >= J), block (I, J) at index I (I + 1) / 2 + J, rows padded to BS floats.
 constexpr int BS = 20;
 constexpr int BLK = 16 * BS;
 __host__ __device__ constexpr int blk(int I, int J) { return (I * (I + 1) / 2 + J) * BLK; }
+
+// A (lower triangular) as the A operand of X = A (B Y) in the state scan: the
+// fragments (row tile t, K-step s) with 32 s <= 16 t + 15, in the order of
+// P_FRAGS, lane 16 a + r, slot 4 h + b holding A[16 t + r][32 s + 16 h + 4 a + b]
+// (perm32: the B operand B Y is two stacked accumulator tiles).
+constexpr int A_FRAGS = 6;
+__host__ __device__ constexpr int a_frag_first(int t) { return t < 2 ? t : 2 * t - 2; }
 
 template <typename T, int D>
 struct PrepLds {
@@ -185,16 +192,19 @@ struct PrepLds {
             float LA[10 * BLK];
             float Tm[4 * BLK];  // products of the block solve
         } sv;                   // during the solve
-        T V[CHUNK][KP];         // after it (once A is in registers)
+        T V[CHUNK][KP];         // W and U for inspection: after it (once A is in registers)
     } u;
     float gc[CHUNK], beta[CHUNK], sk[CHUNK], svb[CHUNK], kd[CHUNK];
 };
 
 // DEV: the sequence table is read from device memory (p.dtab) instead of the
-// kernel arguments (same for the two kernels below).
-template <typename T, int D, bool DEV>
+// kernel arguments (same for the two kernels below).  WU: also form W and U
+// (a separate instantiation, so that the inspection path's registers do not
+// weigh on the hot one).
+template <typename T, int D, bool DEV, bool WU>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel(const ChunkParams p, int padded) {
     using PL = PrepLds<T, D>;
+    using PT = ProdT<T>;  // element type of the A fragments (and of the W and U products)
     constexpr int VEC = 16 / (int)sizeof(T);                  // elements per 16-byte access
     constexpr int NV = CHUNK * D / VEC / 256;                 // 16-byte pieces per thread
     const SeqTable& tab = DEV ? *p.dtab : p.tab;
@@ -202,26 +212,26 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
     if constexpr (DEV) padded = (work + 7) & ~7;  // the grid was sized by a bound
     // Items (chunk, value head) of this workgroup: virtual indices blockIdx.x,
     // blockIdx.x + gridDim.x, ... mapped XCD-aware (gridDim.x is a multiple of 8,
-    // so every item of a workgroup stays on its XCD).  The next item's K, V and
-    // gate rows are loaded into registers while this item's W and U are formed.
+    // so every item of a workgroup stays on its XCD).  The next item's K and
+    // gate rows are loaded into registers as soon as this item's are staged, so
+    // they land while K K^T, the solve and P are formed.
     int v = blockIdx.x;
     if (v >= padded) return;
     int wid = xcd_remap(v, padded);
     if (wid >= work) return;  // padding items come last, so all later ones are padding too
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
     __shared__ __attribute__((aligned(16))) PL s;
     float* const Ls = s.u.sv.LA;
     float* const Tm = s.u.sv.Tm;
     float* const As = s.u.sv.LA;  // block (I, J) of A replaces block (I, J) of L
 
-    // Rows of K and V (zero past the valid length) and wave 0's gate inputs, in
-    // registers.  K and the gates of the next item are fetched ahead (they are
-    // needed first); V is fetched at the start of its own item, since it is not
-    // read before the solve is done.
-    float4 kreg[NV], vreg[NV];
+    // Rows of K (zero past the valid length) and wave 0's gate inputs, in
+    // registers; with W and U also the rows of V (fetched at the start of their
+    // own item: they are not read before the solve is done).
+    float4 kreg[NV], vreg[WU ? NV : 1];
     float graw = 0.f, braw = 0.f;
     auto load_k = [&](int it) {
+        const int tid = threadIdx.x, lane = tid & 63;
         const int hh = it % p.H_v;
         const ChunkPos c = locate_chunk(tab, tab.chunk_begin + it / p.H_v);
         const T* kb = reinterpret_cast<const T*>(p.k) + (size_t)c.t0 * p.H_q * D + (size_t)(hh / p.G) * D;
@@ -231,7 +241,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
             kreg[j] = r < c.ell ? *reinterpret_cast<const float4*>(kb + (size_t)r * p.H_q * D + cc)
                                 : make_float4(0, 0, 0, 0);
         }
-        if (w == 0) {
+        if (tid < 64) {
             const size_t gi = (size_t)(c.t0 + lane) * p.H_v + hh;
             if (p.fa) {  // raw gate inputs (front end)
                 graw = lane < c.ell ? to_f32<T>(reinterpret_cast<const T*>(p.fa)[gi]) : 0.f;
@@ -257,8 +267,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
     const int ell = cp.ell;
     const size_t ch = (size_t)cp.ci * p.H_v + h;
 
-    // V rows into registers (staged in LDS after the solve); K rows into LDS.
-    {
+    if constexpr (WU) {  // V rows into registers (staged in LDS after the solve)
         const T* vb = reinterpret_cast<const T*>(p.v) + (size_t)cp.t0 * p.H_v * D + (size_t)h * D;
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
@@ -294,7 +303,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
         if (write_kc) *reinterpret_cast<float4*>(Kcb + r * D + VEC * ((c / VEC) ^ kswz<T, D>(r))) = kv;
     }
     // In-chunk inclusive cumsum of the log gate (front end: g and beta from the
-    // raw inputs first).
+    // raw inputs first), and the chunk's gate block for the state scan: gc, kf =
+    // gamma_l / gamma, beta and beta gamma, all zero past the valid length.
     if (w == 0) {
         float gv = graw, bv = braw;
         if (p.fa) {
@@ -307,12 +317,26 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
             if (lane >= off) gv += o;
         }
         const float gl = __shfl(gv, ell - 1, 64);
+        const float kd = lane < ell ? __expf(gl - gv) : 0.f;  // gamma_l / gamma
+        const float sk = bv * __expf(gv);                     // beta gamma
         s.gc[lane] = gv;
         s.beta[lane] = bv;
-        s.sk[lane] = bv * __expf(gv);                          // beta gamma
-        s.svb[lane] = bv;                                       // beta
-        s.kd[lane] = lane < ell ? __expf(gl - gv) : 0.f;        // gamma_l / gamma
-        p.gc[ch * CHUNK + lane] = lane < ell ? gv : 0.f;
+        s.sk[lane] = sk;
+        s.svb[lane] = bv;
+        s.kd[lane] = kd;
+        float* G = p.gates + ch * 4 * CHUNK;
+        G[lane] = lane < ell ? gv : 0.f;
+        G[CHUNK + lane] = kd;
+        G[2 * CHUNK + lane] = bv;
+        G[3 * CHUNK + lane] = sk;
+    }
+    // Without W and U the next item's K and gate loads go out now (this item's
+    // are staged), to land while K K^T, the solve and P are formed; with them
+    // they wait until A is in registers (the V rows hold those registers until then).
+    v += gridDim.x;
+    const int next = v < padded ? xcd_remap(v, padded) : work;
+    if constexpr (!WU) {
+        if (next < work) load_k(next);
     }
     lds_sync();
 
@@ -390,6 +414,30 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
     }
     lds_sync();
 
+    // A's fragments for the state scan that forms X from them: wave w writes
+    // those of row tile w.  Rows past the valid length are unit rows e_i (their L
+    // rows vanish with beta), which meet the zero rows of B Y there, so X
+    // vanishes on them unmasked.
+    if (!WU || p.write_af) {
+        PT* Ab = reinterpret_cast<PT*>(p.Af) + ch * A_FRAGS * 512;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ks == 1 && w < 2) break;
+            Frag<PT> f;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int J = 2 * ks + hh;  // column block: columns 32 ks + 16 hh + 4 grp .. + 3
+                float4 x = make_float4(0, 0, 0, 0);
+                if (J <= w) x = *reinterpret_cast<const float4*>(As + blk(w, J) + r16 * BS + 4 * grp);
+                frag_set(f, 4 * hh + 0, x.x);
+                frag_set(f, 4 * hh + 1, x.y);
+                frag_set(f, 4 * hh + 2, x.z);
+                frag_set(f, 4 * hh + 3, x.w);
+            }
+            *reinterpret_cast<Frag<PT>*>(Ab + ((a_frag_first(w) + ks) * 64 + lane) * 8) = f;
+        }
+    }
+
     // P (bf16): the P^T tiles (J, w) = K_J Q_w^T of this wave's query positions
     // i = 16 w + r16, P^T[j][i] = (k_j . q_i) exp(gc_i - gc_j) for j <= i < ell
     // (Lower keeps the diagonal), K_J from the staged keys.  With the front end
@@ -461,172 +509,172 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
         }
     }
 
-    // Fragments of A (rows pos, contiguous columns): Af[mt][ks] is the A operand of
-    // U = A (B V) for row tile mt and the B operand of W^T = (B Gamma K)^T A^T for
-    // column tile mt.  Blocks above the diagonal are zero; rows past the valid
-    // length are unit rows e_i, which meet zero rows of B Gamma K and B V, so W and
-    // U vanish there without masking.
-    using PT = ProdT<T>;  // element type of the W and U products' operands
-    Frag<PT> Af[4][2];
+    // W = A B Gamma K and U = A B V, for the state scan that reads them (and on
+    // request, for inspection), with the operand types and fragment orders
+    // documented for the workspace.
+    if constexpr (WU) {
+        // Fragments of A (rows pos, contiguous columns): Af[mt][ks] is the A operand
+        // of U = A (B V) for row tile mt and the B operand of W^T = (B Gamma K)^T A^T
+        // for column tile mt.  Rows past the valid length are unit rows e_i, which
+        // meet zero rows of B Gamma K and B V, so W and U vanish there unmasked.
+        Frag<PT> Af[4][2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int J = 2 * ks + (grp >> 1);  // column block of this lane's 8 columns
-            float4 lo = make_float4(0, 0, 0, 0), hi = lo;
-            if (J <= mt) {
-                const float4* src = reinterpret_cast<const float4*>(As + blk(mt, J) + r16 * BS + 8 * (grp & 1));
-                lo = src[0];
-                hi = src[1];
+            for (int ks = 0; ks < 2; ++ks) {
+                const int J = 2 * ks + (grp >> 1);  // column block of this lane's 8 columns
+                float4 lo = make_float4(0, 0, 0, 0), hi = lo;
+                if (J <= mt) {
+                    const float4* src = reinterpret_cast<const float4*>(As + blk(mt, J) + r16 * BS + 8 * (grp & 1));
+                    lo = src[0];
+                    hi = src[1];
+                }
+                frag_set(Af[mt][ks], 0, lo.x); frag_set(Af[mt][ks], 1, lo.y);
+                frag_set(Af[mt][ks], 2, lo.z); frag_set(Af[mt][ks], 3, lo.w);
+                frag_set(Af[mt][ks], 4, hi.x); frag_set(Af[mt][ks], 5, hi.y);
+                frag_set(Af[mt][ks], 6, hi.z); frag_set(Af[mt][ks], 7, hi.w);
             }
-            frag_set(Af[mt][ks], 0, lo.x); frag_set(Af[mt][ks], 1, lo.y);
-            frag_set(Af[mt][ks], 2, lo.z); frag_set(Af[mt][ks], 3, lo.w);
-            frag_set(Af[mt][ks], 4, hi.x); frag_set(Af[mt][ks], 5, hi.y);
-            frag_set(Af[mt][ks], 6, hi.z); frag_set(Af[mt][ks], 7, hi.w);
+        lds_sync();  // A is in registers: its LDS takes V (read after W is done)
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
+            *reinterpret_cast<float4*>(&s.u.V[r][c]) = vreg[j];
         }
-    lds_sync();  // A is in registers: its LDS takes V (read after W is done)
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        const int e = tid + 256 * j, r = e / (D / VEC), c = (e % (D / VEC)) * VEC;
-        *reinterpret_cast<float4*>(&s.u.V[r][c]) = vreg[j];
-    }
-    // The next item's K and gate loads go out now; they land while W and U are formed.
-    v += gridDim.x;
-    const int next = v < padded ? xcd_remap(v, padded) : work;
-    if (next < work) load_k(next);
+        // The next item's K and gate loads go out now; they land while W and U are formed.
+        if (next < work) load_k(next);
 
-    constexpr int TPW = D / 64;  // 16-wide tiles of d_k (or d_v) per wave
-    // W^T tiles: rows d_k (this wave's tiles), columns pos.  A is lower triangular,
-    // so column tile nt only needs contraction steps ks with 32 ks <= 16 nt + 15.
-    T* Wb = reinterpret_cast<T*>(p.W) + ch * CHUNK * D;
-    // A fragment of 8 consecutive positions (32 ks + 8 grp ..) of one column of a
-    // staged [pos][col] matrix, each value scaled by its position's factor and
-    // rounded to the product type (fp16 for bf16 inputs: rounding the scaled
-    // values B V to bf16 was the largest single error of the output).  For
-    // bf16 the columns come from LDS with transposed reads (two per fragment);
-    // for fp32 element by element.
-    auto col_frag = [&](Frag<PT>& f, const T* M, const float* sc, int ks, int c) {
-        const int r0 = 32 * ks + 8 * grp;
-        if constexpr (sizeof(T) == 2) {
-            const bf16x4 lo = lds_col4<PL::KP>(M, r0, c & ~15, lane), hi = lds_col4<PL::KP>(M, r0 + 4, c & ~15, lane);
+        constexpr int TPW = D / 64;  // 16-wide tiles of d_k (or d_v) per wave
+        // A fragment of 8 consecutive positions (32 ks + 8 grp ..) of one column of a
+        // staged [pos][col] matrix, each value scaled by its position's factor and
+        // rounded to the product type (fp16 for bf16 inputs: rounding the scaled
+        // values B V to bf16 was the largest single error of the output).  For
+        // bf16 the columns come from LDS with transposed reads (two per fragment);
+        // for fp32 element by element.
+        auto col_frag = [&](Frag<PT>& f, const T* M, const float* sc, int ks, int c) {
+            const int r0 = 32 * ks + 8 * grp;
+            if constexpr (sizeof(T) == 2) {
+                const bf16x4 lo = lds_col4<PL::KP>(M, r0, c & ~15, lane), hi = lds_col4<PL::KP>(M, r0 + 4, c & ~15, lane);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                frag_set(f, j, sc[r0 + j] * (float)lo[j]);
-                frag_set(f, 4 + j, sc[r0 + 4 + j] * (float)hi[j]);
+                for (int j = 0; j < 4; ++j) {
+                    frag_set(f, j, sc[r0 + j] * (float)lo[j]);
+                    frag_set(f, 4 + j, sc[r0 + 4 + j] * (float)hi[j]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) frag_set(f, j, sc[r0 + j] * to_f32<T>(M[(r0 + j) * PL::KP + c]));
+            }
+        };
+        auto w_kfrag = [&](Frag<PT>(&kf)[2], int mt) {  // (B Gamma K)^T rows of d_k tile mt, contraction pos
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) col_frag(kf[ks], &s.K[0][0], s.sk, ks, 16 * mt + r16);
+        };
+        // W^T tiles: rows d_k (this wave's tiles), columns pos; column tile nt only
+        // needs contraction steps ks with 32 ks <= 16 nt + 15.  lane: column pos =
+        // 16 nt + r16, rows d_k = 16 mt + 4 grp + i: fragment (pos tile nt, K-step
+        // mt / 2), same lane, slots 4 (mt % 2) + i.
+        T* Wb = reinterpret_cast<T*>(p.W) + ch * CHUNK * D;
+        if constexpr (TPW == 2) {  // this wave's two d_k tiles fill whole fragments: 16-byte stores
+            Frag<PT> k0[2], k1[2];
+            w_kfrag(k0, 2 * w);
+            w_kfrag(k1, 2 * w + 1);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                f32x4 c0 = mma(k0[0], Af[nt][0], zero4()), c1 = mma(k1[0], Af[nt][0], zero4());
+                if (nt >= 2) {
+                    c0 = mma(k0[1], Af[nt][1], c0);
+                    c1 = mma(k1[1], Af[nt][1], c1);
+                }
+                store8(Wb + frag_w_offset<D>(nt, w, lane), c0, c1);
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) frag_set(f, j, sc[r0 + j] * to_f32<T>(M[(r0 + j) * PL::KP + c]));
-        }
-    };
-    auto w_kfrag = [&](Frag<PT>(&kf)[2], int mt) {  // (B Gamma K)^T rows of d_k tile mt, contraction pos
+            for (int tt = 0; tt < TPW; ++tt) {
+                const int mt = w * TPW + tt;
+                Frag<PT> kf[2];
+                w_kfrag(kf, mt);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) col_frag(kf[ks], &s.K[0][0], s.sk, ks, 16 * mt + r16);
-    };
-    // lane: column pos = 16 nt + r16, rows d_k = 16 mt + 4 grp + i: in fragment
-    // order this is fragment (pos tile nt, K-step mt / 2), same lane, slots 4 (mt % 2) + i
-    if constexpr (TPW == 2) {  // this wave's two d_k tiles fill whole fragments: 16-byte stores
-        Frag<PT> k0[2], k1[2];
-        w_kfrag(k0, 2 * w);
-        w_kfrag(k1, 2 * w + 1);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            f32x4 c0 = mma(k0[0], Af[nt][0], zero4()), c1 = mma(k1[0], Af[nt][0], zero4());
-            if (nt >= 2) {
-                c0 = mma(k0[1], Af[nt][1], c0);
-                c1 = mma(k1[1], Af[nt][1], c1);
+                for (int nt = 0; nt < 4; ++nt) {
+                    f32x4 c = zero4();
+                    c = mma(kf[0], Af[nt][0], c);
+                    if (nt >= 2) c = mma(kf[1], Af[nt][1], c);
+                    store4(Wb + frag_w_offset<D>(nt, mt >> 1, lane) + 4 * (mt & 1), c[0], c[1], c[2], c[3]);
+                }
             }
-            store8(Wb + frag_w_offset<D>(nt, w, lane), c0, c1);
         }
-    } else {
+        lds_sync();  // V staged
+        // U tiles: rows pos, columns d_v (this wave's tiles), stored in the product type.
+        PT* Ub = reinterpret_cast<PT*>(p.Ut) + ch * D * CHUNK;
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
-            const int mt = w * TPW + tt;
-            Frag<PT> kf[2];
-            w_kfrag(kf, mt);
+            const int nt = w * TPW + tt;
+            const int dv = 16 * nt + r16;
+            Frag<PT> vf[2];
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                f32x4 c = zero4();
-                c = mma(kf[0], Af[nt][0], c);
-                if (nt >= 2) c = mma(kf[1], Af[nt][1], c);
-                store4(Wb + frag_w_offset<D>(nt, mt >> 1, lane) + 4 * (mt & 1), c[0], c[1], c[2], c[3]);
+            for (int ks = 0; ks < 2; ++ks) col_frag(vf[ks], &s.u.V[0][0], s.svb, ks, dv);
+            // lane: column d_v = 16 nt + r16, rows pos = 16 mt + 4 grp + i (accumulator
+            // order); row tiles 2 m and 2 m + 1 share one 16-byte store
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                f32x4 c0 = mma(Af[2 * m][0], vf[0], zero4()), c1 = mma(Af[2 * m + 1][0], vf[0], zero4());
+                if (m == 1) {
+                    c0 = mma(Af[2][1], vf[1], c0);
+                    c1 = mma(Af[3][1], vf[1], c1);
+                }
+                store8(Ub + frag_u_offset(nt, m, lane), c0, c1);
             }
         }
     }
-
-    lds_sync();  // V staged
-    // U tiles: rows pos, columns d_v (this wave's tiles), stored in the product type.
-    PT* Ub = reinterpret_cast<PT*>(p.Ut) + ch * D * CHUNK;
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-        const int nt = w * TPW + tt;
-        const int dv = 16 * nt + r16;
-        Frag<PT> vf[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) col_frag(vf[ks], &s.u.V[0][0], s.svb, ks, dv);
-        // lane: column d_v = 16 nt + r16, rows pos = 16 mt + 4 grp + i (accumulator
-        // order); row tiles 2 m and 2 m + 1 share one 16-byte store
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            f32x4 c0 = mma(Af[2 * m][0], vf[0], zero4()), c1 = mma(Af[2 * m + 1][0], vf[0], zero4());
-            if (m == 1) {
-                c0 = mma(Af[2][1], vf[1], c0);
-                c1 = mma(Af[3][1], vf[1], c1);
-            }
-            store8(Ub + frag_u_offset(nt, m, lane), c0, c1);
-        }
-    }
-    // Per-position factor of the state update's keys: gamma_l / gamma_r (zero
-    // past the valid length).
-    if (tid < CHUNK) p.kf[ch * CHUNK + tid] = s.kd[tid];
     if (next >= work) break;
     lds_sync();  // every read of this item's LDS is done before the next item's K lands
     wid = next;
     }
 }
-
 // ---------------------------------------------------------------------------
 // 3. chunk_state_h: one workgroup per (sequence, value head, 16-column tile of
 //    d_v), serial over the sequence's chunks: four compute waves (one per
-//    SIMD), NPW producer waves (one; two for fp32 at d = 128) and one store
-//    wave.
+//    SIMD), NPW producer waves (one) and one store wave.
 //
 //    Compute waves.  The fp32 state slice S[:, tile] (d_k x 16) stays in MFMA
 //    accumulators, split by rows over the waves.  Per chunk:
-//      X = U - W S                 wave w: positions 16w..16w+15, contraction over d_k
-//      S = gamma_l S + K^T (kf X)  wave w: its rows of S, contraction over positions
-//    (kf = gamma_l / gamma per position: the decayed keys of the chunk form,
-//    applied to X rather than to K; with the front end the rows of K are the
-//    L2-normalised keys chunk_prep keeps in Kc).  The two
-//    products exchange bf16 copies of -S, X and kf X through LDS in MFMA
-//    operand order (one 16-byte access per lane and fragment), two barriers a
-//    chunk (B1 before X, B2 before the state update).  A chunk's W, K, U and
-//    gate fragments are copied from its LDS stage into registers during the
-//    previous step (K's column fragments with transposed reads): with three
-//    stages in its first half, where the compute waves would otherwise wait
-//    for the output waves at B2, with two in its second.  The compute waves issue no global
-//    memory instruction inside the loop: a vector-memory instruction stalls
-//    its wave whenever the CU's memory pipeline is backed up, and on this
-//    serial path every stall delays the next barrier for all waves.
+//      B Y = B (V - Gamma K S)     wave w: positions 16w..16w+15, contraction over d_k
+//      X   = A (B Y)               wave w: positions 16w..16w+15, contraction over positions
+//      S   = gamma_l S + K^T (kf X)  wave w: its rows of S, contraction over positions
+//    X is U - W S of the chunk form, regrouped as A B (V - Gamma K S), so the
+//    chunk's operands are its raw key rows (Kc, with the front end the
+//    L2-normalised ones), its value rows, the 64 x 64 A and the gates; kf =
+//    gamma_l / gamma per position applies the chunk form's decayed keys to X
+//    rather than to K.  The products exchange bf16 copies of -S, X and kf X
+//    (and B Y in the type of A's fragments) through LDS in MFMA operand order
+//    (one 16-byte access per lane and fragment), three barriers a chunk (B1
+//    before K S, Bm before the A product, B2 before the state update).  A
+//    chunk's operand fragments are copied from its LDS stage into registers
+//    during the previous step (K's column fragments with transposed reads):
+//    with three stages between Bm and B2, where the compute waves would
+//    otherwise wait for the output waves, with two after B2.  The compute
+//    waves issue no global memory instruction inside the loop: a
+//    vector-memory instruction stalls its wave whenever the CU's memory
+//    pipeline is backed up, and on this serial path every stall delays the
+//    next barrier for all waves.
 //
-//    Producer waves.  Stream each chunk's W, K (Kc, one copy per key head),
-//    U, gc and kf blocks (stored by chunk_prep in exactly the LDS stage
-//    order) into a ring of NST stages (three where they fit) with direct
-//    global->LDS loads.  A stage is free
-//    once its chunk is in registers (B1 of that chunk's step); chunk c + NST
-//    goes out in two halves, at B1(c) and B2(c); vmcnt waits make chunk c + 1
-//    land before B1(c) (three stages) or B2(c) (two) and keep at most 63
-//    loads in flight per wave.
+//    Producer waves.  Stream each chunk's K rows (Kc, one copy per key head),
+//    A fragments, gate block (stored by chunk_prep in exactly the LDS stage
+//    order) and the value rows of the workgroup's column tiles (gathered from
+//    v) into a ring of NST stages (three where they fit) with direct
+//    global->LDS loads.  A stage is free once its chunk is in registers (B1
+//    of that chunk's step); chunk c + NST goes out in two halves, at B1(c) and
+//    B2(c); vmcnt waits make chunk c + 1 land before B1(c) (three stages) or
+//    B2(c) (two) and keep at most 63 loads in flight per wave.
 //
-//    Store wave.  Copies h_c (the sign-flipped -S of LS, between B1(c) and
-//    B2(c)) and X_c (LX, between B2(c) and B1(c + 1)) to HBM.
+//    Store wave.  Writes the output tiles (bf16) or copies h_c (the
+//    sign-flipped -S of LS, between B1(c) and B2(c)) and X_c (LX, between
+//    B2(c) and B1(c + 1)) to HBM.
 // ---------------------------------------------------------------------------
 // Loads producer wave pw of NPW issues in part 0 / part 1 of a chunk of NPIECE
-// 1 KiB pieces (part 1 includes the two 256-byte gate loads of wave 0).
+// 1 KiB pieces.
 __host__ __device__ constexpr int stage_part_loads(int npiece, int npw, int pw, int part) {
     int n = 0;
     for (int j = 0; j < npiece; ++j) n += (j % npw == pw && (j < npiece / 2) == (part == 0)) ? 1 : 0;
-    return n + (part == 1 && pw == 0 ? 2 : 0);
+    return n;
 }
 // Producer waves' vmcnt bound at B2(c) (chunks c + 2 .. c + nst - 1 whole plus
 // part 0 of chunk c + nst issued after chunk c + 1's last load) for wave pw.
@@ -648,27 +696,47 @@ __host__ __device__ constexpr int stage_producers(int npiece, int nst) {
     return 4;
 }
 
+// One chunk's LDS stage, each part a whole number of 1 KiB pieces.
+//   W form (AF false): W fragments | K rows | U of the CT column tiles | gate
+//     block | (FO) P fragments.
+//   A form (AF true): K rows | (FO) P fragments | A fragments | gate block |
+//     value rows of the CT column tiles.  Everything from A on lies in the
+//     second half of the pieces, which the producer issues for chunk c + NST
+//     only at B2(c) (see below), so the compute waves may read A, the gates
+//     and the value rows of chunk c from its stage in step c itself.
 // FO: the output is formed in the scan; the stage also carries the chunk's P
 // fragments (for the output waves) and the workgroup keeps an output tile
 // buffer through which the store wave writes O.
-template <typename T, int D, int CT = 1, bool FO = false>
+template <typename T, int D, int CT = 1, bool FO = false, bool AF = false>
 struct StateStage {
-    static constexpr int W_BYTES = CHUNK * D * (int)sizeof(T);
-    static constexpr int K_BYTES = CHUNK * D * (int)sizeof(T);   // K rows, row-major (pieces permuted by kswz)
-    static constexpr int U1_BYTES = 4 * 64 * 4 * (int)sizeof(T); // one 16-column tile of U
-    static constexpr int U_BYTES = CT * U1_BYTES;                // the workgroup's CT tiles
-    static constexpr int G_BYTES = 2 * CHUNK * 4;                // gc, then kf
-    static constexpr int P_BYTES = FO ? P_FRAGS * 1024 : 0;      // P fragments (bf16)
-    static constexpr int G_OFF = W_BYTES + K_BYTES + U_BYTES;
-    static constexpr int P_OFF = G_OFF + G_BYTES;
-    static constexpr int BYTES = P_OFF + P_BYTES;
-    static constexpr int NPIECE = (W_BYTES + K_BYTES + U_BYTES + P_BYTES) / 1024;  // 1 KiB loads per chunk (+ gates)
-    // Exchange blocks (-S, X and kf X): one fragment per lane, 16 bytes of
-    // padding after every 16 lanes so that the store wave's column gathers
-    // spread over the LDS banks.
+    using PT = ProdT<T>;
+    static constexpr int K_BYTES = CHUNK * D * (int)sizeof(T);            // K rows, row-major (pieces permuted by kswz)
+    static constexpr int G_BYTES = 4 * CHUNK * 4;                         // gc, kf, beta, beta gamma
+    static constexpr int P_BYTES = FO ? P_FRAGS * 1024 : 0;               // P fragments (bf16)
+    static constexpr int W_BYTES = AF ? 0 : CHUNK * D * (int)sizeof(T);   // W fragments
+    static constexpr int U1_BYTES = CHUNK * 16 * (int)sizeof(PT);         // U of one 16-column tile
+    static constexpr int U_BYTES = AF ? 0 : CT * U1_BYTES;
+    static constexpr int A_BYTES = AF ? A_FRAGS * 64 * 8 * (int)sizeof(PT) : 0;  // A's six fragments
+    static constexpr int V1_BYTES = CHUNK * 16 * (int)sizeof(T);          // value rows of one tile, [64][16]
+    static constexpr int V_BYTES = AF ? CT * V1_BYTES : 0;
+    static constexpr int W_OFF = 0;
+    static constexpr int K_OFF = AF ? 0 : W_BYTES;
+    static constexpr int U_OFF = K_OFF + K_BYTES;
+    static constexpr int P_OFF = AF ? K_BYTES : U_OFF + U_BYTES + G_BYTES;
+    static constexpr int A_OFF = AF ? P_OFF + P_BYTES : 0;
+    static constexpr int G_OFF = AF ? A_OFF + A_BYTES : U_OFF + U_BYTES;
+    static constexpr int V_OFF = AF ? G_OFF + G_BYTES : 0;
+    static constexpr int BYTES = W_BYTES + K_BYTES + U_BYTES + G_BYTES + P_BYTES + A_BYTES + V_BYTES;
+    static_assert(BYTES % 1024 == 0 && V1_BYTES % 1024 == 0 && U1_BYTES % 1024 == 0, "stage pieces are 1 KiB");
+    static constexpr int NPIECE = BYTES / 1024;  // 1 KiB loads per chunk
+    static_assert(!AF || A_OFF / 1024 >= NPIECE / 2, "A, the gates and V must lie in the second half of the pieces");
+    // Exchange blocks (-S, X, kf X and, in the A form, B Y): one fragment per
+    // lane, 16 bytes of padding after every 16 lanes so that the store wave's
+    // column gathers spread over the LDS banks.
     static constexpr int XPAD = 16;
     static constexpr int XBLK = 64 * 8 * (int)sizeof(T) + 4 * XPAD;
-    static constexpr int EXCH = (D / 32 + 4) * CT * XBLK;
+    static_assert(sizeof(PT) == sizeof(T), "B Y shares the exchange block size");
+    static constexpr int EXCH = (D / 32 + (AF ? 6 : 4)) * CT * XBLK;
     static constexpr int OBUF = FO ? 4 * CT * 64 * 8 : 0;  // output tiles (bf16: 4 values a lane, per wave and tile)
     static constexpr int QBUF = FO ? 4 * 16 * D * (int)sizeof(T) : 0;  // each output wave's 16 query rows
     // Three stages where they fit and one producer wave can keep them fed (a
@@ -737,39 +805,63 @@ __device__ __forceinline__ void lds_wait_untracked(u32x4* r) {
 }
 
 // Issue this producer wave's share (pieces j with j % NPW == pw) of one
-// chunk's direct-to-LDS loads; part 0 issues the first half of the share,
-// part 1 the rest and the two 256-byte gate blocks gc and kf (producer
-// wave 0).  ch: (chunk, value head) index; kch: (chunk, key head) index of Kc.
-// With the output formed in the scan (FO) the chunk's P fragments follow.
-template <typename T, int D, int CT, bool FO>
-__device__ __forceinline__ void state_issue(char* stage, const ChunkParams& p, size_t ch, size_t kch, int tile,
-                                            int lane, int pw, int part) {
-    using SS = StateStage<T, D, CT, FO>;
+// chunk's direct-to-LDS loads, in stage order; part 0 issues the first half
+// of the share, part 1 the rest.  ch: (chunk, value head) index; kch: (chunk,
+// key head) index of Kc; tok, ell: the chunk's first token and valid length.
+// A form: the value rows of column tile ct come straight from v, one 16-byte
+// piece a lane: a 1 KiB piece covers 32 rows (bf16; 16 for fp32) of the
+// tile's 16 columns, and rows past the valid length repeat the last valid row
+// (finite values that meet beta = 0).
+template <typename T, int D, int CT, bool FO, bool AF>
+__device__ __forceinline__ void state_issue(char* stage, const ChunkParams& p, size_t ch, size_t kch, int tok,
+                                            int ell, int h, int tile, int lane, int pw, int part) {
+    using SS = StateStage<T, D, CT, FO, AF>;
     constexpr int NT = D / 16;
     constexpr int NW = SS::W_BYTES / 1024, NK = SS::K_BYTES / 1024, NU = SS::U_BYTES / 1024;
+    constexpr int NA = SS::A_BYTES / 1024, NPF = SS::P_BYTES / 1024;
     constexpr int NP = SS::NPIECE;
+    constexpr int VPT = SS::V1_BYTES / 1024;       // pieces per column tile of V
+    constexpr int LPR = 16 * (int)sizeof(T) / 16;  // lanes per row of a V tile (2 bf16, 4 fp32)
+    constexpr int RPP = 64 / LPR;                  // rows per piece
     const char* wg = reinterpret_cast<const char*>(p.W) + ch * SS::W_BYTES;
     const char* kg = reinterpret_cast<const char*>(p.Kc) + kch * SS::K_BYTES;
     const char* ug = reinterpret_cast<const char*>(p.Ut) + (ch * NT + CT * tile) * SS::U1_BYTES;
+    const char* pg = reinterpret_cast<const char*>(p.Pf) + ch * SS::P_BYTES;
+    const char* ag = reinterpret_cast<const char*>(p.Af) + ch * SS::A_BYTES;
+    const char* gg = reinterpret_cast<const char*>(p.gates + ch * 4 * CHUNK);
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
         if (j % SS::NPW != pw) continue;
         if ((j < NP / 2) != (part == 0)) continue;
-        if (j < NW) {
-            dma_1k(wg + 1024 * j, stage + 1024 * j, lane);
-        } else if (j < NW + NK) {
-            dma_1k(kg + 1024 * (j - NW), stage + SS::W_BYTES + 1024 * (j - NW), lane);
-        } else if (j < NW + NK + NU) {
-            dma_1k(ug + 1024 * (j - NW - NK), stage + SS::W_BYTES + SS::K_BYTES + 1024 * (j - NW - NK), lane);
+        char* dst = stage + 1024 * j;  // the stage's parts follow one another in piece order
+        if constexpr (!AF) {
+            if (j < NW)
+                dma_1k(wg + 1024 * j, dst, lane);
+            else if (j < NW + NK)
+                dma_1k(kg + 1024 * (j - NW), dst, lane);
+            else if (j < NW + NK + NU)
+                dma_1k(ug + 1024 * (j - NW - NK), dst, lane);
+            else if (j < NW + NK + NU + 1)
+                dma_1k(gg, dst, lane);
+            else
+                dma_1k(pg + 1024 * (j - NW - NK - NU - 1), dst, lane);
         } else {
-            const char* pg = reinterpret_cast<const char*>(p.Pf) + ch * SS::P_BYTES;
-            dma_1k(pg + 1024 * (j - NW - NK - NU), stage + SS::P_OFF + 1024 * (j - NW - NK - NU), lane);
+            if (j < NK) {
+                dma_1k(kg + 1024 * j, dst, lane);
+            } else if (j < NK + NPF) {
+                dma_1k(pg + 1024 * (j - NK), dst, lane);
+            } else if (j < NK + NPF + NA) {
+                dma_1k(ag + 1024 * (j - NK - NPF), dst, lane);
+            } else if (j < NK + NPF + NA + 1) {
+                dma_1k(gg, dst, lane);
+            } else {
+                const int vj = j - NK - NPF - NA - 1, ct = vj / VPT, row = (vj % VPT) * RPP + lane / LPR;
+                const char* src = reinterpret_cast<const char*>(p.v) +
+                                  (((size_t)(tok + min(row, ell - 1)) * p.H_v + h) * D + 16 * (CT * tile + ct)) * sizeof(T) +
+                                  16 * (lane % LPR);
+                __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
+            }
         }
-    }
-    if (part == 1 && pw == 0) {
-        char* g = stage + SS::G_OFF;
-        __builtin_amdgcn_global_load_lds((gptr_t)(p.gc + ch * CHUNK + lane), (lptr_t)g, 4, 0, 0);
-        __builtin_amdgcn_global_load_lds((gptr_t)(p.kf + ch * CHUNK + lane), (lptr_t)(g + 4 * CHUNK), 4, 0, 0);
     }
 }
 
@@ -785,8 +877,10 @@ __host__ __device__ constexpr int state_wait_b2(int pw) {
 // perm32 fragment they belong to: even tile -> slots 0..3, odd -> slots 4..7.
 template <typename T>
 __device__ __forceinline__ void lds_put4(Frag<T>& f, int half, const f32x4& v, float s) {
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (std::is_same_v<T, bf16>) {
         *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(&f) + 4 * half) = cvt4_bf16(v, s);
+    } else if constexpr (std::is_same_v<T, f16>) {
+        *reinterpret_cast<f16x4*>(reinterpret_cast<f16*>(&f) + 4 * half) = __builtin_convertvector(v * s, f16x4);
     } else {
         *reinterpret_cast<float4*>(reinterpret_cast<float*>(&f) + 4 * half) =
             make_float4(s * v[0], s * v[1], s * v[2], s * v[3]);
@@ -828,6 +922,45 @@ __device__ __forceinline__ Frag<T> k_col_frag(const char* kst, int m, int ks, in
     return f;
 }
 
+// A operand of K S for the 16 positions r0 .. r0 + 15 (row r0 + lane % 16) and
+// contraction step ks over d_k in the perm32 order of the exchanged -S
+// fragments (slot 4 h + b <- d_k 32 ks + 16 h + 4 g + b, g = lane / 16), read
+// from a stage's K rows (pieces permuted by kswz): two 4-value reads a fragment.
+template <typename T, int D>
+__device__ __forceinline__ Frag<T> k_row_frag(const char* kst, int r0, int ks, int lane) {
+    constexpr int RB = D * (int)sizeof(T);  // bytes per K row
+    const int g = lane >> 4, row = r0 + (lane & 15);
+    Frag<T> f;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int col = 32 * ks + 16 * hh + 4 * g;                  // first of the four d_k indices
+        const int piece = (col * (int)sizeof(T) / 16) ^ kswz<T, D>(row);
+        const char* a = kst + row * RB + 16 * piece + (col * (int)sizeof(T)) % 16;
+        if constexpr (sizeof(T) == 2) {
+            const bf16x4 x = *reinterpret_cast<const bf16x4*>(a);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f.v[4 * hh + i] = x[i];
+        } else {
+            const float4 x = *reinterpret_cast<const float4*>(a);
+            f.v[4 * hh + 0] = x.x; f.v[4 * hh + 1] = x.y; f.v[4 * hh + 2] = x.z; f.v[4 * hh + 3] = x.w;
+        }
+    }
+    return f;
+}
+
+// Value rows r0 .. r0 + 3 (r0 = 16 w + 4 (lane / 16)) of column lane % 16 of a
+// stage's [64][16] tile: the accumulator layout of the wave's K S tile.
+template <typename T>
+__device__ __forceinline__ f32x4 v_acc4(const char* vst, int r0, int lane) {
+    if constexpr (sizeof(T) == 2) {
+        const bf16x4 x = lds_col4<16>(reinterpret_cast<const bf16*>(vst), r0, 0, lane);
+        return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+    } else {
+        const float* b = reinterpret_cast<const float*>(vst) + r0 * 16 + (lane & 15);
+        return f32x4{b[0], b[16], b[32], b[48]};
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Output waves of chunk_state_h with the output formed in the scan (stage 4 of
 // the chunk form computed beside stage 3).  Wave o forms the outputs of
@@ -844,12 +977,12 @@ __device__ __forceinline__ Frag<T> k_col_frag(const char* kst, int m, int ks, in
 // it after the next barrier, so these waves issue no global store.  Nothing
 // on the serial chain waits for them except the two barriers of a step.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int CT>
+template <typename T, int D, int CT, bool AF>
 __device__ __forceinline__ void chunk_output_waves(const ChunkParams& p, const char* smem, const char* LS,
                                                    const char* LX, char* LO, char* LQ, int o, int lane,
                                                    const SeqTable& tab, int kb, int ke, int hq, int nch) {
     static_assert(sizeof(T) == 2, "the output waves are bf16");
-    using SS = StateStage<T, D, CT, true>;
+    using SS = StateStage<T, D, CT, true, AF>;
     constexpr int KS = D / 32;
     constexpr int NST = SS::NST;
     o = __builtin_amdgcn_readfirstlane(o);
@@ -924,7 +1057,7 @@ __device__ __forceinline__ void chunk_output_waves(const ChunkParams& p, const c
         for (int ks = 0; ks < KS; ++ks) qf[ks] = q_frag(ks);
         wait_lgkmcnt0();                         // read out before the next chunk's rows overwrite them
         if (c + 1 < nch) load_q();
-        // -(h^T Q^T) from LS
+        // -(h^T Q^T) from LS (which holds -h_c until B2(c))
         f32x4 inter[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
@@ -947,10 +1080,10 @@ __device__ __forceinline__ void chunk_output_waves(const ChunkParams& p, const c
     asm volatile("s_barrier" ::: "memory");  // B_end: the last output tile is in LO
 }
 
-template <typename T, int D, bool DEV, int CT, bool FO>
-__global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_state_h_kernel(const ChunkParams p,
-                                                                                            int padded) {
-    using SS = StateStage<T, D, CT, FO>;
+template <typename T, int D, bool DEV, int CT, bool FO, bool AF>
+__global__ __launch_bounds__((64 * StateStage<T, D, CT, FO, AF>::WAVES)) void chunk_state_h_kernel(const ChunkParams p,
+                                                                                                int padded) {
+    using SS = StateStage<T, D, CT, FO, AF>;
     constexpr int NT = D / 16;   // column tiles of d_v per head
     constexpr int NTW = NT / CT; // workgroups per head (CT column tiles each)
     constexpr int KS = D / 32;   // contraction steps over d_k
@@ -965,21 +1098,31 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
     (void)padded;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int gi = (slot / NTW) * 8 + xcd;
+    // All of the workgroup's LDS is one array: the stage ring first (at LDS
+    // offset 0; with another __shared__ object ahead of it the scan ran 50 ->
+    // 73 us at T = 4096 on MI355X), then the exchange, output and query-row
+    // buffers, the L2-prefetch sink, the compute waves' step flags and, for a
+    // device table, its copy.
+    constexpr int SINK_OFF = NST * SS::BYTES + SS::EXCH + SS::OBUF + SS::QBUF;
+    constexpr int FLAG_OFF = SINK_OFF + 256;
+    constexpr int DTAB_OFF = FLAG_OFF + 16;
+    constexpr int LDS_BYTES = DTAB_OFF + (DEV ? (int)((sizeof(SeqTable) + 15) & ~size_t(15)) : 0);
+    static_assert(LDS_BYTES <= SS::LDS_CAP, "LDS of the state scan");
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
     // A device table is copied into LDS first: read from global memory, which
     // the kernel also writes, its entries would be vector loads, and a vector
     // load in a producer wave's cursor would count against the vmcnt that
     // paces the stage loads (its wait would drain the stages in flight).
-    __shared__ __attribute__((aligned(16))) std::conditional_t<DEV, SeqTable, int> dtab_lds;
     if constexpr (DEV) {
         static_assert(sizeof(SeqTable) % 4 == 0, "table copied in words");
         const int32_t* src = reinterpret_cast<const int32_t*>(p.dtab);
-        int32_t* dst = reinterpret_cast<int32_t*>(&dtab_lds);
+        int32_t* dst = reinterpret_cast<int32_t*>(smem + DTAB_OFF);
         for (int i = threadIdx.x; i < (int)(sizeof(SeqTable) / 4); i += blockDim.x) dst[i] = src[i];
         __syncthreads();
     }
     const SeqTable& tab = [&]() -> const SeqTable& {
         if constexpr (DEV)
-            return dtab_lds;
+            return *reinterpret_cast<const SeqTable*>(smem + DTAB_OFF);
         else
             return p.tab;
     }();
@@ -989,20 +1132,23 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
     const int kb = tab.bin_first[bin], ke = tab.bin_first[bin + 1];
     int nch = 0;  // chunks of the bin
     for (int k = kb; k < ke; ++k) nch += tab.choff[tab.order[k] + 1] - tab.choff[tab.order[k]];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, grp = lane >> 4;
     const int hq = h / p.G;
     // (chunk, value head) and (chunk, key head) indices of the chunk a cursor is at
     auto vch = [&](const BinCursor& cu) { return (size_t)cu.ci() * p.H_v + h; };
     auto kch = [&](const BinCursor& cu) { return (size_t)cu.ci() * p.H_q + hq; };
 
-    __shared__ __attribute__((aligned(16))) char smem[NST * SS::BYTES + SS::EXCH + SS::OBUF + SS::QBUF + 256];
+    int* const csync = reinterpret_cast<int*>(smem + FLAG_OFF);  // the compute waves' step flags (see sync4)
     char* const LS = smem + NST * SS::BYTES;  // KS x CT blocks: -S (block ks CT + ct)
     char* const LX = LS + KS * CT * SS::XBLK; // 2 x CT blocks: X (block j CT + ct)
     char* const LY = LX + 2 * CT * SS::XBLK;  // 2 x CT blocks: kf X
-    char* const LO = LY + 2 * CT * SS::XBLK;  // FO: output tiles, 8 bytes per (tile ct, wave, lane)
+    char* const LB = LY + 2 * CT * SS::XBLK;  // A form: 2 x CT blocks: B Y (A's operand type)
+    char* const LO = LB + (AF ? 2 : 0) * CT * SS::XBLK;  // FO: output tiles, 8 bytes per (tile ct, wave, lane)
+    static_assert(SS::EXCH == (KS + (AF ? 6 : 4)) * CT * SS::XBLK, "exchange blocks: LS, LX, LY (and LB)");
     char* const LQ = LO + SS::OBUF;           // FO: each output wave's query rows
-    char* const sink = LQ + SS::QBUF;         // L2-prefetch sink
+    char* const sink = smem + SINK_OFF;       // L2-prefetch sink
+    static_assert(SINK_OFF == (NST * SS::BYTES + SS::EXCH) + SS::OBUF + SS::QBUF, "buffers in order");
     // fragment of lane ln in block b of an exchange buffer
     auto xf = [](char* buf, int b, int ln) -> Frag<T>& {
         return *reinterpret_cast<Frag<T>*>(buf + b * SS::XBLK + ln * (int)sizeof(Frag<T>) + (ln >> 4) * SS::XPAD);
@@ -1013,7 +1159,7 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
 
     if constexpr (FO) {
         if (w > 4 + SS::NPW) {
-            chunk_output_waves<T, D, CT>(p, smem, LS, LX, LO, LQ, w - (5 + SS::NPW), lane, tab, kb, ke, hq, nch);
+            chunk_output_waves<T, D, CT, AF>(p, smem, LS, LX, LO, LQ, w - (5 + SS::NPW), lane, tab, kb, ke, hq, nch);
             return;
         }
     }
@@ -1063,25 +1209,37 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
                 xgo[ct][t] = (unsigned)(((ctile * 2 + j) * 64 + lane) * 8 * EB + 16 * e);
             }
         }
-        // L2 prefetch: once a step, this tile's share of the W and K lines of
-        // chunk c + PF (4 bytes per line, into a sink nobody reads).  The tiles of
+        // L2 prefetch: once a step, this workgroup's share of lines of chunk
+        // c + PF (4 bytes per line, into a sink nobody reads); the workgroups of
         // a head together touch every line, so by the time the producers stream
-        // that chunk it is in L2.  It pays where the stream comes from HBM rather
-        // than from the Infinity Cache (long or many sequences), and costs a few
-        // per cent where it does not, so the launcher enables it by size.  With
-        // one tile a workgroup (long sequences) the output waves' query rows are
-        // prefetched too: read only one step ahead, their HBM latency otherwise
-        // holds up the first half of every step (T = 65536: scan 1151 -> 1000
-        // us); so are the tile's share of P, its U block and the gate blocks
-        // (1000 -> 978 us).  With four tiles the extra lines cost more than they
-        // save.
+        // that chunk it is in L2.  W form: the W and K lines (chunk_prep's
+        // output, which the Infinity Cache usually still holds) pay only where
+        // the stream comes from HBM (long or many sequences) and cost a few per
+        // cent where it does not, so the launcher enables them by size; with one
+        // tile a workgroup the output waves' query rows are prefetched too (read
+        // only one step ahead, their HBM latency otherwise holds up the first
+        // half of every step: T = 65536 scan 1151 -> 1000 us), and so are the
+        // tile's share of P, its U block and the gate block (1000 -> 978 us).
+        // With four tiles those extra lines cost more than they save.  A form:
+        // the K and A lines likewise by size, and the value rows always: nothing
+        // upstream reads them, so they come cold from HBM, and the stage ring
+        // alone issues them only two steps and a half ahead.
         constexpr int PF = 6;
-        constexpr int LPT = SS::W_BYTES / 128 / NTW;  // lines of W (and of K, and of the query rows) per workgroup
-        constexpr int NPF = FO && CT == 1 ? 3 : 2;     // W, K (and the query rows) of a chunk
-        constexpr bool XPF = FO && CT == 1;            // also P (this tile's share of lines), its U and the gates
-        constexpr int PLT = SS::P_BYTES / 128 / NTW, ULT = SS::U_BYTES / 128, GL = 4;
-        constexpr int NXL = XPF ? PLT + ULT + GL : 0;
-        constexpr int NPL = (NPF * LPT + NXL + 63) / 64;    // prefetch loads per lane
+        constexpr bool XPF = FO && CT == 1 && !AF;
+        constexpr int VRL = D * (int)sizeof(T) / 128;                // lines per value row
+        constexpr int VLT = AF ? CHUNK * VRL / NTW : 0;              // value-row lines per workgroup
+        constexpr int WLT = SS::W_BYTES / 128 / NTW;                 // lines of W per workgroup
+        constexpr int KLT = SS::K_BYTES / 128 / NTW;                 // lines of K (and of the query rows) per workgroup
+        constexpr int ALT = SS::A_BYTES / 128 / NTW;                 // lines of A per workgroup
+        static_assert(KLT * NTW * 128 == SS::K_BYTES && ALT * NTW * 128 == SS::A_BYTES &&
+                          WLT * NTW * 128 == SS::W_BYTES && (!AF || VLT * NTW == CHUNK * VRL),
+                      "whole lines per workgroup");
+        constexpr int QLT = XPF ? KLT : 0;
+        constexpr int PLT = XPF ? SS::P_BYTES / 128 / NTW : 0;
+        constexpr int ULT = XPF ? SS::U_BYTES / 128 : 0;
+        constexpr int GLT = XPF ? SS::G_BYTES / 128 : 0;
+        constexpr int NLT = VLT + WLT + KLT + ALT + QLT + PLT + ULT + GLT;
+        constexpr int NPL = (NLT + 63) / 64;                         // prefetch loads per lane
         // Output tile of chunk c (FO) from LO to O.  A row of the tile is 32 CT
         // contiguous bytes of O, so 2 CT lanes share a row, 16 bytes each (column
         // tile ct, half hf), and an instruction covers 64 / (2 CT) whole row
@@ -1124,40 +1282,43 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
             const size_t ch = vch(cs);
             cs.next();
             asm volatile("s_barrier" ::: "memory");  // B1(c)
-            if (p.l2_prefetch && cpf.valid()) {
+            if (cpf.valid() && (AF || p.l2_prefetch)) {
                 const size_t chp = vch(cpf), kchp = kch(cpf);
+                const int nlt = p.l2_prefetch ? NLT : VLT;
 #pragma unroll
                 for (int q = 0; q < NPL; ++q) {
-                    const int L = lane + 64 * q;
-                    if (L < NPF * LPT) {
-                        const int li = tile * LPT + L % LPT;
-                        const char* a = L >= LPT
-                                            ? reinterpret_cast<const char*>(p.Kc) + kchp * SS::K_BYTES + li * 128
-                                            : reinterpret_cast<const char*>(p.W) + chp * SS::W_BYTES + li * 128;
-                        if (L >= 2 * LPT) {  // line li of the chunk's query rows
-                            constexpr int QRB = D * (int)sizeof(T), LPR = QRB / 128;
-                            if (p.Qc) {
-                                a = reinterpret_cast<const char*>(p.Qc) + kchp * CHUNK * QRB + li * 128;
-                            } else {
-                                const int row = min(li / LPR, cpf.ell() - 1);
-                                a = reinterpret_cast<const char*>(p.q) +
-                                    ((size_t)(cpf.token() + row) * p.H_q + hq) * QRB + 128 * (li % LPR);
-                            }
+                    int x = lane + 64 * q;
+                    if (x >= nlt) continue;
+                    const char* a;
+                    if (x < VLT) {  // line li of the head's value rows: row li / VRL, piece li % VRL
+                        const int li = tile * VLT + x, row = min(li / VRL, cpf.ell() - 1);
+                        a = reinterpret_cast<const char*>(p.v) +
+                            ((size_t)(cpf.token() + row) * p.H_v + h) * D * sizeof(T) + 128 * (li % VRL);
+                    } else if ((x -= VLT) < WLT) {
+                        a = reinterpret_cast<const char*>(p.W) + chp * SS::W_BYTES + (tile * WLT + x) * 128;
+                    } else if ((x -= WLT) < KLT) {
+                        a = reinterpret_cast<const char*>(p.Kc) + kchp * SS::K_BYTES + (tile * KLT + x) * 128;
+                    } else if ((x -= KLT) < ALT) {
+                        a = reinterpret_cast<const char*>(p.Af) + chp * SS::A_BYTES + (tile * ALT + x) * 128;
+                    } else if ((x -= ALT) < QLT) {  // line li of the chunk's query rows
+                        constexpr int QRB = D * (int)sizeof(T), LPR = QRB / 128;
+                        const int li = tile * QLT + x;
+                        if (p.Qc) {
+                            a = reinterpret_cast<const char*>(p.Qc) + kchp * CHUNK * QRB + li * 128;
+                        } else {
+                            const int row = min(li / LPR, cpf.ell() - 1);
+                            a = reinterpret_cast<const char*>(p.q) + ((size_t)(cpf.token() + row) * p.H_q + hq) * QRB +
+                                128 * (li % LPR);
                         }
-                        __builtin_amdgcn_global_load_lds((gptr_t)a, (lptr_t)sink, 4, 0, 0);
-                    } else if (L < NPF * LPT + NXL) {
-                        const int x = L - NPF * LPT;
-                        const char* a;
-                        if (x < PLT)
-                            a = reinterpret_cast<const char*>(p.Pf) + chp * SS::P_BYTES + (tile * PLT + x) * 128;
-                        else if (x < PLT + ULT)
-                            a = reinterpret_cast<const char*>(p.Ut) + (chp * NT + CT * tile) * SS::U1_BYTES + (x - PLT) * 128;
-                        else if (x < PLT + ULT + 2)
-                            a = reinterpret_cast<const char*>(p.gc + chp * CHUNK) + (x - PLT - ULT) * 128;
-                        else
-                            a = reinterpret_cast<const char*>(p.kf + chp * CHUNK) + (x - PLT - ULT - 2) * 128;
-                        __builtin_amdgcn_global_load_lds((gptr_t)a, (lptr_t)sink, 4, 0, 0);
+                    } else if ((x -= QLT) < PLT) {
+                        a = reinterpret_cast<const char*>(p.Pf) + chp * SS::P_BYTES + (tile * PLT + x) * 128;
+                    } else if ((x -= PLT) < ULT) {
+                        a = reinterpret_cast<const char*>(p.Ut) + (chp * NT + CT * tile) * SS::U1_BYTES + x * 128;
+                    } else {
+                        x -= ULT;
+                        a = reinterpret_cast<const char*>(p.gates + chp * 4 * CHUNK) + x * 128;
                     }
+                    __builtin_amdgcn_global_load_lds((gptr_t)a, (lptr_t)sink, 4, 0, 0);
                 }
             }
             cpf.next();
@@ -1231,8 +1392,10 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
                 if (pw == 0) wait_vmcnt<RC_0>(); else wait_vmcnt<RC_1>();
             }
             if (b < nch) {
-                state_issue<T, D, CT, FO>(smem + b * SS::BYTES, p, vch(cp), kch(cp), tile, lane, pw, 0);
-                state_issue<T, D, CT, FO>(smem + b * SS::BYTES, p, vch(cp), kch(cp), tile, lane, pw, 1);
+                state_issue<T, D, CT, FO, AF>(smem + b * SS::BYTES, p, vch(cp), kch(cp), cp.token(), cp.ell(), h, tile,
+                                          lane, pw, 0);
+                state_issue<T, D, CT, FO, AF>(smem + b * SS::BYTES, p, vch(cp), kch(cp), cp.token(), cp.ell(), h, tile,
+                                          lane, pw, 1);
                 cp.next();
             }
         }
@@ -1262,9 +1425,10 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
             const int cn = c + NST;
             char* stn = smem + (cn % NST) * SS::BYTES;
             const size_t chn = vch(cp), kchn = kch(cp);  // chunk cn
+            const int tokn = cp.token(), elln = cp.ell();
             if (cn < nch) {
                 if (pw == 0) wait_vmcnt<R0_0>(); else wait_vmcnt<R0_1>();
-                state_issue<T, D, CT, FO>(stn, p, chn, kchn, tile, lane, pw, 0);
+                state_issue<T, D, CT, FO, AF>(stn, p, chn, kchn, tokn, elln, h, tile, lane, pw, 0);
                 if constexpr (NST != 3) {
                     if (pw == 0) wait_vmcnt<WB_0>(); else wait_vmcnt<WB_1>();
                 }
@@ -1274,7 +1438,7 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
             asm volatile("s_barrier" ::: "memory");  // B2(c)
             if (cn < nch) {
                 if (pw == 0) wait_vmcnt<R1_0>(); else wait_vmcnt<R1_1>();
-                state_issue<T, D, CT, FO>(stn, p, chn, kchn, tile, lane, pw, 1);
+                state_issue<T, D, CT, FO, AF>(stn, p, chn, kchn, tokn, elln, h, tile, lane, pw, 1);
                 cp.next();
             }
         }
@@ -1340,32 +1504,95 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
         load_s(rd.n, S);
         put_s();
     }
-    // Operand fragments of one chunk, read from its LDS stage.
-    Frag<T> wf[KS], kfg[TPW][2];
-    Raw4<ProdT<T>> uf[CT];  // U is stored in the product type (fp16 for bf16 inputs)
-    float gl = 0.f;
-    float4 fx;  // kf of this wave's X rows (positions 16 w + 4 grp + i)
+    // Operand fragments of one chunk, copied from its LDS stage into registers
+    // during the previous step: K's columns (the A operand of K^T (kf X)) and
+    // the A operand of the step's first product over d_k, W's rows (W form) or
+    // K's rows (A form).
+    using PT = ProdT<T>;
+    Frag<T> kr[KS], kfg[TPW][2];
+    int rell = CHUNK;  // valid length of the chunk last read
+    // The rest of a chunk's operands of this wave.  W form: U of its positions,
+    // kf of its positions and gamma_l, a step ahead.  A form: its row tile of A,
+    // the value rows, beta, beta gamma and kf of its positions, and gamma_l;
+    // with one column tile and three stages a step ahead too, so that nothing
+    // but the exchanges sits on the serial chain after B1; with more tiles the
+    // registers are not there, and they are read from the chunk's own stage at
+    // the start of its step (the second half of an A-form stage is refilled
+    // only from B2 on).
+    constexpr bool AHEAD = !AF || (CT == 1 && NST == 3);
+    struct ChunkOps {
+        Frag<PT> a0, a1;
+        f32x4 v[CT];
+        Raw4<PT> u[CT];
+        float4 fb, fbg, fx;
+        float gl;
+    } ops;
+    auto read_ops = [&](const char* st, int ell, ChunkOps& o) {
+        const float* Gst = reinterpret_cast<const float*>(st + SS::G_OFF);
+        if constexpr (AF) {
+            const Frag<PT>* Ast = reinterpret_cast<const Frag<PT>*>(st + SS::A_OFF);
+            o.a0 = Ast[a_frag_first(w) * 64 + lane];
+            if (w >= 2) o.a1 = Ast[(a_frag_first(w) + 1) * 64 + lane];
+            if constexpr (AHEAD) {  // else read where they are used (registers)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    o.v[ct] = v_acc4<T>(st + SS::V_OFF + ct * SS::V1_BYTES, 16 * w + 4 * grp, lane);
+            }
+            o.fb = *reinterpret_cast<const float4*>(Gst + 2 * CHUNK + 16 * w + 4 * grp);
+            o.fbg = *reinterpret_cast<const float4*>(Gst + 3 * CHUNK + 16 * w + 4 * grp);
+        } else {
+            const Raw4<PT>* Ust = reinterpret_cast<const Raw4<PT>*>(st + SS::U_OFF);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                o.u[ct] = Ust[ct * (SS::U1_BYTES / (int)sizeof(Raw4<PT>)) + ((w >> 1) * 64 + lane) * 2 + (w & 1)];
+        }
+        o.fx = *reinterpret_cast<const float4*>(Gst + CHUNK + 16 * w + 4 * grp);
+        o.gl = Gst[ell - 1];
+    };
     auto read_stage = [&](int c) {  // chunk c of the bin, at cursor rd
         const char* st = smem + (c % NST) * SS::BYTES;
-        const Frag<T>* Wst = reinterpret_cast<const Frag<T>*>(st);
-        const char* Kst = st + SS::W_BYTES;
-        const Raw4<ProdT<T>>* Ust = reinterpret_cast<const Raw4<ProdT<T>>*>(st + SS::W_BYTES + SS::K_BYTES);
-        const float* Gst = reinterpret_cast<const float*>(st + SS::W_BYTES + SS::K_BYTES + SS::U_BYTES);
+        if constexpr (AF) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) wf[ks] = Wst[(w * KS + ks) * 64 + lane];
+            for (int ks = 0; ks < KS; ++ks) kr[ks] = k_row_frag<T, D>(st + SS::K_OFF, 16 * w, ks, lane);
+        } else {
+            const Frag<T>* Wst = reinterpret_cast<const Frag<T>*>(st + SS::W_OFF);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) kr[ks] = Wst[(w * KS + ks) * 64 + lane];
+        }
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) kfg[tt][ks] = k_col_frag<T, D>(Kst, w * TPW + tt, ks, lane);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) uf[ct] = Ust[ct * (SS::U1_BYTES / (int)sizeof(Raw4<ProdT<T>>)) + ((w >> 1) * 64 + lane) * 2 + (w & 1)];
-        gl = Gst[rd.ell() - 1];
-        fx = *reinterpret_cast<const float4*>(Gst + CHUNK + 16 * w + 4 * grp);
+            for (int ks = 0; ks < 2; ++ks) kfg[tt][ks] = k_col_frag<T, D>(st + SS::K_OFF, w * TPW + tt, ks, lane);
+        rell = rd.ell();
+        if constexpr (AHEAD) read_ops(st, rell, ops);
         rd.next();
     };
     auto bar = [] {  // the compute waves' LDS traffic is all a barrier waits for
         wait_lgkmcnt0();
         asm volatile("s_barrier" ::: "memory");
+    };
+    // A form: fragment of lane ln in block b of the B Y exchange buffer (A's operand type)
+    auto xfb = [&](int b, int ln) -> Frag<PT>& {
+        return *reinterpret_cast<Frag<PT>*>(LB + b * SS::XBLK + ln * (int)sizeof(Frag<PT>) + (ln >> 4) * SS::XPAD);
+    };
+    // A form: the four compute waves alone meet between the two products of a
+    // step (the other waves have no part in B Y, and a workgroup barrier would
+    // make the serial chain wait for them).  A wave writes its B Y fragments,
+    // waits for the writes to complete, then writes its step number into its
+    // flag word; a reader waits until all four flags show the step before it
+    // reads the fragments.  The wait is bounded; it always ends well before the
+    // bound, since all four waves reach this point after the same barrier B1
+    // with nothing else to wait for.
+    if (w == 0 && lane < 4) csync[lane] = 0;  // published by B0
+    const unsigned flag_addr = lds_addr(&csync[w]), flags_addr = lds_addr(&csync[0]);
+    auto sync4 = [&](int target) {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\tds_write_b32 %0, %1" ::"v"(flag_addr), "v"(target) : "memory");
+        for (int it = 0; it < (1 << 20); ++it) {
+            u32x4 fl;
+            asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(fl) : "v"(flags_addr) : "memory");
+            const int mn = min(min((int)fl[0], (int)fl[1]), min((int)fl[2], (int)fl[3]));
+            if (__builtin_amdgcn_readfirstlane(mn) >= target) break;
+        }
     };
     bar();  // B0: stages 0 and 1 ready
     if (nch > 0) read_stage(0);
@@ -1376,25 +1603,58 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO>::WAVES)) void chunk_
         const int n = tab.order[k];
         const int nc = tab.choff[n + 1] - tab.choff[n];
         for (int j = 0; j < nc; ++j, ++c) {
-            bar();  // B1(c): -S in LS; chunk c's stage may be refilled
-            Frag<T> sb[CT][KS];
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) sb[ct][ks] = xf(LS, ks * CT + ct, lane);
-            // X = U - W S for positions 16 w .. 16 w + 15 (one independent chain per column tile)
+            bar();  // B1(c): -S in LS; the first half of chunk c's stage may be refilled
+            if constexpr (!AHEAD) read_ops(smem + (c % NST) * SS::BYTES, rell, ops);
+            const float gl = ops.gl;
+            const float4 fx = ops.fx;
             f32x4 X[CT];
+            if constexpr (AF) {
+                const Frag<PT> a0 = ops.a0, a1 = ops.a1;
+                const f32x4 b4 = f32x4{ops.fb.x, ops.fb.y, ops.fb.z, ops.fb.w};
+                const f32x4 bg4 = f32x4{ops.fbg.x, ops.fbg.y, ops.fbg.z, ops.fbg.w};
+                // B Y = B (V - Gamma K S) for positions 16 w .. 16 w + 15: LS holds -S,
+                // so the product is -(K S) (one independent chain per column tile)
+                f32x4 Y[CT];
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) X[ct] = raw4_to_f32(uf[ct]);
+                for (int ct = 0; ct < CT; ++ct) Y[ct] = zero4();
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+                for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) X[ct] = mma(wf[ks], sb[ct][ks], X[ct]);
+                    for (int ct = 0; ct < CT; ++ct) Y[ct] = mma(kr[ks], xf(LS, ks * CT + ct, lane), Y[ct]);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const f32x4 v4 = AHEAD ? ops.v[ct]
+                                           : v_acc4<T>(smem + (c % NST) * SS::BYTES + SS::V_OFF + ct * SS::V1_BYTES,
+                                                       16 * w + 4 * grp, lane);
+                    // beta v + (beta gamma) (-K S), as one rounding of beta v and one
+                    // fused multiply-add (fixed, so every work split rounds alike)
+                    f32x4 by;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) by[i] = __builtin_fmaf(bg4[i], Y[ct][i], b4[i] * v4[i]);
+                    lds_put4(xfb((w >> 1) * CT + ct, lane), w & 1, by, 1.f);
+                }
+                // X = A (B Y) for positions 16 w .. 16 w + 15 (A is lower triangular:
+                // row tiles 0 and 1 see positions < 32 only)
+                sync4(c + 1);  // Bm(c): all of B Y in LB
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    X[ct] = mma(a0, xfb(ct, lane), zero4());
+                    if (w >= 2) X[ct] = mma(a1, xfb(CT + ct, lane), X[ct]);
+                }
+            } else {
+                // X = U - W S for positions 16 w .. 16 w + 15 (one independent chain per column tile)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) X[ct] = raw4_to_f32(ops.u[ct]);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) X[ct] = mma(kr[ks], xf(LS, ks * CT + ct, lane), X[ct]);
+            }
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
                 lds_put4(xf(LX, (w >> 1) * CT + ct, lane), w & 1, X[ct], 1.f);
-                const f32x4 Y = f32x4{X[ct][0] * fx.x, X[ct][1] * fx.y, X[ct][2] * fx.z, X[ct][3] * fx.w};
-                lds_put4(xf(LY, (w >> 1) * CT + ct, lane), w & 1, Y, 1.f);
+                const f32x4 Yk = f32x4{X[ct][0] * fx.x, X[ct][1] * fx.y, X[ct][2] * fx.z, X[ct][3] * fx.w};
+                lds_put4(xf(LY, (w >> 1) * CT + ct, lane), w & 1, Yk, 1.f);
             }
             const float eg = __expf(gl);
 #pragma unroll
@@ -1519,7 +1779,7 @@ __global__ __launch_bounds__(256) void chunk_output_o_kernel(const ChunkParams p
         *reinterpret_cast<float4*>(&s.Q[r][c]) = qv;
         *reinterpret_cast<float4*>(&s.u.K[r][c]) = kv;
     }
-    if (tid < CHUNK) s.gc[tid] = p.gc[ch * CHUNK + tid];
+    if (tid < CHUNK) s.gc[tid] = p.gates[ch * 4 * CHUNK + tid];
     lds_sync();
     // This wave's operand fragments of H^T and (U - W S)^T (rows d_v), straight to
     // registers; issued after the Q/K staging (needed first, by the P tiles), so
@@ -1898,6 +2158,10 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
     // above 128 MiB of stream.
     ChunkParams pl = p;
     pl.l2_prefetch = (size_t)work_ch * StateStage<T, D>::BYTES > (size_t(128) << 20) ? 1 : 0;
+    // The form of the chunk's operands the state scan reads (decided by the
+    // host from the call's sequence count; fp32 always W and U).
+    const bool af = sizeof(T) == 2 && p.aform;
+    pl.write_af = af ? 1 : 0;
     // chunk_prep: with few items a slot, as many workgroups as fit on the chip at
     // once (four per CU), each looping over its items and prefetching the next
     // one (T = 4096, two items a slot: 36 against 38 us with one workgroup an
@@ -1912,23 +2176,36 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
     constexpr bool FO = sizeof(T) == 2;
     auto run = [&](auto dev) {
         constexpr bool DEV = decltype(dev)::value;
-        if (work_ch > 0) launch(0, chunk_prep_kernel<T, D, DEV>, prep_grid, 256, grid_ch, pl);
+        if (work_ch > 0) {
+            if (!af || p.keep_wu)
+                launch(0, chunk_prep_kernel<T, D, DEV, true>, prep_grid, 256, grid_ch, pl);
+            else
+                launch(0, chunk_prep_kernel<T, D, DEV, false>, prep_grid, 256, grid_ch, pl);
+        }
         // grids: whole groups of workgroups on each XCD
-        auto state = [&](auto ctc) {
+        auto state = [&](auto ctc, auto afc) {
             constexpr int CT = decltype(ctc)::value;
+            constexpr bool AF = decltype(afc)::value;
             const int grid = pad8(groups) * (D / 16 / CT);
-            launch(1, chunk_state_h_kernel<T, D, DEV, CT, FO>, grid, 64 * StateStage<T, D, CT, FO>::WAVES, grid, pl);
+            launch(1, chunk_state_h_kernel<T, D, DEV, CT, FO, AF>, grid, 64 * StateStage<T, D, CT, FO, AF>::WAVES, grid,
+                   pl);
+        };
+        auto state_ct = [&](auto afc) {
+            if (ct == 4)
+                state(std::integral_constant<int, 4>{}, afc);
+            else if (ct == 2)
+                state(std::integral_constant<int, 2>{}, afc);
+            else
+                state(std::integral_constant<int, 1>{}, afc);
         };
         if (groups > 0) {
             if constexpr (sizeof(T) == 2) {
-                if (ct == 4)
-                    state(std::integral_constant<int, 4>{});
-                else if (ct == 2)
-                    state(std::integral_constant<int, 2>{});
+                if (af)
+                    state_ct(std::true_type{});
                 else
-                    state(std::integral_constant<int, 1>{});
+                    state_ct(std::false_type{});
             } else {
-                state(std::integral_constant<int, 1>{});
+                state(std::integral_constant<int, 1>{}, std::false_type{});
             }
         }
         if (work_ch > 0) {

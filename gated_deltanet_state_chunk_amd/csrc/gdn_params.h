@@ -44,12 +44,12 @@ struct ChunkParams {
     void* out;
     float* sfinal;  // may be null
     // workspace regions
-    float* gc;
-    void* A;
-    void* W;
-    void* Ut;
-    float* kf;  // per (chunk, value head, position): factor of the state update's keys
-    void* Kc;   // per (chunk, key head): the chunk's key rows for the state update
+    float* gates;  // per (chunk, value head): [4][64] fp32 rows gc, kf = gamma_l / gamma, beta, beta gamma
+    void* A;       // per (chunk, value head): A row-major, only under keep_A
+    void* Af;      // per (chunk, value head): the six A fragments the state scan multiplies B Y by
+    void* W;       // per (chunk, value head): W = A B Gamma K, only under keep_wu
+    void* Ut;      // per (chunk, value head): U = A B V, only under keep_wu
+    void* Kc;      // per (chunk, key head): the chunk's key rows for the state scan
     void* Ht;
     void* Xt;
     void* Pf;   // per (chunk, value head): P as the output's B operands (bf16; null: P not formed)
@@ -57,6 +57,9 @@ struct ChunkParams {
     int32_t H_q, H_v, G;
     float scale;
     int32_t keep_A;  // nonzero: chunk_prep also writes A to the workspace
+    int32_t keep_wu;  // nonzero: chunk_prep also forms W and U and writes them to the workspace
+    int32_t write_af;  // nonzero: chunk_prep forming W and U also writes A's fragments (set by the launcher)
+    int32_t aform;     // nonzero (bf16): the state scan forms X from A and the raw rows instead of W and U
     int32_t keep_hx;  // nonzero: the state scan writes Ht, Xt even where the output is formed on chip
     int32_t T;       // tokens of the whole batch (bounds the gated read-out's rows on the device-table path)
     int32_t l2_prefetch;  // nonzero: chunk_state_h prefetches W / K into L2 (set by the launcher)

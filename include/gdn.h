@@ -124,7 +124,7 @@ typedef struct ihipStream_t *hipStream_t;
  */
 typedef struct gdn_workspace_layout {
     int64_t n_chunks;
-    size_t off_gc, off_A, off_W, off_U, off_kf, off_Kc, off_Ht, off_Xt, off_P, off_Qc; /* byte offsets */
+    size_t off_gates, off_A, off_Af, off_W, off_U, off_Kc, off_Ht, off_Xt, off_P, off_Qc; /* byte offsets */
     size_t total_bytes;
 } gdn_workspace_layout;
 
@@ -196,6 +196,9 @@ typedef struct gdn_output_gate {
 #define GDN_FWD_SCAN_CT1 4u  /* bf16: the state scan takes 1 / 2 / 4 sixteen-column tiles of d_v a */
 #define GDN_FWD_SCAN_CT2 8u  /* workgroup, with as many bins of sequences as fit on the chip at that */
 #define GDN_FWD_SCAN_CT4 16u /* width, instead of the width the host's cost model picks (at most one) */
+#define GDN_FWD_KEEP_WU 32u  /* also form W and U and write them to their regions where the scan does not read them */
+#define GDN_FWD_FORM_W 64u   /* bf16: the state scan reads W and U (X = U - W S), whatever the batch; */
+#define GDN_FWD_FORM_A 128u  /* or A and the raw rows (X = A B (V - Gamma K S)); at most one (see gdn_chunk_fwd_ex) */
 
 /*
  * gdn_chunk_fwd with options, for inspection, profiling and benchmarks.  Same

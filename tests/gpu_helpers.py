@@ -59,6 +59,24 @@ def frag_w_to_logical(flat, d_k):
     return flat[..., off]
 
 
+# A's fragments as the state scan reads them: (row tile t, K-step s) in this order
+A_FRAG_TILES = [(0, 0), (1, 0), (2, 0), (2, 1), (3, 0), (3, 1)]
+
+
+def a_frags_to_logical(flat):
+    """A [..., 6*64*8] as six fragments (t, s) of A_FRAG_TILES, lane 16 a + r, slot
+    4 h + b holding A[16 t + r][32 s + 16 h + 4 a + b] -> [..., 64, 64] (zero
+    where no fragment is stored: the blocks above the diagonal)."""
+    out = np.zeros(flat.shape[:-1] + (64, 64), dtype=flat.dtype)
+    for f, (t, s) in enumerate(A_FRAG_TILES):
+        for lane in range(64):
+            a, r = lane // 16, lane % 16
+            for h in range(2):
+                for b in range(4):
+                    out[..., 16 * t + r, 32 * s + 16 * h + 4 * a + b] = flat[..., (f * 64 + lane) * 8 + 4 * h + b]
+    return out
+
+
 def frag_rows_to_logical(flat, rows, cols):
     """[..., rows*cols] in the row-operand fragment order of Ht / Xt (block (row/16,
     col/32), lane 16 ((col%32)/8) + row%16, slot col%8) -> [..., rows, cols]."""
@@ -77,7 +95,7 @@ def frag_u_to_logical(flat, d_v):
 
 
 def chunk_fwd_device(inp, device="cuda", initial_state="from_inputs", return_ws=False, keep_A=False, keep_hx=False,
-                     scan_ct=None):
+                     scan_ct=None, keep_wu=False, form=None):
     """Run gdn_chunk_fwd on seeded inputs; returns (out, final, workspace-or-None) as host arrays / tensor."""
     import torch
 
@@ -94,7 +112,7 @@ def chunk_fwd_device(inp, device="cuda", initial_state="from_inputs", return_ws=
     ws = torch.empty(max(gdn.workspace_size(inp.T, inp.cu_seqlens, inp.H_q, inp.H_v, inp.d_k, inp.d_v,
                                             inp.dtype), 1), dtype=torch.uint8, device=device)
     out, fin = gdn.chunk_fwd(q, k, v, g, beta, inp.cu_seqlens, initial_state=s0, scale=inp.scale, workspace=ws,
-                             keep_A=keep_A, keep_hx=keep_hx, scan_ct=scan_ct)
+                             keep_A=keep_A, keep_hx=keep_hx, scan_ct=scan_ct, keep_wu=keep_wu, form=form)
     torch.cuda.synchronize()
     res = (to_host(out), to_host(fin))
     if return_ws:

@@ -102,20 +102,22 @@ def _cu(vals):
 def test_workspace_layout(gdn):
     lay = gdn.workspace_layout(4096, [0, 4096], 16, 32, 128, 128, "bf16")
     assert lay["n_chunks"] == 64
-    offs = [lay[k] for k in ("off_gc", "off_A", "off_W", "off_U", "off_kf", "off_Kc", "off_Ht", "off_Xt",
-                             "off_P", "off_Qc", "total_bytes")]
+    offs = [lay[k] for k in ("off_gates", "off_A", "off_W", "off_U", "off_Kc", "off_Ht", "off_Xt", "off_P",
+                             "off_Qc", "off_Af", "total_bytes")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     chv = 64 * 32
-    assert lay["off_A"] - lay["off_gc"] == chv * 64 * 4
-    assert lay["off_Kc"] - lay["off_kf"] == chv * 64 * 4
+    assert lay["off_A"] - lay["off_gates"] == chv * 4 * 64 * 4      # gc, kf, beta, beta gamma (fp32)
+    assert lay["off_W"] - lay["off_A"] == chv * 64 * 64 * 2
+    assert lay["off_Kc"] - lay["off_U"] == chv * 128 * 64 * 2
+    assert lay["total_bytes"] - lay["off_Af"] == chv * 6 * 64 * 8 * 2  # A's six fragments (binary16)
     assert lay["off_Ht"] - lay["off_Kc"] == 64 * 16 * 64 * 128 * 2  # chunks x key heads x rows x d_k
     assert lay["off_Xt"] - lay["off_Ht"] == chv * 128 * 128 * 2
     assert lay["off_Qc"] - lay["off_P"] == chv * 6 * 1024            # P: six 1 KiB fragments (bf16)
-    assert lay["total_bytes"] - lay["off_Qc"] == 64 * 16 * 64 * 128 * 2  # Qc: as Kc
+    assert lay["off_Af"] - lay["off_Qc"] == 64 * 16 * 64 * 128 * 2  # Qc: as Kc
     # chunks are counted per sequence: ceil(100/64) + 0 + ceil(1/64) + ceil(128/64)
     lay2 = gdn.workspace_layout(229, [0, 100, 100, 101, 229], 2, 4, 64, 64, "f32")
     assert lay2["n_chunks"] == 2 + 0 + 1 + 2
-    assert lay2["total_bytes"] == lay2["off_P"] == lay2["off_Qc"]     # no P or Qc region for fp32
+    assert lay2["off_Af"] == lay2["off_P"] == lay2["off_Qc"]          # no P or Qc region for fp32
     assert gdn.workspace_size(0, [0], 2, 4, 64, 64, "f32") >= 0
 
 
@@ -184,7 +186,11 @@ def test_chunk_fwd_rejects_before_any_device_work(gdn):
                                     a["fin"], a["T"], a["H_q"], a["H_v"], a["dk"], a["dv"], a["scale"], a["dt"],
                                     a["ws"], a["wsb"], a["stream"], flags, None, None)
 
-    assert call_ex(32) == -1                   # unknown flag bit
+    assert call_ex(256) == -1                  # unknown flag bit
+    assert call_ex(gdn.FWD_FORM["W"] | gdn.FWD_FORM["A"]) == -1  # both forms
+    assert call_ex(gdn.FWD_FORM["A"], N=0, T=0, cu=_cu([0])) == 0
+    assert call_ex(gdn.FWD_KEEP_WU, q=None) == -1
+    assert call_ex(gdn.FWD_KEEP_WU, N=0, T=0, cu=_cu([0])) == 0
     assert call_ex(gdn.FWD_SCAN_CT[1] | gdn.FWD_SCAN_CT[2]) == -1  # two tile widths
     assert call_ex(gdn.FWD_SCAN_CT[4], q=None) == -1
     assert call_ex(gdn.FWD_SCAN_CT[2], N=0, T=0, cu=_cu([0])) == 0

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import gdn_inputs
-from tests.gpu_helpers import (chunk_fwd_device, f32_dev, frag_rows_to_logical, frag_u_to_logical, frag_w_to_logical,
+from tests.gpu_helpers import (a_frags_to_logical, chunk_fwd_device, f32_dev, frag_rows_to_logical, frag_u_to_logical, frag_w_to_logical,
                                rel_err, to_dev, to_host, unperm32)
 
 pytestmark = pytest.mark.gpu
@@ -140,9 +140,10 @@ def test_prefill_then_decode_continues(torch_cuda, oracle_mod):
     assert rel_err(to_host(fin_pre), to_host(fin_all)) < 1e-5
 
 
-def test_a_region_untouched_without_keep_a(torch_cuda):
-    """gdn_chunk_fwd leaves the A region as it was; gdn_chunk_fwd_ex with
-    GDN_FWD_KEEP_A fills it, and both give the same outputs."""
+def test_inspection_regions_untouched_without_flags(torch_cuda):
+    """The A region is written only under GDN_FWD_KEEP_A; W and U only where the
+    scan reads them (the W form) or under GDN_FWD_KEEP_WU; A's fragments only in
+    the A form.  The flags never change the outputs."""
     import torch
 
     import gated_deltanet_state_chunk_amd as gdn
@@ -150,24 +151,38 @@ def test_a_region_untouched_without_keep_a(torch_cuda):
     inp = gdn_inputs.make_prefill(seed=12, seqlens=[70, 64], H_q=1, H_v=2, d_k=64, d_v=64, dtype="bf16")
     lay = gdn.workspace_layout(inp.T, inp.cu_seqlens, 1, 2, 64, 64, "bf16")
     a0, a1 = lay["off_A"], lay["off_W"]
+    f0, f1 = lay["off_Af"], lay["total_bytes"]
+    w0, w1 = lay["off_W"], lay["off_Kc"]
+    assert a1 > a0 and f1 > f0 and w1 > w0
     args = [to_dev(inp.q, "bf16"), to_dev(inp.k, "bf16"), to_dev(inp.v, "bf16"), f32_dev(inp.g), f32_dev(inp.beta),
             inp.cu_seqlens]
-    ws = torch.full((lay["total_bytes"],), 0xA5, dtype=torch.uint8, device="cuda")
-    out0, fin0 = gdn.chunk_fwd(*args, scale=inp.scale, workspace=ws)
-    torch.cuda.synchronize()
-    assert bool((ws[a0:a1] == 0xA5).all())
-    out1, fin1 = gdn.chunk_fwd(*args, scale=inp.scale, workspace=ws, keep_A=True)
-    torch.cuda.synchronize()
-    assert not bool((ws[a0:a1] == 0xA5).all())
-    assert torch.equal(out0, out1) and torch.equal(fin0, fin1)
+
+    def run(**kw):
+        ws = torch.full((lay["total_bytes"],), 0xA5, dtype=torch.uint8, device="cuda")
+        out, fin = gdn.chunk_fwd(*args, scale=inp.scale, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        untouched = [bool((ws[lo:hi] == 0xA5).all()) for lo, hi in ((a0, a1), (f0, f1), (w0, w1))]
+        return out, fin, untouched
+
+    ow, fw, u = run(form="W")
+    assert u == [True, True, False]        # W and U are the scan's operands
+    ow2, fw2, u = run(form="W", keep_A=True)
+    assert u == [False, True, False]
+    oa, fa, u = run(form="A")
+    assert u == [True, False, True]        # A's fragments are the scan's operands
+    oa2, fa2, u = run(form="A", keep_A=True, keep_wu=True)
+    assert u == [False, False, False]
+    assert torch.equal(ow, ow2) and torch.equal(fw, fw2)
+    assert torch.equal(oa, oa2) and torch.equal(fa, fa2)
+    assert rel_err(to_host(oa), to_host(ow)) < 1e-2 and rel_err(to_host(fa), to_host(fw)) < 1e-2
 
 
 # ---------------------------------------------------------------------------
 # Per-stage intermediates against the chunk-form oracle
 # ---------------------------------------------------------------------------
-def _x_bound(r, inp, n, h, c, d, dtype, tol_h):
+def _x_bound_w(r, inp, n, h, c, d, dtype, tol_h):
     """Worst-case error of the stored X = U - W S of one chunk, relative to max|X|,
-    from the roundings on its path: the A and B V (B Gamma K) operands of U (W),
+    along the W form's path: the A and B V (B Gamma K) operands of U (W),
     U and W themselves, the S operand, X itself (unit u each: 2^-9 for bf16,
     2^-24 for fp32), fp32 accumulation over the 64 positions or d_k rows
     (2^-24 per term), and the chunk-start state's own error, taken at the
@@ -190,15 +205,49 @@ def _x_bound(r, inp, n, h, c, d, dtype, tol_h):
     return float(dX.max() / X.max())
 
 
-@pytest.mark.parametrize("dtype,d,tol", [("f32", 64, 1e-4), ("bf16", 128, 1e-2)])
-def test_chunk_intermediates_match_chunk_form(torch_cuda, dtype, d, tol):
+def _x_bound_a(r, inp, n, h, c, d, dtype, tol_h):
+    """Worst-case error of the stored X = U - W S of one chunk, relative to max|X|,
+    from the roundings along the A form's path, X = A (B (V - Gamma K S)):
+    the chunk-start state S as an MFMA operand (unit u: 2^-9 for bf16, 2^-24
+    for fp32) and its own error, taken at the tolerance h is held to (tol_h
+    max|h|); fp32 accumulation over d_k rows and 64 positions (2^-24 per term);
+    B Y and A rounded to the product type (binary16 for bf16 inputs: 2^-11;
+    fp32 otherwise); X itself rounded to the input type.  K and V enter exactly
+    (they are the inputs).  Each product term is bounded by the sums of |a| |b|
+    (no cancellation assumed), so this is a bound, not an estimate; it depends
+    on the inputs and the fp64 chunk form, not on the device result."""
+    u = 2.0 ** -9 if dtype == "bf16" else 2.0 ** -24
+    up = 2.0 ** -11 if dtype == "bf16" else 2.0 ** -24
+    ua = 2.0 ** -24
+    ell = r["X"].shape[0]
+    t0 = int(inp.cu_seqlens[n]) + 64 * c
+    hq = h // (inp.H_v // inp.H_q)
+    V = inp.v32()[t0:t0 + ell, h].astype(np.float64)
+    K = inp.k32()[t0:t0 + ell, hq].astype(np.float64)
+    b = inp.beta[t0:t0 + ell, h].astype(np.float64)
+    gam = np.exp(r["gc"])
+    A, S, X = np.abs(r["A"]), r["h"], np.abs(r["X"])
+    BY = np.abs(b[:, None] * (V - gam[:, None] * (K @ S)))
+    dS = (u + d * ua) * np.abs(S) + tol_h * np.abs(S).max()
+    dBY = b[:, None] * gam[:, None] * (np.abs(K) @ dS) + up * BY
+    dX = A @ dBY + (up + 64 * ua) * (A @ BY) + u * X
+    return float(dX.max() / X.max())
+
+
+@pytest.mark.parametrize("dtype,d,tol,form", [("f32", 64, 1e-4, "W"), ("bf16", 128, 1e-2, "W"),
+                                              ("bf16", 128, 1e-2, "A")])
+def test_chunk_intermediates_match_chunk_form(torch_cuda, dtype, d, tol, form):
+    """Every workspace intermediate against the fp64 chunk form, in both forms
+    of the state scan's operands (W and U; A and the raw rows, with W and U
+    written for inspection)."""
     import gated_deltanet_state_chunk_amd as gdn
     from oracle import chunk_form
 
     lens = [100, 64, 30]
     H_q, H_v = 1, 2
     inp = gdn_inputs.make_prefill(seed=9, seqlens=lens, H_q=H_q, H_v=H_v, d_k=d, d_v=d, dtype=dtype)
-    _, _, ws = chunk_fwd_device(inp, return_ws=True, keep_A=True, keep_hx=True)
+    _, _, ws = chunk_fwd_device(inp, return_ws=True, keep_A=True, keep_hx=True, keep_wu=True,
+                                form=None if dtype == "f32" else form)
     lay = gdn.workspace_layout(inp.T, inp.cu_seqlens, H_q, H_v, d, d, dtype)
     nc = lay["n_chunks"]
     assert nc == 2 + 1 + 1
@@ -214,11 +263,12 @@ def test_chunk_intermediates_match_chunk_form(torch_cuda, dtype, d, tol):
             t = raw.view(torch.float16) if half else raw.view(torch.bfloat16)
         return t.float().cpu().numpy().astype(np.float64).reshape(shape)
 
-    gc = region(lay["off_gc"], (nc, H_v, 64), is_f32=True)
+    gates = region(lay["off_gates"], (nc, H_v, 4, 64), is_f32=True)
+    gc, kf, gb, gbg = gates[:, :, 0], gates[:, :, 1], gates[:, :, 2], gates[:, :, 3]
     A = region(lay["off_A"], (nc, H_v, 64, 64))
     W = frag_w_to_logical(region(lay["off_W"], (nc, H_v, 64 * d)), d)
     U = frag_u_to_logical(region(lay["off_U"], (nc, H_v, 64 * d), half=True), d)
-    kf = region(lay["off_kf"], (nc, H_v, 64), is_f32=True)
+    Af = a_frags_to_logical(region(lay["off_Af"], (nc, H_v, 6 * 64 * 8), half=True))
     # Kc: each row's 16-byte pieces stored permuted (piece i at i ^ p(r), as include/gdn.h states)
     es = 4 if dtype == "f32" else 2
     P = d * es // 16
@@ -248,11 +298,21 @@ def test_chunk_intermediates_match_chunk_form(torch_cuda, dtype, d, tol):
                 assert np.all(gc[ci, h, ell:] == 0)
                 assert rel_err(A[ci, h, :ell, :ell], r["A"]) < tol
                 assert np.all(A[ci, h, ell:, :] == 0) and np.all(A[ci, h, :, ell:] == 0)
+                if form == "A":  # the state scan's fragments of A: the same lower triangle
+                    # (in the product type), unit rows past the valid length, zeros above
+                    assert rel_err(Af[ci, h, :ell, :ell], r["A"]) < tol
+                    assert np.array_equal(Af[ci, h, ell:, :], np.eye(64)[ell:])
+                    assert np.all(np.triu(Af[ci, h], 1) == 0)
+                # gate block: beta as given (zero past the valid length), beta gamma
+                b_in = inp.beta[t0:t0 + ell, h].astype(np.float64)
+                assert np.array_equal(gb[ci, h, :ell], b_in) and np.all(gb[ci, h, ell:] == 0)
+                assert rel_err(gbg[ci, h, :ell], b_in * np.exp(r["gc"])) < 1e-5
+                assert np.all(gbg[ci, h, ell:] == 0)
                 assert rel_err(W[ci, h, :ell], r["W"]) < tol
                 assert rel_err(U[ci, h, :ell], r["U"]) < tol
                 assert rel_err(Hs[ci, h], r["h"]) < tol
-                x_tol = max(tol, _x_bound(r, inp, n, h, c, d, dtype, tol)) if dtype == "f32" else \
-                    _x_bound(r, inp, n, h, c, d, dtype, tol)
+                xb = (_x_bound_w if form == "W" else _x_bound_a)(r, inp, n, h, c, d, dtype, tol)
+                x_tol = max(tol, xb) if dtype == "f32" else xb
                 assert rel_err(X[ci, h, :ell], r["X"]) < x_tol, (n, h, c, x_tol)
                 assert np.all(W[ci, h, ell:] == 0) and np.all(X[ci, h, ell:] == 0)
                 # keys of the state update carry the decay to the chunk end: gamma_l / gamma_r

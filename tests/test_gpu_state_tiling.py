@@ -4,9 +4,12 @@ another.  The host picks both from the chunk counts (on a 256-CU part: one
 sequence of 4 chunks x 32 heads -> one tile a workgroup; 4 + 3 chunks -> two
 tiles, one sequence a bin; 4 + 3 + 2 + 1 + 2 chunks -> four tiles, four bins,
 one of them two sequences), checked on bf16 d = 128 with ragged lengths
-against the fp64 oracle on every head.  Every split runs the same MFMAs in
-the same order for a sequence, so the results must also agree bitwise across
-them (the same head, same tokens, in batches of different sizes).
+against the fp64 oracle on every head.  The scan reads either the chunk's W
+and U (X = U - W S) or A and the raw rows (X = A B (V - Gamma K S)); within a
+form every split runs the same MFMAs in the same order for a sequence, so the
+results must also agree bitwise across them (the same head, same tokens, in
+batches of different sizes), and across the two forms within the rounding of
+their different products.
 """
 import dataclasses
 
@@ -41,10 +44,11 @@ def test_state_scan_tiling_matches_oracle(torch_cuda, oracle_mod, lens):
     assert rel_err(fin, ref_s) < 1e-2
 
 
-def test_state_scan_tiling_bitwise_consistent(torch_cuda):
+@pytest.mark.parametrize("form", ["W", "A"])
+def test_state_scan_tiling_bitwise_consistent(torch_cuda, form):
     """The first sequence alone (one tile a CU), with one more (two), and with
-    four more (four tiles a workgroup): its outputs and final state agree bit
-    for bit."""
+    four more (four tiles a workgroup), in one form of the scan's operands:
+    its outputs and final state agree bit for bit."""
     full = gdn_inputs.make_prefill(seed=701, seqlens=[197, 130, 65, 1, 100], H_q=16, H_v=32, d_k=128, d_v=128,
                                    dtype="bf16", state_std=0.02)
     res = []
@@ -52,10 +56,20 @@ def test_state_scan_tiling_bitwise_consistent(torch_cuda):
         t = int(full.cu_seqlens[n])
         sub = dataclasses.replace(full, q=full.q[:t], k=full.k[:t], v=full.v[:t], g=full.g[:t], beta=full.beta[:t],
                                   cu_seqlens=full.cu_seqlens[:n + 1], initial_state=full.initial_state[:n])
-        out, fin = chunk_fwd_device(sub)
+        out, fin = chunk_fwd_device(sub, form=form)
         res.append((out[:197], fin[0]))
     for o, f in res[1:]:
         assert np.array_equal(o, res[0][0]) and np.array_equal(f, res[0][1])
+
+
+def test_state_scan_forms_agree(torch_cuda):
+    """The two forms of the scan's operands on one batch: within the rounding of
+    their different products (each is held to the oracle elsewhere)."""
+    inp = gdn_inputs.make_prefill(seed=704, seqlens=[197, 130, 65, 1, 100], H_q=16, H_v=32, d_k=128, d_v=128,
+                                  dtype="bf16", state_std=0.02)
+    ow, fw = chunk_fwd_device(inp, form="W")
+    oa, fa = chunk_fwd_device(inp, form="A")
+    assert rel_err(oa, ow) < 1e-2 and rel_err(fa, fw) < 1e-2
 
 
 @pytest.mark.parametrize("n_seq,d", [(8, 128), (40, 128), (40, 64)])
@@ -80,24 +94,26 @@ def test_state_scan_every_width_bins_bitwise(torch_cuda, oracle_mod, d):
     (H_v = 4, d = 128: 8 / 16 / 32 bins; d = 64: 16 / 32 / 40), so 40 ragged
     sequences, some empty, make bins of several sequences at every width,
     including the widths whose three-stage ring reads the next chunk's stage
-    half a step early, across sequence changes.  The three results agree bit
-    for bit, and match the oracle on every head."""
+    half a step early, across sequence changes.  In each form of the scan's
+    operands the three results agree bit for bit and match the oracle on every
+    head."""
     lens = [int(x) for x in np.random.default_rng(710 + d).integers(0, 300, 40)]
     for i in (3, 17, 39):
         lens[i] = 0
     inp = gdn_inputs.make_prefill(seed=711 + d, seqlens=lens, H_q=2, H_v=4, d_k=d, d_v=d, dtype="bf16",
                                   state_std=0.02)
-    res = {}
-    for ct in (1, 2, 4):
-        print(f"[widths] d={d} scan_ct={ct} T={inp.T}", flush=True)
-        res[ct] = chunk_fwd_device(inp, scan_ct=ct)
-    for ct in (2, 4):
-        assert np.array_equal(res[ct][0], res[1][0]), ct
-        assert np.array_equal(res[ct][1], res[1][1]), ct
     ref_o, ref_s = oracle_mod.forward(inp.q32(), inp.k32(), inp.v32(), inp.g, inp.beta, inp.cu_seqlens, 2, 4,
                                       inp.scale, initial_state=inp.initial_state.astype(np.float64))
-    assert rel_err(res[1][0], ref_o) < 1e-2
-    assert rel_err(res[1][1], ref_s) < 1e-2
+    for form in ("W", "A"):
+        res = {}
+        for ct in (1, 2, 4):
+            print(f"[widths] d={d} form={form} scan_ct={ct} T={inp.T}", flush=True)
+            res[ct] = chunk_fwd_device(inp, scan_ct=ct, form=form)
+        for ct in (2, 4):
+            assert np.array_equal(res[ct][0], res[1][0]), (form, ct)
+            assert np.array_equal(res[ct][1], res[1][1]), (form, ct)
+        assert rel_err(res[1][0], ref_o) < 1e-2, form
+        assert rel_err(res[1][1], ref_s) < 1e-2, form
 
 
 def test_state_scan_bins_short_sequences_pool_and_empties(torch_cuda, oracle_mod):
