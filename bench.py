@@ -62,21 +62,22 @@ CHUNK = 64
 # exploited)
 # ---------------------------------------------------------------------------
 
-def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True, gated=False):
+def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True, gated=False, form="W"):
     """Algorithmic bytes and flops of each kernel of one gdn_chunk_fwd.
 
     Bytes: every distinct input read once, every output and intermediate written
     once and read once per consuming kernel (K and Q are read once per key
     head).  chunk_prep writes, per (chunk, value head), the gate block (gc, kf,
-    beta, beta gamma) and A as six MFMA fragments, and once per key head the
-    key rows Kc; the state scan forms X = U - W S as A B (V - Gamma K S) from
-    those and the value rows, so W and U are never written.  bf16 (es = 2):
-    chunk_prep also forms P (the masked, decayed Q K^T, six 1 KiB fragments per
-    chunk and value head), the state scan forms the output from P, q and its
-    own on-chip h and X, and the gated read-out (when asked for) is a pass over
-    the output.  fp32: the chunk-start states h and X go through HBM to a
-    separate output kernel.  Flops: 2 x multiply-adds of the chunk form at full
-    chunks, triangles exploited.
+    beta, beta gamma) and, once per key head, the key rows Kc; then either
+    (form "W") W = A B Gamma K and U = A B V, which the state scan reads to
+    form X = U - W S, or (form "A") A as six MFMA fragments, from which with
+    the raw value rows the state scan forms X = A B (V - Gamma K S).  bf16 (es
+    = 2): chunk_prep also forms P (the masked, decayed Q K^T, six 1 KiB
+    fragments per chunk and value head), the state scan forms the output from
+    P, q and its own on-chip h and X, and the gated read-out (when asked for)
+    is a pass over the output.  fp32 (always form "W"): the chunk-start states
+    h and X go through HBM to a separate output kernel.  Flops: 2 x
+    multiply-adds of the chunk form at full chunks, triangles exploited.
     """
     C = CHUNK
     chv, chq = n_chunks * H_v, n_chunks * H_q
@@ -86,29 +87,37 @@ def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True, gated=False):
     G_b = chv * 4 * C * 4    # gate block per (chunk, value head)
     gc_b = chv * C * 4       # its gc row (what the fp32 output kernel reads)
     Af_b = chv * 6 * 64 * 8 * es  # A's six fragments
-    X_b = chv * C * d * es
+    W_b = U_b = X_b = chv * C * d * es
     Kc_b = chq * C * d * es  # the state scan's copy of the keys, one per key head
     H_b = chv * d * d * es
     S_b = N * H_v * d * d * 4
     P_b = chv * 6 * 1024
     tri = C * (C - 1) // 2   # strictly lower entries
     tri1 = C * (C + 1) // 2  # lower incl. diagonal
-    prep = tri * d + C ** 3 // 6                          # K K^T, solve
-    scan = 2 * C * d * d + tri1 * d                        # K S, A (B Y), Kc^T (kf X)
     s0 = S_b if has_s0 else 0
+    if form == "A":
+        prep = tri * d + C ** 3 // 6                       # K K^T, solve
+        scan = 2 * C * d * d + tri1 * d                     # K S, A (B Y), Kc^T (kf X)
+        prep_b = k_b + 2 * gate_b + G_b + Af_b + Kc_b
+        scan_b = Kc_b + Af_b + G_b + v_b
+    else:
+        prep = tri * d + C ** 3 // 6 + 2 * tri1 * d        # K K^T, solve, W, U
+        scan = 2 * C * d * d                                # W S, Kc^T (kf X)
+        prep_b = k_b + v_b + 2 * gate_b + G_b + W_b + U_b + Kc_b
+        scan_b = W_b + U_b + Kc_b + G_b
     if es == 2:
         per = {"chunk_prep": prep + tri1 * d,                              # + Q K^T
                "chunk_state_o": scan + C * d * d + tri1 * d,               # + Q S, P X
                "gated_readout": 0}
-        bytes_ = {"chunk_prep": k_b + 2 * gate_b + G_b + Af_b + Kc_b + q_b + P_b,
-                  "chunk_state_o": Kc_b + Af_b + G_b + v_b + P_b + q_b + s0 + S_b + o_b,
+        bytes_ = {"chunk_prep": prep_b + q_b + P_b,
+                  "chunk_state_o": scan_b + P_b + q_b + s0 + S_b + o_b,
                   "gated_readout": (3 * o_b + d * 4) if gated else 0}      # o read, z read, out written
     else:
         per = {"chunk_prep": prep,
                "chunk_state_h": scan,
                "chunk_output_o": C * d * d + 2 * tri1 * d}                 # Q S, Q K^T, P X
-        bytes_ = {"chunk_prep": k_b + 2 * gate_b + G_b + Af_b + Kc_b,
-                  "chunk_state_h": Kc_b + Af_b + G_b + v_b + s0 + H_b + X_b + S_b,
+        bytes_ = {"chunk_prep": prep_b,
+                  "chunk_state_h": scan_b + s0 + H_b + X_b + S_b,
                   "chunk_output_o": q_b + k_b + gc_b + H_b + X_b + o_b + ((o_b + d * 4) if gated else 0)}
     flops = {k: 2 * v * chv for k, v in per.items()}
     return bytes_, flops
@@ -340,10 +349,11 @@ def bench_prefill(args, torch, gdn, hip, device, gated=False):
     warm = stats(per_step_ms(hip, sptr, step, nstep))
     cold = stats(per_step_ms(hip, sptr, step, nstep, flush=CacheFlush(torch, gdn, device)))
     es = 2 if dt == "bf16" else 4
+    form = gdn.chunk_form(inp.T, inp.N, inp.H_v, inp.d_k, dt)
     bytes_, flops = prefill_work(inp.T, inp.N, lay["n_chunks"], inp.H_q, inp.H_v, inp.d_k, es,
-                                 has_s0=s0 is not None, gated=gated)
+                                 has_s0=s0 is not None, gated=gated, form=form)
     return dict(inp=inp, lay=lay, ms_step=ms_step, wall_s=wall, stage_ms=stage_ms, bytes=bytes_, flops=flops,
-                stages=STAGES, ms_step_with_events=timed_ms, warm=warm, cold=cold)
+                stages=STAGES, ms_step_with_events=timed_ms, warm=warm, cold=cold, form=form)
 
 
 def bench_prefill_serving(args, torch, gdn, device):
@@ -713,7 +723,8 @@ def main():
             "config": {"workload": args.workload, "seqlens": [int(x) for x in
                                                              (inp.cu_seqlens[1:] - inp.cu_seqlens[:-1])],
                        "T": inp.T, "H_q": inp.H_q, "H_v": inp.H_v, "d_k": inp.d_k, "d_v": inp.d_v,
-                       "chunk": CHUNK, "initial_state": inp.initial_state is not None},
+                       "chunk": CHUNK, "initial_state": inp.initial_state is not None,
+                       "scan_operands": pre["form"]},
             "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS,
                          "frac_of_achievable": achieved / hbm["gb_per_s"] if hbm else None,

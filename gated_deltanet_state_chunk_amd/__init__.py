@@ -16,7 +16,7 @@ import math
 import os
 from typing import Optional, Sequence
 
-__all__ = ["chunk_fwd", "chunk_fwd_scratch", "SCRATCH_BYTES", "recurrent_step", "recurrent_step_fused", "conv1d_silu", "conv1d_silu_step",
+__all__ = ["chunk_fwd", "chunk_form", "chunk_fwd_scratch", "SCRATCH_BYTES", "recurrent_step", "recurrent_step_fused", "conv1d_silu", "conv1d_silu_step",
            "chunk_fwd_fused", "chunk_fwd_dev", "chunk_fwd_pooled", "conv1d_silu_pooled", "recurrent_step_fused_pooled", "conv1d_silu_step_pooled",
            "state_rows_zero", "state_rows_copy", "stream_copy", "workspace_layout", "workspace_size", "lib_path", "load_library",
            "GdnError", "CHUNK", "DTYPE_F32", "DTYPE_BF16"]
@@ -138,6 +138,8 @@ def load_library():
     lib.gdn_chunk_fwd_workspace_layout.restype = ctypes.c_int
     lib.gdn_chunk_fwd_workspace_size.argtypes = [P, I32, I32, I32, I32, I32, ctypes.c_int]
     lib.gdn_chunk_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.gdn_chunk_fwd_form.argtypes = [I32, I32, I32, I32, ctypes.c_int]
+    lib.gdn_chunk_fwd_form.restype = ctypes.c_int
     lib.gdn_chunk_fwd.argtypes = [P, P, P, P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, F, ctypes.c_int, P,
                                   ctypes.c_size_t, P]
     lib.gdn_chunk_fwd.restype = ctypes.c_int
@@ -260,6 +262,15 @@ def _dtype_code_from(dtype) -> int:
     if dtype in (torch.float32, "f32"):
         return DTYPE_F32
     raise TypeError(f"unsupported dtype {dtype}")
+
+
+def chunk_form(T: int, num_seqs: int, H_v: int, d: int, dtype) -> str:
+    """Operand form the state scan of chunk_fwd takes for such a call: "W" (W and U)
+    or "A" (A and the raw rows); gdn_chunk_fwd_form."""
+    rc = load_library().gdn_chunk_fwd_form(T, num_seqs, H_v, d, _dtype_code_from(dtype))
+    if rc < 0:
+        raise GdnError(rc, "gdn_chunk_fwd_form")
+    return "A" if rc else "W"
 
 
 def workspace_size(T: int, cu_seqlens, H_q: int, H_v: int, d_k: int, d_v: int, dtype) -> int:

@@ -569,6 +569,12 @@ size_t gdn_chunk_fwd_workspace_size(const int32_t* cu_seqlens_host, int32_t num_
     return L.total_bytes;
 }
 
+int gdn_chunk_fwd_form(int32_t T, int32_t num_seqs, int32_t H_v, int32_t d, gdn_dtype dtype) {
+    if (T < 0 || num_seqs < 0 || H_v <= 0 || (d != 64 && d != 128)) return GDN_EINVAL;
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_EUNSUPPORTED;
+    return a_form(T, num_seqs, H_v, d, dtype, gdn::cu_count());
+}
+
 int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                   const int32_t* cu_seqlens_host, int32_t num_seqs, const float* initial_state, void* out,
                   float* final_state, int32_t T, int32_t H_q, int32_t H_v, int32_t d_k, int32_t d_v, float scale,

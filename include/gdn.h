@@ -71,33 +71,46 @@ typedef struct ihipStream_t *hipStream_t;
 
 /*
  * Workspace of gdn_chunk_fwd.  One region per intermediate of the chunk form
- * (section "计算过程描述": g^cumsum, A, W, U, the chunk-start states, U - W S),
- * each starting on a 256-byte boundary.  The intermediates stay in the
- * workspace after the call and may be read back for inspection; chunks are
- * numbered in sequence order, each sequence's chunks starting at its own first
- * token, so chunk c of sequence n has global index chunk_offset(n) + c where
- * chunk_offset(n) = sum_{m<n} ceil(L_m / 64).  Positions beyond a tail chunk's
- * valid length hold zeros.  W, U, Ht and Xt are kept in the order in which the
- * MFMA units consume them ("fragment order", 8 values per lane of a 64-lane
- * wave; for an index i let i = 32 s + 16 h + 4 a + b with a, b in 0..3):
+ * (section "计算过程描述": g^cumsum, A, W, U, the chunk-start states, U - W S)
+ * and per operand block the state scan reads, each starting on a 256-byte
+ * boundary.  The intermediates stay in the workspace after the call and may be
+ * read back for inspection; chunks are numbered in sequence order, each
+ * sequence's chunks starting at its own first token, so chunk c of sequence n
+ * has global index chunk_offset(n) + c where chunk_offset(n) = sum_{m<n}
+ * ceil(L_m / 64).  Positions beyond a tail chunk's valid length hold zeros.
+ *
+ * The state scan forms X = U - W S in one of two ways (gdn_chunk_fwd_form
+ * tells which for a call; gdn_chunk_fwd_ex can force either):
+ *   W form: chunk_prep writes W and U, and the scan reads them;
+ *   A form: chunk_prep writes A's fragments (Af) instead, and the scan forms
+ *           X = A B (V - Gamma K S) from them and the raw K and V rows, since
+ *           U - W S = A B V - A B Gamma K S.
+ * W and U are written in the W form, or with GDN_FWD_KEEP_WU; Af only in the A
+ * form; A only with GDN_FWD_KEEP_A.  Unwritten regions are left untouched.
+ *
+ * W, U, Af, Ht and Xt are kept in the order in which the MFMA units consume
+ * them ("fragment order", 8 values per lane of a 64-lane wave; for an index i
+ * let i = 32 s + 16 h + 4 a + b with a, b in 0..3):
  *   W   element (pos, k):  ((pos/16 * (d_k/32) + s(k)) * 64 + 16 a(k) + pos%16) * 8 + 4 h(k) + b(k)
  *   U   element (pos, j):  ((j/16 * 2 + pos/32) * 64 + 16 ((pos%16)/4) + j%16) * 8 + 4 ((pos/16)%2) + pos%4
+ *   Af  element (i, j), j <= i: fragment f of (row tile i/16, K-step j/32) in
+ *       the order (0,0), (1,0), (2,0), (2,1), (3,0), (3,1): (f * 64 + 16 a(j) + i%16) * 8 + 4 h(j) + b(j)
  * "perm32" means: within every block of 32 consecutive indices, index
  * 16 h + 4 a + b is stored at offset 8 a + 4 h + b.
  *
- *   gc  fp32  [n_chunks][H_v][64]            inclusive in-chunk cumsum of g
+ *   gates fp32 [n_chunks][H_v][4][64]        per position: the inclusive in-chunk cumsum of g
+ *                                            (gc), gamma_l / gamma (kf: the decay of a key to
+ *                                            the chunk end; the state update is
+ *                                            S <- gamma_l S + Kc^T Diag(kf) X), beta, and
+ *                                            beta gamma; all zero past the valid length
  *   A   dtype [n_chunks][H_v][64][64]        (I + StrictLower(B Gamma K K^T Gamma^-1))^-1,
  *                                            written only under GDN_FWD_KEEP_A (gdn_chunk_fwd_ex)
  *   W   dtype [n_chunks][H_v][64 * d_k]      A B Gamma K, fragment order
  *   U   utype [n_chunks][H_v][64 * d_v]      A B V, fragment order; utype is IEEE binary16
  *                                            for bf16 inputs (the same two bytes, three more
- *                                            mantissa bits; W and U are formed from binary16
+ *                                            mantissa bits; W, U and X are formed from binary16
  *                                            operands, so |beta v|, the entries of A and of U
  *                                            must stay below 65504), fp32 for fp32 inputs
- *   kf  fp32  [n_chunks][H_v][64]            gamma_l / gamma per position (the decay of a
- *                                            key to the chunk end), zero past the valid
- *                                            length: the state update is
- *                                            S <- gamma_l S + Kc^T Diag(kf) X
  *   Kc  dtype [n_chunks][H_q][64][d_k]       the chunk's key rows (L2-normalised with
  *                                            gdn_chunk_fwd_fused), the 16-byte pieces of row
  *                                            r permuted: piece i stored at i ^ p(r), where
@@ -118,13 +131,16 @@ typedef struct ihipStream_t *hipStream_t;
  *                                            chunk's L2-normalised query rows, zero past
  *                                            the valid length, the 16-byte pieces of row r
  *                                            permuted: piece i at i ^ (r mod P), P as for Kc
+ *   Af  utype [n_chunks][H_v][6][64][8]      A's fragments (above), A form only; rows past
+ *                                            the valid length are unit rows
  * For bf16 the chunk-start states and U - W S never leave the chip (the output
  * is formed inside the state scan): Ht and Xt are written only under
  * GDN_FWD_KEEP_HX (gdn_chunk_fwd_ex).
  */
 typedef struct gdn_workspace_layout {
     int64_t n_chunks;
-    size_t off_gates, off_A, off_Af, off_W, off_U, off_Kc, off_Ht, off_Xt, off_P, off_Qc; /* byte offsets */
+    size_t off_gates, off_A, off_Af, off_W, off_U, off_Kc, off_Ht, off_Xt, off_P, off_Qc; /* byte offsets
+                                                        (the regions lie in the order of the table above) */
     size_t total_bytes;
 } gdn_workspace_layout;
 
@@ -143,6 +159,17 @@ int gdn_chunk_fwd_workspace_layout(int32_t T, int32_t num_seqs, const int32_t *c
  * gdn_chunk_fwd_workspace_layout tells the two cases apart). */
 size_t gdn_chunk_fwd_workspace_size(const int32_t *cu_seqlens_host, int32_t num_seqs, int32_t H_q, int32_t H_v,
                                     int32_t d_k, int32_t d_v, gdn_dtype dtype);
+
+/*
+ * Host-only (it asks the HIP runtime for the current device's compute-unit
+ * count).  Which form of the chunk operands the state scan of gdn_chunk_fwd
+ * (and gdn_chunk_fwd_dev) reads for a call of T tokens in num_seqs sequences:
+ * 0 = W and U (X = U - W S), 1 = A and the raw K, V rows (X = A B (V - Gamma
+ * K S)).  Both give the chunk form's results; they differ in rounding and in
+ * which workspace regions are written.  Always 0 for GDN_F32.  Returns
+ * GDN_EINVAL / GDN_EUNSUPPORTED for invalid arguments.
+ */
+int gdn_chunk_fwd_form(int32_t T, int32_t num_seqs, int32_t H_v, int32_t d, gdn_dtype dtype);
 
 /*
  * Chunk-wise prefill ("实验三：GDN Prefill 前向优化", sections "计算过程描述" and
@@ -196,26 +223,31 @@ typedef struct gdn_output_gate {
 #define GDN_FWD_SCAN_CT1 4u  /* bf16: the state scan takes 1 / 2 / 4 sixteen-column tiles of d_v a */
 #define GDN_FWD_SCAN_CT2 8u  /* workgroup, with as many bins of sequences as fit on the chip at that */
 #define GDN_FWD_SCAN_CT4 16u /* width, instead of the width the host's cost model picks (at most one) */
-#define GDN_FWD_KEEP_WU 32u  /* also form W and U and write them to their regions where the scan does not read them */
-#define GDN_FWD_FORM_W 64u   /* bf16: the state scan reads W and U (X = U - W S), whatever the batch; */
-#define GDN_FWD_FORM_A 128u  /* or A and the raw rows (X = A B (V - Gamma K S)); at most one (see gdn_chunk_fwd_ex) */
+#define GDN_FWD_KEEP_WU 32u  /* also write W and U where the state scan does not read them (A form) */
+#define GDN_FWD_FORM_W 64u   /* bf16: the state scan reads W and U, whatever the batch */
+#define GDN_FWD_FORM_A 128u  /* bf16: the state scan reads A and the raw rows, whatever the batch */
 
 /*
  * gdn_chunk_fwd with options, for inspection, profiling and benchmarks.  Same
  * arguments and results as gdn_chunk_fwd, plus:
  *   flags  0 or a combination of the GDN_FWD_ bits above.  A is an
- *          intermediate nothing downstream reads back (W and U are formed from
- *          it on chip), so gdn_chunk_fwd does not spend the HBM write on it;
- *          GDN_FWD_KEEP_A writes it for inspection.  A GDN_FWD_SCAN_CT bit fixes
- *          the state scan's work split (for tests of every split; the results
- *          are bitwise the same for any split); it is ignored for fp32, which
- *          always scans one tile a workgroup.  Unknown bits, or more than one
- *          GDN_FWD_SCAN_CT bit: GDN_EINVAL.
+ *          intermediate nothing downstream reads back in row-major form (W and
+ *          U, or A's fragments, are formed from it on chip), so gdn_chunk_fwd
+ *          does not spend the HBM write on it; GDN_FWD_KEEP_A writes it for
+ *          inspection, GDN_FWD_KEEP_WU likewise W and U in the A form.  A
+ *          GDN_FWD_SCAN_CT bit fixes the state scan's work split, a
+ *          GDN_FWD_FORM bit the operands it reads (gdn_chunk_fwd_form; for
+ *          tests of every split and form: within a form the results are
+ *          bitwise the same for any split, and the two forms agree to rounding);
+ *          both are ignored for fp32, which always scans one tile a workgroup
+ *          from W and U.  Unknown bits, more than one GDN_FWD_SCAN_CT bit or
+ *          both GDN_FWD_FORM bits: GDN_EINVAL.
  *   gate   NULL, or the read-out epilogue above applied to `out`.
  *   stage_events  NULL or an array of six hipEvent_t created by the caller:
  *          the start and stop events of the three kernels (chunk_prep: gate
- *          cumsum, A, W, U; chunk_state_h: the serial state scan;
- *          chunk_output_o) of the first launch (a launch covers up to 64
+ *          cumsum, A, then W and U or A's fragments; chunk_state_h: the serial
+ *          state scan, with the output for bf16; chunk_output_o for fp32, the
+ *          gated read-out for bf16) of the first launch (a launch covers up to 64
  *          sequences; larger batches take several).  They are stamped by the
  *          kernels' own dispatches, so event 2k+1 minus event 2k is the
  *          execution time of kernel k without launch gaps.

@@ -450,3 +450,22 @@ def test_stream_copy_validation(gdn):
     assert lib.gdn_stream_copy(p, p + 8, 256, None) == -2         # misaligned destination
     assert lib.gdn_stream_copy(p, p + 256, 24, None) == -2        # not a multiple of 16 bytes
     assert lib.gdn_stream_copy(p, p + 128, 256, None) == -1       # overlapping
+
+
+def test_chunk_form_rule(gdn):
+    """Which operands the state scan reads: W and U for a short single sequence
+    (the operand stream fits the Infinity Cache, few tile chains), A and the raw
+    rows for long sequences or batches with more tile chains than the chip holds
+    twice over; fp32 always W and U.  Host logic only (on a part without a
+    device the rule takes 256 compute units)."""
+    assert gdn.chunk_form(4096, 1, 32, 128, "bf16") == "W"
+    assert gdn.chunk_form(8192, 1, 32, 128, "bf16") == "A"
+    assert gdn.chunk_form(65536, 1, 32, 128, "bf16") == "A"
+    assert gdn.chunk_form(30702, 8, 32, 128, "bf16") == "A"
+    assert gdn.chunk_form(34422, 256, 32, 128, "bf16") == "A"
+    assert gdn.chunk_form(65536, 1, 32, 128, "f32") == "W"
+    assert gdn.chunk_form(466, 6, 4, 128, "bf16") == "W"
+    lib = gdn.load_library()
+    assert lib.gdn_chunk_fwd_form(-1, 1, 32, 128, 1) == -1
+    assert lib.gdn_chunk_fwd_form(64, 1, 32, 96, 1) == -1
+    assert lib.gdn_chunk_fwd_form(64, 1, 32, 128, 7) == -2
