@@ -1051,6 +1051,9 @@ __device__ __forceinline__ void chunk_output_waves(const ChunkParams& p, const c
     for (int c = 0; c < nch; ++c) {
         wait_lgkmcnt0();
         asm volatile("s_barrier" ::: "memory");  // B1(c): LS holds -h_c
+        // Bm(c), the compute waves' exchange of B Y in the A form: these waves
+        // have no part in it and pass at once, so it never waits for their work.
+        if constexpr (AF) asm volatile("s_barrier" ::: "memory");
         wait_vmcnt<0>();                         // chunk c's query rows (this wave's only loads) are in LQ
         Frag<T> qf[KS];
 #pragma unroll
@@ -1101,11 +1104,9 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO, AF>::WAVES)) void ch
     // All of the workgroup's LDS is one array: the stage ring first (at LDS
     // offset 0; with another __shared__ object ahead of it the scan ran 50 ->
     // 73 us at T = 4096 on MI355X), then the exchange, output and query-row
-    // buffers, the L2-prefetch sink, the compute waves' step flags and, for a
-    // device table, its copy.
+    // buffers, the L2-prefetch sink and, for a device table, its copy.
     constexpr int SINK_OFF = NST * SS::BYTES + SS::EXCH + SS::OBUF + SS::QBUF;
-    constexpr int FLAG_OFF = SINK_OFF + 256;
-    constexpr int DTAB_OFF = FLAG_OFF + 16;
+    constexpr int DTAB_OFF = SINK_OFF + 256;
     constexpr int LDS_BYTES = DTAB_OFF + (DEV ? (int)((sizeof(SeqTable) + 15) & ~size_t(15)) : 0);
     static_assert(LDS_BYTES <= SS::LDS_CAP, "LDS of the state scan");
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
@@ -1139,7 +1140,6 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO, AF>::WAVES)) void ch
     auto vch = [&](const BinCursor& cu) { return (size_t)cu.ci() * p.H_v + h; };
     auto kch = [&](const BinCursor& cu) { return (size_t)cu.ci() * p.H_q + hq; };
 
-    int* const csync = reinterpret_cast<int*>(smem + FLAG_OFF);  // the compute waves' step flags (see sync4)
     char* const LS = smem + NST * SS::BYTES;  // KS x CT blocks: -S (block ks CT + ct)
     char* const LX = LS + KS * CT * SS::XBLK; // 2 x CT blocks: X (block j CT + ct)
     char* const LY = LX + 2 * CT * SS::XBLK;  // 2 x CT blocks: kf X
@@ -1282,6 +1282,7 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO, AF>::WAVES)) void ch
             const size_t ch = vch(cs);
             cs.next();
             asm volatile("s_barrier" ::: "memory");  // B1(c)
+            if constexpr (AF) asm volatile("s_barrier" ::: "memory");  // Bm(c): passed at once
             if (cpf.valid() && (AF || p.l2_prefetch)) {
                 const size_t chp = vch(cpf), kchp = kch(cpf);
                 const int nlt = p.l2_prefetch ? NLT : VLT;
@@ -1429,6 +1430,9 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO, AF>::WAVES)) void ch
             if (cn < nch) {
                 if (pw == 0) wait_vmcnt<R0_0>(); else wait_vmcnt<R0_1>();
                 state_issue<T, D, CT, FO, AF>(stn, p, chn, kchn, tokn, elln, h, tile, lane, pw, 0);
+            }
+            if constexpr (AF) asm volatile("s_barrier" ::: "memory");  // Bm(c): after the first half went out
+            if (cn < nch) {
                 if constexpr (NST != 3) {
                     if (pw == 0) wait_vmcnt<WB_0>(); else wait_vmcnt<WB_1>();
                 }
@@ -1575,25 +1579,6 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO, AF>::WAVES)) void ch
     auto xfb = [&](int b, int ln) -> Frag<PT>& {
         return *reinterpret_cast<Frag<PT>*>(LB + b * SS::XBLK + ln * (int)sizeof(Frag<PT>) + (ln >> 4) * SS::XPAD);
     };
-    // A form: the four compute waves alone meet between the two products of a
-    // step (the other waves have no part in B Y, and a workgroup barrier would
-    // make the serial chain wait for them).  A wave writes its B Y fragments,
-    // waits for the writes to complete, then writes its step number into its
-    // flag word; a reader waits until all four flags show the step before it
-    // reads the fragments.  The wait is bounded; it always ends well before the
-    // bound, since all four waves reach this point after the same barrier B1
-    // with nothing else to wait for.
-    if (w == 0 && lane < 4) csync[lane] = 0;  // published by B0
-    const unsigned flag_addr = lds_addr(&csync[w]), flags_addr = lds_addr(&csync[0]);
-    auto sync4 = [&](int target) {
-        asm volatile("s_waitcnt lgkmcnt(0)\n\tds_write_b32 %0, %1" ::"v"(flag_addr), "v"(target) : "memory");
-        for (int it = 0; it < (1 << 20); ++it) {
-            u32x4 fl;
-            asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(fl) : "v"(flags_addr) : "memory");
-            const int mn = min(min((int)fl[0], (int)fl[1]), min((int)fl[2], (int)fl[3]));
-            if (__builtin_amdgcn_readfirstlane(mn) >= target) break;
-        }
-    };
     bar();  // B0: stages 0 and 1 ready
     if (nch > 0) read_stage(0);
     // The bin's sequences one after another (the inner loop is one sequence's
@@ -1635,7 +1620,7 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO, AF>::WAVES)) void ch
                 }
                 // X = A (B Y) for positions 16 w .. 16 w + 15 (A is lower triangular:
                 // row tiles 0 and 1 see positions < 32 only)
-                sync4(c + 1);  // Bm(c): all of B Y in LB
+                bar();  // Bm(c): all of B Y in LB
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
                     X[ct] = mma(a0, xfb(ct, lane), zero4());
