@@ -1223,9 +1223,12 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO, AF>::WAVES)) void ch
         // With four tiles those extra lines cost more than they save.  A form:
         // the K and A lines likewise by size, and the value rows always: nothing
         // upstream reads them, so they come cold from HBM, and the stage ring
-        // alone issues them only two steps and a half ahead.
+        // alone issues them only two steps and a half ahead; with one tile the
+        // query rows, P and the gate blocks too where the stream is twice that
+        // size (T = 65536 in the A form: 1472 -> 1356 us a call; at T = 8192,
+        // below that size, they cost 5 us).
         constexpr int PF = 6;
-        constexpr bool XPF = FO && CT == 1 && !AF;
+        constexpr bool XPF = FO && CT == 1;
         constexpr int VRL = D * (int)sizeof(T) / 128;                // lines per value row
         constexpr int VLT = AF ? CHUNK * VRL / NTW : 0;              // value-row lines per workgroup
         constexpr int WLT = SS::W_BYTES / 128 / NTW;                 // lines of W per workgroup
@@ -1238,7 +1241,8 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO, AF>::WAVES)) void ch
         constexpr int PLT = XPF ? SS::P_BYTES / 128 / NTW : 0;
         constexpr int ULT = XPF ? SS::U_BYTES / 128 : 0;
         constexpr int GLT = XPF ? SS::G_BYTES / 128 : 0;
-        constexpr int NLT = VLT + WLT + KLT + ALT + QLT + PLT + ULT + GLT;
+        constexpr int XLT = QLT + PLT + ULT + GLT;                   // the lines for the output waves
+        constexpr int NLT = VLT + WLT + KLT + ALT + XLT;
         constexpr int NPL = (NLT + 63) / 64;                         // prefetch loads per lane
         // Output tile of chunk c (FO) from LO to O.  A row of the tile is 32 CT
         // contiguous bytes of O, so 2 CT lanes share a row, 16 bytes each (column
@@ -1285,7 +1289,7 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO, AF>::WAVES)) void ch
             if constexpr (AF) asm volatile("s_barrier" ::: "memory");  // Bm(c): passed at once
             if (cpf.valid() && (AF || p.l2_prefetch)) {
                 const size_t chp = vch(cpf), kchp = kch(cpf);
-                const int nlt = p.l2_prefetch ? NLT : VLT;
+                const int nlt = p.l2_prefetch == 0 ? VLT : AF && p.l2_prefetch == 1 ? NLT - XLT : NLT;
 #pragma unroll
                 for (int q = 0; q < NPL; ++q) {
                     int x = lane + 64 * q;
@@ -2140,9 +2144,11 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
     };
     // The state scan's L2 prefetch pays when its W / K / U stream no longer
     // fits in the 256 MB Infinity Cache next to the layer's other tensors: on
-    // above 128 MiB of stream.
+    // above 128 MiB of stream (level 1), and in the A form the output waves'
+    // lines too above 256 MiB (level 2).
     ChunkParams pl = p;
-    pl.l2_prefetch = (size_t)work_ch * StateStage<T, D>::BYTES > (size_t(128) << 20) ? 1 : 0;
+    const size_t stage_stream = (size_t)work_ch * StateStage<T, D>::BYTES;
+    pl.l2_prefetch = stage_stream > (size_t(256) << 20) ? 2 : stage_stream > (size_t(128) << 20) ? 1 : 0;
     // The form of the chunk's operands the state scan reads (decided by the
     // host from the call's sequence count; fp32 always W and U).
     const bool af = sizeof(T) == 2 && p.aform;

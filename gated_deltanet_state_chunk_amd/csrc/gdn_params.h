@@ -62,7 +62,7 @@ struct ChunkParams {
     int32_t aform;     // nonzero (bf16): the state scan forms X from A and the raw rows instead of W and U
     int32_t keep_hx;  // nonzero: the state scan writes Ht, Xt even where the output is formed on chip
     int32_t T;       // tokens of the whole batch (bounds the gated read-out's rows on the device-table path)
-    int32_t l2_prefetch;  // nonzero: chunk_state_h prefetches W / K into L2 (set by the launcher)
+    int32_t l2_prefetch;  // chunk_state_h's L2 prefetch: 0 off, 1 the stage lines, 2 also the output waves' (launcher)
     // optional read-out epilogue out = rmsnorm(o) * gw * silu(gz) (gz null: none)
     const void* gz;
     const float* gw;
