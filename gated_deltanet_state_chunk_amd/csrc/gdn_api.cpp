@@ -365,7 +365,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, 
     p.Kc = ws + L.off_Kc;
     p.Ht = ws + L.off_Ht; p.Xt = ws + L.off_Xt;
     p.Pf = dtype == GDN_BF16 ? ws + L.off_P : nullptr;
-    p.Qc = (dtype == GDN_BF16 && front) ? ws + L.off_Qc : nullptr;
+    p.Qc = dtype == GDN_BF16 ? ws + L.off_Qc : nullptr;
     p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
     p.keep_A = (flags & GDN_FWD_KEEP_A) ? 1 : 0;
     p.keep_wu = (flags & GDN_FWD_KEEP_WU) ? 1 : 0;
@@ -525,7 +525,8 @@ int layout_for_chunks(int64_t nc, int32_t H_q, int32_t H_v, int32_t d_k, int32_t
     L.off_Xt = off; off = align_up(off + chv * (size_t)d_v * C * es);
     // P (bf16 only: the output is formed inside the state scan): six 1 KiB fragments
     L.off_P = off; off = align_up(off + (dtype == GDN_BF16 ? chv * 6 * 64 * 8 * es : 0));
-    // Qc (bf16 only): the front end's normalised query rows, one copy per key head
+    // Qc (bf16 only): the query rows (normalised by the front end) as the state
+    // scan's output waves' operand fragments, one copy per key head
     L.off_Qc = off; off = align_up(off + (dtype == GDN_BF16 ? chq * C * (size_t)d_k * es : 0));
     // A's six MFMA fragments (64 lanes x 8 values, in the two-byte product type
     // for bf16 inputs, fp32 for fp32)
@@ -650,6 +651,7 @@ int gdn_chunk_fwd_dev(const void* q, const void* k, const void* v, const float* 
     p.Kc = ws + L.off_Kc;
     p.Ht = ws + L.off_Ht; p.Xt = ws + L.off_Xt;
     p.Pf = dtype == GDN_BF16 ? ws + L.off_P : nullptr;
+    p.Qc = dtype == GDN_BF16 ? ws + L.off_Qc : nullptr;
     p.H_q = H_q; p.H_v = H_v; p.G = H_v / H_q; p.scale = scale;
     p.T = T;
     p.aform = a_form(T, num_seqs, H_v, d_k, dtype, gdn::cu_count());

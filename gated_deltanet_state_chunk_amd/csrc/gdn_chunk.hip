@@ -442,8 +442,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
     // i = 16 w + r16, P^T[j][i] = (k_j . q_i) exp(gc_i - gc_j) for j <= i < ell
     // (Lower keeps the diagonal), K_J from the staged keys.  With the front end
     // the query rows are L2-normalised first (the row spread over the four lanes
-    // of lane % 16), and the first value head of each key head keeps them (Qc)
-    // for the state scan's output waves, piece i of row r at i ^ (r mod pieces).
+    // of lane % 16).  Where the state scan reads them (the launcher passes Qc:
+    // one column tile a workgroup, or the front end), the first value head of
+    // each key head keeps the rows for its output waves, as the B operands of their h^T Q^T
+    // product: wave w's fragment (w, ks) holds, in lane 16 a + r, slot 4 hh + b,
+    // q[16 w + r][32 ks + 16 hh + 4 a + b] (the exchanged -S fragments' d_k
+    // order), so that each output wave loads a step's query operand as four
+    // 1 KiB pieces straight into registers.  This lane's 8 values are d_k
+    // 32 ks + 8 grp .. + 7: two 4-value halves, each a half of another lane's slots.
     if constexpr (sizeof(T) == 2) {
         if (p.Pf) {
             const int row = 16 * w + r16;
@@ -458,13 +464,18 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void chunk_prep_kernel
                 for (int ks = 0; ks < D / 32; ++ks)
 #pragma unroll
                     for (int j = 0; j < 8; ++j) frag_set(qw[ks], j, frag_get(qw[ks], j) * r);
-                if (h % p.G == 0) {
-                    constexpr int PPR = D / 8;
-                    T* Qcb = reinterpret_cast<T*>(p.Qc) + (((size_t)cp.ci * p.H_q + h / p.G) * CHUNK + row) * D;
+            }
+            if (p.Qc && h % p.G == 0) {
+                T* Qcb = reinterpret_cast<T*>(p.Qc) + (((size_t)cp.ci * p.H_q + h / p.G) * 4 + w) * (D / 32) * 64 * 8;
 #pragma unroll
-                    for (int ks = 0; ks < D / 32; ++ks)
-                        *reinterpret_cast<Frag<T>*>(Qcb + 8 * ((4 * ks + grp) ^ (row % PPR))) = qw[ks];
-                }
+                for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int e = 8 * grp + 4 * hf;  // first d_k offset of the half within the step
+                        const int a = (e & 15) >> 2, hh = e >> 4;
+                        *reinterpret_cast<bf16x4*>(Qcb + ((ks * 64 + 16 * a + r16) * 8 + 4 * hh)) =
+                            bf16x4{qw[ks].v[4 * hf], qw[ks].v[4 * hf + 1], qw[ks].v[4 * hf + 2], qw[ks].v[4 * hf + 3]};
+                    }
             }
             f32x4 pt[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
@@ -738,7 +749,7 @@ struct StateStage {
     static_assert(sizeof(PT) == sizeof(T), "B Y shares the exchange block size");
     static constexpr int EXCH = (D / 32 + (AF ? 6 : 4)) * CT * XBLK;
     static constexpr int OBUF = FO ? 4 * CT * 64 * 8 : 0;  // output tiles (bf16: 4 values a lane, per wave and tile)
-    static constexpr int QBUF = FO ? 4 * 16 * D * (int)sizeof(T) : 0;  // each output wave's 16 query rows
+    static constexpr int QBUF = FO && CT > 1 ? 4 * 16 * D * (int)sizeof(T) : 0;  // each output wave's 16 query rows
     // Three stages where they fit and one producer wave can keep them fed (a
     // chunk is issued two steps and a half before it is read), else two.  The
     // third stage pays where the stream comes from HBM (T = 65536: 991 -> 902
@@ -992,47 +1003,62 @@ __device__ __forceinline__ void chunk_output_waves(const ChunkParams& p, const c
         return *reinterpret_cast<const Frag<T>*>(buf + b * SS::XBLK + lane * (int)sizeof(Frag<T>) +
                                                  (lane >> 4) * SS::XPAD);
     };
-    // Query rows: each wave copies its 16 rows of the chunk into its own LDS
-    // buffer with 1 KiB direct-to-LDS loads (four rows each; the 16-byte pieces
-    // of row r permuted by r so that the fragment reads below spread over the
-    // banks), issued a step ahead, right after the previous chunk's fragments
-    // have been read out.  Rows past the valid length re-read the last valid
-    // row; their outputs are never stored.  (Loaded straight into registers,
-    // 8 bytes of 16 rows an instruction, the rows cost the serial chain 45 us
-    // at T = 4096: the CU's vector-memory path is shared with the producers.)
+    // Query operand.  One column tile a workgroup: this wave's four fragments
+    // of the chunk's rows come from chunk_prep's copy Qc, already in operand
+    // order (four 1 KiB loads), straight into registers a step ahead, so none
+    // of it passes through LDS, which the first half of a step is short of
+    // (T = 65536: scan 1034 -> 962 us for 25 us more in chunk_prep).  With more
+    // tiles, where the copy costs chunk_prep more than the scan saves, each wave
+    // copies its 16 rows into its own LDS buffer with 1 KiB direct-to-LDS
+    // loads, issued a step ahead right after the previous chunk's fragments
+    // have been read out: from Qc with the front end (normalised, in operand
+    // order), else from q, the 16-byte pieces of row r permuted by r so that
+    // the fragment reads spread over the banks (rows past the valid length
+    // re-read the last valid row; their outputs are never stored).
+    constexpr bool QREG = CT == 1;
     constexpr int RB = D * (int)sizeof(T), PPR = RB / 16;  // row bytes, 16-byte pieces a row
     char* const lq = LQ + o * 16 * RB;
-    // With the front end the rows come normalised, already in that order, from
-    // chunk_prep's copy Qc (contiguous: the wave's 16 rows are 16 RB bytes).
-    BinCursor cq;  // the chunk whose query rows are copied next
+    BinCursor cq;  // the chunk whose query rows are loaded next
     cq.begin(tab, kb, ke);
+    Frag<T> qn[KS];
+    auto qc_block = [&]() {  // this wave's fragments in Qc (16 RB bytes)
+        return reinterpret_cast<const char*>(p.Qc) + (((size_t)cq.ci() * p.H_q + hq) * 4 + o) * 16 * RB;
+    };
     auto load_q = [&]() {
-        if (p.Qc) {
-            const char* q0 = reinterpret_cast<const char*>(p.Qc) + (((size_t)cq.ci() * p.H_q + hq) * CHUNK + 16 * o) * RB;
+        if constexpr (QREG) {
+            const Frag<T>* q0 = reinterpret_cast<const Frag<T>*>(qc_block());
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qn[ks] = q0[ks * 64 + lane];
+        } else if (p.Qc) {
+            const char* q0 = qc_block();
 #pragma unroll
             for (int i = 0; i < 16 * PPR / 64; ++i) dma_1k(q0 + 1024 * i, lq + 1024 * i, lane);
-            cq.next();
-            return;
-        }
-        const int ell = cq.ell();
-        const char* q0 = reinterpret_cast<const char*>(p.q) + ((size_t)cq.token() * p.H_q + hq) * RB;
+        } else {
+            const int ell = cq.ell();
+            const char* q0 = reinterpret_cast<const char*>(p.q) + ((size_t)cq.token() * p.H_q + hq) * RB;
 #pragma unroll
-        for (int i = 0; i < 16 * PPR / 64; ++i) {
-            const int e = 64 * i + lane, r = e / PPR, pc = (e % PPR) ^ (r % PPR);
-            const char* src = q0 + (size_t)min(16 * o + r, ell - 1) * p.H_q * RB + 16 * pc;
-            __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(lq + 1024 * i), 16, 0, 0);
+            for (int i = 0; i < 16 * PPR / 64; ++i) {
+                const int e = 64 * i + lane, r = e / PPR, pc = (e % PPR) ^ (r % PPR);
+                const char* src = q0 + (size_t)min(16 * o + r, ell - 1) * p.H_q * RB + 16 * pc;
+                __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(lq + 1024 * i), 16, 0, 0);
+            }
         }
         cq.next();
     };
     // fragment ks of this lane's row: slots 0..3 <- d_k 32 ks + 4 grp .. + 3,
     // slots 4..7 <- 32 ks + 16 + 4 grp .. + 3 (the exchange fragments' d_k order)
-    auto q_frag = [&](int ks) {
-        const char* row = lq + r16 * RB + 8 * (grp & 1);
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 16 * ((4 * ks + (grp >> 1)) ^ (r16 % PPR)));
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 16 * ((4 * ks + 2 + (grp >> 1)) ^ (r16 % PPR)));
-        Frag<T> f;
-        f.v = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        return f;
+    auto q_frag = [&](int ks) -> Frag<T> {
+        if constexpr (QREG) {
+            return qn[ks];
+        } else {
+            if (p.Qc) return *reinterpret_cast<const Frag<T>*>(lq + (ks * 64 + lane) * 16);
+            const char* row = lq + r16 * RB + 8 * (grp & 1);
+            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 16 * ((4 * ks + (grp >> 1)) ^ (r16 % PPR)));
+            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 16 * ((4 * ks + 2 + (grp >> 1)) ^ (r16 % PPR)));
+            Frag<T> f;
+            f.v = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            return f;
+        }
     };
     Frag<T> pf0, pf1;
     float gq = 0.f;
@@ -1054,11 +1080,11 @@ __device__ __forceinline__ void chunk_output_waves(const ChunkParams& p, const c
         // Bm(c), the compute waves' exchange of B Y in the A form: these waves
         // have no part in it and pass at once, so it never waits for their work.
         if constexpr (AF) asm volatile("s_barrier" ::: "memory");
-        wait_vmcnt<0>();                         // chunk c's query rows (this wave's only loads) are in LQ
+        wait_vmcnt<0>();  // chunk c's query rows (this wave's only loads)
         Frag<T> qf[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[ks] = q_frag(ks);
-        wait_lgkmcnt0();                         // read out before the next chunk's rows overwrite them
+        if constexpr (!QREG) wait_lgkmcnt0();  // read out before the next chunk's rows overwrite them
         if (c + 1 < nch) load_q();
         // -(h^T Q^T) from LS (which holds -h_c until B2(c))
         f32x4 inter[CT];
@@ -1146,7 +1172,7 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO, AF>::WAVES)) void ch
     char* const LB = LY + 2 * CT * SS::XBLK;  // A form: 2 x CT blocks: B Y (A's operand type)
     char* const LO = LB + (AF ? 2 : 0) * CT * SS::XBLK;  // FO: output tiles, 8 bytes per (tile ct, wave, lane)
     static_assert(SS::EXCH == (KS + (AF ? 6 : 4)) * CT * SS::XBLK, "exchange blocks: LS, LX, LY (and LB)");
-    char* const LQ = LO + SS::OBUF;           // FO: each output wave's query rows
+    char* const LQ = LO + SS::OBUF;           // FO, more than one tile: each output wave's query rows
     char* const sink = smem + SINK_OFF;       // L2-prefetch sink
     static_assert(SINK_OFF == (NST * SS::BYTES + SS::EXCH) + SS::OBUF + SS::QBUF, "buffers in order");
     // fragment of lane ln in block b of an exchange buffer
@@ -1305,16 +1331,8 @@ __global__ __launch_bounds__((64 * StateStage<T, D, CT, FO, AF>::WAVES)) void ch
                         a = reinterpret_cast<const char*>(p.Kc) + kchp * SS::K_BYTES + (tile * KLT + x) * 128;
                     } else if ((x -= KLT) < ALT) {
                         a = reinterpret_cast<const char*>(p.Af) + chp * SS::A_BYTES + (tile * ALT + x) * 128;
-                    } else if ((x -= ALT) < QLT) {  // line li of the chunk's query rows
-                        constexpr int QRB = D * (int)sizeof(T), LPR = QRB / 128;
-                        const int li = tile * QLT + x;
-                        if (p.Qc) {
-                            a = reinterpret_cast<const char*>(p.Qc) + kchp * CHUNK * QRB + li * 128;
-                        } else {
-                            const int row = min(li / LPR, cpf.ell() - 1);
-                            a = reinterpret_cast<const char*>(p.q) + ((size_t)(cpf.token() + row) * p.H_q + hq) * QRB +
-                                128 * (li % LPR);
-                        }
+                    } else if ((x -= ALT) < QLT) {  // line of the chunk's query fragments (Qc)
+                        a = reinterpret_cast<const char*>(p.Qc) + kchp * SS::K_BYTES + (tile * QLT + x) * 128;
                     } else if ((x -= QLT) < PLT) {
                         a = reinterpret_cast<const char*>(p.Pf) + chp * SS::P_BYTES + (tile * PLT + x) * 128;
                     } else if ((x -= PLT) < ULT) {
@@ -2153,6 +2171,9 @@ hipError_t launch_chunk_pipeline(const ChunkParams& p, hipStream_t stream, hipEv
     // host from the call's sequence count; fp32 always W and U).
     const bool af = sizeof(T) == 2 && p.aform;
     pl.write_af = af ? 1 : 0;
+    // chunk_prep keeps the query rows (Qc) where the state scan reads them: one
+    // column tile a workgroup, or the front end's normalised rows.
+    pl.Qc = (p.fa || ct == 1) ? p.Qc : nullptr;
     // chunk_prep: with few items a slot, as many workgroups as fit on the chip at
     // once (four per CU), each looping over its items and prefetching the next
     // one (T = 4096, two items a slot: 36 against 38 us with one workgroup an

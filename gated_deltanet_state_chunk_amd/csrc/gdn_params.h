@@ -53,7 +53,7 @@ struct ChunkParams {
     void* Ht;
     void* Xt;
     void* Pf;   // per (chunk, value head): P as the output's B operands (bf16; null: P not formed)
-    void* Qc;   // per (chunk, key head): the L2-normalised query rows (bf16 with the front end; else null)
+    void* Qc;   // per (chunk, key head): the query rows as the output waves' operand fragments (bf16; else null)
     int32_t H_q, H_v, G;
     float scale;
     int32_t keep_A;  // nonzero: chunk_prep also writes A to the workspace

@@ -127,10 +127,13 @@ typedef struct ihipStream_t *hipStream_t;
  *                                            tile t, key step s) = (0,0), (1,0), (2,0), (2,1),
  *                                            (3,0), (3,1): lane 16 a + r, slot 4 h + b holds
  *                                            P[16 t + r][32 s + 16 h + 4 a + b]
- *   Qc  bf16  [n_chunks][H_q][64][d_k]       (bf16 only; written by gdn_chunk_fwd_fused) the
- *                                            chunk's L2-normalised query rows, zero past
- *                                            the valid length, the 16-byte pieces of row r
- *                                            permuted: piece i at i ^ (r mod P), P as for Kc
+ *   Qc  bf16  [n_chunks][H_q][4][d_k/32][64][8] (bf16 only; written when the state scan
+ *                                            takes one 16-column tile a workgroup, and by
+ *                                            gdn_chunk_fwd_fused) the chunk's query rows
+ *                                            (L2-normalised with the front end), zero
+ *                                            past the valid length, as fragments (w, s): lane
+ *                                            16 a + r, slot 4 h + b holds
+ *                                            q[16 w + r][32 s + 16 h + 4 a + b]
  *   Af  utype [n_chunks][H_v][6][64][8]      A's fragments (above), A form only; rows past
  *                                            the valid length are unit rows
  * For bf16 the chunk-start states and U - W S never leave the chip (the output

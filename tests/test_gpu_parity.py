@@ -177,6 +177,50 @@ def test_inspection_regions_untouched_without_flags(torch_cuda):
     assert rel_err(to_host(oa), to_host(ow)) < 1e-2 and rel_err(to_host(fa), to_host(fw)) < 1e-2
 
 
+def test_query_copy_in_operand_order(torch_cuda):
+    """With one 16-column tile a state-scan workgroup, chunk_prep keeps each
+    chunk's query rows (Qc) as the output waves' operand fragments: fragment
+    (w, s) of a chunk and key head holds, in lane 16 a + r, slot 4 h + b,
+    q[16 w + r][32 s + 16 h + 4 a + b], zero past the valid length.  With four
+    tiles (and no front end) the scan reads q itself and Qc is left alone."""
+    import torch
+
+    import gated_deltanet_state_chunk_amd as gdn
+
+    H_q, H_v, d = 2, 4, 128
+    inp = gdn_inputs.make_prefill(seed=13, seqlens=[100, 37], H_q=H_q, H_v=H_v, d_k=d, d_v=d, dtype="bf16")
+    lay = gdn.workspace_layout(inp.T, inp.cu_seqlens, H_q, H_v, d, d, "bf16")
+    q0 = lay["off_Qc"]
+    args = [to_dev(inp.q, "bf16"), to_dev(inp.k, "bf16"), to_dev(inp.v, "bf16"), f32_dev(inp.g), f32_dev(inp.beta),
+            inp.cu_seqlens]
+    # expected copy: [chunk][key head][w][s][lane][slot]
+    starts = [(0, 64), (64, 36), (100, 37)]  # (first token, valid length) of each chunk
+    exp = np.zeros((len(starts), H_q, 4, d // 32, 64, 8), dtype=np.float64)
+    qf = inp.q32()
+    for c, (t0, ell) in enumerate(starts):
+        for hq in range(H_q):
+            for w in range(4):
+                for s in range(d // 32):
+                    for lane in range(64):
+                        a, r = lane // 16, lane % 16
+                        if 16 * w + r < ell:
+                            for hh in range(2):
+                                exp[c, hq, w, s, lane, 4 * hh:4 * hh + 4] = \
+                                    qf[t0 + 16 * w + r, hq, 32 * s + 16 * hh + 4 * a:32 * s + 16 * hh + 4 * a + 4]
+    q1 = q0 + 2 * exp.size
+    assert q1 <= lay["off_Af"]
+    for form in ("W", "A"):
+        ws = torch.full((lay["total_bytes"],), 0xA5, dtype=torch.uint8, device="cuda")
+        gdn.chunk_fwd(*args, scale=inp.scale, workspace=ws, scan_ct=1, form=form)
+        torch.cuda.synchronize()
+        got = to_host(ws[q0:q1].view(torch.bfloat16)).reshape(exp.shape)
+        assert np.array_equal(got, exp), form
+        ws.fill_(0xA5)
+        gdn.chunk_fwd(*args, scale=inp.scale, workspace=ws, scan_ct=4, form=form)
+        torch.cuda.synchronize()
+        assert bool((ws[q0:q1] == 0xA5).all()), form
+
+
 # ---------------------------------------------------------------------------
 # Per-stage intermediates against the chunk-form oracle
 # ---------------------------------------------------------------------------

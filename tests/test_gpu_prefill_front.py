@@ -50,6 +50,29 @@ def test_fused_prefill_matches_oracle(torch_cuda, oracle_mod, dtype, d):
     assert rel_err(to_host(fin), ref_f) < TOL[dtype]
 
 
+def test_fused_prefill_many_sequences_wide_tiles(torch_cuda, oracle_mod):
+    """48 ragged requests (some empty) at H_q = 16, H_v = 32, d = 128, bf16:
+    the host packs them into bins of four 16-column tiles a workgroup, whose
+    output waves read the normalised query rows through LDS (one tile a
+    workgroup loads them straight into registers; both from chunk_prep's copy
+    in operand order).  Sampled heads against the oracle."""
+    import gated_deltanet_state_chunk_amd as gdn
+
+    lens = [int(x) for x in np.random.default_rng(47).integers(1, 200, 48)]
+    lens[5] = lens[30] = 0
+    inp = gdn_inputs.make_prefill_raw(48, lens, 16, 32, 128, 128, "bf16")
+    print(f"[front wide] {len(lens)} sequences, T={inp.T}", flush=True)
+    out, fin = gdn.chunk_fwd_fused(*_dev(inp), inp.cu_seqlens, initial_state=f32_dev(inp.initial_state))
+    heads = [0, 13, 31]
+    ref_o, ref_f = oracle_mod.forward_fused(inp.f32("q"), inp.f32("k"), inp.f32("v"), inp.f32("a"), inp.f32("b"),
+                                            inp.A_log, inp.dt_bias, inp.cu_seqlens, inp.H_q, inp.H_v, inp.scale, True,
+                                            initial_state=inp.initial_state, heads=heads)
+    oh, fh = to_host(out), to_host(fin)
+    for h in heads:
+        assert rel_err(oh[:, h], ref_o[:, h]) < 1e-2, h
+        assert rel_err(fh[:, h], ref_f[:, h]) < 1e-2, h
+
+
 def test_fused_prefill_edge_inputs(torch_cuda, oracle_mod):
     """Gate inputs across both softplus overflow branches, saturated beta, and
     all-zero q or k rows (the 1e-6 inside the norm keeps them zero)."""
