@@ -62,7 +62,7 @@ CHUNK = 64
 # exploited)
 # ---------------------------------------------------------------------------
 
-def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True, gated=False, form="W"):
+def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True, gated=False, form="W", qcopy=False):
     """Algorithmic bytes and flops of each kernel of one gdn_chunk_fwd.
 
     Bytes: every distinct input read once, every output and intermediate written
@@ -75,9 +75,12 @@ def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True, gated=False, form
     = 2): chunk_prep also forms P (the masked, decayed Q K^T, six 1 KiB
     fragments per chunk and value head), the state scan forms the output from
     P, q and its own on-chip h and X, and the gated read-out (when asked for)
-    is a pass over the output.  fp32 (always form "W"): the chunk-start states
-    h and X go through HBM to a separate output kernel.  Flops: 2 x
-    multiply-adds of the chunk form at full chunks, triangles exploited.
+    is a pass over the output.  qcopy (bf16, where the state scan takes one
+    column tile a workgroup): chunk_prep also writes the query rows in the
+    output waves' operand order (Qc, once per key head), which the scan then
+    reads instead of q.  fp32 (always form "W"): the chunk-start states h and
+    X go through HBM to a separate output kernel.  Flops: 2 x multiply-adds of
+    the chunk form at full chunks, triangles exploited.
     """
     C = CHUNK
     chv, chq = n_chunks * H_v, n_chunks * H_q
@@ -106,11 +109,12 @@ def prefill_work(T, N, n_chunks, H_q, H_v, d, es, has_s0=True, gated=False, form
         prep_b = k_b + v_b + 2 * gate_b + G_b + W_b + U_b + Kc_b
         scan_b = W_b + U_b + Kc_b + G_b
     if es == 2:
+        qs_b = Kc_b if qcopy else q_b  # the scan's query rows: Qc (chunk-padded, like Kc) or q
         per = {"chunk_prep": prep + tri1 * d,                              # + Q K^T
                "chunk_state_o": scan + C * d * d + tri1 * d,               # + Q S, P X
                "gated_readout": 0}
-        bytes_ = {"chunk_prep": prep_b + q_b + P_b,
-                  "chunk_state_o": scan_b + P_b + q_b + s0 + S_b + o_b,
+        bytes_ = {"chunk_prep": prep_b + q_b + P_b + (Kc_b if qcopy else 0),
+                  "chunk_state_o": scan_b + P_b + qs_b + s0 + S_b + o_b,
                   "gated_readout": (3 * o_b + d * 4) if gated else 0}      # o read, z read, out written
     else:
         per = {"chunk_prep": prep,
@@ -319,6 +323,16 @@ def bench_prefill(args, torch, gdn, hip, device, gated=False):
         if rc != 0:
             raise gdn.GdnError(rc, "gdn_chunk_fwd_ex")
 
+    # Whether chunk_prep writes the query copy (Qc) for this batch (the state
+    # scan's choice of tile width): one step on a poisoned workspace.
+    qc0 = lay["off_Qc"]
+    qc1 = qc0 + lay["n_chunks"] * inp.H_q * 64 * inp.d_k * 2
+    qcopy = False
+    if dt == "bf16" and qc1 > qc0:
+        ws[qc0:qc1].fill_(0xA5)
+        step()
+        torch.cuda.synchronize()
+        qcopy = not bool((ws[qc0:qc1] == 0xA5).all())
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -351,9 +365,9 @@ def bench_prefill(args, torch, gdn, hip, device, gated=False):
     es = 2 if dt == "bf16" else 4
     form = gdn.chunk_form(inp.T, inp.N, inp.H_v, inp.d_k, dt)
     bytes_, flops = prefill_work(inp.T, inp.N, lay["n_chunks"], inp.H_q, inp.H_v, inp.d_k, es,
-                                 has_s0=s0 is not None, gated=gated, form=form)
+                                 has_s0=s0 is not None, gated=gated, form=form, qcopy=qcopy)
     return dict(inp=inp, lay=lay, ms_step=ms_step, wall_s=wall, stage_ms=stage_ms, bytes=bytes_, flops=flops,
-                stages=STAGES, ms_step_with_events=timed_ms, warm=warm, cold=cold, form=form)
+                stages=STAGES, ms_step_with_events=timed_ms, warm=warm, cold=cold, form=form, qcopy=qcopy)
 
 
 def bench_prefill_serving(args, torch, gdn, device):
@@ -724,7 +738,7 @@ def main():
                                                              (inp.cu_seqlens[1:] - inp.cu_seqlens[:-1])],
                        "T": inp.T, "H_q": inp.H_q, "H_v": inp.H_v, "d_k": inp.d_k, "d_v": inp.d_v,
                        "chunk": CHUNK, "initial_state": inp.initial_state is not None,
-                       "scan_operands": pre["form"]},
+                       "scan_operands": pre["form"], "query_copy": pre["qcopy"]},
             "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS,
                          "frac_of_achievable": achieved / hbm["gb_per_s"] if hbm else None,
